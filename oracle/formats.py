@@ -1,0 +1,125 @@
+"""Number formats: OCP FP8 E4M3 (decode table, round-to-nearest-even encode),
+bf16 and fp16 bit patterns.  TEST INFRASTRUCTURE ONLY (see package header).
+
+[DG-FP8] describes E4M3 as 1 sign bit, 4 exponent bits and 3 mantissa bits
+with a range of about +-448.  The +-448 range identifies the OCP "E4M3FN"
+variant (exponent bias 7, no infinities, only S.1111.111 is NaN); the FNUZ
+variant tops out at 240.  The decode below is that format's definition.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one E4M3FN code (bias 7; exponent field 0 is subnormal; 0x7F/0xFF NaN).
+
+    Pinned by: closed-form values (0x01 = 2^-9, 0x08 = 2^-6, 0x38 = 1, 0x7E = 448),
+    strict monotonicity of 0x00..0x7E, and equality with torch.float8_e4m3fn.
+    """
+    code = int(code) & 0xFF
+    s = code >> 7
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        v = m * 2.0 ** -9  # subnormal: m/8 * 2^(1-7)
+    else:
+        v = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """float64[256]: value of every code (NaN for the two NaN codes)."""
+    return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+_POS_CODES = np.arange(0x7F, dtype=np.int64)           # 0x00 .. 0x7E: all finite non-negative codes
+_POS_VALUES = np.array([e4m3_value(c) for c in range(0x7F)], dtype=np.float64)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Round float64 values to the nearest E4M3FN code, ties to the even code.
+
+    Requires |v| <= 448 (the quantiser guarantees it, so no saturation rule is
+    needed).  Subnormals are kept; the sign is carried even when the magnitude
+    rounds to zero, so tiny negative inputs give 0x80.
+
+    Pinned by: exhaustive comparison with torch's float8_e4m3fn cast over every
+    finite bf16 with |x| <= 448, and encode(decode(c)) == c for all finite codes.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if np.isnan(v).any():
+        raise ValueError("e4m3_encode: NaN input")
+    a = np.abs(v)
+    if (a > E4M3_MAX).any():
+        raise ValueError("e4m3_encode: |v| > 448")
+    hi = np.searchsorted(_POS_VALUES, a, side="left")  # first value >= a
+    hi = np.minimum(hi, len(_POS_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _POS_VALUES[lo]
+    d_hi = _POS_VALUES[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_POS_CODES[hi] % 2 == 0))
+    exact = _POS_VALUES[hi] == a
+    code = np.where(exact | pick_hi, _POS_CODES[hi], _POS_CODES[lo]).astype(np.uint8)
+    return code | (np.signbit(v).astype(np.uint8) << 7)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """uint16 bf16 patterns -> float64 (exact: bf16 is the top half of an fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """float64 -> nearest bf16 (ties to even), returned as uint16 patterns.
+
+    Used to compare a bf16 output with the value an exact result rounds to.
+    Rounds the float64 directly (no intermediate fp32), via the exact neighbour
+    comparison.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_x = x.reshape(-1)
+    flat_o = out.reshape(-1)
+    for i, val in enumerate(flat_x):
+        flat_o[i] = _bf16_rne_scalar(float(val))
+    return out
+
+
+def _bf16_rne_scalar(val: float) -> int:
+    if math.isnan(val):
+        return 0x7FC0
+    sign = 0x8000 if math.copysign(1.0, val) < 0 else 0
+    a = abs(val)
+    if a == 0.0:
+        return sign
+    # candidates: truncation toward zero of a to bf16 and the next pattern up
+    f32 = np.array([a], dtype=np.float64).astype(np.float32)  # may round; fix below
+    bits = int(f32.view(np.uint32)[0]) >> 16
+    # walk to the largest bf16 pattern whose value <= a
+    def val_of(b):
+        return float(np.array([b << 16], dtype=np.uint32).view(np.float32)[0])
+    while bits > 0 and val_of(bits) > a:
+        bits -= 1
+    while val_of(bits + 1) <= a and bits + 1 < 0x7F80:
+        bits += 1
+    lo_v, hi_v = val_of(bits), val_of(bits + 1)
+    if lo_v == a:
+        return sign | bits
+    d_lo, d_hi = a - lo_v, hi_v - a
+    if d_hi < d_lo or (d_hi == d_lo and (bits & 1)):
+        bits += 1
+    return sign | bits
+
+
+def fp16_bits_to_f64(bits) -> np.ndarray:
+    """uint16 IEEE half patterns -> float64 (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
