@@ -1,0 +1,233 @@
+/*
+ * moe.h -- C ABI of libmoe.so, the MoE grouped-GEMM hot path on gfx950 (MI355X).
+ *
+ * Data flow of one MoE expert layer (rainlin, "GEMM 执行方式", sec. 4.6 flow:
+ * scatter -> grouped GEMM -> gather):
+ *
+ *   moe_quant_act          bf16 tokens -> FP8 E4M3 codes + 1x128 pow2 scales
+ *   moe_route_pack         topk_ids -> per-expert segments; copies token rows
+ *   moe_grouped_gemm_fp8   packed rows x expert weights (128x128 pow2 scales) -> bf16
+ *   moe_grouped_gemm_int4  (weight-only variant) bf16 rows x 4-bit weights -> bf16
+ *   moe_unpermute_combine  topk_weights-weighted sum back to token order
+ *
+ * plus two weight-preparation calls (moe_quant_weight_fp8 / _int4) that turn
+ * bf16 expert weights into the formats the GEMMs read.
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers owned by the caller.  The library
+ *     keeps no pointer after the call returns and allocates no device memory;
+ *     scratch memory, when needed, is passed in as `workspace`.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued asynchronously; no call synchronises the host.  Buffers must stay
+ *     alive until the stream work has finished.
+ *   - Arguments are validated on the host before anything is launched.  A
+ *     failure returns a nonzero moe_status, launches nothing, and leaves a
+ *     human-readable reason in moe_last_error() (thread-local).
+ *   - Conditions only the device can see (an expert id >= E, a masked-layout
+ *     expert receiving more than max_m rows) are ORed as MOE_DEV_* bits into
+ *     *dev_status; the caller zeroes it beforehand and reads it after a sync.
+ *   - Row-major layouts everywhere; "bf16" and "fp16" are uint16 bit patterns.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics; the only atomics are order-free integer
+ *     counts in LDS).
+ *   - Calls on different streams may run concurrently; calls are thread-safe.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  MOE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent             */
+  MOE_ERR_UNSUPPORTED = 3, /* valid in principle, not supported (e.g. K % 128)   */
+  MOE_ERR_ALIGN = 4,       /* a pointer or row stride is not aligned as required */
+  MOE_ERR_HIP = 5,         /* the HIP runtime reported an error at launch        */
+  MOE_ERR_WORKSPACE = 6    /* workspace missing or smaller than required         */
+};
+
+/* bits ORed into *dev_status by moe_route_pack */
+enum {
+  MOE_DEV_ID_RANGE = 1 << 0, /* some topk id was >= E; that route was skipped      */
+  MOE_DEV_CAPACITY = 1 << 1  /* masked layout: an expert got more than max_m rows;  */
+                             /* the surplus routes were dropped (output_index -1) */
+};
+
+enum { MOE_LAYOUT_CONTIGUOUS = 0, MOE_LAYOUT_MASKED = 1 };
+
+enum { MOE_MAX_EXPERTS = 1024, MOE_MAX_TOPK = 64 };
+
+/* Version of this ABI (bumped on any incompatible change). */
+int moe_abi_version(void);
+
+/* Static description of a status code. */
+const char* moe_status_str(moe_status s);
+
+/* Reason for the most recent failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Upper bound on the packed rows of the contiguous layout, computable before
+ * routing: every route takes a row and each non-empty expert pads at most
+ * align-1 rows (rainlin, "GEMM 执行方式", sec. 4.6: segment length is the count
+ * rounded up to the alignment; empty experts take no rows).
+ *   = round_up(T*k + min(E, T*k)*(align-1), align).   Returns -1 on bad input. */
+int64_t moe_packed_rows_cap(int T, int k, int E, int align);
+
+/* Workspace bytes moe_route_pack needs for (T, k, E); 0 when T*k is small
+ * enough for the single-launch path.  Returns -1 on bad input. */
+int64_t moe_route_pack_workspace_bytes(int T, int k, int E);
+
+/* ------------------------------------------------------------------------- */
+/* moe_quant_act: 1x128 FP8 quantisation of activations.
+ * (nxmr.cn DeepGEMM FP8 article, "补偿机制一": every scale factor is an exact
+ *  power of two and the quantiser rounds amax/448 up to one; E4M3 range +-448.)
+ *   x  [rows, K] bf16.  q [rows, K] E4M3FN codes.  sf [rows, K/128] fp32.
+ *   For each row and each 128-wide block along K:
+ *     e  = smallest integer with amax <= 448 * 2^e (amax = max |x| of the block),
+ *          clamped to [-126, 127]; e = 0 when amax == 0;
+ *     sf = 2^e;  q = round-to-nearest-even E4M3 of x * 2^-e (subnormals kept,
+ *          sign kept for values that round to zero).
+ *   Requires K % 128 == 0, x and q 16-byte aligned, sf 4-byte aligned.
+ *   rows == 0 is a no-op. */
+moe_status moe_quant_act(const uint16_t* x, int64_t rows, int K,
+                         uint8_t* q, float* sf, void* stream);
+
+/* moe_quant_weight_fp8: 128x128 FP8 quantisation of expert weights (same rule
+ * per 128x128 block; the article's recipe (gran_m, gran_n, gran_k) with
+ * gran_n = gran_k = 128).
+ *   w [E, N, K] bf16 -> q [E, N, K] E4M3FN codes, sfw [E, N/128, K/128] fp32.
+ *   Requires N % 128 == 0, K % 128 == 0, w and q 16-byte aligned. */
+moe_status moe_quant_weight_fp8(const uint16_t* w, int E, int N, int K,
+                                uint8_t* q, float* sfw, void* stream);
+
+/* moe_quant_weight_int4: group-128 4-bit weight quantisation in the
+ * MatMulNBits layout (ONNX Runtime "MatMulNBits -- CUDA Operator
+ * Documentation", sec. 2 "Weight Format": row n holds K/2 bytes, two 4-bit
+ * weights per byte, one scale per 128 along K, value = (q - 8) * scale).
+ * The pages leave the offline scale rule open; this call uses, per (n, group):
+ *   s = fp16(fp32(amax) / 7)  (s = 1 when amax == 0; the smallest fp16
+ *       subnormal if that underflows to 0; at most 65504),
+ *   q = clip(rne(w / s) + 8, 0, 15) with the division in fp32.
+ *   w [E, N, K] bf16 -> q4 [E, N, K/2] (low nibble = even k),
+ *   s16 [E, N, K/128] fp16.  Requires K % 128 == 0, w 16-byte aligned,
+ *   q4 and s16 4-byte aligned. */
+moe_status moe_quant_weight_int4(const uint16_t* w, int E, int N, int K,
+                                 uint8_t* q4, uint16_t* s16, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* moe_route_pack: routing bookkeeping and packing ("scatter").
+ * (rainlin, "GEMM 执行方式", sec. 4.2-4.3 and 4.6; AsymGEMM README, "Token
+ *  Layout Protocols"; CuTeDSL bei Perplexity, MoE dispatch: count per expert,
+ *  a unique index within the expert, copy into padded buffers.)
+ *
+ *   topk_ids [T, k] int32.  Route i = t*k + r with 0 <= id < E is valid; ids < 0
+ *   are skipped silently, ids >= E are skipped and flag MOE_DEV_ID_RANGE.
+ *   Rows within an expert follow route order i (deterministic, bit-exact).
+ *
+ *   layout MOE_LAYOUT_CONTIGUOUS, align_or_max_m = align (>= 1, e.g. 128):
+ *     segment e starts at sum_{e'<e} round_up(count_e', align); empty experts
+ *     take no rows.  rows_cap >= moe_packed_rows_cap(T, k, E, align).
+ *   layout MOE_LAYOUT_MASKED, align_or_max_m = max_m (>= 1):
+ *     segment e starts at e*max_m; an expert's routes beyond the first max_m are
+ *     dropped (output_index -1, MOE_DEV_CAPACITY).  rows_cap >= E*max_m.
+ *
+ *   Outputs:
+ *     counts[E]        rows placed in each segment (masked: at most max_m)
+ *     seg_offsets[E+1] segment starts; [E] = packed total (masked: E*max_m)
+ *     m_indices[rows_cap] expert of each packed row (padding rows included);
+ *                      -1 past the packed total
+ *     output_index[T,k] packed row of each route, -1 if none
+ *     packed  [rows_cap, payload_row_bytes]:   packed[output_index[t,r]] = payload[t]
+ *     packed2 [rows_cap, payload2_row_bytes]:  same for a second per-token payload
+ *                      (e.g. the FP8 scale rows); pass NULL/0 if unused.
+ *   Padding rows of packed/packed2 are never written.
+ *   Row byte counts must be multiples of 4; payload/packed must be 16-byte
+ *   aligned (payload2/packed2: 4-byte).  workspace: at least
+ *   moe_route_pack_workspace_bytes(T, k, E) bytes (may be NULL when that is 0).
+ *   Calls that overlap on one stream must not share a workspace. */
+moe_status moe_route_pack(const int32_t* topk_ids, int T, int k, int E,
+                          int layout, int align_or_max_m,
+                          const void* payload, int64_t payload_row_bytes,
+                          const void* payload2, int64_t payload2_row_bytes,
+                          void* packed, void* packed2, int64_t rows_cap,
+                          int32_t* counts, int32_t* seg_offsets,
+                          int32_t* m_indices, int32_t* output_index,
+                          int32_t* dev_status,
+                          void* workspace, int64_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* moe_grouped_gemm_fp8: block-scaled FP8 grouped GEMM, "NT" (both operands
+ * K-contiguous).  (rainlin, "GEMM 执行方式", sec. 4.1/4.4: Y_e = X_e W_e^T per
+ *  expert; AsymGEMM README, "API Reference" (m_grouped_fp8 contiguous/masked,
+ *  (data, scale) operands, bf16 output) and "asymScheduler" (each workgroup
+ *  owns expert tiles, no atomics); nxmr.cn DeepGEMM article: FP32 accumulation
+ *  with per-block scales.)
+ *
+ *   For every segment e and row p in [start_e, start_e + counts[e]):
+ *     D[p, n] = bf16_rne( sum_kb sa[p,kb] * sw[e, n/128, kb] *
+ *                         sum_{k in kb} dec(A[p,k]) * dec(W[e,n,k]) )
+ *   accumulated in fp32 (the per-128-K-block scales are applied inside the
+ *   matrix instruction, which is exact for powers of two).
+ *     A   [rows, K] E4M3FN, SFA [rows, K/128] fp32 powers of two
+ *     W   [E, N, K] E4M3FN, SFW [E, N/128, K/128] fp32 powers of two
+ *     D   [rows, N] bf16
+ *   layout CONTIGUOUS: start_e = seg_offsets[e], rows_cap_or_max_m = rows of A/D.
+ *   layout MASKED:     start_e = e*max_m, rows_cap_or_max_m = max_m,
+ *                      seg_offsets ignored (may be NULL), rows = E*max_m.
+ *   counts[e] is clipped to the segment capacity on the device.
+ *   expected_m: tiling hint, the mean rows per active expert (0 = choose from
+ *   the layout).  Rows of D outside the segments are never written.
+ *   Requires K % 128 == 0, N % 128 == 0, 1 <= E <= 1024, A/W/D 16-byte aligned. */
+moe_status moe_grouped_gemm_fp8(int layout,
+                                const uint8_t* A, const float* SFA,
+                                const uint8_t* W, const float* SFW,
+                                uint16_t* D,
+                                const int32_t* counts, const int32_t* seg_offsets,
+                                int E, int64_t rows_cap_or_max_m, int N, int K,
+                                int expected_m, void* stream);
+
+/* moe_grouped_gemm_int4: 4-bit weight-only grouped GEMM (ONNX Runtime
+ * "MatMulNBits -- CUDA Operator Documentation", sec. 2: (q - 8) * scale with
+ * group 128 along K).
+ *     D[p, n] = bf16_rne( sum_g s[e,n,g] * sum_{k in g} A[p,k] * (q[e,n,k] - 8) )
+ *   accumulated in fp32.
+ *     A   [rows, K] bf16,  W4 [E, N, K/2] (low nibble = even k),
+ *     S16 [E, N, K/128] fp16,  D [rows, N] bf16.
+ *   Layout, counts, seg_offsets, expected_m and alignment as for
+ *   moe_grouped_gemm_fp8. */
+moe_status moe_grouped_gemm_int4(int layout,
+                                 const uint16_t* A, const uint8_t* W4,
+                                 const uint16_t* S16, uint16_t* D,
+                                 const int32_t* counts, const int32_t* seg_offsets,
+                                 int E, int64_t rows_cap_or_max_m, int N, int K,
+                                 int expected_m, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* moe_unpermute_combine: weighted combine back to token order ("gather").
+ * (rainlin, "GEMM 执行方式", sec. 4.4 and 4.6: z_t = sum_r p[t,r] *
+ *  y_packed[output_index[t,r]], reading only rows named by output_index;
+ *  CuTeDSL bei Perplexity: the combine accumulates in registers.)
+ *     Z[t, n] = bf16_rne( fma-chain over r = 0..k-1 of p[t,r] * Y[output_index[t,r], n] )
+ *   in fp32, slot order r = 0..k-1; slots with output_index < 0 or >= y_rows
+ *   contribute nothing.  Weights are used as given.
+ *     Y [y_rows, N] bf16, output_index [T, k] int32, topk_weights [T, k] fp32,
+ *     Z [T, N] bf16.  Requires N % 8 == 0, Y and Z 16-byte aligned. */
+moe_status moe_unpermute_combine(const uint16_t* Y, int64_t y_rows,
+                                 const int32_t* output_index,
+                                 const float* topk_weights,
+                                 int T, int k, int N,
+                                 uint16_t* Z, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,205 @@
+"""ctypes binding of libmoe.so: argument marshalling only.
+
+Every function has the name of the C entry point it calls (include/moe.h),
+takes torch tensors that already live on the GPU, passes their data pointers
+and the current HIP stream, and raises MoeError on a nonzero status.  No
+computation happens here; there is no fallback if the library is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+LAYOUT_CONTIGUOUS = 0
+LAYOUT_MASKED = 1
+DEV_ID_RANGE = 1
+DEV_CAPACITY = 2
+
+_c_i32, _c_i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_status_str": (ctypes.c_char_p, [_c_i32]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_packed_rows_cap": (_c_i64, [ctypes.c_int] * 4),
+    "moe_route_pack_workspace_bytes": (_c_i64, [ctypes.c_int] * 3),
+    "moe_quant_act": (_c_i32, [_vp, _c_i64, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_quant_weight_fp8": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_quant_weight_int4": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_route_pack": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_i64,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "moe_grouped_gemm_fp8": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
+    "moe_grouped_gemm_int4": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
+    "moe_unpermute_combine": (_c_i32, [_vp, _c_i64, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libmoe.so (once).  Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m int4_weights_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        msg = load().moe_last_error().decode(errors="replace")
+        raise MoeError(status, fn, msg)
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _row_bytes(t) -> int:
+    return math.prod(t.shape[1:]) * t.element_size()
+
+
+def moe_abi_version() -> int:
+    return load().moe_abi_version()
+
+
+def moe_packed_rows_cap(T: int, k: int, E: int, align: int) -> int:
+    return int(load().moe_packed_rows_cap(T, k, E, align))
+
+
+def moe_route_pack_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(load().moe_route_pack_workspace_bytes(T, k, E))
+
+
+def moe_quant_act(x, q, sf, stream=None):
+    """x bf16 [rows, K] -> q uint8 [rows, K] (E4M3 codes), sf float32 [rows, K/128]."""
+    _dev(x, "x", torch.bfloat16, 2), _dev(q, "q", torch.uint8, 2), _dev(sf, "sf", torch.float32, 2)
+    rows, K = x.shape
+    if tuple(q.shape) != (rows, K) or tuple(sf.shape) != (rows, K // 128):
+        raise ValueError("moe_quant_act: shape mismatch")
+    _check(load().moe_quant_act(_ptr(x), rows, K, _ptr(q), _ptr(sf), _stream(stream)), "moe_quant_act")
+
+
+def moe_quant_weight_fp8(w, q, sfw, stream=None):
+    """w bf16 [E, N, K] -> q uint8 [E, N, K], sfw float32 [E, N/128, K/128]."""
+    _dev(w, "w", torch.bfloat16, 3), _dev(q, "q", torch.uint8, 3), _dev(sfw, "sfw", torch.float32, 3)
+    E, N, K = w.shape
+    if tuple(q.shape) != (E, N, K) or tuple(sfw.shape) != (E, N // 128, K // 128):
+        raise ValueError("moe_quant_weight_fp8: shape mismatch")
+    _check(load().moe_quant_weight_fp8(_ptr(w), E, N, K, _ptr(q), _ptr(sfw), _stream(stream)),
+           "moe_quant_weight_fp8")
+
+
+def moe_quant_weight_int4(w, q4, s16, stream=None):
+    """w bf16 [E, N, K] -> q4 uint8 [E, N, K/2], s16 float16 [E, N, K/128]."""
+    _dev(w, "w", torch.bfloat16, 3), _dev(q4, "q4", torch.uint8, 3), _dev(s16, "s16", torch.float16, 3)
+    E, N, K = w.shape
+    if tuple(q4.shape) != (E, N, K // 2) or tuple(s16.shape) != (E, N, K // 128):
+        raise ValueError("moe_quant_weight_int4: shape mismatch")
+    _check(load().moe_quant_weight_int4(_ptr(w), E, N, K, _ptr(q4), _ptr(s16), _stream(stream)),
+           "moe_quant_weight_int4")
+
+
+def moe_route_pack(topk_ids, E: int, layout: int, align_or_max_m: int, payload, packed, counts, seg_offsets,
+                   m_indices, output_index, dev_status, payload2=None, packed2=None, workspace=None, stream=None):
+    """See include/moe.h.  payload [T, ...] and packed [rows_cap, ...] are any contiguous tensors;
+    their row byte counts are taken from the last dimensions."""
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    for n, t in (("payload", payload), ("packed", packed), ("payload2", payload2), ("packed2", packed2)):
+        _dev(t, n)
+    for n, t in (("counts", counts), ("seg_offsets", seg_offsets), ("m_indices", m_indices),
+                 ("output_index", output_index), ("dev_status", dev_status)):
+        _dev(t, n, torch.int32)
+    _dev(workspace, "workspace")
+    T, k = topk_ids.shape
+    rb = _row_bytes(payload)
+    rows_cap = packed.shape[0]
+    if _row_bytes(packed) != rb:
+        raise ValueError("moe_route_pack: payload and packed rows differ in size")
+    rb2 = 0
+    if payload2 is not None:
+        rb2 = _row_bytes(payload2)
+        if packed2 is None or packed2.shape[0] != rows_cap or _row_bytes(packed2) != rb2:
+            raise ValueError("moe_route_pack: payload2/packed2 mismatch")
+    if m_indices.numel() < rows_cap or counts.numel() < E or seg_offsets.numel() < E + 1 or \
+            output_index.numel() < T * k:
+        raise ValueError("moe_route_pack: output arrays too small")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().moe_route_pack(_ptr(topk_ids), T, k, E, layout, align_or_max_m,
+                                 _ptr(payload), rb, _ptr(payload2), rb2, _ptr(packed), _ptr(packed2), rows_cap,
+                                 _ptr(counts), _ptr(seg_offsets), _ptr(m_indices), _ptr(output_index),
+                                 _ptr(dev_status), _ptr(workspace), ws_bytes, _stream(stream)), "moe_route_pack")
+
+
+def moe_grouped_gemm_fp8(layout: int, A, SFA, W, SFW, D, counts, seg_offsets, E: int, rows_cap_or_max_m: int,
+                         N: int, K: int, expected_m: int = 0, stream=None):
+    _dev(A, "A", torch.uint8), _dev(SFA, "SFA", torch.float32), _dev(W, "W", torch.uint8)
+    _dev(SFW, "SFW", torch.float32), _dev(D, "D", torch.bfloat16), _dev(counts, "counts", torch.int32)
+    _dev(seg_offsets, "seg_offsets", torch.int32)
+    _check(load().moe_grouped_gemm_fp8(layout, _ptr(A), _ptr(SFA), _ptr(W), _ptr(SFW), _ptr(D), _ptr(counts),
+                                       _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
+           "moe_grouped_gemm_fp8")
+
+
+def moe_grouped_gemm_int4(layout: int, A, W4, S16, D, counts, seg_offsets, E: int, rows_cap_or_max_m: int,
+                          N: int, K: int, expected_m: int = 0, stream=None):
+    _dev(A, "A", torch.bfloat16), _dev(W4, "W4", torch.uint8), _dev(S16, "S16", torch.float16)
+    _dev(D, "D", torch.bfloat16), _dev(counts, "counts", torch.int32), _dev(seg_offsets, "seg_offsets", torch.int32)
+    _check(load().moe_grouped_gemm_int4(layout, _ptr(A), _ptr(W4), _ptr(S16), _ptr(D), _ptr(counts),
+                                        _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
+           "moe_grouped_gemm_int4")
+
+
+def moe_unpermute_combine(Y, output_index, topk_weights, Z, stream=None):
+    """Y bf16 [y_rows, N], output_index int32 [T, k], topk_weights float32 [T, k] -> Z bf16 [T, N]."""
+    _dev(Y, "Y", torch.bfloat16, 2), _dev(output_index, "output_index", torch.int32, 2)
+    _dev(topk_weights, "topk_weights", torch.float32, 2), _dev(Z, "Z", torch.bfloat16, 2)
+    T, k = output_index.shape
+    N = Z.shape[1]
+    if Y.shape[1] != N or Z.shape[0] != T or tuple(topk_weights.shape) != (T, k):
+        raise ValueError("moe_unpermute_combine: shape mismatch")
+    _check(load().moe_unpermute_combine(_ptr(Y), Y.shape[0], _ptr(output_index), _ptr(topk_weights), T, k, N,
+                                        _ptr(Z), _stream(stream)), "moe_unpermute_combine")

@@ -1,0 +1,272 @@
+// api.hip -- the extern "C" boundary of libmoe.so (declared in include/moe.h).
+// Every entry point validates its arguments on the host, returns a status
+// without launching anything on failure (with a reason in moe_last_error()),
+// and otherwise enqueues its kernels on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+
+#include "../../include/moe.h"
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local char g_err[512];
+
+static moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+static moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+DeviceInfo device_info() {
+  static std::mutex mu;
+  static int cached_cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64 && cached_cus[dev] > 0) return DeviceInfo{cached_cus[dev]};
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 64) cached_cus[dev] = cus;
+  return DeviceInfo{cus};
+}
+
+static bool aligned(const void* p, uintptr_t a) { return (((uintptr_t)p) & (a - 1)) == 0; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_abi_version(void) { return 1; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "bad shape";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_ALIGN: return "misaligned pointer or row";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int64_t moe_packed_rows_cap(int T, int k, int E, int align) {
+  if (T < 0 || k < 1 || E < 1 || align < 1) return -1;
+  const int64_t R = (int64_t)T * k;
+  const int64_t cap = R + (R < E ? R : E) * (int64_t)(align - 1);
+  return (cap + align - 1) / align * align;
+}
+
+int64_t moe_route_pack_workspace_bytes(int T, int k, int E) {
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return -1;
+  const int64_t R = (int64_t)T * k;
+  if (R > 0x7fffffff) return -1;
+  return route_workspace_bytes((int)R, E);
+}
+
+moe_status moe_quant_act(const uint16_t* x, int64_t rows, int K, uint8_t* q, float* sf, void* stream) {
+  g_err[0] = 0;
+  if (rows < 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_quant_act: rows=%lld K=%d", (long long)rows, K);
+  if (K % 128) return fail(MOE_ERR_UNSUPPORTED, "moe_quant_act: K=%d is not a multiple of 128", K);
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !sf) return fail(MOE_ERR_NULL, "moe_quant_act: null pointer");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4))
+    return fail(MOE_ERR_ALIGN, "moe_quant_act: x and q must be 16-byte aligned, sf 4-byte aligned");
+  return hip_status(launch_quant_act(x, rows, K, q, sf, (hipStream_t)stream), "moe_quant_act");
+}
+
+moe_status moe_quant_weight_fp8(const uint16_t* w, int E, int N, int K, uint8_t* q, float* sfw, void* stream) {
+  g_err[0] = 0;
+  if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_quant_weight_fp8: E=%d N=%d K=%d", E, N, K);
+  if (N % 128 || K % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_quant_weight_fp8: N=%d and K=%d must be multiples of 128", N, K);
+  if (E == 0) return MOE_OK;
+  if (!w || !q || !sfw) return fail(MOE_ERR_NULL, "moe_quant_weight_fp8: null pointer");
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(sfw, 4))
+    return fail(MOE_ERR_ALIGN, "moe_quant_weight_fp8: w and q must be 16-byte aligned");
+  return hip_status(launch_quant_weight_fp8(w, E, N, K, q, sfw, (hipStream_t)stream), "moe_quant_weight_fp8");
+}
+
+moe_status moe_quant_weight_int4(const uint16_t* w, int E, int N, int K, uint8_t* q4, uint16_t* s16, void* stream) {
+  g_err[0] = 0;
+  if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_quant_weight_int4: E=%d N=%d K=%d", E, N, K);
+  if (K % 128) return fail(MOE_ERR_UNSUPPORTED, "moe_quant_weight_int4: K=%d is not a multiple of 128", K);
+  if (E == 0) return MOE_OK;
+  if (!w || !q4 || !s16) return fail(MOE_ERR_NULL, "moe_quant_weight_int4: null pointer");
+  if (!aligned(w, 16) || !aligned(q4, 4) || !aligned(s16, 2))
+    return fail(MOE_ERR_ALIGN, "moe_quant_weight_int4: w must be 16-byte aligned, q4 4-byte aligned");
+  return hip_status(launch_quant_weight_int4(w, E, N, K, q4, s16, (hipStream_t)stream), "moe_quant_weight_int4");
+}
+
+moe_status moe_route_pack(const int32_t* topk_ids, int T, int k, int E, int layout, int align_or_max_m,
+                          const void* payload, int64_t payload_row_bytes, const void* payload2,
+                          int64_t payload2_row_bytes, void* packed, void* packed2, int64_t rows_cap, int32_t* counts,
+                          int32_t* seg_offsets, int32_t* m_indices, int32_t* output_index, int32_t* dev_status,
+                          void* workspace, int64_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_SHAPE, "moe_route_pack: T=%d k=%d E=%d (need T>=0, 1<=k<=%d, 1<=E<=%d)", T, k, E,
+                MOE_MAX_TOPK, MOE_MAX_EXPERTS);
+  if ((int64_t)T * k > 0x7fffffff) return fail(MOE_ERR_SHAPE, "moe_route_pack: T*k too large");
+  if (layout != MOE_LAYOUT_CONTIGUOUS && layout != MOE_LAYOUT_MASKED)
+    return fail(MOE_ERR_SHAPE, "moe_route_pack: unknown layout %d", layout);
+  if (align_or_max_m < 1) return fail(MOE_ERR_SHAPE, "moe_route_pack: align/max_m=%d must be >= 1", align_or_max_m);
+  if (payload_row_bytes <= 0 || payload_row_bytes % 4)
+    return fail(MOE_ERR_ALIGN, "moe_route_pack: payload_row_bytes=%lld must be a positive multiple of 4",
+                (long long)payload_row_bytes);
+  if (payload2 && (payload2_row_bytes <= 0 || payload2_row_bytes % 4))
+    return fail(MOE_ERR_ALIGN, "moe_route_pack: payload2_row_bytes=%lld must be a positive multiple of 4",
+                (long long)payload2_row_bytes);
+  const bool any_routes = T > 0;
+  if (any_routes && (!topk_ids || !payload || !output_index))
+    return fail(MOE_ERR_NULL, "moe_route_pack: topk_ids, payload and output_index are required when T > 0");
+  if (!counts || !seg_offsets || !dev_status) return fail(MOE_ERR_NULL, "moe_route_pack: null pointer");
+  if (rows_cap > 0 && (!packed || !m_indices))
+    return fail(MOE_ERR_NULL, "moe_route_pack: packed and m_indices are required when rows_cap > 0");
+  if (payload2 && !packed2) return fail(MOE_ERR_NULL, "moe_route_pack: packed2 is null but payload2 is not");
+  const int64_t need = (layout == MOE_LAYOUT_CONTIGUOUS) ? moe_packed_rows_cap(T, k, E, align_or_max_m)
+                                                          : (int64_t)E * align_or_max_m;
+  if (rows_cap < need || rows_cap > 0x7fffffff)
+    return fail(MOE_ERR_SHAPE, "moe_route_pack: rows_cap=%lld, need at least %lld (and < 2^31)",
+                (long long)rows_cap, (long long)need);
+  if (!aligned(payload, 16) || !aligned(packed, 16) || (payload2 && (!aligned(payload2, 4) || !aligned(packed2, 4))))
+    return fail(MOE_ERR_ALIGN, "moe_route_pack: payload/packed must be 16-byte aligned, payload2/packed2 4-byte");
+  if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(seg_offsets, 4) || !aligned(m_indices, 4) ||
+      !aligned(output_index, 4) || !aligned(dev_status, 4))
+    return fail(MOE_ERR_ALIGN, "moe_route_pack: int32 arrays must be 4-byte aligned");
+  const int R = T * k;
+  const int64_t ws_need = route_workspace_bytes(R, E);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need || !aligned(workspace, 4)))
+    return fail(MOE_ERR_WORKSPACE, "moe_route_pack: needs %lld workspace bytes, got %lld", (long long)ws_need,
+                (long long)workspace_bytes);
+  RouteArgs a;
+  a.ids = topk_ids;
+  a.T = T;
+  a.k = k;
+  a.E = E;
+  a.R = R;
+  a.masked = layout == MOE_LAYOUT_MASKED;
+  a.align = a.masked ? 1 : align_or_max_m;
+  a.max_m = a.masked ? align_or_max_m : 0;
+  a.payload = (const uint8_t*)payload;
+  a.row_bytes = payload_row_bytes;
+  a.payload2 = (const uint8_t*)payload2;
+  a.row_bytes2 = payload2 ? payload2_row_bytes : 0;
+  a.packed = (uint8_t*)packed;
+  a.packed2 = (uint8_t*)packed2;
+  a.rows_cap = rows_cap;
+  a.counts = counts;
+  a.seg_offsets = seg_offsets;
+  a.m_indices = m_indices;
+  a.output_index = output_index;
+  a.dev_status = dev_status;
+  a.ws = (int32_t*)workspace;
+  a.nchunks = 0;
+  return hip_status(launch_route_pack(a, (hipStream_t)stream), "moe_route_pack");
+}
+
+static moe_status check_gemm(const char* fn, int layout, const void* A, const void* W, const void* SW, void* D,
+                             const int32_t* counts, const int32_t* seg_offsets, int E, int64_t rows_cap_or_max_m,
+                             int N, int K) {
+  if (layout != MOE_LAYOUT_CONTIGUOUS && layout != MOE_LAYOUT_MASKED)
+    return fail(MOE_ERR_SHAPE, "%s: unknown layout %d", fn, layout);
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_SHAPE, "%s: E=%d must be in [1, %d]", fn, E, MOE_MAX_EXPERTS);
+  if (N <= 0 || K <= 0 || rows_cap_or_max_m < 1)
+    return fail(MOE_ERR_SHAPE, "%s: N=%d K=%d rows/max_m=%lld", fn, N, K, (long long)rows_cap_or_max_m);
+  if (N % 128 || K % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: N=%d and K=%d must be multiples of 128", fn, N, K);
+  if (K / 128 > kMaxKBlocks) return fail(MOE_ERR_UNSUPPORTED, "%s: K=%d exceeds %d", fn, K, kMaxKBlocks * 128);
+  const int64_t rows = layout == MOE_LAYOUT_MASKED ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
+  if (rows > 0x7fffffff) return fail(MOE_ERR_SHAPE, "%s: too many rows", fn);
+  if ((int64_t)N * K > 0xffffffffll) return fail(MOE_ERR_UNSUPPORTED, "%s: one expert's weights exceed 4 GiB", fn);
+  if (!A || !W || !SW || !D || !counts) return fail(MOE_ERR_NULL, "%s: null pointer", fn);
+  if (layout == MOE_LAYOUT_CONTIGUOUS && !seg_offsets)
+    return fail(MOE_ERR_NULL, "%s: seg_offsets is required for the contiguous layout", fn);
+  if (!aligned(A, 16) || !aligned(W, 16) || !aligned(D, 16))
+    return fail(MOE_ERR_ALIGN, "%s: A, W and D must be 16-byte aligned", fn);
+  return MOE_OK;
+}
+
+moe_status moe_grouped_gemm_fp8(int layout, const uint8_t* A, const float* SFA, const uint8_t* W, const float* SFW,
+                                uint16_t* D, const int32_t* counts, const int32_t* seg_offsets, int E,
+                                int64_t rows_cap_or_max_m, int N, int K, int expected_m, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_gemm("moe_grouped_gemm_fp8", layout, A, W, SFW, D, counts, seg_offsets, E, rows_cap_or_max_m,
+                             N, K);
+  if (st) return st;
+  if (!SFA) return fail(MOE_ERR_NULL, "moe_grouped_gemm_fp8: SFA is null");
+  if (!aligned(SFA, 4) || !aligned(SFW, 4)) return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_fp8: scales misaligned");
+  GemmArgs a;
+  a.A = A;
+  a.SFA = SFA;
+  a.W = W;
+  a.SW = SFW;
+  a.D = D;
+  a.counts = counts;
+  a.seg_offsets = seg_offsets;
+  a.E = E;
+  a.masked = layout == MOE_LAYOUT_MASKED;
+  a.max_m = a.masked ? (int)rows_cap_or_max_m : 0;
+  a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
+  a.N = N;
+  a.K = K;
+  return hip_status(launch_gemm_fp8(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_fp8");
+}
+
+moe_status moe_grouped_gemm_int4(int layout, const uint16_t* A, const uint8_t* W4, const uint16_t* S16, uint16_t* D,
+                                 const int32_t* counts, const int32_t* seg_offsets, int E, int64_t rows_cap_or_max_m,
+                                 int N, int K, int expected_m, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_gemm("moe_grouped_gemm_int4", layout, A, W4, S16, D, counts, seg_offsets, E,
+                             rows_cap_or_max_m, N, K);
+  if (st) return st;
+  if (!aligned(S16, 2)) return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_int4: scales misaligned");
+  GemmArgs a;
+  a.A = (const uint8_t*)A;
+  a.SFA = nullptr;
+  a.W = W4;
+  a.SW = S16;
+  a.D = D;
+  a.counts = counts;
+  a.seg_offsets = seg_offsets;
+  a.E = E;
+  a.masked = layout == MOE_LAYOUT_MASKED;
+  a.max_m = a.masked ? (int)rows_cap_or_max_m : 0;
+  a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
+  a.N = N;
+  a.K = K;
+  return hip_status(launch_gemm_int4(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_int4");
+}
+
+moe_status moe_unpermute_combine(const uint16_t* Y, int64_t y_rows, const int32_t* output_index,
+                                 const float* topk_weights, int T, int k, int N, uint16_t* Z, void* stream) {
+  g_err[0] = 0;
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || N <= 0 || y_rows < 0)
+    return fail(MOE_ERR_SHAPE, "moe_unpermute_combine: T=%d k=%d N=%d y_rows=%lld", T, k, N, (long long)y_rows);
+  if (N % 8) return fail(MOE_ERR_UNSUPPORTED, "moe_unpermute_combine: N=%d must be a multiple of 8", N);
+  if (T == 0) return MOE_OK;
+  if (!output_index || !topk_weights || !Z || (!Y && y_rows > 0))
+    return fail(MOE_ERR_NULL, "moe_unpermute_combine: null pointer");
+  if (!aligned(Z, 16) || (Y && !aligned(Y, 16)) || !aligned(output_index, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_ERR_ALIGN, "moe_unpermute_combine: Y and Z must be 16-byte aligned");
+  return hip_status(launch_combine(Y, y_rows, output_index, topk_weights, T, k, N, Z, (hipStream_t)stream),
+                    "moe_unpermute_combine");
+}
+
+}  // extern "C"

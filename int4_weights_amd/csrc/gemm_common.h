@@ -1,0 +1,92 @@
+// gemm_common.h -- the per-expert tile scheduler shared by the grouped GEMMs.
+//
+// A unit is (expert e, N-tile of 256 columns, M-chunk of at most BM rows).
+// Every workgroup builds the same unit table in LDS from counts (and
+// seg_offsets for the contiguous layout) and walks a fixed share of it, so
+// there are no atomics and no second launch (AsymGEMM README, "asymScheduler":
+// each workgroup owns fixed (N-tile, expert) pairs and reads its rows from the
+// offsets table; "K-outer, M-inner Loop": a weight tile is reused by every
+// token row of its expert).  Within an expert the units run N-tile-major with
+// the M-chunks of one N-tile adjacent, so concurrent workgroups that share a
+// weight panel or an activation chunk find it in the same L2.
+//
+// XCD awareness: workgroup w runs on XCD w % 8 (round-robin dispatch), so the
+// unit list is cut into 8 contiguous slices and the G/8 workgroups of an XCD
+// walk their slice in order.
+#pragma once
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kBN = 256;       // columns per unit (4 waves x 64)
+constexpr int kXcds = 8;
+
+struct Sched {
+  int* rows;    // [E] valid rows per expert
+  int* start;   // [E] first packed row
+  int* up;      // [E+1] unit prefix
+};
+
+// Build the unit table (all threads of the workgroup; ends with a barrier).
+template <int BM>
+__device__ inline void sched_build(const GemmArgs& a, Sched s, int* s_tmp) {
+  const int nt = (a.N + kBN - 1) / kBN;
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
+    int r = a.counts[e];
+    int64_t st;
+    int64_t cap;
+    if (a.masked) {
+      st = (int64_t)e * a.max_m;
+      cap = a.max_m;
+    } else {
+      st = a.seg_offsets[e];
+      cap = (st >= 0 && st < a.rows_cap) ? a.rows_cap - st : 0;
+    }
+    if (r < 0) r = 0;
+    if (r > cap) r = (int)cap;
+    s.rows[e] = r;
+    s.start[e] = (int)st;
+    s.up[e] = ((r + BM - 1) / BM) * nt;
+  }
+  __syncthreads();
+  block_exclusive_scan(s.up, a.E, s_tmp);
+}
+
+struct Unit {
+  int e, row0, mrows, n0;
+};
+
+template <int BM>
+__device__ inline Unit sched_unit(const GemmArgs& a, Sched s, int v) {
+  const int e = upper_bound_minus1(s.up, a.E, v);
+  const int local = v - s.up[e];
+  const int chunks = (s.rows[e] + BM - 1) / BM;
+  const int nt = local / chunks, ch = local - nt * chunks;
+  Unit u;
+  u.e = uniform(e);
+  u.row0 = uniform(s.start[e] + ch * BM);
+  u.mrows = uniform(min(BM, s.rows[e] - ch * BM));
+  u.n0 = uniform(nt * kBN);
+  return u;
+}
+
+// This workgroup's slice of the unit list: units lo + slot + i*stride < hi.
+struct Walk {
+  int first, end, stride;
+};
+__device__ inline Walk sched_walk(int total_units_any) {
+  const int total_units = uniform(total_units_any);
+  const int g = gridDim.x;  // a multiple of 8
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per = g / kXcds;
+  const int lo = (int)((int64_t)total_units * xcd / kXcds);
+  const int hi = (int)((int64_t)total_units * (xcd + 1) / kXcds);
+  Walk w;
+  w.first = lo + slot;
+  w.end = hi;
+  w.stride = per;
+  return w;
+}
+
+}  // namespace moe

@@ -1,0 +1,212 @@
+// gemm_int4.hip -- 4-bit weight-only grouped GEMM for gfx950.
+//
+// D[p, n] = bf16( sum_g s[e,n,g] * sum_{k in g} a[p,k] * (q[e,n,k] - 8) )
+// (ONNX Runtime "MatMulNBits -- CUDA Operator Documentation", sec. 2 "Weight
+// Format": row n is K/2 bytes, two 4-bit weights per byte, one scale per
+// 128-element group along K, symmetric zero point 8; sec. 4.1 describes a
+// warp-per-column GEMV for one token -- prior art for NVIDIA, not used here.)
+//
+// Design for CDNA4 (decode-sized segments: a handful of rows per expert):
+//  * Same persistent per-expert unit scheduler as the FP8 GEMM; a unit is
+//    (expert, 256 columns, up to 16*RB rows).  Each wave owns 64 columns.
+//  * The 4-bit weights stream from HBM into VGPRs through an S-deep ring: one
+//    16-byte load per lane covers 32 k of one column.
+//  * Dequantisation costs one AND-OR per two weights: OR-ing the nibble into
+//    the mantissa of bf16 128.0 (0x4300) gives 128 + q exactly.  The bf16
+//    matrix instruction v_mfma_f32_16x16x32_bf16 multiplies it with the
+//    activations, and one extra instruction per group against the constant
+//    -136 adds -136 * sum(a), so the group partial is exactly
+//    sum a * (128 + q) - 136 * sum a = sum a * (q - 8) up to fp32 rounding.
+//    The correction is shared by all column blocks of the wave.
+//  * The nibble pairs land as (k, k+4) within each 8-k run; the activation
+//    fragment is permuted the same way (dot products are invariant under a
+//    common permutation of k).
+//  * Per-group fp16 scales are applied to the fp32 group partial by one FMA;
+//    the accumulator layout gives each lane one column, hence one scale.
+//  * Activations are staged in LDS (two slots, XOR-swizzled) from VGPR-ring
+//    loads, as in the FP8 kernel.
+#include "gemm_common.h"
+
+namespace moe {
+
+template <int RB, int S>
+struct I4Cfg {
+  static constexpr int BM = 16 * RB;
+  static constexpr int kApw = RB;            // 16-byte A loads per lane per stage (4 rows of 256 B)
+  static constexpr int kAStage = BM * 256;   // bytes per LDS slot
+};
+
+template <int RB, int S>
+struct I4Smem {
+  uint8_t a[2][I4Cfg<RB, S>::kAStage];
+};
+
+__device__ __forceinline__ v8bf as_bf(const v4i& x) { return __builtin_bit_cast(v8bf, x); }
+
+template <int RB, int S>
+__device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Smem<RB, S>& sm, int wv, int lane) {
+  using C = I4Cfg<RB, S>;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int K = a.K, N = a.N, KG = K / 128;
+  const int ncol0 = u.n0 + 64 * wv;
+  const bool wave_on = ncol0 < N;
+
+  const uint8_t* wbase = a.W + (int64_t)u.e * N * (K / 2);
+  const uint16_t* sbase = (const uint16_t*)a.SW + (int64_t)u.e * N * KG;
+  uint32_t woff[4], soff[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    int n = ncol0 + 16 * cb + l16;
+    if (n >= N) n = N - 1;
+    woff[cb] = (uint32_t)n * (uint32_t)(K / 2) + 16u * lg;
+    soff[cb] = (uint32_t)n * (uint32_t)KG;
+  }
+  const uint8_t* abase = a.A + (int64_t)u.row0 * K * 2;
+  uint32_t aoff[C::kApw];
+#pragma unroll
+  for (int i = 0; i < C::kApw; ++i) {
+    const int q = wv * C::kApw + i;            // 1 KB block of the stage (4 rows)
+    const int r = 4 * q + (lane >> 4);         // tile row written by this lane
+    const int c = (lane & 15) ^ (r & 15);      // 16-byte chunk that lands at position lane & 15
+    aoff[i] = (uint32_t)min(r, u.mrows - 1) * (uint32_t)(K * 2) + 16u * c;
+  }
+
+  v4i wq[S][4];
+  uint32_t sc[S][4];
+  v4i ar[S][C::kApw];
+  v4f acc[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto issue = [&](int ks_req, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    const int ks = min(ks_req, KG - 1);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) wq[slot][cb] = *(const v4i*)(wbase + (woff[cb] + (uint32_t)ks * 64u));
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) sc[slot][cb] = sbase[soff[cb] + ks];
+#pragma unroll
+    for (int i = 0; i < C::kApw; ++i) ar[slot][i] = *(const v4i*)(abase + (aoff[i] + (uint32_t)ks * 256u));
+  };
+
+  auto commit = [&](int ks, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    uint8_t* dst = &sm.a[ks & 1][0];
+#pragma unroll
+    for (int i = 0; i < C::kApw; ++i) *(v4i*)(dst + (wv * C::kApw + i) * 1024 + 16 * lane) = ar[slot][i];
+  };
+
+  // activation fragment reads: row m = 16*rb + l16 at m*256, chunk c at c ^ l16
+  int aoff_rd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) aoff_rd[i] = l16 * 256 + 16 * ((4 * lg + i) ^ l16);
+  const v4i kNeg136 = v4i{(int)0xC308C308u, (int)0xC308C308u, (int)0xC308C308u, (int)0xC308C308u};
+
+  auto compute = [&](int ks, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    // dequantised weights: 128 + q as bf16, pairs (k, k+4) of each 8-k run
+    v4i wd[4][4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = (uint32_t)wq[slot][cb][d];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wd[cb][d][i] = (int)(((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u);
+      }
+    float sf[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) sf[cb] = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[slot][cb]);
+    const uint8_t* ab = &sm.a[ks & 1][0];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      v4i x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = *(const v4i*)(ab + aoff_rd[i] + rb * 4096);
+      v4i af[4];  // per MFMA d: (a0,a4) (a1,a5) (a2,a6) (a3,a7) of the 8-k run
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t i0 = (uint32_t)x[d][0], i1 = (uint32_t)x[d][1], i2 = (uint32_t)x[d][2], i3 = (uint32_t)x[d][3];
+        af[d] = v4i{(int)((i0 & 0xffffu) | (i2 << 16)), (int)((i0 >> 16) | (i2 & 0xffff0000u)),
+                    (int)((i1 & 0xffffu) | (i3 << 16)), (int)((i1 >> 16) | (i3 & 0xffff0000u))};
+      }
+      v4f corr = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af[d]), as_bf(kNeg136), corr, 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        v4f p = corr;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af[d]), as_bf(wd[cb][d]), p, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[rb][cb][v] = __builtin_fmaf(sf[cb], p[v], acc[rb][cb][v]);
+      }
+    }
+  };
+
+  auto step = [&](int ks, auto s_c) {
+    constexpr int s = decltype(s_c)::value;
+    commit(ks, s_c);
+    barrier_lds();
+    issue(ks + S - 1, IntC<(s + S - 1) % S>{});
+    compute(ks, s_c);
+  };
+
+  static_for<0, S - 1>([&](auto s_c) { issue(decltype(s_c)::value, s_c); });
+  const int nfull = KG / S;
+  for (int g = 0; g < nfull; ++g) static_for<0, S>([&](auto s_c) { step(g * S + decltype(s_c)::value, s_c); });
+  static_for<0, S>([&](auto s_c) {
+    const int ks = nfull * S + decltype(s_c)::value;
+    if (ks < KG) step(ks, s_c);
+  });
+  barrier_lds();
+
+  if (wave_on) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 16 * rb + 4 * lg + v;
+        if (m < u.mrows) {
+          uint16_t* drow = a.D + (int64_t)(u.row0 + m) * N + ncol0 + l16;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) drow[16 * cb] = (uint16_t)f32_to_bf16_rne(acc[rb][cb][v]);
+        }
+      }
+  }
+}
+
+template <int RB, int S>
+__global__ __launch_bounds__(256, 1) void gemm_int4_kernel(const GemmArgs a) {
+  using C = I4Cfg<RB, S>;
+  __shared__ __attribute__((aligned(1024))) I4Smem<RB, S> sm;
+  __shared__ int s_rows[kMaxExperts], s_start[kMaxExperts], s_up[kMaxExperts + 1], s_tmp[257];
+  const Sched sc{s_rows, s_start, s_up};
+  sched_build<C::BM>(a, sc, s_tmp);
+  const Walk walk = sched_walk(s_up[a.E]);
+  const int lane = lane_id();
+  const int wv = uniform(threadIdx.x >> 6);
+  for (int v = walk.first; v < walk.end; v += walk.stride) {
+    const Unit u = sched_unit<C::BM>(a, sc, v);
+    int4_unit<RB, S>(a, u, sm, wv, lane);
+  }
+}
+
+template <int RB, int S>
+static hipError_t launch_i4(const GemmArgs& a, hipStream_t s) {
+  const int cus = device_info().cus;
+  int grid = cus - cus % kXcds;
+  if (grid < kXcds) grid = kXcds;
+  gemm_int4_kernel<RB, S><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s) {
+  const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 64);
+  if (em <= 16) return launch_i4<1, 8>(a, s);
+  return launch_i4<4, 4>(a, s);
+}
+
+}  // namespace moe

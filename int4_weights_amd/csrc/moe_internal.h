@@ -1,0 +1,66 @@
+// moe_internal.h -- launchers behind the C ABI (host side, C++ linkage).
+// Arguments are validated by the C-ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct DeviceInfo {
+  int cus;  // compute units of the current device
+};
+DeviceInfo device_info();
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int K, uint8_t* q, float* sf, hipStream_t s);
+hipError_t launch_quant_weight_fp8(const uint16_t* w, int E, int N, int K, uint8_t* q, float* sfw, hipStream_t s);
+hipError_t launch_quant_weight_int4(const uint16_t* w, int E, int N, int K, uint8_t* q4, uint16_t* s16,
+                                    hipStream_t s);
+
+struct RouteArgs {
+  const int32_t* ids;
+  int T, k, E, R;
+  int masked;       // 0 = contiguous, 1 = masked
+  int align;        // contiguous alignment
+  int max_m;        // masked capacity per expert
+  const uint8_t* payload;
+  int64_t row_bytes;
+  const uint8_t* payload2;
+  int64_t row_bytes2;
+  uint8_t* packed;
+  uint8_t* packed2;
+  int64_t rows_cap;
+  int32_t* counts;
+  int32_t* seg_offsets;
+  int32_t* m_indices;
+  int32_t* output_index;
+  int32_t* dev_status;
+  int32_t* ws;      // workspace (large path): chunk counts [nchunks*E] then status [nchunks]
+  int nchunks;
+};
+constexpr int kRouteSmallMax = 4096;   // routes handled by the single-launch path
+constexpr int kRouteChunk = 1024;      // routes per counting workgroup (large path)
+int64_t route_workspace_bytes(int R, int E);
+hipError_t launch_route_pack(const RouteArgs& a, hipStream_t s);
+
+struct GemmArgs {
+  const uint8_t* A;      // fp8 codes [rows, K] or bf16 [rows, K] (int4 path)
+  const float* SFA;      // [rows, K/128] (fp8 path)
+  const uint8_t* W;      // fp8 [E, N, K] or int4 [E, N, K/2]
+  const void* SW;        // SFW fp32 [E, N/128, K/128] or S16 fp16 [E, N, K/128]
+  uint16_t* D;           // bf16 [rows, N]
+  const int32_t* counts;
+  const int32_t* seg_offsets;
+  int E;
+  int masked;
+  int64_t rows_cap;      // rows of A/D (contiguous) ; masked: E*max_m
+  int max_m;
+  int N, K;
+};
+hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s);
+hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* oi, const float* w, int T, int k,
+                          int N, uint16_t* Z, hipStream_t s);
+
+}  // namespace moe

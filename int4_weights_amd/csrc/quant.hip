@@ -1,0 +1,189 @@
+// quant.hip -- FP8 1x128 / 128x128 power-of-two quantisation and the group-128
+// 4-bit weight format.
+//
+// FP8 rule (nxmr.cn DeepGEMM FP8 article, "补偿机制一"): each block's scale is an
+// exact power of two, amax/448 rounded up, so scaling is an exponent shift and
+// no scaled value exceeds the E4M3 range of 448.  Codes are round-to-nearest-
+// even E4M3FN of x * 2^-e.
+//
+// INT4 format (ONNX Runtime "MatMulNBits -- CUDA Operator Documentation",
+// sec. 2): per output row n, K/2 bytes with two 4-bit weights per byte (low
+// nibble = even k), one fp16 scale per 128 along K, value (q - 8) * scale.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// One 16-lane group per 128-element block: lane holds 8 consecutive bf16.
+// A wave covers 4 blocks per step.  HBM-bound: 16-byte loads, 8-byte stores.
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int64_t nblocks, int kb,
+                                                         uint8_t* __restrict__ q, float* __restrict__ sf) {
+  const int lane = lane_id();
+  const int sub = lane & 15;
+  const int64_t gwave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t b0 = gwave * 4; b0 < nblocks; b0 += nwaves * 4) {
+    const int64_t blk = b0 + (lane >> 4);
+    const bool ok = blk < nblocks;
+    v4i raw = {0, 0, 0, 0};
+    if (ok) raw = *(const v4i*)(x + blk * 128 + sub * 8);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w = (uint32_t)raw[i];
+      f[2 * i] = bf16_to_f32(w & 0xffffu);
+      f[2 * i + 1] = bf16_to_f32(w >> 16);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    const int e = pow2_exponent(amax);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(__builtin_amdgcn_ldexpf(f[i], -e)) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(__builtin_amdgcn_ldexpf(f[4 + i], -e)) << (8 * i);
+    if (ok) {
+      uint2 out;
+      out.x = lo;
+      out.y = hi;
+      *(uint2*)(q + blk * 128 + sub * 8) = out;
+      if (sub == 0) sf[blk] = pow2f(e);
+    }
+  }
+}
+
+// One workgroup (256 threads) per 128x128 weight block; each thread holds 64
+// elements (8 rows x 8 consecutive k).
+__global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const uint16_t* __restrict__ w, int N, int K,
+                                                                uint8_t* __restrict__ q, float* __restrict__ sfw) {
+  __shared__ float s_red[4];
+  const int nb = N / 128, kb = K / 128;
+  const int64_t blk = blockIdx.x;  // (e, nb, kb) flattened
+  const int kbi = (int)(blk % kb);
+  const int nbi = (int)((blk / kb) % nb);
+  const int64_t e = blk / ((int64_t)kb * nb);
+  const int tid = threadIdx.x;
+  const int col = (tid & 15) * 8;        // k offset within the block
+  const int row0 = tid >> 4;             // 0..15; rows row0 + 16*j
+  const int64_t base = (e * N + (int64_t)nbi * 128) * K + (int64_t)kbi * 128 + col;
+  float f[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v4i raw = *(const v4i*)(w + base + (int64_t)(row0 + 16 * j) * K);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t u = (uint32_t)raw[i];
+      f[j][2 * i] = bf16_to_f32(u & 0xffffu);
+      f[j][2 * i + 1] = bf16_to_f32(u >> 16);
+      amax = fmaxf(amax, fmaxf(fabsf(f[j][2 * i]), fabsf(f[j][2 * i + 1])));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if (lane_id() == 0) s_red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const int ex = pow2_exponent(amax);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(__builtin_amdgcn_ldexpf(f[j][i], -ex)) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(__builtin_amdgcn_ldexpf(f[j][4 + i], -ex)) << (8 * i);
+    uint2 out;
+    out.x = lo;
+    out.y = hi;
+    *(uint2*)(q + base + (int64_t)(row0 + 16 * j) * K) = out;
+  }
+  if (tid == 0) sfw[blk] = pow2f(ex);
+}
+
+// One 16-lane group per (row n, 128-group): lane holds 8 consecutive weights.
+__global__ __launch_bounds__(256) void quant_weight_int4_kernel(const uint16_t* __restrict__ w, int64_t ngroups,
+                                                                 uint8_t* __restrict__ q4,
+                                                                 uint16_t* __restrict__ s16) {
+  const int lane = lane_id();
+  const int sub = lane & 15;
+  const int64_t gwave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t g0 = gwave * 4; g0 < ngroups; g0 += nwaves * 4) {
+    const int64_t g = g0 + (lane >> 4);
+    const bool ok = g < ngroups;
+    v4i raw = {0, 0, 0, 0};
+    if (ok) raw = *(const v4i*)(w + g * 128 + sub * 8);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t u = (uint32_t)raw[i];
+      f[2 * i] = bf16_to_f32(u & 0xffffu);
+      f[2 * i + 1] = bf16_to_f32(u >> 16);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    // s = fp16(amax / 7) with the division in fp32 (correctly rounded) and the
+    // conversion to fp16 round-to-nearest-even; guards for 0, underflow, overflow.
+    _Float16 h;
+    if (amax == 0.0f) {
+      h = (_Float16)1.0f;
+    } else {
+      float s32 = amax / 7.0f;
+      h = (_Float16)s32;
+      if ((float)h == 0.0f) h = (_Float16)5.9604644775390625e-08f;  // 2^-24
+      if (!((float)h <= 65504.0f)) h = (_Float16)65504.0f;
+    }
+    const float s = (float)h;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float qf = __builtin_rintf(f[i] / s) + 8.0f;
+      qf = fminf(fmaxf(qf, 0.0f), 15.0f);
+      packed |= ((uint32_t)qf) << (4 * i);
+    }
+    if (ok) {
+      *(uint32_t*)(q4 + g * 64 + sub * 4) = packed;
+      if (sub == 0) s16[g] = __builtin_bit_cast(uint16_t, h);
+    }
+  }
+}
+
+static int grid_for(int64_t work_items, int per_block, int cap) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int K, uint8_t* q, float* sf, hipStream_t s) {
+  const int64_t nblocks = rows * (K / 128);
+  if (nblocks == 0) return hipSuccess;
+  const int grid = grid_for(nblocks, 16, device_info().cus * 16);  // 16 blocks per 256-thread WG per step
+  quant_act_kernel<<<grid, 256, 0, s>>>(x, nblocks, K / 128, q, sf);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_fp8(const uint16_t* w, int E, int N, int K, uint8_t* q, float* sfw, hipStream_t s) {
+  const int64_t nblocks = (int64_t)E * (N / 128) * (K / 128);
+  if (nblocks == 0) return hipSuccess;
+  if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
+  quant_weight_fp8_kernel<<<(unsigned)nblocks, 256, 0, s>>>(w, N, K, q, sfw);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_int4(const uint16_t* w, int E, int N, int K, uint8_t* q4, uint16_t* s16,
+                                    hipStream_t s) {
+  const int64_t ngroups = (int64_t)E * N * (K / 128);
+  if (ngroups == 0) return hipSuccess;
+  const int grid = grid_for(ngroups, 16, device_info().cus * 16);
+  quant_weight_int4_kernel<<<grid, 256, 0, s>>>(w, ngroups, q4, s16);
+  return hipGetLastError();
+}
+
+}  // namespace moe

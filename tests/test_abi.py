@@ -1,0 +1,128 @@
+"""The C ABI: libmoe.so loads, exports every entry point include/moe.h declares,
+and rejects bad arguments on the host before launching anything (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_weights_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN, MOE_ERR_HIP, MOE_ERR_WORKSPACE = range(7)
+
+
+def _declared():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return moe.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert set(names) == set(moe.SIGNATURES)
+
+
+def test_constants_and_helpers(lib):
+    assert moe.moe_abi_version() == 1
+    assert lib.moe_status_str(MOE_ERR_WORKSPACE) == b"workspace missing or too small"
+    # worked example: 10 routes, 4 experts, 128-aligned -> at most 640 rows
+    assert moe.moe_packed_rows_cap(5, 2, 4, 128) == 640
+    assert moe.moe_packed_rows_cap(4096, 8, 256, 128) == 65280
+    assert moe.moe_packed_rows_cap(0, 8, 256, 128) == 0
+    assert moe.moe_packed_rows_cap(1, 0, 4, 128) == -1
+    assert moe.moe_route_pack_workspace_bytes(128, 8, 256) == 0
+    assert moe.moe_route_pack_workspace_bytes(4096, 8, 256) == 4 * (32 * 256 + 32)
+    assert moe.moe_route_pack_workspace_bytes(1, 1, 2000) == -1
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+A16 = 1 << 20  # a fake, 16-byte aligned address: never dereferenced on these error paths
+
+
+def test_host_validation_rejects_without_launching(lib):
+    # moe_quant_act
+    assert lib.moe_quant_act(_p(A16), 4, 100, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_quant_act(None, 4, 128, _p(A16), _p(A16), None) == MOE_ERR_NULL
+    assert lib.moe_quant_act(_p(A16 + 2), 4, 128, _p(A16), _p(A16), None) == MOE_ERR_ALIGN
+    assert lib.moe_quant_act(_p(A16), -1, 128, _p(A16), _p(A16), None) == MOE_ERR_SHAPE
+    assert lib.moe_quant_act(None, 0, 128, None, None, None) == MOE_OK  # empty input is a no-op
+    assert b"multiple of 128" in (lib.moe_quant_act(_p(A16), 4, 100, _p(A16), _p(A16), None) and
+                                  lib.moe_last_error())
+    # moe_quant_weight_*
+    assert lib.moe_quant_weight_fp8(_p(A16), 2, 100, 128, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_quant_weight_int4(_p(A16), 2, 128, 64, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
+
+    # moe_route_pack
+    def rp(T=5, k=2, E=4, layout=0, am=128, rb=16, rows_cap=640, ws=None, wsb=0, payload=A16, ids=A16):
+        return lib.moe_route_pack(_p(ids) if ids else None, T, k, E, layout, am, _p(payload) if payload else None,
+                                  rb, None, 0, _p(A16), None, rows_cap, _p(A16), _p(A16), _p(A16), _p(A16),
+                                  _p(A16), _p(ws) if ws else None, wsb, None)
+
+    assert rp(E=0) == MOE_ERR_SHAPE
+    assert rp(E=1025) == MOE_ERR_SHAPE
+    assert rp(k=0) == MOE_ERR_SHAPE
+    assert rp(layout=7) == MOE_ERR_SHAPE
+    assert rp(am=0) == MOE_ERR_SHAPE
+    assert rp(rb=6) == MOE_ERR_ALIGN
+    assert rp(payload=0) == MOE_ERR_NULL
+    assert rp(rows_cap=639) == MOE_ERR_SHAPE          # below the packed-rows bound
+    assert rp(layout=1, am=3, rows_cap=11) == MOE_ERR_SHAPE  # masked needs E*max_m rows
+    assert rp(payload=A16 + 4) == MOE_ERR_ALIGN
+    assert rp(T=4096, k=8, E=256, rows_cap=65280) == MOE_ERR_WORKSPACE  # large path needs scratch
+    assert rp(T=4096, k=8, E=256, rows_cap=65280, ws=A16, wsb=100) == MOE_ERR_WORKSPACE
+
+    # moe_grouped_gemm_fp8 / int4
+    def g8(layout=0, N=256, K=256, E=4, rows=512, seg=A16, A=A16):
+        return lib.moe_grouped_gemm_fp8(layout, _p(A) if A else None, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16),
+                                        _p(seg) if seg else None, E, rows, N, K, 0, None)
+
+    assert g8(N=200) == MOE_ERR_UNSUPPORTED
+    assert g8(K=100) == MOE_ERR_UNSUPPORTED
+    assert g8(E=0) == MOE_ERR_SHAPE
+    assert g8(seg=0) == MOE_ERR_NULL                 # contiguous needs seg_offsets
+    assert g8(A=0) == MOE_ERR_NULL
+    assert g8(A=A16 + 8) == MOE_ERR_ALIGN
+    assert g8(K=128 * 300) == MOE_ERR_UNSUPPORTED    # K above the supported maximum
+    assert lib.moe_grouped_gemm_int4(0, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), 4, 64, 100, 256, 0,
+                                     None) == MOE_ERR_UNSUPPORTED
+    # moe_unpermute_combine
+    assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 2, 12, _p(A16), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 0, 16, _p(A16), None) == MOE_ERR_SHAPE
+    assert lib.moe_unpermute_combine(_p(A16), 10, None, _p(A16), 4, 2, 16, _p(A16), None) == MOE_ERR_NULL
+    assert lib.moe_unpermute_combine(None, 0, None, None, 0, 2, 16, None, None) == MOE_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.moe_quant_act(x, torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4, 1))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    from int4_weights_amd import _lib
+    with pytest.raises(ImportError):
+        _lib.load.__wrapped__ if hasattr(_lib.load, "__wrapped__") else None
+        saved = _lib._lib
+        _lib._lib = None
+        try:
+            _lib.load(str(tmp_path / "nope.so"))
+        finally:
+            _lib._lib = saved

@@ -1,0 +1,85 @@
+"""GPU weighted combine vs the oracle.
+
+Tolerance derived from the arithmetic: the GPU sums k fp32 products in slot
+order (each fma rounds once, relative error <= 2^-24 of the running sum) and
+rounds the fp32 result to bf16 once.  So
+  |z_gpu - z_exact| <= ulp_bf16(z_exact)/2 + (k+1) * 2^-24 * sum_r |p_r y_r|
+with ulp_bf16 taken at the larger of |z_exact| and the fp32 result.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import int4_weights_amd as moe
+import oracle
+from gpu_helpers import DEV, bf16_from_u16, require_gpu, u16
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
+
+
+def _bf16_ulp(x):
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def _run(y_bits, oi, w):
+    Y = bf16_from_u16(y_bits)
+    T, k = oi.shape
+    Z = torch.empty(T, y_bits.shape[1], dtype=torch.bfloat16, device=DEV)
+    moe.moe_unpermute_combine(Y, torch.from_numpy(oi.astype(np.int32)).to(DEV),
+                              torch.from_numpy(w.astype(np.float32)).to(DEV), Z)
+    torch.cuda.synchronize()
+    return Z.float().cpu().numpy().astype(np.float64)
+
+
+def _check(y_bits, oi, w, z):
+    y = oracle.bf16_bits_to_f64(y_bits)
+    ref = oracle.combine(y, oi, w.astype(np.float32).astype(np.float64))
+    mag = oracle.combine(np.abs(y), oi, np.abs(w.astype(np.float32).astype(np.float64)))
+    k = oi.shape[1]
+    bound = 0.5 * _bf16_ulp(np.maximum(np.abs(ref), np.abs(z))) + (k + 1) * 2.0 ** -24 * mag
+    assert (np.abs(z - ref) <= bound).all(), float(np.max(np.abs(z - ref) - bound))
+
+
+def test_combine_worked_example():
+    require_gpu()
+    g = json.load(open(GOLDEN, encoding="utf-8"))
+    ids = np.array(g["topk_ids"], np.int32)
+    w = np.array(g["topk_weights"], np.float32)
+    r = oracle.route(ids, 4, "contiguous", align=128)
+    rng = np.random.default_rng(0)
+    y = u16(torch.from_numpy(rng.standard_normal((r["rows_cap"], 64)).astype(np.float32)).to(torch.bfloat16))
+    z = _run(y, r["output_index"], w)
+    _check(y, r["output_index"], w, z)
+    # the page's z_0 = 0.70 * y_packed[0] + 0.30 * y_packed[256]
+    yf = oracle.bf16_bits_to_f64(y)
+    z0 = np.float32(0.70) * yf[0] + np.float32(0.30) * yf[256]
+    assert np.allclose(z[0], z0, rtol=2 ** -7, atol=1e-6)
+
+
+@pytest.mark.parametrize("T,k,N,rows", [(1, 1, 8, 1), (333, 8, 4096, 3000), (64, 2, 256, 512), (9, 5, 1032, 40)])
+def test_combine_random_with_dropped_slots(T, k, N, rows):
+    require_gpu()
+    rng = np.random.default_rng(T + k + N)
+    y = u16(torch.from_numpy(rng.standard_normal((rows, N)).astype(np.float32)).to(torch.bfloat16))
+    oi = rng.integers(0, rows, size=(T, k)).astype(np.int32)
+    oi[rng.random((T, k)) < 0.1] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    z = _run(y, oi, w)
+    _check(y, oi, w, z)
+
+
+def test_combine_determinism_20_runs():
+    require_gpu()
+    rng = np.random.default_rng(5)
+    y = u16(torch.from_numpy(rng.standard_normal((500, 512)).astype(np.float32)).to(torch.bfloat16))
+    oi = rng.integers(0, 500, size=(100, 8)).astype(np.int32)
+    w = rng.random((100, 8)).astype(np.float32)
+    z = _run(y, oi, w)
+    for _ in range(20):
+        assert np.array_equal(_run(y, oi, w), z)

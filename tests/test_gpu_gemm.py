@@ -1,0 +1,208 @@
+"""GPU grouped GEMMs (FP8 block-scaled, INT4 weight-only) vs the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import int4_weights_amd as moe
+import oracle
+from gpu_helpers import DEV, bf16_from_u16, gemm_tolerance_check, require_gpu, u16
+
+pytestmark = pytest.mark.gpu
+SENT_BITS = 0x7BAD  # a bf16 pattern no GEMM result takes in these tests
+
+
+def _layout_rows(counts, layout, align=128, max_m=0):
+    E = len(counts)
+    if layout == moe.LAYOUT_MASKED:
+        starts = np.arange(E + 1) * max_m
+        return starts, E * max_m, np.minimum(counts, max_m)
+    starts = np.zeros(E + 1, np.int64)
+    for e in range(E):
+        starts[e + 1] = starts[e] + -(-counts[e] // align) * align
+    return starts, int(starts[E]) if starts[E] > 0 else align, np.array(counts)
+
+
+def _fp8_case(seed, counts, N, K, layout, max_m=0, act_scale=1.0):
+    rng = np.random.default_rng(seed)
+    E = len(counts)
+    starts, rows, eff = _layout_rows(np.array(counts), layout, max_m=max_m)
+    x = torch.from_numpy((rng.standard_normal((rows, K)) * act_scale).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    a_codes, sfa = oracle.quant_act(u16(x))
+    w_codes, sfw = oracle.quant_weight_fp8(u16(w))
+    return dict(E=E, N=N, K=K, rows=rows, starts=starts, eff=eff, counts=np.array(counts, np.int32), layout=layout,
+                max_m=max_m, a=a_codes, sfa=sfa, w=w_codes, sfw=sfw)
+
+
+def _run_fp8(c, expected_m=0, D=None):
+    A = torch.from_numpy(c["a"]).to(DEV)
+    SFA = torch.from_numpy(c["sfa"]).to(DEV)
+    W = torch.from_numpy(c["w"]).to(DEV)
+    SFW = torch.from_numpy(c["sfw"]).to(DEV)
+    if D is None:
+        D = torch.full((c["rows"], c["N"]), SENT_BITS, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    counts = torch.from_numpy(c["counts"]).to(DEV)
+    seg = torch.from_numpy(c["starts"].astype(np.int32)).to(DEV)
+    am = c["max_m"] if c["layout"] == moe.LAYOUT_MASKED else c["rows"]
+    moe.moe_grouped_gemm_fp8(c["layout"], A, SFA, W, SFW, D, counts, seg, c["E"], am, c["N"], c["K"], expected_m)
+    torch.cuda.synchronize()
+    return D
+
+
+def _check_fp8(c, D):
+    ref = oracle.grouped_gemm_fp8(c["a"], c["sfa"], c["w"], c["sfw"], c["eff"], c["starts"])
+    valid = np.isfinite(ref[:, 0])
+    got = D.float().cpu().numpy().astype(np.float64)
+    gemm_tolerance_check(got[valid], ref[valid], 1e-3)
+    # rows outside the segments are never written
+    bits = u16(D)
+    assert (bits[~valid] == SENT_BITS).all()
+
+
+@pytest.mark.parametrize("expected_m", [0, 16, 64])
+def test_fp8_contiguous_ragged(expected_m):
+    require_gpu()
+    c = _fp8_case(1, [0, 1, 17, 130, 300], N=384, K=640, layout=moe.LAYOUT_CONTIGUOUS)
+    _check_fp8(c, _run_fp8(c, expected_m))
+
+
+@pytest.mark.parametrize("expected_m", [0, 16, 64])
+def test_fp8_masked_with_overfull_expert(expected_m):
+    require_gpu()
+    c = _fp8_case(2, [0, 20, 3, 17, 1, 25], N=256, K=384, layout=moe.LAYOUT_MASKED, max_m=20)
+    _check_fp8(c, _run_fp8(c, expected_m))
+
+
+def test_fp8_many_experts_long_k():
+    require_gpu()
+    rng = np.random.default_rng(3)
+    counts = rng.integers(0, 40, size=33).tolist()
+    c = _fp8_case(3, counts, N=512, K=2304, layout=moe.LAYOUT_CONTIGUOUS)
+    _check_fp8(c, _run_fp8(c, 24))
+
+
+def _int_codes(rng, shape, lo=-4, hi=4):
+    code_of = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48}
+    v = rng.integers(lo, hi + 1, size=shape)
+    codes = np.vectorize(lambda t: code_of[abs(int(t))] | (0x80 if t < 0 else 0))(v).astype(np.uint8)
+    return v, codes
+
+
+def test_fp8_small_integers_bit_exact():
+    """Integer-valued codes with unit scales: every partial sum is exact, so is the bf16 result."""
+    require_gpu()
+    rng = np.random.default_rng(4)
+    E, N, K = 3, 256, 384
+    counts = np.array([5, 0, 40], np.int32)
+    starts = np.array([0, 128, 128, 256])
+    av, a = _int_codes(rng, (256, K), -2, 2)
+    wv, w = _int_codes(rng, (E, N, K), -2, 2)
+    c = dict(E=E, N=N, K=K, rows=256, starts=starts, eff=counts, counts=counts, layout=moe.LAYOUT_CONTIGUOUS,
+             max_m=0, a=a, sfa=np.ones((256, K // 128), np.float32), w=w, sfw=np.ones((E, N // 128, K // 128),
+                                                                                          np.float32))
+    for em in (0, 16, 64):
+        D = _run_fp8(c, em)
+        for e in range(E):
+            s, n = int(starts[e]), int(counts[e])
+            exact = av[s:s + n] @ wv[e].T
+            assert np.array_equal(u16(D)[s:s + n], oracle.f64_to_bf16_bits(exact.astype(np.float64)))
+
+
+def test_fp8_scale_invariance_bit_exact():
+    require_gpu()
+    c = _fp8_case(5, [9, 33], N=256, K=512, layout=moe.LAYOUT_CONTIGUOUS)
+    D0 = _run_fp8(c)
+    c2 = dict(c)
+    c2["sfa"] = c["sfa"] * np.float32(8.0)
+    c2["sfw"] = c["sfw"] * np.float32(0.125)
+    D1 = _run_fp8(c2)
+    assert torch.equal(D0, D1)
+    c3 = dict(c)
+    c3["sfa"] = c["sfa"] * np.float32(4.0)
+    D2 = _run_fp8(c3)
+    valid = np.isfinite(oracle.grouped_gemm_fp8(c["a"], c["sfa"], c["w"], c["sfw"], c["eff"], c["starts"])[:, 0])
+    assert torch.equal((D0.float() * 4)[torch.from_numpy(valid).to(DEV)], D2.float()[torch.from_numpy(valid).to(DEV)])
+
+
+def test_fp8_determinism_20_runs():
+    require_gpu()
+    c = _fp8_case(6, [50, 0, 200, 7], N=256, K=1024, layout=moe.LAYOUT_CONTIGUOUS)
+    ref = _run_fp8(c)
+    for _ in range(20):
+        assert torch.equal(_run_fp8(c), ref)
+
+
+# --------------------------------------------------------------------- INT4 --
+def _int4_case(seed, counts, N, K, layout, max_m=0):
+    rng = np.random.default_rng(seed)
+    E = len(counts)
+    starts, rows, eff = _layout_rows(np.array(counts), layout, max_m=max_m)
+    x = torch.from_numpy(rng.standard_normal((rows, K)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    q4, s16 = oracle.quant_weight_int4(u16(w))
+    return dict(E=E, N=N, K=K, rows=rows, starts=starts, eff=eff, counts=np.array(counts, np.int32), layout=layout,
+                max_m=max_m, a=u16(x), q4=q4, s16=s16)
+
+
+def _run_int4(c, expected_m=0):
+    A = bf16_from_u16(c["a"])
+    W4 = torch.from_numpy(c["q4"]).to(DEV)
+    S16 = torch.from_numpy(c["s16"].view(np.int16)).view(torch.float16).to(DEV)
+    D = torch.full((c["rows"], c["N"]), SENT_BITS, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    counts = torch.from_numpy(c["counts"]).to(DEV)
+    seg = torch.from_numpy(c["starts"].astype(np.int32)).to(DEV)
+    am = c["max_m"] if c["layout"] == moe.LAYOUT_MASKED else c["rows"]
+    moe.moe_grouped_gemm_int4(c["layout"], A, W4, S16, D, counts, seg, c["E"], am, c["N"], c["K"], expected_m)
+    torch.cuda.synchronize()
+    return D
+
+
+def _check_int4(c, D):
+    ref = oracle.grouped_gemm_int4(c["a"], c["q4"], c["s16"], c["eff"], c["starts"])
+    valid = np.isfinite(ref[:, 0])
+    got = D.float().cpu().numpy().astype(np.float64)
+    gemm_tolerance_check(got[valid], ref[valid], 1e-2)
+    assert (u16(D)[~valid] == SENT_BITS).all()
+
+
+@pytest.mark.parametrize("expected_m", [0, 16])
+def test_int4_masked(expected_m):
+    require_gpu()
+    c = _int4_case(7, [0, 1, 16, 5, 9, 30], N=384, K=640, layout=moe.LAYOUT_MASKED, max_m=16)
+    _check_int4(c, _run_int4(c, expected_m))
+
+
+@pytest.mark.parametrize("expected_m", [0, 16])
+def test_int4_contiguous_ragged(expected_m):
+    require_gpu()
+    c = _int4_case(8, [3, 0, 70, 129], N=256, K=1024, layout=moe.LAYOUT_CONTIGUOUS)
+    _check_int4(c, _run_int4(c, expected_m))
+
+
+def test_int4_integer_inputs_bit_exact():
+    """Integer activations and unit scales: the result is an exact integer, so is its bf16."""
+    require_gpu()
+    rng = np.random.default_rng(9)
+    E, N, K = 2, 256, 512
+    counts = np.array([3, 11], np.int32)
+    starts = np.array([0, 16, 32])
+    ai = rng.integers(-3, 4, size=(32, K)).astype(np.float32)
+    q = rng.integers(0, 16, size=(E, N, K)).astype(np.uint8)
+    q4 = (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+    c = dict(E=E, N=N, K=K, rows=32, starts=starts, eff=counts, counts=counts, layout=moe.LAYOUT_MASKED, max_m=16,
+             a=u16(torch.from_numpy(ai).to(torch.bfloat16)), q4=q4, s16=np.full((E, N, K // 128), 0x3C00, np.uint16))
+    for em in (0, 16):
+        D = _run_int4(c, em)
+        for e in range(E):
+            s, n = int(starts[e]), int(counts[e])
+            exact = ai[s:s + n].astype(np.int64) @ (q[e].astype(np.int64) - 8).T
+            assert np.array_equal(u16(D)[s:s + n], oracle.f64_to_bf16_bits(exact.astype(np.float64)))
+
+
+def test_int4_determinism_20_runs():
+    require_gpu()
+    c = _int4_case(10, [4, 16, 0, 2], N=256, K=512, layout=moe.LAYOUT_MASKED, max_m=16)
+    ref = _run_int4(c)
+    for _ in range(20):
+        assert torch.equal(_run_int4(c), ref)
