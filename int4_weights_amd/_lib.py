@@ -174,11 +174,23 @@ def moe_route_pack(topk_ids, E: int, layout: int, align_or_max_m: int, payload, 
                                  _ptr(dev_status), _ptr(workspace), ws_bytes, _stream(stream)), "moe_route_pack")
 
 
+def _gemm_sizes(fn, layout, E, rows_cap_or_max_m, counts, seg_offsets, sizes):
+    rows = E * rows_cap_or_max_m if layout == LAYOUT_MASKED else rows_cap_or_max_m
+    if counts.numel() < E or (layout == LAYOUT_CONTIGUOUS and (seg_offsets is None or seg_offsets.numel() < E)):
+        raise ValueError(f"{fn}: counts/seg_offsets too small")
+    for name, t, need in sizes(rows):
+        if t.numel() < need:
+            raise ValueError(f"{fn}: {name} has {t.numel()} elements, needs {need}")
+
+
 def moe_grouped_gemm_fp8(layout: int, A, SFA, W, SFW, D, counts, seg_offsets, E: int, rows_cap_or_max_m: int,
                          N: int, K: int, expected_m: int = 0, stream=None):
     _dev(A, "A", torch.uint8), _dev(SFA, "SFA", torch.float32), _dev(W, "W", torch.uint8)
     _dev(SFW, "SFW", torch.float32), _dev(D, "D", torch.bfloat16), _dev(counts, "counts", torch.int32)
     _dev(seg_offsets, "seg_offsets", torch.int32)
+    _gemm_sizes("moe_grouped_gemm_fp8", layout, E, rows_cap_or_max_m, counts, seg_offsets,
+                lambda rows: (("A", A, rows * K), ("SFA", SFA, rows * (K // 128)), ("W", W, E * N * K),
+                              ("SFW", SFW, E * (N // 128) * (K // 128)), ("D", D, rows * N)))
     _check(load().moe_grouped_gemm_fp8(layout, _ptr(A), _ptr(SFA), _ptr(W), _ptr(SFW), _ptr(D), _ptr(counts),
                                        _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
            "moe_grouped_gemm_fp8")
@@ -188,6 +200,9 @@ def moe_grouped_gemm_int4(layout: int, A, W4, S16, D, counts, seg_offsets, E: in
                           N: int, K: int, expected_m: int = 0, stream=None):
     _dev(A, "A", torch.bfloat16), _dev(W4, "W4", torch.uint8), _dev(S16, "S16", torch.float16)
     _dev(D, "D", torch.bfloat16), _dev(counts, "counts", torch.int32), _dev(seg_offsets, "seg_offsets", torch.int32)
+    _gemm_sizes("moe_grouped_gemm_int4", layout, E, rows_cap_or_max_m, counts, seg_offsets,
+                lambda rows: (("A", A, rows * K), ("W4", W4, E * N * (K // 2)), ("S16", S16, E * N * (K // 128)),
+                              ("D", D, rows * N)))
     _check(load().moe_grouped_gemm_int4(layout, _ptr(A), _ptr(W4), _ptr(S16), _ptr(D), _ptr(counts),
                                         _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
            "moe_grouped_gemm_int4")

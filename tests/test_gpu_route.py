@@ -26,13 +26,15 @@ def _check(r: Routed, ids: torch.Tensor, payload: torch.Tensor, payload2=None):
     assert np.array_equal(r.m_indices.cpu().numpy(), o["m_indices"])
     assert int(r.dev_status.item()) == o["status"]
     # payload rows: every routed row equals its token row; all other rows untouched
-    pk = r.packed.view(torch.uint8).reshape(r.rows_cap, -1).cpu().numpy()
-    src = payload.view(torch.uint8).reshape(payload.shape[0], -1).cpu().numpy()
+    rb = int(np.prod(payload.shape[1:])) * payload.element_size()
+    pk = r.packed.view(torch.uint8).reshape(r.rows_cap, rb).cpu().numpy()
+    src = payload.view(torch.uint8).reshape(payload.shape[0], rb).cpu().numpy()
     exp = oracle.pack_rows(src, o["output_index"], r.rows_cap, fill=SENT)
     assert np.array_equal(pk, exp)
     if payload2 is not None:
-        pk2 = r.packed2.view(torch.uint8).reshape(r.rows_cap, -1).cpu().numpy()
-        src2 = payload2.view(torch.uint8).reshape(payload2.shape[0], -1).cpu().numpy()
+        rb2 = int(np.prod(payload2.shape[1:])) * payload2.element_size()
+        pk2 = r.packed2.view(torch.uint8).reshape(r.rows_cap, rb2).cpu().numpy()
+        src2 = payload2.view(torch.uint8).reshape(payload2.shape[0], rb2).cpu().numpy()
         assert np.array_equal(pk2, oracle.pack_rows(src2, o["output_index"], r.rows_cap, fill=SENT))
     return o
 
