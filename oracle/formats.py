@@ -40,16 +40,19 @@ def e4m3_decode_table() -> np.ndarray:
     return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
 
 
-_POS_CODES = np.arange(0x7F, dtype=np.int64)           # 0x00 .. 0x7E: all finite non-negative codes
-_POS_VALUES = np.array([e4m3_value(c) for c in range(0x7F)], dtype=np.float64)
-
-
 def e4m3_encode(v) -> np.ndarray:
     """Round float64 values to the nearest E4M3FN code, ties to the even code.
 
+    The format's rounding rule written out: a magnitude below the smallest
+    normal 2^-6 is a multiple of the subnormal step 2^-9 (code = that multiple,
+    rounded half to even; 8 steps is the smallest normal, code 0x08); otherwise
+    a = (1 + f) * 2^E with E in [-6, 8], the 3-bit mantissa is f * 8 rounded half
+    to even, and code = (E + 7) * 8 + mantissa (a carry into the exponent is the
+    next binade, exactly as the code order continues).
+
     Requires |v| <= 448 (the quantiser guarantees it, so no saturation rule is
-    needed).  Subnormals are kept; the sign is carried even when the magnitude
-    rounds to zero, so tiny negative inputs give 0x80.
+    needed).  The sign is carried even when the magnitude rounds to zero, so
+    tiny negative inputs give 0x80.
 
     Pinned by: exhaustive comparison with torch's float8_e4m3fn cast over every
     finite bf16 with |x| <= 448, and encode(decode(c)) == c for all finite codes.
@@ -60,14 +63,13 @@ def e4m3_encode(v) -> np.ndarray:
     a = np.abs(v)
     if (a > E4M3_MAX).any():
         raise ValueError("e4m3_encode: |v| > 448")
-    hi = np.searchsorted(_POS_VALUES, a, side="left")  # first value >= a
-    hi = np.minimum(hi, len(_POS_VALUES) - 1)
-    lo = np.maximum(hi - 1, 0)
-    d_lo = a - _POS_VALUES[lo]
-    d_hi = _POS_VALUES[hi] - a
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_POS_CODES[hi] % 2 == 0))
-    exact = _POS_VALUES[hi] == a
-    code = np.where(exact | pick_hi, _POS_CODES[hi], _POS_CODES[lo]).astype(np.uint8)
+    sub = a < 2.0 ** -6
+    code_sub = np.rint(a * 2.0 ** 9)                      # np.rint rounds half to even; exact scaling
+    _, ex = np.frexp(np.where(sub, 1.0, a))               # a = m * 2^ex, m in [0.5, 1)
+    E = ex - 1                                            # a = (1 + f) * 2^E
+    frac = np.where(sub, 0.0, np.ldexp(a, -E) - 1.0)      # exact
+    code_norm = (E + 7) * 8 + np.rint(frac * 8.0)
+    code = np.where(sub, code_sub, code_norm).astype(np.uint8)
     return code | (np.signbit(v).astype(np.uint8) << 7)
 
 
