@@ -37,7 +37,9 @@ def parse():
     ap.add_argument("--config", default="dsv3_prefill",
                     choices=["tiny", "dsv3_prefill", "dsv3_decode", "qwen3_skewed", "int4_decode"])
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
-    ap.add_argument("--cpu-experts", type=int, default=4, help="experts in the timed oracle sample")
+    ap.add_argument("--cpu-experts", type=int, default=64, help="experts in the timed oracle sample")
+    ap.add_argument("--expected-m", type=int, default=0,
+                    help="tiling hint passed to the GEMM (default: routes per expert)")
     return ap.parse_args()
 
 
@@ -111,7 +113,7 @@ def run(args):
         codes, sfw, kept = fp8_weights(torch, moe, synth, cfg, N, K, synth.STREAM_WEIGHTS, keep=set(sample))
         layout = moe.LAYOUT_MASKED if cfg.layout == "masked" else moe.LAYOUT_CONTIGUOUS
         am = cfg.max_m if cfg.layout == "masked" else cfg.align
-        em = max(1, R // E)
+        em = args.expected_m or max(1, R // E)
         layer = MoeFP8Layer(codes, sfw, k, T, layout, am, expected_m=em)
         down = None
         if cfg.K_down:
@@ -156,7 +158,7 @@ def run(args):
             copies.append((q4, s16))
             del w
         layer = MoeInt4Layer(copies[0][0], copies[0][1], k, T, moe.LAYOUT_MASKED, cfg.max_m,
-                             expected_m=max(1, R // E))
+                             expected_m=args.expected_m or max(1, R // E))
         names = ["moe_route_pack", "gemm", "moe_unpermute_combine"]
 
         def step(tm, s):

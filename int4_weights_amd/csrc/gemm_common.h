@@ -24,30 +24,33 @@ constexpr int kBN = 256;       // columns per unit (4 waves x 64)
 constexpr int kXcds = 8;
 
 struct Sched {
-  int* rows;    // [E] valid rows per expert
-  int* start;   // [E] first packed row
-  int* up;      // [E+1] unit prefix
+  int* up;  // [E+1] unit prefix (LDS)
 };
+
+// Valid rows and first packed row of expert e (clipped to its segment).
+__device__ inline void expert_rows(const GemmArgs& a, int e, int& rows, int& start) {
+  int r = a.counts[e];
+  int64_t st, cap;
+  if (a.masked) {
+    st = (int64_t)e * a.max_m;
+    cap = a.max_m;
+  } else {
+    st = a.seg_offsets[e];
+    cap = (st >= 0 && st < a.rows_cap) ? a.rows_cap - st : 0;
+  }
+  if (r < 0) r = 0;
+  if (r > cap) r = (int)cap;
+  rows = r;
+  start = (int)st;
+}
 
 // Build the unit table (all threads of the workgroup; ends with a barrier).
 template <int BM>
 __device__ inline void sched_build(const GemmArgs& a, Sched s, int* s_tmp) {
   const int nt = (a.N + kBN - 1) / kBN;
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
-    int r = a.counts[e];
-    int64_t st;
-    int64_t cap;
-    if (a.masked) {
-      st = (int64_t)e * a.max_m;
-      cap = a.max_m;
-    } else {
-      st = a.seg_offsets[e];
-      cap = (st >= 0 && st < a.rows_cap) ? a.rows_cap - st : 0;
-    }
-    if (r < 0) r = 0;
-    if (r > cap) r = (int)cap;
-    s.rows[e] = r;
-    s.start[e] = (int)st;
+    int r, st;
+    expert_rows(a, e, r, st);
     s.up[e] = ((r + BM - 1) / BM) * nt;
   }
   __syncthreads();
@@ -60,14 +63,16 @@ struct Unit {
 
 template <int BM>
 __device__ inline Unit sched_unit(const GemmArgs& a, Sched s, int v) {
-  const int e = upper_bound_minus1(s.up, a.E, v);
+  const int e = uniform(upper_bound_minus1(s.up, a.E, v));
+  int rows, start;
+  expert_rows(a, e, rows, start);
   const int local = v - s.up[e];
-  const int chunks = (s.rows[e] + BM - 1) / BM;
+  const int chunks = (rows + BM - 1) / BM;
   const int nt = local / chunks, ch = local - nt * chunks;
   Unit u;
-  u.e = uniform(e);
-  u.row0 = uniform(s.start[e] + ch * BM);
-  u.mrows = uniform(min(BM, s.rows[e] - ch * BM));
+  u.e = e;
+  u.row0 = uniform(start + ch * BM);
+  u.mrows = uniform(min(BM, rows - ch * BM));
   u.n0 = uniform(nt * kBN);
   return u;
 }

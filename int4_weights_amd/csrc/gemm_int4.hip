@@ -151,6 +151,7 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
     commit(ks, s_c);
     barrier_lds();
     issue(ks + S - 1, IntC<(s + S - 1) % S>{});
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this block's MFMAs
     compute(ks, s_c);
   };
 
@@ -182,8 +183,8 @@ template <int RB, int S>
 __global__ __launch_bounds__(256, 1) void gemm_int4_kernel(const GemmArgs a) {
   using C = I4Cfg<RB, S>;
   __shared__ __attribute__((aligned(1024))) I4Smem<RB, S> sm;
-  __shared__ int s_rows[kMaxExperts], s_start[kMaxExperts], s_up[kMaxExperts + 1], s_tmp[257];
-  const Sched sc{s_rows, s_start, s_up};
+  __shared__ int s_up[kMaxExperts + 1], s_tmp[257];
+  const Sched sc{s_up};
   sched_build<C::BM>(a, sc, s_tmp);
   const Walk walk = sched_walk(s_up[a.E]);
   const int lane = lane_id();

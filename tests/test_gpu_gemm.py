@@ -74,6 +74,14 @@ def test_fp8_masked_with_overfull_expert(expected_m):
     _check_fp8(c, _run_fp8(c, expected_m))
 
 
+def test_fp8_masked_tall_segments():
+    """Masked layout with segments taller than one 128-row tile (the LDS-staged kernel)."""
+    require_gpu()
+    c = _fp8_case(12, [150, 0, 200, 65], N=384, K=768, layout=moe.LAYOUT_MASKED, max_m=200)
+    for em in (0, 200):
+        _check_fp8(c, _run_fp8(c, em))
+
+
 def test_fp8_many_experts_long_k():
     require_gpu()
     rng = np.random.default_rng(3)
