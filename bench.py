@@ -40,7 +40,59 @@ def parse():
     ap.add_argument("--cpu-experts", type=int, default=64, help="experts in the timed oracle sample")
     ap.add_argument("--expected-m", type=int, default=0,
                     help="tiling hint passed to the GEMM (default: routes per expert)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times), for scaling "
+                         "the HBM byte counters of a profiler run")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counters calibrate the GEMM's."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}),
+          flush=True)
+
+
+KERNEL_SOURCES = {
+    "moe_grouped_gemm_fp8": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h", "moe_internal.h"],
+    "moe_grouped_gemm_int4": ["gemm_int4.hip", "gemm_common.h", "moe_device.h", "moe_internal.h"],
+}
+
+
+def sources_sha256(kernel):
+    """Hash of the HIP sources a kernel is built from (counter figures are valid only for these)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "int4_weights_amd", "csrc")
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, or None.
+
+    profiles/traffic.json holds, per kernel and workload, the calibrated byte count and the hash of the
+    sources it was measured on; a kernel changed since then reports None."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            entry = json.load(fh).get(f"{kernel}/{workload}")
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("sources_sha256") != sources_sha256(kernel):
+        return None
+    return entry["bytes_per_launch"]
 
 
 def log(*a):
@@ -229,8 +281,8 @@ def run(args):
         value, unit = gemm_bytes / (ms_step / 1e3) / 1e9, "GB/s"
         dtype = "int4xbf16"
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
     roof["kernel"] = "moe_grouped_gemm_fp8" if cfg.weights == "fp8" else "moe_grouped_gemm_int4"
+    roof["traffic"] = measured_traffic(roof["kernel"], cfg.name)
     roof["avg_launch_ms"] = kern["gemm"]
 
     cpu = None
@@ -309,6 +361,9 @@ def main():
                                    "multi-GPU expert parallelism is a design note, not a measured path",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     run(args)
 
 
