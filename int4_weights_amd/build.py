@@ -44,9 +44,22 @@ def _compile(src: str) -> str:
     return out
 
 
+GENERATED = [("gen_fp8_asm.py", "gemm_fp8_tall_loop.inc")]
+
+
+def generate() -> None:
+    """Write the generated assembly includes (the tall FP8 main loop) next to the sources."""
+    for script, out in GENERATED:
+        r = subprocess.run([sys.executable, os.path.join(CSRC, script), os.path.join(CSRC, out)],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"{script} failed:\n{r.stderr}")
+
+
 def build(verbose: bool = True) -> str:
     """Compile every HIP source for gfx950 and link libmoe.so; returns its path."""
     os.makedirs(OBJ, exist_ok=True)
+    generate()
     jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(_compile, SOURCES))

@@ -207,187 +207,107 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 }
 
 // ----------------------------------------------------------------------------
-// Tall tiles (prefill): BM = 192 rows x BN = 256 columns, 4 waves of 64
-// columns, K consumed in halves of 64 bytes with v_mfma_scale_f32_32x32x64_f8f6f4
-// (the two halves of a 128-wide K block share its scales).  Both operands are
-// staged in LDS by direct global->LDS copies in a 5-deep ring (4 half-blocks,
-// ~112 KB per CU, in flight while one is multiplied).  Each wave's weight slab
-// (64 rows x 64 B per half block) is private to it; the activation tile is
-// shared.  The copies are inline asm (moe_device.h), so the waits on them are
-// explicit: a wave issues kLOps copies per stage, and "stage h landed" is
-// vmcnt <= kLOps * (stages issued after h).  Registers hold the accumulators
-// and one row block's fragments only.
-constexpr int kLRB = 6;                    // 32-row blocks (BM = 192)
-constexpr int kLS = 5;                     // LDS ring depth (half blocks)
-constexpr int kLWslab = 64 * 64;           // one wave's weight slab per stage (bytes)
-constexpr int kLAtile = 32 * kLRB * 64;    // activation tile per stage (bytes)
-constexpr int kLApw = kLAtile / 1024 / 4;  // activation copies per wave per stage
-constexpr int kLOps = 4 + kLApw + 1;       // copies per wave per stage (weights, activations, row scales)
+// Tall tiles (prefill): up to 192 rows x 256 columns per unit, 4 waves of 64
+// columns, v_mfma_scale_f32_16x16x128_f8f6f4 as in the short-tile kernel.
+//  * Weights are private to each wave and stream from HBM straight into a
+//    4-deep VGPR ring (3 K blocks in flight); activations are shared by the 4
+//    waves and copied global->LDS (global_load_lds) into a 4-deep LDS ring.
+//    Every K block issues the same loads (the tail re-reads the last block),
+//    so one exact vmcnt serves every step.
+//  * Scales: the unit's row scales are one contiguous block of SFA (its rows
+//    are consecutive); they are read once per unit and kept in LDS as E8M0
+//    exponent bytes, [K block][row], so a step reads one byte per lane for
+//    each 16-row block.  The wave's weight scales are staged the same way.
+//  * The K loop and the epilogue are written out in assembly
+//    (gen_fp8_asm.py -> gemm_fp8_tall_loop.inc): fixed registers for the 192
+//    accumulators and the weight ring, the next row block's activation
+//    fragments read from LDS while the current block's matrix instructions
+//    run, 16-row granularity (a unit computes ceil(rows/16) row blocks), and
+//    v_cvt_pk_bf16_f32 (round to nearest even) in the epilogue.
+#include "gemm_fp8_tall_loop.inc"
 
-struct Fp8LdsSmem {
-  uint8_t w[kLS][4][kLWslab];
-  uint8_t a[kLS][kLAtile];
-  float sa[kLS][256];
-  float sw[4][kMaxKBlocks];  // per-wave weight scales of the current unit
+constexpr int kTS = MOE_FP8_TALL_S;
+constexpr int kTRB = MOE_FP8_TALL_RB;
+constexpr int kTApw = MOE_FP8_TALL_APW;
+
+struct Fp8TallSmem {
+  uint8_t a[kTS][MOE_FP8_TALL_SLOT_A];                // activation rows, 128 B each, 16-B chunks XOR-swizzled
+  uint8_t sae[kMaxKBlocks][MOE_FP8_TALL_SAE_ROWS];    // row-scale exponents of the unit, [K block][row]
+  float sw[4][kMaxKBlocks];                           // per-wave weight scales of the current unit
 };
+static_assert(MOE_FP8_TALL_SLOT_A == 16 * kTRB * 128, "activation slot");
+static_assert(MOE_FP8_TALL_SAE_ROWS == 16 * kTRB, "row-scale staging");
 
-typedef float v16f __attribute__((ext_vector_type(16)));
-// An empty asm that reads and writes x in AGPRs: fixes where x is produced.
-__device__ __forceinline__ void pin_agpr(v16f& x) { asm volatile("" : "+a"(x)); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_rt(int n) {  // n in [0, N], multiples of kLOps
-  if (n >= 3 * kLOps) wait_vmcnt<3 * kLOps>();
-  else if (n >= 2 * kLOps) wait_vmcnt<2 * kLOps>();
-  else if (n >= kLOps) wait_vmcnt<kLOps>();
-  else wait_vmcnt<0>();
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// 64-byte rows: the 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3).
-template <int RBE>
-__device__ __forceinline__ void fp8_unit_lds(const GemmArgs& a, const Unit& u, Fp8LdsSmem& sm, int wv, int lane) {
-  const int l32 = lane & 31, lh = lane >> 5;
-  const int K = a.K, N = a.N, KB = K / 128, KH = K / 64, NB = N / 128;
+__device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, Fp8TallSmem& sm, int wv, int lane) {
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int K = a.K, N = a.N, KB = K / 128, NB = N / 128;
   const int ncol0 = u.n0 + 64 * wv;
-  const bool wave_on = ncol0 < N;
-  const int ncl = wave_on ? ncol0 : N - 64;  // an idle wave re-reads valid rows and stores nothing
+  const int won = ncol0 < N ? 1 : 0;
+  const int ncl = won ? ncol0 : N - 64;  // an idle wave re-reads valid columns and stores nothing
 
-  // copy sources (16 rows of 64 B per copy instruction)
-  const uint8_t* wsrc[4];
+  const uint64_t wb = uniform_u64((uint64_t)(a.W + (int64_t)u.e * N * K));
+  uint32_t wo[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * i + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    wsrc[i] = a.W + ((int64_t)u.e * N + ncl + r) * K + 16 * c;
-  }
-  const uint8_t* asrc[kLApw];
+  for (int c = 0; c < 4; ++c) wo[c] = (uint32_t)(ncl + 16 * c + l16) * (uint32_t)K + 16u * lg;
+  const uint64_t ab = uniform_u64((uint64_t)(a.A + (int64_t)u.row0 * K));
+  uint32_t ao[kTApw];
 #pragma unroll
-  for (int i = 0; i < kLApw; ++i) {
-    const int r = 16 * (wv * kLApw + i) + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    asrc[i] = a.A + (int64_t)(u.row0 + min(r, u.mrows - 1)) * K + 16 * c;
+  for (int i = 0; i < kTApw; ++i) {
+    const int r = 8 * (wv * kTApw + i) + (lane >> 3);  // tile row this lane copies
+    const int c = (lane & 7) ^ ((r >> 1) & 7);        // its chunk, landing at position lane & 7
+    ao[i] = (uint32_t)min(r, u.mrows - 1) * (uint32_t)K + 16u * c;
   }
-  const float* sasrc = a.SFA + (int64_t)(u.row0 + min(64 * wv + lane, u.mrows - 1)) * KB;
-  // this wave's weight scales for the unit -> LDS, with ordinary loads before any copy is in flight
+  // this wave's weight scales and the unit's row-scale exponents -> LDS, with
+  // ordinary loads (nothing else is in flight here; the previous unit ended
+  // with a barrier, so no wave still reads these)
   const float* swsrc = (const float*)a.SW + ((int64_t)u.e * NB + ncl / 128) * KB;
   for (int j = 0; j < KB; j += 64) sm.sw[wv][j + lane] = swsrc[min(j + lane, KB - 1)];
+  const uint32_t* sfa = (const uint32_t*)(a.SFA + (int64_t)u.row0 * KB);
+  for (int r = wv; r < u.mrows; r += 4)
+    for (int kb = lane; kb < KB; kb += 64) sm.sae[kb][r] = (uint8_t)(sfa[(int64_t)r * KB + kb] >> 23);
 
-  // fragment reads: lane (row r = l32, half lh) takes chunks lh and 2 + lh of its row
-  const int fsw = (l32 >> 2) & 3;
-  const int off_lo = l32 * 64 + 16 * (lh ^ fsw);
-  const int off_hi = l32 * 64 + 16 * ((2 + lh) ^ fsw);
-
-  v16f acc[RBE][2];
-#pragma unroll
-  for (int rb = 0; rb < RBE; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
-
-  auto issue = [&](int h, auto slot_c) {
-    constexpr int slot = decltype(slot_c)::value;
-    const int koff = h * 64;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + koff, &sm.w[slot][wv][i * 1024]);
-#pragma unroll
-    for (int i = 0; i < kLApw; ++i) dma16(asrc[i] + koff, &sm.a[slot][(wv * kLApw + i) * 1024]);
-    dma4(sasrc + (h >> 1), &sm.sa[slot][64 * wv]);
-  };
-
-  auto compute = [&](int h, auto slot_c) {
-    constexpr int slot = decltype(slot_c)::value;
-    const int swe = (int)(__float_as_uint(sm.sw[wv][h >> 1]) >> 23);
-    v8i wf[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const v4i lo = *(const v4i*)(&sm.w[slot][wv][0] + off_lo + cb * 2048);
-      const v4i hi = *(const v4i*)(&sm.w[slot][wv][0] + off_hi + cb * 2048);
-      wf[cb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-    const uint8_t* ab = &sm.a[slot][0];
-    const float* sab = &sm.sa[slot][l32];
-#pragma unroll
-    for (int rb = 0; rb < RBE; ++rb) {
-      const v4i lo = *(const v4i*)(ab + off_lo + rb * 2048);
-      const v4i hi = *(const v4i*)(ab + off_hi + rb * 2048);
-      const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const int sae = (int)(__float_as_uint(sab[32 * rb]) >> 23);
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[cb], af, acc[rb][cb], 0, 0, 0, swe, 0,
-                                                                      sae);
-    }
-  };
-
-  // Half block h is in slot h % 5.  Before multiplying it: its copies have
-  // landed (the later stages already issued may stay in flight) and every wave
-  // has passed the barrier, so slot (h + 4) % 5 -- last read for h - 1 -- is free.
-  auto step = [&](int h, auto s_c) {
-    constexpr int s = decltype(s_c)::value;
-    __builtin_amdgcn_sched_barrier(0);
-    const int later = min(KH - 1 - h, kLS - 2);  // stages issued after h
-    wait_vmcnt_rt<3 * kLOps>(later * kLOps);
-    barrier_lds();
-    if (h + kLS - 1 < KH) issue(h + kLS - 1, IntC<(s + kLS - 1) % kLS>{});
-    __builtin_amdgcn_sched_barrier(0);
-    compute(h, s_c);
-    // Pin this half block's MFMAs here: without a use, the optimiser sinks the
-    // pure MFMA chains to the end of the unrolled loop and keeps every stage's
-    // fragments live at once.
-#pragma unroll
-    for (int rb = 0; rb < RBE; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) pin_agpr(acc[rb][cb]);
-  };
-
-  static_for<0, kLS - 1>([&](auto s_c) {
-    constexpr int s = decltype(s_c)::value;
-    if (s < KH) issue(s, s_c);
-  });
-  const int nfull = KH / kLS;
-  for (int g = 0; g < nfull; ++g) static_for<0, kLS>([&](auto s_c) { step(g * kLS + decltype(s_c)::value, s_c); });
-  static_for<0, kLS>([&](auto s_c) {
-    const int h = nfull * kLS + decltype(s_c)::value;
-    if (h < KH) step(h, s_c);
-  });
-  wait_vmcnt<0>();
-  barrier_lds();  // the ring is free for the next unit
-
-  // accumulator (32x32): lane holds column m = l32 and rows n = 8q + 4lh + j
-  if (wave_on) {
-#pragma unroll
-    for (int rb = 0; rb < RBE; ++rb) {
-      const int m = 32 * rb + l32;
-      if (m < u.mrows) {
-        uint16_t* drow = a.D + (int64_t)(u.row0 + m) * N + ncol0 + 4 * lh;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint2 o;
-            o.x = f32_to_bf16_rne(acc[rb][cb][4 * q]) | (f32_to_bf16_rne(acc[rb][cb][4 * q + 1]) << 16);
-            o.y = f32_to_bf16_rne(acc[rb][cb][4 * q + 2]) | (f32_to_bf16_rne(acc[rb][cb][4 * q + 3]) << 16);
-            *(uint2*)(drow + 32 * cb + 8 * q) = o;
-          }
-      }
-    }
-  }
+  const int fsw = (l16 >> 1) & 7;  // fragment reads: row m at m*128, chunk c at position c ^ ((m >> 1) & 7)
+  const uint32_t abase = lds_offset(&sm.a[0][0]);
+  const uint32_t alo = abase + l16 * 128 + 16 * (lg ^ fsw);
+  const uint32_t ahi = abase + l16 * 128 + 16 * ((4 + lg) ^ fsw);
+  const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.a[0][wv * kTApw * 1024]));
+  uint32_t sep = lds_offset(&sm.sae[0][l16]);
+  uint32_t swp = lds_offset(&sm.sw[wv][0]);
+  const uint64_t db = uniform_u64((uint64_t)(a.D + (int64_t)u.row0 * N));
+  uint32_t doff = (uint32_t)(l16 * N + ncol0 + 4 * lg) * 2u;
+  const int dstep = uniform(32 * N);
+  const int rbe = uniform((u.mrows + 15) / 16);
+  const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
+  int ks, q, t, inc, m0v = 0;
+  uint64_t sv;
+  asm volatile(MOE_FP8_TALL_LOOP
+               : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), [wo2] "+v"(wo[2]), [wo3] "+v"(wo[3]), [ao0] "+v"(ao[0]),
+                 [ao1] "+v"(ao[1]), [ao2] "+v"(ao[2]), [ao3] "+v"(ao[3]), [ao4] "+v"(ao[4]), [ao5] "+v"(ao[5]),
+                 [sep] "+v"(sep), [swp] "+v"(swp), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),
+                 [inc] "=&s"(inc), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v)
+               : [wb] "s"(wb), [ab] "s"(ab), [ma] "s"(ma), [alo] "v"(alo), [ahi] "v"(ahi), [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb), [rbe] "s"(rbe),
+                 [mrows] "s"(mrows), [won] "s"(wons), [l16] "v"(l16)
+               : "memory", "vcc", "exec", "scc", MOE_FP8_TALL_CLOBBERS);
 }
 
-__global__ __launch_bounds__(256, 1) void gemm_fp8_lds_kernel(const GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) Fp8LdsSmem sm;
+__global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(const GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) Fp8TallSmem sm;
   __shared__ int s_up[kMaxExperts + 1];
   const Sched sc{s_up};
-  // the scan scratch (257 ints) borrows the row-scale ring, which is idle until the first unit
-  sched_build<32 * kLRB>(a, sc, (int*)&sm.sa[0][0]);
+  // the scan scratch (257 ints) borrows the weight-scale staging, idle until the first unit
+  sched_build<16 * kTRB>(a, sc, (int*)&sm.sw[0][0]);
   const Walk walk = sched_walk(s_up[a.E]);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
-    const Unit u = sched_unit<32 * kLRB>(a, sc, v);
-    if (u.mrows <= 96) fp8_unit_lds<3>(a, u, sm, wv, lane);
-    else fp8_unit_lds<kLRB>(a, u, sm, wv, lane);
+    const Unit u = sched_unit<16 * kTRB>(a, sc, v);
+    fp8_unit_tall(a, u, sm, wv, lane);
   }
 }
 
@@ -400,22 +320,22 @@ static hipError_t launch_fp8(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-static hipError_t launch_fp8_lds(const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_fp8_tall(const GemmArgs& a, hipStream_t s) {
   const int cus = device_info().cus;
   int grid = cus - cus % kXcds;
   if (grid < kXcds) grid = kXcds;
-  gemm_fp8_lds_kernel<<<grid, 256, 0, s>>>(a);
+  gemm_fp8_tall_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s) {
   // Tile height from the expected rows per active expert: decode-sized
   // segments keep the weights in a deep register ring (short tiles), prefill
-  // segments use the LDS-staged 128-row tile.
+  // segments use the tall tile (up to 192 rows).
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 256);
   if (em <= 16) return launch_fp8<1, 8, 4>(a, s);
   if (em <= 64) return launch_fp8<4, 6, 4>(a, s);
-  return launch_fp8_lds(a, s);
+  return launch_fp8_tall(a, s);
 }
 
 }  // namespace moe
