@@ -118,16 +118,20 @@ class Timer:
 
 
 def fp8_weights(torch, moe, synth, cfg, N, K, stream_id, keep=()):
-    """Quantised FP8 expert weights generated on the GPU; bf16 copies of `keep` experts on the host."""
+    """Quantised FP8 expert weights generated on the GPU, stored in the fragment-packed order
+    (moe_pack_weight_fp8, prepared once like any offline weight layout); bf16 copies of `keep`
+    experts on the host."""
     E = cfg.E
     codes = torch.empty(E, N, K, dtype=torch.uint8, device="cuda")
     sfw = torch.empty(E, N // 128, K // 128, dtype=torch.float32, device="cuda")
     kept = {}
     chunk = 16
+    rowmajor = torch.empty(chunk, N, K, dtype=torch.uint8, device="cuda")
     for e0 in range(0, E, chunk):
         ex = list(range(e0, min(E, e0 + chunk)))
         w = synth.expert_weights(cfg, N, K, experts=ex, stream=stream_id, device="cuda")
-        moe.moe_quant_weight_fp8(w, codes[e0:e0 + len(ex)], sfw[e0:e0 + len(ex)])
+        moe.moe_quant_weight_fp8(w, rowmajor[:len(ex)], sfw[e0:e0 + len(ex)])
+        moe.moe_pack_weight_fp8(rowmajor[:len(ex)], codes[e0:e0 + len(ex)])
         for i, e in enumerate(ex):
             if e in keep:
                 kept[e] = w[i].cpu()
@@ -166,7 +170,7 @@ def run(args):
         layout = moe.LAYOUT_MASKED if cfg.layout == "masked" else moe.LAYOUT_CONTIGUOUS
         am = cfg.max_m if cfg.layout == "masked" else cfg.align
         em = args.expected_m or max(1, R // E)
-        layer = MoeFP8Layer(codes, sfw, k, T, layout, am, expected_m=em)
+        layer = MoeFP8Layer(codes, sfw, k, T, layout, am, expected_m=em, weights_packed=True)
         down = None
         if cfg.K_down:
             names = ["moe_quant_act", "moe_route_pack", "gemm", "moe_quant_act_down", "gemm_down",

@@ -62,6 +62,11 @@ enum {
 
 enum { MOE_LAYOUT_CONTIGUOUS = 0, MOE_LAYOUT_MASKED = 1 };
 
+/* Flag ORed into the layout argument of moe_grouped_gemm_fp8: the weight
+ * codes are in the fragment-packed order written by moe_pack_weight_fp8
+ * instead of row-major [E, N, K]. */
+enum { MOE_WEIGHTS_PACKED = 0x10 };
+
 enum { MOE_MAX_EXPERTS = 1024, MOE_MAX_TOPK = 64 };
 
 /* Version of this ABI (bumped on any incompatible change). */
@@ -106,6 +111,24 @@ moe_status moe_quant_act(const uint16_t* x, int64_t rows, int K,
  *   Requires N % 128 == 0, K % 128 == 0, w and q 16-byte aligned. */
 moe_status moe_quant_weight_fp8(const uint16_t* w, int E, int N, int K,
                                 uint8_t* q, float* sfw, void* stream);
+
+/* moe_pack_weight_fp8: reorder row-major E4M3 weight codes [E, N, K] into the
+ * fragment-packed order the FP8 grouped GEMM reads fastest (a weight layout
+ * prepared once, offline, like the prepacked weights of ONNX Runtime
+ * "MatMulNBits -- CUDA Operator Documentation" (the weight_prepacked
+ * attribute of its fpA_intB path) and the transform-once weight scale
+ * layouts of the nxmr.cn DeepGEMM article, "补偿机制三").  Nothing is
+ * quantised or rounded: the output is a permutation of the input bytes.
+ *   For expert e, K block kb (128 K values), 16-column block cb, half h
+ *   (the 64 K values 128kb + 64h ...), lane L = c16 + 16*g (c16 in [0,16),
+ *   g in [0,4)) and byte j in [0,16):
+ *     packed[e*N*K + ((kb*(N/16) + cb)*2 + h)*1024 + L*16 + j]
+ *       = q[e][16*cb + c16][128*kb + 64*h + 16*g + j]
+ *   i.e. each 16 x 128 block is 2 KB contiguous, K blocks outermost, so the
+ *   columns of one K block are adjacent.  q and packed are [E*N*K] bytes,
+ *   16-byte aligned, and must not overlap.  Requires N % 128 == 0, K % 128 == 0.
+ *   The scales (sfw) are unchanged. */
+moe_status moe_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t* packed, void* stream);
 
 /* moe_quant_weight_int4: group-128 4-bit weight quantisation in the
  * MatMulNBits layout (ONNX Runtime "MatMulNBits -- CUDA Operator
@@ -182,6 +205,8 @@ moe_status moe_route_pack(const int32_t* topk_ids, int T, int k, int E,
  *   layout CONTIGUOUS: start_e = seg_offsets[e], rows_cap_or_max_m = rows of A/D.
  *   layout MASKED:     start_e = e*max_m, rows_cap_or_max_m = max_m,
  *                      seg_offsets ignored (may be NULL), rows = E*max_m.
+ *   layout | MOE_WEIGHTS_PACKED: W holds the codes in the order written by
+ *                      moe_pack_weight_fp8 (same values, faster to stream).
  *   counts[e] is clipped to the segment capacity on the device.
  *   expected_m: tiling hint, the mean rows per active expert (0 = choose from
  *   the layout).  Rows of D outside the segments are never written.

@@ -12,11 +12,13 @@ from ._lib import (  # noqa: F401
     LAYOUT_MASKED,
     LIB_PATH,
     SIGNATURES,
+    WEIGHTS_PACKED,
     MoeError,
     load,
     moe_abi_version,
     moe_grouped_gemm_fp8,
     moe_grouped_gemm_int4,
+    moe_pack_weight_fp8,
     moe_packed_rows_cap,
     moe_quant_act,
     moe_quant_weight_fp8,

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 LAYOUT_CONTIGUOUS = 0
 LAYOUT_MASKED = 1
+WEIGHTS_PACKED = 0x10  # flag for moe_grouped_gemm_fp8's layout: W in moe_pack_weight_fp8 order
 DEV_ID_RANGE = 1
 DEV_CAPACITY = 2
 
@@ -34,6 +35,7 @@ SIGNATURES = {
     "moe_quant_act": (_c_i32, [_vp, _c_i64, ctypes.c_int, _vp, _vp, _vp]),
     "moe_quant_weight_fp8": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
     "moe_quant_weight_int4": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_pack_weight_fp8": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
     "moe_route_pack": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_i64,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
@@ -133,6 +135,15 @@ def moe_quant_weight_fp8(w, q, sfw, stream=None):
            "moe_quant_weight_fp8")
 
 
+def moe_pack_weight_fp8(q, packed, stream=None):
+    """q uint8 [E, N, K] (row-major codes) -> packed uint8 [E, N, K] in the fragment order (see include/moe.h)."""
+    _dev(q, "q", torch.uint8, 3), _dev(packed, "packed", torch.uint8, 3)
+    E, N, K = q.shape
+    if tuple(packed.shape) != (E, N, K):
+        raise ValueError("moe_pack_weight_fp8: shape mismatch")
+    _check(load().moe_pack_weight_fp8(_ptr(q), E, N, K, _ptr(packed), _stream(stream)), "moe_pack_weight_fp8")
+
+
 def moe_quant_weight_int4(w, q4, s16, stream=None):
     """w bf16 [E, N, K] -> q4 uint8 [E, N, K/2], s16 float16 [E, N, K/128]."""
     _dev(w, "w", torch.bfloat16, 3), _dev(q4, "q4", torch.uint8, 3), _dev(s16, "s16", torch.float16, 3)
@@ -175,6 +186,7 @@ def moe_route_pack(topk_ids, E: int, layout: int, align_or_max_m: int, payload, 
 
 
 def _gemm_sizes(fn, layout, E, rows_cap_or_max_m, counts, seg_offsets, sizes):
+    layout &= ~WEIGHTS_PACKED
     rows = E * rows_cap_or_max_m if layout == LAYOUT_MASKED else rows_cap_or_max_m
     if counts.numel() < E or (layout == LAYOUT_CONTIGUOUS and (seg_offsets is None or seg_offsets.numel() < E)):
         raise ValueError(f"{fn}: counts/seg_offsets too small")

@@ -49,7 +49,7 @@ using namespace moe;
 
 extern "C" {
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 const char* moe_status_str(moe_status s) {
   switch (s) {
@@ -101,6 +101,22 @@ moe_status moe_quant_weight_fp8(const uint16_t* w, int E, int N, int K, uint8_t*
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(sfw, 4))
     return fail(MOE_ERR_ALIGN, "moe_quant_weight_fp8: w and q must be 16-byte aligned");
   return hip_status(launch_quant_weight_fp8(w, E, N, K, q, sfw, (hipStream_t)stream), "moe_quant_weight_fp8");
+}
+
+moe_status moe_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t* packed, void* stream) {
+  g_err[0] = 0;
+  if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_pack_weight_fp8: E=%d N=%d K=%d", E, N, K);
+  if (N % 128 || K % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_weight_fp8: N=%d and K=%d must be multiples of 128", N, K);
+  if ((int64_t)N * K > 0xffffffffll) return fail(MOE_ERR_UNSUPPORTED, "moe_pack_weight_fp8: one expert exceeds 4 GiB");
+  if (E == 0) return MOE_OK;
+  if (!q || !packed) return fail(MOE_ERR_NULL, "moe_pack_weight_fp8: null pointer");
+  if (!aligned(q, 16) || !aligned(packed, 16))
+    return fail(MOE_ERR_ALIGN, "moe_pack_weight_fp8: q and packed must be 16-byte aligned");
+  const uint8_t* qe = q + (int64_t)E * N * K;
+  const uint8_t* pe = packed + (int64_t)E * N * K;
+  if (q < pe && packed < qe) return fail(MOE_ERR_SHAPE, "moe_pack_weight_fp8: q and packed overlap");
+  return hip_status(launch_pack_weight_fp8(q, E, N, K, packed, (hipStream_t)stream), "moe_pack_weight_fp8");
 }
 
 moe_status moe_quant_weight_int4(const uint16_t* w, int E, int N, int K, uint8_t* q4, uint16_t* s16, void* stream) {
@@ -207,6 +223,8 @@ moe_status moe_grouped_gemm_fp8(int layout, const uint8_t* A, const float* SFA, 
                                 uint16_t* D, const int32_t* counts, const int32_t* seg_offsets, int E,
                                 int64_t rows_cap_or_max_m, int N, int K, int expected_m, void* stream) {
   g_err[0] = 0;
+  const int wpacked = (layout & MOE_WEIGHTS_PACKED) ? 1 : 0;
+  layout &= ~MOE_WEIGHTS_PACKED;
   moe_status st = check_gemm("moe_grouped_gemm_fp8", layout, A, W, SFW, D, counts, seg_offsets, E, rows_cap_or_max_m,
                              N, K);
   if (st) return st;
@@ -226,6 +244,7 @@ moe_status moe_grouped_gemm_fp8(int layout, const uint8_t* A, const float* SFA, 
   a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
   a.N = N;
   a.K = K;
+  a.wpacked = wpacked;
   return hip_status(launch_gemm_fp8(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_fp8");
 }
 
@@ -251,6 +270,7 @@ moe_status moe_grouped_gemm_int4(int layout, const uint16_t* A, const uint8_t* W
   a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
   a.N = N;
   a.K = K;
+  a.wpacked = 0;
   return hip_status(launch_gemm_int4(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_int4");
 }
 

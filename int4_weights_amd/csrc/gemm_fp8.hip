@@ -67,14 +67,19 @@ __device__ __forceinline__ void fp8_unit(const GemmArgs& a, const Unit& u, Fp8Sm
   const int ncol0 = u.n0 + C::kWcols * wv;  // this wave's first column
   const bool wave_on = ncol0 < N;
 
-  // weight bytes: uniform expert base + 32-bit lane offset (rows clamped for an idle wave)
+  // weight bytes: uniform expert base + 32-bit lane offset (columns clamped for an idle wave).
+  // Row-major: column n's K block at n*K + 128kb, halves 64 B apart.  Packed
+  // (moe_pack_weight_fp8): the 16-column block's K block is 2 KB at
+  // (kb*(N/16) + n/16)*2048, lane L's 16 bytes at 16L, halves 1 KB apart.
   const uint8_t* wbase = a.W + (int64_t)u.e * N * K;
+  const uint32_t wstep = a.wpacked ? (uint32_t)N * 128u : 128u;  // bytes per K block
+  const uint32_t whalf = a.wpacked ? 1024u : 64u;
   uint32_t woff[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     int n = ncol0 + 16 * cb + l16;
     if (n >= N) n = N - 1;
-    woff[cb] = (uint32_t)n * (uint32_t)K + 16u * lg;
+    woff[cb] = a.wpacked ? (uint32_t)(n / 16) * 2048u + 16u * lane : (uint32_t)n * (uint32_t)K + 16u * lg;
   }
   // this wave's 128-column block of weight scales for the whole unit -> LDS
   const float* sw_ptr = (const float*)a.SW + ((int64_t)u.e * NB + (wave_on ? ncol0 : 0) / 128) * KB;
@@ -109,11 +114,11 @@ __device__ __forceinline__ void fp8_unit(const GemmArgs& a, const Unit& u, Fp8Sm
   auto issue = [&](int ks_req, auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
     const int ks = min(ks_req, KB - 1);
-    const uint32_t koff = (uint32_t)ks * 128u;
+    const uint32_t koff = (uint32_t)ks * 128u, wkoff = (uint32_t)ks * wstep;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const v4i lo = *(const v4i*)(wbase + (woff[cb] + koff));
-      const v4i hi = *(const v4i*)(wbase + (woff[cb] + koff + 64u));
+      const v4i lo = *(const v4i*)(wbase + (woff[cb] + wkoff));
+      const v4i hi = *(const v4i*)(wbase + (woff[cb] + wkoff + whalf));
       wf[slot][cb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
 #pragma unroll
@@ -244,6 +249,7 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+template <bool PACKED>
 __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, Fp8TallSmem& sm, int wv, int lane) {
   const int l16 = lane & 15, lg = lane >> 4;
   const int K = a.K, N = a.N, KB = K / 128, NB = N / 128;
@@ -254,7 +260,10 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   const uint64_t wb = uniform_u64((uint64_t)(a.W + (int64_t)u.e * N * K));
   uint32_t wo[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) wo[c] = (uint32_t)(ncl + 16 * c + l16) * (uint32_t)K + 16u * lg;
+  for (int c = 0; c < 4; ++c)
+    wo[c] = PACKED ? (uint32_t)((ncl + 16 * c) / 16) * 2048u + 16u * lane
+                   : (uint32_t)(ncl + 16 * c + l16) * (uint32_t)K + 16u * lg;
+  const int wstep = uniform(PACKED ? 128 * N : 128);  // weight bytes per K block
   const uint64_t ab = uniform_u64((uint64_t)(a.A + (int64_t)u.row0 * K));
   uint32_t ao[kTApw];
 #pragma unroll
@@ -286,14 +295,24 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
   int ks, q, t, inc, m0v = 0;
   uint64_t sv;
-  asm volatile(MOE_FP8_TALL_LOOP
-               : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), [wo2] "+v"(wo[2]), [wo3] "+v"(wo[3]), [ao0] "+v"(ao[0]),
-                 [ao1] "+v"(ao[1]), [ao2] "+v"(ao[2]), [ao3] "+v"(ao[3]), [ao4] "+v"(ao[4]), [ao5] "+v"(ao[5]),
-                 [sep] "+v"(sep), [swp] "+v"(swp), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),
-                 [inc] "=&s"(inc), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v)
-               : [wb] "s"(wb), [ab] "s"(ab), [ma] "s"(ma), [alo] "v"(alo), [ahi] "v"(ahi), [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb), [rbe] "s"(rbe),
-                 [mrows] "s"(mrows), [won] "s"(wons), [l16] "v"(l16)
-               : "memory", "vcc", "exec", "scc", MOE_FP8_TALL_CLOBBERS);
+  if constexpr (PACKED)
+    asm volatile(MOE_FP8_TALL_LOOP_PACKED
+                 : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), [wo2] "+v"(wo[2]), [wo3] "+v"(wo[3]), [ao0] "+v"(ao[0]),
+                   [ao1] "+v"(ao[1]), [ao2] "+v"(ao[2]), [ao3] "+v"(ao[3]), [ao4] "+v"(ao[4]), [ao5] "+v"(ao[5]),
+                   [sep] "+v"(sep), [swp] "+v"(swp), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),
+                   [inc] "=&s"(inc), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v)
+                 : [wb] "s"(wb), [ab] "s"(ab), [ma] "s"(ma), [alo] "v"(alo), [ahi] "v"(ahi), [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb), [rbe] "s"(rbe),
+                   [mrows] "s"(mrows), [won] "s"(wons), [l16] "v"(l16), [wstep] "s"(wstep)
+                 : "memory", "vcc", "exec", "scc", MOE_FP8_TALL_CLOBBERS);
+  else
+    asm volatile(MOE_FP8_TALL_LOOP
+                 : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), [wo2] "+v"(wo[2]), [wo3] "+v"(wo[3]), [ao0] "+v"(ao[0]),
+                   [ao1] "+v"(ao[1]), [ao2] "+v"(ao[2]), [ao3] "+v"(ao[3]), [ao4] "+v"(ao[4]), [ao5] "+v"(ao[5]),
+                   [sep] "+v"(sep), [swp] "+v"(swp), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),
+                   [inc] "=&s"(inc), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v)
+                 : [wb] "s"(wb), [ab] "s"(ab), [ma] "s"(ma), [alo] "v"(alo), [ahi] "v"(ahi), [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb), [rbe] "s"(rbe),
+                   [mrows] "s"(mrows), [won] "s"(wons), [l16] "v"(l16), [wstep] "s"(wstep)
+                 : "memory", "vcc", "exec", "scc", MOE_FP8_TALL_CLOBBERS);
 }
 
 __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(const GemmArgs a) {
@@ -307,7 +326,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(const GemmArgs a)
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
     const Unit u = sched_unit<16 * kTRB>(a, sc, v);
-    fp8_unit_tall(a, u, sm, wv, lane);
+    if (a.wpacked) fp8_unit_tall<true>(a, u, sm, wv, lane);
+    else fp8_unit_tall<false>(a, u, sm, wv, lane);
   }
 }
 

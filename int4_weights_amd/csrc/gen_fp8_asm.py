@@ -61,6 +61,9 @@ V_DOFF = 108  # running output offset
 V_T = 110    # epilogue temporaries v110..v125
 
 
+HALF = 64  # byte offset of a column's second 64-K half (64 row-major, 1024 packed); set per program
+
+
 def issue_items(t):
     """The loads of one K block into ring slot t, as separate items (lists of
     instructions), and the offset update that follows them (offsets advance
@@ -69,12 +72,13 @@ def issue_items(t):
     for c in range(CB):
         w = wreg(t, c)
         items.append([f"global_load_dwordx4 v[{w}:{w + 3}], %[wo{c}], %[wb]"])
-        items.append([f"global_load_dwordx4 v[{w + 4}:{w + 7}], %[wo{c}], %[wb] offset:64"])
+        items.append([f"global_load_dwordx4 v[{w + 4}:{w + 7}], %[wo{c}], %[wb] offset:{HALF}"])
     for i in range(APW):
         items.append([f"s_add_u32 m0, %[ma], {t * SLOT_A + i * 1024}", "s_nop 0",
                       f"global_load_lds_dwordx4 %[ao{i}], %[ab]"])
-    upd = ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0"]
-    upd += [f"v_add_u32_e32 %[wo{c}], %[inc], %[wo{c}]" for c in range(CB)]
+    upd = ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0",
+           "s_cselect_b32 %[t], %[wstep], 0"]
+    upd += [f"v_add_u32_e32 %[wo{c}], %[t], %[wo{c}]" for c in range(CB)]
     upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(APW)]
     return items, upd
 
@@ -208,14 +212,16 @@ def clobbers():
 
 def main():
     out_path = sys.argv[1]
-    lines = program()
+    global HALF
     with open(out_path, "w") as f:
         f.write("// Generated by gen_fp8_asm.py -- do not edit.\n")
         f.write(f"// tall FP8 tile: S={S} CB={CB} RBMAX={RBMAX} APW={APW} OPS={OPS} WAIT={WAIT}\n")
-        f.write("#define MOE_FP8_TALL_LOOP \\\n")
-        for ln in lines:
-            f.write(f'  "{ln}\\n" \\\n')
-        f.write("  \"\"\n")
+        for name, half in (("MOE_FP8_TALL_LOOP", 64), ("MOE_FP8_TALL_LOOP_PACKED", 1024)):
+            HALF = half
+            f.write(f"#define {name} \\\n")
+            for ln in program():
+                f.write(f'  "{ln}\\n" \\\n')
+            f.write("  \"\"\n")
         f.write(f"#define MOE_FP8_TALL_CLOBBERS {clobbers()}\n")
         f.write(f"#define MOE_FP8_TALL_S {S}\n#define MOE_FP8_TALL_RB {RBMAX}\n#define MOE_FP8_TALL_APW {APW}\n")
         f.write(f"#define MOE_FP8_TALL_SLOT_A {SLOT_A}\n#define MOE_FP8_TALL_SAE_ROWS {SAE_ROWS}\n")

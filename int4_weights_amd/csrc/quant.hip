@@ -154,6 +154,32 @@ __global__ __launch_bounds__(256) void quant_weight_int4_kernel(const uint16_t* 
   }
 }
 
+// Fragment-packed FP8 weight order (the layout moe_pack_weight_fp8 defines):
+// one thread per 16-byte output chunk.  Output chunk r of an expert is lane
+// L = r % 64 of half h = (r / 64) % 2 of the 2-KB block b = r / 128, with
+// b = kb * (N/16) + cb; it holds bytes 128kb + 64h + 16(L/16) .. +15 of weight
+// column 16cb + L % 16.  Stores are contiguous; each load reads 16 bytes of a
+// row (a permutation, HBM-bound, run once when weights are prepared).
+__global__ __launch_bounds__(256) void pack_weight_fp8_kernel(const uint8_t* __restrict__ q, int64_t chunks,
+                                                              int64_t expert_chunks, int N, int K,
+                                                              uint8_t* __restrict__ out) {
+  const int ncb = N / 16;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = c / expert_chunks;
+    const int64_t r = c - e * expert_chunks;
+    const int64_t b = r >> 7;
+    const int qq = (int)(r & 127);
+    const int h = qq >> 6, L = qq & 63;
+    const int64_t kb = b / ncb;
+    const int cb = (int)(b - kb * ncb);
+    const int64_t n = 16 * cb + (L & 15);
+    const int64_t k = 128 * kb + 64 * h + 16 * (L >> 4);
+    const v4i v = *(const v4i*)(q + (e * N + n) * K + k);
+    *(v4i*)(out + c * 16) = v;
+  }
+}
+
 static int grid_for(int64_t work_items, int per_block, int cap) {
   int64_t g = (work_items + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -174,6 +200,15 @@ hipError_t launch_quant_weight_fp8(const uint16_t* w, int E, int N, int K, uint8
   if (nblocks == 0) return hipSuccess;
   if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
   quant_weight_fp8_kernel<<<(unsigned)nblocks, 256, 0, s>>>(w, N, K, q, sfw);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t* packed, hipStream_t s) {
+  const int64_t expert_chunks = (int64_t)N * K / 16;
+  const int64_t chunks = (int64_t)E * expert_chunks;
+  if (chunks == 0) return hipSuccess;
+  const int grid = grid_for(chunks, 256, device_info().cus * 8);
+  pack_weight_fp8_kernel<<<grid, 256, 0, s>>>(q, chunks, expert_chunks, N, K, packed);
   return hipGetLastError();
 }
 

@@ -17,8 +17,11 @@ class MoeFP8Layer:
     """FP8 block-scaled expert GEMM (1x128 activation scales, 128x128 weight scales)."""
 
     def __init__(self, w_codes: torch.Tensor, sfw: torch.Tensor, topk: int, max_tokens: int,
-                 layout: int = L.LAYOUT_CONTIGUOUS, align_or_max_m: int = 128, expected_m: int = 0):
+                 layout: int = L.LAYOUT_CONTIGUOUS, align_or_max_m: int = 128, expected_m: int = 0,
+                 weights_packed: bool = False):
+        """weights_packed: w_codes (and any weights passed to gemm()) are in moe_pack_weight_fp8 order."""
         E, N, K = w_codes.shape
+        self.wflag = L.WEIGHTS_PACKED if weights_packed else 0
         self.E, self.N, self.K, self.topk = E, N, K, topk
         self.w, self.sfw = w_codes, sfw
         self.layout, self.am = layout, align_or_max_m
@@ -69,8 +72,8 @@ class MoeFP8Layer:
         N = self.N if N is None else N
         K = self.K if K is None else K
         am = self.am if self.layout == L.LAYOUT_MASKED else self.rows_cap
-        L.moe_grouped_gemm_fp8(self.layout, A, SFA, w, sfw, D, self.counts, self.seg_offsets, self.E, am, N, K,
-                               self.expected_m)
+        L.moe_grouped_gemm_fp8(self.layout | self.wflag, A, SFA, w, sfw, D, self.counts, self.seg_offsets, self.E,
+                               am, N, K, self.expected_m)
 
     def combine(self, topk_weights, D=None, Z=None):
         """Weighted combine of packed rows D (default: this layer's GEMM output) into Z [T, D.shape[1]]."""

@@ -58,6 +58,7 @@ from .routing import (
 )
 from .gemm import grouped_gemm_fp8, grouped_gemm_int4, segments
 from .combine import combine
+from .layout import pack_weight_fp8, packed_offset, unpack_weight_fp8
 from .metrics import calc_diff, elementwise_ok, elementwise_excess
 
 __all__ = [
@@ -69,4 +70,5 @@ __all__ = [
     "DEV_ID_RANGE", "DEV_CAPACITY", "packed_rows_cap", "route", "pack_rows",
     "grouped_gemm_fp8", "grouped_gemm_int4", "segments", "combine",
     "calc_diff", "elementwise_ok", "elementwise_excess",
+    "pack_weight_fp8", "packed_offset", "unpack_weight_fp8",
 ]

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_constants_and_helpers(lib):
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     assert lib.moe_status_str(MOE_ERR_WORKSPACE) == b"workspace missing or too small"
     # worked example: 10 routes, 4 experts, 128-aligned -> at most 640 rows
     assert moe.moe_packed_rows_cap(5, 2, 4, 128) == 640
@@ -68,6 +68,12 @@ def test_host_validation_rejects_without_launching(lib):
     # moe_quant_weight_*
     assert lib.moe_quant_weight_fp8(_p(A16), 2, 100, 128, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
     assert lib.moe_quant_weight_int4(_p(A16), 2, 128, 64, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
+    # moe_pack_weight_fp8: shape, alignment, overlap
+    assert lib.moe_pack_weight_fp8(_p(A16), 2, 100, 128, _p(A16 << 4), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_pack_weight_fp8(_p(A16 + 8), 2, 128, 128, _p(A16 << 4), None) == MOE_ERR_ALIGN
+    assert lib.moe_pack_weight_fp8(None, 2, 128, 128, _p(A16 << 4), None) == MOE_ERR_NULL
+    assert lib.moe_pack_weight_fp8(_p(A16), 2, 128, 128, _p(A16 + 4096), None) == MOE_ERR_SHAPE  # overlap
+    assert lib.moe_pack_weight_fp8(None, 0, 128, 128, None, None) == MOE_OK  # no experts: no-op
 
     # moe_route_pack
     def rp(T=5, k=2, E=4, layout=0, am=128, rb=16, rows_cap=640, ws=None, wsb=0, payload=A16, ids=A16):
@@ -100,6 +106,10 @@ def test_host_validation_rejects_without_launching(lib):
     assert g8(A=0) == MOE_ERR_NULL
     assert g8(A=A16 + 8) == MOE_ERR_ALIGN
     assert g8(K=128 * 300) == MOE_ERR_UNSUPPORTED    # K above the supported maximum
+    assert g8(layout=0x10 | 7) == MOE_ERR_SHAPE      # the packed-weights flag does not make a layout valid
+    assert g8(layout=0x10, seg=0) == MOE_ERR_NULL    # packed contiguous still needs seg_offsets
+    assert lib.moe_grouped_gemm_int4(0x10, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), 4, 64, 128, 256, 0,
+                                     None) == MOE_ERR_SHAPE  # no packed order for 4-bit weights
     assert lib.moe_grouped_gemm_int4(0, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), 4, 64, 100, 256, 0,
                                      None) == MOE_ERR_UNSUPPORTED
     # moe_unpermute_combine

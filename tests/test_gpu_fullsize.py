@@ -52,9 +52,12 @@ def _rows_of(start: int, count: int, cap: int = 200):
 
 
 def _gpu_fp8_weights(cfg, N, K, stream, keep):
-    """Expert weights drawn on the GPU, quantised by the library; bf16 copies of `keep` on the host."""
+    """Expert weights drawn on the GPU, quantised by the library (row-major codes, checked against the
+    oracle) and packed by the library into the order the benchmark's layer reads; bf16 copies of
+    `keep` on the host."""
     E = cfg.E
     codes = torch.empty(E, N, K, dtype=torch.uint8, device=DEV)
+    packed = torch.empty(E, N, K, dtype=torch.uint8, device=DEV)
     sfw = torch.empty(E, N // 128, K // 128, dtype=torch.float32, device=DEV)
     kept = {}
     for e0 in range(0, E, 16):
@@ -65,8 +68,9 @@ def _gpu_fp8_weights(cfg, N, K, stream, keep):
             if e in keep:
                 kept[e] = u16(w[i])
         del w
+    moe.moe_pack_weight_fp8(codes, packed)
     torch.cuda.synchronize()
-    return codes, sfw, kept
+    return codes, sfw, kept, packed
 
 
 def _check_routing(layer, ids_np, E, layout_name, am):
@@ -102,14 +106,14 @@ def _fp8_layer_case(cfg, seed_tok):
     tok = seed_tok % T
     sample, counts = _sample_experts(ids_np, E, tok)
     x = synth.activations(cfg, T, K)
-    codes, sfw, kept = _gpu_fp8_weights(cfg, N, K, synth.STREAM_WEIGHTS, set(sample))
+    codes, sfw, kept, packed = _gpu_fp8_weights(cfg, N, K, synth.STREAM_WEIGHTS, set(sample))
     layout = moe.LAYOUT_MASKED if cfg.layout == "masked" else moe.LAYOUT_CONTIGUOUS
     am = cfg.max_m if cfg.layout == "masked" else cfg.align
-    layer = MoeFP8Layer(codes, sfw, k, T, layout, am, expected_m=max(1, T * k // E))
+    layer = MoeFP8Layer(packed, sfw, k, T, layout, am, expected_m=max(1, T * k // E), weights_packed=True)
     z = layer.forward(x.to(DEV), ids.to(DEV), tw.to(DEV))
     torch.cuda.synchronize()
     return dict(T=T, E=E, k=k, K=K, N=N, ids=ids_np, tw=tw.numpy(), tok=tok, sample=sample, x=x, codes=codes,
-                sfw=sfw, kept=kept, layer=layer, z=z, am=am)
+                sfw=sfw, kept=kept, layer=layer, z=z, am=am, packed=packed)
 
 
 def _check_quant_rows(layer, x_bits, tokens):
@@ -222,18 +226,18 @@ def test_full_size_qwen3_skewed_up_down_combine():
 
     fn = _oracle_fp8_weight_blocks(c, c["codes"], c["sfw"], c["kept"], c["N"], c["K"])
     _fp8_gemm_and_combine(c, r, a_of_tokens, layer.D, c["z"], fn, "fp8")
-    del c["codes"]
+    del c["codes"], c["packed"]
 
     # down-projection: independent N(0,1) activations over the packed rows, quantised in place
     Kd, Nd = cfg.K_down, cfg.N_down
-    dcodes, dsfw, dkept = _gpu_fp8_weights(cfg, Nd, Kd, synth.STREAM_WEIGHTS_DOWN, set(c["sample"]))
+    dcodes, dsfw, dkept, dpacked = _gpu_fp8_weights(cfg, Nd, Kd, synth.STREAM_WEIGHTS_DOWN, set(c["sample"]))
     a_down = synth.activations(cfg, layer.rows_cap, Kd, stream=synth.STREAM_ACT_DOWN, device=DEV)
     qd = torch.empty(layer.rows_cap, Kd, dtype=torch.uint8, device=DEV)
     sfd = torch.empty(layer.rows_cap, Kd // 128, dtype=torch.float32, device=DEV)
     Dd = torch.empty(layer.rows_cap, Nd, dtype=torch.bfloat16, device=DEV)
     Zd = torch.empty(c["T"], Nd, dtype=torch.bfloat16, device=DEV)
     moe.moe_quant_act(a_down, qd, sfd)
-    layer.gemm(A=qd, SFA=sfd, D=Dd, w=dcodes, sfw=dsfw, N=Nd, K=Kd)
+    layer.gemm(A=qd, SFA=sfd, D=Dd, w=dpacked, sfw=dsfw, N=Nd, K=Kd)
     layer.combine(torch.from_numpy(c["tw"]).to(DEV), D=Dd, Z=Zd)
     torch.cuda.synchronize()
 

@@ -35,17 +35,20 @@ def _fp8_case(seed, counts, N, K, layout, max_m=0, act_scale=1.0):
                 max_m=max_m, a=a_codes, sfa=sfa, w=w_codes, sfw=sfw)
 
 
-def _run_fp8(c, expected_m=0, D=None):
+def _run_fp8(c, expected_m=0, D=None, packed=False):
+    """packed: the weights go in the oracle's fragment-packed order, with MOE_WEIGHTS_PACKED."""
     A = torch.from_numpy(c["a"]).to(DEV)
     SFA = torch.from_numpy(c["sfa"]).to(DEV)
-    W = torch.from_numpy(c["w"]).to(DEV)
+    wbytes = oracle.pack_weight_fp8(c["w"]).reshape(c["w"].shape) if packed else c["w"]
+    W = torch.from_numpy(np.ascontiguousarray(wbytes)).to(DEV)
     SFW = torch.from_numpy(c["sfw"]).to(DEV)
     if D is None:
         D = torch.full((c["rows"], c["N"]), SENT_BITS, dtype=torch.int16, device=DEV).view(torch.bfloat16)
     counts = torch.from_numpy(c["counts"]).to(DEV)
     seg = torch.from_numpy(c["starts"].astype(np.int32)).to(DEV)
     am = c["max_m"] if c["layout"] == moe.LAYOUT_MASKED else c["rows"]
-    moe.moe_grouped_gemm_fp8(c["layout"], A, SFA, W, SFW, D, counts, seg, c["E"], am, c["N"], c["K"], expected_m)
+    layout = c["layout"] | (moe.WEIGHTS_PACKED if packed else 0)
+    moe.moe_grouped_gemm_fp8(layout, A, SFA, W, SFW, D, counts, seg, c["E"], am, c["N"], c["K"], expected_m)
     torch.cuda.synchronize()
     return D
 
@@ -60,34 +63,50 @@ def _check_fp8(c, D):
     assert (bits[~valid] == SENT_BITS).all()
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("expected_m", [0, 16, 64])
-def test_fp8_contiguous_ragged(expected_m):
+def test_fp8_contiguous_ragged(expected_m, packed):
     require_gpu()
     c = _fp8_case(1, [0, 1, 17, 130, 300], N=384, K=640, layout=moe.LAYOUT_CONTIGUOUS)
-    _check_fp8(c, _run_fp8(c, expected_m))
+    _check_fp8(c, _run_fp8(c, expected_m, packed=packed))
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("expected_m", [0, 16, 64])
-def test_fp8_masked_with_overfull_expert(expected_m):
+def test_fp8_masked_with_overfull_expert(expected_m, packed):
     require_gpu()
     c = _fp8_case(2, [0, 20, 3, 17, 1, 25], N=256, K=384, layout=moe.LAYOUT_MASKED, max_m=20)
-    _check_fp8(c, _run_fp8(c, expected_m))
+    _check_fp8(c, _run_fp8(c, expected_m, packed=packed))
 
 
-def test_fp8_masked_tall_segments():
-    """Masked layout with segments taller than one 128-row tile (the LDS-staged kernel)."""
+@pytest.mark.parametrize("packed", [False, True])
+def test_fp8_masked_tall_segments(packed):
+    """Masked layout with segments taller than one 192-row tile (the tall-tile kernel, several M chunks)."""
     require_gpu()
     c = _fp8_case(12, [150, 0, 200, 65], N=384, K=768, layout=moe.LAYOUT_MASKED, max_m=200)
     for em in (0, 200):
-        _check_fp8(c, _run_fp8(c, em))
+        _check_fp8(c, _run_fp8(c, em, packed=packed))
 
 
-def test_fp8_many_experts_long_k():
+@pytest.mark.parametrize("packed", [False, True])
+def test_fp8_many_experts_long_k(packed):
     require_gpu()
     rng = np.random.default_rng(3)
     counts = rng.integers(0, 40, size=33).tolist()
     c = _fp8_case(3, counts, N=512, K=2304, layout=moe.LAYOUT_CONTIGUOUS)
-    _check_fp8(c, _run_fp8(c, 24))
+    for em in (24, 128):
+        _check_fp8(c, _run_fp8(c, em, packed=packed))
+
+
+def test_pack_weight_fp8_bit_exact():
+    """The library's packed weight order equals the oracle's, byte for byte (two experts, ragged K blocks)."""
+    require_gpu()
+    rng = np.random.default_rng(13)
+    q = rng.integers(0, 256, size=(2, 384, 640), dtype=np.uint8)
+    out = torch.full(q.shape, 0x5A, dtype=torch.uint8, device=DEV)
+    moe.moe_pack_weight_fp8(torch.from_numpy(q).to(DEV), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().reshape(2, -1), oracle.pack_weight_fp8(q))
 
 
 def _int_codes(rng, shape, lo=-4, hi=4):
@@ -109,8 +128,8 @@ def test_fp8_small_integers_bit_exact():
     c = dict(E=E, N=N, K=K, rows=256, starts=starts, eff=counts, counts=counts, layout=moe.LAYOUT_CONTIGUOUS,
              max_m=0, a=a, sfa=np.ones((256, K // 128), np.float32), w=w, sfw=np.ones((E, N // 128, K // 128),
                                                                                           np.float32))
-    for em in (0, 16, 64):
-        D = _run_fp8(c, em)
+    for em, packed in ((0, False), (16, False), (64, False), (0, True), (16, True)):
+        D = _run_fp8(c, em, packed=packed)
         for e in range(E):
             s, n = int(starts[e]), int(counts[e])
             exact = av[s:s + n] @ wv[e].T
@@ -133,12 +152,15 @@ def test_fp8_scale_invariance_bit_exact():
     assert torch.equal((D0.float() * 4)[torch.from_numpy(valid).to(DEV)], D2.float()[torch.from_numpy(valid).to(DEV)])
 
 
-def test_fp8_determinism_20_runs():
+@pytest.mark.parametrize("packed", [False, True])
+def test_fp8_determinism_20_runs(packed):
     require_gpu()
     c = _fp8_case(6, [50, 0, 200, 7], N=256, K=1024, layout=moe.LAYOUT_CONTIGUOUS)
-    ref = _run_fp8(c)
+    ref = _run_fp8(c, packed=packed)
     for _ in range(20):
-        assert torch.equal(_run_fp8(c), ref)
+        assert torch.equal(_run_fp8(c, packed=packed), ref)
+    # the packed order changes the loads only, never the arithmetic
+    assert torch.equal(_run_fp8(c, packed=not packed), ref)
 
 
 # --------------------------------------------------------------------- INT4 --
