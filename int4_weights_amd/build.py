@@ -32,6 +32,7 @@ def flags() -> list[str]:
         # packed fp32 VALU ops stay off (the kernels use plain fp32 math)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",
+        *os.environ.get("MOE_EXTRA_CFLAGS", "").split(),
     ]
 
 

@@ -6,9 +6,9 @@
 // there are no atomics and no second launch (AsymGEMM README, "asymScheduler":
 // each workgroup owns fixed (N-tile, expert) pairs and reads its rows from the
 // offsets table; "K-outer, M-inner Loop": a weight tile is reused by every
-// token row of its expert).  Within an expert the units run N-tile-major with
-// the M-chunks of one N-tile adjacent, so concurrent workgroups that share a
-// weight panel or an activation chunk find it in the same L2.
+// token row of its expert).  Within an expert the units run in 2-D blocks of
+// M chunks x N-tiles (sched_unit), so concurrent workgroups that share a
+// weight slice or an activation slice find it in the same L2.
 //
 // XCD awareness: workgroup w runs on XCD w % 8 (round-robin dispatch), so the
 // unit list is cut into 8 contiguous slices and the G/8 workgroups of an XCD
@@ -22,6 +22,7 @@ namespace moe {
 
 constexpr int kBN = 256;       // columns per unit (4 waves x 64)
 constexpr int kXcds = 8;
+constexpr int kNGroup = 8;     // N-tiles per 2-D block of an expert's units
 
 struct Sched {
   int* up;  // [E+1] unit prefix (LDS)
@@ -68,7 +69,24 @@ __device__ inline Unit sched_unit(const GemmArgs& a, Sched s, int v) {
   expert_rows(a, e, rows, start);
   const int local = v - s.up[e];
   const int chunks = (rows + BM - 1) / BM;
-  const int nt = local / chunks, ch = local - nt * chunks;
+  // Within an expert the units run in 2-D blocks: groups of kNGroup N-tiles,
+  // every M chunk of the group before the next group, the N-tiles of one M
+  // chunk adjacent.  A window of 32 consecutive units (one XCD's workgroups)
+  // then covers about 4 M chunks x 8 N-tiles, sharing each activation slice
+  // 8 ways and each weight slice 4 ways in that XCD's L2.
+  const int ntiles = (a.N + kBN - 1) / kBN;
+  const int full = ntiles / kNGroup;            // complete groups
+  const int in_full = full * chunks * kNGroup;  // units in complete groups
+  int nt, ch;
+  if (local < in_full) {
+    const int g = local / (chunks * kNGroup), r = local - g * chunks * kNGroup;
+    ch = r / kNGroup;
+    nt = g * kNGroup + (r - ch * kNGroup);
+  } else {
+    const int gl = ntiles - full * kNGroup, r = local - in_full;
+    ch = r / gl;
+    nt = full * kNGroup + (r - ch * gl);
+  }
   Unit u;
   u.e = e;
   u.row0 = uniform(start + ch * BM);

@@ -3,27 +3,33 @@
 
 The loop is emitted as the text of one inline-asm statement (a C string
 literal, one line per instruction) that `gemm_fp8.hip` includes.  Writing it
-out instruction by instruction fixes what the compiler would otherwise decide
-for us: which physical registers hold the accumulators and the weight ring
-(no copies at the loop back edge), that the activation fragments of the next
-16-row block are read from LDS while the matrix instructions of the current
-block run, and exact vector-memory wait counts.
+out instruction by instruction fixes what the compiler would otherwise decide:
+which physical registers hold the accumulators and the weight ring (no copies
+at the loop back edge), that the activation fragments of the next 16-row block
+are read from LDS while the current block's matrix instructions run, that the
+loads are spread between the matrix instructions instead of issued as one
+burst, and exact vector-memory wait counts.
 
-Loads are interleaved with the matrix instructions (one load after each row
-block) so the single wave of each SIMD never stalls on a burst of issues.
+Unit tile: up to 192 rows x 256 columns, one 128-wide K block per step,
+v_mfma_scale_f32_16x16x128_f8f6f4 with the power-of-two scales passed as E8M0
+exponents.  Each wave owns 64 columns (4 column blocks of 16).  Two shapes:
 
-Tile: 4 waves x 64 columns (4 column blocks of 16) x up to 192 rows (12 row
-blocks of 16), one 128-wide K block per step, v_mfma_scale_f32_16x16x128_f8f6f4
-with the power-of-two scales passed as E8M0 exponents.  The row scales of the
-unit are staged in LDS as exponent bytes [K block][row] before the loop, so a
-step reads one byte per lane and issues no per-row scale loads.
+  NWR = 1: 4 waves, each all 12 row blocks (1 wave per SIMD, 512 registers);
+  NWR = 2: 8 waves, two per 64-column group, taking the even and the odd row
+           blocks (2 waves per SIMD, so one multiplies while the other waits;
+           256 registers each: the weight ring lives in AGPRs).
+
+The unit's row scales are staged in LDS as exponent bytes [K block][row]
+before the loop, so a step reads one byte per lane for each row block.
 
 Register map (physical, listed as clobbers of the asm statement):
-  a[0:191]    accumulators, block (j, c) at a[16j + 4c : 16j + 4c + 3]
-  a[192:207]  activation fragments, two buffers of 8
-  v[128:255]  weight ring: S = 4 slots x 4 column blocks x 8 registers
-  v[96:127]   addresses of the activation fragments per slot, scale exponents,
-              epilogue temporaries
+  NWR = 1: a[0:191] accumulators (block j, column block c at a[16j + 4c]),
+           a[192:207] activation fragments (2 buffers), v[256-32S:255] weight
+           ring (S slots x 4 column blocks x 8), v[224-32S:255-32S] addresses,
+           scale exponents, epilogue temporaries.
+  NWR = 2: a[0:95] accumulators, a[96:111] activation fragments,
+           a[112:112+32S-1] weight ring, v[40-2S:47] addresses, scale exponents,
+           epilogue temporaries.
 
 Usage: python gen_fp8_asm.py OUT.inc
 """
@@ -32,98 +38,107 @@ from __future__ import annotations
 
 import sys
 
-S = 4            # ring depth (K blocks): S - 1 in flight while one is multiplied
-CB = 4           # 16-column blocks per wave
-RBMAX = 12       # 16-row blocks per unit at most
-APW = 6          # 1-KB activation copies per wave per K block (192 rows x 128 B / 4 waves)
-SLOT_A = RBMAX * 16 * 128   # bytes of one activation slot in LDS
-SAE_ROWS = RBMAX * 16        # bytes per K block of the staged row-scale exponents
-OPS = 2 * CB + APW           # vector-memory instructions per wave per K block
-WAIT = OPS * (S - 2)         # outstanding after the block about to be used has landed
+CB = 4            # 16-column blocks per wave
+ROWS = 192        # rows per unit at most
+SLOT_A = ROWS * 128   # bytes of one activation slot in LDS
+SAE_ROWS = ROWS        # bytes per K block of the staged row-scale exponents
 
 
-def acc(j, c):
-    return 16 * j + 4 * c
+class Cfg:
+    def __init__(self, nwr: int, S: int, name: str):
+        self.nwr, self.S, self.name = nwr, S, name
+        self.nw = 4 * nwr                        # waves per workgroup
+        self.rbw = ROWS // 16 // nwr             # row blocks per wave at most
+        self.apw = ROWS // 8 // self.nw          # 1-KB activation copies per wave per K block
+        self.ops = 2 * CB + self.apw             # vector-memory instructions per wave per K block
+        self.wait = self.ops * (S - 2)           # outstanding once the block about to be used has landed
+        if nwr == 1:
+            self.wbase = 256 - 32 * S            # weight ring in VGPRs
+            self.wreg_prefix = "v"
+            self.buf0 = 192
+            self.v_alo = self.wbase - 32
+        else:
+            self.wbase = 112                     # weight ring in AGPRs
+            self.wreg_prefix = "a"
+            self.buf0 = 96
+            self.v_alo = 48 - (2 * S + 8)        # addresses, exponents, output offset, 4 temporaries below v48
+        self.v_swe = self.v_alo + 2 * S          # weight-scale exponent
+        self.v_sae = self.v_swe + 1              # row-scale exponents, 2 buffers
+        self.v_doff = self.v_swe + 3             # running output offset
+        self.v_t = self.v_swe + 4                # epilogue temporaries
+        self.n_t = 16 if nwr == 1 else 4
+        if nwr == 2:
+            assert self.v_t + self.n_t <= 48, "8-wave map must stay below v48"
+        else:
+            assert self.v_t + self.n_t <= self.wbase
+        self.agpr_top = self.wbase + 32 * S if nwr == 2 else 208
+
+    def acc(self, j, c):
+        return 16 * j + 4 * c
+
+    def buf(self, b):
+        return self.buf0 + 8 * b
 
 
-def wreg(s, c):
-    return 128 + 32 * s + 8 * c
+def wrange(cfg, s, c, lo, hi):
+    r = cfg.wbase + 32 * s + 8 * c
+    return f"{cfg.wreg_prefix}[{r + lo}:{r + hi}]"
 
 
-def buf(b):
-    return 192 + 8 * b
-
-
-V_ALO = 96   # v96 + 2s: fragment read address (low chunks) of slot s; v97 + 2s high chunks
-V_SWE = 104  # weight-scale exponent of the current K block
-V_SAE = 105  # row-scale exponents, buffers 0 and 1 (v105, v106)
-V_DOFF = 108  # running output offset
-V_T = 110    # epilogue temporaries v110..v125
-
-
-HALF = 64  # byte offset of a column's second 64-K half (64 row-major, 1024 packed); set per program
-
-
-def issue_items(t):
-    """The loads of one K block into ring slot t, as separate items (lists of
-    instructions), and the offset update that follows them (offsets advance
-    unless the next block would be past the last one)."""
+def issue_items(cfg, t, half):
+    """The loads of one K block into ring slot t, as separate items, and the offset update after them
+    (offsets advance unless the next block would be past the last one)."""
     items = []
     for c in range(CB):
-        w = wreg(t, c)
-        items.append([f"global_load_dwordx4 v[{w}:{w + 3}], %[wo{c}], %[wb]"])
-        items.append([f"global_load_dwordx4 v[{w + 4}:{w + 7}], %[wo{c}], %[wb] offset:{HALF}"])
-    for i in range(APW):
+        items.append([f"global_load_dwordx4 {wrange(cfg, t, c, 0, 3)}, %[wo{c}], %[wb]"])
+        items.append([f"global_load_dwordx4 {wrange(cfg, t, c, 4, 7)}, %[wo{c}], %[wb] offset:{half}"])
+    for i in range(cfg.apw):
         items.append([f"s_add_u32 m0, %[ma], {t * SLOT_A + i * 1024}", "s_nop 0",
                       f"global_load_lds_dwordx4 %[ao{i}], %[ab]"])
     upd = ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0",
            "s_cselect_b32 %[t], %[wstep], 0"]
     upd += [f"v_add_u32_e32 %[wo{c}], %[t], %[wo{c}]" for c in range(CB)]
-    upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(APW)]
+    upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(cfg.apw)]
     return items, upd
 
 
-def issue(t):
-    items, upd = issue_items(t)
-    return [ins for it in items for ins in it] + upd
-
-
-def compute(s, t):
-    """Multiply K block s of the ring, row blocks 0 .. rbe-1, and issue the loads of
-    ring slot t on the way: one load after each row block's matrix instructions
-    (the rest after the last block), so a wave never sits in a burst of load
-    issues while its matrix unit idles.  The next block's activation fragments
-    are read from LDS while the current block's matrix instructions run."""
-    items, upd = issue_items(t)
-    lo, hi = V_ALO + 2 * s, V_ALO + 2 * s + 1
+def compute(cfg, s, t, half):
+    """Multiply K block s of the ring (this wave's row blocks 0 .. rbe-1) and issue the loads of ring
+    slot t on the way, one after each row block (the rest after the last)."""
+    items, upd = issue_items(cfg, t, half)
+    lo, hi = cfg.v_alo + 2 * s, cfg.v_alo + 2 * s + 1
+    aoff = 2048 * cfg.nwr      # LDS distance between this wave's consecutive row blocks
+    soff = 16 * cfg.nwr        # same for the staged row-scale exponents
+    b0 = cfg.buf(0)
     out = [
-        f"ds_read_b32 v{V_SWE}, %[swp]",
+        f"ds_read_b32 v{cfg.v_swe}, %[swp]",
         "v_add_u32_e32 %[swp], 4, %[swp]",
-        f"ds_read_b128 a[{buf(0)}:{buf(0) + 3}], v{lo}",
-        f"ds_read_b128 a[{buf(0) + 4}:{buf(0) + 7}], v{hi}",
-        f"ds_read_u8 v{V_SAE}, %[sep]",
+        f"ds_read_b128 a[{b0}:{b0 + 3}], v{lo}",
+        f"ds_read_b128 a[{b0 + 4}:{b0 + 7}], v{hi}",
+        f"ds_read_u8 v{cfg.v_sae}, %[sep]",
         "s_waitcnt lgkmcnt(0)",
-        f"v_lshrrev_b32_e32 v{V_SWE}, 23, v{V_SWE}",
+        f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swe}",
     ]
     k = 0
-    for j in range(RBMAX):
+    for j in range(cfg.rbw):
         b, bn = j % 2, 1 - j % 2
         out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 5f"]  # no row block j: only its load item
-        if j + 1 < RBMAX:
+        if j + 1 < cfg.rbw:
+            bb = cfg.buf(bn)
             out += [
                 f"s_cmp_le_u32 %[rbe], {j + 1}",
                 "s_cbranch_scc1 3f",
-                f"ds_read_b128 a[{buf(bn)}:{buf(bn) + 3}], v{lo} offset:{(j + 1) * 2048}",
-                f"ds_read_b128 a[{buf(bn) + 4}:{buf(bn) + 7}], v{hi} offset:{(j + 1) * 2048}",
-                f"ds_read_u8 v{V_SAE + bn}, %[sep] offset:{16 * (j + 1)}",
+                f"ds_read_b128 a[{bb}:{bb + 3}], v{lo} offset:{(j + 1) * aoff}",
+                f"ds_read_b128 a[{bb + 4}:{bb + 7}], v{hi} offset:{(j + 1) * aoff}",
+                f"ds_read_u8 v{cfg.v_sae + bn}, %[sep] offset:{soff * (j + 1)}",
                 "3:",
             ]
         out.append("s_nop 1")
         for c in range(CB):
-            a0 = acc(j, c)
-            w = wreg(s, c)
-            out.append(f"v_mfma_scale_f32_16x16x128_f8f6f4 a[{a0}:{a0 + 3}], v[{w}:{w + 7}], "
-                       f"a[{buf(b)}:{buf(b) + 7}], a[{a0}:{a0 + 3}], v{V_SWE}, v{V_SAE + b} op_sel_hi:[0,0,0]")
+            a0 = cfg.acc(j, c)
+            bb = cfg.buf(b)
+            out.append(f"v_mfma_scale_f32_16x16x128_f8f6f4 a[{a0}:{a0 + 3}], {wrange(cfg, s, c, 0, 7)}, "
+                       f"a[{bb}:{bb + 7}], a[{a0}:{a0 + 3}], v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
         out += ["s_waitcnt lgkmcnt(0)", "5:"]
         if k < len(items):
             out += items[k]
@@ -135,13 +150,9 @@ def compute(s, t):
     return out
 
 
-def step(s, last):
-    out = [
-        f"s_waitcnt vmcnt({WAIT})",
-        "s_waitcnt lgkmcnt(0)",
-        "s_barrier",
-    ]
-    out += compute(s, (s + S - 1) % S)
+def step(cfg, s, last, half):
+    out = [f"s_waitcnt vmcnt({cfg.wait})", "s_waitcnt lgkmcnt(0)", "s_barrier"]
+    out += compute(cfg, s, (s + cfg.S - 1) % cfg.S, half)
     out += [
         "s_add_u32 %[ks], %[ks], 1",
         "s_cmp_lt_u32 %[ks], %[kb]",
@@ -150,7 +161,8 @@ def step(s, last):
     return out
 
 
-def epilogue():
+def epilogue(cfg):
+    """bf16 stores of this wave's rows (rows >= mrows masked off); %[t] counts the rows left."""
     out = [
         "9:",
         "s_waitcnt vmcnt(0)",
@@ -161,70 +173,96 @@ def epilogue():
         "s_cmp_eq_u32 %[won], 0",
         "s_cbranch_scc1 7f",
         "s_mov_b32 %[t], %[mrows]",
-        f"v_mov_b32_e32 v{V_DOFF}, %[doff]",
+        f"v_mov_b32_e32 v{cfg.v_doff}, %[doff]",
     ]
-    for j in range(RBMAX):
+    T = cfg.v_t
+    for j in range(cfg.rbw):
         out += [
             f"s_cmp_le_u32 %[rbe], {j}",
             "s_cbranch_scc1 7f",
             "v_cmp_gt_i32_e32 vcc, %[t], %[l16]",
             "s_and_saveexec_b64 %[sv], vcc",
         ]
-        for c in range(CB):
-            for r in range(4):
-                out.append(f"v_accvgpr_read_b32 v{V_T + 4 * c + r}, a{acc(j, c) + r}")
-        out.append("s_nop 1")
-        for c in range(CB):
-            out.append(f"v_cvt_pk_bf16_f32 v{V_ALO + 2 * c}, v{V_T + 4 * c}, v{V_T + 4 * c + 1}")
-            out.append(f"v_cvt_pk_bf16_f32 v{V_ALO + 2 * c + 1}, v{V_T + 4 * c + 2}, v{V_T + 4 * c + 3}")
-        out.append("s_nop 1")
-        for c in range(CB):
-            out.append(f"global_store_dwordx2 v{V_DOFF}, v[{V_ALO + 2 * c}:{V_ALO + 2 * c + 1}], %[db] offset:{32 * c}")
+        if cfg.n_t >= 16:
+            for c in range(CB):
+                for r in range(4):
+                    out.append(f"v_accvgpr_read_b32 v{T + 4 * c + r}, a{cfg.acc(j, c) + r}")
+            out.append("s_nop 1")
+            for c in range(CB):
+                p = cfg.v_alo + 2 * c
+                out.append(f"v_cvt_pk_bf16_f32 v{p}, v{T + 4 * c}, v{T + 4 * c + 1}")
+                out.append(f"v_cvt_pk_bf16_f32 v{p + 1}, v{T + 4 * c + 2}, v{T + 4 * c + 3}")
+            out.append("s_nop 1")
+            for c in range(CB):
+                p = cfg.v_alo + 2 * c
+                out.append(f"global_store_dwordx2 v{cfg.v_doff}, v[{p}:{p + 1}], %[db] offset:{32 * c}")
+        else:
+            # one column block at a time through 4 temporaries and a packed pair; a store must have
+            # read the pair before the next conversion overwrites it (s_waitcnt vmcnt(0))
+            for c in range(CB):
+                for r in range(4):
+                    out.append(f"v_accvgpr_read_b32 v{T + r}, a{cfg.acc(j, c) + r}")
+                out.append("s_nop 1")
+                out.append(f"v_cvt_pk_bf16_f32 v{cfg.v_alo}, v{T}, v{T + 1}")
+                out.append(f"v_cvt_pk_bf16_f32 v{cfg.v_alo + 1}, v{T + 2}, v{T + 3}")
+                out.append("s_nop 1")
+                out.append(f"global_store_dwordx2 v{cfg.v_doff}, v[{cfg.v_alo}:{cfg.v_alo + 1}], %[db] "
+                           f"offset:{32 * c}")
+                out.append("s_waitcnt vmcnt(0)")
         out += [
             "s_mov_b64 exec, %[sv]",
-            f"v_add_u32_e32 v{V_DOFF}, %[dstep], v{V_DOFF}",
-            "s_sub_i32 %[t], %[t], 16",
+            f"v_add_u32_e32 v{cfg.v_doff}, %[dstep], v{cfg.v_doff}",
+            f"s_sub_i32 %[t], %[t], {16 * cfg.nwr}",
         ]
     out.append("7:")
     return out
 
 
-def program():
-    out = [f"v_mov_b32_e32 v{V_ALO}, %[alo]", f"v_mov_b32_e32 v{V_ALO + 1}, %[ahi]"]
+def program(cfg, half):
+    S = cfg.S
+    out = [f"v_mov_b32_e32 v{cfg.v_alo}, %[alo]", f"v_mov_b32_e32 v{cfg.v_alo + 1}, %[ahi]"]
     for s in range(1, S):
-        out.append(f"v_add_u32_e32 v{V_ALO + 2 * s}, {s * SLOT_A}, %[alo]")
-        out.append(f"v_add_u32_e32 v{V_ALO + 2 * s + 1}, {s * SLOT_A}, %[ahi]")
-    out += [f"v_accvgpr_write_b32 a{r}, 0" for r in range(acc(RBMAX, 0))]
+        out.append(f"v_add_u32_e32 v{cfg.v_alo + 2 * s}, {s * SLOT_A}, %[alo]")
+        out.append(f"v_add_u32_e32 v{cfg.v_alo + 2 * s + 1}, {s * SLOT_A}, %[ahi]")
+    out += [f"v_accvgpr_write_b32 a{r}, 0" for r in range(cfg.acc(cfg.rbw, 0))]
     out += ["s_mov_b32 %[q], 0"]
     for t in range(S - 1):
-        out += issue(t)
+        items, upd = issue_items(cfg, t, half)
+        out += [ins for it in items for ins in it] + upd
     out += ["s_mov_b32 %[ks], 0", "8:"]
     for s in range(S):
-        out += step(s, s == S - 1)
-    out += epilogue()
+        out += step(cfg, s, s == S - 1, half)
+    out += epilogue(cfg)
     return out
 
 
-def clobbers():
-    regs = [f'"v{r}"' for r in range(96, 256)] + [f'"a{r}"' for r in range(0, 208)]
+def clobbers(cfg):
+    if cfg.nwr == 1:
+        regs = [f'"v{r}"' for r in range(cfg.v_alo, 256)] + [f'"a{r}"' for r in range(0, 208)]
+    else:
+        regs = [f'"v{r}"' for r in range(cfg.v_alo, 48)] + [f'"a{r}"' for r in range(0, cfg.agpr_top)]
     return ", ".join(regs)
+
+
+CONFIGS = [Cfg(1, 3, "TALL4"), Cfg(2, 3, "TALL8")]
 
 
 def main():
     out_path = sys.argv[1]
-    global HALF
     with open(out_path, "w") as f:
         f.write("// Generated by gen_fp8_asm.py -- do not edit.\n")
-        f.write(f"// tall FP8 tile: S={S} CB={CB} RBMAX={RBMAX} APW={APW} OPS={OPS} WAIT={WAIT}\n")
-        for name, half in (("MOE_FP8_TALL_LOOP", 64), ("MOE_FP8_TALL_LOOP_PACKED", 1024)):
-            HALF = half
-            f.write(f"#define {name} \\\n")
-            for ln in program():
-                f.write(f'  "{ln}\\n" \\\n')
-            f.write("  \"\"\n")
-        f.write(f"#define MOE_FP8_TALL_CLOBBERS {clobbers()}\n")
-        f.write(f"#define MOE_FP8_TALL_S {S}\n#define MOE_FP8_TALL_RB {RBMAX}\n#define MOE_FP8_TALL_APW {APW}\n")
-        f.write(f"#define MOE_FP8_TALL_SLOT_A {SLOT_A}\n#define MOE_FP8_TALL_SAE_ROWS {SAE_ROWS}\n")
+        f.write(f"#define MOE_FP8_TALL_ROWS {ROWS}\n#define MOE_FP8_TALL_SLOT_A {SLOT_A}\n"
+                f"#define MOE_FP8_TALL_SAE_ROWS {SAE_ROWS}\n")
+        for cfg in CONFIGS:
+            f.write(f"// {cfg.name}: {cfg.nw} waves, ring {cfg.S}, {cfg.rbw} row blocks per wave, "
+                    f"{cfg.apw} activation copies and {cfg.ops} loads per wave per K block, wait {cfg.wait}\n")
+            for suffix, half in (("", 64), ("_PACKED", 1024)):
+                f.write(f"#define MOE_FP8_{cfg.name}_LOOP{suffix} \\\n")
+                for ln in program(cfg, half):
+                    f.write(f'  "{ln}\\n" \\\n')
+                f.write("  \"\"\n")
+            f.write(f"#define MOE_FP8_{cfg.name}_CLOBBERS {clobbers(cfg)}\n")
+            f.write(f"#define MOE_FP8_{cfg.name}_S {cfg.S}\n#define MOE_FP8_{cfg.name}_APW {cfg.apw}\n")
 
 
 if __name__ == "__main__":
