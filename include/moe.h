@@ -62,9 +62,9 @@ enum {
 
 enum { MOE_LAYOUT_CONTIGUOUS = 0, MOE_LAYOUT_MASKED = 1 };
 
-/* Flag ORed into the layout argument of moe_grouped_gemm_fp8: the weight
- * codes are in the fragment-packed order written by moe_pack_weight_fp8
- * instead of row-major [E, N, K]. */
+/* Flag ORed into the layout argument of moe_grouped_gemm_fp8 (and _int4): the
+ * weights are in the fragment-packed order written by moe_pack_weight_fp8
+ * (moe_pack_weight_int4) instead of row-major [E, N, K] ([E, N, K/2]). */
 enum { MOE_WEIGHTS_PACKED = 0x10 };
 
 enum { MOE_MAX_EXPERTS = 1024, MOE_MAX_TOPK = 64 };
@@ -129,6 +129,17 @@ moe_status moe_quant_weight_fp8(const uint16_t* w, int E, int N, int K,
  *   16-byte aligned, and must not overlap.  Requires N % 128 == 0, K % 128 == 0.
  *   The scales (sfw) are unchanged. */
 moe_status moe_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t* packed, void* stream);
+
+/* moe_pack_weight_int4: the same idea for 4-bit weights (MatMulNBits layout in,
+ * fragment order out; ONNX Runtime "MatMulNBits -- CUDA Operator
+ * Documentation" describes prepacked weights for its fpA_intB path).  A pure
+ * byte permutation; the fp16 scales are unchanged.
+ *   For expert e, group g (128 K values = 64 bytes of a column), 16-column
+ *   block cb, lane L = c16 + 16*h (c16 in [0,16), h in [0,4)), byte j:
+ *     packed[e*N*K/2 + (g*(N/16) + cb)*1024 + L*16 + j] = q4[e][16*cb + c16][64*g + 16*h + j]
+ *   q4 and packed are [E*N*K/2] bytes, 16-byte aligned, not overlapping.
+ *   Requires N % 128 == 0, K % 128 == 0. */
+moe_status moe_pack_weight_int4(const uint8_t* q4, int E, int N, int K, uint8_t* packed, void* stream);
 
 /* moe_quant_weight_int4: group-128 4-bit weight quantisation in the
  * MatMulNBits layout (ONNX Runtime "MatMulNBits -- CUDA Operator
@@ -227,7 +238,8 @@ moe_status moe_grouped_gemm_fp8(int layout,
  *     A   [rows, K] bf16,  W4 [E, N, K/2] (low nibble = even k),
  *     S16 [E, N, K/128] fp16,  D [rows, N] bf16.
  *   Layout, counts, seg_offsets, expected_m and alignment as for
- *   moe_grouped_gemm_fp8. */
+ *   moe_grouped_gemm_fp8; layout | MOE_WEIGHTS_PACKED: W4 in the order written
+ *   by moe_pack_weight_int4. */
 moe_status moe_grouped_gemm_int4(int layout,
                                  const uint16_t* A, const uint8_t* W4,
                                  const uint16_t* S16, uint16_t* D,

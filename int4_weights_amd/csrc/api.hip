@@ -119,6 +119,21 @@ moe_status moe_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t* p
   return hip_status(launch_pack_weight_fp8(q, E, N, K, packed, (hipStream_t)stream), "moe_pack_weight_fp8");
 }
 
+moe_status moe_pack_weight_int4(const uint8_t* q4, int E, int N, int K, uint8_t* packed, void* stream) {
+  g_err[0] = 0;
+  if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_pack_weight_int4: E=%d N=%d K=%d", E, N, K);
+  if (N % 128 || K % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_weight_int4: N=%d and K=%d must be multiples of 128", N, K);
+  if ((int64_t)N * K / 2 > 0xffffffffll) return fail(MOE_ERR_UNSUPPORTED, "moe_pack_weight_int4: one expert exceeds 4 GiB");
+  if (E == 0) return MOE_OK;
+  if (!q4 || !packed) return fail(MOE_ERR_NULL, "moe_pack_weight_int4: null pointer");
+  if (!aligned(q4, 16) || !aligned(packed, 16))
+    return fail(MOE_ERR_ALIGN, "moe_pack_weight_int4: q4 and packed must be 16-byte aligned");
+  const int64_t bytes = (int64_t)E * N * (K / 2);
+  if (q4 < packed + bytes && packed < q4 + bytes) return fail(MOE_ERR_SHAPE, "moe_pack_weight_int4: q4 and packed overlap");
+  return hip_status(launch_pack_weight_int4(q4, E, N, K, packed, (hipStream_t)stream), "moe_pack_weight_int4");
+}
+
 moe_status moe_quant_weight_int4(const uint16_t* w, int E, int N, int K, uint8_t* q4, uint16_t* s16, void* stream) {
   g_err[0] = 0;
   if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_quant_weight_int4: E=%d N=%d K=%d", E, N, K);
@@ -252,6 +267,8 @@ moe_status moe_grouped_gemm_int4(int layout, const uint16_t* A, const uint8_t* W
                                  const int32_t* counts, const int32_t* seg_offsets, int E, int64_t rows_cap_or_max_m,
                                  int N, int K, int expected_m, void* stream) {
   g_err[0] = 0;
+  const int wpacked = (layout & MOE_WEIGHTS_PACKED) ? 1 : 0;
+  layout &= ~MOE_WEIGHTS_PACKED;
   moe_status st = check_gemm("moe_grouped_gemm_int4", layout, A, W4, S16, D, counts, seg_offsets, E,
                              rows_cap_or_max_m, N, K);
   if (st) return st;
@@ -270,7 +287,7 @@ moe_status moe_grouped_gemm_int4(int layout, const uint16_t* A, const uint8_t* W
   a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
   a.N = N;
   a.K = K;
-  a.wpacked = 0;
+  a.wpacked = wpacked;
   return hip_status(launch_gemm_int4(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_int4");
 }
 

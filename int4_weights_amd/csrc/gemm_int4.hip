@@ -34,11 +34,15 @@ struct I4Cfg {
   static constexpr int BM = 16 * RB;
   static constexpr int kApw = RB;            // 16-byte A loads per lane per stage (4 rows of 256 B)
   static constexpr int kAStage = BM * 256;   // bytes per LDS slot
+  // K groups whose scales are held in LDS at once (a power of two); a longer K
+  // restages them every kScG groups
+  static constexpr int kScG = RB == 1 ? kMaxKBlocks : kMaxKBlocks / 2;
 };
 
 template <int RB, int S>
 struct I4Smem {
   uint8_t a[2][I4Cfg<RB, S>::kAStage];
+  uint16_t sc[I4Cfg<RB, S>::kScG][kBN];  // group scales (fp16) of the unit, [group mod kScG][column of the N tile]
 };
 
 __device__ __forceinline__ v8bf as_bf(const v4i& x) { return __builtin_bit_cast(v8bf, x); }
@@ -51,16 +55,49 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
   const int ncol0 = u.n0 + 64 * wv;
   const bool wave_on = ncol0 < N;
 
+  // 4-bit weights.  Row-major: column n's group g is 64 bytes at n*K/2 + 64g.
+  // Packed (moe_pack_weight_int4): the 16-column block's group is 1 KB at
+  // (g*(N/16) + n/16)*1024, lane L's 16 bytes at 16L.
   const uint8_t* wbase = a.W + (int64_t)u.e * N * (K / 2);
-  const uint16_t* sbase = (const uint16_t*)a.SW + (int64_t)u.e * N * KG;
-  uint32_t woff[4], soff[4];
+  const uint32_t wstep = a.wpacked ? (uint32_t)N * 64u : 64u;  // bytes per K group
+  uint32_t woff[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     int n = ncol0 + 16 * cb + l16;
     if (n >= N) n = N - 1;
-    woff[cb] = (uint32_t)n * (uint32_t)(K / 2) + 16u * lg;
-    soff[cb] = (uint32_t)n * (uint32_t)KG;
+    woff[cb] = a.wpacked ? (uint32_t)(n / 16) * 1024u + 16u * lane : (uint32_t)n * (uint32_t)(K / 2) + 16u * lg;
   }
+  // the unit's group scales: its columns' rows of S16 are one contiguous block
+  // (kBN x KG halves); groups gb .. gb+kScG-1 are staged into LDS
+  // [group][column] with a batch of coalesced loads
+  const uint16_t* sblk = (const uint16_t*)a.SW + ((int64_t)u.e * N + u.n0) * KG;
+  const int scols = min(kBN, N - u.n0);
+  auto stage_scales = [&](int gb) {
+    const int cnt = min(C::kScG, KG - gb), total = scols * cnt;
+    const float inv = 1.0f / (float)cnt;
+    for (int base = threadIdx.x; base < total; base += 256 * 16) {
+      uint16_t v[16];
+      int col[16], grp[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int idx = base + 256 * i;
+        int c = (int)(((float)idx + 0.5f) * inv);  // idx / cnt, corrected to be exact below
+        int g = idx - c * cnt;
+        if (g < 0) { --c; g += cnt; }
+        if (g >= cnt) { ++c; g -= cnt; }
+        col[i] = c;
+        grp[i] = g;
+        v[i] = idx < total ? sblk[(int64_t)c * KG + gb + g] : (uint16_t)0;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (base + 256 * i < total) sm.sc[grp[i]][col[i]] = v[i];
+    }
+  };
+  stage_scales(0);  // the previous unit ended with a barrier
+  int scol[4];  // this lane's columns within the N tile (clamped for an idle wave)
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) scol[cb] = min(64 * wv + 16 * cb + l16, min(kBN, N - u.n0) - 1);
   const uint8_t* abase = a.A + (int64_t)u.row0 * K * 2;
   uint32_t aoff[C::kApw];
 #pragma unroll
@@ -72,7 +109,6 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
   }
 
   v4i wq[S][4];
-  uint32_t sc[S][4];
   v4i ar[S][C::kApw];
   v4f acc[RB][4];
 #pragma unroll
@@ -84,9 +120,7 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
     constexpr int slot = decltype(slot_c)::value;
     const int ks = min(ks_req, KG - 1);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) wq[slot][cb] = *(const v4i*)(wbase + (woff[cb] + (uint32_t)ks * 64u));
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) sc[slot][cb] = sbase[soff[cb] + ks];
+    for (int cb = 0; cb < 4; ++cb) wq[slot][cb] = *(const v4i*)(wbase + (woff[cb] + (uint32_t)ks * wstep));
 #pragma unroll
     for (int i = 0; i < C::kApw; ++i) ar[slot][i] = *(const v4i*)(abase + (aoff[i] + (uint32_t)ks * 256u));
   };
@@ -103,6 +137,12 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
 #pragma unroll
   for (int i = 0; i < 4; ++i) aoff_rd[i] = l16 * 256 + 16 * ((4 * lg + i) ^ l16);
   const v4i kNeg136 = v4i{(int)0xC308C308u, (int)0xC308C308u, (int)0xC308C308u, (int)0xC308C308u};
+  // The nibble mask and the bf16 bias live in registers the compiler cannot
+  // fold back into literals, so each dequantised pair is one v_and_or_b32
+  // (an instruction takes at most one literal) instead of an AND and an OR.
+  uint32_t kNib, kBias;
+  asm volatile("s_mov_b32 %0, 0xf000f" : "=s"(kNib));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(kBias));
 
   auto compute = [&](int ks, auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
@@ -114,11 +154,11 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
       for (int d = 0; d < 4; ++d) {
         const uint32_t w = (uint32_t)wq[slot][cb][d];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wd[cb][d][i] = (int)(((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u);
+        for (int i = 0; i < 4; ++i) wd[cb][d][i] = (int)(((w >> (4 * i)) & kNib) | kBias);
       }
     float sf[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) sf[cb] = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[slot][cb]);
+    for (int cb = 0; cb < 4; ++cb) sf[cb] = (float)__builtin_bit_cast(_Float16, sm.sc[ks & (C::kScG - 1)][scol[cb]]);
     const uint8_t* ab = &sm.a[ks & 1][0];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -129,8 +169,8 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const uint32_t i0 = (uint32_t)x[d][0], i1 = (uint32_t)x[d][1], i2 = (uint32_t)x[d][2], i3 = (uint32_t)x[d][3];
-        af[d] = v4i{(int)((i0 & 0xffffu) | (i2 << 16)), (int)((i0 >> 16) | (i2 & 0xffff0000u)),
-                    (int)((i1 & 0xffffu) | (i3 << 16)), (int)((i1 >> 16) | (i3 & 0xffff0000u))};
+        af[d] = v4i{(int)__builtin_amdgcn_perm(i2, i0, 0x05040100u), (int)__builtin_amdgcn_perm(i2, i0, 0x07060302u),
+                    (int)__builtin_amdgcn_perm(i3, i1, 0x05040100u), (int)__builtin_amdgcn_perm(i3, i1, 0x07060302u)};
       }
       v4f corr = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -150,6 +190,10 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
     constexpr int s = decltype(s_c)::value;
     commit(ks, s_c);
     barrier_lds();
+    if (C::kScG < kMaxKBlocks && ks > 0 && (ks & (C::kScG - 1)) == 0) {
+      stage_scales(ks);  // every wave is past the previous group's reads
+      barrier_lds();
+    }
     issue(ks + S - 1, IntC<(s + S - 1) % S>{});
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this block's MFMAs
     compute(ks, s_c);

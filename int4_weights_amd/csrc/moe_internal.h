@@ -15,6 +15,7 @@ DeviceInfo device_info();
 hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int K, uint8_t* q, float* sf, hipStream_t s);
 hipError_t launch_quant_weight_fp8(const uint16_t* w, int E, int N, int K, uint8_t* q, float* sfw, hipStream_t s);
 hipError_t launch_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t* packed, hipStream_t s);
+hipError_t launch_pack_weight_int4(const uint8_t* q4, int E, int N, int K, uint8_t* packed, hipStream_t s);
 hipError_t launch_quant_weight_int4(const uint16_t* w, int E, int N, int K, uint8_t* q4, uint16_t* s16,
                                     hipStream_t s);
 
@@ -57,7 +58,7 @@ struct GemmArgs {
   int64_t rows_cap;      // rows of A/D (contiguous) ; masked: E*max_m
   int max_m;
   int N, K;
-  int wpacked;           // fp8 path: W in the fragment-packed order (moe_pack_weight_fp8)
+  int wpacked;           // W in the fragment-packed order (moe_pack_weight_fp8 / _int4)
 };
 hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s);

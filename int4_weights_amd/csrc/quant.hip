@@ -180,6 +180,30 @@ __global__ __launch_bounds__(256) void pack_weight_fp8_kernel(const uint8_t* __r
   }
 }
 
+// Fragment-packed 4-bit weight order (moe_pack_weight_int4): one thread per
+// 16-byte output chunk.  Output chunk r of an expert is lane L = r % 64 of the
+// 1-KB block b = r / 64 = g * (N/16) + cb; it holds bytes 64g + 16(L/16) .. +15
+// of weight column 16cb + L % 16.
+__global__ __launch_bounds__(256) void pack_weight_int4_kernel(const uint8_t* __restrict__ q4, int64_t chunks,
+                                                               int64_t expert_chunks, int N, int K,
+                                                               uint8_t* __restrict__ out) {
+  const int ncb = N / 16;
+  const int64_t rowb = K / 2;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = c / expert_chunks;
+    const int64_t r = c - e * expert_chunks;
+    const int64_t b = r >> 6;
+    const int L = (int)(r & 63);
+    const int64_t g = b / ncb;
+    const int cb = (int)(b - g * ncb);
+    const int64_t n = 16 * cb + (L & 15);
+    const int64_t kb = 64 * g + 16 * (L >> 4);
+    const v4i v = *(const v4i*)(q4 + (e * N + n) * rowb + kb);
+    *(v4i*)(out + c * 16) = v;
+  }
+}
+
 static int grid_for(int64_t work_items, int per_block, int cap) {
   int64_t g = (work_items + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -209,6 +233,15 @@ hipError_t launch_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t
   if (chunks == 0) return hipSuccess;
   const int grid = grid_for(chunks, 256, device_info().cus * 8);
   pack_weight_fp8_kernel<<<grid, 256, 0, s>>>(q, chunks, expert_chunks, N, K, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weight_int4(const uint8_t* q4, int E, int N, int K, uint8_t* packed, hipStream_t s) {
+  const int64_t expert_chunks = (int64_t)N * K / 32;
+  const int64_t chunks = (int64_t)E * expert_chunks;
+  if (chunks == 0) return hipSuccess;
+  const int grid = grid_for(chunks, 256, device_info().cus * 8);
+  pack_weight_int4_kernel<<<grid, 256, 0, s>>>(q4, chunks, expert_chunks, N, K, packed);
   return hipGetLastError();
 }
 

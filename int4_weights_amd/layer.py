@@ -98,11 +98,14 @@ class MoeInt4Layer:
     """4-bit weight-only expert GEMM (group 128, fp16 scales, zero point 8), bf16 activations."""
 
     def __init__(self, w_q4: torch.Tensor, s16: torch.Tensor, topk: int, max_tokens: int,
-                 layout: int = L.LAYOUT_MASKED, align_or_max_m: int = 16, expected_m: int = 0):
+                 layout: int = L.LAYOUT_MASKED, align_or_max_m: int = 16, expected_m: int = 0,
+                 weights_packed: bool = False):
+        """weights_packed: w_q4 is in the order written by moe_pack_weight_int4."""
         E, N, K2 = w_q4.shape
         K = K2 * 2
         self.E, self.N, self.K, self.topk = E, N, K, topk
         self.w, self.s16 = w_q4, s16
+        self.wflag = L.WEIGHTS_PACKED if weights_packed else 0
         self.layout, self.am, self.expected_m = layout, align_or_max_m, expected_m
         dev = w_q4.device
         if layout == L.LAYOUT_CONTIGUOUS:
@@ -132,8 +135,8 @@ class MoeInt4Layer:
         w = self.w if w is None else w
         s16 = self.s16 if s16 is None else s16
         am = self.am if self.layout == L.LAYOUT_MASKED else self.rows_cap
-        L.moe_grouped_gemm_int4(self.layout, self.packed, w, s16, self.D, self.counts, self.seg_offsets, self.E, am,
-                                self.N, self.K, self.expected_m)
+        L.moe_grouped_gemm_int4(self.layout | self.wflag, self.packed, w, s16, self.D, self.counts, self.seg_offsets,
+                                self.E, am, self.N, self.K, self.expected_m)
 
     def combine(self, topk_weights):
         T = topk_weights.shape[0]

@@ -108,8 +108,15 @@ def test_host_validation_rejects_without_launching(lib):
     assert g8(K=128 * 300) == MOE_ERR_UNSUPPORTED    # K above the supported maximum
     assert g8(layout=0x10 | 7) == MOE_ERR_SHAPE      # the packed-weights flag does not make a layout valid
     assert g8(layout=0x10, seg=0) == MOE_ERR_NULL    # packed contiguous still needs seg_offsets
-    assert lib.moe_grouped_gemm_int4(0x10, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), 4, 64, 128, 256, 0,
-                                     None) == MOE_ERR_SHAPE  # no packed order for 4-bit weights
+    assert lib.moe_grouped_gemm_int4(0x10 | 7, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), 4, 64, 128,
+                                     256, 0, None) == MOE_ERR_SHAPE  # the flag does not make a layout valid
+    # moe_pack_weight_int4
+    assert lib.moe_pack_weight_int4(_p(A16), 2, 100, 128, _p(A16 << 4), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_pack_weight_int4(_p(A16), 2, 128, 64, _p(A16 << 4), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_pack_weight_int4(_p(A16 + 8), 2, 128, 128, _p(A16 << 4), None) == MOE_ERR_ALIGN
+    assert lib.moe_pack_weight_int4(None, 2, 128, 128, _p(A16 << 4), None) == MOE_ERR_NULL
+    assert lib.moe_pack_weight_int4(_p(A16), 2, 128, 128, _p(A16 + 4096), None) == MOE_ERR_SHAPE  # overlap
+    assert lib.moe_pack_weight_int4(None, 0, 128, 128, None, None) == MOE_OK
     assert lib.moe_grouped_gemm_int4(0, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), 4, 64, 100, 256, 0,
                                      None) == MOE_ERR_UNSUPPORTED
     # moe_unpermute_combine

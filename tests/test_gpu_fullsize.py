@@ -284,7 +284,10 @@ def test_full_size_int4_decode_layer():
     moe.moe_quant_weight_int4(w, q4, s16)
     kept = {e: u16(w[e]) for e in sample}
     del w
-    layer = MoeInt4Layer(q4, s16, k, T, moe.LAYOUT_MASKED, cfg.max_m, expected_m=max(1, T * k // E))
+    q4p = torch.empty_like(q4)
+    moe.moe_pack_weight_int4(q4, q4p)
+    layer = MoeInt4Layer(q4p, s16, k, T, moe.LAYOUT_MASKED, cfg.max_m, expected_m=max(1, T * k // E),
+                         weights_packed=True)
     z = layer.forward(x.to(DEV), ids.to(DEV), tw.to(DEV))
     torch.cuda.synchronize()
     r = _check_routing(layer, ids_np, E, "masked", cfg.max_m)

@@ -175,15 +175,18 @@ def _int4_case(seed, counts, N, K, layout, max_m=0):
                 max_m=max_m, a=u16(x), q4=q4, s16=s16)
 
 
-def _run_int4(c, expected_m=0):
+def _run_int4(c, expected_m=0, packed=False):
+    """packed: the weights go in the oracle's fragment-packed order, with MOE_WEIGHTS_PACKED."""
     A = bf16_from_u16(c["a"])
-    W4 = torch.from_numpy(c["q4"]).to(DEV)
+    wbytes = oracle.pack_weight_int4(c["q4"]).reshape(c["q4"].shape) if packed else c["q4"]
+    W4 = torch.from_numpy(wbytes).to(DEV)
     S16 = torch.from_numpy(c["s16"].view(np.int16)).view(torch.float16).to(DEV)
     D = torch.full((c["rows"], c["N"]), SENT_BITS, dtype=torch.int16, device=DEV).view(torch.bfloat16)
     counts = torch.from_numpy(c["counts"]).to(DEV)
     seg = torch.from_numpy(c["starts"].astype(np.int32)).to(DEV)
     am = c["max_m"] if c["layout"] == moe.LAYOUT_MASKED else c["rows"]
-    moe.moe_grouped_gemm_int4(c["layout"], A, W4, S16, D, counts, seg, c["E"], am, c["N"], c["K"], expected_m)
+    layout = c["layout"] | (moe.WEIGHTS_PACKED if packed else 0)
+    moe.moe_grouped_gemm_int4(layout, A, W4, S16, D, counts, seg, c["E"], am, c["N"], c["K"], expected_m)
     torch.cuda.synchronize()
     return D
 
@@ -196,18 +199,40 @@ def _check_int4(c, D):
     assert (u16(D)[~valid] == SENT_BITS).all()
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("expected_m", [0, 16])
-def test_int4_masked(expected_m):
+def test_int4_masked(expected_m, packed):
     require_gpu()
     c = _int4_case(7, [0, 1, 16, 5, 9, 30], N=384, K=640, layout=moe.LAYOUT_MASKED, max_m=16)
-    _check_int4(c, _run_int4(c, expected_m))
+    _check_int4(c, _run_int4(c, expected_m, packed=packed))
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("expected_m", [0, 16])
-def test_int4_contiguous_ragged(expected_m):
+def test_int4_contiguous_ragged(expected_m, packed):
     require_gpu()
     c = _int4_case(8, [3, 0, 70, 129], N=256, K=1024, layout=moe.LAYOUT_CONTIGUOUS)
-    _check_int4(c, _run_int4(c, expected_m))
+    _check_int4(c, _run_int4(c, expected_m, packed=packed))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_int4_long_k_restages_scales(packed):
+    """130 K groups: the 64-row tile holds 128 groups of scales in LDS and restages once; 16-row tiles hold all."""
+    require_gpu()
+    c = _int4_case(12, [40, 0, 70], N=256, K=130 * 128, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (16, 64):
+        _check_int4(c, _run_int4(c, em, packed=packed))
+
+
+def test_pack_weight_int4_bit_exact():
+    """The library's packed 4-bit order equals the oracle's, byte for byte (two experts, three groups)."""
+    require_gpu()
+    rng = np.random.default_rng(14)
+    q4 = rng.integers(0, 256, size=(2, 384, 192), dtype=np.uint8)
+    out = torch.full(q4.shape, 0x5A, dtype=torch.uint8, device=DEV)
+    moe.moe_pack_weight_int4(torch.from_numpy(q4).to(DEV), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().reshape(2, -1), oracle.pack_weight_int4(q4))
 
 
 def test_int4_integer_inputs_bit_exact():
@@ -222,17 +247,20 @@ def test_int4_integer_inputs_bit_exact():
     q4 = (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
     c = dict(E=E, N=N, K=K, rows=32, starts=starts, eff=counts, counts=counts, layout=moe.LAYOUT_MASKED, max_m=16,
              a=u16(torch.from_numpy(ai).to(torch.bfloat16)), q4=q4, s16=np.full((E, N, K // 128), 0x3C00, np.uint16))
-    for em in (0, 16):
-        D = _run_int4(c, em)
+    for em, packed in ((0, False), (16, False), (0, True), (16, True)):
+        D = _run_int4(c, em, packed=packed)
         for e in range(E):
             s, n = int(starts[e]), int(counts[e])
             exact = ai[s:s + n].astype(np.int64) @ (q[e].astype(np.int64) - 8).T
             assert np.array_equal(u16(D)[s:s + n], oracle.f64_to_bf16_bits(exact.astype(np.float64)))
 
 
-def test_int4_determinism_20_runs():
+@pytest.mark.parametrize("packed", [False, True])
+def test_int4_determinism_20_runs(packed):
     require_gpu()
     c = _int4_case(10, [4, 16, 0, 2], N=256, K=512, layout=moe.LAYOUT_MASKED, max_m=16)
-    ref = _run_int4(c)
+    ref = _run_int4(c, packed=packed)
     for _ in range(20):
-        assert torch.equal(_run_int4(c), ref)
+        assert torch.equal(_run_int4(c, packed=packed), ref)
+    # the packed order changes the loads only, never the arithmetic
+    assert torch.equal(_run_int4(c, packed=not packed), ref)
