@@ -212,10 +212,10 @@ def run(args):
             s16 = torch.empty(E, N, K // 128, dtype=torch.float16, device=dev)
             moe.moe_quant_weight_int4(w, q4, s16)
             del w
-            q4p = torch.empty_like(q4)
-            moe.moe_pack_weight_int4(q4, q4p)
-            del q4
-            copies.append((q4p, s16))
+            q4p, s16p = torch.empty_like(q4), torch.empty_like(s16)
+            moe.moe_pack_weight_int4(q4, s16, q4p, s16p)
+            del q4, s16
+            copies.append((q4p, s16p))
         layer = MoeInt4Layer(copies[0][0], copies[0][1], k, T, moe.LAYOUT_MASKED, cfg.max_m,
                              expected_m=args.expected_m or max(1, R // E), weights_packed=True)
         names = ["moe_route_pack", "gemm", "moe_unpermute_combine"]

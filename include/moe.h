@@ -130,16 +130,25 @@ moe_status moe_quant_weight_fp8(const uint16_t* w, int E, int N, int K,
  *   The scales (sfw) are unchanged. */
 moe_status moe_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t* packed, void* stream);
 
-/* moe_pack_weight_int4: the same idea for 4-bit weights (MatMulNBits layout in,
- * fragment order out; ONNX Runtime "MatMulNBits -- CUDA Operator
- * Documentation" describes prepacked weights for its fpA_intB path).  A pure
- * byte permutation; the fp16 scales are unchanged.
- *   For expert e, group g (128 K values = 64 bytes of a column), 16-column
- *   block cb, lane L = c16 + 16*h (c16 in [0,16), h in [0,4)), byte j:
- *     packed[e*N*K/2 + (g*(N/16) + cb)*1024 + L*16 + j] = q4[e][16*cb + c16][64*g + 16*h + j]
- *   q4 and packed are [E*N*K/2] bytes, 16-byte aligned, not overlapping.
+/* moe_pack_weight_int4: the same idea for 4-bit weights (MatMulNBits codes and
+ * scales in, fragment order out; ONNX Runtime "MatMulNBits -- CUDA Operator
+ * Documentation" describes prepacked weights for its fpA_intB path).  Nothing
+ * is quantised or rounded: weights and scales are only permuted.
+ *   Weights, per expert e, K group g (128 weights), 16-column block cb, lane
+ *   L = c16 + 16*h (c16, h as above), dword d in [0,4), nibble position p in
+ *   [0,8) (bits 4p..4p+3 of the little-endian dword):
+ *     weight (n = 16*cb + c16, k = 128*g + 8*(4*d + h) + sigma(p)),
+ *     sigma = (0 2 4 6 1 3 5 7), is stored at byte
+ *     e*N*K/2 + (g*(N/16) + cb)*1024 + 16*L + 4*d + p/2, low nibble if p is even.
+ *   So each dword holds 8 consecutive k of one column, k + 2i and k + 2i + 1
+ *   at nibbles i and i + 4.
+ *   Scales: s16_packed[e*N*K/128 + ((g*(N/64) + n/64)*16 + n%16)*4 + (n%64)/16]
+ *     = s16[e][n][g].
+ *   q4/q4_packed are [E*N*K/2] bytes, s16/s16_packed [E*N*K/128] fp16; all
+ *   16-byte aligned, inputs and outputs not overlapping.
  *   Requires N % 128 == 0, K % 128 == 0. */
-moe_status moe_pack_weight_int4(const uint8_t* q4, int E, int N, int K, uint8_t* packed, void* stream);
+moe_status moe_pack_weight_int4(const uint8_t* q4, const uint16_t* s16, int E, int N, int K, uint8_t* q4_packed,
+                                uint16_t* s16_packed, void* stream);
 
 /* moe_quant_weight_int4: group-128 4-bit weight quantisation in the
  * MatMulNBits layout (ONNX Runtime "MatMulNBits -- CUDA Operator
@@ -238,8 +247,8 @@ moe_status moe_grouped_gemm_fp8(int layout,
  *     A   [rows, K] bf16,  W4 [E, N, K/2] (low nibble = even k),
  *     S16 [E, N, K/128] fp16,  D [rows, N] bf16.
  *   Layout, counts, seg_offsets, expected_m and alignment as for
- *   moe_grouped_gemm_fp8; layout | MOE_WEIGHTS_PACKED: W4 in the order written
- *   by moe_pack_weight_int4. */
+ *   moe_grouped_gemm_fp8; layout | MOE_WEIGHTS_PACKED: W4 and S16 in the orders
+ *   written by moe_pack_weight_int4. */
 moe_status moe_grouped_gemm_int4(int layout,
                                  const uint16_t* A, const uint8_t* W4,
                                  const uint16_t* S16, uint16_t* D,

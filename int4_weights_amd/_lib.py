@@ -36,7 +36,7 @@ SIGNATURES = {
     "moe_quant_weight_fp8": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
     "moe_quant_weight_int4": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
     "moe_pack_weight_fp8": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
-    "moe_pack_weight_int4": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
+    "moe_pack_weight_int4": (_c_i32, [_vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
     "moe_route_pack": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_i64,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
@@ -145,13 +145,16 @@ def moe_pack_weight_fp8(q, packed, stream=None):
     _check(load().moe_pack_weight_fp8(_ptr(q), E, N, K, _ptr(packed), _stream(stream)), "moe_pack_weight_fp8")
 
 
-def moe_pack_weight_int4(q4, packed, stream=None):
-    """q4 uint8 [E, N, K/2] (MatMulNBits order) -> packed uint8 [E, N, K/2] in the fragment order."""
-    _dev(q4, "q4", torch.uint8, 3), _dev(packed, "packed", torch.uint8, 3)
+def moe_pack_weight_int4(q4, s16, q4_packed, s16_packed, stream=None):
+    """q4 uint8 [E, N, K/2] and s16 fp16 [E, N, K/128] (MatMulNBits order) -> the packed orders, same shapes."""
+    _dev(q4, "q4", torch.uint8, 3), _dev(q4_packed, "q4_packed", torch.uint8, 3)
+    _dev(s16, "s16", torch.float16, 3), _dev(s16_packed, "s16_packed", torch.float16, 3)
     E, N, K2 = q4.shape
-    if tuple(packed.shape) != (E, N, K2):
+    if tuple(q4_packed.shape) != (E, N, K2) or tuple(s16.shape) != (E, N, K2 // 64) or \
+            tuple(s16_packed.shape) != (E, N, K2 // 64):
         raise ValueError("moe_pack_weight_int4: shape mismatch")
-    _check(load().moe_pack_weight_int4(_ptr(q4), E, N, 2 * K2, _ptr(packed), _stream(stream)), "moe_pack_weight_int4")
+    _check(load().moe_pack_weight_int4(_ptr(q4), _ptr(s16), E, N, 2 * K2, _ptr(q4_packed), _ptr(s16_packed),
+                                       _stream(stream)), "moe_pack_weight_int4")
 
 
 def moe_quant_weight_int4(w, q4, s16, stream=None):

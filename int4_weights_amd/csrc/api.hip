@@ -119,19 +119,29 @@ moe_status moe_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t* p
   return hip_status(launch_pack_weight_fp8(q, E, N, K, packed, (hipStream_t)stream), "moe_pack_weight_fp8");
 }
 
-moe_status moe_pack_weight_int4(const uint8_t* q4, int E, int N, int K, uint8_t* packed, void* stream) {
+moe_status moe_pack_weight_int4(const uint8_t* q4, const uint16_t* s16, int E, int N, int K, uint8_t* q4_packed,
+                                uint16_t* s16_packed, void* stream) {
   g_err[0] = 0;
   if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_pack_weight_int4: E=%d N=%d K=%d", E, N, K);
   if (N % 128 || K % 128)
     return fail(MOE_ERR_UNSUPPORTED, "moe_pack_weight_int4: N=%d and K=%d must be multiples of 128", N, K);
   if ((int64_t)N * K / 2 > 0xffffffffll) return fail(MOE_ERR_UNSUPPORTED, "moe_pack_weight_int4: one expert exceeds 4 GiB");
   if (E == 0) return MOE_OK;
-  if (!q4 || !packed) return fail(MOE_ERR_NULL, "moe_pack_weight_int4: null pointer");
-  if (!aligned(q4, 16) || !aligned(packed, 16))
-    return fail(MOE_ERR_ALIGN, "moe_pack_weight_int4: q4 and packed must be 16-byte aligned");
-  const int64_t bytes = (int64_t)E * N * (K / 2);
-  if (q4 < packed + bytes && packed < q4 + bytes) return fail(MOE_ERR_SHAPE, "moe_pack_weight_int4: q4 and packed overlap");
-  return hip_status(launch_pack_weight_int4(q4, E, N, K, packed, (hipStream_t)stream), "moe_pack_weight_int4");
+  if (!q4 || !s16 || !q4_packed || !s16_packed) return fail(MOE_ERR_NULL, "moe_pack_weight_int4: null pointer");
+  if (!aligned(q4, 16) || !aligned(q4_packed, 16) || !aligned(s16, 16) || !aligned(s16_packed, 16))
+    return fail(MOE_ERR_ALIGN, "moe_pack_weight_int4: all four buffers must be 16-byte aligned");
+  const uint8_t* ranges[4][2] = {{q4, q4 + (int64_t)E * N * (K / 2)},
+                                 {(const uint8_t*)s16, (const uint8_t*)(s16 + (int64_t)E * N * (K / 128))},
+                                 {q4_packed, q4_packed + (int64_t)E * N * (K / 2)},
+                                 {(const uint8_t*)s16_packed, (const uint8_t*)(s16_packed + (int64_t)E * N * (K / 128))}};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 2; j < 4; ++j)
+      if (ranges[i][0] < ranges[j][1] && ranges[j][0] < ranges[i][1])
+        return fail(MOE_ERR_SHAPE, "moe_pack_weight_int4: an input overlaps an output");
+  if (ranges[2][0] < ranges[3][1] && ranges[3][0] < ranges[2][1])
+    return fail(MOE_ERR_SHAPE, "moe_pack_weight_int4: the two outputs overlap");
+  return hip_status(launch_pack_weight_int4(q4, s16, E, N, K, q4_packed, s16_packed, (hipStream_t)stream),
+                    "moe_pack_weight_int4");
 }
 
 moe_status moe_quant_weight_int4(const uint16_t* w, int E, int N, int K, uint8_t* q4, uint16_t* s16, void* stream) {

@@ -25,6 +25,20 @@
 //    the accumulator layout gives each lane one column, hence one scale.
 //  * Activations are staged in LDS (two slots, XOR-swizzled) from VGPR-ring
 //    loads, as in the FP8 kernel.
+//
+// Weights in the packed order (moe_pack_weight_int4) take a second kernel
+// built for decode, where each expert holds a handful of rows and the kernel
+// is bound by the weight stream:
+//  * the four waves of a workgroup share nothing but the unit table: each
+//    streams its own 64 columns with no barrier, so a late load stalls one
+//    wave only;
+//  * each dword of the packed order holds 8 consecutive k with k + 2i and
+//    k + 2i + 1 at nibbles i and i + 4, so the dequantised pairs are in
+//    natural order and the activation fragment is used as loaded: 16 bytes
+//    per matrix instruction, read straight from global memory (the rows of an
+//    expert stay in L2 for its column tiles);
+//  * the packed scales put the 4 column blocks of one lane's column next to
+//    each other: one 8-byte load per lane and K group, in the weight ring.
 #include "gemm_common.h"
 
 namespace moe {
@@ -55,17 +69,14 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
   const int ncol0 = u.n0 + 64 * wv;
   const bool wave_on = ncol0 < N;
 
-  // 4-bit weights.  Row-major: column n's group g is 64 bytes at n*K/2 + 64g.
-  // Packed (moe_pack_weight_int4): the 16-column block's group is 1 KB at
-  // (g*(N/16) + n/16)*1024, lane L's 16 bytes at 16L.
+  // 4-bit weights, MatMulNBits order: column n's group g is 64 bytes at n*K/2 + 64g
   const uint8_t* wbase = a.W + (int64_t)u.e * N * (K / 2);
-  const uint32_t wstep = a.wpacked ? (uint32_t)N * 64u : 64u;  // bytes per K group
   uint32_t woff[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     int n = ncol0 + 16 * cb + l16;
     if (n >= N) n = N - 1;
-    woff[cb] = a.wpacked ? (uint32_t)(n / 16) * 1024u + 16u * lane : (uint32_t)n * (uint32_t)(K / 2) + 16u * lg;
+    woff[cb] = (uint32_t)n * (uint32_t)(K / 2) + 16u * lg;
   }
   // the unit's group scales: its columns' rows of S16 are one contiguous block
   // (kBN x KG halves); groups gb .. gb+kScG-1 are staged into LDS
@@ -120,7 +131,7 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
     constexpr int slot = decltype(slot_c)::value;
     const int ks = min(ks_req, KG - 1);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) wq[slot][cb] = *(const v4i*)(wbase + (woff[cb] + (uint32_t)ks * wstep));
+    for (int cb = 0; cb < 4; ++cb) wq[slot][cb] = *(const v4i*)(wbase + (woff[cb] + (uint32_t)ks * 64u));
 #pragma unroll
     for (int i = 0; i < C::kApw; ++i) ar[slot][i] = *(const v4i*)(abase + (aoff[i] + (uint32_t)ks * 256u));
   };
@@ -175,14 +186,18 @@ __device__ __forceinline__ void int4_unit(const GemmArgs& a, const Unit& u, I4Sm
       v4f corr = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int d = 0; d < 4; ++d) corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af[d]), as_bf(kNeg136), corr, 0, 0, 0);
+      // four independent accumulation chains, interleaved so that no matrix
+      // instruction waits on the one issued just before it
+      v4f p[4];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        v4f p = corr;
+      for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af[d]), as_bf(wd[cb][d]), p, 0, 0, 0);
+        for (int cb = 0; cb < 4; ++cb)
+          p[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af[d]), as_bf(wd[cb][d]), d == 0 ? corr : p[cb], 0, 0, 0);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[rb][cb][v] = __builtin_fmaf(sf[cb], p[v], acc[rb][cb][v]);
-      }
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[rb][cb][v] = __builtin_fmaf(sf[cb], p[cb][v], acc[rb][cb][v]);
     }
   };
 
@@ -239,6 +254,118 @@ __global__ __launch_bounds__(256, 1) void gemm_int4_kernel(const GemmArgs a) {
   }
 }
 
+// ------------------------------------------------------- packed weights --
+template <int S, int SA>
+__device__ __forceinline__ void int4_unit_packed(const GemmArgs& a, const Unit& u, int wv, int lane) {
+  static_assert(S % SA == 0, "the activation ring must divide the weight ring");
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int K = a.K, N = a.N, KG = K / 128;
+  const int ncol0 = u.n0 + 64 * wv;
+  if (ncol0 >= N) return;  // N is a multiple of 128: a wave with work has 64 whole columns
+
+  // weights: group g of 16-column block b is 1 KB at (g*(N/16) + b)*1024; lane L's 16 bytes at 16L
+  const uint8_t* wbase = a.W + (int64_t)u.e * N * (K / 2) + (int64_t)(ncol0 / 16) * 1024 + 16 * lane;
+  const uint32_t wstep = (uint32_t)N * 64u;
+  // scales [K/128][N/64][16][4]: the 4 column blocks of column l16 of this wave's 64, per group
+  const uint16_t* sbase = (const uint16_t*)a.SW + (int64_t)u.e * N * KG + ncol0 + 4 * l16;
+  // activations: row l16 (clamped to the unit's rows), 16 bytes per matrix instruction d at
+  // k = 128g + 8(4d + lg): byte 256g + 64d + 16lg of the row
+  const uint8_t* abase = a.A + ((int64_t)u.row0 + min(l16, u.mrows - 1)) * K * 2 + 16 * lg;
+
+  v4i wq[S][4];
+  uint2 sq[S];
+  v4i ar[SA][4];
+  v4f acc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto issue_w = [&](int ks_req, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    const uint32_t ks = (uint32_t)min(ks_req, KG - 1);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) wq[slot][cb] = *(const v4i*)(wbase + (ks * wstep + 1024u * cb));
+    sq[slot] = *(const uint2*)(sbase + ks * (uint32_t)N);
+  };
+  auto issue_a = [&](int ks_req, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    const uint32_t ks = (uint32_t)min(ks_req, KG - 1);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) ar[slot][d] = *(const v4i*)(abase + (ks * 256u + 64u * d));
+  };
+
+  const v4i kNeg136 = v4i{(int)0xC308C308u, (int)0xC308C308u, (int)0xC308C308u, (int)0xC308C308u};
+  uint32_t kNib, kBias;  // registers, not literals: one v_and_or_b32 per dequantised pair
+  asm volatile("s_mov_b32 %0, 0xf000f" : "=s"(kNib));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(kBias));
+
+  auto compute = [&](auto s_c) {
+    constexpr int s = decltype(s_c)::value, sa = s % SA;
+    const uint32_t s01 = sq[s].x, s23 = sq[s].y;
+    const float sf[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(s01 & 0xffffu)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(s01 >> 16)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(s23 & 0xffffu)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(s23 >> 16))};
+    v4f corr = v4f{0.f, 0.f, 0.f, 0.f};  // -136 * sum of the group's activations, per row
+#pragma unroll
+    for (int d = 0; d < 4; ++d) corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(ar[sa][d]), as_bf(kNeg136), corr, 0, 0, 0);
+    v4f p[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const uint32_t w = (uint32_t)wq[s][cb][d];
+        v4i wd;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wd[i] = (int)(((w >> (4 * i)) & kNib) | kBias);  // 128 + q, bf16 pairs
+        p[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(ar[sa][d]), as_bf(wd), d == 0 ? corr : p[cb], 0, 0, 0);
+      }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[cb][v] = __builtin_fmaf(sf[cb], p[cb][v], acc[cb][v]);
+  };
+
+  auto step = [&](int ks, auto s_c) {
+    constexpr int s = decltype(s_c)::value;
+    issue_w(ks + S - 1, IntC<(s + S - 1) % S>{});
+    issue_a(ks + SA - 1, IntC<(s + SA - 1) % SA>{});
+    compute(s_c);
+  };
+
+  static_for<0, S - 1>([&](auto s_c) { issue_w(decltype(s_c)::value, s_c); });
+  static_for<0, SA - 1>([&](auto s_c) { issue_a(decltype(s_c)::value, s_c); });
+  const int nfull = KG / S;
+  for (int g = 0; g < nfull; ++g) static_for<0, S>([&](auto s_c) { step(g * S + decltype(s_c)::value, s_c); });
+  static_for<0, S>([&](auto s_c) {
+    const int ks = nfull * S + decltype(s_c)::value;
+    if (ks < KG) step(ks, s_c);
+  });
+
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int m = 4 * lg + v;
+    if (m < u.mrows) {
+      uint16_t* drow = a.D + (int64_t)(u.row0 + m) * N + ncol0 + l16;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) drow[16 * cb] = (uint16_t)f32_to_bf16_rne(acc[cb][v]);
+    }
+  }
+}
+
+template <int S, int SA>
+__global__ __launch_bounds__(256, 1) void gemm_int4_packed_kernel(const GemmArgs a) {
+  __shared__ int s_up[kMaxExperts + 1], s_tmp[257];
+  const Sched sc{s_up};
+  sched_build<16>(a, sc, s_tmp);
+  const Walk walk = sched_walk(s_up[a.E]);
+  const int lane = lane_id();
+  const int wv = uniform(threadIdx.x >> 6);
+  for (int v = walk.first; v < walk.end; v += walk.stride) {
+    const Unit u = sched_unit<16>(a, sc, v);
+    int4_unit_packed<S, SA>(a, u, wv, lane);
+  }
+}
+
 template <int RB, int S>
 static hipError_t launch_i4(const GemmArgs& a, hipStream_t s) {
   const int cus = device_info().cus;
@@ -248,7 +375,17 @@ static hipError_t launch_i4(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int S, int SA>
+static hipError_t launch_i4p(const GemmArgs& a, hipStream_t s) {
+  const int cus = device_info().cus;
+  int grid = cus - cus % kXcds;
+  if (grid < kXcds) grid = kXcds;
+  gemm_int4_packed_kernel<S, SA><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s) {
+  if (a.wpacked) return launch_i4p<8, 4>(a, s);  // 16-row units whatever the rows per expert
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 64);
   if (em <= 16) return launch_i4<1, 8>(a, s);
   return launch_i4<4, 4>(a, s);

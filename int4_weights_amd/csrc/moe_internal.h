@@ -15,7 +15,8 @@ DeviceInfo device_info();
 hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int K, uint8_t* q, float* sf, hipStream_t s);
 hipError_t launch_quant_weight_fp8(const uint16_t* w, int E, int N, int K, uint8_t* q, float* sfw, hipStream_t s);
 hipError_t launch_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t* packed, hipStream_t s);
-hipError_t launch_pack_weight_int4(const uint8_t* q4, int E, int N, int K, uint8_t* packed, hipStream_t s);
+hipError_t launch_pack_weight_int4(const uint8_t* q4, const uint16_t* s16, int E, int N, int K, uint8_t* q4_packed,
+                                   uint16_t* s16_packed, hipStream_t s);
 hipError_t launch_quant_weight_int4(const uint16_t* w, int E, int N, int K, uint8_t* q4, uint16_t* s16,
                                     hipStream_t s);
 

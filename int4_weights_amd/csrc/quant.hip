@@ -182,8 +182,14 @@ __global__ __launch_bounds__(256) void pack_weight_fp8_kernel(const uint8_t* __r
 
 // Fragment-packed 4-bit weight order (moe_pack_weight_int4): one thread per
 // 16-byte output chunk.  Output chunk r of an expert is lane L = r % 64 of the
-// 1-KB block b = r / 64 = g * (N/16) + cb; it holds bytes 64g + 16(L/16) .. +15
-// of weight column 16cb + L % 16.
+// 1-KB block b = r / 64 = g * (N/16) + cb: column 16cb + L % 16, and for each
+// dword d the 8 weights k0 = 128g + 8(4d + L/16) .. k0 + 7, whose MatMulNBits
+// bytes are one source dword s.  The even k (low nibbles of s) fill the low
+// half of the output dword, the odd k (high nibbles) the high half.
+__device__ __forceinline__ uint32_t gather_nibbles(uint32_t x) {  // low nibbles of the 4 bytes -> 16 bits
+  x &= 0x0F0F0F0Fu;
+  return (x & 0xFu) | ((x >> 4) & 0xF0u) | ((x >> 8) & 0xF00u) | ((x >> 12) & 0xF000u);
+}
 __global__ __launch_bounds__(256) void pack_weight_int4_kernel(const uint8_t* __restrict__ q4, int64_t chunks,
                                                                int64_t expert_chunks, int N, int K,
                                                                uint8_t* __restrict__ out) {
@@ -198,9 +204,30 @@ __global__ __launch_bounds__(256) void pack_weight_int4_kernel(const uint8_t* __
     const int64_t g = b / ncb;
     const int cb = (int)(b - g * ncb);
     const int64_t n = 16 * cb + (L & 15);
-    const int64_t kb = 64 * g + 16 * (L >> 4);
-    const v4i v = *(const v4i*)(q4 + (e * N + n) * rowb + kb);
+    const uint8_t* src = q4 + (e * N + n) * rowb + 64 * g + 4 * (L >> 4);
+    v4i v;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t sw = *(const uint32_t*)(src + 16 * d);  // k0 = 128g + 8(4d + h): byte 64g + 16d + 4h
+      v[d] = (int)(gather_nibbles(sw) | (gather_nibbles(sw >> 4) << 16));
+    }
     *(v4i*)(out + c * 16) = v;
+  }
+}
+
+// Packed scale order: element i of an expert's [K/128][N/64][16][4] block.
+__global__ __launch_bounds__(256) void pack_scale_int4_kernel(const uint16_t* __restrict__ s16, int64_t total,
+                                                              int64_t per_expert, int N, int KG,
+                                                              uint16_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i / per_expert;
+    int64_t r = i - e * per_expert;
+    const int cb = (int)(r & 3);
+    const int c16 = (int)((r >> 2) & 15);
+    r >>= 6;
+    const int64_t n64 = r % (N / 64), g = r / (N / 64);
+    const int64_t n = 64 * n64 + 16 * cb + c16;
+    out[i] = s16[(e * N + n) * KG + g];
   }
 }
 
@@ -236,12 +263,16 @@ hipError_t launch_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t
   return hipGetLastError();
 }
 
-hipError_t launch_pack_weight_int4(const uint8_t* q4, int E, int N, int K, uint8_t* packed, hipStream_t s) {
+hipError_t launch_pack_weight_int4(const uint8_t* q4, const uint16_t* s16, int E, int N, int K, uint8_t* q4_packed,
+                                   uint16_t* s16_packed, hipStream_t s) {
   const int64_t expert_chunks = (int64_t)N * K / 32;
   const int64_t chunks = (int64_t)E * expert_chunks;
   if (chunks == 0) return hipSuccess;
-  const int grid = grid_for(chunks, 256, device_info().cus * 8);
-  pack_weight_int4_kernel<<<grid, 256, 0, s>>>(q4, chunks, expert_chunks, N, K, packed);
+  pack_weight_int4_kernel<<<grid_for(chunks, 256, device_info().cus * 8), 256, 0, s>>>(q4, chunks, expert_chunks, N, K,
+                                                                                       q4_packed);
+  const int64_t per_expert = (int64_t)N * (K / 128), total = (int64_t)E * per_expert;
+  pack_scale_int4_kernel<<<grid_for(total, 256, device_info().cus * 8), 256, 0, s>>>(s16, total, per_expert, N, K / 128,
+                                                                                     s16_packed);
   return hipGetLastError();
 }
 

@@ -58,8 +58,8 @@ from .routing import (
 )
 from .gemm import grouped_gemm_fp8, grouped_gemm_int4, segments
 from .combine import combine
-from .layout import (pack_weight_fp8, pack_weight_int4, packed_offset, packed_offset_int4, unpack_weight_fp8,
-                     unpack_weight_int4)
+from .layout import (pack_weight_fp8, pack_weight_int4, packed_nibble_int4, packed_offset, packed_scale_offset_int4,
+                     unpack_weight_fp8, unpack_weight_int4)
 from .metrics import calc_diff, elementwise_ok, elementwise_excess
 
 __all__ = [

@@ -13,11 +13,17 @@ contiguous bytes at ((kb * (N/16) + cb) * 2048); inside it, byte j of the
 16-byte piece for column 16cb + c and K offset 64h + 16g + j sits at
 h*1024 + (c + 16g)*16 + j.
 
-4-bit weights (MatMulNBits order [E, N, K/2], two weights per byte): the 64
-bytes of column 16cb + c in K group g (one quantisation group of 128 weights)
-are four 16-byte pieces h = 0..3; the 16 columns' pieces of group g form 1024
-contiguous bytes at (g * (N/16) + cb) * 1024, piece h of column c at
-(c + 16h) * 16.
+4-bit weights (MatMulNBits order [E, N, K/2], two weights per byte, low
+nibble first) are packed at the level of single weights.  For expert e, K group
+g (128 weights), 16-column block cb, lane L = c + 16h (c < 16, h < 4), dword
+d < 4 and nibble position p < 8 (bits 4p..4p+3 of the little-endian dword):
+    column 16cb + c, k = 128g + 8(4d + h) + sigma(p),  sigma = (0 2 4 6 1 3 5 7)
+sits at byte (g*(N/16) + cb)*1024 + 16L + 4d + p//2, nibble p % 2.  Each
+dword then holds 8 consecutive k of one column with k and k+1 at nibbles i and
+i+4, so shifting by 4i and masking both 16-bit halves yields the pair
+(k + 2i, k + 2i + 1) in natural order.
+The group scales [E, N, K/128] are packed to [E, K/128, N/64, 16, 4]: scale
+(n, g) sits at ((g*(N/64) + n//64)*16 + n%16)*4 + (n%64)//16.
 """
 
 from __future__ import annotations
@@ -57,30 +63,69 @@ def unpack_weight_fp8(packed: np.ndarray, N: int, K: int) -> np.ndarray:
     return np.ascontiguousarray(x.transpose(0, 2, 5, 1, 3, 4, 6)).reshape(E, N, K)
 
 
-def packed_offset_int4(n: int, b: int, N: int) -> int:
-    """Byte offset (within one expert) of byte b of column n (MatMulNBits order) in the packed order.
+SIGMA = (0, 2, 4, 6, 1, 3, 5, 7)
 
-    Pinned by: bijection over every (n, b) of small shapes (tests)."""
-    g, rest = divmod(b, 64)
-    h, j = divmod(rest, 16)
+
+def packed_nibble_int4(n: int, k: int, N: int) -> tuple[int, int]:
+    """(byte offset within one expert, nibble 0 = low / 1 = high) of weight (n, k) in the packed order.
+
+    Pinned by: bijection over every (n, k) of small shapes and hand-decoded dwords (tests)."""
+    g, kk = divmod(k, 128)
+    chunk, j = divmod(kk, 8)
+    d, h = divmod(chunk, 4)
+    p = SIGMA.index(j)
     cb, c = divmod(n, 16)
-    return (g * (N // 16) + cb) * 1024 + (c + 16 * h) * 16 + j
+    L = c + 16 * h
+    return (g * (N // 16) + cb) * 1024 + 16 * L + 4 * d + p // 2, p % 2
 
 
-def pack_weight_int4(q4: np.ndarray) -> np.ndarray:
-    """uint8 [E, N, K/2] MatMulNBits bytes -> uint8 [E, N*K/2] in the packed order (a pure permutation)."""
+def packed_scale_offset_int4(n: int, g: int, N: int) -> int:
+    """Element offset (within one expert) of the scale of column n, group g, in the packed scale order."""
+    return ((g * (N // 64) + n // 64) * 16 + n % 16) * 4 + (n % 64) // 16
+
+
+def _nibbles(q4: np.ndarray) -> np.ndarray:
+    """uint8 [..., B] -> the 2B 4-bit values, low nibble first."""
+    out = np.empty(q4.shape[:-1] + (2 * q4.shape[-1],), np.uint8)
+    out[..., 0::2] = q4 & 15
+    out[..., 1::2] = q4 >> 4
+    return out
+
+
+def pack_weight_int4(q4: np.ndarray, s16: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """MatMulNBits codes uint8 [E, N, K/2] and scales uint16 [E, N, K/128] -> the packed orders
+    (uint8 [E, N*K/2], uint16 [E, N*K/128]); a permutation of weights and of scales."""
     q4 = np.asarray(q4, dtype=np.uint8)
+    s16 = np.asarray(s16, dtype=np.uint16)
     E, N, K2 = q4.shape
-    if N % 128 or (2 * K2) % 128:
+    K = 2 * K2
+    if N % 128 or K % 128:
         raise ValueError("N and K must be multiples of 128")
-    # axes: e, cb, c, g, h, j  ->  e, g, cb, h, c, j
-    x = q4.reshape(E, N // 16, 16, K2 // 64, 4, 16)
-    return np.ascontiguousarray(x.transpose(0, 3, 1, 4, 2, 5)).reshape(E, N * K2)
+    w = _nibbles(q4)  # [E, N, K]
+    # k = 128g + 8(4d + h) + sigma(p); n = 16cb + c
+    x = w.reshape(E, N // 16, 16, K // 128, 4, 4, 8)       # e, cb, c, g, d, h, j
+    x = x[..., list(SIGMA)]                               # j -> nibble position p
+    x = x.transpose(0, 3, 1, 5, 2, 4, 6)                  # e, g, cb, h, c, d, p  (L = c + 16h)
+    x = np.ascontiguousarray(x).reshape(E, N * K // 8, 8)  # dwords of 8 nibbles
+    packed = np.zeros((E, N * K // 8, 4), np.uint8)
+    for b in range(4):
+        packed[..., b] = x[..., 2 * b] | (x[..., 2 * b + 1] << 4)
+    sp = s16.reshape(E, N // 64, 4, 16, K // 128)         # e, n64, cb, c, g
+    sp = np.ascontiguousarray(sp.transpose(0, 4, 1, 3, 2)).reshape(E, N * K // 128)
+    return packed.reshape(E, N * K // 2), sp
 
 
 def unpack_weight_int4(packed: np.ndarray, N: int, K: int) -> np.ndarray:
-    """Inverse of pack_weight_int4: uint8 [E, N*K/2] -> [E, N, K/2]."""
+    """Inverse of the weight half of pack_weight_int4: uint8 [E, N*K/2] -> [E, N, K/2]."""
     packed = np.asarray(packed, dtype=np.uint8)
     E = packed.shape[0]
-    x = packed.reshape(E, K // 128, N // 16, 4, 16, 16)  # e, g, cb, h, c, j
-    return np.ascontiguousarray(x.transpose(0, 2, 4, 1, 3, 5)).reshape(E, N, K // 2)
+    by = packed.reshape(E, N * K // 8, 4)
+    x = np.empty((E, N * K // 8, 8), np.uint8)
+    for b in range(4):
+        x[..., 2 * b] = by[..., b] & 15
+        x[..., 2 * b + 1] = by[..., b] >> 4
+    x = x.reshape(E, K // 128, N // 16, 4, 16, 4, 8)      # e, g, cb, h, c, d, p
+    inv = [SIGMA.index(j) for j in range(8)]
+    x = x[..., inv]                                       # p -> j
+    w = x.transpose(0, 2, 4, 1, 5, 3, 6).reshape(E, N, K)  # e, cb, c, g, d, h, j
+    return (w[..., 0::2] | (w[..., 1::2] << 4)).astype(np.uint8)

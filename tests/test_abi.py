@@ -110,13 +110,21 @@ def test_host_validation_rejects_without_launching(lib):
     assert g8(layout=0x10, seg=0) == MOE_ERR_NULL    # packed contiguous still needs seg_offsets
     assert lib.moe_grouped_gemm_int4(0x10 | 7, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), 4, 64, 128,
                                      256, 0, None) == MOE_ERR_SHAPE  # the flag does not make a layout valid
-    # moe_pack_weight_int4
-    assert lib.moe_pack_weight_int4(_p(A16), 2, 100, 128, _p(A16 << 4), None) == MOE_ERR_UNSUPPORTED
-    assert lib.moe_pack_weight_int4(_p(A16), 2, 128, 64, _p(A16 << 4), None) == MOE_ERR_UNSUPPORTED
-    assert lib.moe_pack_weight_int4(_p(A16 + 8), 2, 128, 128, _p(A16 << 4), None) == MOE_ERR_ALIGN
-    assert lib.moe_pack_weight_int4(None, 2, 128, 128, _p(A16 << 4), None) == MOE_ERR_NULL
-    assert lib.moe_pack_weight_int4(_p(A16), 2, 128, 128, _p(A16 + 4096), None) == MOE_ERR_SHAPE  # overlap
-    assert lib.moe_pack_weight_int4(None, 0, 128, 128, None, None) == MOE_OK
+    # moe_pack_weight_int4(q4, s16, E, N, K, q4_packed, s16_packed, stream)
+    def p4(q=A16, sc=A16 << 2, E=2, N=128, K=128, qo=A16 << 4, so=A16 << 6):
+        return lib.moe_pack_weight_int4(_p(q) if q else None, _p(sc) if sc else None, E, N, K, _p(qo) if qo else None,
+                                        _p(so) if so else None, None)
+
+    assert p4(N=100) == MOE_ERR_UNSUPPORTED
+    assert p4(K=64) == MOE_ERR_UNSUPPORTED
+    assert p4(q=A16 + 8) == MOE_ERR_ALIGN
+    assert p4(so=(A16 << 6) + 2) == MOE_ERR_ALIGN
+    assert p4(q=0) == MOE_ERR_NULL
+    assert p4(so=0) == MOE_ERR_NULL
+    assert p4(qo=A16 + 4096) == MOE_ERR_SHAPE         # weights in and out overlap
+    assert p4(so=A16 + 4096) == MOE_ERR_SHAPE         # scales out overlap weights in
+    assert p4(so=(A16 << 4) + 256) == MOE_ERR_SHAPE   # the two outputs overlap
+    assert p4(q=0, sc=0, E=0, qo=0, so=0) == MOE_OK
     assert lib.moe_grouped_gemm_int4(0, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), 4, 64, 100, 256, 0,
                                      None) == MOE_ERR_UNSUPPORTED
     # moe_unpermute_combine

@@ -284,9 +284,9 @@ def test_full_size_int4_decode_layer():
     moe.moe_quant_weight_int4(w, q4, s16)
     kept = {e: u16(w[e]) for e in sample}
     del w
-    q4p = torch.empty_like(q4)
-    moe.moe_pack_weight_int4(q4, q4p)
-    layer = MoeInt4Layer(q4p, s16, k, T, moe.LAYOUT_MASKED, cfg.max_m, expected_m=max(1, T * k // E),
+    q4p, s16p = torch.empty_like(q4), torch.empty_like(s16)
+    moe.moe_pack_weight_int4(q4, s16, q4p, s16p)
+    layer = MoeInt4Layer(q4p, s16p, k, T, moe.LAYOUT_MASKED, cfg.max_m, expected_m=max(1, T * k // E),
                          weights_packed=True)
     z = layer.forward(x.to(DEV), ids.to(DEV), tw.to(DEV))
     torch.cuda.synchronize()

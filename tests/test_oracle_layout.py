@@ -32,26 +32,46 @@ def test_unpack_inverts_pack_and_blocks_are_2kb_fragments():
     assert np.array_equal(packed[0, base + 1024:base + 1040], codes[0, 32, 192:208])
 
 
+def _nib(q4, n, k):
+    b = q4[n, k // 2]
+    return (b >> 4) & 15 if k % 2 else b & 15
+
+
 @pytest.mark.parametrize("E,N,K", [(1, 128, 128), (2, 256, 384)])
-def test_int4_pack_matches_scalar_offsets_everywhere(E, N, K):
+def test_int4_pack_matches_scalar_positions_everywhere(E, N, K):
     rng = np.random.default_rng(N * K)
     q4 = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
-    packed = oracle.pack_weight_int4(q4)
-    offs = np.array([[oracle.packed_offset_int4(n, b, N) for b in range(K // 2)] for n in range(N)])
-    assert np.array_equal(np.sort(offs.reshape(-1)), np.arange(N * K // 2))
+    s16 = rng.integers(0, 65536, size=(E, N, K // 128), dtype=np.uint16)
+    packed, sp = oracle.pack_weight_int4(q4, s16)
+    pos = np.array([[2 * o + h for o, h in (oracle.packed_nibble_int4(n, k, N),)] for n in range(N) for k in range(K)])
+    assert np.array_equal(np.sort(pos.reshape(-1)), np.arange(N * K))  # a bijection onto the nibbles
     for e in range(E):
-        assert np.array_equal(packed[e][offs], q4[e])
+        flat = np.empty(N * K, np.uint8)
+        flat[0::2] = packed[e] & 15
+        flat[1::2] = packed[e] >> 4
+        want = np.array([_nib(q4[e], n, k) for n in range(N) for k in range(K)], np.uint8)
+        assert np.array_equal(flat[pos.reshape(-1)], want)
+        soff = np.array([[oracle.packed_scale_offset_int4(n, g, N) for g in range(K // 128)] for n in range(N)])
+        assert np.array_equal(np.sort(soff.reshape(-1)), np.arange(N * K // 128))
+        assert np.array_equal(sp[e][soff], s16[e])
     assert np.array_equal(oracle.unpack_weight_int4(packed, N, K), q4)
 
 
-def test_int4_blocks_are_1kb_group_fragments():
-    rng = np.random.default_rng(11)
-    E, N, K = 1, 256, 384
-    q4 = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
-    packed = oracle.pack_weight_int4(q4)
-    # group 2 (bytes 128..191 of each column), columns 48..63 (cb = 3)
-    base = (2 * (N // 16) + 3) * 1024
-    assert np.array_equal(packed[0, base:base + 16], q4[0, 48, 128:144])            # lane 0
-    assert np.array_equal(packed[0, base + 5 * 16:base + 6 * 16], q4[0, 53, 128:144])  # lane 5
-    assert np.array_equal(packed[0, base + 21 * 16:base + 22 * 16], q4[0, 53, 144:160])  # lane 21: piece 1
-    assert np.array_equal(packed[0, base + 63 * 16:base + 64 * 16], q4[0, 63, 176:192])  # lane 63: piece 3
+def test_int4_dword_holds_natural_pairs_after_shift_and_mask():
+    """Column 37 of group 1 holds k = 128 + j with value j % 16; the packed dwords decode to natural pairs."""
+    N, K = 128, 256
+    q = np.zeros((N, K), np.uint8)
+    q[37, :] = np.arange(K) % 16
+    q4 = (q[:, 0::2] | (q[:, 1::2] << 4))[None]
+    packed, _ = oracle.pack_weight_int4(q4, np.zeros((1, N, 2), np.uint16))
+    cb, c = divmod(37, 16)
+    for h in range(4):
+        for d in range(4):
+            off = (1 * (N // 16) + cb) * 1024 + 16 * (c + 16 * h) + 4 * d
+            w = int.from_bytes(packed[0, off:off + 4].tobytes(), "little")
+            k0 = 128 + 8 * (4 * d + h)
+            for i in range(4):
+                lo, hi = (w >> (4 * i)) & 15, (w >> (4 * i + 16)) & 15
+                assert (lo, hi) == ((k0 + 2 * i) % 16, (k0 + 2 * i + 1) % 16)
+    # scales: column 37 is in 64-column slice 0, c = 5, cb = 2
+    assert oracle.packed_scale_offset_int4(37, 1, N) == ((1 * 2 + 0) * 16 + 5) * 4 + 2
