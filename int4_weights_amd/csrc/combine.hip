@@ -22,16 +22,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int r = 0; r < k; ++r) {
-      const int p = oi[(int64_t)t * k + r];
-      if (p < 0 || p >= y_rows) continue;
-      const float wt = w[(int64_t)t * k + r];
-      const v4i y = *(const v4i*)(Y + (int64_t)p * N + 8 * c);
+    // slots in batches of 8: every index, then every row load, then the sums
+    // in slot order (two memory round trips per batch instead of two per slot)
+    for (int r0 = 0; r0 < k; r0 += 8) {
+      int p[8];
+      float wt[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t u = (uint32_t)y[i];
-        acc[2 * i] = __builtin_fmaf(wt, bf16_to_f32(u & 0xffffu), acc[2 * i]);
-        acc[2 * i + 1] = __builtin_fmaf(wt, bf16_to_f32(u >> 16), acc[2 * i + 1]);
+      for (int j = 0; j < 8; ++j) {
+        p[j] = r0 + j < k ? oi[(int64_t)t * k + r0 + j] : -1;
+        wt[j] = r0 + j < k ? w[(int64_t)t * k + r0 + j] : 0.0f;
+      }
+      v4i y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        y[j] = (p[j] >= 0 && p[j] < y_rows) ? *(const v4i*)(Y + (int64_t)p[j] * N + 8 * c) : v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (p[j] < 0 || p[j] >= y_rows) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t u = (uint32_t)y[j][i];
+          acc[2 * i] = __builtin_fmaf(wt[j], bf16_to_f32(u & 0xffffu), acc[2 * i]);
+          acc[2 * i + 1] = __builtin_fmaf(wt[j], bf16_to_f32(u >> 16), acc[2 * i + 1]);
+        }
       }
     }
     v4i o;

@@ -283,7 +283,8 @@ __device__ __forceinline__ void int4_unit_packed(const GemmArgs& a, const Unit& 
     constexpr int slot = decltype(slot_c)::value;
     const uint32_t ks = (uint32_t)min(ks_req, KG - 1);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) wq[slot][cb] = *(const v4i*)(wbase + (ks * wstep + 1024u * cb));
+    for (int cb = 0; cb < 4; ++cb)  // read once: streamed past the caches
+      wq[slot][cb] = __builtin_nontemporal_load((const v4i*)(wbase + (ks * wstep + 1024u * cb)));
     sq[slot] = *(const uint2*)(sbase + ks * (uint32_t)N);
   };
   auto issue_a = [&](int ks_req, auto slot_c) {
@@ -352,8 +353,12 @@ __device__ __forceinline__ void int4_unit_packed(const GemmArgs& a, const Unit& 
   }
 }
 
+// Three workgroups per CU (12 waves): the load latency of one wave is covered by
+// the others, so each keeps only the next group's loads in flight.
+constexpr int kI4PackedWgPerCu = 3;
+
 template <int S, int SA>
-__global__ __launch_bounds__(256, 1) void gemm_int4_packed_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(256, kI4PackedWgPerCu) void gemm_int4_packed_kernel(const GemmArgs a) {
   __shared__ int s_up[kMaxExperts + 1], s_tmp[257];
   const Sched sc{s_up};
   sched_build<16>(a, sc, s_tmp);
@@ -380,12 +385,12 @@ static hipError_t launch_i4p(const GemmArgs& a, hipStream_t s) {
   const int cus = device_info().cus;
   int grid = cus - cus % kXcds;
   if (grid < kXcds) grid = kXcds;
-  gemm_int4_packed_kernel<S, SA><<<grid, 256, 0, s>>>(a);
+  gemm_int4_packed_kernel<S, SA><<<kI4PackedWgPerCu * grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s) {
-  if (a.wpacked) return launch_i4p<8, 4>(a, s);  // 16-row units whatever the rows per expert
+  if (a.wpacked) return launch_i4p<2, 2>(a, s);  // 16-row units whatever the rows per expert
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 64);
   if (em <= 16) return launch_i4<1, 8>(a, s);
   return launch_i4<4, 4>(a, s);

@@ -59,17 +59,30 @@ __device__ inline int rank_subchunk(int id, int E, int nbits, int* s_hist, int* 
 
 __device__ inline int id_bits(int E) { return 32 - __clz(E); }  // bits to hold 0..E
 
-// Copy one payload row (all lanes of the wave cooperate).
-__device__ inline void copy_row(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t nbytes) {
-  const int lane = lane_id();
-  const bool v16 = ((nbytes & 15) == 0) && ((((uintptr_t)src) | ((uintptr_t)dst)) & 15) == 0;
-  if (v16) {
-    for (int64_t off = (int64_t)lane * 16; off < nbytes; off += 64 * 16)
-      *(v4i*)(dst + off) = *(const v4i*)(src + off);
-  } else {
-    for (int64_t off = (int64_t)lane * 4; off < nbytes; off += 64 * 4)
-      *(uint32_t*)(dst + off) = *(const uint32_t*)(src + off);
+// Copy one payload row (all lanes of the wave cooperate).  Loads go out in
+// batches of 8 per lane before any store: the compiler cannot move a load
+// above a store to a possibly aliasing address, so a plain loop would pay one
+// memory round trip per 1 KB.
+template <typename T>
+__device__ inline void copy_row_as(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t nbytes) {
+  constexpr int kB = 8;
+  constexpr int64_t kStep = 64 * (int64_t)sizeof(T);
+  for (int64_t base = (int64_t)lane_id() * sizeof(T); base < nbytes; base += kB * kStep) {
+    T r[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      if (base + b * kStep < nbytes) r[b] = *(const T*)(src + base + b * kStep);
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      if (base + b * kStep < nbytes) *(T*)(dst + base + b * kStep) = r[b];
   }
+}
+__device__ inline void copy_row(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t nbytes) {
+  const bool v16 = ((nbytes & 15) == 0) && ((((uintptr_t)src) | ((uintptr_t)dst)) & 15) == 0;
+  if (v16)
+    copy_row_as<v4i>(src, dst, nbytes);
+  else
+    copy_row_as<uint32_t>(src, dst, nbytes);
 }
 
 __device__ inline void place_route(const RouteArgs& a, int i, int p) {
