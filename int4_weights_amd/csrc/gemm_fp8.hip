@@ -212,20 +212,19 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 }
 
 // ----------------------------------------------------------------------------
-// Tall tiles (prefill): up to 192 rows x 256 columns per unit, each wave 64
-// columns, v_mfma_scale_f32_16x16x128_f8f6f4 as in the short-tile kernel.
-// NW = 4: one wave per 64-column group takes all 12 row blocks (one wave per
-// SIMD).  NW = 8: two waves per group take the even and the odd row blocks,
-// two waves per SIMD, so one multiplies while the other waits on memory.
-//  * Weights are private to a column group and stream from HBM straight into
-//    a 3-deep register ring (2 K blocks in flight); activations are shared and
-//    copied global->LDS (global_load_lds) into a 3-deep LDS ring.  Every K
-//    block issues the same loads (the tail re-reads the last block), so one
+// Tall tiles (prefill): up to 192 rows x 256 columns per unit, 4 waves, each
+// owning 64 columns and all 12 row blocks (one wave per SIMD),
+// v_mfma_scale_f32_16x16x128_f8f6f4 as in the short-tile kernel.
+//  * Weights are private to a wave and stream from HBM straight into an
+//    S-deep register ring (S - 1 K blocks in flight); activations are shared
+//    and copied global->LDS (global_load_lds) into an S-deep LDS ring.  Every
+//    K block issues the same loads (the tail re-reads the last block), so one
 //    exact vmcnt serves every step.
-//  * Scales: the unit's row scales are one contiguous block of SFA (its rows
-//    are consecutive); they are read once per unit and kept in LDS as E8M0
-//    exponent bytes, [K block][row], so a step reads one byte per lane for
-//    each 16-row block.  The wave's weight scales are staged the same way.
+//  * Scales ride the same pipeline, so a unit starts without any staging
+//    round trip: each LDS slot carries its K block's fp32 row scales (one
+//    4-byte global_load_lds per lane, 256 rows per block), each wave loads
+//    its weight scale for the block into a register ring, and the E8M0
+//    exponent is the fp32 pattern shifted right by 23.
 //  * The K loop and the epilogue are written out in assembly
 //    (gen_fp8_asm.py -> gemm_fp8_tall_loop.inc): fixed registers for the
 //    accumulators and the weight ring, the next row block's activation
@@ -236,25 +235,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 #include "gemm_fp8_tall_loop.inc"
 
 constexpr int kTRows = MOE_FP8_TALL_ROWS;
+constexpr int kTS = MOE_FP8_TALL_S;
+constexpr int kTApw = MOE_FP8_TALL_APW;
 
-template <int NW>
-struct TallCfg;
-template <>
-struct TallCfg<4> {
-  static constexpr int S = MOE_FP8_TALL4_S, kApw = MOE_FP8_TALL4_APW;
-};
-template <>
-struct TallCfg<8> {
-  static constexpr int S = MOE_FP8_TALL8_S, kApw = MOE_FP8_TALL8_APW;
-};
-
-template <int NW>
 struct Fp8TallSmem {
-  uint8_t a[TallCfg<NW>::S][MOE_FP8_TALL_SLOT_A];      // activation rows, 128 B each, 16-B chunks XOR-swizzled
-  uint8_t sae[kMaxKBlocks][MOE_FP8_TALL_SAE_ROWS];      // row-scale exponents of the unit, [K block][row]
-  float sw[NW][kMaxKBlocks];                            // per-wave weight scales of the current unit
+  // per ring slot: activation rows (128 B each, 16-B chunks XOR-swizzled), then the block's fp32 row scales
+  uint8_t a[kTS][MOE_FP8_TALL_SLOT];
 };
-static_assert(MOE_FP8_TALL_SLOT_A == kTRows * 128 && MOE_FP8_TALL_SAE_ROWS == kTRows, "tall slots");
+static_assert(MOE_FP8_TALL_SLOT_A == kTRows * 128 && MOE_FP8_TALL_SCALE_ROWS == 256 && kTApw == 6, "tall slots");
 
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
@@ -262,57 +250,22 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// The asm statement of one unit (the operand list differs with the number of
-// activation copies per wave).
-#define MOE_TALL_ASM(LOOP, CLOBBERS, AO_OUTS)                                                                     \
+#define MOE_TALL_ASM(LOOP)                                                                                       \
   asm volatile(LOOP                                                                                             \
-               : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), [wo2] "+v"(wo[2]), [wo3] "+v"(wo[3]), AO_OUTS,           \
-                 [sep] "+v"(sep), [swp] "+v"(swp), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q),             \
-                 [t] "=&s"(t), [inc] "=&s"(inc), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v)                              \
-               : [wb] "s"(wb), [ab] "s"(ab), [ma] "s"(ma), [alo] "v"(alo), [ahi] "v"(ahi), [db] "s"(db),         \
-                 [dstep] "s"(dstep), [kb] "s"(kb), [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons),        \
-                 [l16] "v"(l16), [wstep] "s"(wstep)                                                             \
-               : "memory", "vcc", "exec", "scc", CLOBBERS)
-#define MOE_AO6 [ao0] "+v"(ao[0]), [ao1] "+v"(ao[1]), [ao2] "+v"(ao[2]), [ao3] "+v"(ao[3]), [ao4] "+v"(ao[4]), \
-                [ao5] "+v"(ao[5])
-#define MOE_AO3 [ao0] "+v"(ao[0]), [ao1] "+v"(ao[1]), [ao2] "+v"(ao[2])
+               : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), [wo2] "+v"(wo[2]), [wo3] "+v"(wo[3]), [ao0] "+v"(ao[0]), \
+                 [ao1] "+v"(ao[1]), [ao2] "+v"(ao[2]), [ao3] "+v"(ao[3]), [ao4] "+v"(ao[4]), [ao5] "+v"(ao[5]), \
+                 [so] "+v"(so), [wso] "+v"(wso), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),  \
+                 [inc] "=&s"(inc), [inc4] "=&s"(inc4), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v)                         \
+               : [wb] "s"(wb), [ab] "s"(ab), [sb] "s"(sb), [swb] "s"(swb), [ma] "s"(ma), [ms] "s"(ms),           \
+                 [alo] "v"(alo), [ahi] "v"(ahi), [sadr] "v"(sadr), [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb), \
+                 [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [l16] "v"(l16), [wstep] "s"(wstep)         \
+               : "memory", "vcc", "exec", "scc", MOE_FP8_TALL_CLOBBERS)
 
-// The unit's row scales (mrows x KB fp32, contiguous) -> LDS exponent bytes
-// sae[kb * kTRows + r], by all threads, in batches of kB coalesced loads.
-template <int NW>
-__device__ __forceinline__ void stage_row_exponents(const float* sfa, int mrows, int KB, uint8_t* sae) {
-  constexpr int NT = NW * 64, kB = 16;
-  const int total = mrows * KB;
-  const float inv = 1.0f / (float)KB;
-  for (int base = threadIdx.x; base < total; base += NT * kB) {
-    uint32_t v[kB];
-#pragma unroll
-    for (int i = 0; i < kB; ++i) {
-      const int idx = base + i * NT;
-      v[i] = idx < total ? __float_as_uint(sfa[idx]) : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < kB; ++i) {
-      const int idx = base + i * NT;
-      if (idx < total) {
-        int r = (int)(((float)idx + 0.5f) * inv);  // idx / KB, corrected to be exact below
-        int kb = idx - r * KB;
-        if (kb < 0) { --r; kb += KB; }
-        if (kb >= KB) { ++r; kb -= KB; }
-        sae[kb * kTRows + r] = (uint8_t)(v[i] >> 23);
-      }
-    }
-  }
-}
-
-template <int NW, bool PACKED>
-__device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, Fp8TallSmem<NW>& sm, int wv,
-                                              int lane) {
-  constexpr int NWR = NW / 4, kApw = TallCfg<NW>::kApw;
+template <bool PACKED>
+__device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, Fp8TallSmem& sm, int wv, int lane) {
   const int l16 = lane & 15, lg = lane >> 4;
-  const int wr = wv / 4, wc = wv % 4;  // row group (row blocks wr, wr + NWR, ...) and 64-column group
   const int K = a.K, N = a.N, KB = K / 128, NB = N / 128;
-  const int ncol0 = u.n0 + 64 * wc;
+  const int ncol0 = u.n0 + 64 * wv;
   const int won = ncol0 < N ? 1 : 0;
   const int ncl = won ? ncol0 : N - 64;  // an idle wave re-reads valid columns and stores nothing
 
@@ -324,66 +277,51 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
                    : (uint32_t)(ncl + 16 * c + l16) * (uint32_t)K + 16u * lg;
   const int wstep = uniform(PACKED ? 128 * N : 128);  // weight bytes per K block
   const uint64_t ab = uniform_u64((uint64_t)(a.A + (int64_t)u.row0 * K));
-  uint32_t ao[kApw];
+  uint32_t ao[kTApw];
 #pragma unroll
-  for (int i = 0; i < kApw; ++i) {
-    const int r = 8 * (wv * kApw + i) + (lane >> 3);  // tile row this lane copies
-    const int c = (lane & 7) ^ ((r >> 1) & 7);        // its chunk, landing at position lane & 7
+  for (int i = 0; i < kTApw; ++i) {
+    const int r = 8 * (wv * kTApw + i) + (lane >> 3);  // tile row this lane copies
+    const int c = (lane & 7) ^ ((r >> 1) & 7);         // its chunk, landing at position lane & 7
     ao[i] = (uint32_t)min(r, u.mrows - 1) * (uint32_t)K + 16u * c;
   }
-  // this wave's weight scales and the unit's row-scale exponents -> LDS, with
-  // ordinary loads (nothing else is in flight here; the previous unit ended
-  // with a barrier, so no wave still reads these).  The loads of a batch are
-  // all issued before any is used, so staging costs a few memory round trips.
-  {
-    const float* swsrc = (const float*)a.SW + ((int64_t)u.e * NB + ncl / 128) * KB;
-    float w4[kMaxKBlocks / 64];
-#pragma unroll
-    for (int i = 0; i < kMaxKBlocks / 64; ++i) w4[i] = 64 * i < KB ? swsrc[min(64 * i + lane, KB - 1)] : 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxKBlocks / 64; ++i)
-      if (64 * i < KB) sm.sw[wv][64 * i + lane] = w4[i];
-  }
-  stage_row_exponents<NW>(a.SFA + (int64_t)u.row0 * KB, u.mrows, KB, &sm.sae[0][0]);
+  // row scales: lane copies row 64 wv + lane (the unit's last row past its end), 4 bytes per K block
+  const uint64_t sb = uniform_u64((uint64_t)(a.SFA + (int64_t)u.row0 * KB));
+  uint32_t so = (uint32_t)min(64 * wv + lane, u.mrows - 1) * (uint32_t)(KB * 4);
+  // weight scale of this wave's 64 columns (one 128-column block), the same address in every lane
+  const uint64_t swb = uniform_u64((uint64_t)((const float*)a.SW + ((int64_t)u.e * NB + ncl / 128) * KB));
+  uint32_t wso = 0;
 
   const int fsw = (l16 >> 1) & 7;  // fragment reads: row m at m*128, chunk c at position c ^ ((m >> 1) & 7)
-  const uint32_t abase = lds_offset(&sm.a[0][0]) + wr * 2048;  // this wave's first row block
+  const uint32_t abase = lds_offset(&sm.a[0][0]);
   const uint32_t alo = abase + l16 * 128 + 16 * (lg ^ fsw);
   const uint32_t ahi = abase + l16 * 128 + 16 * ((4 + lg) ^ fsw);
-  const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.a[0][wv * kApw * 1024]));
-  uint32_t sep = lds_offset(&sm.sae[0][16 * wr + l16]);
-  uint32_t swp = lds_offset(&sm.sw[wv][0]);
+  const uint32_t sadr = abase + MOE_FP8_TALL_SLOT_A + 4 * l16;
+  const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.a[0][wv * kTApw * 1024]));
+  const uint32_t ms = (uint32_t)uniform((int)lds_offset(&sm.a[0][MOE_FP8_TALL_SLOT_A + wv * 256]));
   const uint64_t db = uniform_u64((uint64_t)(a.D + (int64_t)u.row0 * N));
-  uint32_t doff = (uint32_t)((16 * wr + l16) * N + ncol0 + 4 * lg) * 2u;
-  const int dstep = uniform(32 * N * NWR);  // output bytes between this wave's row blocks
-  const int nblk = (u.mrows + 15) / 16;
-  const int rbe = uniform((nblk - wr + NWR - 1) / NWR);
-  const int kb = uniform(KB), mrows = uniform(u.mrows - 16 * wr), wons = uniform(won);
-  int ks, q, t, inc, m0v = 0;
+  uint32_t doff = (uint32_t)(l16 * N + ncol0 + 4 * lg) * 2u;
+  const int dstep = uniform(32 * N);  // output bytes between row blocks
+  const int rbe = uniform((u.mrows + 15) / 16);
+  const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
+  int ks, q, t, inc, inc4, m0v = 0;
   uint64_t sv;
-  if constexpr (NW == 4) {
-    if constexpr (PACKED) MOE_TALL_ASM(MOE_FP8_TALL4_LOOP_PACKED, MOE_FP8_TALL4_CLOBBERS, MOE_AO6);
-    else MOE_TALL_ASM(MOE_FP8_TALL4_LOOP, MOE_FP8_TALL4_CLOBBERS, MOE_AO6);
-  } else {
-    if constexpr (PACKED) MOE_TALL_ASM(MOE_FP8_TALL8_LOOP_PACKED, MOE_FP8_TALL8_CLOBBERS, MOE_AO3);
-    else MOE_TALL_ASM(MOE_FP8_TALL8_LOOP, MOE_FP8_TALL8_CLOBBERS, MOE_AO3);
-  }
+  if constexpr (PACKED) MOE_TALL_ASM(MOE_FP8_TALL_LOOP_PACKED);
+  else MOE_TALL_ASM(MOE_FP8_TALL_LOOP);
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_tall_kernel(const GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) Fp8TallSmem<NW> sm;
+__global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(const GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) Fp8TallSmem sm;
   __shared__ int s_up[kMaxExperts + 1];
   const Sched sc{s_up};
-  // the scan scratch (NW*64 + 1 ints) borrows the weight-scale staging, idle until the first unit
-  sched_build<kTRows>(a, sc, (int*)&sm.sw[0][0]);
+  // the scan scratch (257 ints) borrows the first ring slot, idle until the first unit
+  sched_build<kTRows>(a, sc, (int*)&sm.a[0][0]);
   const Walk walk = sched_walk(s_up[a.E]);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
     const Unit u = sched_unit<kTRows>(a, sc, v);
-    if (a.wpacked) fp8_unit_tall<NW, true>(a, u, sm, wv, lane);
-    else fp8_unit_tall<NW, false>(a, u, sm, wv, lane);
+    if (a.wpacked) fp8_unit_tall<true>(a, u, sm, wv, lane);
+    else fp8_unit_tall<false>(a, u, sm, wv, lane);
   }
 }
 
@@ -396,23 +334,11 @@ static hipError_t launch_fp8(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-#ifndef MOE_TALL_WAVES
-#define MOE_TALL_WAVES 4
-#endif
-
 static hipError_t launch_fp8_tall(const GemmArgs& a, hipStream_t s) {
   const int cus = device_info().cus;
   int grid = cus - cus % kXcds;
   if (grid < kXcds) grid = kXcds;
-  // The asm loop pins registers: refuse (rather than dispatch) a build whose
-  // register use does not fit a workgroup of this size.
-  static const int max_threads = [] {
-    hipFuncAttributes fa;
-    if (hipFuncGetAttributes(&fa, (const void*)gemm_fp8_tall_kernel<MOE_TALL_WAVES>) != hipSuccess) return 0;
-    return fa.maxThreadsPerBlock;
-  }();
-  if (max_threads < MOE_TALL_WAVES * 64) return hipErrorInvalidConfiguration;
-  gemm_fp8_tall_kernel<MOE_TALL_WAVES><<<grid, MOE_TALL_WAVES * 64, 0, s>>>(a);
+  gemm_fp8_tall_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

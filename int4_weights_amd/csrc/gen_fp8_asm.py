@@ -12,24 +12,22 @@ burst, and exact vector-memory wait counts.
 
 Unit tile: up to 192 rows x 256 columns, one 128-wide K block per step,
 v_mfma_scale_f32_16x16x128_f8f6f4 with the power-of-two scales passed as E8M0
-exponents.  Each wave owns 64 columns (4 column blocks of 16).  Two shapes:
+exponents.  4 waves, each owning 64 columns (4 column blocks of 16) and all 12
+row blocks (1 wave per SIMD, 512 registers).
 
-  NWR = 1: 4 waves, each all 12 row blocks (1 wave per SIMD, 512 registers);
-  NWR = 2: 8 waves, two per 64-column group, taking the even and the odd row
-           blocks (2 waves per SIMD, so one multiplies while the other waits;
-           256 registers each: the weight ring lives in AGPRs).
-
-The unit's row scales are staged in LDS as exponent bytes [K block][row]
-before the loop, so a step reads one byte per lane for each row block.
+The scales travel with the K pipeline instead of being staged per unit: each
+ring slot of LDS holds the K block's activation rows and, after them, the
+block's fp32 row scales (one global_load_lds_dword per wave: 64 rows each, the
+4 waves cover 256 rows); each wave also loads its weight scale for the block
+into a VGPR ring.  The exponent is the fp32 bit pattern shifted right by 23.
 
 Register map (physical, listed as clobbers of the asm statement):
-  NWR = 1: a[0:191] accumulators (block j, column block c at a[16j + 4c]),
-           a[192:207] activation fragments (2 buffers), v[256-32S:255] weight
-           ring (S slots x 4 column blocks x 8), v[224-32S:255-32S] addresses,
-           scale exponents, epilogue temporaries.
-  NWR = 2: a[0:95] accumulators, a[96:111] activation fragments,
-           a[112:112+32S-1] weight ring, v[40-2S:47] addresses, scale exponents,
-           epilogue temporaries.
+  a[0:191] accumulators (block j, column block c at a[16j + 4c]);
+  a[192:207] activation fragments (2 buffers);
+  v[256-32S:255] weight ring (S slots x 4 column blocks x 8);
+  below it: per slot the two fragment addresses, the row-scale address and the
+  weight-scale register; the two exponents in use, the output offset and 16
+  epilogue temporaries.
 
 Usage: python gen_fp8_asm.py OUT.inc
 """
@@ -40,49 +38,40 @@ import sys
 
 CB = 4            # 16-column blocks per wave
 ROWS = 192        # rows per unit at most
-SLOT_A = ROWS * 128   # bytes of one activation slot in LDS
-SAE_ROWS = ROWS        # bytes per K block of the staged row-scale exponents
+SLOT_A = ROWS * 128   # activation bytes of one ring slot in LDS
+SCALE_ROWS = 256      # row scales per slot (4 waves x 64 lanes; rows past the unit repeat its last row)
+SLOT = SLOT_A + 4 * SCALE_ROWS  # bytes of one ring slot
+APW = ROWS // 8 // 4  # 1-KB activation copies per wave per K block
 
 
 class Cfg:
-    def __init__(self, nwr: int, S: int, name: str):
-        self.nwr, self.S, self.name = nwr, S, name
-        self.nw = 4 * nwr                        # waves per workgroup
-        self.rbw = ROWS // 16 // nwr             # row blocks per wave at most
-        self.apw = ROWS // 8 // self.nw          # 1-KB activation copies per wave per K block
-        self.ops = 2 * CB + self.apw             # vector-memory instructions per wave per K block
+    def __init__(self, S: int, name: str):
+        self.S, self.name = S, name
+        self.rbw = ROWS // 16                    # row blocks per wave at most
+        self.apw = APW
+        self.ops = 2 * CB + APW + 2              # vector-memory instructions per wave per K block
         self.wait = self.ops * (S - 2)           # outstanding once the block about to be used has landed
-        if nwr == 1:
-            self.wbase = 256 - 32 * S            # weight ring in VGPRs
-            self.wreg_prefix = "v"
-            self.buf0 = 192
-            self.v_alo = self.wbase - 32
-        else:
-            self.wbase = 112                     # weight ring in AGPRs
-            self.wreg_prefix = "a"
-            self.buf0 = 96
-            self.v_alo = 48 - (2 * S + 8)        # addresses, exponents, output offset, 4 temporaries below v48
-        self.v_swe = self.v_alo + 2 * S          # weight-scale exponent
+        assert self.wait <= 63, "vmcnt holds at most 63"
+        self.wbase = 256 - 32 * S                # weight ring
+        self.v_alo = self.wbase - (4 * S + 20)   # fragment addresses (2 per slot)
+        self.v_sadr = self.v_alo + 2 * S         # row-scale LDS address, per slot
+        self.v_swr = self.v_sadr + S             # weight scale, per slot
+        self.v_swe = self.v_swr + S              # weight-scale exponent
         self.v_sae = self.v_swe + 1              # row-scale exponents, 2 buffers
         self.v_doff = self.v_swe + 3             # running output offset
-        self.v_t = self.v_swe + 4                # epilogue temporaries
-        self.n_t = 16 if nwr == 1 else 4
-        if nwr == 2:
-            assert self.v_t + self.n_t <= 48, "8-wave map must stay below v48"
-        else:
-            assert self.v_t + self.n_t <= self.wbase
-        self.agpr_top = self.wbase + 32 * S if nwr == 2 else 208
+        self.v_t = self.v_swe + 4                # 16 epilogue temporaries
+        assert self.v_t + 16 == self.wbase and self.v_alo >= 0
 
     def acc(self, j, c):
         return 16 * j + 4 * c
 
     def buf(self, b):
-        return self.buf0 + 8 * b
+        return 192 + 8 * b
 
 
 def wrange(cfg, s, c, lo, hi):
     r = cfg.wbase + 32 * s + 8 * c
-    return f"{cfg.wreg_prefix}[{r + lo}:{r + hi}]"
+    return f"v[{r + lo}:{r + hi}]"
 
 
 def issue_items(cfg, t, half):
@@ -93,31 +82,31 @@ def issue_items(cfg, t, half):
         items.append([f"global_load_dwordx4 {wrange(cfg, t, c, 0, 3)}, %[wo{c}], %[wb]"])
         items.append([f"global_load_dwordx4 {wrange(cfg, t, c, 4, 7)}, %[wo{c}], %[wb] offset:{half}"])
     for i in range(cfg.apw):
-        items.append([f"s_add_u32 m0, %[ma], {t * SLOT_A + i * 1024}", "s_nop 0",
+        items.append([f"s_add_u32 m0, %[ma], {t * SLOT + i * 1024}", "s_nop 0",
                       f"global_load_lds_dwordx4 %[ao{i}], %[ab]"])
+    items.append([f"s_add_u32 m0, %[ms], {t * SLOT}", "s_nop 0", "global_load_lds_dword %[so], %[sb]"])
+    items.append([f"global_load_dword v{cfg.v_swr + t}, %[wso], %[swb]"])
     upd = ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0",
-           "s_cselect_b32 %[t], %[wstep], 0"]
+           "s_cselect_b32 %[t], %[wstep], 0", "s_cselect_b32 %[inc4], 4, 0"]
     upd += [f"v_add_u32_e32 %[wo{c}], %[t], %[wo{c}]" for c in range(CB)]
     upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(cfg.apw)]
+    upd += ["v_add_u32_e32 %[so], %[inc4], %[so]", "v_add_u32_e32 %[wso], %[inc4], %[wso]"]
     return items, upd
 
 
 def compute(cfg, s, t, half):
-    """Multiply K block s of the ring (this wave's row blocks 0 .. rbe-1) and issue the loads of ring
-    slot t on the way, one after each row block (the rest after the last)."""
+    """Multiply K block s of the ring (row blocks 0 .. rbe-1) and issue the loads of ring slot t on the
+    way, one item after each row block (the rest after the last)."""
     items, upd = issue_items(cfg, t, half)
-    lo, hi = cfg.v_alo + 2 * s, cfg.v_alo + 2 * s + 1
-    aoff = 2048 * cfg.nwr      # LDS distance between this wave's consecutive row blocks
-    soff = 16 * cfg.nwr        # same for the staged row-scale exponents
+    lo, hi, sadr = cfg.v_alo + 2 * s, cfg.v_alo + 2 * s + 1, cfg.v_sadr + s
     b0 = cfg.buf(0)
     out = [
-        f"ds_read_b32 v{cfg.v_swe}, %[swp]",
-        "v_add_u32_e32 %[swp], 4, %[swp]",
+        f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}",
         f"ds_read_b128 a[{b0}:{b0 + 3}], v{lo}",
         f"ds_read_b128 a[{b0 + 4}:{b0 + 7}], v{hi}",
-        f"ds_read_u8 v{cfg.v_sae}, %[sep]",
+        f"ds_read_b32 v{cfg.v_sae}, v{sadr}",
         "s_waitcnt lgkmcnt(0)",
-        f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swe}",
+        f"v_lshrrev_b32_e32 v{cfg.v_sae}, 23, v{cfg.v_sae}",
     ]
     k = 0
     for j in range(cfg.rbw):
@@ -128,9 +117,9 @@ def compute(cfg, s, t, half):
             out += [
                 f"s_cmp_le_u32 %[rbe], {j + 1}",
                 "s_cbranch_scc1 3f",
-                f"ds_read_b128 a[{bb}:{bb + 3}], v{lo} offset:{(j + 1) * aoff}",
-                f"ds_read_b128 a[{bb + 4}:{bb + 7}], v{hi} offset:{(j + 1) * aoff}",
-                f"ds_read_u8 v{cfg.v_sae + bn}, %[sep] offset:{soff * (j + 1)}",
+                f"ds_read_b128 a[{bb}:{bb + 3}], v{lo} offset:{(j + 1) * 2048}",
+                f"ds_read_b128 a[{bb + 4}:{bb + 7}], v{hi} offset:{(j + 1) * 2048}",
+                f"ds_read_b32 v{cfg.v_sae + bn}, v{sadr} offset:{64 * (j + 1)}",
                 "3:",
             ]
         out.append("s_nop 1")
@@ -139,14 +128,13 @@ def compute(cfg, s, t, half):
             bb = cfg.buf(b)
             out.append(f"v_mfma_scale_f32_16x16x128_f8f6f4 a[{a0}:{a0 + 3}], {wrange(cfg, s, c, 0, 7)}, "
                        f"a[{bb}:{bb + 7}], a[{a0}:{a0 + 3}], v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
-        out += ["s_waitcnt lgkmcnt(0)", "5:"]
+        out += ["s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}", "5:"]
         if k < len(items):
             out += items[k]
             k += 1
     for it in items[k:]:
         out += it
     out += upd
-    out.append(f"v_add_u32_e32 %[sep], {SAE_ROWS}, %[sep]")
     return out
 
 
@@ -183,36 +171,22 @@ def epilogue(cfg):
             "v_cmp_gt_i32_e32 vcc, %[t], %[l16]",
             "s_and_saveexec_b64 %[sv], vcc",
         ]
-        if cfg.n_t >= 16:
-            for c in range(CB):
-                for r in range(4):
-                    out.append(f"v_accvgpr_read_b32 v{T + 4 * c + r}, a{cfg.acc(j, c) + r}")
-            out.append("s_nop 1")
-            for c in range(CB):
-                p = cfg.v_alo + 2 * c
-                out.append(f"v_cvt_pk_bf16_f32 v{p}, v{T + 4 * c}, v{T + 4 * c + 1}")
-                out.append(f"v_cvt_pk_bf16_f32 v{p + 1}, v{T + 4 * c + 2}, v{T + 4 * c + 3}")
-            out.append("s_nop 1")
-            for c in range(CB):
-                p = cfg.v_alo + 2 * c
-                out.append(f"global_store_dwordx2 v{cfg.v_doff}, v[{p}:{p + 1}], %[db] offset:{32 * c}")
-        else:
-            # one column block at a time through 4 temporaries and a packed pair; a store must have
-            # read the pair before the next conversion overwrites it (s_waitcnt vmcnt(0))
-            for c in range(CB):
-                for r in range(4):
-                    out.append(f"v_accvgpr_read_b32 v{T + r}, a{cfg.acc(j, c) + r}")
-                out.append("s_nop 1")
-                out.append(f"v_cvt_pk_bf16_f32 v{cfg.v_alo}, v{T}, v{T + 1}")
-                out.append(f"v_cvt_pk_bf16_f32 v{cfg.v_alo + 1}, v{T + 2}, v{T + 3}")
-                out.append("s_nop 1")
-                out.append(f"global_store_dwordx2 v{cfg.v_doff}, v[{cfg.v_alo}:{cfg.v_alo + 1}], %[db] "
-                           f"offset:{32 * c}")
-                out.append("s_waitcnt vmcnt(0)")
+        for c in range(CB):
+            for r in range(4):
+                out.append(f"v_accvgpr_read_b32 v{T + 4 * c + r}, a{cfg.acc(j, c) + r}")
+        out.append("s_nop 1")
+        for c in range(CB):
+            p = cfg.v_alo + 2 * c
+            out.append(f"v_cvt_pk_bf16_f32 v{p}, v{T + 4 * c}, v{T + 4 * c + 1}")
+            out.append(f"v_cvt_pk_bf16_f32 v{p + 1}, v{T + 4 * c + 2}, v{T + 4 * c + 3}")
+        out.append("s_nop 1")
+        for c in range(CB):
+            p = cfg.v_alo + 2 * c
+            out.append(f"global_store_dwordx2 v{cfg.v_doff}, v[{p}:{p + 1}], %[db] offset:{32 * c}")
         out += [
             "s_mov_b64 exec, %[sv]",
             f"v_add_u32_e32 v{cfg.v_doff}, %[dstep], v{cfg.v_doff}",
-            f"s_sub_i32 %[t], %[t], {16 * cfg.nwr}",
+            "s_sub_i32 %[t], %[t], 16",
         ]
     out.append("7:")
     return out
@@ -220,10 +194,12 @@ def epilogue(cfg):
 
 def program(cfg, half):
     S = cfg.S
-    out = [f"v_mov_b32_e32 v{cfg.v_alo}, %[alo]", f"v_mov_b32_e32 v{cfg.v_alo + 1}, %[ahi]"]
+    out = [f"v_mov_b32_e32 v{cfg.v_alo}, %[alo]", f"v_mov_b32_e32 v{cfg.v_alo + 1}, %[ahi]",
+           f"v_mov_b32_e32 v{cfg.v_sadr}, %[sadr]"]
     for s in range(1, S):
-        out.append(f"v_add_u32_e32 v{cfg.v_alo + 2 * s}, {s * SLOT_A}, %[alo]")
-        out.append(f"v_add_u32_e32 v{cfg.v_alo + 2 * s + 1}, {s * SLOT_A}, %[ahi]")
+        out.append(f"v_add_u32_e32 v{cfg.v_alo + 2 * s}, {s * SLOT}, %[alo]")
+        out.append(f"v_add_u32_e32 v{cfg.v_alo + 2 * s + 1}, {s * SLOT}, %[ahi]")
+        out.append(f"v_add_u32_e32 v{cfg.v_sadr + s}, {s * SLOT}, %[sadr]")
     out += [f"v_accvgpr_write_b32 a{r}, 0" for r in range(cfg.acc(cfg.rbw, 0))]
     out += ["s_mov_b32 %[q], 0"]
     for t in range(S - 1):
@@ -237,14 +213,11 @@ def program(cfg, half):
 
 
 def clobbers(cfg):
-    if cfg.nwr == 1:
-        regs = [f'"v{r}"' for r in range(cfg.v_alo, 256)] + [f'"a{r}"' for r in range(0, 208)]
-    else:
-        regs = [f'"v{r}"' for r in range(cfg.v_alo, 48)] + [f'"a{r}"' for r in range(0, cfg.agpr_top)]
+    regs = [f'"v{r}"' for r in range(cfg.v_alo, 256)] + [f'"a{r}"' for r in range(0, 208)]
     return ", ".join(regs)
 
 
-CONFIGS = [Cfg(1, 3, "TALL4"), Cfg(2, 3, "TALL8")]
+CONFIGS = [Cfg(4, "TALL")]
 
 
 def main():
@@ -252,17 +225,18 @@ def main():
     with open(out_path, "w") as f:
         f.write("// Generated by gen_fp8_asm.py -- do not edit.\n")
         f.write(f"#define MOE_FP8_TALL_ROWS {ROWS}\n#define MOE_FP8_TALL_SLOT_A {SLOT_A}\n"
-                f"#define MOE_FP8_TALL_SAE_ROWS {SAE_ROWS}\n")
+                f"#define MOE_FP8_TALL_SLOT {SLOT}\n#define MOE_FP8_TALL_SCALE_ROWS {SCALE_ROWS}\n"
+                f"#define MOE_FP8_TALL_APW {APW}\n")
         for cfg in CONFIGS:
-            f.write(f"// {cfg.name}: {cfg.nw} waves, ring {cfg.S}, {cfg.rbw} row blocks per wave, "
-                    f"{cfg.apw} activation copies and {cfg.ops} loads per wave per K block, wait {cfg.wait}\n")
+            f.write(f"// {cfg.name}: ring {cfg.S}, {cfg.rbw} row blocks per wave, {cfg.apw} activation copies "
+                    f"and {cfg.ops} loads per wave per K block, wait {cfg.wait}\n")
             for suffix, half in (("", 64), ("_PACKED", 1024)):
                 f.write(f"#define MOE_FP8_{cfg.name}_LOOP{suffix} \\\n")
                 for ln in program(cfg, half):
                     f.write(f'  "{ln}\\n" \\\n')
                 f.write("  \"\"\n")
             f.write(f"#define MOE_FP8_{cfg.name}_CLOBBERS {clobbers(cfg)}\n")
-            f.write(f"#define MOE_FP8_{cfg.name}_S {cfg.S}\n#define MOE_FP8_{cfg.name}_APW {cfg.apw}\n")
+            f.write(f"#define MOE_FP8_{cfg.name}_S {cfg.S}\n")
 
 
 if __name__ == "__main__":
