@@ -212,8 +212,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 }
 
 // ----------------------------------------------------------------------------
-// Tall tiles (prefill): up to 192 rows x 256 columns per unit, 4 waves, each
-// owning 64 columns and all 12 row blocks (one wave per SIMD),
+// Tall tiles (prefill): up to 192 or 256 rows x 256 columns per unit, 4 waves,
+// each owning 64 columns and all 12 or 16 row blocks (one wave per SIMD),
 // v_mfma_scale_f32_16x16x128_f8f6f4 as in the short-tile kernel.
 //  * Weights are private to a wave and stream from HBM straight into an
 //    S-deep register ring (S - 1 K blocks in flight); activations are shared
@@ -234,15 +234,27 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 //    to nearest even) in the epilogue.
 #include "gemm_fp8_tall_loop.inc"
 
-constexpr int kTRows = MOE_FP8_TALL_ROWS;
-constexpr int kTS = MOE_FP8_TALL_S;
-constexpr int kTApw = MOE_FP8_TALL_APW;
+template <int ROWS>
+struct TallCfg;
+template <>
+struct TallCfg<192> {
+  static constexpr int S = MOE_FP8_TALL192_S, kApw = MOE_FP8_TALL192_APW, kSlot = MOE_FP8_TALL192_SLOT,
+                       kSlotA = MOE_FP8_TALL192_SLOT_A;
+};
+template <>
+struct TallCfg<256> {
+  static constexpr int S = MOE_FP8_TALL256_S, kApw = MOE_FP8_TALL256_APW, kSlot = MOE_FP8_TALL256_SLOT,
+                       kSlotA = MOE_FP8_TALL256_SLOT_A;
+};
 
+template <int ROWS>
 struct Fp8TallSmem {
   // per ring slot: activation rows (128 B each, 16-B chunks XOR-swizzled), then the block's fp32 row scales
-  uint8_t a[kTS][MOE_FP8_TALL_SLOT];
+  uint8_t a[TallCfg<ROWS>::S][TallCfg<ROWS>::kSlot];
 };
-static_assert(MOE_FP8_TALL_SLOT_A == kTRows * 128 && MOE_FP8_TALL_SCALE_ROWS == 256 && kTApw == 6, "tall slots");
+static_assert(MOE_FP8_TALL_SCALE_ROWS == 256, "row scales: 4 waves x 64 lanes");
+static_assert(TallCfg<192>::kSlotA == 192 * 128 && TallCfg<192>::kApw * 32 == 192, "192-row slots");
+static_assert(TallCfg<256>::kSlotA == 256 * 128 && TallCfg<256>::kApw * 32 == 256, "256-row slots");
 
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
@@ -250,19 +262,20 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-#define MOE_TALL_ASM(LOOP)                                                                                       \
+#define MOE_TALL_ASM(LOOP, AO_OUTS, CLOBBERS)                                                                     \
   asm volatile(LOOP                                                                                             \
-               : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), [wo2] "+v"(wo[2]), [wo3] "+v"(wo[3]), [ao0] "+v"(ao[0]), \
-                 [ao1] "+v"(ao[1]), [ao2] "+v"(ao[2]), [ao3] "+v"(ao[3]), [ao4] "+v"(ao[4]), [ao5] "+v"(ao[5]), \
+               : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), [wo2] "+v"(wo[2]), [wo3] "+v"(wo[3]), AO_OUTS,               \
                  [so] "+v"(so), [wso] "+v"(wso), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),  \
                  [inc] "=&s"(inc), [inc4] "=&s"(inc4), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v)                         \
                : [wb] "s"(wb), [ab] "s"(ab), [sb] "s"(sb), [swb] "s"(swb), [ma] "s"(ma), [ms] "s"(ms),           \
                  [alo] "v"(alo), [ahi] "v"(ahi), [sadr] "v"(sadr), [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb), \
                  [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [l16] "v"(l16), [wstep] "s"(wstep)         \
-               : "memory", "vcc", "exec", "scc", MOE_FP8_TALL_CLOBBERS)
+               : "memory", "vcc", "exec", "scc", CLOBBERS)
 
-template <bool PACKED>
-__device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, Fp8TallSmem& sm, int wv, int lane) {
+template <int ROWS, bool PACKED>
+__device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, Fp8TallSmem<ROWS>& sm, int wv,
+                                              int lane) {
+  constexpr int kTApw = TallCfg<ROWS>::kApw, kSlotA = TallCfg<ROWS>::kSlotA;
   const int l16 = lane & 15, lg = lane >> 4;
   const int K = a.K, N = a.N, KB = K / 128, NB = N / 128;
   const int ncol0 = u.n0 + 64 * wv;
@@ -295,9 +308,9 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   const uint32_t abase = lds_offset(&sm.a[0][0]);
   const uint32_t alo = abase + l16 * 128 + 16 * (lg ^ fsw);
   const uint32_t ahi = abase + l16 * 128 + 16 * ((4 + lg) ^ fsw);
-  const uint32_t sadr = abase + MOE_FP8_TALL_SLOT_A + 4 * l16;
+  const uint32_t sadr = abase + kSlotA + 4 * l16;
   const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.a[0][wv * kTApw * 1024]));
-  const uint32_t ms = (uint32_t)uniform((int)lds_offset(&sm.a[0][MOE_FP8_TALL_SLOT_A + wv * 256]));
+  const uint32_t ms = (uint32_t)uniform((int)lds_offset(&sm.a[0][kSlotA + wv * 256]));
   const uint64_t db = uniform_u64((uint64_t)(a.D + (int64_t)u.row0 * N));
   uint32_t doff = (uint32_t)(l16 * N + ncol0 + 4 * lg) * 2u;
   const int dstep = uniform(32 * N);  // output bytes between row blocks
@@ -305,23 +318,33 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
   int ks, q, t, inc, inc4, m0v = 0;
   uint64_t sv;
-  if constexpr (PACKED) MOE_TALL_ASM(MOE_FP8_TALL_LOOP_PACKED);
-  else MOE_TALL_ASM(MOE_FP8_TALL_LOOP);
+  if constexpr (ROWS == 192) {
+    if constexpr (PACKED)
+      MOE_TALL_ASM(MOE_FP8_TALL192_LOOP_PACKED, MOE_FP8_TALL192_AO_OUTS, MOE_FP8_TALL192_CLOBBERS);
+    else
+      MOE_TALL_ASM(MOE_FP8_TALL192_LOOP, MOE_FP8_TALL192_AO_OUTS, MOE_FP8_TALL192_CLOBBERS);
+  } else {
+    if constexpr (PACKED)
+      MOE_TALL_ASM(MOE_FP8_TALL256_LOOP_PACKED, MOE_FP8_TALL256_AO_OUTS, MOE_FP8_TALL256_CLOBBERS);
+    else
+      MOE_TALL_ASM(MOE_FP8_TALL256_LOOP, MOE_FP8_TALL256_AO_OUTS, MOE_FP8_TALL256_CLOBBERS);
+  }
 }
 
+template <int ROWS>
 __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(const GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) Fp8TallSmem sm;
+  __shared__ __attribute__((aligned(1024))) Fp8TallSmem<ROWS> sm;
   __shared__ int s_up[kMaxExperts + 1];
   const Sched sc{s_up};
   // the scan scratch (257 ints) borrows the first ring slot, idle until the first unit
-  sched_build<kTRows>(a, sc, (int*)&sm.a[0][0]);
+  sched_build<ROWS>(a, sc, (int*)&sm.a[0][0]);
   const Walk walk = sched_walk(s_up[a.E]);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
-    const Unit u = sched_unit<kTRows>(a, sc, v);
-    if (a.wpacked) fp8_unit_tall<true>(a, u, sm, wv, lane);
-    else fp8_unit_tall<false>(a, u, sm, wv, lane);
+    const Unit u = sched_unit<ROWS>(a, sc, v);
+    if (a.wpacked) fp8_unit_tall<ROWS, true>(a, u, sm, wv, lane);
+    else fp8_unit_tall<ROWS, false>(a, u, sm, wv, lane);
   }
 }
 
@@ -334,11 +357,12 @@ static hipError_t launch_fp8(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int ROWS>
 static hipError_t launch_fp8_tall(const GemmArgs& a, hipStream_t s) {
   const int cus = device_info().cus;
   int grid = cus - cus % kXcds;
   if (grid < kXcds) grid = kXcds;
-  gemm_fp8_tall_kernel<<<grid, 256, 0, s>>>(a);
+  gemm_fp8_tall_kernel<ROWS><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -349,7 +373,11 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s) {
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 256);
   if (em <= 16) return launch_fp8<1, 8, 4>(a, s);
   if (em <= 64) return launch_fp8<4, 6, 4>(a, s);
-  return launch_fp8_tall(a, s);
+  // 256-row tiles read each weight tile once per 256 rows instead of 192 but
+  // copy 256 activation rows per K block whatever the unit holds: worth it
+  // once a typical expert fills them
+  if (em >= 256) return launch_fp8_tall<256>(a, s);
+  return launch_fp8_tall<192>(a, s);
 }
 
 }  // namespace moe

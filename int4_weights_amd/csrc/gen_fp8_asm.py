@@ -10,10 +10,10 @@ are read from LDS while the current block's matrix instructions run, that the
 loads are spread between the matrix instructions instead of issued as one
 burst, and exact vector-memory wait counts.
 
-Unit tile: up to 192 rows x 256 columns, one 128-wide K block per step,
-v_mfma_scale_f32_16x16x128_f8f6f4 with the power-of-two scales passed as E8M0
-exponents.  4 waves, each owning 64 columns (4 column blocks of 16) and all 12
-row blocks (1 wave per SIMD, 512 registers).
+Unit tile: up to 192 or 256 rows x 256 columns, one 128-wide K block per
+step, v_mfma_scale_f32_16x16x128_f8f6f4 with the power-of-two scales passed as
+E8M0 exponents.  4 waves, each owning 64 columns (4 column blocks of 16) and
+all 12 (16) row blocks (1 wave per SIMD, 512 registers).
 
 The scales travel with the K pipeline instead of being staged per unit: each
 ring slot of LDS holds the K block's activation rows and, after them, the
@@ -22,8 +22,9 @@ block's fp32 row scales (one global_load_lds_dword per wave: 64 rows each, the
 into a VGPR ring.  The exponent is the fp32 bit pattern shifted right by 23.
 
 Register map (physical, listed as clobbers of the asm statement):
-  a[0:191] accumulators (block j, column block c at a[16j + 4c]);
-  a[192:207] activation fragments (2 buffers);
+  a[0:16*rows/16-1] accumulators (block j, column block c at a[16j + 4c]);
+  activation fragments (2 buffers of 8): a[192:207] for 192 rows, the 16
+  VGPRs below the weight ring for 256 rows (the accumulators fill the AGPRs);
   v[256-32S:255] weight ring (S slots x 4 column blocks x 8);
   below it: per slot the two fragment addresses, the row-scale address and the
   weight-scale register; the two exponents in use, the output offset and 16
@@ -37,36 +38,39 @@ from __future__ import annotations
 import sys
 
 CB = 4            # 16-column blocks per wave
-ROWS = 192        # rows per unit at most
-SLOT_A = ROWS * 128   # activation bytes of one ring slot in LDS
 SCALE_ROWS = 256      # row scales per slot (4 waves x 64 lanes; rows past the unit repeat its last row)
-SLOT = SLOT_A + 4 * SCALE_ROWS  # bytes of one ring slot
-APW = ROWS // 8 // 4  # 1-KB activation copies per wave per K block
 
 
 class Cfg:
-    def __init__(self, S: int, name: str):
-        self.S, self.name = S, name
-        self.rbw = ROWS // 16                    # row blocks per wave at most
-        self.apw = APW
-        self.ops = 2 * CB + APW + 2              # vector-memory instructions per wave per K block
+    def __init__(self, rows: int, S: int, name: str):
+        assert rows in (192, 256)
+        self.rows, self.S, self.name = rows, S, name
+        self.slot_a = rows * 128                 # activation bytes of one ring slot in LDS
+        self.slot = self.slot_a + 4 * SCALE_ROWS  # bytes of one ring slot
+        self.rbw = rows // 16                    # row blocks per wave at most
+        self.apw = rows // 8 // 4                # 1-KB activation copies per wave per K block
+        self.ops = 2 * CB + self.apw + 2         # vector-memory instructions per wave per K block
         self.wait = self.ops * (S - 2)           # outstanding once the block about to be used has landed
         assert self.wait <= 63, "vmcnt holds at most 63"
         self.wbase = 256 - 32 * S                # weight ring
-        self.v_alo = self.wbase - (4 * S + 20)   # fragment addresses (2 per slot)
+        # activation fragments (2 buffers of 8): AGPRs above the accumulators while they fit
+        self.frag_v = 16 * self.rbw + 16 > 256
+        self.v_frag = self.wbase - 16
+        self.v_alo = (self.v_frag if self.frag_v else self.wbase) - (4 * S + 20)  # fragment addresses (2 per slot)
         self.v_sadr = self.v_alo + 2 * S         # row-scale LDS address, per slot
         self.v_swr = self.v_sadr + S             # weight scale, per slot
         self.v_swe = self.v_swr + S              # weight-scale exponent
         self.v_sae = self.v_swe + 1              # row-scale exponents, 2 buffers
         self.v_doff = self.v_swe + 3             # running output offset
         self.v_t = self.v_swe + 4                # 16 epilogue temporaries
-        assert self.v_t + 16 == self.wbase and self.v_alo >= 0
+        assert self.v_alo >= 0
 
     def acc(self, j, c):
         return 16 * j + 4 * c
 
-    def buf(self, b):
-        return 192 + 8 * b
+    def buf(self, b, lo=0, hi=7):
+        base = (self.v_frag if self.frag_v else 16 * self.rbw) + 8 * b
+        return f"{'v' if self.frag_v else 'a'}[{base + lo}:{base + hi}]"
 
 
 def wrange(cfg, s, c, lo, hi):
@@ -82,9 +86,9 @@ def issue_items(cfg, t, half):
         items.append([f"global_load_dwordx4 {wrange(cfg, t, c, 0, 3)}, %[wo{c}], %[wb]"])
         items.append([f"global_load_dwordx4 {wrange(cfg, t, c, 4, 7)}, %[wo{c}], %[wb] offset:{half}"])
     for i in range(cfg.apw):
-        items.append([f"s_add_u32 m0, %[ma], {t * SLOT + i * 1024}", "s_nop 0",
+        items.append([f"s_add_u32 m0, %[ma], {t * cfg.slot + i * 1024}", "s_nop 0",
                       f"global_load_lds_dwordx4 %[ao{i}], %[ab]"])
-    items.append([f"s_add_u32 m0, %[ms], {t * SLOT}", "s_nop 0", "global_load_lds_dword %[so], %[sb]"])
+    items.append([f"s_add_u32 m0, %[ms], {t * cfg.slot}", "s_nop 0", "global_load_lds_dword %[so], %[sb]"])
     items.append([f"global_load_dword v{cfg.v_swr + t}, %[wso], %[swb]"])
     upd = ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0",
            "s_cselect_b32 %[t], %[wstep], 0", "s_cselect_b32 %[inc4], 4, 0"]
@@ -99,11 +103,10 @@ def compute(cfg, s, t, half):
     way, one item after each row block (the rest after the last)."""
     items, upd = issue_items(cfg, t, half)
     lo, hi, sadr = cfg.v_alo + 2 * s, cfg.v_alo + 2 * s + 1, cfg.v_sadr + s
-    b0 = cfg.buf(0)
     out = [
         f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}",
-        f"ds_read_b128 a[{b0}:{b0 + 3}], v{lo}",
-        f"ds_read_b128 a[{b0 + 4}:{b0 + 7}], v{hi}",
+        f"ds_read_b128 {cfg.buf(0, 0, 3)}, v{lo}",
+        f"ds_read_b128 {cfg.buf(0, 4, 7)}, v{hi}",
         f"ds_read_b32 v{cfg.v_sae}, v{sadr}",
         "s_waitcnt lgkmcnt(0)",
         f"v_lshrrev_b32_e32 v{cfg.v_sae}, 23, v{cfg.v_sae}",
@@ -113,21 +116,19 @@ def compute(cfg, s, t, half):
         b, bn = j % 2, 1 - j % 2
         out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 5f"]  # no row block j: only its load item
         if j + 1 < cfg.rbw:
-            bb = cfg.buf(bn)
             out += [
                 f"s_cmp_le_u32 %[rbe], {j + 1}",
                 "s_cbranch_scc1 3f",
-                f"ds_read_b128 a[{bb}:{bb + 3}], v{lo} offset:{(j + 1) * 2048}",
-                f"ds_read_b128 a[{bb + 4}:{bb + 7}], v{hi} offset:{(j + 1) * 2048}",
+                f"ds_read_b128 {cfg.buf(bn, 0, 3)}, v{lo} offset:{(j + 1) * 2048}",
+                f"ds_read_b128 {cfg.buf(bn, 4, 7)}, v{hi} offset:{(j + 1) * 2048}",
                 f"ds_read_b32 v{cfg.v_sae + bn}, v{sadr} offset:{64 * (j + 1)}",
                 "3:",
             ]
         out.append("s_nop 1")
         for c in range(CB):
             a0 = cfg.acc(j, c)
-            bb = cfg.buf(b)
             out.append(f"v_mfma_scale_f32_16x16x128_f8f6f4 a[{a0}:{a0 + 3}], {wrange(cfg, s, c, 0, 7)}, "
-                       f"a[{bb}:{bb + 7}], a[{a0}:{a0 + 3}], v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
+                       f"{cfg.buf(b)}, a[{a0}:{a0 + 3}], v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
         out += ["s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}", "5:"]
         if k < len(items):
             out += items[k]
@@ -197,9 +198,9 @@ def program(cfg, half):
     out = [f"v_mov_b32_e32 v{cfg.v_alo}, %[alo]", f"v_mov_b32_e32 v{cfg.v_alo + 1}, %[ahi]",
            f"v_mov_b32_e32 v{cfg.v_sadr}, %[sadr]"]
     for s in range(1, S):
-        out.append(f"v_add_u32_e32 v{cfg.v_alo + 2 * s}, {s * SLOT}, %[alo]")
-        out.append(f"v_add_u32_e32 v{cfg.v_alo + 2 * s + 1}, {s * SLOT}, %[ahi]")
-        out.append(f"v_add_u32_e32 v{cfg.v_sadr + s}, {s * SLOT}, %[sadr]")
+        out.append(f"v_add_u32_e32 v{cfg.v_alo + 2 * s}, {s * cfg.slot}, %[alo]")
+        out.append(f"v_add_u32_e32 v{cfg.v_alo + 2 * s + 1}, {s * cfg.slot}, %[ahi]")
+        out.append(f"v_add_u32_e32 v{cfg.v_sadr + s}, {s * cfg.slot}, %[sadr]")
     out += [f"v_accvgpr_write_b32 a{r}, 0" for r in range(cfg.acc(cfg.rbw, 0))]
     out += ["s_mov_b32 %[q], 0"]
     for t in range(S - 1):
@@ -213,30 +214,33 @@ def program(cfg, half):
 
 
 def clobbers(cfg):
-    regs = [f'"v{r}"' for r in range(cfg.v_alo, 256)] + [f'"a{r}"' for r in range(0, 208)]
+    top = 16 * cfg.rbw + (0 if cfg.frag_v else 16)
+    regs = [f'"v{r}"' for r in range(cfg.v_alo, 256)] + [f'"a{r}"' for r in range(0, top)]
     return ", ".join(regs)
 
 
-CONFIGS = [Cfg(4, "TALL")]
+CONFIGS = [Cfg(192, 4, "TALL192"), Cfg(256, 4, "TALL256")]
 
 
 def main():
     out_path = sys.argv[1]
     with open(out_path, "w") as f:
         f.write("// Generated by gen_fp8_asm.py -- do not edit.\n")
-        f.write(f"#define MOE_FP8_TALL_ROWS {ROWS}\n#define MOE_FP8_TALL_SLOT_A {SLOT_A}\n"
-                f"#define MOE_FP8_TALL_SLOT {SLOT}\n#define MOE_FP8_TALL_SCALE_ROWS {SCALE_ROWS}\n"
-                f"#define MOE_FP8_TALL_APW {APW}\n")
+        f.write(f"#define MOE_FP8_TALL_SCALE_ROWS {SCALE_ROWS}\n")
         for cfg in CONFIGS:
-            f.write(f"// {cfg.name}: ring {cfg.S}, {cfg.rbw} row blocks per wave, {cfg.apw} activation copies "
-                    f"and {cfg.ops} loads per wave per K block, wait {cfg.wait}\n")
+            n = cfg.name
+            f.write(f"// {n}: {cfg.rows} rows, ring {cfg.S}, {cfg.rbw} row blocks per wave, {cfg.apw} activation "
+                    f"copies and {cfg.ops} loads per wave per K block, wait {cfg.wait}\n")
+            f.write(f"#define MOE_FP8_{n}_SLOT_A {cfg.slot_a}\n#define MOE_FP8_{n}_SLOT {cfg.slot}\n"
+                    f"#define MOE_FP8_{n}_APW {cfg.apw}\n#define MOE_FP8_{n}_S {cfg.S}\n")
+            f.write(f"#define MOE_FP8_{n}_AO_OUTS " + ", ".join(f'[ao{i}] "+v"(ao[{i}])' for i in range(cfg.apw))
+                    + "\n")
             for suffix, half in (("", 64), ("_PACKED", 1024)):
-                f.write(f"#define MOE_FP8_{cfg.name}_LOOP{suffix} \\\n")
+                f.write(f"#define MOE_FP8_{n}_LOOP{suffix} \\\n")
                 for ln in program(cfg, half):
                     f.write(f'  "{ln}\\n" \\\n')
                 f.write("  \"\"\n")
-            f.write(f"#define MOE_FP8_{cfg.name}_CLOBBERS {clobbers(cfg)}\n")
-            f.write(f"#define MOE_FP8_{cfg.name}_S {cfg.S}\n")
+            f.write(f"#define MOE_FP8_{n}_CLOBBERS {clobbers(cfg)}\n")
 
 
 if __name__ == "__main__":

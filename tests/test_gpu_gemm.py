@@ -64,7 +64,7 @@ def _check_fp8(c, D):
 
 
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("expected_m", [0, 16, 64])
+@pytest.mark.parametrize("expected_m", [0, 16, 64, 256])
 def test_fp8_contiguous_ragged(expected_m, packed):
     require_gpu()
     c = _fp8_case(1, [0, 1, 17, 130, 300], N=384, K=640, layout=moe.LAYOUT_CONTIGUOUS)
@@ -81,10 +81,10 @@ def test_fp8_masked_with_overfull_expert(expected_m, packed):
 
 @pytest.mark.parametrize("packed", [False, True])
 def test_fp8_masked_tall_segments(packed):
-    """Masked layout with segments taller than one 192-row tile (the tall-tile kernel, several M chunks)."""
+    """Masked layout with segments taller than one tall tile (192 or 256 rows: several M chunks, ragged tails)."""
     require_gpu()
-    c = _fp8_case(12, [150, 0, 200, 65], N=384, K=768, layout=moe.LAYOUT_MASKED, max_m=200)
-    for em in (0, 200):
+    c = _fp8_case(12, [150, 0, 300, 65], N=384, K=768, layout=moe.LAYOUT_MASKED, max_m=300)
+    for em in (0, 200, 256):
         _check_fp8(c, _run_fp8(c, em, packed=packed))
 
 
@@ -128,7 +128,8 @@ def test_fp8_small_integers_bit_exact():
     c = dict(E=E, N=N, K=K, rows=256, starts=starts, eff=counts, counts=counts, layout=moe.LAYOUT_CONTIGUOUS,
              max_m=0, a=a, sfa=np.ones((256, K // 128), np.float32), w=w, sfw=np.ones((E, N // 128, K // 128),
                                                                                           np.float32))
-    for em, packed in ((0, False), (16, False), (64, False), (0, True), (16, True)):
+    # em 16 and 64: short tiles; 128: 192-row tall tiles; 0 (contiguous default) and 256: 256-row tall tiles
+    for em, packed in ((0, False), (16, False), (64, False), (128, False), (0, True), (16, True), (128, True)):
         D = _run_fp8(c, em, packed=packed)
         for e in range(E):
             s, n = int(starts[e]), int(counts[e])
