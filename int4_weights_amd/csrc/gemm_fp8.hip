@@ -213,8 +213,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 
 // ----------------------------------------------------------------------------
 // Tall tiles (prefill): up to 192 or 256 rows x 256 columns per unit, 4 waves,
-// each owning 64 columns and all 12 or 16 row blocks (one wave per SIMD),
-// v_mfma_scale_f32_16x16x128_f8f6f4 as in the short-tile kernel.
+// each owning 64 columns and all 6 or 8 row tiles of 32 (one wave per SIMD),
+// v_mfma_scale_f32_32x32x64_f8f6f4 (full rate from a single wave per SIMD,
+// where the 16x16x128 form needs two).
 //  * Weights are private to a wave and stream from HBM straight into an
 //    S-deep register ring (S - 1 K blocks in flight); activations are shared
 //    and copied global->LDS (global_load_lds) into an S-deep LDS ring.  Every
@@ -229,8 +230,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 //    (gen_fp8_asm.py -> gemm_fp8_tall_loop.inc): fixed registers for the
 //    accumulators and the weight ring, the next row block's activation
 //    fragments read from LDS while the current block's matrix instructions
-//    run, loads spread between the matrix instructions, 16-row granularity
-//    (a unit computes ceil(rows/16) row blocks), and v_cvt_pk_bf16_f32 (round
+//    run, loads spread between the matrix instructions, 32-row granularity
+//    (a unit computes ceil(rows/32) row tiles), and v_cvt_pk_bf16_f32 (round
 //    to nearest even) in the epilogue.
 #include "gemm_fp8_tall_loop.inc"
 
@@ -264,30 +265,32 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
 
 #define MOE_TALL_ASM(LOOP, AO_OUTS, CLOBBERS)                                                                     \
   asm volatile(LOOP                                                                                             \
-               : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), [wo2] "+v"(wo[2]), [wo3] "+v"(wo[3]), AO_OUTS,               \
+               : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), AO_OUTS,                                                    \
                  [so] "+v"(so), [wso] "+v"(wso), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),  \
                  [inc] "=&s"(inc), [inc4] "=&s"(inc4), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v)                         \
                : [wb] "s"(wb), [ab] "s"(ab), [sb] "s"(sb), [swb] "s"(swb), [ma] "s"(ma), [ms] "s"(ms),           \
-                 [alo] "v"(alo), [ahi] "v"(ahi), [sadr] "v"(sadr), [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb), \
-                 [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [l16] "v"(l16), [wstep] "s"(wstep)         \
+                 [a00] "v"(af[0]), [a01] "v"(af[1]), [a10] "v"(af[2]), [a11] "v"(af[3]), [sadr] "v"(sadr),        \
+                 [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb),                                                 \
+                 [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [l32] "v"(l32), [wstep] "s"(wstep)         \
                : "memory", "vcc", "exec", "scc", CLOBBERS)
 
 template <int ROWS, bool PACKED>
 __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, Fp8TallSmem<ROWS>& sm, int wv,
                                               int lane) {
   constexpr int kTApw = TallCfg<ROWS>::kApw, kSlotA = TallCfg<ROWS>::kSlotA;
-  const int l16 = lane & 15, lg = lane >> 4;
+  const int l32 = lane & 31, hh = lane >> 5;  // operand row and K half of this lane
   const int K = a.K, N = a.N, KB = K / 128, NB = N / 128;
   const int ncol0 = u.n0 + 64 * wv;
   const int won = ncol0 < N ? 1 : 0;
   const int ncl = won ? ncol0 : N - 64;  // an idle wave re-reads valid columns and stores nothing
 
+  // weights: column tile c (32 columns) of this wave; see the operand notes in gen_fp8_asm.py
   const uint64_t wb = uniform_u64((uint64_t)(a.W + (int64_t)u.e * N * K));
-  uint32_t wo[4];
+  uint32_t wo[2];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    wo[c] = PACKED ? (uint32_t)((ncl + 16 * c) / 16) * 2048u + 16u * lane
-                   : (uint32_t)(ncl + 16 * c + l16) * (uint32_t)K + 16u * lg;
+  for (int c = 0; c < 2; ++c)
+    wo[c] = PACKED ? (uint32_t)((ncl + 32 * c) / 16 + l32 / 16) * 2048u + (uint32_t)((l32 & 15) + 32 * hh) * 16u
+                   : (uint32_t)(ncl + 32 * c + l32) * (uint32_t)K + 32u * hh;
   const int wstep = uniform(PACKED ? 128 * N : 128);  // weight bytes per K block
   const uint64_t ab = uniform_u64((uint64_t)(a.A + (int64_t)u.row0 * K));
   uint32_t ao[kTApw];
@@ -304,17 +307,20 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   const uint64_t swb = uniform_u64((uint64_t)((const float*)a.SW + ((int64_t)u.e * NB + ncl / 128) * KB));
   uint32_t wso = 0;
 
-  const int fsw = (l16 >> 1) & 7;  // fragment reads: row m at m*128, chunk c at position c ^ ((m >> 1) & 7)
+  // fragment reads: row m at m*128, chunk c at position c ^ ((m >> 1) & 7); lane (row l32, half hh) reads
+  // chunks 4 kk + 2 hh + p for the halves kk and pieces p of the K block
+  const int fsw = (l32 >> 1) & 7;
   const uint32_t abase = lds_offset(&sm.a[0][0]);
-  const uint32_t alo = abase + l16 * 128 + 16 * (lg ^ fsw);
-  const uint32_t ahi = abase + l16 * 128 + 16 * ((4 + lg) ^ fsw);
-  const uint32_t sadr = abase + kSlotA + 4 * l16;
+  uint32_t af[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) af[i] = abase + l32 * 128 + 16 * ((4 * (i >> 1) + 2 * hh + (i & 1)) ^ fsw);
+  const uint32_t sadr = abase + kSlotA + 4 * l32;
   const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.a[0][wv * kTApw * 1024]));
   const uint32_t ms = (uint32_t)uniform((int)lds_offset(&sm.a[0][kSlotA + wv * 256]));
   const uint64_t db = uniform_u64((uint64_t)(a.D + (int64_t)u.row0 * N));
-  uint32_t doff = (uint32_t)(l16 * N + ncol0 + 4 * lg) * 2u;
-  const int dstep = uniform(32 * N);  // output bytes between row blocks
-  const int rbe = uniform((u.mrows + 15) / 16);
+  uint32_t doff = (uint32_t)(l32 * N + ncol0 + 4 * hh) * 2u;
+  const int dstep = uniform(64 * N);  // output bytes between 32-row tiles
+  const int rbe = uniform((u.mrows + 31) / 32);
   const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
   int ks, q, t, inc, inc4, m0v = 0;
   uint64_t sv;
