@@ -24,8 +24,15 @@ constexpr int kBN = 256;       // columns per unit (4 waves x 64)
 constexpr int kXcds = 8;
 constexpr int kNGroup = 16;    // N-tiles per 2-D block of an expert's units
 
+// The unit table in LDS: unit prefix per expert and the expert's rows and first
+// packed row, read once from global memory.
+struct SchedSmem {
+  int up[kMaxExperts + 1];
+  int rows[kMaxExperts];
+  int start[kMaxExperts];
+};
 struct Sched {
-  int* up;  // [E+1] unit prefix (LDS)
+  SchedSmem* t;
 };
 
 // Valid rows and first packed row of expert e (clipped to its segment).
@@ -45,17 +52,41 @@ __device__ inline void expert_rows(const GemmArgs& a, int e, int& rows, int& sta
   start = (int)st;
 }
 
-// Build the unit table (all threads of the workgroup; ends with a barrier).
+// Build the unit table (called by all threads of the workgroup; ends with a
+// barrier).  The first wave does the work: each lane takes a run of experts,
+// and one wave-wide scan of the lanes' sums gives the prefix -- no barrier
+// inside, so the first unit starts about one memory round trip after launch.
 template <int BM>
-__device__ inline void sched_build(const GemmArgs& a, Sched s, int* s_tmp) {
-  const int nt = (a.N + kBN - 1) / kBN;
-  for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
-    int r, st;
-    expert_rows(a, e, r, st);
-    s.up[e] = ((r + BM - 1) / BM) * nt;
+__device__ inline void sched_build(const GemmArgs& a, Sched s) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int nt = (a.N + kBN - 1) / kBN;
+    const int per = (a.E + 63) / 64;
+    const int e0 = lane * per;
+    int sum = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < a.E) {
+        int r, st;
+        expert_rows(a, e, r, st);
+        s.t->rows[e] = r;
+        s.t->start[e] = st;
+        s.t->up[e] = sum;  // exclusive within the lane's run
+        sum += ((r + BM - 1) / BM) * nt;
+      }
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int excl = incl - sum;
+    for (int i = 0; i < per; ++i)
+      if (e0 + i < a.E) s.t->up[e0 + i] += excl;
+    if (lane == 63) s.t->up[a.E] = incl;
   }
   __syncthreads();
-  block_exclusive_scan(s.up, a.E, s_tmp);
 }
 
 struct Unit {
@@ -64,10 +95,9 @@ struct Unit {
 
 template <int BM>
 __device__ inline Unit sched_unit(const GemmArgs& a, Sched s, int v) {
-  const int e = uniform(upper_bound_minus1(s.up, a.E, v));
-  int rows, start;
-  expert_rows(a, e, rows, start);
-  const int local = v - s.up[e];
+  const int e = uniform(upper_bound_minus1(s.t->up, a.E, v));
+  const int rows = s.t->rows[e], start = s.t->start[e];
+  const int local = v - s.t->up[e];
   const int chunks = (rows + BM - 1) / BM;
   // Within an expert the units run in 2-D blocks: groups of kNGroup N-tiles,
   // every M chunk of the group before the next group, the N-tiles of one M

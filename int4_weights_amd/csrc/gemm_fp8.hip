@@ -195,11 +195,11 @@ template <int RB, int S, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) {
   using C = Fp8Cfg<RB, S, NW>;
   __shared__ __attribute__((aligned(1024))) Fp8Smem<RB, S, NW> sm;
-  __shared__ int s_up[kMaxExperts + 1], s_tmp[NW * 64 + 1];
+  __shared__ SchedSmem s_sched;
 
-  const Sched sc{s_up};
-  sched_build<C::BM>(a, sc, s_tmp);
-  const Walk walk = sched_walk(s_up[a.E]);
+  const Sched sc{&s_sched};
+  sched_build<C::BM>(a, sc);
+  const Walk walk = sched_walk(s_sched.up[a.E]);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   constexpr int RH = (RB + 1) / 2;  // the shorter tile height
@@ -340,11 +340,10 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
 template <int ROWS>
 __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) Fp8TallSmem<ROWS> sm;
-  __shared__ int s_up[kMaxExperts + 1];
-  const Sched sc{s_up};
-  // the scan scratch (257 ints) borrows the first ring slot, idle until the first unit
-  sched_build<ROWS>(a, sc, (int*)&sm.a[0][0]);
-  const Walk walk = sched_walk(s_up[a.E]);
+  __shared__ SchedSmem s_sched;
+  const Sched sc{&s_sched};
+  sched_build<ROWS>(a, sc);
+  const Walk walk = sched_walk(s_sched.up[a.E]);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {

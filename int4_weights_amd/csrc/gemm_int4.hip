@@ -242,10 +242,10 @@ template <int RB, int S>
 __global__ __launch_bounds__(256, 1) void gemm_int4_kernel(const GemmArgs a) {
   using C = I4Cfg<RB, S>;
   __shared__ __attribute__((aligned(1024))) I4Smem<RB, S> sm;
-  __shared__ int s_up[kMaxExperts + 1], s_tmp[257];
-  const Sched sc{s_up};
-  sched_build<C::BM>(a, sc, s_tmp);
-  const Walk walk = sched_walk(s_up[a.E]);
+  __shared__ SchedSmem s_sched;
+  const Sched sc{&s_sched};
+  sched_build<C::BM>(a, sc);
+  const Walk walk = sched_walk(s_sched.up[a.E]);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
@@ -359,10 +359,10 @@ constexpr int kI4PackedWgPerCu = 3;
 
 template <int S, int SA>
 __global__ __launch_bounds__(256, kI4PackedWgPerCu) void gemm_int4_packed_kernel(const GemmArgs a) {
-  __shared__ int s_up[kMaxExperts + 1], s_tmp[257];
-  const Sched sc{s_up};
-  sched_build<16>(a, sc, s_tmp);
-  const Walk walk = sched_walk(s_up[a.E]);
+  __shared__ SchedSmem s_sched;
+  const Sched sc{&s_sched};
+  sched_build<16>(a, sc);
+  const Walk walk = sched_walk(s_sched.up[a.E]);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
