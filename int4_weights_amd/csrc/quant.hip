@@ -15,42 +15,61 @@
 namespace moe {
 
 // One 16-lane group per 128-element block: lane holds 8 consecutive bf16.
-// A wave covers 4 blocks per step.  HBM-bound: 16-byte loads, 8-byte stores.
+// A wave covers 4 blocks per step and takes kQ steps at a time, all loads
+// first, so kQ KB per wave are in flight.  HBM-bound: 16-byte loads, 8-byte
+// stores.
+constexpr int kQ = 4;
+
+__device__ __forceinline__ void quant_act_block(const v4i raw, int64_t blk, bool ok, int sub, uint8_t* __restrict__ q,
+                                                float* __restrict__ sf) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w = (uint32_t)raw[i];
+    f[2 * i] = bf16_to_f32(w & 0xffffu);
+    f[2 * i + 1] = bf16_to_f32(w >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  const int e = pow2_exponent(amax);
+  // gfx950's v_cvt_pk_fp8_f32 converts to OCP E4M3FN with round to nearest
+  // even, subnormals kept, sign kept; the scaled values never exceed 448
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = __builtin_amdgcn_ldexpf(f[i], -e);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  if (ok) {
+    uint2 out;
+    out.x = (uint32_t)lo;
+    out.y = (uint32_t)hi;
+    *(uint2*)(q + blk * 128 + sub * 8) = out;
+    if (sub == 0) sf[blk] = pow2f(e);
+  }
+}
+
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int64_t nblocks, int kb,
                                                          uint8_t* __restrict__ q, float* __restrict__ sf) {
   const int lane = lane_id();
   const int sub = lane & 15;
   const int64_t gwave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
-  for (int64_t b0 = gwave * 4; b0 < nblocks; b0 += nwaves * 4) {
-    const int64_t blk = b0 + (lane >> 4);
-    const bool ok = blk < nblocks;
-    v4i raw = {0, 0, 0, 0};
-    if (ok) raw = *(const v4i*)(x + blk * 128 + sub * 8);
-    float f[8];
+  for (int64_t b0 = gwave * 4 * kQ; b0 < nblocks; b0 += nwaves * 4 * kQ) {
+    v4i raw[kQ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t w = (uint32_t)raw[i];
-      f[2 * i] = bf16_to_f32(w & 0xffffu);
-      f[2 * i + 1] = bf16_to_f32(w >> 16);
+    for (int j = 0; j < kQ; ++j) {
+      const int64_t blk = b0 + 4 * j + (lane >> 4);
+      raw[j] = blk < nblocks ? *(const v4i*)(x + blk * 128 + sub * 8) : v4i{0, 0, 0, 0};
     }
-    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-    const int e = pow2_exponent(amax);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(__builtin_amdgcn_ldexpf(f[i], -e)) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(__builtin_amdgcn_ldexpf(f[4 + i], -e)) << (8 * i);
-    if (ok) {
-      uint2 out;
-      out.x = lo;
-      out.y = hi;
-      *(uint2*)(q + blk * 128 + sub * 8) = out;
-      if (sub == 0) sf[blk] = pow2f(e);
+    for (int j = 0; j < kQ; ++j) {
+      const int64_t blk = b0 + 4 * j + (lane >> 4);
+      quant_act_block(raw[j], blk, blk < nblocks, sub, q, sf);
     }
   }
 }
@@ -241,7 +260,7 @@ static int grid_for(int64_t work_items, int per_block, int cap) {
 hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int K, uint8_t* q, float* sf, hipStream_t s) {
   const int64_t nblocks = rows * (K / 128);
   if (nblocks == 0) return hipSuccess;
-  const int grid = grid_for(nblocks, 16, device_info().cus * 16);  // 16 blocks per 256-thread WG per step
+  const int grid = grid_for(nblocks, 16 * kQ, device_info().cus * 16);  // 16 kQ blocks per 256-thread WG per pass
   quant_act_kernel<<<grid, 256, 0, s>>>(x, nblocks, K / 128, q, sf);
   return hipGetLastError();
 }
