@@ -353,9 +353,11 @@ __device__ __forceinline__ void int4_unit_packed(const GemmArgs& a, const Unit& 
   }
 }
 
-// Three workgroups per CU (12 waves): the load latency of one wave is covered by
-// the others, so each keeps only the next group's loads in flight.
-constexpr int kI4PackedWgPerCu = 3;
+// Two workgroups per CU (8 waves): the load latency of one wave is covered by
+// the others, so each keeps only the next group's loads in flight (measured:
+// 2 or 3 workgroups per CU with 2-deep rings within 2% of each other, deeper
+// rings no better).
+constexpr int kI4PackedWgPerCu = 2;
 
 template <int S, int SA>
 __global__ __launch_bounds__(256, kI4PackedWgPerCu) void gemm_int4_packed_kernel(const GemmArgs a) {
