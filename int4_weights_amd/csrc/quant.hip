@@ -64,7 +64,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
       const int64_t blk = b0 + 4 * j + (lane >> 4);
-      raw[j] = blk < nblocks ? *(const v4i*)(x + blk * 128 + sub * 8) : v4i{0, 0, 0, 0};
+      // read once: streamed past the caches
+      raw[j] = blk < nblocks ? __builtin_nontemporal_load((const v4i*)(x + blk * 128 + sub * 8)) : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
