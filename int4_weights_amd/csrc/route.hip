@@ -213,18 +213,26 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const RouteArgs a) {
   __shared__ int s_tmp[1025];
   __shared__ int s_flags;
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    int f = 0;
-    for (int c = 0; c < a.nchunks; ++c) f |= a.ws[(int64_t)a.nchunks * a.E + c];
-    s_flags = f;
+  if (tid == 0) s_flags = 0;
+  __syncthreads();
+  for (int c = tid; c < a.nchunks; c += blockDim.x) {
+    const int f = a.ws[(int64_t)a.nchunks * a.E + c];
+    if (f) atomicOr(&s_flags, f);
   }
   for (int e = tid; e < a.E; e += blockDim.x) {
+    // 16 chunks' counts are loaded before any prefix is written back (a plain
+    // loop would pay one memory round trip per chunk: the store may alias)
     int run = 0;
-    for (int c = 0; c < a.nchunks; ++c) {
-      int32_t* p = a.ws + (int64_t)c * a.E + e;
-      const int v = *p;
-      *p = run;
-      run += v;
+    for (int c0 = 0; c0 < a.nchunks; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = c0 + j < a.nchunks ? a.ws[(int64_t)(c0 + j) * a.E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (c0 + j < a.nchunks) {
+          a.ws[(int64_t)(c0 + j) * a.E + e] = run;
+          run += v[j];
+        }
     }
     s_tot[e] = run;
     s_start[e] = run;
