@@ -293,7 +293,7 @@ hipError_t launch_route_pack(const RouteArgs& a0, hipStream_t s) {
   route_scan_kernel<<<1, 1024, 0, s>>>(a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  int g = gather_grid < cus * 8 ? gather_grid : cus * 8;
+  int g = gather_grid < cus * 32 ? gather_grid : cus * 32;
   if (g < 1) g = 1;
   route_gather_kernel<<<g, 256, 0, s>>>(a);
   return hipGetLastError();
