@@ -215,18 +215,20 @@ def run(args):
                 tm.mark(s, 6)
     else:
         # 4-bit weights: several copies rotate across steps so the 256 MB cache never holds the weights
-        copies = []
+        # (one allocation holds all copies, made before the generation temporaries)
         ncopy = 4
+        all_q4 = torch.empty(ncopy, E, N, K // 2, dtype=torch.uint8, device=dev)
+        all_s16 = torch.empty(ncopy, E, N, K // 128, dtype=torch.float16, device=dev)
+        copies = []
         for c in range(ncopy):
             w = synth.expert_weights(cfg, N, K, device=dev, seed=0)
             q4 = torch.empty(E, N, K // 2, dtype=torch.uint8, device=dev)
             s16 = torch.empty(E, N, K // 128, dtype=torch.float16, device=dev)
             moe.moe_quant_weight_int4(w, q4, s16)
             del w
-            q4p, s16p = torch.empty_like(q4), torch.empty_like(s16)
-            moe.moe_pack_weight_int4(q4, s16, q4p, s16p)
+            moe.moe_pack_weight_int4(q4, s16, all_q4[c], all_s16[c])
             del q4, s16
-            copies.append((q4p, s16p))
+            copies.append((all_q4[c], all_s16[c]))
         layer = MoeInt4Layer(copies[0][0], copies[0][1], k, T, moe.LAYOUT_MASKED, cfg.max_m,
                              expected_m=args.expected_m or max(1, R // E), weights_packed=True)
         names = ["moe_route_pack", "gemm", "moe_unpermute_combine"]
