@@ -271,7 +271,8 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
                : [wb] "s"(wb), [ab] "s"(ab), [sb] "s"(sb), [swb] "s"(swb), [ma] "s"(ma), [ms] "s"(ms),           \
                  [a00] "v"(af[0]), [a01] "v"(af[1]), [a10] "v"(af[2]), [a11] "v"(af[3]), [sadr] "v"(sadr),        \
                  [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb),                                                 \
-                 [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [l32] "v"(l32), [wstep] "s"(wstep)         \
+                 [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [wstep] "s"(wstep), [l8] "v"(l8),           \
+                 [xr] "v"(xr), [epb] "v"(epb), [rb] "v"(rb)                                                      \
                : "memory", "vcc", "exec", "scc", CLOBBERS)
 
 template <int ROWS, bool PACKED>
@@ -317,9 +318,15 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   const uint32_t sadr = abase + kSlotA + 4 * l32;
   const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.a[0][wv * kTApw * 1024]));
   const uint32_t ms = (uint32_t)uniform((int)lds_offset(&sm.a[0][kSlotA + wv * 256]));
+  // epilogue: the wave's bf16 rows go through its own LDS region (row m at m*128, 16-byte chunk c at
+  // position c ^ (m & 7)); each lane writes 8 bytes of row l32 and reads back 16 bytes (chunk lane & 7) of
+  // row lane >> 3 of every 8-row group, stored as whole 128-byte rows
+  const uint32_t epb = abase + (uint32_t)(wv * ROWS * 128 + l32 * 128 + 8 * hh);
+  const int xr = l32 & 7, l8 = lane >> 3;
+  const uint32_t rb = abase + (uint32_t)(wv * ROWS * 128 + l8 * 128 + 16 * ((lane & 7) ^ (l8 & 7)));
   const uint64_t db = uniform_u64((uint64_t)(a.D + (int64_t)u.row0 * N));
-  uint32_t doff = (uint32_t)(l32 * N + ncol0 + 4 * hh) * 2u;
-  const int dstep = uniform(64 * N);  // output bytes between 32-row tiles
+  uint32_t doff = (uint32_t)(l8 * N + ncol0 + 8 * (lane & 7)) * 2u;
+  const int dstep = uniform(16 * N);  // output bytes between 8-row groups
   const int rbe = uniform((u.mrows + 31) / 32);
   const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
   int ks, q, t, inc, inc4, m0v = 0;

@@ -40,7 +40,9 @@ Register map (physical, listed as clobbers of the asm statement):
   v[256-32S:255] weight ring (S slots x 2 column tiles x 2 halves x 8);
   below it: per slot the four fragment addresses, the row-scale address and
   the weight-scale register; the two exponents in use, the output offset and
-  16 epilogue temporaries.
+  16 epilogue temporaries.  The epilogue reuses the weight ring for the rows
+  it reads back from LDS and keeps its 8 LDS addresses in the fragment
+  registers (256 rows) or above the rows read back (192 rows).
 
 Usage: python gen_fp8_asm.py OUT.inc
 """
@@ -76,6 +78,11 @@ class Cfg:
         self.v_doff = self.v_swe + 3
         self.v_t = self.v_swe + 4
         assert self.v_alo >= 0 and 6 * S >= 16  # epilogue packs 16 dwords into the address registers
+        # epilogue: 8 LDS chunk addresses in the (then idle) fragment registers or above the rows read back
+        # into the weight ring (4 registers per 8 rows)
+        self.v_ep = self.v_frag if self.frag_v else self.wbase + rows // 2
+        assert self.frag_v or self.v_ep + 8 <= 256
+        assert 4 * (rows // 8) <= 32 * S and 4 * rows * 128 <= S * self.slot  # read-back registers; LDS regions
 
     def acc(self, j, ct):
         return 32 * j + 16 * ct
@@ -165,14 +172,19 @@ def step(cfg, s, last, packed):
 
 
 def epilogue(cfg):
-    """bf16 stores of this wave's rows (rows >= mrows masked off); %[t] counts the rows left."""
+    """bf16 results through LDS to full-line global stores.
+
+    The ring is idle once the loop has ended, so each wave writes its rows x 64 columns of bf16 to a private
+    LDS region (row m at m*128, 16-byte chunk c at position c ^ (m & 7)), reads them back as 16 bytes per lane,
+    8 lanes per row, and stores 8 whole 128-byte rows per instruction (rows >= mrows masked off; %[t] counts
+    the rows left).  A final barrier keeps the next unit's copies into the ring behind every wave's reads."""
     out = ["9:", "s_waitcnt vmcnt(0)", "s_waitcnt lgkmcnt(0)", "s_barrier", "s_nop 15", "s_nop 15",
-           "s_cmp_eq_u32 %[won], 0", "s_cbranch_scc1 7f", "s_mov_b32 %[t], %[mrows]",
-           f"v_mov_b32_e32 v{cfg.v_doff}, %[doff]"]
-    T = cfg.v_t
+           "s_cmp_eq_u32 %[won], 0", "s_cbranch_scc1 7f"]
+    T, E = cfg.v_t, cfg.v_ep
+    for c in range(8):  # LDS address of logical chunk c of this lane's row (plus the lane's 8-byte half)
+        out += [f"v_xor_b32_e32 v{E + c}, {c}, %[xr]", f"v_lshl_add_u32 v{E + c}, v{E + c}, 4, %[epb]"]
     for j in range(cfg.rt):
-        out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 7f", "v_cmp_gt_i32_e32 vcc, %[t], %[l32]",
-                "s_and_saveexec_b64 %[sv], vcc"]
+        out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 6f"]
         for ct in range(2):
             for r in range(16):
                 out.append(f"v_accvgpr_read_b32 v{T + r}, a{cfg.acc(j, ct) + r}")
@@ -181,13 +193,29 @@ def epilogue(cfg):
                 pr = cfg.v_alo + 8 * ct + 2 * g
                 out.append(f"v_cvt_pk_bf16_f32 v{pr}, v{T + 4 * g}, v{T + 4 * g + 1}")
                 out.append(f"v_cvt_pk_bf16_f32 v{pr + 1}, v{T + 4 * g + 2}, v{T + 4 * g + 3}")
-            out.append("s_nop 1")
+        out.append("s_nop 1")
+        for ct in range(2):
             for g in range(4):
                 pr = cfg.v_alo + 8 * ct + 2 * g
-                out.append(f"global_store_dwordx2 v{cfg.v_doff}, v[{pr}:{pr + 1}], %[db] offset:{64 * ct + 16 * g}")
-        out += ["s_mov_b64 exec, %[sv]", f"v_add_u32_e32 v{cfg.v_doff}, %[dstep], v{cfg.v_doff}",
-                "s_sub_i32 %[t], %[t], 32"]
-    out.append("7:")
+                off = f" offset:{4096 * j}" if j else ""
+                out.append(f"ds_write_b64 v{E + 4 * ct + g}, v[{pr}:{pr + 1}]{off}")
+    out += ["6:", "s_waitcnt lgkmcnt(0)"]
+    for j in range(cfg.rt):
+        out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 5f"]
+        for q in range(4):
+            i = 4 * j + q
+            r = cfg.wbase + 4 * i
+            off = f" offset:{1024 * i}" if i else ""
+            out.append(f"ds_read_b128 v[{r}:{r + 3}], %[rb]{off}")
+    out += ["5:", "s_waitcnt lgkmcnt(0)", "s_mov_b32 %[t], %[mrows]", f"v_mov_b32_e32 v{cfg.v_doff}, %[doff]"]
+    for j in range(cfg.rt):
+        out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 7f"]
+        for q in range(4):
+            r = cfg.wbase + 4 * (4 * j + q)
+            out += ["v_cmp_gt_i32_e32 vcc, %[t], %[l8]", "s_and_saveexec_b64 %[sv], vcc",
+                    f"global_store_dwordx4 v{cfg.v_doff}, v[{r}:{r + 3}], %[db]", "s_mov_b64 exec, %[sv]",
+                    f"v_add_u32_e32 v{cfg.v_doff}, %[dstep], v{cfg.v_doff}", "s_sub_i32 %[t], %[t], 8"]
+    out += ["7:", "s_barrier"]
     return out
 
 
