@@ -222,10 +222,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 //    K block issues the same loads (the tail re-reads the last block), so one
 //    exact vmcnt serves every step.
 //  * Scales ride the same pipeline, so a unit starts without any staging
-//    round trip: each LDS slot carries its K block's fp32 row scales (one
-//    4-byte global_load_lds per lane, 256 rows per block), each wave loads
-//    its weight scale for the block into a register ring, and the E8M0
-//    exponent is the fp32 pattern shifted right by 23.
+//    round trip: every 4 K blocks one 16-byte global_load_lds per lane copies
+//    the next 4 fp32 row scales of 256 rows into one of two LDS group buffers
+//    (a 4-byte copy per block would cost as many cache-line requests as the
+//    activations themselves), each wave loads its weight scale for the block
+//    into a register ring, and the E8M0 exponent is the fp32 pattern shifted
+//    right by 23.  This needs K/128 to be a multiple of 4 and SFA 16-byte
+//    aligned; other calls take the 64-row tile.
 //  * The K loop and the epilogue are written out in assembly
 //    (gen_fp8_asm.py -> gemm_fp8_tall_loop.inc): fixed registers for the
 //    accumulators and the weight ring, the next row block's activation
@@ -240,20 +243,24 @@ struct TallCfg;
 template <>
 struct TallCfg<192> {
   static constexpr int S = MOE_FP8_TALL192_S, kApw = MOE_FP8_TALL192_APW, kSlot = MOE_FP8_TALL192_SLOT,
-                       kSlotA = MOE_FP8_TALL192_SLOT_A;
+                       kSlotA = MOE_FP8_TALL192_SLOT_A, kScOff = MOE_FP8_TALL192_SC_OFF,
+                       kLds = MOE_FP8_TALL192_LDS;
 };
 template <>
 struct TallCfg<256> {
   static constexpr int S = MOE_FP8_TALL256_S, kApw = MOE_FP8_TALL256_APW, kSlot = MOE_FP8_TALL256_SLOT,
-                       kSlotA = MOE_FP8_TALL256_SLOT_A;
+                       kSlotA = MOE_FP8_TALL256_SLOT_A, kScOff = MOE_FP8_TALL256_SC_OFF,
+                       kLds = MOE_FP8_TALL256_LDS;
 };
 
 template <int ROWS>
 struct Fp8TallSmem {
-  // per ring slot: activation rows (128 B each, 16-B chunks XOR-swizzled), then the block's fp32 row scales
-  uint8_t a[TallCfg<ROWS>::S][TallCfg<ROWS>::kSlot];
+  // S ring slots of activation rows (128 B each, 16-B chunks XOR-swizzled), then two row-scale group
+  // buffers (row r's 4 fp32 scales at 16 r)
+  uint8_t b[TallCfg<ROWS>::kLds];
 };
 static_assert(MOE_FP8_TALL_SCALE_ROWS == 256, "row scales: 4 waves x 64 lanes");
+static_assert(MOE_FP8_TALL_SCALE_GROUP == 4, "a row-scale copy covers 4 K blocks (16 bytes)");
 static_assert(TallCfg<192>::kSlotA == 192 * 128 && TallCfg<192>::kApw * 32 == 192, "192-row slots");
 static_assert(TallCfg<256>::kSlotA == 256 * 128 && TallCfg<256>::kApw * 32 == 256, "256-row slots");
 
@@ -267,8 +274,8 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   asm volatile(LOOP                                                                                             \
                : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), AO_OUTS,                                                    \
                  [so] "+v"(so), [wso] "+v"(wso), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),  \
-                 [inc] "=&s"(inc), [inc4] "=&s"(inc4), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v)                         \
-               : [wb] "s"(wb), [ab] "s"(ab), [sb] "s"(sb), [swb] "s"(swb), [ma] "s"(ma), [ms] "s"(ms),           \
+                 [inc] "=&s"(inc), [inc4] "=&s"(inc4), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v), [msg] "+s"(msg)                         \
+               : [wb] "s"(wb), [ab] "s"(ab), [sb] "s"(sb), [swb] "s"(swb), [ma] "s"(ma),                       \
                  [a00] "v"(af[0]), [a01] "v"(af[1]), [a10] "v"(af[2]), [a11] "v"(af[3]), [sadr] "v"(sadr),        \
                  [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb),                                                 \
                  [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [wstep] "s"(wstep), [l8] "v"(l8),           \
@@ -278,7 +285,7 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
 template <int ROWS, bool PACKED>
 __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, Fp8TallSmem<ROWS>& sm, int wv,
                                               int lane) {
-  constexpr int kTApw = TallCfg<ROWS>::kApw, kSlotA = TallCfg<ROWS>::kSlotA;
+  constexpr int kTApw = TallCfg<ROWS>::kApw, kScOff = TallCfg<ROWS>::kScOff;
   const int l32 = lane & 31, hh = lane >> 5;  // operand row and K half of this lane
   const int K = a.K, N = a.N, KB = K / 128, NB = N / 128;
   const int ncol0 = u.n0 + 64 * wv;
@@ -301,7 +308,7 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
     const int c = (lane & 7) ^ ((r >> 1) & 7);         // its chunk, landing at position lane & 7
     ao[i] = (uint32_t)min(r, u.mrows - 1) * (uint32_t)K + 16u * c;
   }
-  // row scales: lane copies row 64 wv + lane (the unit's last row past its end), 4 bytes per K block
+  // row scales: lane copies row 64 wv + lane (the unit's last row past its end), 16 bytes per 4 K blocks
   const uint64_t sb = uniform_u64((uint64_t)(a.SFA + (int64_t)u.row0 * KB));
   uint32_t so = (uint32_t)min(64 * wv + lane, u.mrows - 1) * (uint32_t)(KB * 4);
   // weight scale of this wave's 64 columns (one 128-column block), the same address in every lane
@@ -311,13 +318,13 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   // fragment reads: row m at m*128, chunk c at position c ^ ((m >> 1) & 7); lane (row l32, half hh) reads
   // chunks 4 kk + 2 hh + p for the halves kk and pieces p of the K block
   const int fsw = (l32 >> 1) & 7;
-  const uint32_t abase = lds_offset(&sm.a[0][0]);
+  const uint32_t abase = lds_offset(&sm.b[0]);
   uint32_t af[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) af[i] = abase + l32 * 128 + 16 * ((4 * (i >> 1) + 2 * hh + (i & 1)) ^ fsw);
-  const uint32_t sadr = abase + kSlotA + 4 * l32;
-  const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.a[0][wv * kTApw * 1024]));
-  const uint32_t ms = (uint32_t)uniform((int)lds_offset(&sm.a[0][kSlotA + wv * 256]));
+  const uint32_t sadr = abase + kScOff + 16 * l32;  // row scale of row tile j, block s of the group: +512 j + 4 s
+  const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.b[wv * kTApw * 1024]));
+  uint32_t msg = (uint32_t)uniform((int)lds_offset(&sm.b[kScOff + wv * 1024]));  // group buffer 0, this wave's rows
   // epilogue: the wave's bf16 rows go through its own LDS region (row m at m*128, 16-byte chunk c at
   // position c ^ (m & 7)); each lane writes 8 bytes of row l32 and reads back 16 bytes (chunk lane & 7) of
   // row lane >> 3 of every 8-row group, stored as whole 128-byte rows
@@ -384,7 +391,9 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s) {
   // segments use the tall tile (up to 192 rows).
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 256);
   if (em <= 16) return launch_fp8<1, 8, 4>(a, s);
-  if (em <= 64) return launch_fp8<4, 6, 4>(a, s);
+  // the tall tile copies 4 K blocks of row scales per 16-byte load
+  const bool tall_ok = (a.K / 128) % MOE_FP8_TALL_SCALE_GROUP == 0 && (((uintptr_t)a.SFA) & 15) == 0;
+  if (em <= 64 || !tall_ok) return launch_fp8<4, 6, 4>(a, s);
   // 256-row tiles read each weight tile once per 256 rows instead of 192 but
   // copy 256 activation rows per K block whatever the unit holds: worth it
   // once a typical expert fills them

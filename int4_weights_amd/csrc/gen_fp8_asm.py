@@ -51,20 +51,24 @@ from __future__ import annotations
 
 import sys
 
-SCALE_ROWS = 256  # row scales per slot (4 waves x 64 lanes; rows past the unit repeat its last row)
+SCALE_ROWS = 256  # rows of a scale group (4 waves x 64 lanes; rows past the unit repeat its last row)
+GROUP = 4         # K blocks per row-scale copy (one 16-byte copy per row)
 
 
 class Cfg:
     def __init__(self, rows: int, S: int, name: str):
         assert rows in (192, 256)
         self.rows, self.S, self.name = rows, S, name
+        assert S == GROUP, "the unrolled loop body is one scale group"
         self.slot_a = rows * 128                 # activation bytes of one ring slot in LDS
-        self.slot = self.slot_a + 4 * SCALE_ROWS  # bytes of one ring slot
+        self.slot = self.slot_a                   # bytes of one ring slot
+        self.sc_off = S * self.slot               # two scale-group buffers of SCALE_ROWS x 16 bytes follow
+        self.lds = self.sc_off + 2 * SCALE_ROWS * 16
         self.rt = rows // 32                      # 32-row tiles per unit at most
         self.apw = rows // 32                     # 1-KB activation copies per wave per K block
-        self.ops = 8 + self.apw + 2               # vector-memory instructions per wave per K block
-        self.wait = self.ops * (S - 2)            # outstanding once the block about to be used has landed
-        assert self.wait <= 63, "vmcnt holds at most 63"
+        self.ops = 8 + self.apw + 1               # vector-memory instructions per wave per K block (+1 for
+        # the blocks that start a scale group)
+        assert self.wait_at(2) <= 63, "vmcnt holds at most 63"
         self.wbase = 256 - 32 * S
         self.nacc = 32 * self.rt
         self.frag_v = self.nacc + 32 > 256
@@ -87,6 +91,12 @@ class Cfg:
     def acc(self, j, ct):
         return 32 * j + 16 * ct
 
+    def wait_at(self, s):
+        """Loads allowed outstanding at the start of step s (K block ks = s mod S): those of blocks ks + 1
+        .. ks + S - 2, plus one for each of them that starts a scale group."""
+        blocks = [(s + d) % GROUP for d in range(1, self.S - 1)]
+        return self.ops * (self.S - 2) + sum(1 for b in blocks if b == 0)
+
     def buf(self, b, kk, lo=0, hi=7):
         base = (self.v_frag if self.frag_v else self.nacc) + 16 * b + 8 * kk
         return f"{'v' if self.frag_v else 'a'}[{base + lo}:{base + hi}]"
@@ -99,7 +109,9 @@ def wreg(cfg, s, ct, kk, lo, hi):
 
 def issue_items(cfg, t, packed):
     """The loads of one K block into ring slot t, as separate items, and the offset update after them
-    (offsets advance unless the next block would be past the last one)."""
+    (offsets advance unless the next block would be past the last one).  Block t mod S == 0 starts a scale
+    group: one 16-byte copy per row of the group's 4 row scales into the group buffer %[msg] points at
+    (the buffers alternate), its offset advancing unless the next group would be past the last block."""
     items = []
     for ct in range(2):
         for kk in range(2):
@@ -110,13 +122,17 @@ def issue_items(cfg, t, packed):
     for i in range(cfg.apw):
         items.append([f"s_add_u32 m0, %[ma], {t * cfg.slot + i * 1024}", "s_nop 0",
                       f"global_load_lds_dwordx4 %[ao{i}], %[ab]"])
-    items.append([f"s_add_u32 m0, %[ms], {t * cfg.slot}", "s_nop 0", "global_load_lds_dword %[so], %[sb]"])
     items.append([f"global_load_dword v{cfg.v_swr + t}, %[wso], %[swb]"])
-    upd = ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0",
+    upd = []
+    if t % GROUP == 0:
+        items.append(["s_mov_b32 m0, %[msg]", "s_nop 0", "global_load_lds_dwordx4 %[so], %[sb]"])
+        upd += ["s_xor_b32 %[msg], %[msg], " + str(SCALE_ROWS * 16), f"s_add_u32 %[t], %[q], {GROUP}",
+                "s_cmp_lt_u32 %[t], %[kb]", "s_cselect_b32 %[inc4], 16, 0", "v_add_u32_e32 %[so], %[inc4], %[so]"]
+    upd += ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0",
            "s_cselect_b32 %[t], %[wstep], 0", "s_cselect_b32 %[inc4], 4, 0"]
     upd += [f"v_add_u32_e32 %[wo{ct}], %[t], %[wo{ct}]" for ct in range(2)]
     upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(cfg.apw)]
-    upd += ["v_add_u32_e32 %[so], %[inc4], %[so]", "v_add_u32_e32 %[wso], %[inc4], %[wso]"]
+    upd += ["v_add_u32_e32 %[wso], %[inc4], %[wso]"]
     return items, upd
 
 
@@ -135,9 +151,9 @@ def compute(cfg, s, t, packed):
     a few items after each row tile (the rest after the last)."""
     items, upd = issue_items(cfg, t, packed)
     per = -(-len(items) // cfg.rt)
-    sadr = cfg.v_sadr + s
+    sadr = cfg.v_sadr  # row r's scale of K block s of the group at r * 16 + 4 s
     out = [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}"] + frag_reads(cfg, s, 0, 0) + [
-        f"ds_read_b32 v{cfg.v_sae}, v{sadr}", "s_waitcnt lgkmcnt(0)",
+        f"ds_read_b32 v{cfg.v_sae}, v{sadr}" + (f" offset:{4 * s}" if s else ""), "s_waitcnt lgkmcnt(0)",
         f"v_lshrrev_b32_e32 v{cfg.v_sae}, 23, v{cfg.v_sae}"]
     k = 0
     for j in range(cfg.rt):
@@ -145,7 +161,7 @@ def compute(cfg, s, t, packed):
         out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 5f"]  # no row tile j: only its load items
         if j + 1 < cfg.rt:
             out += [f"s_cmp_le_u32 %[rbe], {j + 1}", "s_cbranch_scc1 3f"] + frag_reads(cfg, s, bn, j + 1) + [
-                f"ds_read_b32 v{cfg.v_sae + bn}, v{sadr} offset:{128 * (j + 1)}", "3:"]
+                f"ds_read_b32 v{cfg.v_sae + bn}, v{sadr} offset:{512 * (j + 1) + 4 * s}", "3:"]
         out.append("s_nop 1")
         for kk in range(2):  # consecutive instructions write different accumulators
             for ct in range(2):
@@ -164,8 +180,10 @@ def compute(cfg, s, t, packed):
 
 
 def step(cfg, s, last, packed):
-    out = [f"s_waitcnt vmcnt({cfg.wait})", "s_waitcnt lgkmcnt(0)", "s_barrier"]
+    out = [f"s_waitcnt vmcnt({cfg.wait_at(s)})", "s_waitcnt lgkmcnt(0)", "s_barrier"]
     out += compute(cfg, s, (s + cfg.S - 1) % cfg.S, packed)
+    if last:  # the next step reads the other group buffer
+        out.append(f"v_xor_b32_e32 v{cfg.v_sadr}, {SCALE_ROWS * 16}, v{cfg.v_sadr}")
     out += ["s_add_u32 %[ks], %[ks], 1", "s_cmp_lt_u32 %[ks], %[kb]",
             "s_cbranch_scc1 8b" if last else "s_cbranch_scc0 9f"]
     return out
@@ -230,7 +248,6 @@ def program(cfg, packed):
         for kk in range(2):
             for p in range(2):
                 out.append(f"v_add_u32_e32 v{cfg.v_aadr + 4 * s + 2 * kk + p}, {s * cfg.slot}, %[a{kk}{p}]")
-        out.append(f"v_add_u32_e32 v{cfg.v_sadr + s}, {s * cfg.slot}, %[sadr]")
     out += [f"v_accvgpr_write_b32 a{r}, 0" for r in range(cfg.nacc)]
     out += ["s_mov_b32 %[q], 0"]
     for t in range(S - 1):
@@ -255,12 +272,13 @@ CONFIGS = [Cfg(192, 4, "TALL192"), Cfg(256, 4, "TALL256")]
 def main():
     with open(sys.argv[1], "w") as f:
         f.write("// Generated by gen_fp8_asm.py -- do not edit.\n")
-        f.write(f"#define MOE_FP8_TALL_SCALE_ROWS {SCALE_ROWS}\n")
+        f.write(f"#define MOE_FP8_TALL_SCALE_ROWS {SCALE_ROWS}\n#define MOE_FP8_TALL_SCALE_GROUP {GROUP}\n")
         for cfg in CONFIGS:
             n = cfg.name
-            f.write(f"// {n}: {cfg.rows} rows, ring {cfg.S}, {cfg.rt} row tiles, {cfg.ops} loads/K block, "
-                    f"wait {cfg.wait}\n")
+            f.write(f"// {n}: {cfg.rows} rows, ring {cfg.S}, {cfg.rt} row tiles, {cfg.ops} loads/K block "
+                    f"(+1 per scale group)\n")
             f.write(f"#define MOE_FP8_{n}_SLOT_A {cfg.slot_a}\n#define MOE_FP8_{n}_SLOT {cfg.slot}\n"
+                    f"#define MOE_FP8_{n}_SC_OFF {cfg.sc_off}\n#define MOE_FP8_{n}_LDS {cfg.lds}\n"
                     f"#define MOE_FP8_{n}_APW {cfg.apw}\n#define MOE_FP8_{n}_S {cfg.S}\n")
             f.write(f"#define MOE_FP8_{n}_AO_OUTS " + ", ".join(f'[ao{i}] "+v"(ao[{i}])' for i in range(cfg.apw))
                     + "\n")

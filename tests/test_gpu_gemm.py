@@ -35,10 +35,15 @@ def _fp8_case(seed, counts, N, K, layout, max_m=0, act_scale=1.0):
                 max_m=max_m, a=a_codes, sfa=sfa, w=w_codes, sfw=sfw)
 
 
-def _run_fp8(c, expected_m=0, D=None, packed=False):
-    """packed: the weights go in the oracle's fragment-packed order, with MOE_WEIGHTS_PACKED."""
+def _run_fp8(c, expected_m=0, D=None, packed=False, sfa_shift=0):
+    """packed: the weights go in the oracle's fragment-packed order, with MOE_WEIGHTS_PACKED.
+    sfa_shift: place SFA that many floats into a larger buffer (a pointer that is only 4-byte aligned)."""
     A = torch.from_numpy(c["a"]).to(DEV)
     SFA = torch.from_numpy(c["sfa"]).to(DEV)
+    if sfa_shift:
+        buf = torch.zeros(SFA.numel() + sfa_shift, dtype=torch.float32, device=DEV)
+        buf[sfa_shift:] = SFA.reshape(-1)
+        SFA = buf[sfa_shift:].view(SFA.shape)
     wbytes = oracle.pack_weight_fp8(c["w"]).reshape(c["w"].shape) if packed else c["w"]
     W = torch.from_numpy(np.ascontiguousarray(wbytes)).to(DEV)
     SFW = torch.from_numpy(c["sfw"]).to(DEV)
@@ -67,8 +72,21 @@ def _check_fp8(c, D):
 @pytest.mark.parametrize("expected_m", [0, 16, 64, 256])
 def test_fp8_contiguous_ragged(expected_m, packed):
     require_gpu()
-    c = _fp8_case(1, [0, 1, 17, 130, 300], N=384, K=640, layout=moe.LAYOUT_CONTIGUOUS)
+    # K = 1536: 12 K blocks, three row-scale groups of the tall tile
+    c = _fp8_case(1, [0, 1, 17, 130, 300], N=384, K=1536, layout=moe.LAYOUT_CONTIGUOUS)
     _check_fp8(c, _run_fp8(c, expected_m, packed=packed))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_fp8_tall_sized_calls_the_tall_tile_cannot_take(packed):
+    """K/128 not a multiple of 4, or SFA only 4-byte aligned: prefill-sized calls run on the 64-row tile."""
+    require_gpu()
+    c = _fp8_case(14, [0, 1, 17, 130, 300], N=384, K=640, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (0, 128, 256):
+        _check_fp8(c, _run_fp8(c, em, packed=packed))
+    c = _fp8_case(15, [70, 260, 0, 5], N=256, K=1024, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (0, 128):
+        _check_fp8(c, _run_fp8(c, em, packed=packed, sfa_shift=1))
 
 
 @pytest.mark.parametrize("packed", [False, True])
@@ -83,7 +101,7 @@ def test_fp8_masked_with_overfull_expert(expected_m, packed):
 def test_fp8_masked_tall_segments(packed):
     """Masked layout with segments taller than one tall tile (192 or 256 rows: several M chunks, ragged tails)."""
     require_gpu()
-    c = _fp8_case(12, [150, 0, 300, 65], N=384, K=768, layout=moe.LAYOUT_MASKED, max_m=300)
+    c = _fp8_case(12, [150, 0, 300, 65], N=384, K=1024, layout=moe.LAYOUT_MASKED, max_m=300)
     for em in (0, 200, 256):
         _check_fp8(c, _run_fp8(c, em, packed=packed))
 
@@ -93,7 +111,7 @@ def test_fp8_many_experts_long_k(packed):
     require_gpu()
     rng = np.random.default_rng(3)
     counts = rng.integers(0, 40, size=33).tolist()
-    c = _fp8_case(3, counts, N=512, K=2304, layout=moe.LAYOUT_CONTIGUOUS)
+    c = _fp8_case(3, counts, N=512, K=2560, layout=moe.LAYOUT_CONTIGUOUS)
     for em in (24, 128):
         _check_fp8(c, _run_fp8(c, em, packed=packed))
 
@@ -120,7 +138,7 @@ def test_fp8_small_integers_bit_exact():
     """Integer-valued codes with unit scales: every partial sum is exact, so is the bf16 result."""
     require_gpu()
     rng = np.random.default_rng(4)
-    E, N, K = 3, 256, 384
+    E, N, K = 3, 256, 512
     counts = np.array([5, 0, 40], np.int32)
     starts = np.array([0, 128, 128, 256])
     av, a = _int_codes(rng, (256, K), -2, 2)
