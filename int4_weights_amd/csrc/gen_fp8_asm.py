@@ -195,7 +195,8 @@ def epilogue(cfg):
     The ring is idle once the loop has ended, so each wave writes its rows x 64 columns of bf16 to a private
     LDS region (row m at m*128, 16-byte chunk c at position c ^ (m & 7)), reads them back as 16 bytes per lane,
     8 lanes per row, and stores 8 whole 128-byte rows per instruction (rows >= mrows masked off; %[t] counts
-    the rows left).  A final barrier keeps the next unit's copies into the ring behind every wave's reads."""
+    the rows left; the stores are nontemporal: the output is read back by another kernel, not by this one).
+    A final barrier keeps the next unit's copies into the ring behind every wave's reads."""
     out = ["9:", "s_waitcnt vmcnt(0)", "s_waitcnt lgkmcnt(0)", "s_barrier", "s_nop 15", "s_nop 15",
            "s_cmp_eq_u32 %[won], 0", "s_cbranch_scc1 7f"]
     T, E = cfg.v_t, cfg.v_ep
@@ -231,7 +232,7 @@ def epilogue(cfg):
         for q in range(4):
             r = cfg.wbase + 4 * (4 * j + q)
             out += ["v_cmp_gt_i32_e32 vcc, %[t], %[l8]", "s_and_saveexec_b64 %[sv], vcc",
-                    f"global_store_dwordx4 v{cfg.v_doff}, v[{r}:{r + 3}], %[db]", "s_mov_b64 exec, %[sv]",
+                    f"global_store_dwordx4 v{cfg.v_doff}, v[{r}:{r + 3}], %[db] nt", "s_mov_b64 exec, %[sv]",
                     f"v_add_u32_e32 v{cfg.v_doff}, %[dstep], v{cfg.v_doff}", "s_sub_i32 %[t], %[t], 8"]
     out += ["7:", "s_barrier"]
     return out
