@@ -22,7 +22,7 @@ namespace moe {
 
 constexpr int kBN = 256;       // columns per unit (4 waves x 64)
 constexpr int kXcds = 8;
-constexpr int kNGroup = 16;    // N-tiles per 2-D block of an expert's units
+constexpr int kNGroup = 8;     // N-tiles per 2-D block of an expert's units
 
 // The unit table in LDS: unit prefix per expert and the expert's rows and first
 // packed row, read once from global memory.
@@ -101,11 +101,11 @@ __device__ inline Unit sched_unit(const GemmArgs& a, Sched s, int v) {
   const int chunks = (rows + BM - 1) / BM;
   // Within an expert the units run in 2-D blocks: groups of kNGroup N-tiles,
   // every M chunk of the group before the next group, the N-tiles of one M
-  // chunk adjacent.  For N up to 4096 a group is the whole width, so a window
-  // of 32 consecutive units (one XCD's workgroups) covers 2-3 M chunks of all
-  // N-tiles: each activation chunk is read once and shared by all its
-  // N-tiles, each weight tile shared by the chunks in flight.  (Measured on
-  // the Qwen3-shaped GEMMs: groups of 12-16 beat groups of 8 by about 6%.)
+  // chunk adjacent.  A window of 32 consecutive units (one XCD's workgroups)
+  // then covers about 4 M chunks x 8 N-tiles: each activation chunk is shared
+  // by 8 concurrent units, each weight tile by 4.  (Measured on the
+  // Qwen3-shaped GEMMs: groups of 8 beat groups of 16, i.e. the whole width,
+  // by 1% on the up-projection and 5% on the down-projection.)
   const int ntiles = (a.N + kBN - 1) / kBN;
   const int full = ntiles / kNGroup;            // complete groups
   const int in_full = full * chunks * kNGroup;  // units in complete groups
