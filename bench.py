@@ -99,13 +99,60 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class HipEvent:
+    """A timing-only HIP event recorded on torch's current stream (the stream every libmoe call is
+    enqueued on), created with hipEventDisableSystemFence: recording it releases to device scope instead
+    of writing back and invalidating the caches for the host, which would otherwise land inside the
+    interval of the kernel that follows (the HIP runtime documents the flag for timing events).  The
+    host reads the times after a device synchronize."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, torch):
+        import ctypes
+        if HipEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has loaded (same soname)
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = hip
+        self.ctypes, self.torch = ctypes, torch
+        self.ev = ctypes.c_void_p()
+        rc = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        rc = HipEvent._hip.hipEventRecord(self.ev, ctypes_stream(self.torch))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        ms = self.ctypes.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(self.ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.ev:
+            HipEvent._hip.hipEventDestroy(self.ev)
+
+
+def ctypes_stream(torch):
+    import ctypes
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
 class Timer:
-    """HIP events on torch's current stream (the stream every libmoe call is enqueued on)."""
+    """Timing-only HIP events around every kernel of every timed step."""
 
     def __init__(self, torch, names, steps):
         self.torch = torch
         self.names = names
-        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+        self.ev = [[HipEvent(torch) for _ in range(len(names) + 1)] for _ in range(steps)]
 
     def mark(self, step, i):
         self.ev[step][i].record()
@@ -262,7 +309,7 @@ def run(args):
     # not host gaps.  The spin kernel itself lies before the start event.
     cycles_per_ms = spin_calibration(torch)
     tm = Timer(torch, names, args.steps)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start, end = HipEvent(torch), HipEvent(torch)
     t_host = time.perf_counter()
     for s in range(min(args.steps, 3)):
         step(wt, s % max(args.warmup, 1))
