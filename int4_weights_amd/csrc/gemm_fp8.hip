@@ -199,7 +199,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 
   const Sched sc{&s_sched};
   sched_build<C::BM>(a, sc);
-  const Walk walk = sched_walk(s_sched.up[a.E]);
+  const Walk walk = sched_walk(s_sched.total);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   constexpr int RH = (RB + 1) / 2;  // the shorter tile height
@@ -334,7 +334,9 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   const uint64_t db = uniform_u64((uint64_t)(a.D + (int64_t)u.row0 * N));
   uint32_t doff = (uint32_t)(l8 * N + ncol0 + 8 * (lane & 7)) * 2u;
   const int dstep = uniform(16 * N);  // output bytes between 8-row groups
-  const int rbe = uniform((u.mrows + 31) / 32);
+  // row tiles computed: at least 2, so the barrier that publishes the next K block (after the fragments of
+  // the second-to-last row tile's successor are read) has a place in every step
+  const int rbe = uniform(max(2, (u.mrows + 31) / 32));
   const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
   int ks, q, t, inc, inc4, m0v = 0;
   uint64_t sv;
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(const GemmArgs a)
   __shared__ SchedSmem s_sched;
   const Sched sc{&s_sched};
   sched_build<ROWS>(a, sc);
-  const Walk walk = sched_walk(s_sched.up[a.E]);
+  const Walk walk = sched_walk(s_sched.total);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {

@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void gemm_int4_kernel(const GemmArgs a) {
   __shared__ SchedSmem s_sched;
   const Sched sc{&s_sched};
   sched_build<C::BM>(a, sc);
-  const Walk walk = sched_walk(s_sched.up[a.E]);
+  const Walk walk = sched_walk(s_sched.total);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(256, kI4PackedWgPerCu) void gemm_int4_packed_kernel
   __shared__ SchedSmem s_sched;
   const Sched sc{&s_sched};
   sched_build<16>(a, sc);
-  const Walk walk = sched_walk(s_sched.up[a.E]);
+  const Walk walk = sched_walk(s_sched.total);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {

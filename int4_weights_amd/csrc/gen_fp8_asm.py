@@ -33,16 +33,27 @@ block's fp32 row scales (one global_load_lds_dword per wave: 64 rows each, the
 4 waves cover 256 rows); each wave also loads its weight scale for the block
 into a VGPR ring.  The exponent is the fp32 bit pattern shifted right by 23.
 
+Pipeline.  Step ks multiplies K block ks and issues the loads of block ks + 3
+(into the slot block ks - 1 used).  The barrier that publishes block ks + 1 sits
+inside step ks, after the fragments of the step's last row tile have been read
+into registers: from then on no wave reads slot ks, so row tile 0 of block
+ks + 1 (and its row scale) is read into a third fragment buffer while the last
+row tile's matrix instructions run, and the next step starts without an LDS
+round trip.  A unit always computes at least two row tiles (the surplus rows
+repeat the last valid row and are never stored), so that barrier always has a
+row tile after it.
+
 Register map (physical, listed as clobbers of the asm statement):
   a[0:rows-1] accumulators (row tile j, column tile ct at a[32j + 16ct]);
-  activation fragments (2 buffers of 16): a[192:223] for 192 rows, the 32
-  VGPRs below the weight ring for 256 rows (the accumulators fill the AGPRs);
+  activation fragments (3 buffers of 16; row tile 0 in buffer 2, tile j >= 1 in
+  buffer j % 2): a[192:239] for 192 rows, the 48 VGPRs below the weight ring
+  for 256 rows (the accumulators fill the AGPRs);
   v[256-32S:255] weight ring (S slots x 2 column tiles x 2 halves x 8);
   below it: per slot the four fragment addresses, the row-scale address and
-  the weight-scale register; the two exponents in use, the output offset and
-  16 epilogue temporaries.  The epilogue reuses the weight ring for the rows
-  it reads back from LDS and keeps its 8 LDS addresses in the fragment
-  registers (256 rows) or above the rows read back (192 rows).
+  the weight-scale register; the weight exponent, one row-scale exponent per
+  fragment buffer and the output offset.  The epilogue's 16 temporaries and the
+  rows it reads back from LDS use the weight ring; its 8 LDS addresses sit in
+  the fragment registers (256 rows) or above the rows read back (192 rows).
 
 Usage: python gen_fp8_asm.py OUT.inc
 """
@@ -51,6 +62,7 @@ from __future__ import annotations
 
 import sys
 
+NBUF = 3          # activation fragment buffers (row tile 0 of the next block is read into its own)
 SCALE_ROWS = 256  # rows of a scale group (4 waves x 64 lanes; rows past the unit repeat its last row)
 GROUP = 4         # K blocks per row-scale copy (one 16-byte copy per row)
 
@@ -68,19 +80,19 @@ class Cfg:
         self.apw = rows // 32                     # 1-KB activation copies per wave per K block
         self.ops = 8 + self.apw + 1               # vector-memory instructions per wave per K block (+1 for
         # the blocks that start a scale group)
-        assert self.wait_at(2) <= 63, "vmcnt holds at most 63"
+        assert 2 * self.ops + 2 <= 63, "vmcnt holds at most 63"
         self.wbase = 256 - 32 * S
         self.nacc = 32 * self.rt
-        self.frag_v = self.nacc + 32 > 256
-        self.v_frag = self.wbase - 32
-        self.v_alo = (self.v_frag if self.frag_v else self.wbase) - (6 * S + 20)
+        self.frag_v = self.nacc + 16 * NBUF > 256
+        self.v_frag = self.wbase - 16 * NBUF
+        self.v_alo = (self.v_frag if self.frag_v else self.wbase) - (6 * S + 6)  # even: 64-bit pairs
         self.v_aadr = self.v_alo                  # slot s, (kk, p): v_aadr + 4s + 2kk + p
         self.v_sadr = self.v_alo + 4 * S
         self.v_swr = self.v_sadr + S
         self.v_swe = self.v_swr + S
-        self.v_sae = self.v_swe + 1
-        self.v_doff = self.v_swe + 3
-        self.v_t = self.v_swe + 4
+        self.v_sae = self.v_swe + 1                # one per fragment buffer
+        self.v_doff = self.v_swe + 1 + NBUF
+        self.v_t = self.wbase  # 16 epilogue temporaries in the (then idle) weight ring, before the read-back
         assert self.v_alo >= 0 and 6 * S >= 16  # epilogue packs 16 dwords into the address registers
         # epilogue: 8 LDS chunk addresses in the (then idle) fragment registers or above the rows read back
         # into the weight ring (4 registers per 8 rows)
@@ -91,11 +103,16 @@ class Cfg:
     def acc(self, j, ct):
         return 32 * j + 16 * ct
 
-    def wait_at(self, s):
-        """Loads allowed outstanding at the start of step s (K block ks = s mod S): those of blocks ks + 1
-        .. ks + S - 2, plus one for each of them that starts a scale group."""
-        blocks = [(s + d) % GROUP for d in range(1, self.S - 1)]
-        return self.ops * (self.S - 2) + sum(1 for b in blocks if b == 0)
+    def wait_at(self, s, issued):
+        """Loads allowed outstanding at the barrier of step s (K block ks = s mod S) that publishes block
+        ks + 1: those of block ks + 2 (issued in the previous step, plus one if it starts a scale group) and
+        the `issued` loads of block ks + 3 this step has issued so far."""
+        return self.ops + (1 if (s + 2) % GROUP == 0 else 0) + issued
+
+    @staticmethod
+    def bufid(j):
+        """Fragment buffer of row tile j: buffer 2 for tile 0 (filled before the step starts), then 1, 0, ..."""
+        return 2 if j == 0 else j % 2
 
     def buf(self, b, kk, lo=0, hi=7):
         base = (self.v_frag if self.frag_v else self.nacc) + 16 * b + 8 * kk
@@ -146,20 +163,36 @@ def frag_reads(cfg, s, b, j):
     return out
 
 
+def publish(cfg, s, issued):
+    """The barrier of step s that publishes K block ks + 1, placed after the fragments of the step's last
+    row tile are in registers: wait for this wave's loads of block ks + 1, barrier (every wave's copies of the
+    block have landed and every wave has read all of slot s), then read row tile 0 of block ks + 1 and its
+    row scale into buffer 2 while the last row tile's matrix instructions run."""
+    sn = (s + 1) % cfg.S
+    out = [f"s_waitcnt vmcnt({cfg.wait_at(s, issued)})", "s_barrier"]
+    if s == cfg.S - 1:  # block ks + 1 opens the next scale group, in the other group buffer
+        out.append(f"v_xor_b32_e32 v{cfg.v_sadr}, {SCALE_ROWS * 16}, v{cfg.v_sadr}")
+    out += frag_reads(cfg, sn, 2, 0)
+    out.append(f"ds_read_b32 v{cfg.v_sae + 2}, v{cfg.v_sadr}" + (f" offset:{4 * sn}" if sn else ""))
+    return out
+
+
 def compute(cfg, s, t, packed):
-    """Multiply K block s of the ring (row tiles 0 .. rbe-1) and issue the loads of ring slot t on the way,
-    a few items after each row tile (the rest after the last)."""
+    """Multiply K block s of the ring (row tiles 0 .. rbe-1, rbe >= 2) and issue the loads of ring slot t
+    (block ks + 3) on the way, a few items after each row tile (the rest after the last).  Row tile 0's
+    fragments and row scale were read into buffer 2 by the previous step; the barrier that publishes the
+    next block sits after row tile rbe - 2 (publish)."""
     items, upd = issue_items(cfg, t, packed)
     per = -(-len(items) // cfg.rt)
     sadr = cfg.v_sadr  # row r's scale of K block s of the group at r * 16 + 4 s
-    out = [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}"] + frag_reads(cfg, s, 0, 0) + [
-        f"ds_read_b32 v{cfg.v_sae}, v{sadr}" + (f" offset:{4 * s}" if s else ""), "s_waitcnt lgkmcnt(0)",
-        f"v_lshrrev_b32_e32 v{cfg.v_sae}, 23, v{cfg.v_sae}"]
+    out = [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}", "s_waitcnt lgkmcnt(0)",
+           f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"]
     k = 0
     for j in range(cfg.rt):
-        b, bn = j % 2, 1 - j % 2
+        b = cfg.bufid(j)
         out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 5f"]  # no row tile j: only its load items
         if j + 1 < cfg.rt:
+            bn = cfg.bufid(j + 1)
             out += [f"s_cmp_le_u32 %[rbe], {j + 1}", "s_cbranch_scc1 3f"] + frag_reads(cfg, s, bn, j + 1) + [
                 f"ds_read_b32 v{cfg.v_sae + bn}, v{sadr} offset:{512 * (j + 1) + 4 * s}", "3:"]
         out.append("s_nop 1")
@@ -168,7 +201,11 @@ def compute(cfg, s, t, packed):
                 a0 = cfg.acc(j, ct)
                 out.append(f"v_mfma_scale_f32_32x32x64_f8f6f4 a[{a0}:{a0 + 15}], {wreg(cfg, s, ct, kk, 0, 7)}, "
                            f"{cfg.buf(b, kk)}, a[{a0}:{a0 + 15}], v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
-        out += ["s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}", "5:"]
+        if j + 1 < cfg.rt:
+            out += ["s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"]
+            # row tile j + 1 is the last one: its fragments are in registers, publish the next block
+            out += [f"s_cmp_eq_u32 %[rbe], {j + 2}", "s_cbranch_scc0 4f"] + publish(cfg, s, k) + ["4:"]
+        out.append("5:")
         for _ in range(per):
             if k < len(items):
                 out += items[k]
@@ -180,10 +217,7 @@ def compute(cfg, s, t, packed):
 
 
 def step(cfg, s, last, packed):
-    out = [f"s_waitcnt vmcnt({cfg.wait_at(s)})", "s_waitcnt lgkmcnt(0)", "s_barrier"]
-    out += compute(cfg, s, (s + cfg.S - 1) % cfg.S, packed)
-    if last:  # the next step reads the other group buffer
-        out.append(f"v_xor_b32_e32 v{cfg.v_sadr}, {SCALE_ROWS * 16}, v{cfg.v_sadr}")
+    out = compute(cfg, s, (s + cfg.S - 1) % cfg.S, packed)
     out += ["s_add_u32 %[ks], %[ks], 1", "s_cmp_lt_u32 %[ks], %[kb]",
             "s_cbranch_scc1 8b" if last else "s_cbranch_scc0 9f"]
     return out
@@ -254,6 +288,9 @@ def program(cfg, packed):
     for t in range(S - 1):
         items, upd = issue_items(cfg, t, packed)
         out += [ins for it in items for ins in it] + upd
+    # block 0 in place (blocks 1 and 2 may still be in flight), then its row tile 0 into buffer 2
+    out += [f"s_waitcnt vmcnt({2 * cfg.ops})", "s_barrier"] + frag_reads(cfg, 0, 2, 0) + [
+        f"ds_read_b32 v{cfg.v_sae + 2}, v{cfg.v_sadr}"]
     out += ["s_mov_b32 %[ks], 0", "8:"]
     for s in range(S):
         out += step(cfg, s, s == S - 1, packed)
@@ -262,7 +299,7 @@ def program(cfg, packed):
 
 
 def clobbers(cfg):
-    top = cfg.nacc + (0 if cfg.frag_v else 32)
+    top = cfg.nacc + (0 if cfg.frag_v else 16 * NBUF)
     regs = [f'"v{r}"' for r in range(cfg.v_alo, 256)] + [f'"a{r}"' for r in range(0, top)]
     return ", ".join(regs)
 
