@@ -167,9 +167,11 @@ def publish(cfg, s, issued):
     """The barrier of step s that publishes K block ks + 1, placed after the fragments of the step's last
     row tile are in registers: wait for this wave's loads of block ks + 1, barrier (every wave's copies of the
     block have landed and every wave has read all of slot s), then read row tile 0 of block ks + 1 and its
-    row scale into buffer 2 while the last row tile's matrix instructions run."""
+    row scale into buffer 2 while the last row tile's matrix instructions run.  In the last three steps no
+    loads are issued (%[tl] set), so the count below would be too weak there: wait for everything."""
     sn = (s + 1) % cfg.S
-    out = [f"s_waitcnt vmcnt({cfg.wait_at(s, issued)})", "s_barrier"]
+    out = ["s_cmp_eq_u32 %[tl], 0", "s_cbranch_scc1 1f", "s_waitcnt vmcnt(0)", "1:",
+           f"s_waitcnt vmcnt({cfg.wait_at(s, issued)})", "s_barrier"]
     if s == cfg.S - 1:  # block ks + 1 opens the next scale group, in the other group buffer
         out.append(f"v_xor_b32_e32 v{cfg.v_sadr}, {SCALE_ROWS * 16}, v{cfg.v_sadr}")
     out += frag_reads(cfg, sn, 2, 0)
@@ -177,17 +179,28 @@ def publish(cfg, s, issued):
     return out
 
 
+def guarded(items):
+    """Load items, skipped in the last three steps of the K loop (their blocks would be past the end)."""
+    if not items:
+        return []
+    return ["s_cmp_lg_u32 %[tl], 0", "s_cbranch_scc1 6f"] + [ins for it in items for ins in it] + ["6:"]
+
+
 def compute(cfg, s, t, packed):
     """Multiply K block s of the ring (row tiles 0 .. rbe-1, rbe >= 2) and issue the loads of ring slot t
-    (block ks + 3) on the way, a few items after each row tile (the rest after the last).  Row tile 0's
-    fragments and row scale were read into buffer 2 by the previous step; the barrier that publishes the
-    next block sits after row tile rbe - 2 (publish)."""
+    (block ks + 3) on the way, one item after each of the evenly spaced matrix instructions (a burst of loads
+    stalls every wave on the shared load path).  Row tile 0's fragments and row scale were read into
+    buffer 2 by the previous step; the barrier that publishes the next block sits after row tile rbe - 2
+    (publish)."""
     items, upd = issue_items(cfg, t, packed)
-    per = -(-len(items) // cfg.rt)
+    nslots = 4 * cfg.rt
+    place = [[] for _ in range(nslots)]  # matrix-instruction slot -> the items issued right after it
+    for i, it in enumerate(items):
+        place[(i * nslots) // len(items)].append(it)
     sadr = cfg.v_sadr  # row r's scale of K block s of the group at r * 16 + 4 s
-    out = [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}", "s_waitcnt lgkmcnt(0)",
-           f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"]
-    k = 0
+    out = [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}",
+           "s_add_u32 %[tl], %[ks], 3", "s_cmp_ge_u32 %[tl], %[kb]", "s_cselect_b32 %[tl], 1, 0",
+           "s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"]
     for j in range(cfg.rt):
         b = cfg.bufid(j)
         out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 5f"]  # no row tile j: only its load items
@@ -196,22 +209,21 @@ def compute(cfg, s, t, packed):
             out += [f"s_cmp_le_u32 %[rbe], {j + 1}", "s_cbranch_scc1 3f"] + frag_reads(cfg, s, bn, j + 1) + [
                 f"ds_read_b32 v{cfg.v_sae + bn}, v{sadr} offset:{512 * (j + 1) + 4 * s}", "3:"]
         out.append("s_nop 1")
+        q = 0
         for kk in range(2):  # consecutive instructions write different accumulators
             for ct in range(2):
                 a0 = cfg.acc(j, ct)
                 out.append(f"v_mfma_scale_f32_32x32x64_f8f6f4 a[{a0}:{a0 + 15}], {wreg(cfg, s, ct, kk, 0, 7)}, "
                            f"{cfg.buf(b, kk)}, a[{a0}:{a0 + 15}], v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
+                out += guarded(place[4 * j + q])
+                q += 1
         if j + 1 < cfg.rt:
             out += ["s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"]
             # row tile j + 1 is the last one: its fragments are in registers, publish the next block
-            out += [f"s_cmp_eq_u32 %[rbe], {j + 2}", "s_cbranch_scc0 4f"] + publish(cfg, s, k) + ["4:"]
-        out.append("5:")
-        for _ in range(per):
-            if k < len(items):
-                out += items[k]
-                k += 1
-    for it in items[k:]:
-        out += it
+            issued = sum(len(place[i]) for i in range(4 * (j + 1)))
+            out += [f"s_cmp_eq_u32 %[rbe], {j + 2}", "s_cbranch_scc0 4f"] + publish(cfg, s, issued) + ["4:"]
+        tile_items = [it for i in range(4 * j, 4 * j + 4) for it in place[i]]
+        out += ["s_branch 2f", "5:"] + guarded(tile_items) + ["2:"]
     out += upd
     return out
 
