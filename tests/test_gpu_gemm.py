@@ -107,6 +107,20 @@ def test_fp8_masked_tall_segments(packed):
 
 
 @pytest.mark.parametrize("packed", [False, True])
+def test_fp8_tall_schedule_every_chunk_class(packed):
+    """The unit table orders full chunks first, then partial chunks by size: 100 experts (several per lane of
+    the table build), rows that are exact multiples of both tall heights, and partial chunks of every 32-row
+    size class, on both tall tiles."""
+    require_gpu()
+    rng = np.random.default_rng(21)
+    counts = [0, 192, 256, 384, 512, 768, 1000, 7, 33] + [32 * c - int(rng.integers(0, 32)) for c in range(1, 9)]
+    counts += rng.integers(0, 600, size=100 - len(counts)).tolist()
+    c = _fp8_case(21, counts, N=512, K=512, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (128, 256):
+        _check_fp8(c, _run_fp8(c, em, packed=packed))
+
+
+@pytest.mark.parametrize("packed", [False, True])
 def test_fp8_many_experts_long_k(packed):
     require_gpu()
     rng = np.random.default_rng(3)
