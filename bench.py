@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--config", default="dsv3_prefill",
                     choices=["tiny", "dsv3_prefill", "dsv3_decode", "qwen3_skewed", "int4_decode"])
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
-    ap.add_argument("--cpu-experts", type=int, default=64, help="experts in the timed oracle sample")
+    ap.add_argument("--cpu-experts", type=int, default=128, help="experts in the timed oracle sample")
     ap.add_argument("--expected-m", type=int, default=0,
                     help="tiling hint passed to the GEMM (default: routes per expert)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
