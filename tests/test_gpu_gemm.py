@@ -121,6 +121,25 @@ def test_fp8_tall_schedule_every_chunk_class(packed):
 
 
 @pytest.mark.parametrize("packed", [False, True])
+def test_fp8_degenerate_expert_counts(packed):
+    """No rows at all (an empty unit table), 1024 experts with 0..3 rows (16 experts per lane of the table
+    build, every 4-bit size-class slot used; N = 128, so half of each tall tile's waves store nothing), and a
+    single expert with several chunks, on every tile height."""
+    require_gpu()
+    for layout, mm in ((moe.LAYOUT_CONTIGUOUS, 0), (moe.LAYOUT_MASKED, 16)):
+        c = _fp8_case(31, [0] * 8, N=256, K=512, layout=layout, max_m=mm)
+        for em in (16, 64, 128, 256):
+            _check_fp8(c, _run_fp8(c, em, packed=packed))
+    counts = np.random.default_rng(33).integers(0, 4, size=1024).tolist()
+    c = _fp8_case(33, counts, N=128, K=512, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (16, 128, 256):
+        _check_fp8(c, _run_fp8(c, em, packed=packed))
+    c = _fp8_case(34, [700], N=384, K=512, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (64, 128, 256):
+        _check_fp8(c, _run_fp8(c, em, packed=packed))
+
+
+@pytest.mark.parametrize("packed", [False, True])
 def test_fp8_many_experts_long_k(packed):
     require_gpu()
     rng = np.random.default_rng(3)
@@ -257,6 +276,21 @@ def test_int4_long_k_restages_scales(packed):
     require_gpu()
     c = _int4_case(12, [40, 0, 70], N=256, K=130 * 128, layout=moe.LAYOUT_CONTIGUOUS)
     for em in (16, 64):
+        _check_int4(c, _run_int4(c, em, packed=packed))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_int4_degenerate_expert_counts(packed):
+    """No rows at all, 1024 experts with 0..2 rows, one expert with several M chunks."""
+    require_gpu()
+    c = _int4_case(41, [0] * 8, N=256, K=512, layout=moe.LAYOUT_MASKED, max_m=16)
+    for em in (0, 16):
+        _check_int4(c, _run_int4(c, em, packed=packed))
+    counts = np.random.default_rng(42).integers(0, 3, size=1024).tolist()
+    c = _int4_case(42, counts, N=128, K=256, layout=moe.LAYOUT_MASKED, max_m=2)
+    _check_int4(c, _run_int4(c, 0, packed=packed))
+    c = _int4_case(43, [300], N=256, K=512, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (0, 16):
         _check_int4(c, _run_int4(c, em, packed=packed))
 
 
