@@ -273,7 +273,7 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
 #define MOE_TALL_ASM(LOOP, AO_OUTS, CLOBBERS)                                                                     \
   asm volatile(LOOP                                                                                             \
                : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), AO_OUTS,                                                    \
-                 [so] "+v"(so), [wso] "+v"(wso), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t), [tl] "=&s"(tl), \
+                 [so] "+v"(so), [wso] "+v"(wso), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),  \
                  [inc] "=&s"(inc), [inc4] "=&s"(inc4), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v), [msg] "+s"(msg)                         \
                : [wb] "s"(wb), [ab] "s"(ab), [sb] "s"(sb), [swb] "s"(swb), [ma] "s"(ma),                       \
                  [a00] "v"(af[0]), [a01] "v"(af[1]), [a10] "v"(af[2]), [a11] "v"(af[3]), [sadr] "v"(sadr),        \
@@ -338,7 +338,7 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   // the second-to-last row tile's successor are read) has a place in every step
   const int rbe = uniform(max(2, (u.mrows + 31) / 32));
   const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
-  int ks, q, t, tl, inc, inc4, m0v = 0;
+  int ks, q, t, inc, inc4, m0v = 0;
   uint64_t sv;
   if constexpr (ROWS == 192) {
     if constexpr (PACKED)

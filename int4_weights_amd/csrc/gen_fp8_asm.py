@@ -166,15 +166,14 @@ def frag_reads(cfg, s, b, j):
     return out
 
 
-def publish(cfg, s, issued):
+def publish(cfg, s, wait):
     """The barrier of step s that publishes K block ks + 1, placed after the fragments of the step's last
-    row tile are in registers: wait for this wave's loads of block ks + 1, barrier (every wave's copies of the
-    block have landed and every wave has read all of slot s), then read row tile 0 of block ks + 1 and its
-    row scale into buffer 2 while the last row tile's matrix instructions run.  In the last three steps no
-    loads are issued (%[tl] set), so the count below would be too weak there: wait for everything."""
+    row tile are in registers: wait until at most `wait` loads are outstanding (this wave's loads of block
+    ks + 1 have landed), barrier (every wave's copies of the block have landed and every wave has read all of
+    slot s), then read row tile 0 of block ks + 1 and its row scale into buffer 2 while the last row tile's
+    matrix instructions run."""
     sn = (s + 1) % cfg.S
-    out = ["s_cmp_eq_u32 %[tl], 0", "s_cbranch_scc1 1f", "s_waitcnt vmcnt(0)", "1:",
-           f"s_waitcnt vmcnt({cfg.wait_at(s, issued)})", "s_barrier"]
+    out = [f"s_waitcnt vmcnt({wait})", "s_barrier"]
     if s == cfg.S - 1:  # block ks + 1 opens the next scale group, in the other group buffer
         out.append(f"v_xor_b32_e32 v{cfg.v_sadr}, {SCALE_ROWS * 16}, v{cfg.v_sadr}")
     out += frag_reads(cfg, sn, 2, 0)
@@ -182,28 +181,26 @@ def publish(cfg, s, issued):
     return out
 
 
-def guarded(items):
-    """Load items, skipped in the last three steps of the K loop (their blocks would be past the end)."""
-    if not items:
-        return []
-    return ["s_cmp_lg_u32 %[tl], 0", "s_cbranch_scc1 6f"] + [ins for it in items for ins in it] + ["6:"]
-
-
-def compute(cfg, s, t, packed, rbe):
+def compute(cfg, s, t, packed, rbe, final=False):
     """Multiply K block s of the ring (row tiles 0 .. rbe-1; rbe >= 2 is fixed for the body, so the code has no
     branch between matrix instructions) and issue the loads of ring slot t (block ks + 3) on the way, one item
     after each of the evenly spaced matrix instructions (a burst of loads stalls every wave on the shared load
     path).  Row tile 0's fragments and row scale were read into buffer 2 by the previous step; the barrier that
-    publishes the next block sits after row tile rbe - 2 (publish)."""
+    publishes the next block sits after row tile rbe - 2 (publish).
+
+    final: step s of the loop's last iteration (K blocks kb-4 .. kb-1).  Step 0 still issues block kb - 1;
+    steps 1 .. 3 issue nothing, so their waits are for fewer loads (step 1: block kb - 1's; step 2: none),
+    and step 3 has no next block to publish."""
     items, upd = issue_items(cfg, t, packed)
+    if final and s > 0:
+        items, upd = [], []
     nslots = 4 * rbe
     place = [[] for _ in range(nslots)]  # matrix-instruction slot -> the items issued right after it
     for i, it in enumerate(items):
         place[(i * nslots) // len(items)].append(it)
     sadr = cfg.v_sadr  # row r's scale of K block s of the group at r * 16 + 4 s
-    out = [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}",
-           "s_add_u32 %[tl], %[ks], 3", "s_cmp_ge_u32 %[tl], %[kb]", "s_cselect_b32 %[tl], 1, 0",
-           "s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"]
+    out = [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}", "s_waitcnt lgkmcnt(0)",
+           f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"]
     for j in range(rbe):
         b = cfg.bufid(j)
         if j + 1 < rbe:
@@ -217,25 +214,29 @@ def compute(cfg, s, t, packed, rbe):
                 a0 = cfg.acc(j, ct)
                 out.append(f"v_mfma_scale_f32_32x32x64_f8f6f4 a[{a0}:{a0 + 15}], {wreg(cfg, s, ct, kk, 0, 7)}, "
                            f"{cfg.buf(b, kk)}, a[{a0}:{a0 + 15}], v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
-                out += guarded(place[4 * j + q])
+                out += [ins for it in place[4 * j + q] for ins in it]
                 q += 1
         if j + 1 < rbe:
             out += ["s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"]
-            if j + 2 == rbe:  # row tile j + 1 is the last one: its fragments are in registers
-                out += publish(cfg, s, sum(len(place[i]) for i in range(4 * (j + 1))))
+            if j + 2 == rbe and not (final and s == cfg.S - 1):  # row tile j + 1 is the last one
+                issued = sum(len(place[i]) for i in range(4 * (j + 1)))
+                wait = 0 if final and s == 2 else cfg.wait_at(s, issued)
+                out += publish(cfg, s, wait)
     out += upd
     return out
 
 
 def body(cfg, packed, rbe):
-    """The K loop for units of rbe row tiles: S steps per iteration (one per ring slot), each leaving for the
-    epilogue (9f) once the last K block is done."""
-    head = 200 + rbe
-    out = ["s_mov_b32 %[ks], 0", f"{head}:"]
+    """The K loop for units of rbe row tiles: iterations of S steps (one per ring slot, S = 4 K blocks); all
+    but the last issue the loads of the block 3 ahead in every step, the last one (final) is emitted apart."""
+    head, fin = 200 + rbe, 300 + rbe
+    out = ["s_cmp_le_u32 %[kb], 4", f"s_cbranch_scc1 {fin}f", "s_mov_b32 %[ks], 4", f"{head}:"]
     for s in range(cfg.S):
         out += compute(cfg, s, (s + cfg.S - 1) % cfg.S, packed, rbe)
-        out += ["s_add_u32 %[ks], %[ks], 1", "s_cmp_lt_u32 %[ks], %[kb]"]
-        out += [f"s_cbranch_scc1 {head}b", "s_branch 9f"] if s == cfg.S - 1 else ["s_cbranch_scc0 9f"]
+    out += ["s_add_u32 %[ks], %[ks], 4", "s_cmp_lt_u32 %[ks], %[kb]", f"s_cbranch_scc1 {head}b", f"{fin}:"]
+    for s in range(cfg.S):
+        out += compute(cfg, s, (s + cfg.S - 1) % cfg.S, packed, rbe, final=True)
+    out.append("s_branch 9f")
     return out
 
 
