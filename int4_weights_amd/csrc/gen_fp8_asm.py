@@ -44,7 +44,11 @@ repeat the last valid row and are never stored), so that barrier always has a
 row tile after it.  The loop is emitted once per row-tile count (2 .. 6 or 8):
 a unit jumps to its body once, and no branch sits between the matrix
 instructions of a step (with one wave per SIMD a taken branch at every row
-tile left the matrix pipe idle; the branch-free bodies are 4-9% faster).
+tile left the matrix pipe idle; the branch-free bodies are 4-9% faster).  The
+loop's last iteration is emitted apart (it issues only block kb - 1 and waits
+for fewer loads), so the main loop's only branch is its back-edge, and a
+unit's first step is emitted apart too: its matrix instructions add to 0, so
+the accumulators are never zeroed.
 
 Register map (physical, listed as clobbers of the asm statement):
   a[0:rows-1] accumulators (row tile j, column tile ct at a[32j + 16ct]);
@@ -181,7 +185,7 @@ def publish(cfg, s, wait):
     return out
 
 
-def compute(cfg, s, t, packed, rbe, final=False):
+def compute(cfg, s, t, packed, rbe, final=False, first=False):
     """Multiply K block s of the ring (row tiles 0 .. rbe-1; rbe >= 2 is fixed for the body, so the code has no
     branch between matrix instructions) and issue the loads of ring slot t (block ks + 3) on the way, one item
     after each of the evenly spaced matrix instructions (a burst of loads stalls every wave on the shared load
@@ -190,7 +194,10 @@ def compute(cfg, s, t, packed, rbe, final=False):
 
     final: step s of the loop's last iteration (K blocks kb-4 .. kb-1).  Step 0 still issues block kb - 1;
     steps 1 .. 3 issue nothing, so their waits are for fewer loads (step 1: block kb - 1's; step 2: none),
-    and step 3 has no next block to publish."""
+    and step 3 has no next block to publish.
+
+    first: the unit's first K block; each accumulator's first matrix instruction adds to 0 instead of the
+    accumulator, so the accumulators need no zeroing."""
     items, upd = issue_items(cfg, t, packed)
     if final and s > 0:
         items, upd = [], []
@@ -212,8 +219,9 @@ def compute(cfg, s, t, packed, rbe, final=False):
         for kk in range(2):  # consecutive instructions write different accumulators
             for ct in range(2):
                 a0 = cfg.acc(j, ct)
+                src_c = "0" if first and kk == 0 else f"a[{a0}:{a0 + 15}]"
                 out.append(f"v_mfma_scale_f32_32x32x64_f8f6f4 a[{a0}:{a0 + 15}], {wreg(cfg, s, ct, kk, 0, 7)}, "
-                           f"{cfg.buf(b, kk)}, a[{a0}:{a0 + 15}], v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
+                           f"{cfg.buf(b, kk)}, {src_c}, v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
                 out += [ins for it in place[4 * j + q] for ins in it]
                 q += 1
         if j + 1 < rbe:
@@ -228,13 +236,21 @@ def compute(cfg, s, t, packed, rbe, final=False):
 
 def body(cfg, packed, rbe):
     """The K loop for units of rbe row tiles: iterations of S steps (one per ring slot, S = 4 K blocks); all
-    but the last issue the loads of the block 3 ahead in every step, the last one (final) is emitted apart."""
-    head, fin = 200 + rbe, 300 + rbe
-    out = ["s_cmp_le_u32 %[kb], 4", f"s_cbranch_scc1 {fin}f", "s_mov_b32 %[ks], 4", f"{head}:"]
-    for s in range(cfg.S):
+    but the last issue the loads of the block 3 ahead in every step, the last one (final) is emitted apart.
+    The unit's first step (accumulating onto 0) is emitted once more for either kind of iteration and then
+    joins the loop at its second step."""
+    head, mid, fin, fin_mid, first_fin = 200 + rbe, 300 + rbe, 400 + rbe, 500 + rbe, 600 + rbe
+    t0 = cfg.S - 1  # ring slot of the loads issued by step 0
+    out = ["s_cmp_le_u32 %[kb], 4", f"s_cbranch_scc1 {first_fin}f", "s_mov_b32 %[ks], 4"]
+    out += compute(cfg, 0, t0, packed, rbe, first=True) + [f"s_branch {mid}f", f"{head}:"]
+    out += compute(cfg, 0, t0, packed, rbe) + [f"{mid}:"]
+    for s in range(1, cfg.S):
         out += compute(cfg, s, (s + cfg.S - 1) % cfg.S, packed, rbe)
-    out += ["s_add_u32 %[ks], %[ks], 4", "s_cmp_lt_u32 %[ks], %[kb]", f"s_cbranch_scc1 {head}b", f"{fin}:"]
-    for s in range(cfg.S):
+    out += ["s_add_u32 %[ks], %[ks], 4", "s_cmp_lt_u32 %[ks], %[kb]", f"s_cbranch_scc1 {head}b", f"s_branch {fin}f",
+            f"{first_fin}:"]
+    out += compute(cfg, 0, t0, packed, rbe, final=True, first=True) + [f"s_branch {fin_mid}f", f"{fin}:"]
+    out += compute(cfg, 0, t0, packed, rbe, final=True) + [f"{fin_mid}:"]
+    for s in range(1, cfg.S):
         out += compute(cfg, s, (s + cfg.S - 1) % cfg.S, packed, rbe, final=True)
     out.append("s_branch 9f")
     return out
@@ -300,7 +316,6 @@ def program(cfg, packed):
         for kk in range(2):
             for p in range(2):
                 out.append(f"v_add_u32_e32 v{cfg.v_aadr + 4 * s + 2 * kk + p}, {s * cfg.slot}, %[a{kk}{p}]")
-    out += [f"v_accvgpr_write_b32 a{r}, 0" for r in range(cfg.nacc)]
     out += ["s_mov_b32 %[q], 0"]
     for t in range(S - 1):
         items, upd = issue_items(cfg, t, packed)
