@@ -99,7 +99,8 @@ class Cfg:
         self.v_swe = self.v_swr + S
         self.v_sae = self.v_swe + 1                # one per fragment buffer
         self.v_doff = self.v_swe + 1 + NBUF
-        self.v_t = self.wbase  # 16 epilogue temporaries in the (then idle) weight ring, before the read-back
+        self.v_t = self.wbase + 32  # 16 epilogue temporaries in the (then idle) weight ring, above the two
+        # 16-register read-back buffers
         assert self.v_alo >= 0 and 6 * S >= 16  # epilogue packs 16 dwords into the address registers
         # epilogue: 8 LDS chunk addresses in the (then idle) fragment registers or above the rows read back
         # into the weight ring (4 registers per 8 rows)
@@ -252,25 +253,38 @@ def body(cfg, packed, rbe):
     out += compute(cfg, 0, t0, packed, rbe, final=True) + [f"{fin_mid}:"]
     for s in range(1, cfg.S):
         out += compute(cfg, s, (s + cfg.S - 1) % cfg.S, packed, rbe, final=True)
-    out.append("s_branch 9f")
+    out.append(f"s_branch {700 + rbe}f")
     return out
 
 
-def epilogue(cfg):
-    """bf16 results through LDS to full-line global stores.
+def epilogue(cfg, rbe):
+    """bf16 results through LDS to full-line global stores, for units of rbe row tiles.
 
     The ring is idle once the loop has ended, so each wave writes its rows x 64 columns of bf16 to a private
     LDS region (row m at m*128, 16-byte chunk c at position c ^ (m & 7)), reads them back as 16 bytes per lane,
     8 lanes per row, and stores 8 whole 128-byte rows per instruction (rows >= mrows masked off; %[t] counts
     the rows left; the stores are nontemporal: the output is read back by another kernel, not by this one).
-    A final barrier keeps the next unit's copies into the ring behind every wave's reads."""
-    out = ["9:", "s_waitcnt vmcnt(0)", "s_waitcnt lgkmcnt(0)", "s_barrier", "s_nop 15", "s_nop 15",
+    The three phases are pipelined by row tile: while row tile j is converted and written to LDS, row tile
+    j - 1's read-back lands and its stores leave (the conversions, the LDS traffic and the stores use
+    different units).  The final barrier (label 7, shared) keeps the next unit's copies into the ring behind
+    every wave's reads."""
+    out = [f"{700 + rbe}:", "s_waitcnt vmcnt(0)", "s_waitcnt lgkmcnt(0)", "s_barrier", "s_nop 15", "s_nop 15",
            "s_cmp_eq_u32 %[won], 0", "s_cbranch_scc1 7f"]
     T, E = cfg.v_t, cfg.v_ep
     for c in range(8):  # LDS address of logical chunk c of this lane's row (plus the lane's 8-byte half)
         out += [f"v_xor_b32_e32 v{E + c}, {c}, %[xr]", f"v_lshl_add_u32 v{E + c}, v{E + c}, 4, %[epb]"]
-    for j in range(cfg.rt):
-        out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 6f"]
+    out += ["s_mov_b32 %[t], %[mrows]", f"v_mov_b32_e32 v{cfg.v_doff}, %[doff]"]
+
+    def stores(j):  # row tile j's 4 groups of 8 rows, read back into buffer j % 2 of the weight ring
+        st = []
+        for q in range(4):
+            r = cfg.wbase + 16 * (j % 2) + 4 * q
+            st += ["v_cmp_gt_i32_e32 vcc, %[t], %[l8]", "s_and_saveexec_b64 %[sv], vcc",
+                   f"global_store_dwordx4 v{cfg.v_doff}, v[{r}:{r + 3}], %[db] nt", "s_mov_b64 exec, %[sv]",
+                   f"v_add_u32_e32 v{cfg.v_doff}, %[dstep], v{cfg.v_doff}", "s_sub_i32 %[t], %[t], 8"]
+        return st
+
+    for j in range(rbe):
         for ct in range(2):
             for r in range(16):
                 out.append(f"v_accvgpr_read_b32 v{T + r}, a{cfg.acc(j, ct) + r}")
@@ -285,23 +299,14 @@ def epilogue(cfg):
                 pr = cfg.v_alo + 8 * ct + 2 * g
                 off = f" offset:{4096 * j}" if j else ""
                 out.append(f"ds_write_b64 v{E + 4 * ct + g}, v[{pr}:{pr + 1}]{off}")
-    out += ["6:", "s_waitcnt lgkmcnt(0)"]
-    for j in range(cfg.rt):
-        out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 5f"]
-        for q in range(4):
+        for q in range(4):  # in order after this wave's writes of the same rows
+            r = cfg.wbase + 16 * (j % 2) + 4 * q
             i = 4 * j + q
-            r = cfg.wbase + 4 * i
             off = f" offset:{1024 * i}" if i else ""
             out.append(f"ds_read_b128 v[{r}:{r + 3}], %[rb]{off}")
-    out += ["5:", "s_waitcnt lgkmcnt(0)", "s_mov_b32 %[t], %[mrows]", f"v_mov_b32_e32 v{cfg.v_doff}, %[doff]"]
-    for j in range(cfg.rt):
-        out += [f"s_cmp_le_u32 %[rbe], {j}", "s_cbranch_scc1 7f"]
-        for q in range(4):
-            r = cfg.wbase + 4 * (4 * j + q)
-            out += ["v_cmp_gt_i32_e32 vcc, %[t], %[l8]", "s_and_saveexec_b64 %[sv], vcc",
-                    f"global_store_dwordx4 v{cfg.v_doff}, v[{r}:{r + 3}], %[db] nt", "s_mov_b64 exec, %[sv]",
-                    f"v_add_u32_e32 v{cfg.v_doff}, %[dstep], v{cfg.v_doff}", "s_sub_i32 %[t], %[t], 8"]
-    out += ["7:", "s_barrier"]
+        if j:  # row tile j - 1's read-back is in once at most this tile's 8 writes and 4 reads are pending
+            out += ["s_waitcnt lgkmcnt(12)"] + stores(j - 1)
+    out += ["s_waitcnt lgkmcnt(0)"] + stores(rbe - 1) + ["s_branch 7f"]
     return out
 
 
@@ -328,7 +333,9 @@ def program(cfg, packed):
         out += [f"s_cmp_eq_u32 %[rbe], {r}", f"s_cbranch_scc1 {100 + r}f"]
     for r in range(cfg.rt, 1, -1):
         out += [f"{100 + r}:"] + body(cfg, packed, r)
-    out += epilogue(cfg)
+    for r in range(cfg.rt, 1, -1):
+        out += epilogue(cfg, r)
+    out += ["7:", "s_barrier"]
     return out
 
 
