@@ -213,14 +213,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 
 // ----------------------------------------------------------------------------
 // Tall tiles (prefill): up to 192 or 256 rows x 256 columns per unit, 4 waves,
-// each owning 64 columns and all 6 or 8 row tiles of 32 (one wave per SIMD),
-// v_mfma_scale_f32_32x32x64_f8f6f4 (full rate from a single wave per SIMD,
-// where the 16x16x128 form needs two).
-//  * Weights are private to a wave and stream from HBM straight into an
-//    S-deep register ring (S - 1 K blocks in flight); activations are shared
-//    and copied global->LDS (global_load_lds) into an S-deep LDS ring.  Every
-//    K block issues the same loads (the tail re-reads the last block), so one
-//    exact vmcnt serves every step.
+// each owning 64 columns and all 6 or 8 row tiles of 32 (one wave per SIMD:
+// the 192 or 256 accumulators fill the AGPRs), v_mfma_scale_f32_32x32x64_f8f6f4.
+//  * Weights are private to a wave and stream from HBM straight into a 4-deep
+//    register ring; activations are shared and copied global->LDS
+//    (global_load_lds) into a 4-deep LDS ring.  K step ks issues the loads of
+//    block ks + 3; the barrier that publishes block ks + 1 sits before the
+//    step's last row tile, so the next block's first fragments are read
+//    behind that tile's matrix instructions.
 //  * Scales ride the same pipeline, so a unit starts without any staging
 //    round trip: every 4 K blocks one 16-byte global_load_lds per lane copies
 //    the next 4 fp32 row scales of 256 rows into one of two LDS group buffers
@@ -230,12 +230,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 //    right by 23.  This needs K/128 to be a multiple of 4 and SFA 16-byte
 //    aligned; other calls take the 64-row tile.
 //  * The K loop and the epilogue are written out in assembly
-//    (gen_fp8_asm.py -> gemm_fp8_tall_loop.inc): fixed registers for the
-//    accumulators and the weight ring, the next row block's activation
-//    fragments read from LDS while the current block's matrix instructions
-//    run, loads spread between the matrix instructions, 32-row granularity
-//    (a unit computes ceil(rows/32) row tiles), and v_cvt_pk_bf16_f32 (round
-//    to nearest even) in the epilogue.
+//    (gen_fp8_asm.py -> gemm_fp8_tall_loop.inc), once per row-tile count, so
+//    no branch sits between matrix instructions: fixed registers for the
+//    accumulators and the weight ring, loads spread one per matrix
+//    instruction, exact vmcnt waits, a unit computes max(2, ceil(rows/32))
+//    row tiles (the surplus rows repeat the last valid row and are never
+//    stored), and v_cvt_pk_bf16_f32 (round to nearest even) in an epilogue
+//    pipelined by row tile.
 #include "gemm_fp8_tall_loop.inc"
 
 template <int ROWS>
