@@ -435,7 +435,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU: the hot path runs on one MI355X; "
+        print(json.dumps({"error": "bench.py measures one GPU: the hot path runs on one MI355X; "
                                    "multi-GPU expert parallelism is a design note, not a measured path",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
