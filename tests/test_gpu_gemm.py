@@ -121,6 +121,18 @@ def test_fp8_tall_schedule_every_chunk_class(packed):
 
 
 @pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("K", [1536, 2560])
+def test_fp8_tall_every_row_tile_count_long_k(K, packed):
+    """Every row-tile count of both tall heights (units of 1..256 rows, so every loop body) with a K loop that
+    has main iterations before its last one (K/128 = 12 or 20)."""
+    require_gpu()
+    counts = [32 * r - 5 for r in range(1, 9)] + [32 * r for r in range(1, 9)] + [0, 3, 256 + 100, 192 + 40]
+    c = _fp8_case(51 + K, counts, N=256, K=K, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (128, 256):
+        _check_fp8(c, _run_fp8(c, em, packed=packed))
+
+
+@pytest.mark.parametrize("packed", [False, True])
 def test_fp8_degenerate_expert_counts(packed):
     """No rows at all (an empty unit table), 1024 experts with 0..3 rows (16 experts per lane of the table
     build, every 4-bit size-class slot used; N = 128, so half of each tall tile's waves store nothing), and a
