@@ -235,8 +235,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 //    accumulators and the weight ring, loads spread one per matrix
 //    instruction, exact vmcnt waits, a unit computes max(2, ceil(rows/32))
 //    row tiles (the surplus rows repeat the last valid row and are never
-//    stored), and v_cvt_pk_bf16_f32 (round to nearest even) in an epilogue
-//    pipelined by row tile.
+//    stored), and v_cvt_pk_bf16_f32 (round to nearest even).  The epilogue
+//    runs inside the last K block, which issues no loads: while row tile j is
+//    multiplied, row tile j - 1 is converted and staged through the wave's
+//    4 KB of the idle ring slot 0 and row tile j - 2 is stored as whole
+//    128-byte rows; only the last row tile is stored after the loop.
 #include "gemm_fp8_tall_loop.inc"
 
 template <int ROWS>
@@ -279,8 +282,8 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
                : [wb] "s"(wb), [ab] "s"(ab), [sb] "s"(sb), [swb] "s"(swb), [ma] "s"(ma),                       \
                  [a00] "v"(af[0]), [a01] "v"(af[1]), [a10] "v"(af[2]), [a11] "v"(af[3]), [sadr] "v"(sadr),        \
                  [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb),                                                 \
-                 [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [wstep] "s"(wstep), [l8] "v"(l8),           \
-                 [xr] "v"(xr), [epb] "v"(epb), [rb] "v"(rb)                                                      \
+                 [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [wm] "s"(wm), [wstep] "s"(wstep),           \
+                 [l8] "v"(l8), [epb] "v"(epb), [rb] "v"(rb)                                                      \
                : "memory", "vcc", "exec", "scc", CLOBBERS)
 
 template <int ROWS, bool PACKED>
@@ -326,12 +329,14 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   const uint32_t sadr = abase + kScOff + 16 * l32;  // row scale of row tile j, block s of the group: +512 j + 4 s
   const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.b[wv * kTApw * 1024]));
   uint32_t msg = (uint32_t)uniform((int)lds_offset(&sm.b[kScOff + wv * 1024]));  // group buffer 0, this wave's rows
-  // epilogue: the wave's bf16 rows go through its own LDS region (row m at m*128, 16-byte chunk c at
-  // position c ^ (m & 7)); each lane writes 8 bytes of row l32 and reads back 16 bytes (chunk lane & 7) of
-  // row lane >> 3 of every 8-row group, stored as whole 128-byte rows
-  const uint32_t epb = abase + (uint32_t)(wv * ROWS * 128 + l32 * 128 + 8 * hh);
-  const int xr = l32 & 7, l8 = lane >> 3;
-  const uint32_t rb = abase + (uint32_t)(wv * ROWS * 128 + l8 * 128 + 16 * ((lane & 7) ^ (l8 & 7)));
+  // epilogue: one 32-row tile of the wave's bf16 rows at a time goes through its own 4 KB of ring slot 0
+  // (row m at m*128, 16-byte chunk c at position c ^ (m & 7)); each lane writes 8 bytes of row l32 (epb:
+  // chunk 0's address, including the lane's half) and reads back 16 bytes (chunk lane & 7) of row lane >> 3
+  // of every 8-row group, stored as whole 128-byte rows
+  const uint32_t epb = abase + (uint32_t)(wv * 4096 + l32 * 128 + 16 * (l32 & 7) + 8 * hh);
+  const int l8 = lane >> 3;
+  const uint32_t rb = abase + (uint32_t)(wv * 4096 + l8 * 128 + 16 * ((lane & 7) ^ (l8 & 7)));
+  const uint64_t wm = uniform_u64(won ? ~0ull : 0ull);  // exec mask of the stores: none for an idle wave
   const uint64_t db = uniform_u64((uint64_t)(a.D + (int64_t)u.row0 * N));
   uint32_t doff = (uint32_t)(l8 * N + ncol0 + 8 * (lane & 7)) * 2u;
   const int dstep = uniform(16 * N);  // output bytes between 8-row groups

@@ -48,7 +48,11 @@ tile left the matrix pipe idle; the branch-free bodies are 4-9% faster).  The
 loop's last iteration is emitted apart (it issues only block kb - 1 and waits
 for fewer loads), so the main loop's only branch is its back-edge, and a
 unit's first step is emitted apart too: its matrix instructions add to 0, so
-the accumulators are never zeroed.
+the accumulators are never zeroed.  The unit's last K block issues no loads
+and leaves ring slots 0 .. 2 idle, so the epilogue runs inside it: while row
+tile j is multiplied, row tile j - 1 is converted to bf16 and staged through
+the wave's 4 KB of LDS slot 0, and row tile j - 2 is stored as whole 128-byte
+rows; after the loop only the last row tile remains.
 
 Register map (physical, listed as clobbers of the asm statement):
   a[0:rows-1] accumulators (row tile j, column tile ct at a[32j + 16ct]);
@@ -58,9 +62,9 @@ Register map (physical, listed as clobbers of the asm statement):
   v[256-32S:255] weight ring (S slots x 2 column tiles x 2 halves x 8);
   below it: per slot the four fragment addresses, the row-scale address and
   the weight-scale register; the weight exponent, one row-scale exponent per
-  fragment buffer and the output offset.  The epilogue's 16 temporaries and the
-  rows it reads back from LDS use the weight ring; its 8 LDS addresses sit in
-  the fragment registers (256 rows) or above the rows read back (192 rows).
+  fragment buffer and the output offset.  The epilogue uses weight-ring slots
+  0 .. 2, idle in the last K block: two 16-register buffers for the rows read
+  back from LDS, 32 temporaries, 16 packed bf16 pairs and 8 LDS addresses.
 
 Usage: python gen_fp8_asm.py OUT.inc
 """
@@ -99,14 +103,16 @@ class Cfg:
         self.v_swe = self.v_swr + S
         self.v_sae = self.v_swe + 1                # one per fragment buffer
         self.v_doff = self.v_swe + 1 + NBUF
-        self.v_t = self.wbase + 32  # 16 epilogue temporaries in the (then idle) weight ring, above the two
-        # 16-register read-back buffers
-        assert self.v_alo >= 0 and 6 * S >= 16  # epilogue packs 16 dwords into the address registers
-        # epilogue: 8 LDS chunk addresses in the (then idle) fragment registers or above the rows read back
-        # into the weight ring (4 registers per 8 rows)
-        self.v_ep = self.v_frag if self.frag_v else self.wbase + rows // 2
-        assert self.frag_v or self.v_ep + 8 <= 256
-        assert 4 * (rows // 8) <= 32 * S and 4 * rows * 128 <= S * self.slot  # read-back registers; LDS regions
+        assert self.v_alo >= 0
+        # epilogue registers, in weight-ring slots 0 .. 2 (idle during the last K block, which uses slot 3):
+        # two 16-register read-back buffers, 32 temporaries, 16 packed bf16 pairs, 8 LDS chunk addresses
+        self.v_rbk = self.wbase
+        self.v_t = self.wbase + 32
+        self.v_pk = self.wbase + 64
+        self.v_ep = self.wbase + 80
+        assert self.v_ep + 8 <= self.wbase + 32 * (S - 1)
+        # each wave stages one 32-row tile of bf16 (32 x 128 bytes) in its 4 KB of ring slot 0
+        assert 4 * 4096 <= self.slot
 
     def acc(self, j, ct):
         return 32 * j + 16 * ct
@@ -199,6 +205,8 @@ def compute(cfg, s, t, packed, rbe, final=False, first=False):
 
     first: the unit's first K block; each accumulator's first matrix instruction adds to 0 instead of the
     accumulator, so the accumulators need no zeroing."""
+    if final and s == cfg.S - 1:
+        return compute_last(cfg, s, rbe)
     items, upd = issue_items(cfg, t, packed)
     if final and s > 0:
         items, upd = [], []
@@ -257,56 +265,114 @@ def body(cfg, packed, rbe):
     return out
 
 
-def epilogue(cfg, rbe):
-    """bf16 results through LDS to full-line global stores, for units of rbe row tiles.
+def ep_setup(cfg):
+    """Output offset, rows left, and the LDS address of each logical 16-byte chunk c of this lane's staged row
+    (row m at m*128 of the wave's 4 KB, chunk c at position c ^ (m & 7), plus the lane's 8-byte half): %[epb]
+    is chunk 0's, and the XOR flips the position bits."""
+    E = cfg.v_ep
+    return ([f"v_mov_b32_e32 v{cfg.v_doff}, %[doff]", "s_mov_b32 %[t], %[mrows]", f"v_mov_b32_e32 v{E}, %[epb]"]
+            + [f"v_xor_b32_e32 v{E + c}, {16 * c}, %[epb]" for c in range(1, 8)])
 
-    The ring is idle once the loop has ended, so each wave writes its rows x 64 columns of bf16 to a private
-    LDS region (row m at m*128, 16-byte chunk c at position c ^ (m & 7)), reads them back as 16 bytes per lane,
-    8 lanes per row, and stores 8 whole 128-byte rows per instruction (rows >= mrows masked off; %[t] counts
-    the rows left; the stores are nontemporal: the output is read back by another kernel, not by this one).
-    The three phases are pipelined by row tile: while row tile j is converted and written to LDS, row tile
-    j - 1's read-back lands and its stores leave (the conversions, the LDS traffic and the stores use
-    different units).  The final barrier (label 7, shared) keeps the next unit's copies into the ring behind
-    every wave's reads."""
-    out = [f"{700 + rbe}:", "s_waitcnt vmcnt(0)", "s_waitcnt lgkmcnt(0)", "s_barrier", "s_nop 15", "s_nop 15",
-           "s_cmp_eq_u32 %[won], 0", "s_cbranch_scc1 7f"]
-    T, E = cfg.v_t, cfg.v_ep
-    for c in range(8):  # LDS address of logical chunk c of this lane's row (plus the lane's 8-byte half)
-        out += [f"v_xor_b32_e32 v{E + c}, {c}, %[xr]", f"v_lshl_add_u32 v{E + c}, v{E + c}, 4, %[epb]"]
-    out += ["s_mov_b32 %[t], %[mrows]", f"v_mov_b32_e32 v{cfg.v_doff}, %[doff]"]
 
-    def stores(j):  # row tile j's 4 groups of 8 rows, read back into buffer j % 2 of the weight ring
-        st = []
-        for q in range(4):
-            r = cfg.wbase + 16 * (j % 2) + 4 * q
-            st += ["v_cmp_gt_i32_e32 vcc, %[t], %[l8]", "s_and_saveexec_b64 %[sv], vcc",
-                   f"global_store_dwordx4 v{cfg.v_doff}, v[{r}:{r + 3}], %[db] nt", "s_mov_b64 exec, %[sv]",
-                   f"v_add_u32_e32 v{cfg.v_doff}, %[dstep], v{cfg.v_doff}", "s_sub_i32 %[t], %[t], 8"]
-        return st
+def ep_convert(cfg, j, ct):
+    """Row tile j, column tile ct: accumulators to 8 packed bf16 pairs (RNE)."""
+    T = cfg.v_t + 16 * ct
+    out = [f"v_accvgpr_read_b32 v{T + r}, a{cfg.acc(j, ct) + r}" for r in range(16)] + ["s_nop 1"]
+    for g in range(4):
+        pr = cfg.v_pk + 8 * ct + 2 * g
+        out += [f"v_cvt_pk_bf16_f32 v{pr}, v{T + 4 * g}, v{T + 4 * g + 1}",
+                f"v_cvt_pk_bf16_f32 v{pr + 1}, v{T + 4 * g + 2}, v{T + 4 * g + 3}"]
+    return out
 
+
+def ep_stage(cfg, j):
+    """Write row tile j's bf16 rows to the wave's staging area and read them back as 16 bytes per lane, 8 lanes
+    per 128-byte row, into read-back buffer j % 2 (LDS operations of one wave complete in order)."""
+    out = [f"ds_write_b64 v{cfg.v_ep + 4 * ct + g}, v[{cfg.v_pk + 8 * ct + 2 * g}:{cfg.v_pk + 8 * ct + 2 * g + 1}]"
+           for ct in range(2) for g in range(4)]
+    for q in range(4):
+        r = cfg.v_rbk + 16 * (j % 2) + 4 * q
+        out.append(f"ds_read_b128 v[{r}:{r + 3}], %[rb]" + (f" offset:{1024 * q}" if q else ""))
+    return out
+
+
+def ep_store_full(cfg, j):
+    """Row tile j, all 32 rows valid: 8 whole 128-byte rows per store (none from a wave without columns)."""
+    out = ["s_and_saveexec_b64 %[sv], %[wm]"]
+    for q in range(4):
+        r = cfg.v_rbk + 16 * (j % 2) + 4 * q
+        out += [f"global_store_dwordx4 v{cfg.v_doff}, v[{r}:{r + 3}], %[db] nt",
+                f"v_add_u32_e32 v{cfg.v_doff}, %[dstep], v{cfg.v_doff}"]
+    return out + ["s_mov_b64 exec, %[sv]", "s_sub_i32 %[t], %[t], 32", "s_nop 1"]
+
+
+def ep_store_masked(cfg, j):
+    """Row tile j's 4 groups of 8 rows, rows at or past the unit's end masked off (%[t] counts the rows left)."""
+    out = []
+    for q in range(4):
+        r = cfg.v_rbk + 16 * (j % 2) + 4 * q
+        out += ["v_cmp_gt_i32_e32 vcc, %[t], %[l8]", "s_and_saveexec_b64 %[sv], vcc",
+                f"global_store_dwordx4 v{cfg.v_doff}, v[{r}:{r + 3}], %[db] nt", "s_mov_b64 exec, %[sv]",
+                f"v_add_u32_e32 v{cfg.v_doff}, %[dstep], v{cfg.v_doff}", "s_sub_i32 %[t], %[t], 8"]
+    return out
+
+
+def compute_last(cfg, s, rbe):
+    """The unit's last K block (ring slot s = S - 1 of the final iteration), with the epilogue folded in.
+
+    No loads are issued and no block is published, so the load path and ring slots 0 .. 2 are idle: while row
+    tile j is multiplied, row tile j - 1 (final since the previous row tile's matrix instructions) is
+    converted to bf16 and staged through the wave's 4 KB of slot 0, and row tile j - 2, read back in the
+    previous row tile, is stored as whole 128-byte rows.  All rows of the row tiles stored here are valid
+    (only the last row tile, and row tile 0 of a two-tile unit, can be partial; both are stored by the
+    epilogue after the loop).  Row tile j + 1's fragments are read after row tile j's first matrix
+    instruction, and the LDS operations in flight stay within the 15 that lgkmcnt counts."""
+    out = [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}", "s_waitcnt lgkmcnt(0)",
+           f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"]
     for j in range(rbe):
-        for ct in range(2):
-            for r in range(16):
-                out.append(f"v_accvgpr_read_b32 v{T + r}, a{cfg.acc(j, ct) + r}")
-            out.append("s_nop 1")
-            for g in range(4):
-                pr = cfg.v_alo + 8 * ct + 2 * g
-                out.append(f"v_cvt_pk_bf16_f32 v{pr}, v{T + 4 * g}, v{T + 4 * g + 1}")
-                out.append(f"v_cvt_pk_bf16_f32 v{pr + 1}, v{T + 4 * g + 2}, v{T + 4 * g + 3}")
+        b = cfg.bufid(j)
+        nxt = j + 1 < rbe
+        bn = cfg.bufid(j + 1)
+        place = [[] for _ in range(4)]
+        if nxt:
+            if j >= 2:  # row tile j - 2's 12 staging operations may be in flight
+                place[0].append("s_waitcnt lgkmcnt(10)")
+            place[0] += frag_reads(cfg, s, bn, j + 1) + [
+                f"ds_read_b32 v{cfg.v_sae + bn}, v{cfg.v_sadr} offset:{512 * (j + 1) + 4 * s}"]
+        if j == 0:
+            place[1] += ep_setup(cfg)
+        if j >= 2:  # row tile j - 2 read back (the fragment reads of row tile j + 1 may still be in flight)
+            place[1] += [f"s_waitcnt lgkmcnt({5 if nxt else 0})"] + ep_store_full(cfg, j - 2)
+        if j >= 1:
+            # the accumulators of row tile j - 1 were last written 4 matrix instructions ago; the nops make
+            # the required wait states explicit where few other instructions lie between
+            place[2] += (["s_nop 15"] if j == 1 else []) + ep_convert(cfg, j - 1, 0)
+            place[3] += ep_convert(cfg, j - 1, 1)
+        if nxt:
+            place[3] += ["s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"]
+        if j >= 1:
+            place[3] += ["s_nop 1"] + ep_stage(cfg, j - 1)
         out.append("s_nop 1")
-        for ct in range(2):
-            for g in range(4):
-                pr = cfg.v_alo + 8 * ct + 2 * g
-                off = f" offset:{4096 * j}" if j else ""
-                out.append(f"ds_write_b64 v{E + 4 * ct + g}, v[{pr}:{pr + 1}]{off}")
-        for q in range(4):  # in order after this wave's writes of the same rows
-            r = cfg.wbase + 16 * (j % 2) + 4 * q
-            i = 4 * j + q
-            off = f" offset:{1024 * i}" if i else ""
-            out.append(f"ds_read_b128 v[{r}:{r + 3}], %[rb]{off}")
-        if j:  # row tile j - 1's read-back is in once at most this tile's 8 writes and 4 reads are pending
-            out += ["s_waitcnt lgkmcnt(12)"] + stores(j - 1)
-    out += ["s_waitcnt lgkmcnt(0)"] + stores(rbe - 1) + ["s_branch 7f"]
+        q = 0
+        for kk in range(2):
+            for ct in range(2):
+                a0 = cfg.acc(j, ct)
+                out.append(f"v_mfma_scale_f32_32x32x64_f8f6f4 a[{a0}:{a0 + 15}], {wreg(cfg, s, ct, kk, 0, 7)}, "
+                           f"{cfg.buf(b, kk)}, a[{a0}:{a0 + 15}], v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
+                out += place[q]
+                q += 1
+    return out
+
+
+def epilogue(cfg, rbe):
+    """After the loop, for units of rbe row tiles: store row tile rbe - 2 (staged while the last row tile was
+    multiplied) and convert, stage and store row tile rbe - 1, masking rows at or past the unit's end.  A
+    wave without columns stores nothing.  The final barrier (label 7, shared) keeps the next unit's copies
+    into the ring behind every wave's use of its staging area."""
+    out = [f"{700 + rbe}:", "s_cmp_eq_u32 %[won], 0", "s_cbranch_scc1 7f", "s_waitcnt lgkmcnt(0)"]
+    out += ep_store_masked(cfg, rbe - 2) + ["s_nop 15", "s_nop 15"]
+    out += ep_convert(cfg, rbe - 1, 0) + ep_convert(cfg, rbe - 1, 1) + ["s_nop 1"] + ep_stage(cfg, rbe - 1)
+    out += ["s_waitcnt lgkmcnt(0)"] + ep_store_masked(cfg, rbe - 1) + ["s_branch 7f"]
     return out
 
 

@@ -45,10 +45,39 @@ def test_wait_counts_fit_the_hardware_fields(gen):
                 assert 0 <= int(m.group(1)) <= 15, line
 
 
+_REG = re.compile(r"\b([va])(?:\[(\d+):(\d+)\]|(\d+)\b)")
+
+
+def _regs(text):
+    out = set()
+    for m in _REG.finditer(text):
+        lo = int(m.group(2) if m.group(2) is not None else m.group(4))
+        hi = int(m.group(3)) if m.group(3) is not None else lo
+        out |= {(m.group(1), r) for r in range(lo, hi + 1)}
+    return out
+
+
+def _reads_writes(line):
+    """Fixed registers an instruction reads and writes (operands the compiler assigns, %[...], are not
+    fixed registers and are left out)."""
+    line = re.sub(r"\s+op_sel_hi:\[[^\]]*\]", "", line)
+    mnem, _, rest = line.partition(" ")
+    ops = [o.strip().split()[0] for o in rest.split(",")] if rest else []
+    if mnem.startswith(("global_store", "ds_write", "global_load_lds", "s_")) or not ops:
+        return set().union(*map(_regs, ops)) if ops else set(), set()
+    return set().union(set(), *map(_regs, ops[1:])), _regs(ops[0])
+
+
 def _walk(prog, rbe, kb):
     """Follow the generated control flow for one unit (row-tile count rbe, kb K blocks) and count what it
-    executes: barriers, matrix instructions and vector-memory loads.  Scalar tests are evaluated for the three
-    conditions the text branches on (the row-tile dispatch, kb <= 4, the loop back-edge)."""
+    executes: barriers, matrix instructions, vector-memory loads and stores.  Scalar tests are evaluated for
+    the three conditions the text branches on (the row-tile dispatch, kb <= 4, the loop back-edge).
+
+    Along the way it models this wave's own counters with nothing completing before it is waited for: an
+    instruction that reads or overwrites a register still targeted by a pending LDS read or vector-memory load
+    fails, as does a 16th LDS operation in flight; reading an accumulator needs 18 wait states (instructions,
+    s_nop N counting N + 1) after the matrix instruction that wrote it, and a matrix instruction reading a VGPR
+    written by a vector ALU instruction needs 2."""
     labels = {l[:-1]: i for i, l in enumerate(prog) if re.fullmatch(r"\d+:", l)}
 
     def target(ref, i):
@@ -58,7 +87,10 @@ def _walk(prog, rbe, kb):
         return max(j for j in range(i) if prog[j] == f"{n}:")
 
     pc, scc, ks = 0, False, None
-    counts = {"barrier": 0, "mfma": 0, "load": 0, "steps": 0}
+    counts = {"barrier": 0, "mfma": 0, "load": 0, "store": 0, "lds_max": 0}
+    lgkm, vm = [], []   # pending LDS / vector-memory operations: the registers each will write
+    ws = 0              # wait states so far
+    mfma_w, valu_w = {}, {}
     for _ in range(10_000_000):
         if pc >= len(prog):
             break
@@ -69,6 +101,36 @@ def _walk(prog, rbe, kb):
             counts["mfma"] += 1
         elif line.startswith("global_load"):
             counts["load"] += 1
+        elif line.startswith("global_store"):
+            counts["store"] += 1
+        m = re.fullmatch(r"s_waitcnt lgkmcnt\((\d+)\)", line)
+        if m:
+            del lgkm[:max(0, len(lgkm) - int(m.group(1)))]
+        m = re.fullmatch(r"s_waitcnt vmcnt\((\d+)\)", line)
+        if m:
+            del vm[:max(0, len(vm) - int(m.group(1)))]
+        if not re.fullmatch(r"\d+:", line):
+            rd, wr = _reads_writes(line)
+            pending = set().union(set(), *lgkm, *vm)
+            assert not (rd | wr) & pending, (rbe, kb, pc, line, sorted((rd | wr) & pending))
+            if line.startswith("v_accvgpr_read"):
+                for r in rd:
+                    assert ws - mfma_w.get(r, -99) >= 18, (rbe, kb, pc, line)
+            if line.startswith("v_mfma"):
+                for r in rd:
+                    assert ws - valu_w.get(r, -99) >= 2, (rbe, kb, pc, line)
+                for r in wr:
+                    mfma_w[r] = ws
+            elif line.startswith("v_"):
+                for r in wr:
+                    valu_w[r] = ws
+            if line.startswith("ds_"):
+                lgkm.append(wr)
+                counts["lds_max"] = max(counts["lds_max"], len(lgkm))
+            elif line.startswith("global_"):
+                vm.append(wr)
+            m = re.fullmatch(r"s_nop (\d+)", line)
+            ws += int(m.group(1)) + 1 if m else 1
         m = re.fullmatch(r"s_cmp_eq_u32 %\[rbe\], (\d+)", line)
         if m:
             scc = rbe == int(m.group(1))
@@ -98,16 +160,20 @@ def _walk(prog, rbe, kb):
 @pytest.mark.parametrize("kb", [4, 8, 12, 56])
 def test_each_unit_path_runs_its_blocks_once(gen, kb):
     """For every row-tile count: 4 MFMAs per row tile and K block, one barrier per K block but the last, plus
-    the prologue's and the epilogue's two (so all waves of a workgroup meet at the same barriers), and the
-    loads of exactly kb blocks."""
+    the prologue's and the one that ends the unit (so all waves of a workgroup meet at the same barriers), the
+    loads of exactly kb blocks, 4 stores (of 8 rows each) per row tile, at most 15 LDS operations in flight, and
+    no register used before the load or LDS read that fills it has been waited for."""
     for cfg in gen.CONFIGS:
-        prog = gen.program(cfg, True)
-        for rbe in range(2, cfg.rt + 1):
-            c = _walk(prog, rbe, kb)
-            assert c["mfma"] == 4 * rbe * kb, (cfg.name, rbe, kb, c)
-            assert c["barrier"] == 1 + (kb - 1) + 2, (cfg.name, rbe, kb, c)
-            groups = kb // gen.GROUP
-            assert c["load"] == kb * cfg.ops + groups, (cfg.name, rbe, kb, c)
+        for packed in (False, True):
+            prog = gen.program(cfg, packed)
+            for rbe in range(2, cfg.rt + 1):
+                c = _walk(prog, rbe, kb)
+                assert c["mfma"] == 4 * rbe * kb, (cfg.name, rbe, kb, c)
+                assert c["barrier"] == 1 + (kb - 1) + 1, (cfg.name, rbe, kb, c)
+                groups = kb // gen.GROUP
+                assert c["load"] == kb * cfg.ops + groups, (cfg.name, rbe, kb, c)
+                assert c["store"] == 4 * rbe, (cfg.name, rbe, kb, c)
+                assert c["lds_max"] <= 15, (cfg.name, rbe, kb, c)
 
 
 def test_register_regions_do_not_overlap(gen):
@@ -121,5 +187,8 @@ def test_register_regions_do_not_overlap(gen):
         else:
             assert cfg.nacc + 16 * gen.NBUF <= 256  # fragments in the AGPRs above the accumulators
         assert cfg.v_doff < (cfg.v_frag if cfg.frag_v else cfg.wbase)
-        # epilogue: two 16-register read-back buffers and 16 temporaries inside the (idle) weight ring
-        assert cfg.wbase + 32 <= cfg.v_t and cfg.v_t + 16 <= 256
+        # epilogue registers: inside weight-ring slots 0 .. 2, which the last K block does not use
+        ep = [(cfg.v_rbk, 32), (cfg.v_t, 32), (cfg.v_pk, 16), (cfg.v_ep, 8)]
+        used = [r for base, n in ep for r in range(base, base + n)]
+        assert len(set(used)) == len(used)
+        assert min(used) >= cfg.wbase and max(used) < cfg.wbase + 32 * (cfg.S - 1)
