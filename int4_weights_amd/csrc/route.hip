@@ -62,7 +62,10 @@ __device__ inline int id_bits(int E) { return 32 - __clz(E); }  // bits to hold 
 // Copy one payload row (all lanes of the wave cooperate).  Loads go out in
 // batches of 8 per lane before any store: the compiler cannot move a load
 // above a store to a possibly aliasing address, so a plain loop would pay one
-// memory round trip per 1 KB.
+// memory round trip per 1 KB.  The packed rows are written once and next read
+// by the grouped GEMM, so the stores stream past the caches (the whole
+// DeepSeek-V3- and Qwen3-shaped steps were 0.3-0.5% faster: no dirty packed
+// rows are left to be written back while the GEMM streams its weights).
 template <typename T>
 __device__ inline void copy_row_as(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t nbytes) {
   constexpr int kB = 8;
@@ -74,7 +77,7 @@ __device__ inline void copy_row_as(const uint8_t* __restrict__ src, uint8_t* __r
       if (base + b * kStep < nbytes) r[b] = *(const T*)(src + base + b * kStep);
 #pragma unroll
     for (int b = 0; b < kB; ++b)
-      if (base + b * kStep < nbytes) *(T*)(dst + base + b * kStep) = r[b];
+      if (base + b * kStep < nbytes) __builtin_nontemporal_store(r[b], (T*)(dst + base + b * kStep));
   }
 }
 __device__ inline void copy_row(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t nbytes) {
