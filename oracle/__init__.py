@@ -57,9 +57,7 @@ from .routing import (
     pack_rows,
 )
 from .gemm import grouped_gemm_fp8, grouped_gemm_int4, segments
-from .combine import combine
-from .layout import (pack_weight_fp8, pack_weight_int4, packed_nibble_int4, packed_offset, packed_scale_offset_int4,
-                     unpack_weight_fp8, unpack_weight_int4)
+from .combine import combine, combine_fp32, f32_to_bf16_bits
 from .metrics import calc_diff, elementwise_ok, elementwise_excess
 
 __all__ = [
@@ -69,7 +67,6 @@ __all__ = [
     "quant_weight_int4", "dequant_act", "dequant_weight_fp8", "unpack_int4",
     "dequant_weight_int4",
     "DEV_ID_RANGE", "DEV_CAPACITY", "packed_rows_cap", "route", "pack_rows",
-    "grouped_gemm_fp8", "grouped_gemm_int4", "segments", "combine",
+    "grouped_gemm_fp8", "grouped_gemm_int4", "segments", "combine", "combine_fp32", "f32_to_bf16_bits",
     "calc_diff", "elementwise_ok", "elementwise_excess",
-    "pack_weight_fp8", "packed_offset", "unpack_weight_fp8",
 ]

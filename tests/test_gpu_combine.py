@@ -1,10 +1,11 @@
-"""GPU weighted combine vs the oracle.
+"""GPU weighted combine vs the oracle, bit for bit.
 
-Tolerance derived from the arithmetic: the GPU sums k fp32 products in slot
-order (each fma rounds once, relative error <= 2^-24 of the running sum) and
-rounds the fp32 result to bf16 once.  So
-  |z_gpu - z_exact| <= ulp_bf16(z_exact)/2 + (k+1) * 2^-24 * sum_r |p_r y_r|
-with ulp_bf16 taken at the larger of |z_exact| and the fp32 result.
+The path defines the combine's precision (reading A13): an fp32 fused
+multiply-add per slot in slot order r = 0..k-1 from +0, then round to nearest
+even to bf16.  oracle.combine_fp32 evaluates exactly that, so the GPU result
+must equal it in every bit.  The float64 oracle.combine is checked as well,
+with the bound the fp32 chain implies:
+  |z - z_exact| <= ulp_bf16/2 + (k+1) * 2^-24 * sum_r |p_r y_r|.
 """
 
 import json
@@ -34,10 +35,12 @@ def _run(y_bits, oi, w):
     moe.moe_unpermute_combine(Y, torch.from_numpy(oi.astype(np.int32)).to(DEV),
                               torch.from_numpy(w.astype(np.float32)).to(DEV), Z)
     torch.cuda.synchronize()
-    return Z.float().cpu().numpy().astype(np.float64)
+    return u16(Z)
 
 
-def _check(y_bits, oi, w, z):
+def _check(y_bits, oi, w, z_bits):
+    assert np.array_equal(z_bits, oracle.combine_fp32(y_bits, oi, w.astype(np.float32)))
+    z = oracle.bf16_bits_to_f64(z_bits)
     y = oracle.bf16_bits_to_f64(y_bits)
     ref = oracle.combine(y, oi, w.astype(np.float32).astype(np.float64))
     mag = oracle.combine(np.abs(y), oi, np.abs(w.astype(np.float32).astype(np.float64)))
@@ -59,19 +62,35 @@ def test_combine_worked_example():
     # the page's z_0 = 0.70 * y_packed[0] + 0.30 * y_packed[256]
     yf = oracle.bf16_bits_to_f64(y)
     z0 = np.float32(0.70) * yf[0] + np.float32(0.30) * yf[256]
-    assert np.allclose(z[0], z0, rtol=2 ** -7, atol=1e-6)
+    assert np.allclose(oracle.bf16_bits_to_f64(z[0]), z0, rtol=2 ** -7, atol=1e-6)
 
 
-@pytest.mark.parametrize("T,k,N,rows", [(1, 1, 8, 1), (333, 8, 4096, 3000), (64, 2, 256, 512), (9, 5, 1032, 40)])
+@pytest.mark.parametrize("T,k,N,rows", [(1, 1, 8, 1), (333, 8, 4096, 3000), (64, 2, 256, 512), (9, 5, 1032, 40),
+                                        (50, 12, 136, 64), (7, 64, 16, 100)])
 def test_combine_random_with_dropped_slots(T, k, N, rows):
     require_gpu()
     rng = np.random.default_rng(T + k + N)
     y = u16(torch.from_numpy(rng.standard_normal((rows, N)).astype(np.float32)).to(torch.bfloat16))
     oi = rng.integers(0, rows, size=(T, k)).astype(np.int32)
     oi[rng.random((T, k)) < 0.1] = -1
+    oi[rng.random((T, k)) < 0.02] = rows + 5  # past the rows of Y: skipped like -1
     w = rng.random((T, k)).astype(np.float32)
+    w[rng.random((T, k)) < 0.1] *= -1
     z = _run(y, oi, w)
     _check(y, oi, w, z)
+
+
+def test_combine_halfway_accumulator():
+    """Sums whose float64 value is an fp32 halfway point while the exact value is not."""
+    require_gpu()
+    import test_oracle_combine as pins
+
+    cases = pins._halfway_cases()
+    yb = oracle.f32_to_bf16_bits(np.array([[c[0]] * 8 for c in cases] + [[c[2]] * 8 for c in cases], np.float32))
+    n = len(cases)
+    oi = np.array([[i, n + i] for i in range(n)], np.int32)
+    w = np.array([[1.0, c[1]] for c in cases], np.float32)
+    _check(yb, oi, w, _run(yb, oi, w))
 
 
 def test_combine_determinism_20_runs():

@@ -167,6 +167,18 @@ def _fp8_gemm_and_combine(c, r, A_bits_of_token, D, Z, kept_codes_fn, label):
             zr += float(c["tw"][t, s]) * y_ref_rows[p]
     zg = Z[t][torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
     gemm_tolerance_check(zg[None], zr[None], 1e-3 if label == "fp8" else 1e-2)
+    _combine_bit_exact(D, Z, r["output_index"], c["tw"], [t, 0, c["T"] - 1])
+
+
+def _combine_bit_exact(D, Z, oi, tw, tokens):
+    """The combine alone, given the GPU's own GEMM rows: every bit of Z[t] equals the fp32 fma chain."""
+    for t in sorted(set(int(x) for x in tokens)):
+        slots = [int(p) for p in oi[t]]
+        valid = [p for p in slots if p >= 0]
+        rows = u16(D[torch.tensor(valid, dtype=torch.int64, device=DEV)]) if valid else np.zeros((0, D.shape[1]), np.uint16)
+        local = np.array([[valid.index(p) if p >= 0 else -1 for p in slots]], np.int32)
+        want = oracle.combine_fp32(rows, local, np.asarray(tw[t:t + 1], np.float32))
+        assert np.array_equal(u16(Z[t:t + 1]), want), f"combine of token {t}"
 
 
 def _oracle_fp8_weight_blocks(c, codes, sfw, kept, N, K):
@@ -266,6 +278,7 @@ def test_full_size_qwen3_skewed_up_down_combine():
     zr = sum(float(c["tw"][t, s]) * yrow[int(r["output_index"][t, s])] for s in range(c["k"]))
     zg = Zd[t][torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
     gemm_tolerance_check(zg[None], np.asarray(zr)[None], 1e-3)
+    _combine_bit_exact(Dd, Zd, r["output_index"], c["tw"], [t, 0, c["T"] - 1])
 
 
 def test_full_size_int4_decode_layer():

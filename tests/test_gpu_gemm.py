@@ -6,6 +6,7 @@ import torch
 
 import int4_weights_amd as moe
 import oracle
+import weight_layout as wl
 from gpu_helpers import DEV, bf16_from_u16, gemm_tolerance_check, require_gpu, u16
 
 pytestmark = pytest.mark.gpu
@@ -44,7 +45,7 @@ def _run_fp8(c, expected_m=0, D=None, packed=False, sfa_shift=0):
         buf = torch.zeros(SFA.numel() + sfa_shift, dtype=torch.float32, device=DEV)
         buf[sfa_shift:] = SFA.reshape(-1)
         SFA = buf[sfa_shift:].view(SFA.shape)
-    wbytes = oracle.pack_weight_fp8(c["w"]).reshape(c["w"].shape) if packed else c["w"]
+    wbytes = wl.pack_weight_fp8(c["w"]).reshape(c["w"].shape) if packed else c["w"]
     W = torch.from_numpy(np.ascontiguousarray(wbytes)).to(DEV)
     SFW = torch.from_numpy(c["sfw"]).to(DEV)
     if D is None:
@@ -169,7 +170,7 @@ def test_pack_weight_fp8_bit_exact():
     out = torch.full(q.shape, 0x5A, dtype=torch.uint8, device=DEV)
     moe.moe_pack_weight_fp8(torch.from_numpy(q).to(DEV), out)
     torch.cuda.synchronize()
-    assert np.array_equal(out.cpu().numpy().reshape(2, -1), oracle.pack_weight_fp8(q))
+    assert np.array_equal(out.cpu().numpy().reshape(2, -1), wl.pack_weight_fp8(q))
 
 
 def _int_codes(rng, shape, lo=-4, hi=4):
@@ -244,7 +245,7 @@ def _run_int4(c, expected_m=0, packed=False):
     A = bf16_from_u16(c["a"])
     wbytes, sbits = c["q4"], c["s16"]
     if packed:
-        wbytes, sbits = oracle.pack_weight_int4(c["q4"], c["s16"])
+        wbytes, sbits = wl.pack_weight_int4(c["q4"], c["s16"])
         wbytes, sbits = wbytes.reshape(c["q4"].shape), sbits.reshape(c["s16"].shape)
     W4 = torch.from_numpy(wbytes).to(DEV)
     S16 = torch.from_numpy(sbits.view(np.int16)).view(torch.float16).to(DEV)
@@ -325,7 +326,7 @@ def test_pack_weight_int4_bit_exact():
     moe.moe_pack_weight_int4(torch.from_numpy(q4).to(DEV), torch.from_numpy(s16.view(np.int16)).to(DEV).view(torch.float16),
                              qo, so)
     torch.cuda.synchronize()
-    wq, ws = oracle.pack_weight_int4(q4, s16)
+    wq, ws = wl.pack_weight_int4(q4, s16)
     assert np.array_equal(qo.cpu().numpy().reshape(2, -1), wq)
     assert np.array_equal(so.view(torch.int16).cpu().numpy().view(np.uint16).reshape(2, -1), ws)
 

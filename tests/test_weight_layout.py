@@ -1,17 +1,17 @@
-"""Pins of the oracle's fragment-packed weight order (a permutation of bytes)."""
+"""Pins of the test helper's fragment-packed weight orders (permutations of bytes)."""
 
 import numpy as np
 import pytest
 
-import oracle
+import weight_layout as wl
 
 
 @pytest.mark.parametrize("E,N,K", [(1, 128, 128), (2, 256, 384)])
 def test_pack_matches_scalar_offsets_everywhere(E, N, K):
     rng = np.random.default_rng(N + K)
     codes = rng.integers(0, 256, size=(E, N, K), dtype=np.uint8)
-    packed = oracle.pack_weight_fp8(codes)
-    offs = np.array([[oracle.packed_offset(n, k, N) for k in range(K)] for n in range(N)])
+    packed = wl.pack_weight_fp8(codes)
+    offs = np.array([[wl.packed_offset(n, k, N) for k in range(K)] for n in range(N)])
     # bijection onto [0, N*K)
     assert np.array_equal(np.sort(offs.reshape(-1)), np.arange(N * K))
     for e in range(E):
@@ -22,8 +22,8 @@ def test_unpack_inverts_pack_and_blocks_are_2kb_fragments():
     rng = np.random.default_rng(7)
     E, N, K = 1, 256, 256
     codes = rng.integers(0, 256, size=(E, N, K), dtype=np.uint8)
-    packed = oracle.pack_weight_fp8(codes)
-    assert np.array_equal(oracle.unpack_weight_fp8(packed, N, K), codes)
+    packed = wl.pack_weight_fp8(codes)
+    assert np.array_equal(wl.unpack_weight_fp8(packed, N, K), codes)
     # block (kb=1, cb=2): first 16 bytes are column 32, K 128..143; lane 17 is column 33, K 144..159
     base = (1 * (N // 16) + 2) * 2048
     assert np.array_equal(packed[0, base:base + 16], codes[0, 32, 128:144])
@@ -42,8 +42,8 @@ def test_int4_pack_matches_scalar_positions_everywhere(E, N, K):
     rng = np.random.default_rng(N * K)
     q4 = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
     s16 = rng.integers(0, 65536, size=(E, N, K // 128), dtype=np.uint16)
-    packed, sp = oracle.pack_weight_int4(q4, s16)
-    pos = np.array([[2 * o + h for o, h in (oracle.packed_nibble_int4(n, k, N),)] for n in range(N) for k in range(K)])
+    packed, sp = wl.pack_weight_int4(q4, s16)
+    pos = np.array([[2 * o + h for o, h in (wl.packed_nibble_int4(n, k, N),)] for n in range(N) for k in range(K)])
     assert np.array_equal(np.sort(pos.reshape(-1)), np.arange(N * K))  # a bijection onto the nibbles
     for e in range(E):
         flat = np.empty(N * K, np.uint8)
@@ -51,10 +51,10 @@ def test_int4_pack_matches_scalar_positions_everywhere(E, N, K):
         flat[1::2] = packed[e] >> 4
         want = np.array([_nib(q4[e], n, k) for n in range(N) for k in range(K)], np.uint8)
         assert np.array_equal(flat[pos.reshape(-1)], want)
-        soff = np.array([[oracle.packed_scale_offset_int4(n, g, N) for g in range(K // 128)] for n in range(N)])
+        soff = np.array([[wl.packed_scale_offset_int4(n, g, N) for g in range(K // 128)] for n in range(N)])
         assert np.array_equal(np.sort(soff.reshape(-1)), np.arange(N * K // 128))
         assert np.array_equal(sp[e][soff], s16[e])
-    assert np.array_equal(oracle.unpack_weight_int4(packed, N, K), q4)
+    assert np.array_equal(wl.unpack_weight_int4(packed, N, K), q4)
 
 
 def test_int4_dword_holds_natural_pairs_after_shift_and_mask():
@@ -63,7 +63,7 @@ def test_int4_dword_holds_natural_pairs_after_shift_and_mask():
     q = np.zeros((N, K), np.uint8)
     q[37, :] = np.arange(K) % 16
     q4 = (q[:, 0::2] | (q[:, 1::2] << 4))[None]
-    packed, _ = oracle.pack_weight_int4(q4, np.zeros((1, N, 2), np.uint16))
+    packed, _ = wl.pack_weight_int4(q4, np.zeros((1, N, 2), np.uint16))
     cb, c = divmod(37, 16)
     for h in range(4):
         for d in range(4):
@@ -74,4 +74,4 @@ def test_int4_dword_holds_natural_pairs_after_shift_and_mask():
                 lo, hi = (w >> (4 * i)) & 15, (w >> (4 * i + 16)) & 15
                 assert (lo, hi) == ((k0 + 2 * i) % 16, (k0 + 2 * i + 1) % 16)
     # scales: column 37 is in 64-column slice 0, c = 5, cb = 2
-    assert oracle.packed_scale_offset_int4(37, 1, N) == ((1 * 2 + 0) * 16 + 5) * 4 + 2
+    assert wl.packed_scale_offset_int4(37, 1, N) == ((1 * 2 + 0) * 16 + 5) * 4 + 2

@@ -1,4 +1,11 @@
-"""Fragment-packed orders of FP8 and 4-bit weight codes.  TEST INFRASTRUCTURE ONLY.
+"""Fragment-packed orders of FP8 and 4-bit weight codes: a test helper.
+
+These orders are the library's storage formats (moe_pack_weight_fp8 /
+moe_pack_weight_int4), not part of the method the oracle computes: the oracle
+always takes row-major weights.  The tests use this module to check the
+library's packers byte for byte and to feed the GEMMs packed weights in small
+cases; it is written from the layout definition in include/moe.h and imports
+nothing from the library.
 
 Weights are quantised once, offline, and may be stored in whatever order the
 kernel reads fastest: ONNX Runtime's MatMulNBits page describes prepacked
