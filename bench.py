@@ -9,9 +9,12 @@ GEMM in place of the FP8 one for the INT4 workload).
 
 Default workload: DeepSeek-V3-shaped prefill (T=4096 tokens, 256 experts,
 top-8, K=7168, N=4096, FP8 E4M3 with 1x128 / 128x128 power-of-two scales,
-contiguous 128-row-aligned layout).  Prints ONE JSON line.
+contiguous 128-row-aligned layout).  The other workloads (the Qwen3-shaped
+skewed prefill, whose up-projection is the MFMA-bound GEMM, the masked FP8
+decode and the 4-bit decode) are timed in the same run and reported under
+"workloads".  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME] [--cpu-baseline off]
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--also NAMES|none] [--cpu-baseline off]
 """
 
 from __future__ import annotations
@@ -20,13 +23,16 @@ import argparse
 import json
 import os
 import platform
+import statistics
 import sys
+import threading
 import time
 
 METRIC = "grouped-GEMM FP8 TFLOPS (prefill) & HBM GB/s (decode), % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+WORKLOADS = ["tiny", "dsv3_prefill", "dsv3_decode", "qwen3_skewed", "int4_decode"]
 
 
 def parse():
@@ -34,10 +40,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="dsv3_prefill",
-                    choices=["tiny", "dsv3_prefill", "dsv3_decode", "qwen3_skewed", "int4_decode"])
+    ap.add_argument("--config", default="dsv3_prefill", choices=WORKLOADS)
+    ap.add_argument("--also", default="qwen3_skewed,dsv3_decode,int4_decode",
+                    help="further workloads timed in the same run (comma-separated, or 'none')")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-experts", type=int, default=128, help="experts in the timed oracle sample")
+    ap.add_argument("--clock", choices=["on", "off"], default="on",
+                    help="sample the GPU clock over back-to-back steps after the timed ones")
     ap.add_argument("--expected-m", type=int, default=0,
                     help="tiling hint passed to the GEMM (default: routes per expert)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -61,33 +70,36 @@ def copy_calibration(mib):
           flush=True)
 
 
+# the files each kernel is built from (its HIP sources, the generator of its assembly, the build script)
 KERNEL_SOURCES = {
-    "moe_grouped_gemm_fp8": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h", "moe_internal.h"],
-    "moe_grouped_gemm_int4": ["gemm_int4.hip", "gemm_common.h", "moe_device.h", "moe_internal.h"],
+    "moe_grouped_gemm_fp8": ["csrc/gemm_fp8.hip", "csrc/gen_fp8_asm.py", "csrc/gemm_common.h", "csrc/moe_device.h",
+                             "csrc/moe_internal.h", "build.py"],
+    "moe_grouped_gemm_int4": ["csrc/gemm_int4.hip", "csrc/gemm_common.h", "csrc/moe_device.h", "csrc/moe_internal.h",
+                              "build.py"],
 }
 
 
 def sources_sha256(kernel):
-    """Hash of the HIP sources a kernel is built from (counter figures are valid only for these)."""
+    """Hash of the files a kernel is built from (counter figures are valid only for these)."""
     import hashlib
 
     h = hashlib.sha256()
-    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "int4_weights_amd", "csrc")
+    pkg = os.path.join(os.path.dirname(os.path.abspath(__file__)), "int4_weights_amd")
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, f), "rb") as fh:
+        with open(os.path.join(pkg, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, key):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, or None.
 
     profiles/traffic.json holds, per kernel and workload, the calibrated byte count and the hash of the
-    sources it was measured on; a kernel changed since then reports None."""
+    files it was measured on; a kernel changed since then reports None."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
     try:
         with open(path) as fh:
-            entry = json.load(fh).get(f"{kernel}/{workload}")
+            entry = json.load(fh).get(f"{kernel}/{key}")
     except (OSError, ValueError):
         return None
     if not entry or entry.get("sources_sha256") != sources_sha256(kernel):
@@ -157,11 +169,13 @@ class Timer:
     def mark(self, step, i):
         self.ev[step][i].record()
 
-    def mean_ms(self):
-        out = {}
-        for i, n in enumerate(self.names):
-            out[n] = sum(e[i].elapsed_time(e[i + 1]) for e in self.ev) / len(self.ev)
-        return out
+    def per_kernel(self):
+        """{name: [ms of each step]}"""
+        return {n: [e[i].elapsed_time(e[i + 1]) for e in self.ev] for i, n in enumerate(self.names)}
+
+
+def stats(xs):
+    return {"mean": sum(xs) / len(xs), "median": statistics.median(xs), "min": min(xs), "max": max(xs)}
 
 
 def spin_calibration(torch):
@@ -198,18 +212,29 @@ def fp8_weights(torch, moe, synth, cfg, N, K, stream_id, keep=()):
     return codes, sfw, kept
 
 
-def run(args):
-    import numpy as np
-    import torch
+def fp8_gemm_roofline(rows_valid, active, N, K, t_ms):
+    """Algorithmic flops and bytes of one FP8 grouped-GEMM launch and where they put it on the roofline."""
+    flops = 2.0 * rows_valid * N * K
+    nbytes = active * N * K + active * (N // 128) * (K // 128) * 4 + rows_valid * (K + 4 * K // 128) \
+        + rows_valid * N * 2
+    t = t_ms / 1e3
+    ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops / nbytes < ridge:
+        roof = {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["tflops"] = flops / t / 1e12
+    roof["hbm_gbs"] = nbytes / t / 1e9
+    roof["flops_per_launch"] = flops
+    roof["bytes_per_launch"] = nbytes
+    return roof
 
-    import int4_weights_amd as moe
-    import synth
+
+def build_workload(args, cfg, torch, np, moe, synth, want_cpu):
+    """Buffers, weights and the step function of one workload (set-up, untimed)."""
     from int4_weights_amd.layer import MoeFP8Layer, MoeInt4Layer
 
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
-    moe.load()
-    cfg = synth.config_by_name(args.config)
     dev = "cuda"
     T, E, k, K, N = cfg.T, cfg.E, cfg.topk, cfg.K, cfg.N
     R = T * k
@@ -217,20 +242,29 @@ def run(args):
     ids, tw = ids_cpu.to(dev), tw_cpu.to(dev)
     x = synth.activations(cfg, T, K).to(dev)
     counts_np = np.bincount(ids_cpu.flatten().numpy(), minlength=E)
-    sample = [int(e) for e in np.argsort(-counts_np, kind="stable")[: args.cpu_experts]] if args.cpu_baseline == "on" else []
-    log(f"[bench] workload {cfg.name}: T={T} E={E} top-{k} K={K} N={N} ({cfg.layout}, {cfg.weights})")
-
-    t_setup = time.perf_counter()
-    names = ["moe_quant_act", "moe_route_pack", "gemm", "moe_unpermute_combine"]
-    extra = {}
+    sample = [int(e) for e in np.argsort(-counts_np, kind="stable")[: args.cpu_experts]] if want_cpu else []
+    w = {"cfg": cfg, "ids_cpu": ids_cpu, "tw_cpu": tw_cpu, "x": x, "sample": sample}
     if cfg.weights == "fp8":
         codes, sfw, kept = fp8_weights(torch, moe, synth, cfg, N, K, synth.STREAM_WEIGHTS, keep=set(sample))
         layout = moe.LAYOUT_MASKED if cfg.layout == "masked" else moe.LAYOUT_CONTIGUOUS
         am = cfg.max_m if cfg.layout == "masked" else cfg.align
         em = args.expected_m or max(1, R // E)
         layer = MoeFP8Layer(codes, sfw, k, T, layout, am, expected_m=em, weights_packed=True)
-        down = None
-        if cfg.K_down:
+        w["kept"] = kept
+        if not cfg.K_down:
+            names = ["moe_quant_act", "moe_route_pack", "gemm", "moe_unpermute_combine"]
+
+            def step(tm, s):
+                tm.mark(s, 0)
+                layer.quant(x)
+                tm.mark(s, 1)
+                layer.route(ids)
+                tm.mark(s, 2)
+                layer.gemm()
+                tm.mark(s, 3)
+                layer.combine(tw)
+                tm.mark(s, 4)
+        else:
             names = ["moe_quant_act", "moe_route_pack", "gemm", "moe_quant_act_down", "gemm_down",
                      "moe_unpermute_combine"]
             dcodes, dsfw, _ = fp8_weights(torch, moe, synth, cfg, cfg.N_down, cfg.K_down, synth.STREAM_WEIGHTS_DOWN)
@@ -239,21 +273,15 @@ def run(args):
             sfd = torch.empty(layer.rows_cap, cfg.K_down // 128, dtype=torch.float32, device=dev)
             Dd = torch.empty(layer.rows_cap, cfg.N_down, dtype=torch.bfloat16, device=dev)
             Zd = torch.empty(T, cfg.N_down, dtype=torch.bfloat16, device=dev)
-            down = (dcodes, dsfw, a_down, qd, sfd, Dd, Zd)
 
-        def step(tm, s):
-            tm.mark(s, 0)
-            layer.quant(x)
-            tm.mark(s, 1)
-            layer.route(ids)
-            tm.mark(s, 2)
-            layer.gemm()
-            tm.mark(s, 3)
-            if down is None:
-                layer.combine(tw)
-                tm.mark(s, 4)
-            else:
-                dcodes, dsfw, a_down, qd, sfd, Dd, Zd = down
+            def step(tm, s):
+                tm.mark(s, 0)
+                layer.quant(x)
+                tm.mark(s, 1)
+                layer.route(ids)
+                tm.mark(s, 2)
+                layer.gemm()
+                tm.mark(s, 3)
                 moe.moe_quant_act(a_down, qd, sfd)
                 tm.mark(s, 4)
                 layer.gemm(A=qd, SFA=sfd, D=Dd, w=dcodes, sfw=dsfw, N=cfg.N_down, K=cfg.K_down)
@@ -267,18 +295,22 @@ def run(args):
         all_q4 = torch.empty(ncopy, E, N, K // 2, dtype=torch.uint8, device=dev)
         all_s16 = torch.empty(ncopy, E, N, K // 128, dtype=torch.float16, device=dev)
         copies = []
+        kept = {}
         for c in range(ncopy):
-            w = synth.expert_weights(cfg, N, K, device=dev, seed=0)
+            wb = synth.expert_weights(cfg, N, K, device=dev, seed=0)
+            if c == 0:
+                kept = {e: wb[e].cpu() for e in sample}
             q4 = torch.empty(E, N, K // 2, dtype=torch.uint8, device=dev)
             s16 = torch.empty(E, N, K // 128, dtype=torch.float16, device=dev)
-            moe.moe_quant_weight_int4(w, q4, s16)
-            del w
+            moe.moe_quant_weight_int4(wb, q4, s16)
+            del wb
             moe.moe_pack_weight_int4(q4, s16, all_q4[c], all_s16[c])
             del q4, s16
             copies.append((all_q4[c], all_s16[c]))
         layer = MoeInt4Layer(copies[0][0], copies[0][1], k, T, moe.LAYOUT_MASKED, cfg.max_m,
                              expected_m=args.expected_m or max(1, R // E), weights_packed=True)
         names = ["moe_route_pack", "gemm", "moe_unpermute_combine"]
+        w["kept"] = kept
 
         def step(tm, s):
             q4, s16 = copies[s % ncopy]
@@ -289,25 +321,23 @@ def run(args):
             tm.mark(s, 2)
             layer.combine(tw)
             tm.mark(s, 3)
-
     torch.cuda.synchronize()
-    log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s; warmup {args.warmup} steps")
+    w.update(layer=layer, names=names, step=step)
+    return w
+
+
+def time_workload(args, torch, wl, cycles_per_ms):
+    """Warm-up, then exactly args.steps timed steps back to back; per-kernel event times of every step."""
+    names, step = wl["names"], wl["step"]
     wt = Timer(torch, names, max(args.warmup, 1))
     for s in range(args.warmup):
         step(wt, s)
     torch.cuda.synchronize()
-
-    # algorithmic work from the routing the device produced (read outside the timed region)
-    counts = layer.counts.cpu().numpy().astype(np.int64)
-    rows_valid = int(counts.sum())
-    active = int((counts > 0).sum())
-
     # Launches go through Python, which for the decode workloads takes longer
     # than the kernels themselves.  A spin kernel holds the stream while every
     # timed launch is enqueued, so the K steps then run back to back on the GPU
     # (as from a graph or a native serving loop) and the events see kernel time,
     # not host gaps.  The spin kernel itself lies before the start event.
-    cycles_per_ms = spin_calibration(torch)
     tm = Timer(torch, names, args.steps)
     start, end = HipEvent(torch), HipEvent(torch)
     t_host = time.perf_counter()
@@ -321,97 +351,190 @@ def run(args):
         step(tm, s)
     end.record()
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
-    kern = tm.mean_ms()
-    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; " + ", ".join(f"{n} {v:.3f} ms" for n, v in kern.items()))
+    return start.elapsed_time(end) / args.steps, tm.per_kernel(), host_ms
 
+
+def clock_pass(torch, wl, seconds=0.6):
+    """GPU clock (MHz) sampled every 5 ms by the SMI library while steps run back to back."""
+    samples, stop = [], threading.Event()
+    try:
+        torch.cuda.clock_rate()
+    except Exception as e:  # no SMI access on this machine
+        return {"error": f"clock not readable: {type(e).__name__}"}
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                samples.append(float(torch.cuda.clock_rate()))
+            except Exception:
+                pass
+            time.sleep(0.005)
+
+    tm = Timer(torch, wl["names"], 1)
+    th = threading.Thread(target=sampler, daemon=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        wl["step"](tm, 0)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()  # keep the host at most a few steps ahead
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    busy = samples[2:] if len(samples) > 4 else samples
+    if not busy:
+        return {"error": "no samples"}
+    return {"median_mhz": statistics.median(busy), "min_mhz": min(busy), "max_mhz": max(busy),
+            "samples": len(busy), "steps": n,
+            "source": "torch.cuda.clock_rate() (SMI current GFX clock) every 5 ms over back-to-back steps"}
+
+
+def summarise(args, np, wl, ms_step, per, host_ms, clock):
+    """The result dict of one workload (value, rooflines, per-kernel statistics)."""
+    cfg, layer = wl["cfg"], wl["layer"]
+    T, E, k, K, N = cfg.T, cfg.E, cfg.topk, cfg.K, cfg.N
+    counts = layer.counts.cpu().numpy().astype(np.int64)
+    rows_valid = int(counts.sum())
+    active = int((counts > 0).sum())
+    kern = {n: stats(v) for n, v in per.items()}
+    out = {"ms_per_step": ms_step, "kernels_ms": kern}
     if cfg.weights == "fp8":
-        flops = 2.0 * rows_valid * N * K
-        gemm_bytes = active * N * K + active * (N // 128) * (K // 128) * 4 + rows_valid * (K + 4 * K // 128) \
-            + rows_valid * N * 2
+        roof = fp8_gemm_roofline(rows_valid, active, N, K, kern["gemm"]["mean"])
+        flops = roof["flops_per_launch"]
         if cfg.K_down:
-            flops += 2.0 * rows_valid * cfg.N_down * cfg.K_down
-        t_gemm = kern["gemm"] / 1e3
-        gemm_flops = 2.0 * rows_valid * N * K
-        ai = gemm_flops / gemm_bytes
-        ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-        if ai < ridge:
-            roof = {"bound": "hbm", "achieved": gemm_bytes / t_gemm / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-        else:
-            roof = {"bound": "mfma", "achieved": gemm_flops / t_gemm / 1e12, "peak": FP8_PEAK_TFLOPS,
-                    "unit": "TFLOP/s"}
-        extra["gemm_tflops"] = gemm_flops / t_gemm / 1e12
-        extra["gemm_hbm_gbs"] = gemm_bytes / t_gemm / 1e9
-        extra["gemm_bytes_per_launch"] = gemm_bytes
-        extra["gemm_flops_per_launch"] = gemm_flops
+            rd = fp8_gemm_roofline(rows_valid, active, cfg.N_down, cfg.K_down, kern["gemm_down"]["mean"])
+            rd.update(kernel="moe_grouped_gemm_fp8", avg_launch_ms=kern["gemm_down"]["mean"],
+                      median_launch_ms=kern["gemm_down"]["median"], min_launch_ms=kern["gemm_down"]["min"],
+                      traffic=measured_traffic("moe_grouped_gemm_fp8", cfg.name + "_down"))
+            out["roofline_down"] = rd
+            flops += rd["flops_per_launch"]
         if cfg.layout == "masked":
-            value, unit = gemm_bytes / (ms_step / 1e3) / 1e9, "GB/s"
+            value, unit = roof["bytes_per_launch"] / (ms_step / 1e3) / 1e9, "GB/s"
         else:
             value, unit = flops / (ms_step / 1e3) / 1e12, "TFLOP/s"
         dtype = "fp8_e4m3"
+        kernel = "moe_grouped_gemm_fp8"
     else:
-        gemm_bytes = active * N * (K // 2) + active * N * (K // 128) * 2 + rows_valid * K * 2 + rows_valid * N * 2
-        flops = 2.0 * rows_valid * N * K
-        t_gemm = kern["gemm"] / 1e3
-        roof = {"bound": "hbm", "achieved": gemm_bytes / t_gemm / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-        extra["gemm_hbm_gbs"] = gemm_bytes / t_gemm / 1e9
-        extra["gemm_bytes_per_launch"] = gemm_bytes
-        value, unit = gemm_bytes / (ms_step / 1e3) / 1e9, "GB/s"
+        nbytes = active * N * (K // 2) + active * N * (K // 128) * 2 + rows_valid * K * 2 + rows_valid * N * 2
+        t = kern["gemm"]["mean"] / 1e3
+        roof = {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": nbytes / t / 1e9 / HBM_PEAK_GBS, "hbm_gbs": nbytes / t / 1e9, "bytes_per_launch": nbytes,
+                "flops_per_launch": 2.0 * rows_valid * N * K}
+        value, unit = nbytes / (ms_step / 1e3) / 1e9, "GB/s"
         dtype = "int4xbf16"
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "moe_grouped_gemm_fp8" if cfg.weights == "fp8" else "moe_grouped_gemm_int4"
-    roof["traffic"] = measured_traffic(roof["kernel"], cfg.name)
-    roof["avg_launch_ms"] = kern["gemm"]
+        kernel = "moe_grouped_gemm_int4"
+    roof.update(kernel=kernel, avg_launch_ms=kern["gemm"]["mean"], median_launch_ms=kern["gemm"]["median"],
+                min_launch_ms=kern["gemm"]["min"], traffic=measured_traffic(kernel, cfg.name))
+    out.update(value=value, unit=unit, dtype=dtype, roofline=roof,
+               config={"workload": cfg.name, "T": T, "E": E, "topk": k, "K": K, "N": N, "layout": cfg.layout,
+                       "weights": cfg.weights, "routing": cfg.routing, "rows_valid": rows_valid,
+                       "experts_active": active, "K_down": cfg.K_down or None, "N_down": cfg.N_down or None},
+               clock=clock, host_enqueue_ms_per_step=host_ms)
+    return out
 
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import int4_weights_amd as moe
+    import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    moe.load()
+    also = [] if args.also in ("", "none") else [a for a in args.also.split(",") if a and a != args.config]
+    for a in also:
+        if a not in WORKLOADS:
+            raise SystemExit(f"unknown workload {a}")
+    cycles_per_ms = spin_calibration(torch)
+    results = {}
     cpu = None
-    if args.cpu_baseline == "on" and cfg.weights == "fp8":
-        cpu = cpu_baseline(np, torch, synth, cfg, ids_cpu, tw_cpu, x, kept, sample)
+    for i, name in enumerate([args.config] + also):
+        cfg = synth.config_by_name(name)
+        primary = i == 0
+        log(f"[bench] workload {cfg.name}: T={cfg.T} E={cfg.E} top-{cfg.topk} K={cfg.K} N={cfg.N} "
+            f"({cfg.layout}, {cfg.weights})")
+        t_setup = time.perf_counter()
+        wl = build_workload(args, cfg, torch, np, moe, synth, primary and args.cpu_baseline == "on")
+        log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s; warmup {args.warmup}, timed {args.steps} steps")
+        ms_step, per, host_ms = time_workload(args, torch, wl, cycles_per_ms)
+        clock = clock_pass(torch, wl) if args.clock == "on" else None
+        res = summarise(args, np, wl, ms_step, per, host_ms, clock)
+        log(f"[bench] {name}: {ms_step:.3f} ms/step; " +
+            ", ".join(f"{n} {v['median']:.3f} ms" for n, v in res["kernels_ms"].items()) +
+            (f"; clock {clock.get('median_mhz')} MHz" if clock else ""))
+        if primary and args.cpu_baseline == "on":
+            cpu = cpu_baseline(np, torch, wl)
+            log(f"[bench] oracle on the host: {cpu['value']:.4f} {cpu['unit']} ({cpu['seconds']:.1f} s)")
+        results[name] = res
+        del wl
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
 
+    p = results[args.config]
     out = {
         "metric": METRIC,
-        "value": value,
-        "unit": unit,
+        "value": p["value"],
+        "unit": p["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": p["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": p["dtype"],
         "data": "synthetic: seeded router logits/activations/weights with the workload's shapes and distributions",
-        "config": {"workload": cfg.name, "T": T, "E": E, "topk": k, "K": K, "N": N, "layout": cfg.layout,
-                   "weights": cfg.weights, "routing": cfg.routing, "rows_valid": rows_valid,
-                   "experts_active": active, "K_down": cfg.K_down or None, "N_down": cfg.N_down or None},
-        "roofline": roof,
+        "config": p["config"],
+        "roofline": p["roofline"],
         "cpu_baseline": cpu,
-        "kernels_ms": kern,
-        **extra,
+        "kernels_ms": p["kernels_ms"],
+        "clock": p["clock"],
     }
+    if "roofline_down" in p:
+        out["roofline_down"] = p["roofline_down"]
+    out["workloads"] = {n: {kk: v for kk, v in r.items()} for n, r in results.items() if n != args.config}
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(np, torch, synth, cfg, ids_cpu, tw_cpu, x_dev, kept, sample):
-    """The oracle timed on the host: the whole step restricted to a few experts."""
+def cpu_baseline(np, torch, wl):
+    """The oracle timed on the host: the whole step restricted to the most-loaded experts."""
     import oracle
     from threadpoolctl import threadpool_info
 
+    cfg, ids_cpu, tw_cpu, kept, sample = wl["cfg"], wl["ids_cpu"], wl["tw_cpu"], wl["kept"], wl["sample"]
     E, K, N = cfg.E, cfg.K, cfg.N
     ids = ids_cpu.numpy()
-    xb = x_dev.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    xb = wl["x"].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    bits = {e: kept[e][None].contiguous().view(torch.int16).numpy().view(np.uint16) for e in sample}
     # weights of the sample experts, quantised by the oracle (preparation, not timed)
-    wq = {e: oracle.quant_weight_fp8(kept[e][None].contiguous().view(torch.int16).numpy().view(np.uint16))
-          for e in sample}
+    if cfg.weights == "fp8":
+        wq = {e: oracle.quant_weight_fp8(bits[e]) for e in sample}
+    else:
+        wq = {e: oracle.quant_weight_int4(bits[e]) for e in sample}
+    layout = "masked" if cfg.layout == "masked" else "contiguous"
+    kw = {"max_m": cfg.max_m} if layout == "masked" else {"align": cfg.align}
     t0 = time.perf_counter()
-    r = oracle.route(ids, E, "contiguous", align=cfg.align)
+    r = oracle.route(ids, E, layout, **kw)
     tok_rows = {e: np.nonzero((ids == e).any(axis=1))[0] for e in sample}
     ys = {}
     flops = 0.0
+    nbytes = 0.0
     for e in sample:
         rows = tok_rows[e]
-        a, sa = oracle.quant_act(xb[rows])
-        wc, sw = wq[e]
-        y = oracle.grouped_gemm_fp8(a, sa, wc, sw, np.array([len(rows)]), np.array([0, len(rows)]))
+        if cfg.weights == "fp8":
+            a, sa = oracle.quant_act(xb[rows])
+            wc, sw = wq[e]
+            y = oracle.grouped_gemm_fp8(a, sa, wc, sw, np.array([len(rows)]), np.array([0, len(rows)]))
+            nbytes += N * K + len(rows) * (K + N * 2)
+        else:
+            q4, s4 = wq[e]
+            y = oracle.grouped_gemm_int4(xb[rows], q4, s4, np.array([len(rows)]), np.array([0, len(rows)]))
+            nbytes += N * K // 2 + N * (K // 128) * 2 + len(rows) * (2 * K + 2 * N)
         ys[e] = (rows, y)
         flops += 2.0 * len(rows) * N * K
     # weighted combine of the sample experts' rows into their tokens
@@ -424,11 +547,18 @@ def cpu_baseline(np, torch, synth, cfg, ids_cpu, tw_cpu, x_dev, kept, sample):
                     z[t] = z.get(t, 0.0) + float(tw_cpu[t, s]) * y[j]
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": dt, "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count(),
-            "sample": f"{len(sample)} of {E} experts (the most loaded: {int(sum(len(ys[e][0]) for e in sample))} "
-                      f"routed rows), full K={K} and N={N}: oracle routing of all {cfg.T * cfg.topk} routes, "
-                      f"quantisation of the sample rows, fp64 grouped GEMM, weighted combine"}
+    nrows = int(sum(len(ys[e][0]) for e in sample))
+    desc = (f"{len(sample)} of {E} experts (the most loaded: {nrows} routed rows), full K={K} and N={N}: oracle "
+            f"routing of all {cfg.T * cfg.topk} routes, " +
+            ("quantisation of the sample rows, fp64 grouped GEMM" if cfg.weights == "fp8"
+             else "fp64 4-bit weight-only grouped GEMM (dequantised weights)") + ", weighted combine")
+    if cfg.layout == "masked" or cfg.weights == "int4":
+        value, unit = nbytes / dt / 1e9, "GB/s"
+    else:
+        value, unit = flops / dt / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle", "seconds": dt,
+            "tflops": flops / dt / 1e12, "cpu": platform.processor() or platform.machine(),
+            "host_cpus": os.cpu_count(), "sample": desc}
 
 
 def main():

@@ -247,8 +247,8 @@ moe_status moe_grouped_gemm_fp8(int layout,
  *     A   [rows, K] bf16,  W4 [E, N, K/2] (low nibble = even k),
  *     S16 [E, N, K/128] fp16,  D [rows, N] bf16.
  *   Layout, counts, seg_offsets, expected_m and alignment as for
- *   moe_grouped_gemm_fp8; layout | MOE_WEIGHTS_PACKED: W4 and S16 in the orders
- *   written by moe_pack_weight_int4. */
+ *   moe_grouped_gemm_fp8 (S16 2-byte aligned); layout | MOE_WEIGHTS_PACKED: W4
+ *   and S16 in the orders written by moe_pack_weight_int4, S16 8-byte aligned. */
 moe_status moe_grouped_gemm_int4(int layout,
                                  const uint16_t* A, const uint8_t* W4,
                                  const uint16_t* S16, uint16_t* D,

@@ -283,6 +283,9 @@ moe_status moe_grouped_gemm_int4(int layout, const uint16_t* A, const uint8_t* W
                              rows_cap_or_max_m, N, K);
   if (st) return st;
   if (!aligned(S16, 2)) return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_int4: scales misaligned");
+  // the packed kernel reads one lane's 4 scales of a group as one 8-byte load
+  if (wpacked && !aligned(S16, 8))
+    return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_int4: packed scales must be 8-byte aligned");
   GemmArgs a;
   a.A = (const uint8_t*)A;
   a.SFA = nullptr;

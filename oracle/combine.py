@@ -3,7 +3,8 @@
 [GEMM-modes] sec. 4.4 and 4.6: z_t = sum_r p[t, r] * y_packed[output_index[t, r]],
 reading only rows named by output_index (padding rows have none).  [CuTeDSL]:
 the combine accumulates the gathered rows in registers.  Slots whose
-output_index is -1 (dropped or invalid routes) contribute nothing.
+output_index is -1 (dropped or invalid routes), or names no row of y,
+contribute nothing.
 Weights are used as given (no renormalisation).
 
 Two forms:
@@ -34,7 +35,7 @@ def combine(y: np.ndarray, output_index: np.ndarray, topk_weights: np.ndarray) -
     for t in range(T):
         for r in range(k):
             p = int(output_index[t, r])
-            if p < 0:
+            if p < 0 or p >= y.shape[0]:
                 continue
             z[t] += float(topk_weights[t, r]) * y[p]
     return z

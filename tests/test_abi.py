@@ -127,6 +127,12 @@ def test_host_validation_rejects_without_launching(lib):
     assert p4(q=0, sc=0, E=0, qo=0, so=0) == MOE_OK
     assert lib.moe_grouped_gemm_int4(0, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), 4, 64, 100, 256, 0,
                                      None) == MOE_ERR_UNSUPPORTED
+    # packed 4-bit scales are read 8 bytes at a time: a 4-byte aligned S16 is refused with packed weights only
+    # (a valid call would launch, so the accepted case is checked as not refused for alignment on the GPU)
+    assert lib.moe_grouped_gemm_int4(0x10 | 1, _p(A16), _p(A16), _p(A16 + 4), _p(A16), _p(A16), _p(A16), 4, 64, 128,
+                                     256, 0, None) == MOE_ERR_ALIGN
+    assert lib.moe_grouped_gemm_int4(1, _p(A16), _p(A16), _p(A16 + 3), _p(A16), _p(A16), _p(A16), 4, 64, 128,
+                                     256, 0, None) == MOE_ERR_ALIGN
     # moe_unpermute_combine
     assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 2, 12, _p(A16), None) == MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 0, 16, _p(A16), None) == MOE_ERR_SHAPE
