@@ -206,6 +206,30 @@ moe_status moe_route_pack(const int32_t* topk_ids, int T, int k, int E,
                           void* workspace, int64_t workspace_bytes,
                           void* stream);
 
+/* moe_route_pack_noalloc: moe_route_pack for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, results and errors, minus the
+ * workspace.  The scratch the large-T*k path needs lives in one fixed device
+ * array inside the library, moe_route_pack_noalloc_max_bytes() bytes (4 MiB)
+ * per device, held until the process ends; calls whose
+ * moe_route_pack_workspace_bytes(T, k, E) exceeds it fail with
+ * MOE_ERR_WORKSPACE before anything is launched (4 MiB covers, e.g., 1M
+ * routes over 1024 experts or 8M routes over 128).  The call allocates
+ * nothing: no hipMalloc, no hipFree, no allocating library routine.  Every
+ * call on one device shares that device's array, so calls that overlap in
+ * time on one device (different streams, or different host threads) race and
+ * must be serialised by the caller; calls on different devices do not
+ * interact.  Nothing in the array needs clearing between calls. */
+int64_t moe_route_pack_noalloc_max_bytes(void);
+moe_status moe_route_pack_noalloc(const int32_t* topk_ids, int T, int k, int E,
+                                  int layout, int align_or_max_m,
+                                  const void* payload, int64_t payload_row_bytes,
+                                  const void* payload2, int64_t payload2_row_bytes,
+                                  void* packed, void* packed2, int64_t rows_cap,
+                                  int32_t* counts, int32_t* seg_offsets,
+                                  int32_t* m_indices, int32_t* output_index,
+                                  int32_t* dev_status, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* moe_grouped_gemm_fp8: block-scaled FP8 grouped GEMM, "NT" (both operands
  * K-contiguous).  (rainlin, "GEMM 执行方式", sec. 4.1/4.4: Y_e = X_e W_e^T per

@@ -25,6 +25,8 @@ from ._lib import (  # noqa: F401
     moe_quant_weight_fp8,
     moe_quant_weight_int4,
     moe_route_pack,
+    moe_route_pack_noalloc,
+    moe_route_pack_noalloc_max_bytes,
     moe_route_pack_workspace_bytes,
     moe_unpermute_combine,
 )

@@ -40,6 +40,10 @@ SIGNATURES = {
     "moe_route_pack": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_i64,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "moe_route_pack_noalloc_max_bytes": (_c_i64, []),
+    "moe_route_pack_noalloc": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_i64,
+                                        _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_fp8": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_grouped_gemm_int4": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -196,6 +200,39 @@ def moe_route_pack(topk_ids, E: int, layout: int, align_or_max_m: int, payload, 
                                  _ptr(payload), rb, _ptr(payload2), rb2, _ptr(packed), _ptr(packed2), rows_cap,
                                  _ptr(counts), _ptr(seg_offsets), _ptr(m_indices), _ptr(output_index),
                                  _ptr(dev_status), _ptr(workspace), ws_bytes, _stream(stream)), "moe_route_pack")
+
+
+def moe_route_pack_noalloc_max_bytes() -> int:
+    return int(load().moe_route_pack_noalloc_max_bytes())
+
+
+def moe_route_pack_noalloc(topk_ids, E: int, layout: int, align_or_max_m: int, payload, packed, counts, seg_offsets,
+                           m_indices, output_index, dev_status, payload2=None, packed2=None, stream=None):
+    """moe_route_pack without a workspace (the library's fixed device scratch; see include/moe.h)."""
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    for n, t in (("payload", payload), ("packed", packed), ("payload2", payload2), ("packed2", packed2)):
+        _dev(t, n)
+    for n, t in (("counts", counts), ("seg_offsets", seg_offsets), ("m_indices", m_indices),
+                 ("output_index", output_index), ("dev_status", dev_status)):
+        _dev(t, n, torch.int32)
+    T, k = topk_ids.shape
+    rb = _row_bytes(payload)
+    rows_cap = packed.shape[0]
+    if _row_bytes(packed) != rb:
+        raise ValueError("moe_route_pack_noalloc: payload and packed rows differ in size")
+    rb2 = 0
+    if payload2 is not None:
+        rb2 = _row_bytes(payload2)
+        if packed2 is None or packed2.shape[0] != rows_cap or _row_bytes(packed2) != rb2:
+            raise ValueError("moe_route_pack_noalloc: payload2/packed2 mismatch")
+    if m_indices.numel() < rows_cap or counts.numel() < E or seg_offsets.numel() < E + 1 or \
+            output_index.numel() < T * k:
+        raise ValueError("moe_route_pack_noalloc: output arrays too small")
+    _check(load().moe_route_pack_noalloc(_ptr(topk_ids), T, k, E, layout, align_or_max_m,
+                                         _ptr(payload), rb, _ptr(payload2), rb2, _ptr(packed), _ptr(packed2),
+                                         rows_cap, _ptr(counts), _ptr(seg_offsets), _ptr(m_indices),
+                                         _ptr(output_index), _ptr(dev_status), _stream(stream)),
+           "moe_route_pack_noalloc")
 
 
 def _gemm_sizes(fn, layout, E, rows_cap_or_max_m, counts, seg_offsets, sizes):

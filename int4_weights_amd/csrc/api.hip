@@ -155,53 +155,49 @@ moe_status moe_quant_weight_int4(const uint16_t* w, int E, int N, int K, uint8_t
   return hip_status(launch_quant_weight_int4(w, E, N, K, q4, s16, (hipStream_t)stream), "moe_quant_weight_int4");
 }
 
-moe_status moe_route_pack(const int32_t* topk_ids, int T, int k, int E, int layout, int align_or_max_m,
-                          const void* payload, int64_t payload_row_bytes, const void* payload2,
-                          int64_t payload2_row_bytes, void* packed, void* packed2, int64_t rows_cap, int32_t* counts,
-                          int32_t* seg_offsets, int32_t* m_indices, int32_t* output_index, int32_t* dev_status,
-                          void* workspace, int64_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+// Validation shared by moe_route_pack and moe_route_pack_noalloc; fills `a` (workspace left unset).
+static moe_status check_route(const char* fn, const int32_t* topk_ids, int T, int k, int E, int layout,
+                              int align_or_max_m, const void* payload, int64_t payload_row_bytes,
+                              const void* payload2, int64_t payload2_row_bytes, void* packed, void* packed2,
+                              int64_t rows_cap, int32_t* counts, int32_t* seg_offsets, int32_t* m_indices,
+                              int32_t* output_index, int32_t* dev_status, RouteArgs& a) {
   if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS)
-    return fail(MOE_ERR_SHAPE, "moe_route_pack: T=%d k=%d E=%d (need T>=0, 1<=k<=%d, 1<=E<=%d)", T, k, E,
-                MOE_MAX_TOPK, MOE_MAX_EXPERTS);
-  if ((int64_t)T * k > 0x7fffffff) return fail(MOE_ERR_SHAPE, "moe_route_pack: T*k too large");
+    return fail(MOE_ERR_SHAPE, "%s: T=%d k=%d E=%d (need T>=0, 1<=k<=%d, 1<=E<=%d)", fn, T, k, E, MOE_MAX_TOPK,
+                MOE_MAX_EXPERTS);
+  if ((int64_t)T * k > 0x7fffffff) return fail(MOE_ERR_SHAPE, "%s: T*k too large", fn);
   if (layout != MOE_LAYOUT_CONTIGUOUS && layout != MOE_LAYOUT_MASKED)
-    return fail(MOE_ERR_SHAPE, "moe_route_pack: unknown layout %d", layout);
-  if (align_or_max_m < 1) return fail(MOE_ERR_SHAPE, "moe_route_pack: align/max_m=%d must be >= 1", align_or_max_m);
+    return fail(MOE_ERR_SHAPE, "%s: unknown layout %d", fn, layout);
+  if (align_or_max_m < 1) return fail(MOE_ERR_SHAPE, "%s: align/max_m=%d must be >= 1", fn, align_or_max_m);
   if (payload_row_bytes <= 0 || payload_row_bytes % 4)
-    return fail(MOE_ERR_ALIGN, "moe_route_pack: payload_row_bytes=%lld must be a positive multiple of 4",
+    return fail(MOE_ERR_ALIGN, "%s: payload_row_bytes=%lld must be a positive multiple of 4", fn,
                 (long long)payload_row_bytes);
   if (payload2 && (payload2_row_bytes <= 0 || payload2_row_bytes % 4))
-    return fail(MOE_ERR_ALIGN, "moe_route_pack: payload2_row_bytes=%lld must be a positive multiple of 4",
+    return fail(MOE_ERR_ALIGN, "%s: payload2_row_bytes=%lld must be a positive multiple of 4", fn,
                 (long long)payload2_row_bytes);
   const bool any_routes = T > 0;
   if (any_routes && (!topk_ids || !payload || !output_index))
-    return fail(MOE_ERR_NULL, "moe_route_pack: topk_ids, payload and output_index are required when T > 0");
-  if (!counts || !seg_offsets || !dev_status) return fail(MOE_ERR_NULL, "moe_route_pack: null pointer");
+    return fail(MOE_ERR_NULL, "%s: topk_ids, payload and output_index are required when T > 0", fn);
+  if (!counts || !seg_offsets || !dev_status) return fail(MOE_ERR_NULL, "%s: null pointer", fn);
   if (rows_cap > 0 && (!packed || !m_indices))
-    return fail(MOE_ERR_NULL, "moe_route_pack: packed and m_indices are required when rows_cap > 0");
-  if (payload2 && !packed2) return fail(MOE_ERR_NULL, "moe_route_pack: packed2 is null but payload2 is not");
+    return fail(MOE_ERR_NULL, "%s: packed and m_indices are required when rows_cap > 0", fn);
+  if (payload2 && !packed2) return fail(MOE_ERR_NULL, "%s: packed2 is null but payload2 is not", fn);
   const int64_t need = (layout == MOE_LAYOUT_CONTIGUOUS) ? moe_packed_rows_cap(T, k, E, align_or_max_m)
                                                           : (int64_t)E * align_or_max_m;
   if (rows_cap < need || rows_cap > 0x7fffffff)
-    return fail(MOE_ERR_SHAPE, "moe_route_pack: rows_cap=%lld, need at least %lld (and < 2^31)",
-                (long long)rows_cap, (long long)need);
+    return fail(MOE_ERR_SHAPE, "%s: rows_cap=%lld, need at least %lld (and < 2^31)", fn, (long long)rows_cap,
+                (long long)need);
   if (!aligned(payload, 16) || !aligned(packed, 16) || (payload2 && (!aligned(payload2, 4) || !aligned(packed2, 4))))
-    return fail(MOE_ERR_ALIGN, "moe_route_pack: payload/packed must be 16-byte aligned, payload2/packed2 4-byte");
+    return fail(MOE_ERR_ALIGN, "%s: payload/packed must be 16-byte aligned, payload2/packed2 4-byte", fn);
   if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(seg_offsets, 4) || !aligned(m_indices, 4) ||
       !aligned(output_index, 4) || !aligned(dev_status, 4))
-    return fail(MOE_ERR_ALIGN, "moe_route_pack: int32 arrays must be 4-byte aligned");
-  const int R = T * k;
-  const int64_t ws_need = route_workspace_bytes(R, E);
-  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need || !aligned(workspace, 4)))
-    return fail(MOE_ERR_WORKSPACE, "moe_route_pack: needs %lld workspace bytes, got %lld", (long long)ws_need,
-                (long long)workspace_bytes);
-  RouteArgs a;
+    return fail(MOE_ERR_ALIGN, "%s: int32 arrays must be 4-byte aligned", fn);
   a.ids = topk_ids;
   a.T = T;
   a.k = k;
   a.E = E;
-  a.R = R;
+  a.R = T * k;
   a.masked = layout == MOE_LAYOUT_MASKED;
   a.align = a.masked ? 1 : align_or_max_m;
   a.max_m = a.masked ? align_or_max_m : 0;
@@ -217,9 +213,58 @@ moe_status moe_route_pack(const int32_t* topk_ids, int T, int k, int E, int layo
   a.m_indices = m_indices;
   a.output_index = output_index;
   a.dev_status = dev_status;
-  a.ws = (int32_t*)workspace;
+  a.ws = nullptr;
   a.nchunks = 0;
+  return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_route_pack(const int32_t* topk_ids, int T, int k, int E, int layout, int align_or_max_m,
+                          const void* payload, int64_t payload_row_bytes, const void* payload2,
+                          int64_t payload2_row_bytes, void* packed, void* packed2, int64_t rows_cap, int32_t* counts,
+                          int32_t* seg_offsets, int32_t* m_indices, int32_t* output_index, int32_t* dev_status,
+                          void* workspace, int64_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  RouteArgs a;
+  moe_status st = check_route("moe_route_pack", topk_ids, T, k, E, layout, align_or_max_m, payload,
+                              payload_row_bytes, payload2, payload2_row_bytes, packed, packed2, rows_cap, counts,
+                              seg_offsets, m_indices, output_index, dev_status, a);
+  if (st) return st;
+  const int64_t ws_need = route_workspace_bytes(a.R, E);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need || !aligned(workspace, 4)))
+    return fail(MOE_ERR_WORKSPACE, "moe_route_pack: needs %lld workspace bytes, got %lld", (long long)ws_need,
+                (long long)workspace_bytes);
+  a.ws = (int32_t*)workspace;
   return hip_status(launch_route_pack(a, (hipStream_t)stream), "moe_route_pack");
+}
+
+int64_t moe_route_pack_noalloc_max_bytes(void) { return route_scratch_bytes(); }
+
+moe_status moe_route_pack_noalloc(const int32_t* topk_ids, int T, int k, int E, int layout, int align_or_max_m,
+                                  const void* payload, int64_t payload_row_bytes, const void* payload2,
+                                  int64_t payload2_row_bytes, void* packed, void* packed2, int64_t rows_cap,
+                                  int32_t* counts, int32_t* seg_offsets, int32_t* m_indices, int32_t* output_index,
+                                  int32_t* dev_status, void* stream) {
+  g_err[0] = 0;
+  RouteArgs a;
+  moe_status st = check_route("moe_route_pack_noalloc", topk_ids, T, k, E, layout, align_or_max_m, payload,
+                              payload_row_bytes, payload2, payload2_row_bytes, packed, packed2, rows_cap, counts,
+                              seg_offsets, m_indices, output_index, dev_status, a);
+  if (st) return st;
+  const int64_t ws_need = route_workspace_bytes(a.R, E);
+  if (ws_need > route_scratch_bytes())
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_route_pack_noalloc: T*k=%d routes over E=%d experts need %lld scratch bytes, more than the "
+                "library's fixed %lld; use moe_route_pack with a workspace",
+                a.R, E, (long long)ws_need, (long long)route_scratch_bytes());
+  if (ws_need > 0) {
+    int32_t* ptr = nullptr;
+    st = hip_status(route_scratch_ptr(&ptr), "moe_route_pack_noalloc: device address of the scratch array");
+    if (st) return st;
+    a.ws = ptr;
+  }
+  return hip_status(launch_route_pack(a, (hipStream_t)stream), "moe_route_pack_noalloc");
 }
 
 static moe_status check_gemm(const char* fn, int layout, const void* A, const void* W, const void* SW, void* D,

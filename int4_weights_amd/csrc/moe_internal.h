@@ -44,6 +44,10 @@ struct RouteArgs {
 constexpr int kRouteSmallMax = 4096;   // routes handled by the single-launch path
 constexpr int kRouteChunk = 1024;      // routes per counting workgroup (large path)
 int64_t route_workspace_bytes(int R, int E);
+constexpr int kMaxDevices = 64;
+// the fixed device scratch of moe_route_pack_noalloc: its size, and its address on the current device
+int64_t route_scratch_bytes();
+hipError_t route_scratch_ptr(int32_t** out);
 hipError_t launch_route_pack(const RouteArgs& a, hipStream_t s);
 
 struct GemmArgs {

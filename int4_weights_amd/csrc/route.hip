@@ -17,6 +17,8 @@
 //   R >  4096: three launches -- count (one workgroup per 1024 routes, ranks
 //     within the chunk + chunk histogram), scan (one workgroup: per-expert
 //     prefix over chunks, segment offsets), gather (bandwidth-sized grid).
+#include <mutex>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -266,6 +268,36 @@ __global__ __launch_bounds__(256) void route_gather_kernel(const RouteArgs a) {
     place_route(a, i, p);
   }
   fill_m_indices(a, s_start);
+}
+
+// Scratch of moe_route_pack_noalloc: the large path's chunk counts and flags
+// in a device array of fixed size instead of a caller's workspace.  Host code
+// never names the array itself (on the host the name is only a stand-in for
+// the symbol): it uses the device address hipGetSymbolAddress returns, looked
+// up once per device with that device current.  Every call on one device
+// shares the array, so calls that overlap on one device race.  Nothing in it
+// needs clearing: the count kernel writes every entry the scan then reads.
+constexpr int64_t kRouteScratchBytes = 4ll << 20;
+static __device__ __align__(256) int32_t scratch[kRouteScratchBytes / 4];
+
+int64_t route_scratch_bytes() { return kRouteScratchBytes; }
+
+hipError_t route_scratch_ptr(int32_t** out) {
+  static std::mutex mu;
+  static int32_t* ptrs[kMaxDevices] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = (int32_t*)p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 int64_t route_workspace_bytes(int R, int E) {

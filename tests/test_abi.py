@@ -133,6 +133,21 @@ def test_host_validation_rejects_without_launching(lib):
                                      256, 0, None) == MOE_ERR_ALIGN
     assert lib.moe_grouped_gemm_int4(1, _p(A16), _p(A16), _p(A16 + 3), _p(A16), _p(A16), _p(A16), 4, 64, 128,
                                      256, 0, None) == MOE_ERR_ALIGN
+    # moe_route_pack_noalloc: the same checks as moe_route_pack, and a refusal (before any launch) of calls
+    # whose scratch would exceed the fixed 4 MiB array
+    assert lib.moe_route_pack_noalloc_max_bytes() == 4 << 20
+
+    def rpn(T=5, k=2, E=4, layout=0, am=128, rb=16, rows_cap=640, payload=A16):
+        return lib.moe_route_pack_noalloc(_p(A16), T, k, E, layout, am, _p(payload) if payload else None, rb, None, 0,
+                                          _p(A16), None, rows_cap, _p(A16), _p(A16), _p(A16), _p(A16), _p(A16), None)
+
+    assert rpn(layout=7) == MOE_ERR_SHAPE
+    assert rpn(rb=6) == MOE_ERR_ALIGN
+    assert rpn(payload=0) == MOE_ERR_NULL
+    assert rpn(rows_cap=100) == MOE_ERR_SHAPE
+    big_T = 1 << 20
+    assert rpn(T=big_T, k=8, E=1024, rows_cap=lib.moe_packed_rows_cap(big_T, 8, 1024, 128)) == MOE_ERR_WORKSPACE
+    assert b"scratch" in lib.moe_last_error()
     # moe_unpermute_combine
     assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 2, 12, _p(A16), None) == MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 0, 16, _p(A16), None) == MOE_ERR_SHAPE
