@@ -256,11 +256,11 @@ __global__ __launch_bounds__(256, 1) void gemm_int4_kernel(const GemmArgs a) {
 
 // ------------------------------------------------------- packed weights --
 template <int S, int SA>
-__device__ __forceinline__ void int4_unit_packed(const GemmArgs& a, const Unit& u, int wv, int lane) {
+__device__ __forceinline__ void int4_unit_packed(const GemmArgs& a, const Unit& u, int sub, int lane) {
   static_assert(S % SA == 0, "the activation ring must divide the weight ring");
   const int l16 = lane & 15, lg = lane >> 4;
   const int K = a.K, N = a.N, KG = K / 128;
-  const int ncol0 = u.n0 + 64 * wv;
+  const int ncol0 = u.n0 + 64 * sub;
   if (ncol0 >= N) return;  // N is a multiple of 128: a wave with work has 64 whole columns
 
   // weights: group g of 16-column block b is 1 KB at (g*(N/16) + b)*1024; lane L's 16 bytes at 16L
@@ -353,23 +353,35 @@ __device__ __forceinline__ void int4_unit_packed(const GemmArgs& a, const Unit& 
   }
 }
 
-// Two workgroups per CU (8 waves): the load latency of one wave is covered by
-// the others, so each keeps only the next group's loads in flight (measured:
-// 2 or 3 workgroups per CU with 2-deep rings within 2% of each other, deeper
-// rings no better).
-constexpr int kI4PackedWgPerCu = 2;
+// Ring depths (K groups in flight per wave) and workgroups per CU of the
+// packed kernel.
+#ifndef MOE_I4P_S
+#define MOE_I4P_S 2
+#endif
+#ifndef MOE_I4P_SA
+#define MOE_I4P_SA 2
+#endif
+#ifndef MOE_I4P_WGPC
+#define MOE_I4P_WGPC 2
+#endif
 
-template <int S, int SA>
-__global__ __launch_bounds__(256, kI4PackedWgPerCu) void gemm_int4_packed_kernel(const GemmArgs a) {
+// The waves of a workgroup share nothing, so the work is dealt per wave: a
+// wave's unit is 64 columns of a 256-column unit of the table (its sub-tile
+// sub = v % 4), and the units go round-robin over all waves of the grid, wave
+// slot wv * G + blockIdx.x first, so consecutive units (the column tiles of
+// one expert, of equal cost) land on different workgroups and CUs.
+template <int S, int SA, int WGPC>
+__global__ __launch_bounds__(256, WGPC) void gemm_int4_packed_kernel(const GemmArgs a) {
   __shared__ SchedSmem s_sched;
   const Sched sc{&s_sched};
   sched_build<16>(a, sc);
-  const Walk walk = sched_walk(s_sched.total);
+  const int total = uniform(s_sched.total) * 4;
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
-  for (int v = walk.first; v < walk.end; v += walk.stride) {
-    const Unit u = sched_unit<16>(a, sc, v);
-    int4_unit_packed<S, SA>(a, u, wv, lane);
+  const int G = gridDim.x;
+  for (int v = wv * G + blockIdx.x; v < total; v += 4 * G) {
+    const Unit u = sched_unit<16>(a, sc, v >> 2);
+    int4_unit_packed<S, SA>(a, u, v & 3, lane);
   }
 }
 
@@ -382,17 +394,17 @@ static hipError_t launch_i4(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int S, int SA>
+template <int S, int SA, int WGPC>
 static hipError_t launch_i4p(const GemmArgs& a, hipStream_t s) {
   const int cus = device_info().cus;
   int grid = cus - cus % kXcds;
   if (grid < kXcds) grid = kXcds;
-  gemm_int4_packed_kernel<S, SA><<<kI4PackedWgPerCu * grid, 256, 0, s>>>(a);
+  gemm_int4_packed_kernel<S, SA, WGPC><<<WGPC * grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s) {
-  if (a.wpacked) return launch_i4p<2, 2>(a, s);  // 16-row units whatever the rows per expert
+  if (a.wpacked) return launch_i4p<MOE_I4P_S, MOE_I4P_SA, MOE_I4P_WGPC>(a, s);  // 16-row units whatever the rows
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 64);
   if (em <= 16) return launch_i4<1, 8>(a, s);
   return launch_i4<4, 4>(a, s);

@@ -24,7 +24,8 @@ Sources (the five pages the method is described on):
                 4-bit weight format and zero point 8 (sec. 2 "Weight Format").
   [CuTeDSL]     Perplexity, "CuTeDSL bei Perplexity": MoE dispatch (count per
                 expert, unique index within the expert, copy into padded
-                buffers) and combine (weighted accumulation).
+                buffers) and combine (weighted accumulation); activation
+                kernels in the MoE kernel library.
 
 Parity status of every function is listed in its docstring ("pinned by ...").
 """
@@ -58,6 +59,7 @@ from .routing import (
 )
 from .gemm import grouped_gemm_fp8, grouped_gemm_int4, segments
 from .combine import combine, combine_fp32, f32_to_bf16_bits
+from .activation import quant_act_values, silu, swiglu, swiglu_quant
 from .metrics import calc_diff, elementwise_ok, elementwise_excess
 
 __all__ = [
@@ -69,4 +71,5 @@ __all__ = [
     "DEV_ID_RANGE", "DEV_CAPACITY", "packed_rows_cap", "route", "pack_rows",
     "grouped_gemm_fp8", "grouped_gemm_int4", "segments", "combine", "combine_fp32", "f32_to_bf16_bits",
     "calc_diff", "elementwise_ok", "elementwise_excess",
+    "silu", "swiglu", "quant_act_values", "swiglu_quant",
 ]

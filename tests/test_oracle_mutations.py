@@ -90,3 +90,32 @@ def test_mutation_combine_wrong_slot_weight_is_caught(monkeypatch):
     orig = oracle.combine
     monkeypatch.setattr(oracle, "combine", lambda y, oi, w: orig(y, oi, w[:, ::-1].copy()))
     _expect_fail(tg.test_combine_worked_example_and_brute_force)
+
+
+def test_mutation_sigmoid_instead_of_silu_is_caught(monkeypatch):
+    import test_oracle_activation as ta
+    monkeypatch.setattr(oracle, "silu", lambda x: 1.0 / (1.0 + np.exp(-np.asarray(x, np.float64))))
+    _expect_fail(ta.test_silu_closed_forms)
+
+
+def test_mutation_up_then_gate_is_caught(monkeypatch):
+    import oracle.activation as oa
+    import test_oracle_activation as ta
+    orig = oa.swiglu
+
+    def swapped(gu):
+        gu = np.asarray(gu, np.float64)
+        i = gu.shape[1] // 2
+        return orig(np.concatenate([gu[:, i:], gu[:, :i]], axis=1))
+
+    monkeypatch.setattr(oracle, "swiglu", swapped)
+    _expect_fail(ta.test_swiglu_takes_gate_then_up)
+
+
+def test_mutation_fma_rounded_twice_is_caught(monkeypatch):
+    import importlib
+    import test_oracle_combine as tc
+    oc = importlib.import_module("oracle.combine")
+    monkeypatch.setattr(oc, "_fma_f32", lambda w, y, acc: (w.astype(np.float32) * y.astype(np.float32) + acc)
+                        .astype(np.float32))
+    _expect_fail(tc.test_fma_step_is_the_exactly_rounded_fused_multiply_add)
