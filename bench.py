@@ -4,8 +4,9 @@
 A step is one pass of the whole path over one batch of synthetic input with
 everything already resident in HBM:
     moe_quant_act -> moe_route_pack -> moe_grouped_gemm_fp8 -> moe_unpermute_combine
-(plus the down-projection GEMM for the Qwen3-shaped workload, and the 4-bit
-GEMM in place of the FP8 one for the INT4 workload).
+(for the Qwen3-shaped workload the whole expert FFN: up-projection, SwiGLU +
+requantisation (moe_swiglu_quant), down-projection, then the combine; the
+4-bit GEMM in place of the FP8 one for the INT4 workload).
 
 Default workload: DeepSeek-V3-shaped prefill (T=4096 tokens, 256 experts,
 top-8, K=7168, N=4096, FP8 E4M3 with 1x128 / 128x128 power-of-two scales,
@@ -265,10 +266,11 @@ def build_workload(args, cfg, torch, np, moe, synth, want_cpu):
                 layer.combine(tw)
                 tm.mark(s, 4)
         else:
-            names = ["moe_quant_act", "moe_route_pack", "gemm", "moe_quant_act_down", "gemm_down",
+            # the whole expert FFN: up-projection (gate and up columns), SwiGLU + requantisation, down-projection
+            names = ["moe_quant_act", "moe_route_pack", "gemm", "moe_swiglu_quant", "gemm_down",
                      "moe_unpermute_combine"]
+            assert N == 2 * cfg.K_down
             dcodes, dsfw, _ = fp8_weights(torch, moe, synth, cfg, cfg.N_down, cfg.K_down, synth.STREAM_WEIGHTS_DOWN)
-            a_down = synth.activations(cfg, layer.rows_cap, cfg.K_down, stream=synth.STREAM_ACT_DOWN, device=dev)
             qd = torch.empty(layer.rows_cap, cfg.K_down, dtype=torch.uint8, device=dev)
             sfd = torch.empty(layer.rows_cap, cfg.K_down // 128, dtype=torch.float32, device=dev)
             Dd = torch.empty(layer.rows_cap, cfg.N_down, dtype=torch.bfloat16, device=dev)
@@ -282,7 +284,7 @@ def build_workload(args, cfg, torch, np, moe, synth, want_cpu):
                 tm.mark(s, 2)
                 layer.gemm()
                 tm.mark(s, 3)
-                moe.moe_quant_act(a_down, qd, sfd)
+                layer.swiglu_quant(qd, sfd)
                 tm.mark(s, 4)
                 layer.gemm(A=qd, SFA=sfd, D=Dd, w=dcodes, sfw=dsfw, N=cfg.N_down, K=cfg.K_down)
                 tm.mark(s, 5)

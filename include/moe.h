@@ -8,6 +8,7 @@
  *   moe_route_pack         topk_ids -> per-expert segments; copies token rows
  *   moe_grouped_gemm_fp8   packed rows x expert weights (128x128 pow2 scales) -> bf16
  *   moe_grouped_gemm_int4  (weight-only variant) bf16 rows x 4-bit weights -> bf16
+ *   moe_swiglu_quant       (between up- and down-projection) silu(gate) * up -> FP8 + 1x128 scales
  *   moe_unpermute_combine  topk_weights-weighted sum back to token order
  *
  * plus two weight-preparation calls (moe_quant_weight_fp8 / _int4) that turn
@@ -279,6 +280,32 @@ moe_status moe_grouped_gemm_int4(int layout,
                                  const int32_t* counts, const int32_t* seg_offsets,
                                  int E, int64_t rows_cap_or_max_m, int N, int K,
                                  int expected_m, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* moe_swiglu_quant: SwiGLU between the up- and down-projection, requantised
+ * for the down-projection's FP8 GEMM.  (The pages' fused gate+up expert weight
+ * -- a DeepSeek-V3-shaped up-projection has 2 x 2048 output columns -- and
+ * the activation kernels CuTeDSL bei Perplexity lists among the MoE kernels;
+ * the requantisation is the 1x128 rule of moe_quant_act, nxmr.cn DeepGEMM FP8
+ * article, "补偿机制一".)
+ *   gate_up [rows, 2I] bf16: the up-projection's output, gate in columns
+ *   0..I-1 and up in columns I..2I-1.  For every row p of every segment (the
+ *   same segments and clipping as moe_grouped_gemm_fp8: contiguous
+ *   rows_cap_or_max_m = rows and start_e = seg_offsets[e]; masked
+ *   rows_cap_or_max_m = max_m and start_e = e*max_m):
+ *     h[p, j] = silu(gate[p, j]) * up[p, j],  silu(x) = x / (1 + exp(-x)),
+ *   evaluated in fp32 (t = exp(-g) by the hardware exp2 of -g*log2(e), the
+ *   product carried with its rounding error; s = g * rcp(1 + t); h = s * u;
+ *   a few fp32 ulps from the exact value), then per
+ *   128-column block: sf = 2^e with e the smallest integer with
+ *   amax|h| <= 448 * 2^e (clamped to [-126, 127], 0 when amax == 0) and
+ *   q = round-to-nearest-even E4M3 of h * 2^-e.  h is never rounded to bf16.
+ *     q [rows, I] E4M3FN codes, sf [rows, I/128] fp32 powers of two.
+ *   Rows outside the segments are neither read nor written.
+ *   Requires I % 128 == 0, gate_up and q 16-byte aligned, sf 4-byte aligned. */
+moe_status moe_swiglu_quant(int layout, const uint16_t* gate_up, int64_t rows_cap_or_max_m, int I,
+                            const int32_t* counts, const int32_t* seg_offsets, int E,
+                            uint8_t* q, float* sf, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* moe_unpermute_combine: weighted combine back to token order ("gather").

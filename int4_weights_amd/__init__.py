@@ -28,5 +28,6 @@ from ._lib import (  # noqa: F401
     moe_route_pack_noalloc,
     moe_route_pack_noalloc_max_bytes,
     moe_route_pack_workspace_bytes,
+    moe_swiglu_quant,
     moe_unpermute_combine,
 )

@@ -48,6 +48,7 @@ SIGNATURES = {
                                       ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_grouped_gemm_int4": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                                        ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
+    "moe_swiglu_quant": (_c_i32, [ctypes.c_int, _vp, _c_i64, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp]),
     "moe_unpermute_combine": (_c_i32, [_vp, _c_i64, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
 }
 
@@ -268,6 +269,20 @@ def moe_grouped_gemm_int4(layout: int, A, W4, S16, D, counts, seg_offsets, E: in
     _check(load().moe_grouped_gemm_int4(layout, _ptr(A), _ptr(W4), _ptr(S16), _ptr(D), _ptr(counts),
                                         _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
            "moe_grouped_gemm_int4")
+
+
+def moe_swiglu_quant(layout: int, gate_up, rows_cap_or_max_m: int, counts, seg_offsets, E: int, q, sf,
+                     stream=None):
+    """gate_up bf16 [rows, 2I] -> q uint8 [rows, I] (E4M3 codes of silu(gate)*up), sf float32 [rows, I/128]."""
+    _dev(gate_up, "gate_up", torch.bfloat16), _dev(q, "q", torch.uint8), _dev(sf, "sf", torch.float32)
+    _dev(counts, "counts", torch.int32), _dev(seg_offsets, "seg_offsets", torch.int32)
+    I = gate_up.shape[-1] // 2
+    rows = E * rows_cap_or_max_m if layout == LAYOUT_MASKED else rows_cap_or_max_m
+    if gate_up.numel() < rows * 2 * I or q.numel() < rows * I or sf.numel() < rows * (I // 128) or \
+            counts.numel() < E or (layout == LAYOUT_CONTIGUOUS and (seg_offsets is None or seg_offsets.numel() < E)):
+        raise ValueError("moe_swiglu_quant: buffers too small")
+    _check(load().moe_swiglu_quant(layout, _ptr(gate_up), rows_cap_or_max_m, I, _ptr(counts), _ptr(seg_offsets), E,
+                                   _ptr(q), _ptr(sf), _stream(stream)), "moe_swiglu_quant")
 
 
 def moe_unpermute_combine(Y, output_index, topk_weights, Z, stream=None):

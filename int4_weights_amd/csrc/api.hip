@@ -349,6 +349,39 @@ moe_status moe_grouped_gemm_int4(int layout, const uint16_t* A, const uint8_t* W
   return hip_status(launch_gemm_int4(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_int4");
 }
 
+moe_status moe_swiglu_quant(int layout, const uint16_t* gate_up, int64_t rows_cap_or_max_m, int I,
+                            const int32_t* counts, const int32_t* seg_offsets, int E, uint8_t* q, float* sf,
+                            void* stream) {
+  g_err[0] = 0;
+  if (layout != MOE_LAYOUT_CONTIGUOUS && layout != MOE_LAYOUT_MASKED)
+    return fail(MOE_ERR_SHAPE, "moe_swiglu_quant: unknown layout %d", layout);
+  if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_SHAPE, "moe_swiglu_quant: E=%d must be in [1, %d]", E,
+                                                MOE_MAX_EXPERTS);
+  if (I <= 0 || rows_cap_or_max_m < 1)
+    return fail(MOE_ERR_SHAPE, "moe_swiglu_quant: I=%d rows/max_m=%lld", I, (long long)rows_cap_or_max_m);
+  if (I % 128) return fail(MOE_ERR_UNSUPPORTED, "moe_swiglu_quant: I=%d is not a multiple of 128", I);
+  const int64_t rows = layout == MOE_LAYOUT_MASKED ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
+  if (rows > 0x7fffffff) return fail(MOE_ERR_SHAPE, "moe_swiglu_quant: too many rows");
+  if (!gate_up || !counts || !q || !sf) return fail(MOE_ERR_NULL, "moe_swiglu_quant: null pointer");
+  if (layout == MOE_LAYOUT_CONTIGUOUS && !seg_offsets)
+    return fail(MOE_ERR_NULL, "moe_swiglu_quant: seg_offsets is required for the contiguous layout");
+  if (!aligned(gate_up, 16) || !aligned(q, 16) || !aligned(sf, 4) || !aligned(counts, 4) ||
+      (seg_offsets && !aligned(seg_offsets, 4)))
+    return fail(MOE_ERR_ALIGN, "moe_swiglu_quant: gate_up and q must be 16-byte aligned, sf and tables 4-byte");
+  SwigluArgs a;
+  a.gu = gate_up;
+  a.q = q;
+  a.sf = sf;
+  a.counts = counts;
+  a.seg_offsets = seg_offsets;
+  a.E = E;
+  a.masked = layout == MOE_LAYOUT_MASKED;
+  a.max_m = a.masked ? (int)rows_cap_or_max_m : 0;
+  a.rows_cap = rows;
+  a.I = I;
+  return hip_status(launch_swiglu_quant(a, (hipStream_t)stream), "moe_swiglu_quant");
+}
+
 moe_status moe_unpermute_combine(const uint16_t* Y, int64_t y_rows, const int32_t* output_index,
                                  const float* topk_weights, int T, int k, int N, uint16_t* Z, void* stream) {
   g_err[0] = 0;

@@ -68,6 +68,20 @@ struct GemmArgs {
 hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s);
 
+struct SwigluArgs {
+  const uint16_t* gu;    // bf16 [rows, 2I]: gate columns then up columns
+  uint8_t* q;            // E4M3 [rows, I]
+  float* sf;             // fp32 [rows, I/128]
+  const int32_t* counts;
+  const int32_t* seg_offsets;
+  int E;
+  int masked;
+  int max_m;
+  int64_t rows_cap;      // rows of gate_up / q (masked: E*max_m)
+  int I;
+};
+hipError_t launch_swiglu_quant(const SwigluArgs& a, hipStream_t s);
+
 hipError_t launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* oi, const float* w, int T, int k,
                           int N, uint16_t* Z, hipStream_t s);
 

@@ -75,6 +75,13 @@ class MoeFP8Layer:
         L.moe_grouped_gemm_fp8(self.layout | self.wflag, A, SFA, w, sfw, D, self.counts, self.seg_offsets, self.E,
                                am, N, K, self.expected_m)
 
+    def swiglu_quant(self, q, sf, D=None):
+        """silu(gate) * up of the up-projection output D (default: this layer's), requantised into the
+        down-projection's FP8 codes q [rows, N/2] and 1x128 scales sf [rows, N/256]."""
+        D = self.D if D is None else D
+        am = self.am if self.layout == L.LAYOUT_MASKED else self.rows_cap
+        L.moe_swiglu_quant(self.layout, D, am, self.counts, self.seg_offsets, self.E, q, sf)
+
     def combine(self, topk_weights, D=None, Z=None):
         """Weighted combine of packed rows D (default: this layer's GEMM output) into Z [T, D.shape[1]]."""
         T = topk_weights.shape[0]

@@ -37,6 +37,7 @@ from .formats import (
     e4m3_encode,
     bf16_bits_to_f64,
     f64_to_bf16_bits,
+    f64_to_bf16_bits_normal,
     fp16_bits_to_f64,
 )
 from .quant import (
@@ -64,7 +65,7 @@ from .metrics import calc_diff, elementwise_ok, elementwise_excess
 
 __all__ = [
     "E4M3_MAX", "e4m3_value", "e4m3_decode_table", "e4m3_encode",
-    "bf16_bits_to_f64", "f64_to_bf16_bits", "fp16_bits_to_f64",
+    "bf16_bits_to_f64", "f64_to_bf16_bits", "f64_to_bf16_bits_normal", "fp16_bits_to_f64",
     "pow2_exponent", "pow2_exponents", "quant_act", "quant_weight_fp8",
     "quant_weight_int4", "dequant_act", "dequant_weight_fp8", "unpack_int4",
     "dequant_weight_int4",

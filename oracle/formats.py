@@ -96,6 +96,28 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     return out
 
 
+def f64_to_bf16_bits_normal(x) -> np.ndarray:
+    """float64 -> nearest bf16 (ties to even) as uint16 patterns, vectorised, for values that are zero or
+    whose magnitude lies in bf16's normal range [2^-126, 2^128); raises otherwise.
+
+    With x = m * 2^e (frexp, 0.5 <= |m| < 1), bf16 keeps 8 significant bits: the result is
+    rint(m * 2^8) * 2^(e-8), where the scaling is exact and np.rint rounds half to even.
+
+    Pinned by: equality with f64_to_bf16_bits (the neighbour-comparison rounding) on random values
+    spanning many binades, on exact halfway cases and on the carry into the next binade.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.isnan(x).any() or ((a != 0) & (a < 2.0 ** -126)).any() or (a >= 2.0 ** 128).any():
+        raise ValueError("f64_to_bf16_bits_normal: value outside the normal range of bf16")
+    m, e = np.frexp(x)
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)      # may carry to the next power of two: still exact
+    if (np.abs(r) >= 2.0 ** 128).any():
+        raise ValueError("f64_to_bf16_bits_normal: rounds past the bf16 range")
+    bits = r.astype(np.float32).view(np.uint32)          # r has 8 significant bits: exact in fp32
+    return (bits >> 16).astype(np.uint16)
+
+
 def _bf16_rne_scalar(val: float) -> int:
     if math.isnan(val):
         return 0x7FC0

@@ -148,6 +148,19 @@ def test_host_validation_rejects_without_launching(lib):
     big_T = 1 << 20
     assert rpn(T=big_T, k=8, E=1024, rows_cap=lib.moe_packed_rows_cap(big_T, 8, 1024, 128)) == MOE_ERR_WORKSPACE
     assert b"scratch" in lib.moe_last_error()
+    # moe_swiglu_quant(layout, gate_up, rows_or_max_m, I, counts, seg_offsets, E, q, sf, stream)
+    def sw(layout=0, gu=A16, rows=512, I=256, seg=A16, E=4, q=A16, sf=A16):
+        return lib.moe_swiglu_quant(layout, _p(gu) if gu else None, rows, I, _p(A16), _p(seg) if seg else None, E,
+                                    _p(q) if q else None, _p(sf) if sf else None, None)
+
+    assert sw(I=200) == MOE_ERR_UNSUPPORTED
+    assert sw(layout=3) == MOE_ERR_SHAPE
+    assert sw(E=0) == MOE_ERR_SHAPE
+    assert sw(rows=0) == MOE_ERR_SHAPE
+    assert sw(gu=0) == MOE_ERR_NULL
+    assert sw(seg=0) == MOE_ERR_NULL                 # contiguous needs seg_offsets
+    assert sw(q=A16 + 8) == MOE_ERR_ALIGN
+    assert sw(sf=A16 + 2) == MOE_ERR_ALIGN
     # moe_unpermute_combine
     assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 2, 12, _p(A16), None) == MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 0, 16, _p(A16), None) == MOE_ERR_SHAPE

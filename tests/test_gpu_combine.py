@@ -102,3 +102,27 @@ def test_combine_determinism_20_runs():
     z = _run(y, oi, w)
     for _ in range(20):
         assert np.array_equal(_run(y, oi, w), z)
+
+
+def test_combine_full_size_qwen3_routing_bit_exact():
+    """The Qwen3-shaped combine (65536 routes into 8192 x 4096) on seeded rows, every bit of sampled tokens."""
+    require_gpu()
+    import synth
+
+    cfg = synth.config_by_name("qwen3_skewed")
+    ids, tw = synth.route_inputs(cfg)
+    r = oracle.route(ids.numpy(), cfg.E, "contiguous", align=cfg.align)
+    rows, N = r["rows_cap"], cfg.N_down
+    Y = synth.activations(cfg, rows, N, stream=synth.STREAM_ACT_DOWN, device=DEV)
+    T, k = r["output_index"].shape
+    Z = torch.empty(T, N, dtype=torch.bfloat16, device=DEV)
+    moe.moe_unpermute_combine(Y, torch.from_numpy(r["output_index"].astype(np.int32)).to(DEV), tw.to(DEV), Z)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([np.arange(0, T, 97), [T - 1]]))
+    oi = r["output_index"][toks]
+    used = np.unique(oi[oi >= 0])
+    local = np.searchsorted(used, oi).astype(np.int32)
+    local[oi < 0] = -1
+    yb = u16(Y[torch.from_numpy(used).to(DEV)])
+    want = oracle.combine_fp32(yb, local, tw.numpy()[toks])
+    assert np.array_equal(u16(Z[torch.from_numpy(toks).to(DEV)]), want)

@@ -167,18 +167,6 @@ def _fp8_gemm_and_combine(c, r, A_bits_of_token, D, Z, kept_codes_fn, label):
             zr += float(c["tw"][t, s]) * y_ref_rows[p]
     zg = Z[t][torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
     gemm_tolerance_check(zg[None], zr[None], 1e-3 if label == "fp8" else 1e-2)
-    _combine_bit_exact(D, Z, r["output_index"], c["tw"], [t, 0, c["T"] - 1])
-
-
-def _combine_bit_exact(D, Z, oi, tw, tokens):
-    """The combine alone, given the GPU's own GEMM rows: every bit of Z[t] equals the fp32 fma chain."""
-    for t in sorted(set(int(x) for x in tokens)):
-        slots = [int(p) for p in oi[t]]
-        valid = [p for p in slots if p >= 0]
-        rows = u16(D[torch.tensor(valid, dtype=torch.int64, device=DEV)]) if valid else np.zeros((0, D.shape[1]), np.uint16)
-        local = np.array([[valid.index(p) if p >= 0 else -1 for p in slots]], np.int32)
-        want = oracle.combine_fp32(rows, local, np.asarray(tw[t:t + 1], np.float32))
-        assert np.array_equal(u16(Z[t:t + 1]), want), f"combine of token {t}"
 
 
 def _oracle_fp8_weight_blocks(c, codes, sfw, kept, N, K):
@@ -221,7 +209,7 @@ def test_full_size_fp8_layer(name):
 
 
 def test_full_size_qwen3_skewed_up_down_combine():
-    """Zipf-skewed prefill: up-projection, down-projection on the same segments, combine of the down output."""
+    """Zipf-skewed prefill: up-projection, SwiGLU + requantisation, down-projection, combine of the down output."""
     require_gpu()
     cfg = synth.config_by_name("qwen3_skewed")
     print("[fullsize] qwen3_skewed", flush=True)
@@ -240,45 +228,79 @@ def test_full_size_qwen3_skewed_up_down_combine():
     _fp8_gemm_and_combine(c, r, a_of_tokens, layer.D, c["z"], fn, "fp8")
     del c["codes"], c["packed"]
 
-    # down-projection: independent N(0,1) activations over the packed rows, quantised in place
+    # down-projection on SwiGLU(gate, up) of the up-projection's output, requantised by moe_swiglu_quant, as the
+    # layer runs it (the up-projection's 3072 columns are gate 0..1535 and up 1536..3071)
     Kd, Nd = cfg.K_down, cfg.N_down
+    assert c["N"] == 2 * Kd
     dcodes, dsfw, dkept, dpacked = _gpu_fp8_weights(cfg, Nd, Kd, synth.STREAM_WEIGHTS_DOWN, set(c["sample"]))
-    a_down = synth.activations(cfg, layer.rows_cap, Kd, stream=synth.STREAM_ACT_DOWN, device=DEV)
     qd = torch.empty(layer.rows_cap, Kd, dtype=torch.uint8, device=DEV)
     sfd = torch.empty(layer.rows_cap, Kd // 128, dtype=torch.float32, device=DEV)
     Dd = torch.empty(layer.rows_cap, Nd, dtype=torch.bfloat16, device=DEV)
     Zd = torch.empty(c["T"], Nd, dtype=torch.bfloat16, device=DEV)
-    moe.moe_quant_act(a_down, qd, sfd)
+    layer.swiglu_quant(qd, sfd)
     layer.gemm(A=qd, SFA=sfd, D=Dd, w=dpacked, sfw=dsfw, N=Nd, K=Kd)
     layer.combine(torch.from_numpy(c["tw"]).to(DEV), D=Dd, Z=Zd)
     torch.cuda.synchronize()
 
-    def a_of_rows(rows):
-        bits = u16(a_down[torch.from_numpy(np.asarray(rows)).to(DEV)])
-        a, sa = oracle.quant_act(bits)
-        assert np.array_equal(qd[torch.from_numpy(np.asarray(rows)).to(DEV)].cpu().numpy(), a)
-        return oracle.dequant_act(a, sa)
-
-    # rows of the down GEMM are addressed by packed row, not by token
+    # The oracle chain, by the path's definitions: the up-projection's exact output rounded to bf16 (the GEMM's
+    # output format), SwiGLU and the 1x128 requantisation of those values, the down-projection in float64.
+    owner = _token_of_rows(r, c["T"])
     fnd = _oracle_fp8_weight_blocks(c, dcodes, dsfw, dkept, Nd, Kd)
     blocks = _col_blocks(Nd)
     cols = np.concatenate([np.arange(128 * b, 128 * b + 128) for b in blocks])
     yrow = {}
+    flips = total = 0
     for e in c["sample"]:
         cnt, st = int(r["counts"][e]), int(r["seg_offsets"][e])
+        if cnt == 0:
+            continue
         rows = set(_rows_of(st, cnt).tolist())
         rows |= set(int(p) for p in r["output_index"][c["tok"]] if st <= p < st + cnt)
         rows = np.array(sorted(rows))
-        y = a_of_rows(rows) @ fnd(e, blocks).T
-        got = Dd[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].float().cpu().numpy()
-        gemm_tolerance_check(got.astype(np.float64), y, 1e-3)
+        toks = np.array([owner[int(p)][0] for p in rows])
+        wq, ws = oracle.quant_weight_fp8(c["kept"][e][None])
+        y_up = a_of_tokens(toks) @ oracle.dequant_weight_fp8(wq[0], ws[0]).T
+        qo, so = oracle.swiglu_quant(oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits_normal(y_up)))
+        sel = torch.from_numpy(rows).to(DEV)
+        qg = qd[sel].cpu().numpy()
+        flips += int((qg != qo).sum())
+        total += qo.size
+        wd = fnd(e, blocks)
+        y = oracle.dequant_act(qo, so) @ wd.T
+        got = Dd[sel][:, torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
+        _chain_check(got, y, qo, so, wd)
         for i, p in enumerate(rows):
             yrow[int(p)] = y[i]
+    # codes differ only where the GPU's up-projection rounds to another bf16 than the exact value (the FP8 matrix
+    # instruction's accumulation, about 1% of its outputs by one ulp) or the fp32 SwiGLU lands on the other side of
+    # an E4M3 rounding midpoint: rare
+    assert flips <= total // 200, f"{flips} of {total} SwiGLU codes differ"
     t = c["tok"]
     zr = sum(float(c["tw"][t, s]) * yrow[int(r["output_index"][t, s])] for s in range(c["k"]))
     zg = Zd[t][torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
-    gemm_tolerance_check(zg[None], np.asarray(zr)[None], 1e-3)
-    _combine_bit_exact(Dd, Zd, r["output_index"], c["tw"], [t, 0, c["T"] - 1])
+    assert oracle.calc_diff(zg, zr) < 1e-3
+
+
+def _chain_check(got, y, qo, so, wd):
+    """Down-projection output after the GPU's own up-projection and SwiGLU vs the oracle chain.
+
+    The requantised codes of the two chains can differ by one E4M3 step where the up-projection's bf16 output
+    differs from the exact rounding (see the flip count).  The bar: the pages' calc_diff < 1e-3; every element
+    within the GEMM bound 2e-2*|y| + 1e-2*rms(y) plus three such steps at the element's largest |step * w|; and
+    99.5% of the elements within the GEMM bound alone."""
+    assert oracle.calc_diff(got, y) < 1e-3
+    tab = oracle.e4m3_decode_table()
+    v = np.abs(tab[qo])
+    # one E4M3 step at each code's magnitude (2^-9 in the subnormal range), times the block scale
+    step = np.where(v < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(v, 2.0 ** -6))) - 3))
+    step = step * np.repeat(so.astype(np.float64), 128, axis=1)
+    aw = np.abs(wd)
+    worst = np.concatenate([np.max(step[i:i + 8, None, :] * aw[None], axis=2) for i in range(0, len(step), 8)])
+    rms = float(np.sqrt(np.mean(y * y)))
+    bound = 2e-2 * np.abs(y) + 1e-2 * rms
+    err = np.abs(got - y)
+    assert (err <= bound + 3 * worst).all(), float(np.max(err - bound - 3 * worst))
+    assert np.mean(err <= bound) >= 0.995, float(np.mean(err <= bound))
 
 
 def test_full_size_int4_decode_layer():

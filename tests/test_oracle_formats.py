@@ -82,3 +82,16 @@ def test_bf16_fp16_decode():
     got = oracle.f64_to_bf16_bits(x)
     ref = torch.tensor(x, dtype=torch.float64).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(got, ref)
+
+
+def test_vectorised_bf16_rounding_equals_the_neighbour_rounding():
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal(4000) * 2.0 ** rng.integers(-100, 100, 4000)
+    # exact halfway points between neighbours (ties to even) and the carry into the next binade
+    base = oracle.bf16_bits_to_f64(np.arange(0x3F80, 0x3F80 + 300, dtype=np.uint16))
+    half = (base[:-1] + base[1:]) / 2
+    edge = np.array([2.0 - 2.0 ** -9, 2.0 - 2.0 ** -8 - 2.0 ** -10, -(1.0 + 2.0 ** -8), 0.0, -0.0, 3.0e38])
+    for v in (x, half, -half, edge):
+        assert np.array_equal(oracle.f64_to_bf16_bits_normal(v), oracle.f64_to_bf16_bits(v))
+    with pytest.raises(ValueError):
+        oracle.f64_to_bf16_bits_normal(np.array([1e-40]))
