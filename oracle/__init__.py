@@ -58,7 +58,7 @@ from .routing import (
     route,
     pack_rows,
 )
-from .gemm import grouped_gemm_fp8, grouped_gemm_int4, segments
+from .gemm import grouped_gemm_bf16, grouped_gemm_fp8, grouped_gemm_int4, segments
 from .combine import combine, combine_fp32, f32_to_bf16_bits
 from .activation import quant_act_values, silu, swiglu, swiglu_quant
 from .metrics import calc_diff, elementwise_ok, elementwise_excess
@@ -70,7 +70,7 @@ __all__ = [
     "quant_weight_int4", "dequant_act", "dequant_weight_fp8", "unpack_int4",
     "dequant_weight_int4",
     "DEV_ID_RANGE", "DEV_CAPACITY", "packed_rows_cap", "route", "pack_rows",
-    "grouped_gemm_fp8", "grouped_gemm_int4", "segments", "combine", "combine_fp32", "f32_to_bf16_bits",
+    "grouped_gemm_bf16", "grouped_gemm_fp8", "grouped_gemm_int4", "segments", "combine", "combine_fp32", "f32_to_bf16_bits",
     "calc_diff", "elementwise_ok", "elementwise_excess",
     "silu", "swiglu", "quant_act_values", "swiglu_quant",
 ]

@@ -15,6 +15,13 @@ within a few ulps of the exact value.  Output rows that belong to no valid
 assignment are NaN (never compared).
 
 INT4 ([MatMulNBits] sec. 2):  D[p, n] = sum_k a[p,k] * (q[e,n,k] - 8) * s[e, n, k/128].
+
+BF16 ([AsymGEMM] "API Reference", BF16 m_grouped contiguous / masked; [GEMM-modes]
+sec. 4.6, the BF16 contiguous grouped GEMM SGLang calls):
+    D[p, n] = sum_k a[p,k] * w[e,n,k]   with bf16 operands, in float64.
+Every product of two bf16 values is exact in float64 (8 + 8 significant bits)
+and sums of them stay exact while the exponent range of a row is modest, so
+the result is the exact value for all practical purposes.
 """
 
 from __future__ import annotations
@@ -57,6 +64,32 @@ def grouped_gemm_fp8(a_codes, sfa, w_codes, sfw, counts, seg_offsets, rows_out=N
         p0 = int(seg_offsets[e])
         a = dequant_act(a_codes[p0:p0 + c], sfa[p0:p0 + c])
         w = dequant_weight_fp8(w_codes[wi], sfw[wi])
+        out[p0:p0 + c] = a @ w.T
+    return out
+
+
+def grouped_gemm_bf16(a_bits, w_bits, counts, seg_offsets, rows_out=None, experts=None):
+    """BF16 grouped GEMM in float64.
+
+    a_bits uint16 [rows, K] bf16; w_bits uint16 [E, N, K] bf16.
+    Returns float64 [rows_out, N] (NaN outside valid rows).
+
+    Pinned by: exact rational brute force, small-integer and one-hot cases, per-expert single-GEMM
+    equivalence.
+    """
+    rows = a_bits.shape[0] if rows_out is None else rows_out
+    E_all = len(counts)
+    N = w_bits.shape[-2]
+    out = np.full((rows, N), np.nan, dtype=np.float64)
+    sel = range(E_all) if experts is None else list(experts)
+    for j, e in enumerate(sel):
+        c = int(counts[e])
+        if c <= 0:
+            continue
+        wi = e if experts is None else j
+        p0 = int(seg_offsets[e])
+        a = bf16_bits_to_f64(a_bits[p0:p0 + c])
+        w = bf16_bits_to_f64(w_bits[wi])
         out[p0:p0 + c] = a @ w.T
     return out
 

@@ -172,3 +172,48 @@ def test_calc_diff_closed_forms():
         assert oracle.calc_diff(x, c * x) == pytest.approx((1 - c) ** 2 / (1 + c * c), rel=1e-9, abs=1e-15)
     assert oracle.calc_diff(np.zeros(4), np.zeros(4)) == 0.0
     assert oracle.elementwise_ok(x, x) and not oracle.elementwise_ok(x + 1.0, x)
+
+
+def _bf16_problem(rng, E=2, K=64, N=16, counts=(3, 5), align=8, scale=1.0):
+    counts = np.array(counts, dtype=np.int32)
+    starts = np.zeros(E + 1, dtype=np.int32)
+    for e in range(E):
+        starts[e + 1] = starts[e] + -(-counts[e] // align) * align
+    rows = int(starts[E])
+    a = oracle.f32_to_bf16_bits((rng.standard_normal((rows, K)) * scale).astype(np.float32))
+    w = oracle.f32_to_bf16_bits((rng.standard_normal((E, N, K)) * 0.02).astype(np.float32))
+    return a, w, counts, starts
+
+
+def test_bf16_gemm_exact_rational_brute_force():
+    rng = np.random.default_rng(10)
+    a, w, counts, starts = _bf16_problem(rng)
+    d = oracle.grouped_gemm_bf16(a, w, counts, starts)
+    af, wf = oracle.bf16_bits_to_f64(a), oracle.bf16_bits_to_f64(w)
+    for e in range(2):
+        for p in range(int(starts[e]), int(starts[e]) + int(counts[e])):
+            for n in (0, 5, 15):
+                exact = sum(Fraction(float(af[p, k])) * Fraction(float(wf[e, n, k])) for k in range(a.shape[1]))
+                assert d[p, n] == float(exact)
+    assert np.isnan(d[int(starts[0]) + int(counts[0]):int(starts[1])]).all()
+
+
+def test_bf16_gemm_integers_one_hot_and_per_expert():
+    rng = np.random.default_rng(11)
+    E, K, N = 3, 128, 32
+    counts = np.array([4, 0, 6], np.int32)
+    starts = np.array([0, 8, 8, 16], np.int32)
+    ai = rng.integers(-8, 9, size=(16, K)).astype(np.float32)
+    wi = rng.integers(-8, 9, size=(E, N, K)).astype(np.float32)
+    a, w = oracle.f32_to_bf16_bits(ai), oracle.f32_to_bf16_bits(wi)
+    d = oracle.grouped_gemm_bf16(a, w, counts, starts)
+    for e in (0, 2):
+        s, c = starts[e], counts[e]
+        assert np.array_equal(d[s:s + c], (ai[s:s + c].astype(np.int64) @ wi[e].astype(np.int64).T).astype(np.float64))
+        single = oracle.grouped_gemm_bf16(a[s:s + c], w[e:e + 1], np.array([c]), np.array([0, c]))
+        assert np.array_equal(d[s:s + c], single)
+    # one-hot row: a single 1.0 at k0 picks column k0 of the weights
+    a1 = np.zeros((16, K), np.uint16)
+    a1[0, 37] = 0x3F80
+    d1 = oracle.grouped_gemm_bf16(a1, w, counts, starts)
+    assert np.array_equal(d1[0], wi[0, :, 37].astype(np.float64))

@@ -119,3 +119,16 @@ def test_mutation_fma_rounded_twice_is_caught(monkeypatch):
     monkeypatch.setattr(oc, "_fma_f32", lambda w, y, acc: (w.astype(np.float32) * y.astype(np.float32) + acc)
                         .astype(np.float32))
     _expect_fail(tc.test_fma_step_is_the_exactly_rounded_fused_multiply_add)
+
+
+def test_mutation_bf16_transposed_weight_is_caught(monkeypatch):
+    orig = og.grouped_gemm_bf16
+
+    def transposed(a_bits, w_bits, counts, seg_offsets, rows_out=None, experts=None):
+        # weights read K-major from an [E, K, N] view of the same bytes
+        E, N, K = w_bits.shape
+        wt = np.ascontiguousarray(w_bits.reshape(E, K, N).transpose(0, 2, 1))
+        return orig(a_bits, wt, counts, seg_offsets, rows_out, experts)
+
+    monkeypatch.setattr(oracle, "grouped_gemm_bf16", transposed)
+    _expect_fail(tg.test_bf16_gemm_exact_rational_brute_force)
