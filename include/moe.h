@@ -8,6 +8,7 @@
  *   moe_route_pack         topk_ids -> per-expert segments; copies token rows
  *   moe_grouped_gemm_fp8   packed rows x expert weights (128x128 pow2 scales) -> bf16
  *   moe_grouped_gemm_int4  (weight-only variant) bf16 rows x 4-bit weights -> bf16
+ *   moe_grouped_gemm_bf16  (BF16 variant) bf16 rows x bf16 expert weights -> bf16
  *   moe_swiglu_quant       (between up- and down-projection) silu(gate) * up -> FP8 + 1x128 scales
  *   moe_unpermute_combine  topk_weights-weighted sum back to token order
  *
@@ -277,6 +278,21 @@ moe_status moe_grouped_gemm_fp8(int layout,
 moe_status moe_grouped_gemm_int4(int layout,
                                  const uint16_t* A, const uint8_t* W4,
                                  const uint16_t* S16, uint16_t* D,
+                                 const int32_t* counts, const int32_t* seg_offsets,
+                                 int E, int64_t rows_cap_or_max_m, int N, int K,
+                                 int expected_m, void* stream);
+
+/* moe_grouped_gemm_bf16: BF16 grouped GEMM, "NT" (both operands
+ * K-contiguous).  (AsymGEMM README, "API Reference": BF16 m_grouped
+ * contiguous and masked grouped GEMMs with bf16 output; rainlin, "GEMM
+ * 执行方式", sec. 4.6: the BF16 contiguous grouped GEMM on the packed segments.)
+ *     D[p, n] = bf16_rne( sum_k A[p,k] * W[e,n,k] ), accumulated in fp32.
+ *     A [rows, K] bf16, W [E, N, K] bf16, D [rows, N] bf16.
+ *   Layout, counts, seg_offsets, expected_m, the rows of D that are written,
+ *   alignment and size limits as for moe_grouped_gemm_fp8 (no packed-weight
+ *   order: layout must be MOE_LAYOUT_CONTIGUOUS or MOE_LAYOUT_MASKED). */
+moe_status moe_grouped_gemm_bf16(int layout,
+                                 const uint16_t* A, const uint16_t* W, uint16_t* D,
                                  const int32_t* counts, const int32_t* seg_offsets,
                                  int E, int64_t rows_cap_or_max_m, int N, int K,
                                  int expected_m, void* stream);

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     MoeError,
     load,
     moe_abi_version,
+    moe_grouped_gemm_bf16,
     moe_grouped_gemm_fp8,
     moe_grouped_gemm_int4,
     moe_pack_weight_fp8,

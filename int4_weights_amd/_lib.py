@@ -49,6 +49,8 @@ SIGNATURES = {
     "moe_grouped_gemm_int4": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                                        ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_swiglu_quant": (_c_i32, [ctypes.c_int, _vp, _c_i64, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_grouped_gemm_bf16": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_unpermute_combine": (_c_i32, [_vp, _c_i64, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
 }
 
@@ -269,6 +271,17 @@ def moe_grouped_gemm_int4(layout: int, A, W4, S16, D, counts, seg_offsets, E: in
     _check(load().moe_grouped_gemm_int4(layout, _ptr(A), _ptr(W4), _ptr(S16), _ptr(D), _ptr(counts),
                                         _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
            "moe_grouped_gemm_int4")
+
+
+def moe_grouped_gemm_bf16(layout: int, A, W, D, counts, seg_offsets, E: int, rows_cap_or_max_m: int, N: int, K: int,
+                          expected_m: int = 0, stream=None):
+    _dev(A, "A", torch.bfloat16), _dev(W, "W", torch.bfloat16), _dev(D, "D", torch.bfloat16)
+    _dev(counts, "counts", torch.int32), _dev(seg_offsets, "seg_offsets", torch.int32)
+    _gemm_sizes("moe_grouped_gemm_bf16", layout, E, rows_cap_or_max_m, counts, seg_offsets,
+                lambda rows: (("A", A, rows * K), ("W", W, E * N * K), ("D", D, rows * N)))
+    _check(load().moe_grouped_gemm_bf16(layout, _ptr(A), _ptr(W), _ptr(D), _ptr(counts), _ptr(seg_offsets), E,
+                                        rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
+           "moe_grouped_gemm_bf16")
 
 
 def moe_swiglu_quant(layout: int, gate_up, rows_cap_or_max_m: int, counts, seg_offsets, E: int, q, sf,

@@ -349,6 +349,33 @@ moe_status moe_grouped_gemm_int4(int layout, const uint16_t* A, const uint8_t* W
   return hip_status(launch_gemm_int4(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_int4");
 }
 
+moe_status moe_grouped_gemm_bf16(int layout, const uint16_t* A, const uint16_t* W, uint16_t* D,
+                                 const int32_t* counts, const int32_t* seg_offsets, int E, int64_t rows_cap_or_max_m,
+                                 int N, int K, int expected_m, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_gemm("moe_grouped_gemm_bf16", layout, A, W, W, D, counts, seg_offsets, E, rows_cap_or_max_m,
+                             N, K);
+  if (st) return st;
+  if ((int64_t)N * K * 2 > 0xffffffffll)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_gemm_bf16: one expert's weights exceed 4 GiB");
+  GemmArgs a;
+  a.A = (const uint8_t*)A;
+  a.SFA = nullptr;
+  a.W = (const uint8_t*)W;
+  a.SW = nullptr;
+  a.D = D;
+  a.counts = counts;
+  a.seg_offsets = seg_offsets;
+  a.E = E;
+  a.masked = layout == MOE_LAYOUT_MASKED;
+  a.max_m = a.masked ? (int)rows_cap_or_max_m : 0;
+  a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
+  a.N = N;
+  a.K = K;
+  a.wpacked = 0;
+  return hip_status(launch_gemm_bf16(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_bf16");
+}
+
 moe_status moe_swiglu_quant(int layout, const uint16_t* gate_up, int64_t rows_cap_or_max_m, int I,
                             const int32_t* counts, const int32_t* seg_offsets, int E, uint8_t* q, float* sf,
                             void* stream) {

@@ -51,9 +51,9 @@ hipError_t route_scratch_ptr(int32_t** out);
 hipError_t launch_route_pack(const RouteArgs& a, hipStream_t s);
 
 struct GemmArgs {
-  const uint8_t* A;      // fp8 codes [rows, K] or bf16 [rows, K] (int4 path)
+  const uint8_t* A;      // fp8 codes [rows, K] or bf16 [rows, K] (int4 and bf16 paths)
   const float* SFA;      // [rows, K/128] (fp8 path)
-  const uint8_t* W;      // fp8 [E, N, K] or int4 [E, N, K/2]
+  const uint8_t* W;      // fp8 [E, N, K], int4 [E, N, K/2] or bf16 [E, N, K]
   const void* SW;        // SFW fp32 [E, N/128, K/128] or S16 fp16 [E, N, K/128]
   uint16_t* D;           // bf16 [rows, N]
   const int32_t* counts;
@@ -67,6 +67,7 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmArgs& a, int expected_m, hipStream_t s);
 
 struct SwigluArgs {
   const uint16_t* gu;    // bf16 [rows, 2I]: gate columns then up columns

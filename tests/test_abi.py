@@ -148,6 +148,19 @@ def test_host_validation_rejects_without_launching(lib):
     big_T = 1 << 20
     assert rpn(T=big_T, k=8, E=1024, rows_cap=lib.moe_packed_rows_cap(big_T, 8, 1024, 128)) == MOE_ERR_WORKSPACE
     assert b"scratch" in lib.moe_last_error()
+    # moe_grouped_gemm_bf16(layout, A, W, D, counts, seg, E, rows, N, K, expected_m, stream)
+    def gb(layout=0, N=256, K=256, E=4, rows=512, seg=A16, A=A16, W=A16):
+        return lib.moe_grouped_gemm_bf16(layout, _p(A) if A else None, _p(W) if W else None, _p(A16), _p(A16),
+                                         _p(seg) if seg else None, E, rows, N, K, 0, None)
+
+    assert gb(N=200) == MOE_ERR_UNSUPPORTED
+    assert gb(K=64) == MOE_ERR_UNSUPPORTED
+    assert gb(E=0) == MOE_ERR_SHAPE
+    assert gb(layout=0x10) == MOE_ERR_SHAPE          # no packed-weight order for bf16
+    assert gb(seg=0) == MOE_ERR_NULL
+    assert gb(W=0) == MOE_ERR_NULL
+    assert gb(A=A16 + 8) == MOE_ERR_ALIGN
+    assert gb(K=128 * 300) == MOE_ERR_UNSUPPORTED
     # moe_swiglu_quant(layout, gate_up, rows_or_max_m, I, counts, seg_offsets, E, q, sf, stream)
     def sw(layout=0, gu=A16, rows=512, I=256, seg=A16, E=4, q=A16, sf=A16):
         return lib.moe_swiglu_quant(layout, _p(gu) if gu else None, rows, I, _p(A16), _p(seg) if seg else None, E,
