@@ -39,6 +39,11 @@ from .formats import (
     f64_to_bf16_bits,
     f64_to_bf16_bits_normal,
     fp16_bits_to_f64,
+    E2M1_MAX,
+    e2m1_value,
+    e2m1_decode_table,
+    e2m1_encode,
+    e8m0_value,
 )
 from .quant import (
     pow2_exponent,
@@ -50,6 +55,9 @@ from .quant import (
     dequant_weight_fp8,
     unpack_int4,
     dequant_weight_int4,
+    pow2_exponent_e2m1,
+    quant_weight_fp4,
+    dequant_weight_fp4,
 )
 from .routing import (
     DEV_ID_RANGE,
@@ -58,7 +66,7 @@ from .routing import (
     route,
     pack_rows,
 )
-from .gemm import grouped_gemm_bf16, grouped_gemm_fp8, grouped_gemm_int4, segments
+from .gemm import grouped_gemm_bf16, grouped_gemm_fp8, grouped_gemm_fp8_fp4, grouped_gemm_int4, segments
 from .combine import combine, combine_fp32, f32_to_bf16_bits
 from .activation import quant_act_values, silu, swiglu, swiglu_quant
 from .metrics import calc_diff, elementwise_ok, elementwise_excess
@@ -70,7 +78,9 @@ __all__ = [
     "quant_weight_int4", "dequant_act", "dequant_weight_fp8", "unpack_int4",
     "dequant_weight_int4",
     "DEV_ID_RANGE", "DEV_CAPACITY", "packed_rows_cap", "route", "pack_rows",
-    "grouped_gemm_bf16", "grouped_gemm_fp8", "grouped_gemm_int4", "segments", "combine", "combine_fp32", "f32_to_bf16_bits",
+    "grouped_gemm_bf16", "grouped_gemm_fp8", "grouped_gemm_fp8_fp4", "grouped_gemm_int4", "segments",
+    "E2M1_MAX", "e2m1_value", "e2m1_decode_table", "e2m1_encode", "e8m0_value", "pow2_exponent_e2m1",
+    "quant_weight_fp4", "dequant_weight_fp4", "combine", "combine_fp32", "f32_to_bf16_bits",
     "calc_diff", "elementwise_ok", "elementwise_excess",
     "silu", "swiglu", "quant_act_values", "swiglu_quant",
 ]

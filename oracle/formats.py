@@ -1,5 +1,6 @@
 """Number formats: OCP FP8 E4M3 (decode table, round-to-nearest-even encode),
-bf16 and fp16 bit patterns.  TEST INFRASTRUCTURE ONLY (see package header).
+OCP FP4 E2M1 and its E8M0 block scales, bf16 and fp16 bit patterns.
+TEST INFRASTRUCTURE ONLY (see package header).
 
 [DG-FP8] describes E4M3 as 1 sign bit, 4 exponent bits and 3 mantissa bits
 with a range of about +-448.  The +-448 range identifies the OCP "E4M3FN"
@@ -147,3 +148,62 @@ def _bf16_rne_scalar(val: float) -> int:
 def fp16_bits_to_f64(bits) -> np.ndarray:
     """uint16 IEEE half patterns -> float64 (exact)."""
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------------------------- FP4 E2M1 --
+# The pages name 4-bit floating-point weights (E2M1: 1 sign, 2 exponent, 1 mantissa bit) in the MXFP4 and
+# NVFP4 block-scaled forms ([CuTeDSL] Blackwell quantisation schemes; [AsymGEMM] "API Reference", FP4).  The
+# element format is OCP E2M1: exponent bias 1, exponent field 0 subnormal (0 and 0.5), no infinities or NaN,
+# largest magnitude 6.
+E2M1_MAX = 6.0
+
+
+def e2m1_value(code: int) -> float:
+    """Value of one E2M1 code (low 4 bits).
+
+    Pinned by: the closed-form table 0, 0.5, 1, 1.5, 2, 3, 4, 6 (and negatives) and strict monotonicity.
+    """
+    code = int(code) & 0xF
+    s, e, m = code >> 3, (code >> 1) & 3, code & 1
+    v = m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1)
+    return -v if s else v
+
+
+def e2m1_decode_table() -> np.ndarray:
+    """float64[16]: value of every E2M1 code."""
+    return np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e2m1_encode(v) -> np.ndarray:
+    """Round float64 values to the nearest E2M1 code, ties to the code with an even mantissa bit.
+
+    The rule written out: magnitudes below 1 are multiples of the subnormal step 0.5 (rounded half to even:
+    0.25 -> 0, 0.75 -> 1.0); otherwise a = (1 + f) * 2^E with E in {0, 1, 2} and the 1-bit mantissa f * 2
+    rounded half to even, a carry moving to the next binade.  Requires |v| <= 6; the sign is kept for values
+    that round to zero.
+
+    Pinned by: comparison with a nearest-value search over the eight magnitudes (ties broken toward the
+    even code) on a dense grid including every halfway point, and encode(decode(c)) == c.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if np.isnan(v).any():
+        raise ValueError("e2m1_encode: NaN input")
+    a = np.abs(v)
+    if (a > E2M1_MAX).any():
+        raise ValueError("e2m1_encode: |v| > 6")
+    sub = a < 1.0
+    code_sub = np.rint(a * 2.0)                            # 0, 1 or 2 (2 is the code of 1.0)
+    _, ex = np.frexp(np.where(sub, 1.0, a))
+    E = ex - 1                                             # a = (1 + f) * 2^E, E in 0..2
+    frac = np.where(sub, 0.0, np.ldexp(a, -E) - 1.0)
+    code_norm = (E + 1) * 2 + np.rint(frac * 2.0)
+    code = np.where(sub, code_sub, code_norm).astype(np.uint8)
+    return code | (np.signbit(v).astype(np.uint8) << 3)
+
+
+def e8m0_value(byte) -> np.ndarray:
+    """Value 2^(b - 127) of E8M0 scale bytes (255, the NaN encoding, is rejected)."""
+    b = np.asarray(byte, dtype=np.int64)
+    if (b == 255).any():
+        raise ValueError("E8M0 255 is NaN")
+    return np.ldexp(np.ones(b.shape), b - 127)

@@ -16,6 +16,10 @@ assignment are NaN (never compared).
 
 INT4 ([MatMulNBits] sec. 2):  D[p, n] = sum_k a[p,k] * (q[e,n,k] - 8) * s[e, n, k/128].
 
+FP8 x FP4 ([AsymGEMM] "API Reference", FP4 grouped GEMMs; [CuTeDSL] MXFP4 block scaling;
+[DG-FP8] "精度与吞吐的平衡点": one FP4 side is held to calc_diff < 0.01):
+    D[p, n] = sum_k (dec8(a[p,k]) * sa[p, k/128]) * (dec4(w[e,n,k]) * 2^(sw[e,n,k/32] - 127)).
+
 BF16 ([AsymGEMM] "API Reference", BF16 m_grouped contiguous / masked; [GEMM-modes]
 sec. 4.6, the BF16 contiguous grouped GEMM SGLang calls):
     D[p, n] = sum_k a[p,k] * w[e,n,k]   with bf16 operands, in float64.
@@ -29,7 +33,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import bf16_bits_to_f64
-from .quant import dequant_act, dequant_weight_fp8, dequant_weight_int4
+from .quant import dequant_act, dequant_weight_fp4, dequant_weight_fp8, dequant_weight_int4
 
 
 def segments(counts, seg_offsets):
@@ -91,6 +95,34 @@ def grouped_gemm_bf16(a_bits, w_bits, counts, seg_offsets, rows_out=None, expert
         a = bf16_bits_to_f64(a_bits[p0:p0 + c])
         w = bf16_bits_to_f64(w_bits[wi])
         out[p0:p0 + c] = a @ w.T
+    return out
+
+
+def grouped_gemm_fp8_fp4(a_codes, sfa, w4, sw, counts, seg_offsets, rows_out=None, experts=None):
+    """FP8 activations x MXFP4 weights grouped GEMM in float64.
+
+        D[p, n] = sum_k (dec8(a[p,k]) * sa[p, k/128]) * (dec4(w[e,n,k]) * 2^(sw[e, n, k/32] - 127))
+
+    a_codes uint8 [rows, K] E4M3, sfa float32 [rows, K/128]; w4 uint8 [E, N, K/2] E2M1 pairs (even k low),
+    sw uint8 [E, N, K/32] E8M0.  Every product is exact in float64 and so is each 32-block partial sum.
+    Returns float64 [rows_out, N] (NaN outside valid rows).
+
+    Pinned by: exact rational brute force, small-integer codes vs integer matmul, one-hot rows, scale
+    invariance, per-expert single-GEMM equivalence.
+    """
+    rows = a_codes.shape[0] if rows_out is None else rows_out
+    E_all = len(counts)
+    N = w4.shape[-2]
+    out = np.full((rows, N), np.nan, dtype=np.float64)
+    sel = range(E_all) if experts is None else list(experts)
+    for j, e in enumerate(sel):
+        c = int(counts[e])
+        if c <= 0:
+            continue
+        wi = e if experts is None else j
+        p0 = int(seg_offsets[e])
+        a = dequant_act(a_codes[p0:p0 + c], sfa[p0:p0 + c])
+        out[p0:p0 + c] = a @ dequant_weight_fp4(w4[wi], sw[wi]).T
     return out
 
 

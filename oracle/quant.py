@@ -29,7 +29,8 @@ import math
 
 import numpy as np
 
-from .formats import E4M3_MAX, e4m3_decode_table, e4m3_encode, bf16_bits_to_f64, fp16_bits_to_f64
+from .formats import (E2M1_MAX, E4M3_MAX, bf16_bits_to_f64, e2m1_decode_table, e2m1_encode, e4m3_decode_table,
+                      e4m3_encode, e8m0_value, fp16_bits_to_f64)
 
 BLOCK = 128
 EXP_MIN, EXP_MAX = -126, 127
@@ -165,3 +166,53 @@ def dequant_weight_int4(q4: np.ndarray, s16_bits: np.ndarray) -> np.ndarray:
     q = unpack_int4(q4).astype(np.float64)
     s = np.repeat(fp16_bits_to_f64(s16_bits), BLOCK, axis=-1)
     return (q - 8.0) * s
+
+
+# ------------------------------------------------------------------------------------- FP4 (MXFP4) weights --
+FP4_BLOCK = 32
+E8M0_MIN, E8M0_MAX = -127, 127
+
+
+def pow2_exponent_e2m1(amax: float) -> int:
+    """Smallest integer e with amax <= 6 * 2^e, clamped to [-127, 127]; 0 for amax == 0 (the FP8 rule with the
+    E2M1 maximum 6).  Pinned by: minimality on random and edge values."""
+    amax = float(amax)
+    if amax < 0 or math.isnan(amax):
+        raise ValueError("amax must be a non-negative number")
+    if amax == 0.0:
+        return 0
+    e = int(math.floor(math.log2(amax / E2M1_MAX)))
+    while amax > math.ldexp(E2M1_MAX, e):
+        e += 1
+    while amax <= math.ldexp(E2M1_MAX, e - 1):
+        e -= 1
+    return min(max(e, E8M0_MIN), E8M0_MAX)
+
+
+def quant_weight_fp4(w_bits: np.ndarray):
+    """MXFP4 weight quantisation: one power-of-two scale per 32 consecutive K values of an output column.
+
+    Reading taken (the pages give the FP4 element format and block scaling, not the offline rule): the scale is
+    the smallest power of two 2^e with amax <= 6 * 2^e (rounded up, as the FP8 rule), stored as the E8M0 byte
+    e + 127; codes = E2M1 RNE of w * 2^-e (exact multiply), two per byte, the even k in the low nibble.
+    w_bits: uint16 [E, N, K] bf16, K % 128 == 0.
+    Returns (w4 uint8 [E, N, K/2], sw uint8 [E, N, K/32]).
+    Pinned by: the scale rule's minimality and amax bound, the E2M1 error bound, rescale invariance.
+    """
+    w = bf16_bits_to_f64(w_bits)
+    E, N, K = w.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    nb = K // FP4_BLOCK
+    amax = np.abs(w.reshape(E, N, nb, FP4_BLOCK)).max(axis=3)
+    e = np.vectorize(pow2_exponent_e2m1, otypes=[np.int64])(amax) if amax.size else amax.astype(np.int64)
+    scaled = w / np.repeat(np.ldexp(np.ones(e.shape), e), FP4_BLOCK, axis=2)
+    codes = e2m1_encode(scaled)
+    w4 = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return w4, (e + 127).astype(np.uint8)
+
+
+def dequant_weight_fp4(w4: np.ndarray, sw: np.ndarray) -> np.ndarray:
+    """float64 [..., N, K] = decode(code) * 2^(sw - 127) of the code's 32-block."""
+    codes = unpack_int4(w4)
+    return e2m1_decode_table()[codes] * np.repeat(e8m0_value(sw), FP4_BLOCK, axis=-1)

@@ -132,3 +132,22 @@ def test_mutation_bf16_transposed_weight_is_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "grouped_gemm_bf16", transposed)
     _expect_fail(tg.test_bf16_gemm_exact_rational_brute_force)
+
+
+def test_mutation_fp4_nibble_order_is_caught(monkeypatch):
+    import oracle.gemm as og2
+    import test_oracle_fp4 as tf4
+    orig = og2.grouped_gemm_fp8_fp4
+
+    def swapped(a, sa, w4, sw, counts, seg, rows_out=None, experts=None):
+        return orig(a, sa, ((w4 >> 4) | ((w4 & 15) << 4)).astype(np.uint8), sw, counts, seg, rows_out, experts)
+
+    monkeypatch.setattr(oracle, "grouped_gemm_fp8_fp4", swapped)
+    _expect_fail(tf4.test_fp8_fp4_gemm_exact_rational_brute_force)
+
+
+def test_mutation_fp4_ties_away_is_caught(monkeypatch):
+    import test_oracle_fp4 as tf4
+    orig = oracle.e2m1_encode
+    monkeypatch.setattr(oracle, "e2m1_encode", lambda v: orig(np.clip(np.asarray(v, np.float64) * (1 + 1e-12), -6, 6)))
+    _expect_fail(tf4.test_e2m1_encode_equals_nearest_search_on_a_dense_grid)
