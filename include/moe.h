@@ -9,11 +9,13 @@
  *   moe_grouped_gemm_fp8   packed rows x expert weights (128x128 pow2 scales) -> bf16
  *   moe_grouped_gemm_int4  (weight-only variant) bf16 rows x 4-bit weights -> bf16
  *   moe_grouped_gemm_bf16  (BF16 variant) bf16 rows x bf16 expert weights -> bf16
+ *   moe_grouped_gemm_fp8_fp4 (FP4 variant) FP8 rows x MXFP4 (E2M1 + E8M0) weights -> bf16
  *   moe_swiglu_quant       (between up- and down-projection) silu(gate) * up -> FP8 + 1x128 scales
  *   moe_unpermute_combine  topk_weights-weighted sum back to token order
  *
- * plus two weight-preparation calls (moe_quant_weight_fp8 / _int4) that turn
- * bf16 expert weights into the formats the GEMMs read.
+ * plus weight-preparation calls (moe_quant_weight_fp8 / _int4 / _fp4,
+ * moe_pack_weight_fp8 / _int4) that turn bf16 expert weights into the formats
+ * the GEMMs read.
  *
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers owned by the caller.  The library
@@ -296,6 +298,44 @@ moe_status moe_grouped_gemm_bf16(int layout,
                                  const int32_t* counts, const int32_t* seg_offsets,
                                  int E, int64_t rows_cap_or_max_m, int N, int K,
                                  int expected_m, void* stream);
+
+/* moe_quant_weight_fp4: MXFP4 quantisation of expert weights for
+ * moe_grouped_gemm_fp8_fp4 (AsymGEMM README, "API Reference": FP4 weights as
+ * packed 4-bit data plus scales; CuTeDSL bei Perplexity: the MXFP4 block
+ * scaling).  Per output column n and block of 32 consecutive k: amax; e = the
+ * smallest integer with amax <= 6 * 2^e, clamped to [-127, 127], 0 when
+ * amax == 0 (the pages give no offline rule: the FP8 rule with the E2M1
+ * maximum 6); sw = e + 127 (an E8M0 byte); codes = E2M1 round-to-nearest-even
+ * of w * 2^-e (sign kept for values that round to zero).
+ *   w [E, N, K] bf16 -> w4 [E, N, K/2] (two codes per byte, the even k in the
+ *   low nibble), sw [E, N, K/32] E8M0 bytes.
+ *   Requires K % 128 == 0, w and w4 16-byte aligned. */
+moe_status moe_quant_weight_fp4(const uint16_t* w, int E, int N, int K,
+                                uint8_t* w4, uint8_t* sw, void* stream);
+
+/* moe_grouped_gemm_fp8_fp4: FP8 activations x MXFP4 weights grouped GEMM
+ * (AsymGEMM README, "API Reference": FP4 m_grouped contiguous and masked
+ * grouped GEMMs; nxmr.cn DeepGEMM article, "精度与吞吐的平衡点": a product with
+ * one FP4 operand is held to calc_diff < 0.01).
+ *   For every segment e and row p in [start_e, start_e + counts[e]):
+ *     D[p, n] = bf16_rne( sum_k (dec(A[p,k]) * SFA[p, k/128]) *
+ *                         (e2m1(W4[e,n,k]) * 2^(SW[e,n,k/32] - 127)) )
+ *   accumulated in fp32, the power-of-two scales applied inside the matrix
+ *   instruction (exact).
+ *     A [rows, K] E4M3FN, SFA [rows, K/128] fp32 powers of two (moe_quant_act);
+ *     W4 [E, N, K/2] and SW [E, N, K/32] as written by moe_quant_weight_fp4;
+ *     D [rows, N] bf16.
+ *   Layout, counts, seg_offsets, expected_m, the rows of D that are written,
+ *   alignment (SFA and SW 4-byte aligned) and size limits as for
+ *   moe_grouped_gemm_fp8 (no packed order: layout must be
+ *   MOE_LAYOUT_CONTIGUOUS or MOE_LAYOUT_MASKED). */
+moe_status moe_grouped_gemm_fp8_fp4(int layout,
+                                    const uint8_t* A, const float* SFA,
+                                    const uint8_t* W4, const uint8_t* SW,
+                                    uint16_t* D,
+                                    const int32_t* counts, const int32_t* seg_offsets,
+                                    int E, int64_t rows_cap_or_max_m, int N, int K,
+                                    int expected_m, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* moe_swiglu_quant: SwiGLU between the up- and down-projection, requantised

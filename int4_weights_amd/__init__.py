@@ -18,11 +18,13 @@ from ._lib import (  # noqa: F401
     moe_abi_version,
     moe_grouped_gemm_bf16,
     moe_grouped_gemm_fp8,
+    moe_grouped_gemm_fp8_fp4,
     moe_grouped_gemm_int4,
     moe_pack_weight_fp8,
     moe_pack_weight_int4,
     moe_packed_rows_cap,
     moe_quant_act,
+    moe_quant_weight_fp4,
     moe_quant_weight_fp8,
     moe_quant_weight_int4,
     moe_route_pack,

@@ -51,6 +51,9 @@ SIGNATURES = {
     "moe_swiglu_quant": (_c_i32, [ctypes.c_int, _vp, _c_i64, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp]),
     "moe_grouped_gemm_bf16": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                        ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
+    "moe_quant_weight_fp4": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_grouped_gemm_fp8_fp4": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_unpermute_combine": (_c_i32, [_vp, _c_i64, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
 }
 
@@ -282,6 +285,28 @@ def moe_grouped_gemm_bf16(layout: int, A, W, D, counts, seg_offsets, E: int, row
     _check(load().moe_grouped_gemm_bf16(layout, _ptr(A), _ptr(W), _ptr(D), _ptr(counts), _ptr(seg_offsets), E,
                                         rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
            "moe_grouped_gemm_bf16")
+
+
+def moe_quant_weight_fp4(w, w4, sw, stream=None):
+    """w bf16 [E, N, K] -> w4 uint8 [E, N, K/2] (E2M1 pairs), sw uint8 [E, N, K/32] (E8M0 scales)."""
+    _dev(w, "w", torch.bfloat16, 3), _dev(w4, "w4", torch.uint8, 3), _dev(sw, "sw", torch.uint8, 3)
+    E, N, K = w.shape
+    if tuple(w4.shape) != (E, N, K // 2) or tuple(sw.shape) != (E, N, K // 32):
+        raise ValueError("moe_quant_weight_fp4: shape mismatch")
+    _check(load().moe_quant_weight_fp4(_ptr(w), E, N, K, _ptr(w4), _ptr(sw), _stream(stream)), "moe_quant_weight_fp4")
+
+
+def moe_grouped_gemm_fp8_fp4(layout: int, A, SFA, W4, SW, D, counts, seg_offsets, E: int, rows_cap_or_max_m: int,
+                             N: int, K: int, expected_m: int = 0, stream=None):
+    _dev(A, "A", torch.uint8), _dev(SFA, "SFA", torch.float32), _dev(W4, "W4", torch.uint8)
+    _dev(SW, "SW", torch.uint8), _dev(D, "D", torch.bfloat16), _dev(counts, "counts", torch.int32)
+    _dev(seg_offsets, "seg_offsets", torch.int32)
+    _gemm_sizes("moe_grouped_gemm_fp8_fp4", layout, E, rows_cap_or_max_m, counts, seg_offsets,
+                lambda rows: (("A", A, rows * K), ("SFA", SFA, rows * (K // 128)), ("W4", W4, E * N * (K // 2)),
+                              ("SW", SW, E * N * (K // 32)), ("D", D, rows * N)))
+    _check(load().moe_grouped_gemm_fp8_fp4(layout, _ptr(A), _ptr(SFA), _ptr(W4), _ptr(SW), _ptr(D), _ptr(counts),
+                                           _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m,
+                                           _stream(stream)), "moe_grouped_gemm_fp8_fp4")
 
 
 def moe_swiglu_quant(layout: int, gate_up, rows_cap_or_max_m: int, counts, seg_offsets, E: int, q, sf,

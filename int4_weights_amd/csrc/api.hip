@@ -376,6 +376,46 @@ moe_status moe_grouped_gemm_bf16(int layout, const uint16_t* A, const uint16_t* 
   return hip_status(launch_gemm_bf16(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_bf16");
 }
 
+moe_status moe_quant_weight_fp4(const uint16_t* w, int E, int N, int K, uint8_t* w4, uint8_t* sw, void* stream) {
+  g_err[0] = 0;
+  if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_quant_weight_fp4: E=%d N=%d K=%d", E, N, K);
+  if (K % 128) return fail(MOE_ERR_UNSUPPORTED, "moe_quant_weight_fp4: K=%d is not a multiple of 128", K);
+  if (E == 0) return MOE_OK;
+  if (!w || !w4 || !sw) return fail(MOE_ERR_NULL, "moe_quant_weight_fp4: null pointer");
+  if (!aligned(w, 16) || !aligned(w4, 16))
+    return fail(MOE_ERR_ALIGN, "moe_quant_weight_fp4: w and w4 must be 16-byte aligned");
+  return hip_status(launch_quant_weight_fp4(w, E, N, K, w4, sw, (hipStream_t)stream), "moe_quant_weight_fp4");
+}
+
+moe_status moe_grouped_gemm_fp8_fp4(int layout, const uint8_t* A, const float* SFA, const uint8_t* W4,
+                                    const uint8_t* SW, uint16_t* D, const int32_t* counts,
+                                    const int32_t* seg_offsets, int E, int64_t rows_cap_or_max_m, int N, int K,
+                                    int expected_m, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_gemm("moe_grouped_gemm_fp8_fp4", layout, A, W4, SW, D, counts, seg_offsets, E,
+                             rows_cap_or_max_m, N, K);
+  if (st) return st;
+  if (!SFA) return fail(MOE_ERR_NULL, "moe_grouped_gemm_fp8_fp4: SFA is null");
+  if (!aligned(SFA, 4) || !aligned(SW, 4))
+    return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_fp8_fp4: SFA and SW must be 4-byte aligned");
+  GemmArgs a;
+  a.A = A;
+  a.SFA = SFA;
+  a.W = W4;
+  a.SW = SW;
+  a.D = D;
+  a.counts = counts;
+  a.seg_offsets = seg_offsets;
+  a.E = E;
+  a.masked = layout == MOE_LAYOUT_MASKED;
+  a.max_m = a.masked ? (int)rows_cap_or_max_m : 0;
+  a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
+  a.N = N;
+  a.K = K;
+  a.wpacked = 0;
+  return hip_status(launch_gemm_fp4(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_fp8_fp4");
+}
+
 moe_status moe_swiglu_quant(int layout, const uint16_t* gate_up, int64_t rows_cap_or_max_m, int I,
                             const int32_t* counts, const int32_t* seg_offsets, int E, uint8_t* q, float* sf,
                             void* stream) {

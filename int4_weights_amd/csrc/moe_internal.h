@@ -53,8 +53,8 @@ hipError_t launch_route_pack(const RouteArgs& a, hipStream_t s);
 struct GemmArgs {
   const uint8_t* A;      // fp8 codes [rows, K] or bf16 [rows, K] (int4 and bf16 paths)
   const float* SFA;      // [rows, K/128] (fp8 path)
-  const uint8_t* W;      // fp8 [E, N, K], int4 [E, N, K/2] or bf16 [E, N, K]
-  const void* SW;        // SFW fp32 [E, N/128, K/128] or S16 fp16 [E, N, K/128]
+  const uint8_t* W;      // fp8 [E, N, K], int4 or fp4 [E, N, K/2], or bf16 [E, N, K]
+  const void* SW;        // SFW fp32 [E, N/128, K/128], S16 fp16 [E, N, K/128] or E8M0 bytes [E, N, K/32] (fp4)
   uint16_t* D;           // bf16 [rows, N]
   const int32_t* counts;
   const int32_t* seg_offsets;
@@ -68,6 +68,8 @@ struct GemmArgs {
 hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, int expected_m, hipStream_t s);
+hipError_t launch_gemm_fp4(const GemmArgs& a, int expected_m, hipStream_t s);
+hipError_t launch_quant_weight_fp4(const uint16_t* w, int E, int N, int K, uint8_t* w4, uint8_t* sw, hipStream_t s);
 
 struct SwigluArgs {
   const uint16_t* gu;    // bf16 [rows, 2I]: gate columns then up columns

@@ -161,6 +161,24 @@ def test_host_validation_rejects_without_launching(lib):
     assert gb(W=0) == MOE_ERR_NULL
     assert gb(A=A16 + 8) == MOE_ERR_ALIGN
     assert gb(K=128 * 300) == MOE_ERR_UNSUPPORTED
+    # moe_grouped_gemm_fp8_fp4(layout, A, SFA, W4, SW, D, counts, seg, E, rows, N, K, expected_m, stream)
+    def g4(layout=0, N=256, K=256, E=4, rows=512, seg=A16, A=A16, SW=A16, SFA=A16):
+        return lib.moe_grouped_gemm_fp8_fp4(layout, _p(A) if A else None, _p(SFA) if SFA else None, _p(A16),
+                                            _p(SW) if SW else None, _p(A16), _p(A16), _p(seg) if seg else None, E,
+                                            rows, N, K, 0, None)
+
+    assert g4(N=200) == MOE_ERR_UNSUPPORTED
+    assert g4(K=192) == MOE_ERR_UNSUPPORTED
+    assert g4(layout=0x10) == MOE_ERR_SHAPE
+    assert g4(seg=0) == MOE_ERR_NULL
+    assert g4(SFA=0) == MOE_ERR_NULL
+    assert g4(SW=0) == MOE_ERR_NULL
+    assert g4(SW=A16 + 2) == MOE_ERR_ALIGN
+    assert g4(A=A16 + 8) == MOE_ERR_ALIGN
+    assert lib.moe_quant_weight_fp4(_p(A16), 2, 128, 100, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_quant_weight_fp4(_p(A16 + 8), 2, 128, 128, _p(A16), _p(A16), None) == MOE_ERR_ALIGN
+    assert lib.moe_quant_weight_fp4(None, 2, 128, 128, _p(A16), _p(A16), None) == MOE_ERR_NULL
+    assert lib.moe_quant_weight_fp4(None, 0, 128, 128, None, None, None) == MOE_OK
     # moe_swiglu_quant(layout, gate_up, rows_or_max_m, I, counts, seg_offsets, E, q, sf, stream)
     def sw(layout=0, gu=A16, rows=512, I=256, seg=A16, E=4, q=A16, sf=A16):
         return lib.moe_swiglu_quant(layout, _p(gu) if gu else None, rows, I, _p(A16), _p(seg) if seg else None, E,
