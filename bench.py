@@ -13,7 +13,8 @@ top-8, K=7168, N=4096, FP8 E4M3 with 1x128 / 128x128 power-of-two scales,
 contiguous 128-row-aligned layout).  The other workloads (the Qwen3-shaped
 skewed prefill, whose up-projection is the MFMA-bound GEMM, the masked FP8
 decode and the 4-bit decode) are timed in the same run and reported under
-"workloads".  Prints ONE JSON line.
+"workloads", and the DeepSeek-V3-shaped steps with MXFP4 or bf16 expert
+weights under "variants".  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--also NAMES|none] [--cpu-baseline off]
 """
@@ -44,6 +45,8 @@ def parse():
     ap.add_argument("--config", default="dsv3_prefill", choices=WORKLOADS)
     ap.add_argument("--also", default="qwen3_skewed,dsv3_decode,int4_decode",
                     help="further workloads timed in the same run (comma-separated, or 'none')")
+    ap.add_argument("--variants", default="fp4_dsv3_decode,fp4_dsv3_prefill,bf16_dsv3_decode,bf16_dsv3_prefill",
+                    help="weight-format variants timed in the same run: <fp4|bf16>_<workload> (or 'none')")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-experts", type=int, default=128, help="experts in the timed oracle sample")
     ap.add_argument("--clock", choices=["on", "off"], default="on",
@@ -328,6 +331,112 @@ def build_workload(args, cfg, torch, np, moe, synth, want_cpu):
     return w
 
 
+def build_variant(args, fmt, cfg, torch, np, moe, synth):
+    """The same routing and step as the FP8 workload, with the expert weights in another format:
+    fp4 -- MXFP4 weights (E2M1 codes, one E8M0 scale per 32 K values) x FP8 activations;
+    bf16 -- bf16 weights x bf16 activations (the rows are packed as bf16, no quantisation)."""
+    dev = "cuda"
+    T, E, k, K, N = cfg.T, cfg.E, cfg.topk, cfg.K, cfg.N
+    ids_cpu, tw_cpu = synth.route_inputs(cfg)
+    ids, tw = ids_cpu.to(dev), tw_cpu.to(dev)
+    x = synth.activations(cfg, T, K).to(dev)
+    layout = moe.LAYOUT_MASKED if cfg.layout == "masked" else moe.LAYOUT_CONTIGUOUS
+    am = cfg.max_m if cfg.layout == "masked" else cfg.align
+    rows_cap = moe.moe_packed_rows_cap(T, k, E, am) if layout == moe.LAYOUT_CONTIGUOUS else E * am
+    em = args.expected_m or max(1, T * k // E)
+    counts = torch.zeros(E, dtype=torch.int32, device=dev)
+    seg = torch.zeros(E + 1, dtype=torch.int32, device=dev)
+    mi = torch.empty(rows_cap, dtype=torch.int32, device=dev)
+    oi = torch.empty(T, k, dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(moe.moe_route_pack_workspace_bytes(T, k, E), 16), dtype=torch.uint8, device=dev)
+    D = torch.empty(rows_cap, N, dtype=torch.bfloat16, device=dev)
+    Z = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    am_gemm = am if layout == moe.LAYOUT_MASKED else rows_cap
+    if fmt == "fp4":
+        # MXFP4 weights in the fragment-packed order (moe_pack_weight_fp4, prepared once)
+        W4 = torch.empty(E, N, K // 2, dtype=torch.uint8, device=dev)
+        SW = torch.empty(E, N, K // 32, dtype=torch.uint8, device=dev)
+        r4 = torch.empty(16, N, K // 2, dtype=torch.uint8, device=dev)
+        rs = torch.empty(16, N, K // 32, dtype=torch.uint8, device=dev)
+        for e0 in range(0, E, 16):
+            ex = list(range(e0, min(E, e0 + 16)))
+            w = synth.expert_weights(cfg, N, K, experts=ex, stream=synth.STREAM_WEIGHTS, device=dev)
+            moe.moe_quant_weight_fp4(w, r4[:len(ex)], rs[:len(ex)])
+            moe.moe_pack_weight_fp4(r4[:len(ex)], rs[:len(ex)], W4[e0:e0 + len(ex)], SW[e0:e0 + len(ex)])
+            del w
+        q = torch.empty(T, K, dtype=torch.uint8, device=dev)
+        sf = torch.empty(T, K // 128, dtype=torch.float32, device=dev)
+        P = torch.empty(rows_cap, K, dtype=torch.uint8, device=dev)
+        Psf = torch.empty(rows_cap, K // 128, dtype=torch.float32, device=dev)
+        names = ["moe_quant_act", "moe_route_pack", "gemm", "moe_unpermute_combine"]
+
+        def step(tm, s):
+            tm.mark(s, 0)
+            moe.moe_quant_act(x, q, sf)
+            tm.mark(s, 1)
+            moe.moe_route_pack(ids, E, layout, am, q, P, counts, seg, mi, oi, st, payload2=sf, packed2=Psf,
+                               workspace=ws)
+            tm.mark(s, 2)
+            moe.moe_grouped_gemm_fp8_fp4(layout | moe.WEIGHTS_PACKED, P, Psf, W4, SW, D, counts, seg, E, am_gemm, N, K,
+                                         em)
+            tm.mark(s, 3)
+            moe.moe_unpermute_combine(D, oi, tw, Z)
+            tm.mark(s, 4)
+    else:
+        W = torch.empty(E, N, K, dtype=torch.bfloat16, device=dev)
+        for e0 in range(0, E, 16):
+            W[e0:e0 + 16] = synth.expert_weights(cfg, N, K, experts=range(e0, min(E, e0 + 16)),
+                                                 stream=synth.STREAM_WEIGHTS, device=dev)
+        P = torch.empty(rows_cap, K, dtype=torch.bfloat16, device=dev)
+        names = ["moe_route_pack", "gemm", "moe_unpermute_combine"]
+
+        def step(tm, s):
+            tm.mark(s, 0)
+            moe.moe_route_pack(ids, E, layout, am, x, P, counts, seg, mi, oi, st, workspace=ws)
+            tm.mark(s, 1)
+            moe.moe_grouped_gemm_bf16(layout, P, W, D, counts, seg, E, am_gemm, N, K, em)
+            tm.mark(s, 2)
+            moe.moe_unpermute_combine(D, oi, tw, Z)
+            tm.mark(s, 3)
+    torch.cuda.synchronize()
+
+    class _L:  # what summarise reads of a layer
+        pass
+
+    layer = _L()
+    layer.counts = counts
+    return {"cfg": cfg, "layer": layer, "names": names, "step": step, "fmt": fmt}
+
+
+def summarise_variant(np, wl, ms_step, per, host_ms):
+    cfg, fmt = wl["cfg"], wl["fmt"]
+    E, K, N = cfg.E, cfg.K, cfg.N
+    counts = wl["layer"].counts.cpu().numpy().astype(np.int64)
+    rows_valid, active = int(counts.sum()), int((counts > 0).sum())
+    kern = {n: stats(v) for n, v in per.items()}
+    t = kern["gemm"]["mean"] / 1e3
+    flops = 2.0 * rows_valid * N * K
+    if fmt == "fp4":
+        nbytes = active * N * (K // 2 + K // 32) + rows_valid * (K + 4 * K // 128) + rows_valid * N * 2
+        peak_f, kernel = FP8_PEAK_TFLOPS, "moe_grouped_gemm_fp8_fp4"
+    else:
+        nbytes = active * N * K * 2 + rows_valid * K * 2 + rows_valid * N * 2
+        peak_f, kernel = BF16_PEAK_TFLOPS, "moe_grouped_gemm_bf16"
+    ridge = peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops / nbytes < ridge:
+        roof = {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
+    roof.update(frac=roof["achieved"] / roof["peak"], tflops=flops / t / 1e12, hbm_gbs=nbytes / t / 1e9,
+                flops_per_launch=flops, bytes_per_launch=nbytes, kernel=kernel, avg_launch_ms=kern["gemm"]["mean"],
+                median_launch_ms=kern["gemm"]["median"], min_launch_ms=kern["gemm"]["min"])
+    return {"ms_per_step": ms_step, "kernels_ms": kern, "roofline": roof, "dtype": "fp8xe2m1" if fmt == "fp4" else
+            "bf16", "config": {"workload": cfg.name, "weights": fmt, "T": cfg.T, "E": E, "topk": cfg.topk, "K": K,
+                               "N": N, "layout": cfg.layout, "rows_valid": rows_valid, "experts_active": active},
+            "host_enqueue_ms_per_step": host_ms}
+
+
 def time_workload(args, torch, wl, cycles_per_ms):
     """Warm-up, then exactly args.steps timed steps back to back; per-kernel event times of every step."""
     names, step = wl["names"], wl["step"]
@@ -477,6 +586,24 @@ def run(args):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
+    variants = {}
+    for v in ([] if args.variants in ("", "none") else args.variants.split(",")):
+        fmt, _, name = v.partition("_")
+        if fmt not in ("fp4", "bf16") or name not in WORKLOADS or synth.config_by_name(name).weights != "fp8":
+            raise SystemExit(f"unknown variant {v}")
+        t_setup = time.perf_counter()
+        wl = build_variant(args, fmt, synth.config_by_name(name), torch, np, moe, synth)
+        log(f"[bench] variant {v}: setup {time.perf_counter() - t_setup:.1f}s")
+        ms_step, per, host_ms = time_workload(args, torch, wl, cycles_per_ms)
+        res = summarise_variant(np, wl, ms_step, per, host_ms)
+        log(f"[bench] {v}: {ms_step:.3f} ms/step; " +
+            ", ".join(f"{n} {x['median']:.3f} ms" for n, x in res["kernels_ms"].items()) +
+            f"; GEMM {res['roofline']['frac'] * 100:.1f}% of the {res['roofline']['bound']} roofline")
+        variants[v] = res
+        del wl
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
     p = results[args.config]
     out = {
         "metric": METRIC,
@@ -500,6 +627,7 @@ def run(args):
     if "roofline_down" in p:
         out["roofline_down"] = p["roofline_down"]
     out["workloads"] = {n: {kk: v for kk, v in r.items()} for n, r in results.items() if n != args.config}
+    out["variants"] = variants
     print(json.dumps(out), flush=True)
 
 

@@ -14,8 +14,8 @@
  *   moe_unpermute_combine  topk_weights-weighted sum back to token order
  *
  * plus weight-preparation calls (moe_quant_weight_fp8 / _int4 / _fp4,
- * moe_pack_weight_fp8 / _int4) that turn bf16 expert weights into the formats
- * the GEMMs read.
+ * moe_pack_weight_fp8 / _int4 / _fp4) that turn bf16 expert weights into the
+ * formats the GEMMs read.
  *
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers owned by the caller.  The library
@@ -66,9 +66,10 @@ enum {
 
 enum { MOE_LAYOUT_CONTIGUOUS = 0, MOE_LAYOUT_MASKED = 1 };
 
-/* Flag ORed into the layout argument of moe_grouped_gemm_fp8 (and _int4): the
- * weights are in the fragment-packed order written by moe_pack_weight_fp8
- * (moe_pack_weight_int4) instead of row-major [E, N, K] ([E, N, K/2]). */
+/* Flag ORed into the layout argument of moe_grouped_gemm_fp8 (and _int4,
+ * _fp8_fp4): the weights are in the fragment-packed order written by
+ * moe_pack_weight_fp8 (moe_pack_weight_int4, moe_pack_weight_fp4) instead of
+ * row-major [E, N, K] ([E, N, K/2]). */
 enum { MOE_WEIGHTS_PACKED = 0x10 };
 
 enum { MOE_MAX_EXPERTS = 1024, MOE_MAX_TOPK = 64 };
@@ -313,6 +314,24 @@ moe_status moe_grouped_gemm_bf16(int layout,
 moe_status moe_quant_weight_fp4(const uint16_t* w, int E, int N, int K,
                                 uint8_t* w4, uint8_t* sw, void* stream);
 
+/* moe_pack_weight_fp4: reorder MXFP4 weights (moe_quant_weight_fp4's codes and
+ * E8M0 scales) into the fragment-packed orders the FP8 x FP4 grouped GEMM
+ * streams fastest (a layout prepared once, offline, as moe_pack_weight_fp8).
+ * Nothing is quantised or rounded: codes and scales are only permuted.
+ *   Codes: for expert e, step ks (128 K values), 16-column block cb and lane
+ *   L = c16 + 16*g (c16 in [0,16), g in [0,4)), the 16 bytes of column
+ *   16*cb + c16, K = 128*ks + 32*g .. +31 (row-major bytes
+ *   w4[e][n][64*ks + 16*g .. +15]) are stored at
+ *     w4_packed[e*N*K/2 + ((ks*(N/16) + cb)*64 + L)*16].
+ *   Scales: for expert e, step ks, 64-column group n64 and lane L, byte j of
+ *   the dword at sw_packed[e*N*K/32 + ((ks*(N/64) + n64)*64 + L)*4] is the
+ *   scale of column 64*n64 + 16*j + c16, block 4*ks + g:
+ *     sw_packed[... + j] = sw[e][64*n64 + 16*j + c16][4*ks + g],   j in [0,4).
+ *   Requires N % 128 == 0 and K % 128 == 0; codes 16-byte aligned, scales
+ *   4-byte aligned; outputs must not overlap any buffer. */
+moe_status moe_pack_weight_fp4(const uint8_t* w4, const uint8_t* sw, int E, int N, int K,
+                               uint8_t* w4_packed, uint8_t* sw_packed, void* stream);
+
 /* moe_grouped_gemm_fp8_fp4: FP8 activations x MXFP4 weights grouped GEMM
  * (AsymGEMM README, "API Reference": FP4 m_grouped contiguous and masked
  * grouped GEMMs; nxmr.cn DeepGEMM article, "精度与吞吐的平衡点": a product with
@@ -327,8 +346,8 @@ moe_status moe_quant_weight_fp4(const uint16_t* w, int E, int N, int K,
  *     D [rows, N] bf16.
  *   Layout, counts, seg_offsets, expected_m, the rows of D that are written,
  *   alignment (SFA and SW 4-byte aligned) and size limits as for
- *   moe_grouped_gemm_fp8 (no packed order: layout must be
- *   MOE_LAYOUT_CONTIGUOUS or MOE_LAYOUT_MASKED). */
+ *   moe_grouped_gemm_fp8.  layout | MOE_WEIGHTS_PACKED: W4 and SW in the
+ *   orders written by moe_pack_weight_fp4. */
 moe_status moe_grouped_gemm_fp8_fp4(int layout,
                                     const uint8_t* A, const float* SFA,
                                     const uint8_t* W4, const uint8_t* SW,

@@ -52,6 +52,7 @@ SIGNATURES = {
     "moe_grouped_gemm_bf16": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                        ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_quant_weight_fp4": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_pack_weight_fp4": (_c_i32, [_vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
     "moe_grouped_gemm_fp8_fp4": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_unpermute_combine": (_c_i32, [_vp, _c_i64, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
@@ -294,6 +295,18 @@ def moe_quant_weight_fp4(w, w4, sw, stream=None):
     if tuple(w4.shape) != (E, N, K // 2) or tuple(sw.shape) != (E, N, K // 32):
         raise ValueError("moe_quant_weight_fp4: shape mismatch")
     _check(load().moe_quant_weight_fp4(_ptr(w), E, N, K, _ptr(w4), _ptr(sw), _stream(stream)), "moe_quant_weight_fp4")
+
+
+def moe_pack_weight_fp4(w4, sw, w4_packed, sw_packed, stream=None):
+    """MXFP4 codes uint8 [E, N, K/2] and scales uint8 [E, N, K/32] -> the packed orders, same shapes."""
+    _dev(w4, "w4", torch.uint8, 3), _dev(sw, "sw", torch.uint8, 3)
+    _dev(w4_packed, "w4_packed", torch.uint8, 3), _dev(sw_packed, "sw_packed", torch.uint8, 3)
+    E, N, K2 = w4.shape
+    if tuple(w4_packed.shape) != (E, N, K2) or tuple(sw.shape) != (E, N, K2 // 16) or \
+            tuple(sw_packed.shape) != (E, N, K2 // 16):
+        raise ValueError("moe_pack_weight_fp4: shape mismatch")
+    _check(load().moe_pack_weight_fp4(_ptr(w4), _ptr(sw), E, N, 2 * K2, _ptr(w4_packed), _ptr(sw_packed),
+                                      _stream(stream)), "moe_pack_weight_fp4")
 
 
 def moe_grouped_gemm_fp8_fp4(layout: int, A, SFA, W4, SW, D, counts, seg_offsets, E: int, rows_cap_or_max_m: int,

@@ -387,11 +387,36 @@ moe_status moe_quant_weight_fp4(const uint16_t* w, int E, int N, int K, uint8_t*
   return hip_status(launch_quant_weight_fp4(w, E, N, K, w4, sw, (hipStream_t)stream), "moe_quant_weight_fp4");
 }
 
+moe_status moe_pack_weight_fp4(const uint8_t* w4, const uint8_t* sw, int E, int N, int K, uint8_t* w4_packed,
+                               uint8_t* sw_packed, void* stream) {
+  g_err[0] = 0;
+  if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_pack_weight_fp4: E=%d N=%d K=%d", E, N, K);
+  if (N % 128 || K % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_weight_fp4: N=%d and K=%d must be multiples of 128", N, K);
+  if ((int64_t)N * K / 2 > 0xffffffffll) return fail(MOE_ERR_UNSUPPORTED, "moe_pack_weight_fp4: one expert exceeds 4 GiB");
+  if (E == 0) return MOE_OK;
+  if (!w4 || !sw || !w4_packed || !sw_packed) return fail(MOE_ERR_NULL, "moe_pack_weight_fp4: null pointer");
+  if (!aligned(w4, 16) || !aligned(w4_packed, 16) || !aligned(sw, 4) || !aligned(sw_packed, 4))
+    return fail(MOE_ERR_ALIGN, "moe_pack_weight_fp4: codes must be 16-byte aligned, scales 4-byte aligned");
+  const uint8_t* ranges[4][2] = {{w4, w4 + (int64_t)E * N * (K / 2)},
+                                 {sw, sw + (int64_t)E * N * (K / 32)},
+                                 {w4_packed, w4_packed + (int64_t)E * N * (K / 2)},
+                                 {sw_packed, sw_packed + (int64_t)E * N * (K / 32)}};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if ((i >= 2 || j >= 2) && ranges[i][0] < ranges[j][1] && ranges[j][0] < ranges[i][1])
+        return fail(MOE_ERR_SHAPE, "moe_pack_weight_fp4: an output overlaps another buffer");
+  return hip_status(launch_pack_weight_fp4(w4, sw, E, N, K, w4_packed, sw_packed, (hipStream_t)stream),
+                    "moe_pack_weight_fp4");
+}
+
 moe_status moe_grouped_gemm_fp8_fp4(int layout, const uint8_t* A, const float* SFA, const uint8_t* W4,
                                     const uint8_t* SW, uint16_t* D, const int32_t* counts,
                                     const int32_t* seg_offsets, int E, int64_t rows_cap_or_max_m, int N, int K,
                                     int expected_m, void* stream) {
   g_err[0] = 0;
+  const int wpacked = (layout & MOE_WEIGHTS_PACKED) ? 1 : 0;
+  layout &= ~MOE_WEIGHTS_PACKED;
   moe_status st = check_gemm("moe_grouped_gemm_fp8_fp4", layout, A, W4, SW, D, counts, seg_offsets, E,
                              rows_cap_or_max_m, N, K);
   if (st) return st;
@@ -412,7 +437,7 @@ moe_status moe_grouped_gemm_fp8_fp4(int layout, const uint8_t* A, const float* S
   a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
   a.N = N;
   a.K = K;
-  a.wpacked = 0;
+  a.wpacked = wpacked;
   return hip_status(launch_gemm_fp4(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_fp8_fp4");
 }
 

@@ -25,8 +25,12 @@
 //  * weights stream from HBM into an S-deep register ring (16 bytes of codes
 //    and one scale dword per lane and 16-column block), activations and their
 //    row scales through two XOR-swizzled LDS slots as in the FP8 kernel;
-//  * the scale dword holds the scales of the 4 blocks of the step; a lane
-//    shifts its own byte down (one VALU operation per block and step).
+//  * packed weights (moe_pack_weight_fp4, the form the benchmark uses): each
+//    load instruction reads one contiguous 1 KB fragment of codes, and one
+//    256-byte load per step gives every lane a dword with its scales for the
+//    wave's four 16-column blocks, the matrix instruction's op_sel picking the
+//    block's byte; row-major weights read 64 bytes of each of 16 columns per
+//    instruction and a lane shifts its byte out of the block's scale dword.
 #include "gemm_common.h"
 
 namespace moe {
@@ -47,7 +51,7 @@ struct Fp4Smem {
   float sa[2][256];  // row scales of the stage (one per lane of the 4 waves)
 };
 
-template <int RB, int S, int RBE>
+template <int RB, int S, int RBE, bool PACKED>
 __device__ __forceinline__ void fp4_unit(const GemmArgs& a, const Unit& u, Fp4Smem<RB, S>& sm, int wv, int lane) {
   using C = Fp4Cfg<RB, S>;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -57,6 +61,9 @@ __device__ __forceinline__ void fp4_unit(const GemmArgs& a, const Unit& u, Fp4Sm
 
   // weights: column n's step ks is 64 bytes at n*K/2 + 64 ks, the lane's 16 at + 16 lg; its scale dword (the
   // step's 4 blocks) at n*K/32 + 4 ks of the scale bytes
+  // Packed (moe_pack_weight_fp4): the step's 16-column block cb is 1 KB at ((ks*(N/16) + cb)*64 + lane)*16, and
+  // the step's scales of the wave's 64 columns are one dword per lane at ((ks*(N/64) + n/64)*64 + lane)*4, the
+  // block of column block cb in byte cb.
   const uint8_t* wbase = a.W + (int64_t)u.e * N * (K / 2);
   const uint8_t* sbase = (const uint8_t*)a.SW + (int64_t)u.e * N * (K / 32);
   uint32_t woff[4], soff[4];
@@ -64,9 +71,16 @@ __device__ __forceinline__ void fp4_unit(const GemmArgs& a, const Unit& u, Fp4Sm
   for (int cb = 0; cb < 4; ++cb) {
     int n = ncol0 + 16 * cb + l16;
     if (n >= N) n = N - 1;  // an idle wave re-reads valid columns and stores nothing
-    woff[cb] = (uint32_t)n * (uint32_t)(K / 2) + 16u * lg;
-    soff[cb] = (uint32_t)n * (uint32_t)(K / 32);
+    if constexpr (PACKED) {
+      woff[cb] = ((uint32_t)(n / 16) * 64u + (uint32_t)lane) * 16u;
+      soff[cb] = ((uint32_t)(n / 64) * 64u + (uint32_t)lane) * 4u;  // the same for the 4 blocks
+    } else {
+      woff[cb] = (uint32_t)n * (uint32_t)(K / 2) + 16u * lg;
+      soff[cb] = (uint32_t)n * (uint32_t)(K / 32);
+    }
   }
+  const uint32_t wstep = PACKED ? (uint32_t)N * 64u : 64u;     // code bytes between steps
+  const uint32_t sstep = (uint32_t)N * 4u;                     // packed scale bytes between steps
   const int sshift = 8 * lg;
   const uint8_t* abase = a.A + (int64_t)u.row0 * K;
   uint32_t aoff[C::kApw];
@@ -99,12 +113,16 @@ __device__ __forceinline__ void fp4_unit(const GemmArgs& a, const Unit& u, Fp4Sm
     const int ks = min(ks_req, KB - 1);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const v4i* wp = (const v4i*)(wbase + (woff[cb] + (uint32_t)ks * 64u));
-      if constexpr (RB == 1)
-        wq[slot][cb] = __builtin_nontemporal_load(wp);  // decode: each weight byte is read once
+      const v4i* wp = (const v4i*)(wbase + (woff[cb] + (uint32_t)ks * wstep));
+      if constexpr (RB == 1 && PACKED)
+        wq[slot][cb] = __builtin_nontemporal_load(wp);  // decode, whole lines: each weight byte is read once
       else
         wq[slot][cb] = *wp;
-      sq[slot][cb] = *(const uint32_t*)(sbase + (soff[cb] + 4u * (uint32_t)ks));
+      if constexpr (PACKED) {
+        if (cb == 0) sq[slot][0] = *(const uint32_t*)(sbase + (soff[0] + (uint32_t)ks * sstep));
+      } else {
+        sq[slot][cb] = *(const uint32_t*)(sbase + (soff[cb] + 4u * (uint32_t)ks));
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::kApw; ++i) ar[slot][i] = *(const v4i*)(abase + (aoff[i] + (uint32_t)ks * 128u));
@@ -123,21 +141,24 @@ __device__ __forceinline__ void fp4_unit(const GemmArgs& a, const Unit& u, Fp4Sm
     constexpr int slot = decltype(slot_c)::value;
     const uint8_t* ab = &sm.a[ks & 1][0];
     const float* sab = &sm.sa[ks & 1][l16];
+    // scale of the lane's block: packed, byte cb of the step's dword (op_sel); otherwise the lane's byte of
+    // the block's dword, shifted down
     int swe[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) swe[cb] = (int)((sq[slot][cb] >> sshift) & 0xffu);
+    for (int cb = 0; cb < 4; ++cb) swe[cb] = PACKED ? (int)sq[slot][0] : (int)((sq[slot][cb] >> sshift) & 0xffu);
 #pragma unroll
     for (int rb = 0; rb < RBE; ++rb) {
       const v4i x0 = *(const v4i*)(ab + off0 + rb * 2048);
       const v4i x1 = *(const v4i*)(ab + off1 + rb * 2048);
       const v8i af = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       const int sae = (int)(__float_as_uint(sab[16 * rb]) >> 23);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      static_for<0, 4>([&](auto cb_c) {
+        constexpr int cb = decltype(cb_c)::value;
         const v4i w = wq[slot][cb];
         const v8i wf = v8i{w[0], w[1], w[2], w[3], 0, 0, 0, 0};  // E2M1: the instruction reads 4 registers
-        acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, af, acc[rb][cb], 4, 0, 0, swe[cb], 0, sae);
-      }
+        acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, af, acc[rb][cb], 4, 0, PACKED ? cb : 0,
+                                                                       swe[cb], 0, sae);
+      });
     }
   };
 
@@ -177,7 +198,7 @@ __device__ __forceinline__ void fp4_unit(const GemmArgs& a, const Unit& u, Fp4Sm
   }
 }
 
-template <int RB, int S>
+template <int RB, int S, bool PACKED>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(const GemmArgs a) {
   using C = Fp4Cfg<RB, S>;
   __shared__ __attribute__((aligned(1024))) Fp4Smem<RB, S> sm;
@@ -190,24 +211,28 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(const GemmArgs a) {
   constexpr int RH = (RB + 1) / 2;
   for (int v = walk.first; v < walk.end; v += walk.stride) {
     const Unit u = sched_unit<C::BM>(a, sc, v);
-    if (RB > 1 && u.mrows <= 16 * RH) fp4_unit<RB, S, RH>(a, u, sm, wv, lane);
-    else fp4_unit<RB, S, RB>(a, u, sm, wv, lane);
+    if (RB > 1 && u.mrows <= 16 * RH) fp4_unit<RB, S, RH, PACKED>(a, u, sm, wv, lane);
+    else fp4_unit<RB, S, RB, PACKED>(a, u, sm, wv, lane);
   }
 }
 
-template <int RB, int S>
+template <int RB, int S, bool PACKED>
 static hipError_t launch_fp4(const GemmArgs& a, hipStream_t s) {
   const int cus = device_info().cus;
   int grid = cus - cus % kXcds;
   if (grid < kXcds) grid = kXcds;
-  gemm_fp4_kernel<RB, S><<<grid, 256, 0, s>>>(a);
+  gemm_fp4_kernel<RB, S, PACKED><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_fp4(const GemmArgs& a, int expected_m, hipStream_t s) {
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 64);
-  if (em <= 16) return launch_fp4<1, 8>(a, s);
-  return launch_fp4<4, 6>(a, s);
+  if (a.wpacked) {
+    if (em <= 16) return launch_fp4<1, 8, true>(a, s);
+    return launch_fp4<4, 6, true>(a, s);
+  }
+  if (em <= 16) return launch_fp4<1, 8, false>(a, s);
+  return launch_fp4<4, 6, false>(a, s);
 }
 
 // ------------------------------------------------------------------ weights --
@@ -266,6 +291,57 @@ __global__ __launch_bounds__(256) void quant_weight_fp4_kernel(const uint16_t* _
     *(v4i*)(w4 + b * 16) = v4i{(int)out[0], (int)out[1], (int)out[2], (int)out[3]};
     sw[b] = (uint8_t)(e + 127);
   }
+}
+
+// Fragment-packed MXFP4 order (moe_pack_weight_fp4): one thread per 16-byte output chunk of codes, then one
+// per output scale dword.  A permutation of bytes; run once when weights are prepared.
+__global__ __launch_bounds__(256) void pack_weight_fp4_kernel(const uint8_t* __restrict__ w4, const uint8_t* __restrict__ sw,
+                                                              int E, int N, int K, uint8_t* __restrict__ w4p,
+                                                              uint8_t* __restrict__ swp) {
+  const int ncb = N / 16, n64 = N / 64, kb = K / 128;
+  const int64_t cchunks = (int64_t)E * kb * ncb * 64;  // 16-byte code chunks
+  const int64_t sdwords = (int64_t)E * kb * n64 * 64;  // scale dwords
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < cchunks + sdwords;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    if (c < cchunks) {
+      // chunk ((e*kb + ks)*ncb + cb)*64 + L: column 16cb + L%16, K 128ks + 32(L/16) .. +31
+      const int L = (int)(c & 63);
+      int64_t r = c >> 6;
+      const int cb = (int)(r % ncb);
+      r /= ncb;
+      const int ks = (int)(r % kb);
+      const int64_t e = r / kb;
+      const int64_t n = 16 * cb + (L & 15);
+      const v4i v = *(const v4i*)(w4 + (e * N + n) * (K / 2) + 64 * ks + 16 * (L >> 4));
+      *(v4i*)(w4p + c * 16) = v;
+    } else {
+      // dword ((e*kb + ks)*n64 + g64)*64 + L: byte j = scale of column 64 g64 + 16 j + L%16, block 4 ks + L/16
+      const int64_t d = c - cchunks;
+      const int L = (int)(d & 63);
+      int64_t r = d >> 6;
+      const int g64 = (int)(r % n64);
+      r /= n64;
+      const int ks = (int)(r % kb);
+      const int64_t e = r / kb;
+      const int64_t n0 = 64 * g64 + (L & 15);
+      const uint8_t* src = sw + (e * N + n0) * (K / 32) + 4 * ks + (L >> 4);
+      const int64_t cs = 16 * (int64_t)(K / 32);  // 16 columns further
+      const uint32_t v = (uint32_t)src[0] | ((uint32_t)src[cs] << 8) | ((uint32_t)src[2 * cs] << 16) |
+                         ((uint32_t)src[3 * cs] << 24);
+      *(uint32_t*)(swp + d * 4) = v;
+    }
+  }
+}
+
+hipError_t launch_pack_weight_fp4(const uint8_t* w4, const uint8_t* sw, int E, int N, int K, uint8_t* w4p,
+                                  uint8_t* swp, hipStream_t s) {
+  const int64_t work = (int64_t)E * (K / 128) * ((N / 16) * 64 + (N / 64) * 64);
+  if (work == 0) return hipSuccess;
+  int64_t grid = (work + 255) / 256;
+  const int64_t cap = (int64_t)device_info().cus * 8;
+  if (grid > cap) grid = cap;
+  pack_weight_fp4_kernel<<<(unsigned)grid, 256, 0, s>>>(w4, sw, E, N, K, w4p, swp);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_weight_fp4(const uint16_t* w, int E, int N, int K, uint8_t* w4, uint8_t* sw, hipStream_t s) {

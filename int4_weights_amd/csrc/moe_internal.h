@@ -70,6 +70,8 @@ hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_fp4(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_quant_weight_fp4(const uint16_t* w, int E, int N, int K, uint8_t* w4, uint8_t* sw, hipStream_t s);
+hipError_t launch_pack_weight_fp4(const uint8_t* w4, const uint8_t* sw, int E, int N, int K, uint8_t* w4p,
+                                  uint8_t* swp, hipStream_t s);
 
 struct SwigluArgs {
   const uint16_t* gu;    // bf16 [rows, 2I]: gate columns then up columns

@@ -169,12 +169,23 @@ def test_host_validation_rejects_without_launching(lib):
 
     assert g4(N=200) == MOE_ERR_UNSUPPORTED
     assert g4(K=192) == MOE_ERR_UNSUPPORTED
-    assert g4(layout=0x10) == MOE_ERR_SHAPE
+    assert g4(layout=0x10 | 7) == MOE_ERR_SHAPE         # the packed-weights flag does not make a layout valid
     assert g4(seg=0) == MOE_ERR_NULL
     assert g4(SFA=0) == MOE_ERR_NULL
     assert g4(SW=0) == MOE_ERR_NULL
     assert g4(SW=A16 + 2) == MOE_ERR_ALIGN
     assert g4(A=A16 + 8) == MOE_ERR_ALIGN
+    def pf4(q=A16, sc=A16 << 2, E=2, N=128, K=512, qo=A16 << 4, so=A16 << 6):
+        return lib.moe_pack_weight_fp4(_p(q) if q else None, _p(sc) if sc else None, E, N, K, _p(qo) if qo else None,
+                                       _p(so) if so else None, None)
+
+    assert pf4(K=320) == MOE_ERR_UNSUPPORTED
+    assert pf4(N=100) == MOE_ERR_UNSUPPORTED
+    assert pf4(qo=A16 + 8) == MOE_ERR_ALIGN
+    assert pf4(so=(A16 << 6) + 2) == MOE_ERR_ALIGN
+    assert pf4(sc=0) == MOE_ERR_NULL
+    assert pf4(qo=A16 + 4096) == MOE_ERR_SHAPE        # codes out overlap codes in
+    assert pf4(q=0, sc=0, E=0, qo=0, so=0) == MOE_OK
     assert lib.moe_quant_weight_fp4(_p(A16), 2, 128, 100, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
     assert lib.moe_quant_weight_fp4(_p(A16 + 8), 2, 128, 128, _p(A16), _p(A16), None) == MOE_ERR_ALIGN
     assert lib.moe_quant_weight_fp4(None, 2, 128, 128, _p(A16), _p(A16), None) == MOE_ERR_NULL

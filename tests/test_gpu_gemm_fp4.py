@@ -16,6 +16,7 @@ import torch
 
 import int4_weights_amd as moe
 import oracle
+import weight_layout as wl
 from gpu_helpers import DEV, bf16_from_u16, gemm_tolerance_check, require_gpu, u16
 
 pytestmark = pytest.mark.gpu
@@ -74,11 +75,18 @@ def _case(seed, counts, N, K, layout, max_m=0, ints=False):
                 max_m=max_m, a=a, sa=sa, w4=w4, sw=sw)
 
 
-def _run(c, expected_m=0):
+def _run(c, expected_m=0, packed=False):
+    """packed: the weights go in the test helper's packed order with MOE_WEIGHTS_PACKED."""
     D = torch.full((c["rows"], c["N"]), SENT, dtype=torch.int16, device=DEV).view(torch.bfloat16)
     am = c["max_m"] if c["layout"] == moe.LAYOUT_MASKED else c["rows"]
-    moe.moe_grouped_gemm_fp8_fp4(c["layout"], torch.from_numpy(c["a"]).to(DEV), torch.from_numpy(c["sa"]).to(DEV),
-                                 torch.from_numpy(c["w4"]).to(DEV), torch.from_numpy(c["sw"]).to(DEV), D,
+    w4, sw = c["w4"], c["sw"]
+    if packed:
+        w4, sw = wl.pack_weight_fp4(w4, sw)
+        w4, sw = w4.reshape(c["w4"].shape), sw.reshape(c["sw"].shape)
+    layout = c["layout"] | (moe.WEIGHTS_PACKED if packed else 0)
+    moe.moe_grouped_gemm_fp8_fp4(layout, torch.from_numpy(c["a"]).to(DEV), torch.from_numpy(c["sa"]).to(DEV),
+                                 torch.from_numpy(np.ascontiguousarray(w4)).to(DEV),
+                                 torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), D,
                                  torch.from_numpy(c["counts"]).to(DEV),
                                  torch.from_numpy(c["starts"].astype(np.int32)).to(DEV), c["E"], am, c["N"], c["K"],
                                  expected_m)
@@ -102,8 +110,10 @@ def _check(c, D, exact=False):
     gemm_tolerance_check(oracle.bf16_bits_to_f64(bits[valid]), ref[valid], 1e-3)
 
 
-def test_fp4_one_hot_rows_pin_the_operand_layout():
-    """Row r has one activation 2.0 at k_r (scale 1): D[r] = 2 * column k_r of the dequantised weights, exactly."""
+@pytest.mark.parametrize("packed", [False, True])
+def test_fp4_one_hot_rows_pin_the_operand_layout(packed):
+    """Row r has one activation 2.0 at k_r (scale 1): D[r] = 2 * column k_r of the dequantised weights, exactly
+    (packed: also pins which byte of the scale dword each step's instruction selects)."""
     require_gpu()
     c = _case(2, [40], N=256, K=512, layout=moe.LAYOUT_CONTIGUOUS)
     ks = [0, 1, 2, 31, 32, 33, 63, 64, 95, 127, 128, 129, 200, 255, 300, 383, 384, 447, 510, 511] + list(range(3, 23))
@@ -111,7 +121,7 @@ def test_fp4_one_hot_rows_pin_the_operand_layout():
     c["sa"][:] = 1.0
     for r, k in enumerate(ks[:40]):
         c["a"][r, k] = 0x40
-    D = _run(c, 64)
+    D = _run(c, 64, packed)
     bits = u16(D)[:40]
     wd = oracle.dequant_weight_fp4(c["w4"][0], c["sw"][0])
     for r, k in enumerate(ks[:40]):
@@ -121,27 +131,45 @@ def test_fp4_one_hot_rows_pin_the_operand_layout():
         assert np.array_equal(oracle.bf16_bits_to_f64(bits[r]), want), f"row {r}, k {k}"
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("expected_m", [0, 16, 64])
-def test_fp4_contiguous_ragged(expected_m):
+def test_fp4_contiguous_ragged(expected_m, packed):
     require_gpu()
     c = _case(3, [0, 1, 17, 130, 300], N=384, K=1536, layout=moe.LAYOUT_CONTIGUOUS)
-    _check(c, _run(c, expected_m))
+    _check(c, _run(c, expected_m, packed))
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("expected_m", [0, 16])
-def test_fp4_masked_clipped(expected_m):
+def test_fp4_masked_clipped(expected_m, packed):
     require_gpu()
     c = _case(4, [5, 0, 64, 90, 1, 33], N=256, K=768, layout=moe.LAYOUT_MASKED, max_m=64)
-    _check(c, _run(c, expected_m))
+    _check(c, _run(c, expected_m, packed))
 
 
-def test_fp4_small_integers_exact_and_deterministic():
+def test_pack_weight_fp4_matches_the_layout_definition():
     require_gpu()
-    c = _case(5, [7, 64, 129], N=512, K=256, layout=moe.LAYOUT_CONTIGUOUS, ints=True)
-    D = _run(c, 64)
+    rng = np.random.default_rng(8)
+    E, N, K = 3, 256, 896
+    w4 = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    sw = rng.integers(0, 255, (E, N, K // 32), dtype=np.uint8)
+    w4p = torch.empty(E, N, K // 2, dtype=torch.uint8, device=DEV)
+    swp = torch.empty(E, N, K // 32, dtype=torch.uint8, device=DEV)
+    moe.moe_pack_weight_fp4(torch.from_numpy(w4).to(DEV), torch.from_numpy(sw).to(DEV), w4p, swp)
+    torch.cuda.synchronize()
+    cw, cs = wl.pack_weight_fp4(w4, sw)
+    assert np.array_equal(w4p.cpu().numpy().reshape(E, -1), cw)
+    assert np.array_equal(swp.cpu().numpy().reshape(E, -1), cs)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_fp4_small_integers_exact_and_deterministic(packed):
+    require_gpu()
+    c = _case(5, [7, 64, 129], N=512, K=512, layout=moe.LAYOUT_CONTIGUOUS, ints=True)
+    D = _run(c, 64, packed)
     _check(c, D, exact=True)
     for _ in range(20):
-        assert torch.equal(_run(c, 64), D)
+        assert torch.equal(_run(c, 64, packed), D)
 
 
 def test_fp4_full_size_dsv3_decode_and_prefill_samples():
@@ -180,7 +208,10 @@ def test_fp4_full_size_dsv3_decode_and_prefill_samples():
                     kept[e] = u16(w[i])
             del w
         D = torch.full((rows, N), SENT, dtype=torch.int16, device=DEV).view(torch.bfloat16)
-        moe.moe_grouped_gemm_fp8_fp4(moe.LAYOUT_MASKED if lay == "masked" else moe.LAYOUT_CONTIGUOUS, A, SFA, W4, SW,
+        W4p, SWp = torch.empty_like(W4), torch.empty_like(SW)
+        moe.moe_pack_weight_fp4(W4, SW, W4p, SWp)  # the benchmark's weight order
+        moe.moe_grouped_gemm_fp8_fp4((moe.LAYOUT_MASKED if lay == "masked" else moe.LAYOUT_CONTIGUOUS) |
+                                     moe.WEIGHTS_PACKED, A, SFA, W4p, SWp,
                                      D, torch.from_numpy(counts.astype(np.int32)).to(DEV),
                                      torch.from_numpy(r["seg_offsets"].astype(np.int32)).to(DEV), E,
                                      am if lay == "masked" else rows, N, K, max(1, cfg.T * cfg.topk // E))
@@ -201,5 +232,5 @@ def test_fp4_full_size_dsv3_decode_and_prefill_samples():
             # the FP8 x FP4 product against the unquantised bf16 inputs: the pages' one-FP4-side bar
             raw = oracle.bf16_bits_to_f64(u16(x[sel])) @ oracle.bf16_bits_to_f64(kept[e][cols]).T
             assert oracle.calc_diff(got, raw) < 1e-2
-        del W4, SW, D, A, x
+        del W4, SW, W4p, SWp, D, A, x
         torch.cuda.empty_cache()

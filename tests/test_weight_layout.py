@@ -75,3 +75,38 @@ def test_int4_dword_holds_natural_pairs_after_shift_and_mask():
                 assert (lo, hi) == ((k0 + 2 * i) % 16, (k0 + 2 * i + 1) % 16)
     # scales: column 37 is in 64-column slice 0, c = 5, cb = 2
     assert wl.packed_scale_offset_int4(37, 1, N) == ((1 * 2 + 0) * 16 + 5) * 4 + 2
+
+
+@pytest.mark.parametrize("E,N,K", [(1, 128, 384), (2, 256, 1024)])
+def test_fp4_pack_matches_scalar_offsets_everywhere(E, N, K):
+    rng = np.random.default_rng(N + K + 1)
+    w4 = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    sw = rng.integers(0, 255, size=(E, N, K // 32), dtype=np.uint8)
+    codes, scales = wl.pack_weight_fp4(w4, sw)
+    pos = np.array([[2 * o + h for o, h in (wl.packed_code_offset_fp4(n, k, N),)] for n in range(N) for k in range(K)])
+    assert np.array_equal(np.sort(pos.reshape(-1)), np.arange(N * K))
+    soff = np.array([[wl.packed_scale_offset_fp4(n, b, N) for b in range(K // 32)] for n in range(N)])
+    assert np.array_equal(np.sort(soff.reshape(-1)), np.arange(N * K // 32))
+    for e in range(E):
+        flat = np.empty(N * K, np.uint8)
+        flat[0::2] = codes[e] & 15
+        flat[1::2] = codes[e] >> 4
+        want = np.empty((N, K), np.uint8)
+        want[:, 0::2] = w4[e] & 15
+        want[:, 1::2] = w4[e] >> 4
+        assert np.array_equal(flat[pos.reshape(-1)], want.reshape(-1))
+        assert np.array_equal(scales[e][soff], sw[e])
+
+
+def test_fp4_pack_hand_decoded_lane():
+    """Lane L = 5 + 16*2 of block cb = 3 in step 1: column 53, K 128 + 64 .. 128 + 95; its scale dword in step 1,
+    64-column group 0, holds block 4*1 + 2 of columns 5, 21, 37, 53."""
+    N, K = 128, 512
+    w4 = np.arange(N * K // 2, dtype=np.int64).reshape(1, N, K // 2).astype(np.uint8)
+    sw = (np.arange(N * K // 32, dtype=np.int64).reshape(1, N, K // 32) % 251).astype(np.uint8)
+    codes, scales = wl.pack_weight_fp4(w4, sw)
+    L = 5 + 16 * 2
+    off = ((1 * (N // 16) + 3) * 64 + L) * 16
+    assert np.array_equal(codes[0, off:off + 16], w4[0, 53, 64 + 32:64 + 48])
+    soff = ((1 * (N // 64) + 0) * 64 + L) * 4
+    assert list(scales[0, soff:soff + 4]) == [int(sw[0, 5 + 16 * j, 4 * 1 + 2]) for j in range(4)]

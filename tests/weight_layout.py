@@ -136,3 +136,43 @@ def unpack_weight_int4(packed: np.ndarray, N: int, K: int) -> np.ndarray:
     x = x[..., inv]                                       # p -> j
     w = x.transpose(0, 2, 4, 1, 5, 3, 6).reshape(E, N, K)  # e, cb, c, g, d, h, j
     return (w[..., 0::2] | (w[..., 1::2] << 4)).astype(np.uint8)
+
+
+# ------------------------------------------------------------------------------------------------ MXFP4 --
+# moe_pack_weight_fp4 (include/moe.h): codes [E, N, K/2] and E8M0 scales [E, N, K/32] are permuted so that, per
+# step ks of 128 K values and 16-column block cb, lane L = c + 16g (c < 16, g < 4) finds its 16 bytes of codes
+# (column 16cb + c, K 128ks + 32g .. +31) at ((ks*(N/16) + cb)*64 + L)*16, and per step and 64-column group n64
+# one dword at ((ks*(N/64) + n64)*64 + L)*4 whose byte j is the scale of column 64 n64 + 16 j + c, block 4 ks + g.
+
+
+def pack_weight_fp4(w4: np.ndarray, sw: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """uint8 codes [E, N, K/2] and scales [E, N, K/32] -> packed orders (uint8 [E, N*K/2], uint8 [E, N*K/32])."""
+    w4 = np.asarray(w4, dtype=np.uint8)
+    sw = np.asarray(sw, dtype=np.uint8)
+    E, N, K2 = w4.shape
+    K = 2 * K2
+    if N % 128 or K % 128:
+        raise ValueError("N and K must be multiples of 128")
+    # codes: axes e, cb, c, ks, g, bytes(16) -> e, ks, cb, g, c, bytes
+    x = w4.reshape(E, N // 16, 16, K // 128, 4, 16)
+    codes = np.ascontiguousarray(x.transpose(0, 3, 1, 4, 2, 5)).reshape(E, N * K2)
+    # scales: n = 64 n64 + 16 j + c, block b = 4 ks + g: axes e, n64, j, c, ks, g -> e, ks, n64, g, c, j
+    y = sw.reshape(E, N // 64, 4, 16, K // 128, 4)
+    scales = np.ascontiguousarray(y.transpose(0, 4, 1, 5, 3, 2)).reshape(E, N * K // 32)
+    return codes, scales
+
+
+def packed_code_offset_fp4(n: int, k: int, N: int) -> tuple[int, int]:
+    """(byte offset within one expert, nibble 0 = low) of the code of weight (n, k) in the packed order."""
+    ks, kk = divmod(k, 128)
+    g, j = divmod(kk, 32)
+    cb, c = divmod(n, 16)
+    return ((ks * (N // 16) + cb) * 64 + c + 16 * g) * 16 + j // 2, j % 2
+
+
+def packed_scale_offset_fp4(n: int, b: int, N: int) -> int:
+    """Byte offset (within one expert) of the scale of column n, 32-value block b, in the packed order."""
+    ks, g = divmod(b, 4)
+    n64, r = divmod(n, 64)
+    j, c = divmod(r, 16)
+    return ((ks * (N // 64) + n64) * 64 + c + 16 * g) * 4 + j
