@@ -80,6 +80,10 @@ KERNEL_SOURCES = {
                              "csrc/moe_internal.h", "build.py"],
     "moe_grouped_gemm_int4": ["csrc/gemm_int4.hip", "csrc/gemm_common.h", "csrc/moe_device.h", "csrc/moe_internal.h",
                               "build.py"],
+    "moe_grouped_gemm_fp8_fp4": ["csrc/gemm_fp4.hip", "csrc/gemm_common.h", "csrc/moe_device.h",
+                                 "csrc/moe_internal.h", "build.py"],
+    "moe_grouped_gemm_bf16": ["csrc/gemm_bf16.hip", "csrc/gemm_common.h", "csrc/moe_device.h", "csrc/moe_internal.h",
+                              "build.py"],
 }
 
 
@@ -430,7 +434,8 @@ def summarise_variant(np, wl, ms_step, per, host_ms):
         roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
     roof.update(frac=roof["achieved"] / roof["peak"], tflops=flops / t / 1e12, hbm_gbs=nbytes / t / 1e9,
                 flops_per_launch=flops, bytes_per_launch=nbytes, kernel=kernel, avg_launch_ms=kern["gemm"]["mean"],
-                median_launch_ms=kern["gemm"]["median"], min_launch_ms=kern["gemm"]["min"])
+                median_launch_ms=kern["gemm"]["median"], min_launch_ms=kern["gemm"]["min"],
+                traffic=measured_traffic(kernel, f"{fmt}_{cfg.name}"))
     return {"ms_per_step": ms_step, "kernels_ms": kern, "roofline": roof, "dtype": "fp8xe2m1" if fmt == "fp4" else
             "bf16", "config": {"workload": cfg.name, "weights": fmt, "T": cfg.T, "E": E, "topk": cfg.topk, "K": K,
                                "N": N, "layout": cfg.layout, "rows_valid": rows_valid, "experts_active": active},
