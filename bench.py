@@ -83,7 +83,7 @@ KERNEL_SOURCES = {
     "moe_grouped_gemm_fp8_fp4": ["csrc/gemm_fp4.hip", "csrc/gemm_common.h", "csrc/moe_device.h",
                                  "csrc/moe_internal.h", "build.py"],
     "moe_grouped_gemm_bf16": ["csrc/gemm_bf16.hip", "csrc/gemm_common.h", "csrc/moe_device.h", "csrc/moe_internal.h",
-                              "build.py"],
+                              "csrc/gen_fp8_asm.py", "build.py"],
 }
 
 
@@ -388,10 +388,13 @@ def build_variant(args, fmt, cfg, torch, np, moe, synth):
             moe.moe_unpermute_combine(D, oi, tw, Z)
             tm.mark(s, 4)
     else:
+        # bf16 weights in the fragment-packed order (moe_pack_weight_bf16, prepared once)
         W = torch.empty(E, N, K, dtype=torch.bfloat16, device=dev)
         for e0 in range(0, E, 16):
-            W[e0:e0 + 16] = synth.expert_weights(cfg, N, K, experts=range(e0, min(E, e0 + 16)),
-                                                 stream=synth.STREAM_WEIGHTS, device=dev)
+            w = synth.expert_weights(cfg, N, K, experts=range(e0, min(E, e0 + 16)), stream=synth.STREAM_WEIGHTS,
+                                     device=dev)
+            moe.moe_pack_weight_bf16(w, W[e0:e0 + w.shape[0]])
+            del w
         P = torch.empty(rows_cap, K, dtype=torch.bfloat16, device=dev)
         names = ["moe_route_pack", "gemm", "moe_unpermute_combine"]
 
@@ -399,7 +402,7 @@ def build_variant(args, fmt, cfg, torch, np, moe, synth):
             tm.mark(s, 0)
             moe.moe_route_pack(ids, E, layout, am, x, P, counts, seg, mi, oi, st, workspace=ws)
             tm.mark(s, 1)
-            moe.moe_grouped_gemm_bf16(layout, P, W, D, counts, seg, E, am_gemm, N, K, em)
+            moe.moe_grouped_gemm_bf16(layout | moe.WEIGHTS_PACKED, P, W, D, counts, seg, E, am_gemm, N, K, em)
             tm.mark(s, 2)
             moe.moe_unpermute_combine(D, oi, tw, Z)
             tm.mark(s, 3)

@@ -14,8 +14,8 @@
  *   moe_unpermute_combine  topk_weights-weighted sum back to token order
  *
  * plus weight-preparation calls (moe_quant_weight_fp8 / _int4 / _fp4,
- * moe_pack_weight_fp8 / _int4 / _fp4) that turn bf16 expert weights into the
- * formats the GEMMs read.
+ * moe_pack_weight_fp8 / _int4 / _fp4 / _bf16) that turn bf16 expert weights
+ * into the formats the GEMMs read.
  *
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers owned by the caller.  The library
@@ -67,8 +67,8 @@ enum {
 enum { MOE_LAYOUT_CONTIGUOUS = 0, MOE_LAYOUT_MASKED = 1 };
 
 /* Flag ORed into the layout argument of moe_grouped_gemm_fp8 (and _int4,
- * _fp8_fp4): the weights are in the fragment-packed order written by
- * moe_pack_weight_fp8 (moe_pack_weight_int4, moe_pack_weight_fp4) instead of
+ * _fp8_fp4, _bf16): the weights are in the fragment-packed order written by
+ * moe_pack_weight_fp8 (moe_pack_weight_int4, _fp4, _bf16) instead of
  * row-major [E, N, K] ([E, N, K/2]). */
 enum { MOE_WEIGHTS_PACKED = 0x10 };
 
@@ -285,6 +285,15 @@ moe_status moe_grouped_gemm_int4(int layout,
                                  int E, int64_t rows_cap_or_max_m, int N, int K,
                                  int expected_m, void* stream);
 
+/* moe_pack_weight_bf16: reorder bf16 expert weights [E, N, K] into the
+ * fragment-packed order the BF16 grouped GEMM streams fastest: the weight
+ * bytes, viewed as [E, N, 2K], in moe_pack_weight_fp8's order with 2K in place
+ * of K (each 16-column x 128-byte block, i.e. 64 bf16 values of 16 columns,
+ * is 2 KB contiguous, K blocks outermost).  A permutation of the 16-bit
+ * values; nothing is rounded.  Requires N % 128 == 0, K % 128 == 0, both
+ * buffers 16-byte aligned and not overlapping. */
+moe_status moe_pack_weight_bf16(const uint16_t* w, int E, int N, int K, uint16_t* packed, void* stream);
+
 /* moe_grouped_gemm_bf16: BF16 grouped GEMM, "NT" (both operands
  * K-contiguous).  (AsymGEMM README, "API Reference": BF16 m_grouped
  * contiguous and masked grouped GEMMs with bf16 output; rainlin, "GEMM
@@ -292,8 +301,8 @@ moe_status moe_grouped_gemm_int4(int layout,
  *     D[p, n] = bf16_rne( sum_k A[p,k] * W[e,n,k] ), accumulated in fp32.
  *     A [rows, K] bf16, W [E, N, K] bf16, D [rows, N] bf16.
  *   Layout, counts, seg_offsets, expected_m, the rows of D that are written,
- *   alignment and size limits as for moe_grouped_gemm_fp8 (no packed-weight
- *   order: layout must be MOE_LAYOUT_CONTIGUOUS or MOE_LAYOUT_MASKED). */
+ *   alignment and size limits as for moe_grouped_gemm_fp8; layout |
+ *   MOE_WEIGHTS_PACKED: W in the order written by moe_pack_weight_bf16. */
 moe_status moe_grouped_gemm_bf16(int layout,
                                  const uint16_t* A, const uint16_t* W, uint16_t* D,
                                  const int32_t* counts, const int32_t* seg_offsets,

@@ -49,6 +49,7 @@ SIGNATURES = {
     "moe_grouped_gemm_int4": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                                        ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_swiglu_quant": (_c_i32, [ctypes.c_int, _vp, _c_i64, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_pack_weight_bf16": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
     "moe_grouped_gemm_bf16": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                        ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_quant_weight_fp4": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
@@ -275,6 +276,15 @@ def moe_grouped_gemm_int4(layout: int, A, W4, S16, D, counts, seg_offsets, E: in
     _check(load().moe_grouped_gemm_int4(layout, _ptr(A), _ptr(W4), _ptr(S16), _ptr(D), _ptr(counts),
                                         _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
            "moe_grouped_gemm_int4")
+
+
+def moe_pack_weight_bf16(w, packed, stream=None):
+    """w bf16 [E, N, K] -> packed bf16 [E, N, K] in the fragment order (see include/moe.h)."""
+    _dev(w, "w", torch.bfloat16, 3), _dev(packed, "packed", torch.bfloat16, 3)
+    E, N, K = w.shape
+    if tuple(packed.shape) != (E, N, K):
+        raise ValueError("moe_pack_weight_bf16: shape mismatch")
+    _check(load().moe_pack_weight_bf16(_ptr(w), E, N, K, _ptr(packed), _stream(stream)), "moe_pack_weight_bf16")
 
 
 def moe_grouped_gemm_bf16(layout: int, A, W, D, counts, seg_offsets, E: int, rows_cap_or_max_m: int, N: int, K: int,

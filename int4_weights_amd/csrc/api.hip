@@ -349,10 +349,30 @@ moe_status moe_grouped_gemm_int4(int layout, const uint16_t* A, const uint8_t* W
   return hip_status(launch_gemm_int4(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_int4");
 }
 
+moe_status moe_pack_weight_bf16(const uint16_t* w, int E, int N, int K, uint16_t* packed, void* stream) {
+  g_err[0] = 0;
+  if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_pack_weight_bf16: E=%d N=%d K=%d", E, N, K);
+  if (N % 128 || K % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_weight_bf16: N=%d and K=%d must be multiples of 128", N, K);
+  if ((int64_t)N * K * 2 > 0xffffffffll) return fail(MOE_ERR_UNSUPPORTED, "moe_pack_weight_bf16: one expert exceeds 4 GiB");
+  if (E == 0) return MOE_OK;
+  if (!w || !packed) return fail(MOE_ERR_NULL, "moe_pack_weight_bf16: null pointer");
+  if (!aligned(w, 16) || !aligned(packed, 16))
+    return fail(MOE_ERR_ALIGN, "moe_pack_weight_bf16: w and packed must be 16-byte aligned");
+  const uint16_t* we = w + (int64_t)E * N * K;
+  const uint16_t* pe = packed + (int64_t)E * N * K;
+  if (w < pe && packed < we) return fail(MOE_ERR_SHAPE, "moe_pack_weight_bf16: w and packed overlap");
+  // the bf16 bytes [E, N, 2K] in the FP8 fragment order with 2K bytes per row
+  return hip_status(launch_pack_weight_fp8((const uint8_t*)w, E, N, 2 * K, (uint8_t*)packed, (hipStream_t)stream),
+                    "moe_pack_weight_bf16");
+}
+
 moe_status moe_grouped_gemm_bf16(int layout, const uint16_t* A, const uint16_t* W, uint16_t* D,
                                  const int32_t* counts, const int32_t* seg_offsets, int E, int64_t rows_cap_or_max_m,
                                  int N, int K, int expected_m, void* stream) {
   g_err[0] = 0;
+  const int wpacked = (layout & MOE_WEIGHTS_PACKED) ? 1 : 0;
+  layout &= ~MOE_WEIGHTS_PACKED;
   moe_status st = check_gemm("moe_grouped_gemm_bf16", layout, A, W, W, D, counts, seg_offsets, E, rows_cap_or_max_m,
                              N, K);
   if (st) return st;
@@ -372,7 +392,7 @@ moe_status moe_grouped_gemm_bf16(int layout, const uint16_t* A, const uint16_t* 
   a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
   a.N = N;
   a.K = K;
-  a.wpacked = 0;
+  a.wpacked = wpacked;
   return hip_status(launch_gemm_bf16(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_bf16");
 }
 

@@ -79,18 +79,19 @@ GROUP = 4         # K blocks per row-scale copy (one 16-byte copy per row)
 
 
 class Cfg:
-    def __init__(self, rows: int, S: int, name: str):
-        assert rows in (192, 256)
+    def __init__(self, rows: int, S: int, name: str, dtype: str = "fp8"):
+        assert rows in (192, 256) and dtype in ("fp8", "bf16")
         self.rows, self.S, self.name = rows, S, name
+        self.bf16 = dtype == "bf16"               # bf16 operands: four 32x32x16 instructions per 128-byte step, no scales
         assert S == GROUP, "the unrolled loop body is one scale group"
         self.slot_a = rows * 128                 # activation bytes of one ring slot in LDS
         self.slot = self.slot_a                   # bytes of one ring slot
-        self.sc_off = S * self.slot               # two scale-group buffers of SCALE_ROWS x 16 bytes follow
-        self.lds = self.sc_off + 2 * SCALE_ROWS * 16
+        self.sc_off = S * self.slot               # (fp8) two scale-group buffers of SCALE_ROWS x 16 bytes follow
+        self.lds = self.sc_off + (0 if self.bf16 else 2 * SCALE_ROWS * 16)
         self.rt = rows // 32                      # 32-row tiles per unit at most
         self.apw = rows // 32                     # 1-KB activation copies per wave per K block
-        self.ops = 8 + self.apw + 1               # vector-memory instructions per wave per K block (+1 for
-        # the blocks that start a scale group)
+        self.ops = 8 + self.apw + (0 if self.bf16 else 1)  # vector-memory instructions per wave per K block (fp8:
+        # +1 for the weight scale, +1 more for the blocks that start a scale group)
         assert 2 * self.ops + 2 <= 63, "vmcnt holds at most 63"
         self.wbase = 256 - 32 * S
         self.nacc = 32 * self.rt
@@ -121,7 +122,7 @@ class Cfg:
         """Loads allowed outstanding at the barrier of step s (K block ks = s mod S) that publishes block
         ks + 1: those of block ks + 2 (issued in the previous step, plus one if it starts a scale group) and
         the `issued` loads of block ks + 3 this step has issued so far."""
-        return self.ops + (1 if (s + 2) % GROUP == 0 else 0) + issued
+        return self.ops + (1 if (s + 2) % GROUP == 0 and not self.bf16 else 0) + issued
 
     @staticmethod
     def bufid(j):
@@ -153,8 +154,14 @@ def issue_items(cfg, t, packed):
     for i in range(cfg.apw):
         items.append([f"s_add_u32 m0, %[ma], {t * cfg.slot + i * 1024}", "s_nop 0",
                       f"global_load_lds_dwordx4 %[ao{i}], %[ab]"])
-    items.append([f"global_load_dword v{cfg.v_swr + t}, %[wso], %[swb]"])
     upd = []
+    if cfg.bf16:  # no scales: only the weight and activation offsets advance
+        upd += ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0",
+                "s_cselect_b32 %[t], %[wstep], 0"]
+        upd += [f"v_add_u32_e32 %[wo{ct}], %[t], %[wo{ct}]" for ct in range(2)]
+        upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(cfg.apw)]
+        return items, upd
+    items.append([f"global_load_dword v{cfg.v_swr + t}, %[wso], %[swb]"])
     if t % GROUP == 0:
         items.append(["s_mov_b32 m0, %[msg]", "s_nop 0", "global_load_lds_dwordx4 %[so], %[sb]"])
         upd += ["s_xor_b32 %[msg], %[msg], " + str(SCALE_ROWS * 16), f"s_add_u32 %[t], %[q], {GROUP}",
@@ -185,11 +192,25 @@ def publish(cfg, s, wait):
     matrix instructions run."""
     sn = (s + 1) % cfg.S
     out = [f"s_waitcnt vmcnt({wait})", "s_barrier"]
-    if s == cfg.S - 1:  # block ks + 1 opens the next scale group, in the other group buffer
+    if s == cfg.S - 1 and not cfg.bf16:  # block ks + 1 opens the next scale group, in the other group buffer
         out.append(f"v_xor_b32_e32 v{cfg.v_sadr}, {SCALE_ROWS * 16}, v{cfg.v_sadr}")
     out += frag_reads(cfg, sn, 2, 0)
-    out.append(f"ds_read_b32 v{cfg.v_sae + 2}, v{cfg.v_sadr}" + (f" offset:{4 * sn}" if sn else ""))
+    if not cfg.bf16:
+        out.append(f"ds_read_b32 v{cfg.v_sae + 2}, v{cfg.v_sadr}" + (f" offset:{4 * sn}" if sn else ""))
     return out
+
+
+def mfma(cfg, s, b, j, ct, kk, src_zero):
+    """The matrix instructions of K half kk for row tile j (fragment buffer b) and column tile ct: one scaled
+    32x32x64 FP8 instruction, or two 32x32x16 bf16 ones on the two 16-byte pieces of each operand (the same K
+    values in both operands, so the products match), the second accumulating onto the first."""
+    a0 = cfg.acc(j, ct)
+    acc = f"a[{a0}:{a0 + 15}]"
+    if not cfg.bf16:
+        return [f"v_mfma_scale_f32_32x32x64_f8f6f4 {acc}, {wreg(cfg, s, ct, kk, 0, 7)}, {cfg.buf(b, kk)}, "
+                f"{'0' if src_zero else acc}, v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]"]
+    return [f"v_mfma_f32_32x32x16_bf16 {acc}, {wreg(cfg, s, ct, kk, 4 * p, 4 * p + 3)}, {cfg.buf(b, kk, 4 * p, 4 * p + 3)}, "
+            f"{'0' if src_zero and p == 0 else acc}" for p in range(2)]
 
 
 def compute(cfg, s, t, packed, rbe, final=False, first=False):
@@ -215,26 +236,26 @@ def compute(cfg, s, t, packed, rbe, final=False, first=False):
     for i, it in enumerate(items):
         place[(i * nslots) // len(items)].append(it)
     sadr = cfg.v_sadr  # row r's scale of K block s of the group at r * 16 + 4 s
-    out = [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}", "s_waitcnt lgkmcnt(0)",
-           f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"]
+    out = (["s_waitcnt lgkmcnt(0)"] if cfg.bf16 else
+           [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}", "s_waitcnt lgkmcnt(0)",
+            f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"])
     for j in range(rbe):
         b = cfg.bufid(j)
         if j + 1 < rbe:
             bn = cfg.bufid(j + 1)
-            out += frag_reads(cfg, s, bn, j + 1) + [
-                f"ds_read_b32 v{cfg.v_sae + bn}, v{sadr} offset:{512 * (j + 1) + 4 * s}"]
+            out += frag_reads(cfg, s, bn, j + 1)
+            if not cfg.bf16:
+                out.append(f"ds_read_b32 v{cfg.v_sae + bn}, v{sadr} offset:{512 * (j + 1) + 4 * s}")
         out.append("s_nop 1")
         q = 0
         for kk in range(2):  # consecutive instructions write different accumulators
             for ct in range(2):
-                a0 = cfg.acc(j, ct)
-                src_c = "0" if first and kk == 0 else f"a[{a0}:{a0 + 15}]"
-                out.append(f"v_mfma_scale_f32_32x32x64_f8f6f4 a[{a0}:{a0 + 15}], {wreg(cfg, s, ct, kk, 0, 7)}, "
-                           f"{cfg.buf(b, kk)}, {src_c}, v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
+                out += mfma(cfg, s, b, j, ct, kk, first and kk == 0)
                 out += [ins for it in place[4 * j + q] for ins in it]
                 q += 1
         if j + 1 < rbe:
-            out += ["s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"]
+            out += ["s_waitcnt lgkmcnt(0)"] + ([] if cfg.bf16 else
+                                               [f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"])
             if j + 2 == rbe and not (final and s == cfg.S - 1):  # row tile j + 1 is the last one
                 issued = sum(len(place[i]) for i in range(4 * (j + 1)))
                 wait = 0 if final and s == 2 else cfg.wait_at(s, issued)
@@ -327,8 +348,9 @@ def compute_last(cfg, s, rbe):
     (only the last row tile, and row tile 0 of a two-tile unit, can be partial; both are stored by the
     epilogue after the loop).  Row tile j + 1's fragments are read after row tile j's first matrix
     instruction, and the LDS operations in flight stay within the 15 that lgkmcnt counts."""
-    out = [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}", "s_waitcnt lgkmcnt(0)",
-           f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"]
+    out = (["s_waitcnt lgkmcnt(0)"] if cfg.bf16 else
+           [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}", "s_waitcnt lgkmcnt(0)",
+            f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"])
     for j in range(rbe):
         b = cfg.bufid(j)
         nxt = j + 1 < rbe
@@ -337,28 +359,29 @@ def compute_last(cfg, s, rbe):
         if nxt:
             if j >= 2:  # row tile j - 2's 12 staging operations may be in flight
                 place[0].append("s_waitcnt lgkmcnt(10)")
-            place[0] += frag_reads(cfg, s, bn, j + 1) + [
-                f"ds_read_b32 v{cfg.v_sae + bn}, v{cfg.v_sadr} offset:{512 * (j + 1) + 4 * s}"]
+            place[0] += frag_reads(cfg, s, bn, j + 1)
+            if not cfg.bf16:
+                place[0].append(f"ds_read_b32 v{cfg.v_sae + bn}, v{cfg.v_sadr} offset:{512 * (j + 1) + 4 * s}")
         if j == 0:
             place[1] += ep_setup(cfg)
-        if j >= 2:  # row tile j - 2 read back (the fragment reads of row tile j + 1 may still be in flight)
-            place[1] += [f"s_waitcnt lgkmcnt({5 if nxt else 0})"] + ep_store_full(cfg, j - 2)
+        if j >= 2:  # row tile j - 2 read back (the fragment reads of row tile j + 1 may still be in flight: 4, and
+            # for FP8 its row-scale read)
+            place[1] += [f"s_waitcnt lgkmcnt({(4 if cfg.bf16 else 5) if nxt else 0})"] + ep_store_full(cfg, j - 2)
         if j >= 1:
             # the accumulators of row tile j - 1 were last written 4 matrix instructions ago; the nops make
             # the required wait states explicit where few other instructions lie between
             place[2] += (["s_nop 15"] if j == 1 else []) + ep_convert(cfg, j - 1, 0)
             place[3] += ep_convert(cfg, j - 1, 1)
         if nxt:
-            place[3] += ["s_waitcnt lgkmcnt(0)", f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"]
+            place[3] += ["s_waitcnt lgkmcnt(0)"] + ([] if cfg.bf16 else
+                                                   [f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"])
         if j >= 1:
             place[3] += ["s_nop 1"] + ep_stage(cfg, j - 1)
         out.append("s_nop 1")
         q = 0
         for kk in range(2):
             for ct in range(2):
-                a0 = cfg.acc(j, ct)
-                out.append(f"v_mfma_scale_f32_32x32x64_f8f6f4 a[{a0}:{a0 + 15}], {wreg(cfg, s, ct, kk, 0, 7)}, "
-                           f"{cfg.buf(b, kk)}, a[{a0}:{a0 + 15}], v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]")
+                out += mfma(cfg, s, b, j, ct, kk, False)
                 out += place[q]
                 q += 1
     return out
@@ -382,7 +405,8 @@ def program(cfg, packed):
     for kk in range(2):
         for p in range(2):
             out.append(f"v_mov_b32_e32 v{cfg.v_aadr + 2 * kk + p}, %[a{kk}{p}]")
-    out.append(f"v_mov_b32_e32 v{cfg.v_sadr}, %[sadr]")
+    if not cfg.bf16:
+        out.append(f"v_mov_b32_e32 v{cfg.v_sadr}, %[sadr]")
     for s in range(1, S):
         for kk in range(2):
             for p in range(2):
@@ -392,8 +416,8 @@ def program(cfg, packed):
         items, upd = issue_items(cfg, t, packed)
         out += [ins for it in items for ins in it] + upd
     # block 0 in place (blocks 1 and 2 may still be in flight), then its row tile 0 into buffer 2
-    out += [f"s_waitcnt vmcnt({2 * cfg.ops})", "s_barrier"] + frag_reads(cfg, 0, 2, 0) + [
-        f"ds_read_b32 v{cfg.v_sae + 2}, v{cfg.v_sadr}"]
+    out += [f"s_waitcnt vmcnt({2 * cfg.ops})", "s_barrier"] + frag_reads(cfg, 0, 2, 0) + (
+        [] if cfg.bf16 else [f"ds_read_b32 v{cfg.v_sae + 2}, v{cfg.v_sadr}"])
     # one loop body per row-tile count (2 .. rt): no branch between the matrix instructions of a step
     for r in range(2, cfg.rt):
         out += [f"s_cmp_eq_u32 %[rbe], {r}", f"s_cbranch_scc1 {100 + r}f"]
@@ -411,7 +435,8 @@ def clobbers(cfg):
     return ", ".join(regs)
 
 
-CONFIGS = [Cfg(192, 4, "TALL192"), Cfg(256, 4, "TALL256")]
+CONFIGS = [Cfg(192, 4, "TALL192"), Cfg(256, 4, "TALL256"),
+           Cfg(192, 4, "BF16_TALL192", "bf16"), Cfg(256, 4, "BF16_TALL256", "bf16")]
 
 
 def main():
@@ -419,20 +444,20 @@ def main():
         f.write("// Generated by gen_fp8_asm.py -- do not edit.\n")
         f.write(f"#define MOE_FP8_TALL_SCALE_ROWS {SCALE_ROWS}\n#define MOE_FP8_TALL_SCALE_GROUP {GROUP}\n")
         for cfg in CONFIGS:
-            n = cfg.name
+            n = cfg.name if cfg.bf16 else "FP8_" + cfg.name
             f.write(f"// {n}: {cfg.rows} rows, ring {cfg.S}, {cfg.rt} row tiles, {cfg.ops} loads/K block "
-                    f"(+1 per scale group)\n")
-            f.write(f"#define MOE_FP8_{n}_SLOT_A {cfg.slot_a}\n#define MOE_FP8_{n}_SLOT {cfg.slot}\n"
-                    f"#define MOE_FP8_{n}_SC_OFF {cfg.sc_off}\n#define MOE_FP8_{n}_LDS {cfg.lds}\n"
-                    f"#define MOE_FP8_{n}_APW {cfg.apw}\n#define MOE_FP8_{n}_S {cfg.S}\n")
-            f.write(f"#define MOE_FP8_{n}_AO_OUTS " + ", ".join(f'[ao{i}] "+v"(ao[{i}])' for i in range(cfg.apw))
+                    + ("\n" if cfg.bf16 else "(+1 per scale group)\n"))
+            f.write(f"#define MOE_{n}_SLOT_A {cfg.slot_a}\n#define MOE_{n}_SLOT {cfg.slot}\n"
+                    f"#define MOE_{n}_SC_OFF {cfg.sc_off}\n#define MOE_{n}_LDS {cfg.lds}\n"
+                    f"#define MOE_{n}_APW {cfg.apw}\n#define MOE_{n}_S {cfg.S}\n")
+            f.write(f"#define MOE_{n}_AO_OUTS " + ", ".join(f'[ao{i}] "+v"(ao[{i}])' for i in range(cfg.apw))
                     + "\n")
             for suffix, packed in (("", False), ("_PACKED", True)):
-                f.write(f"#define MOE_FP8_{n}_LOOP{suffix} \\\n")
+                f.write(f"#define MOE_{n}_LOOP{suffix} \\\n")
                 for ln in program(cfg, packed):
                     f.write(f'  "{ln}\\n" \\\n')
                 f.write("  \"\"\n")
-            f.write(f"#define MOE_FP8_{n}_CLOBBERS {clobbers(cfg)}\n")
+            f.write(f"#define MOE_{n}_CLOBBERS {clobbers(cfg)}\n")
 
 
 if __name__ == "__main__":

@@ -156,7 +156,11 @@ def test_host_validation_rejects_without_launching(lib):
     assert gb(N=200) == MOE_ERR_UNSUPPORTED
     assert gb(K=64) == MOE_ERR_UNSUPPORTED
     assert gb(E=0) == MOE_ERR_SHAPE
-    assert gb(layout=0x10) == MOE_ERR_SHAPE          # no packed-weight order for bf16
+    assert gb(layout=0x10 | 7) == MOE_ERR_SHAPE      # the packed-weights flag does not make a layout valid
+    assert lib.moe_pack_weight_bf16(_p(A16), 2, 100, 128, _p(A16 << 4), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_pack_weight_bf16(_p(A16 + 8), 2, 128, 128, _p(A16 << 4), None) == MOE_ERR_ALIGN
+    assert lib.moe_pack_weight_bf16(_p(A16), 2, 128, 128, _p(A16 + 4096), None) == MOE_ERR_SHAPE  # overlap
+    assert lib.moe_pack_weight_bf16(None, 0, 128, 128, None, None) == MOE_OK
     assert gb(seg=0) == MOE_ERR_NULL
     assert gb(W=0) == MOE_ERR_NULL
     assert gb(A=A16 + 8) == MOE_ERR_ALIGN

@@ -1,5 +1,5 @@
-"""Host checks of the generated tall-tile FP8 loop (gen_fp8_asm.py): the text the build compiles into the
-kernel must keep the invariants the loop relies on.  No GPU needed."""
+"""Host checks of the generated tall-tile loops (gen_fp8_asm.py; FP8 and bf16 configurations): the text the
+build compiles into the kernels must keep the invariants the loop relies on.  No GPU needed."""
 
 import importlib.util
 import os
@@ -159,18 +159,19 @@ def _walk(prog, rbe, kb):
 
 @pytest.mark.parametrize("kb", [4, 8, 12, 56])
 def test_each_unit_path_runs_its_blocks_once(gen, kb):
-    """For every row-tile count: 4 MFMAs per row tile and K block, one barrier per K block but the last, plus
-    the prologue's and the one that ends the unit (so all waves of a workgroup meet at the same barriers), the
-    loads of exactly kb blocks, 4 stores (of 8 rows each) per row tile, at most 15 LDS operations in flight, and
-    no register used before the load or LDS read that fills it has been waited for."""
+    """For every row-tile count: 4 MFMAs (FP8; 8 bf16 ones) per row tile and K block, one barrier per K block
+    but the last, plus the prologue's and the one that ends the unit (so all waves of a workgroup meet at the
+    same barriers), the loads of exactly kb blocks (FP8: with one row-scale copy per 4 blocks), 4 stores (of 8
+    rows each) per row tile, at most 15 LDS operations in flight, and no register used before the load or LDS
+    read that fills it has been waited for."""
     for cfg in gen.CONFIGS:
         for packed in (False, True):
             prog = gen.program(cfg, packed)
             for rbe in range(2, cfg.rt + 1):
                 c = _walk(prog, rbe, kb)
-                assert c["mfma"] == 4 * rbe * kb, (cfg.name, rbe, kb, c)
+                assert c["mfma"] == (8 if cfg.bf16 else 4) * rbe * kb, (cfg.name, rbe, kb, c)
                 assert c["barrier"] == 1 + (kb - 1) + 1, (cfg.name, rbe, kb, c)
-                groups = kb // gen.GROUP
+                groups = 0 if cfg.bf16 else kb // gen.GROUP
                 assert c["load"] == kb * cfg.ops + groups, (cfg.name, rbe, kb, c)
                 assert c["store"] == 4 * rbe, (cfg.name, rbe, kb, c)
                 assert c["lds_max"] <= 15, (cfg.name, rbe, kb, c)

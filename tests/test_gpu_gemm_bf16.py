@@ -15,6 +15,7 @@ import torch
 
 import int4_weights_amd as moe
 import oracle
+import weight_layout as wl
 from gpu_helpers import DEV, bf16_from_u16, require_gpu, u16
 
 pytestmark = pytest.mark.gpu
@@ -45,10 +46,15 @@ def _case(seed, counts, N, K, layout, max_m=0, ints=False):
                 max_m=max_m, a=oracle.f32_to_bf16_bits(a), w=oracle.f32_to_bf16_bits(w))
 
 
-def _run(c, expected_m=0):
+def _run(c, expected_m=0, packed=False):
     D = torch.full((c["rows"], c["N"]), SENT, dtype=torch.int16, device=DEV).view(torch.bfloat16)
     am = c["max_m"] if c["layout"] == moe.LAYOUT_MASKED else c["rows"]
-    moe.moe_grouped_gemm_bf16(c["layout"], bf16_from_u16(c["a"]), bf16_from_u16(c["w"]), D,
+    if packed:
+        w = bf16_from_u16(wl.pack_weight_bf16(c["w"]).reshape(c["w"].shape))
+        layout = c["layout"] | moe.WEIGHTS_PACKED
+    else:
+        w, layout = bf16_from_u16(c["w"]), c["layout"]
+    moe.moe_grouped_gemm_bf16(layout, bf16_from_u16(c["a"]), w, D,
                               torch.from_numpy(c["counts"]).to(DEV),
                               torch.from_numpy(c["starts"].astype(np.int32)).to(DEV), c["E"], am, c["N"], c["K"],
                               expected_m)
@@ -73,27 +79,32 @@ def _check(c, D, exact=False):
     assert (np.abs(got - y) <= 2.0 ** -8 * np.abs(y) + 1e-5 * m).all()
 
 
-@pytest.mark.parametrize("expected_m", [0, 16, 64])
-def test_bf16_contiguous_ragged(expected_m):
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("expected_m", [0, 16, 64, 128])
+def test_bf16_contiguous_ragged(expected_m, packed):
+    """expected_m picks the tile: 16 -> 16-row, 64 -> 64-row, 128 -> 192-row tall, 0 (= 256) -> 256-row tall."""
     require_gpu()
     c = _case(1, [0, 1, 17, 130, 300], N=384, K=1536, layout=moe.LAYOUT_CONTIGUOUS)
-    _check(c, _run(c, expected_m))
+    _check(c, _run(c, expected_m, packed))
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("expected_m", [0, 16])
-def test_bf16_masked_clipped(expected_m):
+def test_bf16_masked_clipped(expected_m, packed):
     require_gpu()
     c = _case(2, [5, 0, 64, 90, 1, 33], N=256, K=768, layout=moe.LAYOUT_MASKED, max_m=64)
-    _check(c, _run(c, expected_m))
+    _check(c, _run(c, expected_m, packed))
 
 
-def test_bf16_small_integers_bit_exact_and_deterministic():
+@pytest.mark.parametrize("packed", [False, True])
+def test_bf16_small_integers_bit_exact_and_deterministic(packed):
     require_gpu()
-    c = _case(3, [7, 64, 129], N=512, K=256, layout=moe.LAYOUT_CONTIGUOUS, ints=True)
-    D = _run(c, 64)
-    _check(c, D, exact=True)
-    for _ in range(20):
-        assert torch.equal(_run(c, 64), D)
+    c = _case(3, [7, 64, 129, 300], N=512, K=256, layout=moe.LAYOUT_CONTIGUOUS, ints=True)
+    for em in (16, 64, 128, 256):
+        D = _run(c, em, packed)
+        _check(c, D, exact=True)
+        for _ in range(10):
+            assert torch.equal(_run(c, em, packed), D)
 
 
 def test_bf16_many_experts_and_narrow_n():
@@ -101,7 +112,61 @@ def test_bf16_many_experts_and_narrow_n():
     rng = np.random.default_rng(4)
     counts = rng.integers(0, 40, 300)
     c = _case(5, list(counts), N=128, K=256, layout=moe.LAYOUT_CONTIGUOUS)
-    _check(c, _run(c, 0))
+    for em in (0, 16, 64):
+        _check(c, _run(c, em))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("K", [1536, 2560])
+def test_bf16_tall_every_row_tile_count_long_k(K, packed):
+    """Both tall heights on units of every 32-row count (1..256 rows, so every loop body), N = 384 (the second
+    256-column tile has two idle waves), K/64 = 24 or 40 steps (main loop iterations before the last)."""
+    require_gpu()
+    counts = [32 * r - 5 for r in range(1, 9)] + [32 * r for r in range(1, 9)] + [0, 3, 256 + 100, 192 + 40]
+    c = _case(61 + K, counts, N=384, K=K, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (128, 256):
+        _check(c, _run(c, em, packed))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_bf16_tall_masked_segments_and_short_k_fallback(packed):
+    """Masked segments taller than a tall tile, and K/64 not a multiple of 4 (the tall loop cannot run: the
+    64-row tile takes prefill-sized calls)."""
+    require_gpu()
+    c = _case(12, [150, 0, 300, 65], N=256, K=1024, layout=moe.LAYOUT_MASKED, max_m=300)
+    for em in (0, 200, 256):
+        _check(c, _run(c, em, packed))
+    c = _case(14, [0, 1, 17, 130, 300], N=256, K=384, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (0, 128):
+        _check(c, _run(c, em, packed))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_bf16_degenerate_expert_counts(packed):
+    """No rows at all, 1024 experts with 0..3 rows (N = 128: half of each tall tile's waves store nothing), and
+    one expert with several tall chunks, on every tile height."""
+    require_gpu()
+    c = _case(31, [0] * 8, N=256, K=512, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (16, 64, 128, 256):
+        _check(c, _run(c, em, packed))
+    counts = np.random.default_rng(33).integers(0, 4, size=1024).tolist()
+    c = _case(33, counts, N=128, K=256, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (16, 128, 256):
+        _check(c, _run(c, em, packed))
+    c = _case(34, [700], N=384, K=512, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (64, 128, 256):
+        _check(c, _run(c, em, packed))
+
+
+def test_pack_weight_bf16_bit_exact():
+    require_gpu()
+    rng = np.random.default_rng(9)
+    E, N, K = 3, 384, 640
+    w = rng.integers(0, 1 << 16, size=(E, N, K), dtype=np.uint16)
+    out = torch.zeros(E, N, K, dtype=torch.bfloat16, device=DEV)
+    moe.moe_pack_weight_bf16(bf16_from_u16(w), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(out).reshape(E, N * K), wl.pack_weight_bf16(w))
 
 
 def test_bf16_full_size_dsv3_decode_and_prefill_samples():

@@ -32,6 +32,23 @@ def test_unpack_inverts_pack_and_blocks_are_2kb_fragments():
     assert np.array_equal(packed[0, base + 1024:base + 1040], codes[0, 32, 192:208])
 
 
+def test_bf16_pack_round_trip_and_hand_placed_values():
+    """bf16 weights: the 16-bit values of each 16-column x 64-value block form one 2 KB fragment."""
+    rng = np.random.default_rng(8)
+    E, N, K = 2, 256, 192
+    w = rng.integers(0, 1 << 16, size=(E, N, K), dtype=np.uint16)
+    packed = wl.pack_weight_bf16(w)
+    assert packed.shape == (E, N * K) and packed.dtype == np.uint16
+    assert np.array_equal(wl.unpack_weight_bf16(packed, N, K), w)
+    assert np.array_equal(np.sort(packed[1]), np.sort(w[1].reshape(-1)))
+    # block (K values 64..127, columns 32..47) starts at value (1 * 16 + 2) * 1024: column 32, K 64..71 first;
+    # the 18th 8-value piece is column 33, K 72..79; the second half (+512 values) starts with column 32, K 96..103
+    base = (1 * (N // 16) + 2) * 1024
+    assert np.array_equal(packed[1, base:base + 8], w[1, 32, 64:72])
+    assert np.array_equal(packed[1, base + 17 * 8:base + 18 * 8], w[1, 33, 72:80])
+    assert np.array_equal(packed[1, base + 512:base + 520], w[1, 32, 96:104])
+
+
 def _nib(q4, n, k):
     b = q4[n, k // 2]
     return (b >> 4) & 15 if k % 2 else b & 15

@@ -70,6 +70,25 @@ def unpack_weight_fp8(packed: np.ndarray, N: int, K: int) -> np.ndarray:
     return np.ascontiguousarray(x.transpose(0, 2, 5, 1, 3, 4, 6)).reshape(E, N, K)
 
 
+def pack_weight_bf16(w_bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns uint16 [E, N, K] -> uint16 [E, N*K]: the weight bytes, viewed as uint8 [E, N, 2K]
+    (little-endian), in pack_weight_fp8's order with 2K bytes per row (moe_pack_weight_bf16).
+
+    Pinned by: the inverse round trip and one-hot positions (tests)."""
+    w_bits = np.ascontiguousarray(np.asarray(w_bits, dtype="<u2"))
+    E, N, K = w_bits.shape
+    if N % 128 or K % 64:
+        raise ValueError("N must be a multiple of 128 and 2K of 128")
+    return pack_weight_fp8(w_bits.view(np.uint8).reshape(E, N, 2 * K)).view("<u2").reshape(E, N * K)
+
+
+def unpack_weight_bf16(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Inverse of pack_weight_bf16: uint16 [E, N*K] -> [E, N, K]."""
+    packed = np.ascontiguousarray(np.asarray(packed, dtype="<u2"))
+    E = packed.shape[0]
+    return unpack_weight_fp8(packed.view(np.uint8).reshape(E, 2 * N * K), N, 2 * K).view("<u2").reshape(E, N, K)
+
+
 SIGMA = (0, 2, 4, 6, 1, 3, 5, 7)
 
 
