@@ -225,11 +225,148 @@ static hipError_t launch_fp4(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------
+// Tall tiles (prefill, packed weights): 192 or 256 rows x 256 columns per
+// unit, the FP8 tall tiles' generated loop (gen_fp8_asm.py, the fp4
+// configurations) on v_mfma_scale_f32_32x32x64_f8f6f4 with the weights as an
+// E2M1 A operand (cbsz = 4).  In that instruction a weight lane (column l32,
+// half h) holds the 32 contiguous values K = 64 kk + 32 h .. +31 -- one MXFP4
+// block, chunk 2 kk + h of the column's 1 KB fragment in the packed order --
+// and takes its own E8M0 scale, while an E4M3 activation lane holds
+// K = 64 kk + 16 h .. +15 and 64 kk + 32 + 16 h .. +15 (measured with random
+// small-integer operands against an exact product), so the activation
+// fragment is read as chunks 4 kk + h and 4 kk + 2 + h of the row.  Each lane
+// loads the packed scale dword of its 16-column group and block 2 kk + h and
+// shifts it right by 8 (l32 / 16) bits x 8, so that byte 2 ct holds the scale
+// of its column in column tile ct, which op_sel picks.  Activations and their
+// row scales go through the LDS ring exactly as in the FP8 tall tile.
+#include "gemm_fp8_tall_loop.inc"
+
+template <int ROWS>
+struct Fp4TallCfg;
+template <>
+struct Fp4TallCfg<192> {
+  static constexpr int kApw = MOE_FP4_TALL192_APW, kScOff = MOE_FP4_TALL192_SC_OFF, kLds = MOE_FP4_TALL192_LDS;
+};
+template <>
+struct Fp4TallCfg<256> {
+  static constexpr int kApw = MOE_FP4_TALL256_APW, kScOff = MOE_FP4_TALL256_SC_OFF, kLds = MOE_FP4_TALL256_LDS;
+};
+static_assert(MOE_FP4_TALL192_S == 4 && MOE_FP4_TALL256_S == 4, "4-step loop body");
+static_assert(MOE_FP4_TALL192_SLOT_A == 192 * 128 && MOE_FP4_TALL256_SLOT_A == 256 * 128, "128-byte rows per slot");
+static_assert(MOE_FP8_TALL_SCALE_ROWS == 256 && MOE_FP8_TALL_SCALE_GROUP == 4, "row-scale groups");
+
+__device__ __forceinline__ uint64_t uniform_u64_f4(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+#define MOE_FP4_TALL_ASM(LOOP, AO_OUTS, CLOBBERS)                                                                 \
+  asm volatile(LOOP                                                                                             \
+               : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), AO_OUTS,                                                    \
+                 [so] "+v"(so), [wso] "+v"(wso), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),  \
+                 [inc] "=&s"(inc), [inc4] "=&s"(inc4), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v), [msg] "+s"(msg)         \
+               : [wb] "s"(wb), [ab] "s"(ab), [sb] "s"(sb), [swb] "s"(swb), [ma] "s"(ma),                       \
+                 [a00] "v"(af[0]), [a01] "v"(af[1]), [a10] "v"(af[2]), [a11] "v"(af[3]), [sadr] "v"(sadr),        \
+                 [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb), [sstep] "s"(sstep), [fsh] "v"(fsh),             \
+                 [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [wm] "s"(wm), [wstep] "s"(wstep),           \
+                 [l8] "v"(l8), [epb] "v"(epb), [rb] "v"(rb)                                                      \
+               : "memory", "vcc", "exec", "scc", CLOBBERS)
+
+template <int ROWS>
+__device__ __forceinline__ void fp4_unit_tall(const GemmArgs& a, const Unit& u, uint8_t* smem, int wv, int lane) {
+  constexpr int kTApw = Fp4TallCfg<ROWS>::kApw, kScOff = Fp4TallCfg<ROWS>::kScOff;
+  const int l32 = lane & 31, hh = lane >> 5;  // operand row and K half of this lane
+  const int K = a.K, N = a.N, KB = K / 128;
+  const int ncol0 = u.n0 + 64 * wv;
+  const int won = ncol0 < N ? 1 : 0;
+  const int ncl = won ? ncol0 : N - 64;  // an idle wave re-reads valid columns and stores nothing
+
+  // codes: column tile c's 16-column group (ncl + 32 c) / 16 + l32 / 16, chunk (l32 % 16) + 16 (2 kk + hh)
+  const uint64_t wb = uniform_u64_f4((uint64_t)(a.W + (int64_t)u.e * N * (K / 2)));
+  uint32_t wo[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    wo[c] = (uint32_t)((ncl + 32 * c) / 16 + l32 / 16) * 1024u + (uint32_t)(l32 & 15) * 16u + 256u * hh;
+  const int wstep = uniform(64 * N);  // code bytes per K block
+  // scales: the dword of entry (l32 % 16) + 16 (2 kk + hh) of the wave's 64-column group, bytes = the group's
+  // four 16-column blocks
+  const uint64_t swb = uniform_u64_f4((uint64_t)((const uint8_t*)a.SW + (int64_t)u.e * N * (K / 32)));
+  uint32_t wso = (uint32_t)((ncl / 64) * 64 + (l32 & 15) + 16 * hh) * 4u;
+  const int sstep = uniform(4 * N);   // scale bytes per K block
+  const uint32_t fsh = 8u * (uint32_t)(l32 >> 4);
+  // activations and row scales as in the FP8 tall tile
+  const uint64_t ab = uniform_u64_f4((uint64_t)(a.A + (int64_t)u.row0 * K));
+  uint32_t ao[kTApw];
+#pragma unroll
+  for (int i = 0; i < kTApw; ++i) {
+    const int r = 8 * (wv * kTApw + i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    ao[i] = (uint32_t)min(r, u.mrows - 1) * (uint32_t)K + 16u * c;
+  }
+  const uint64_t sb = uniform_u64_f4((uint64_t)(a.SFA + (int64_t)u.row0 * KB));
+  uint32_t so = (uint32_t)min(64 * wv + lane, u.mrows - 1) * (uint32_t)(KB * 4);
+  // fragment reads: row m at m*128, chunk c at position c ^ ((m >> 1) & 7); the E4M3 lane (row l32, half hh)
+  // reads chunks 4 kk + hh + 2 p for the halves kk and pieces p of the K block
+  const int fsw = (l32 >> 1) & 7;
+  const uint32_t abase = lds_offset(smem);
+  uint32_t af[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) af[i] = abase + l32 * 128 + 16 * ((4 * (i >> 1) + hh + 2 * (i & 1)) ^ fsw);
+  const uint32_t sadr = abase + kScOff + 16 * l32;
+  const uint32_t ma = (uint32_t)uniform((int)lds_offset(smem + wv * kTApw * 1024));
+  uint32_t msg = (uint32_t)uniform((int)lds_offset(smem + kScOff + wv * 1024));
+  const uint32_t epb = abase + (uint32_t)(wv * 4096 + l32 * 128 + 16 * (l32 & 7) + 8 * hh);
+  const int l8 = lane >> 3;
+  const uint32_t rb = abase + (uint32_t)(wv * 4096 + l8 * 128 + 16 * ((lane & 7) ^ (l8 & 7)));
+  const uint64_t wm = uniform_u64_f4(won ? ~0ull : 0ull);
+  const uint64_t db = uniform_u64_f4((uint64_t)(a.D + (int64_t)u.row0 * N));
+  uint32_t doff = (uint32_t)(l8 * N + ncol0 + 8 * (lane & 7)) * 2u;
+  const int dstep = uniform(16 * N);
+  const int rbe = uniform(max(2, (u.mrows + 31) / 32));
+  const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
+  int ks, q, t, inc, inc4, m0v = 0;
+  uint64_t sv;
+  if constexpr (ROWS == 192)
+    MOE_FP4_TALL_ASM(MOE_FP4_TALL192_LOOP_PACKED, MOE_FP4_TALL192_AO_OUTS, MOE_FP4_TALL192_CLOBBERS);
+  else
+    MOE_FP4_TALL_ASM(MOE_FP4_TALL256_LOOP_PACKED, MOE_FP4_TALL256_AO_OUTS, MOE_FP4_TALL256_CLOBBERS);
+}
+
+template <int ROWS>
+__global__ __launch_bounds__(256, 1) void gemm_fp4_tall_kernel(const GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sm[Fp4TallCfg<ROWS>::kLds];
+  __shared__ SchedSmem s_sched;
+  const Sched sc{&s_sched};
+  sched_build<ROWS>(a, sc);
+  const Walk walk = sched_walk(s_sched.total);
+  const int lane = lane_id();
+  const int wv = uniform(threadIdx.x >> 6);
+  for (int v = walk.first; v < walk.end; v += walk.stride) {
+    const Unit u = sched_unit<ROWS>(a, sc, v);
+    fp4_unit_tall<ROWS>(a, u, sm, wv, lane);
+  }
+}
+
+template <int ROWS>
+static hipError_t launch_fp4_tall(const GemmArgs& a, hipStream_t s) {
+  const int cus = device_info().cus;
+  int grid = cus - cus % kXcds;
+  if (grid < kXcds) grid = kXcds;
+  gemm_fp4_tall_kernel<ROWS><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_fp4(const GemmArgs& a, int expected_m, hipStream_t s) {
-  const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 64);
+  const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 256);
   if (a.wpacked) {
     if (em <= 16) return launch_fp4<1, 8, true>(a, s);
-    return launch_fp4<4, 6, true>(a, s);
+    // the tall tiles copy 4 K blocks of row scales per 16-byte load
+    const bool tall_ok = (a.K / 128) % MOE_FP8_TALL_SCALE_GROUP == 0 && (((uintptr_t)a.SFA) & 15) == 0;
+    if (em <= 64 || !tall_ok) return launch_fp4<4, 6, true>(a, s);
+    if (em >= 256) return launch_fp4_tall<256>(a, s);
+    return launch_fp4_tall<192>(a, s);
   }
   if (em <= 16) return launch_fp4<1, 8, false>(a, s);
   return launch_fp4<4, 6, false>(a, s);

@@ -80,9 +80,11 @@ GROUP = 4         # K blocks per row-scale copy (one 16-byte copy per row)
 
 class Cfg:
     def __init__(self, rows: int, S: int, name: str, dtype: str = "fp8"):
-        assert rows in (192, 256) and dtype in ("fp8", "bf16")
+        assert rows in (192, 256) and dtype in ("fp8", "bf16", "fp4")
         self.rows, self.S, self.name = rows, S, name
         self.bf16 = dtype == "bf16"               # bf16 operands: four 32x32x16 instructions per 128-byte step, no scales
+        self.fp4 = dtype == "fp4"                 # MXFP4 weights (packed order only): 16 bytes per lane and K half,
+        # one E8M0 scale per 32 K values and lane (two scale dwords per K block, shifted per lane)
         assert S == GROUP, "the unrolled loop body is one scale group"
         self.slot_a = rows * 128                 # activation bytes of one ring slot in LDS
         self.slot = self.slot_a                   # bytes of one ring slot
@@ -90,20 +92,23 @@ class Cfg:
         self.lds = self.sc_off + (0 if self.bf16 else 2 * SCALE_ROWS * 16)
         self.rt = rows // 32                      # 32-row tiles per unit at most
         self.apw = rows // 32                     # 1-KB activation copies per wave per K block
-        self.ops = 8 + self.apw + (0 if self.bf16 else 1)  # vector-memory instructions per wave per K block (fp8:
-        # +1 for the weight scale, +1 more for the blocks that start a scale group)
+        self.nsw = 0 if self.bf16 else (2 if self.fp4 else 1)  # weight-scale loads per K block
+        self.ops = (4 if self.fp4 else 8) + self.apw + self.nsw  # vector-memory instructions per wave per K block
+        # (+1 more for the blocks that start a row-scale group)
         assert 2 * self.ops + 2 <= 63, "vmcnt holds at most 63"
         self.wbase = 256 - 32 * S
         self.nacc = 32 * self.rt
         self.frag_v = self.nacc + 16 * NBUF > 256
         self.v_frag = self.wbase - 16 * NBUF
-        self.v_alo = (self.v_frag if self.frag_v else self.wbase) - (6 * S + 6)  # even: 64-bit pairs
+        nsw = max(1, self.nsw)
+        nlo = 4 * S + S + nsw * S + nsw + NBUF + 1
+        self.v_alo = (self.v_frag if self.frag_v else self.wbase) - (nlo + nlo % 2)  # even: 64-bit pairs
         self.v_aadr = self.v_alo                  # slot s, (kk, p): v_aadr + 4s + 2kk + p
         self.v_sadr = self.v_alo + 4 * S
-        self.v_swr = self.v_sadr + S
-        self.v_swe = self.v_swr + S
-        self.v_sae = self.v_swe + 1                # one per fragment buffer
-        self.v_doff = self.v_swe + 1 + NBUF
+        self.v_swr = self.v_sadr + S              # weight-scale ring: slot s (and fp4 K half kk) at v_swr + nsw s + kk
+        self.v_swe = self.v_swr + nsw * S         # the block's weight exponent(s): fp4 K half kk at v_swe + kk
+        self.v_sae = self.v_swe + nsw             # one per fragment buffer
+        self.v_doff = self.v_sae + NBUF
         assert self.v_alo >= 0
         # epilogue registers, in weight-ring slots 0 .. 2 (idle during the last K block, which uses slot 3):
         # two 16-register read-back buffers, 32 temporaries, 16 packed bf16 pairs, 8 LDS chunk addresses
@@ -147,6 +152,10 @@ def issue_items(cfg, t, packed):
     items = []
     for ct in range(2):
         for kk in range(2):
+            if cfg.fp4:  # E2M1: 16 bytes per lane and K half (packed: chunk 2 kk + h of the column's 1 KB fragment)
+                assert packed
+                items.append([f"global_load_dwordx4 {wreg(cfg, t, ct, kk, 0, 3)}, %[wo{ct}], %[wb] offset:{512 * kk}"])
+                continue
             for p in range(2):
                 off = kk * 1024 + p * 256 if packed else kk * 64 + p * 16
                 items.append([f"global_load_dwordx4 {wreg(cfg, t, ct, kk, 4 * p, 4 * p + 3)}, %[wo{ct}], %[wb] "
@@ -161,17 +170,30 @@ def issue_items(cfg, t, packed):
         upd += [f"v_add_u32_e32 %[wo{ct}], %[t], %[wo{ct}]" for ct in range(2)]
         upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(cfg.apw)]
         return items, upd
-    items.append([f"global_load_dword v{cfg.v_swr + t}, %[wso], %[swb]"])
+    if cfg.fp4:  # the scale dwords of K halves 0 and 1 (block 2 kk + h of the lane's 16-column group)
+        items += [[f"global_load_dword v{cfg.v_swr + 2 * t + kk}, %[wso], %[swb]" + (" offset:128" if kk else "")]
+                  for kk in range(2)]
+    else:
+        items.append([f"global_load_dword v{cfg.v_swr + t}, %[wso], %[swb]"])
     if t % GROUP == 0:
         items.append(["s_mov_b32 m0, %[msg]", "s_nop 0", "global_load_lds_dwordx4 %[so], %[sb]"])
         upd += ["s_xor_b32 %[msg], %[msg], " + str(SCALE_ROWS * 16), f"s_add_u32 %[t], %[q], {GROUP}",
                 "s_cmp_lt_u32 %[t], %[kb]", "s_cselect_b32 %[inc4], 16, 0", "v_add_u32_e32 %[so], %[inc4], %[so]"]
     upd += ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0",
-           "s_cselect_b32 %[t], %[wstep], 0", "s_cselect_b32 %[inc4], 4, 0"]
+           "s_cselect_b32 %[t], %[wstep], 0", "s_cselect_b32 %[inc4], " + ("%[sstep]" if cfg.fp4 else "4") + ", 0"]
     upd += [f"v_add_u32_e32 %[wo{ct}], %[t], %[wo{ct}]" for ct in range(2)]
     upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(cfg.apw)]
     upd += ["v_add_u32_e32 %[wso], %[inc4], %[wso]"]
     return items, upd
+
+
+def weight_exponents(cfg, s):
+    """The weight scale exponents of ring slot s: the fp32 scale's bit pattern shifted right by 23 (FP8), or
+    (fp4) each K half's scale dword shifted right by 8 (l32 / 16) bytes, so that byte 2 ct is the scale of the
+    lane's column in column tile ct."""
+    if cfg.fp4:
+        return [f"v_lshrrev_b32_e32 v{cfg.v_swe + kk}, %[fsh], v{cfg.v_swr + 2 * s + kk}" for kk in range(2)]
+    return [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}"]
 
 
 def frag_reads(cfg, s, b, j):
@@ -206,6 +228,9 @@ def mfma(cfg, s, b, j, ct, kk, src_zero):
     values in both operands, so the products match), the second accumulating onto the first."""
     a0 = cfg.acc(j, ct)
     acc = f"a[{a0}:{a0 + 15}]"
+    if cfg.fp4:  # E2M1 A operand (cbsz 4), 4 registers; scale byte 2 ct of the lane's shifted scale dword
+        return [f"v_mfma_scale_f32_32x32x64_f8f6f4 {acc}, {wreg(cfg, s, ct, kk, 0, 3)}, {cfg.buf(b, kk)}, "
+                f"{'0' if src_zero else acc}, v{cfg.v_swe + kk}, v{cfg.v_sae + b} op_sel_hi:[{ct},0,0] cbsz:4"]
     if not cfg.bf16:
         return [f"v_mfma_scale_f32_32x32x64_f8f6f4 {acc}, {wreg(cfg, s, ct, kk, 0, 7)}, {cfg.buf(b, kk)}, "
                 f"{'0' if src_zero else acc}, v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]"]
@@ -237,8 +262,8 @@ def compute(cfg, s, t, packed, rbe, final=False, first=False):
         place[(i * nslots) // len(items)].append(it)
     sadr = cfg.v_sadr  # row r's scale of K block s of the group at r * 16 + 4 s
     out = (["s_waitcnt lgkmcnt(0)"] if cfg.bf16 else
-           [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}", "s_waitcnt lgkmcnt(0)",
-            f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"])
+           weight_exponents(cfg, s) + ["s_waitcnt lgkmcnt(0)",
+                                       f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"])
     for j in range(rbe):
         b = cfg.bufid(j)
         if j + 1 < rbe:
@@ -349,8 +374,8 @@ def compute_last(cfg, s, rbe):
     epilogue after the loop).  Row tile j + 1's fragments are read after row tile j's first matrix
     instruction, and the LDS operations in flight stay within the 15 that lgkmcnt counts."""
     out = (["s_waitcnt lgkmcnt(0)"] if cfg.bf16 else
-           [f"v_lshrrev_b32_e32 v{cfg.v_swe}, 23, v{cfg.v_swr + s}", "s_waitcnt lgkmcnt(0)",
-            f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"])
+           weight_exponents(cfg, s) + ["s_waitcnt lgkmcnt(0)",
+                                       f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"])
     for j in range(rbe):
         b = cfg.bufid(j)
         nxt = j + 1 < rbe
@@ -436,7 +461,8 @@ def clobbers(cfg):
 
 
 CONFIGS = [Cfg(192, 4, "TALL192"), Cfg(256, 4, "TALL256"),
-           Cfg(192, 4, "BF16_TALL192", "bf16"), Cfg(256, 4, "BF16_TALL256", "bf16")]
+           Cfg(192, 4, "BF16_TALL192", "bf16"), Cfg(256, 4, "BF16_TALL256", "bf16"),
+           Cfg(192, 4, "FP4_TALL192", "fp4"), Cfg(256, 4, "FP4_TALL256", "fp4")]
 
 
 def main():
@@ -444,7 +470,7 @@ def main():
         f.write("// Generated by gen_fp8_asm.py -- do not edit.\n")
         f.write(f"#define MOE_FP8_TALL_SCALE_ROWS {SCALE_ROWS}\n#define MOE_FP8_TALL_SCALE_GROUP {GROUP}\n")
         for cfg in CONFIGS:
-            n = cfg.name if cfg.bf16 else "FP8_" + cfg.name
+            n = cfg.name if cfg.bf16 or cfg.fp4 else "FP8_" + cfg.name
             f.write(f"// {n}: {cfg.rows} rows, ring {cfg.S}, {cfg.rt} row tiles, {cfg.ops} loads/K block "
                     + ("\n" if cfg.bf16 else "(+1 per scale group)\n"))
             f.write(f"#define MOE_{n}_SLOT_A {cfg.slot_a}\n#define MOE_{n}_SLOT {cfg.slot}\n"
@@ -452,7 +478,7 @@ def main():
                     f"#define MOE_{n}_APW {cfg.apw}\n#define MOE_{n}_S {cfg.S}\n")
             f.write(f"#define MOE_{n}_AO_OUTS " + ", ".join(f'[ao{i}] "+v"(ao[{i}])' for i in range(cfg.apw))
                     + "\n")
-            for suffix, packed in (("", False), ("_PACKED", True)):
+            for suffix, packed in ((("_PACKED", True),) if cfg.fp4 else (("", False), ("_PACKED", True))):
                 f.write(f"#define MOE_{n}_LOOP{suffix} \\\n")
                 for ln in program(cfg, packed):
                     f.write(f'  "{ln}\\n" \\\n')

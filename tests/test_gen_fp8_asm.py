@@ -1,5 +1,5 @@
-"""Host checks of the generated tall-tile loops (gen_fp8_asm.py; FP8 and bf16 configurations): the text the
-build compiles into the kernels must keep the invariants the loop relies on.  No GPU needed."""
+"""Host checks of the generated tall-tile loops (gen_fp8_asm.py; FP8, bf16 and MXFP4 configurations): the text
+the build compiles into the kernels must keep the invariants the loop relies on.  No GPU needed."""
 
 import importlib.util
 import os
@@ -19,9 +19,13 @@ def gen():
     return m
 
 
+def _orders(cfg):
+    return (True,) if cfg.fp4 else (False, True)  # MXFP4 weights: packed order only
+
+
 def _programs(gen):
     for cfg in gen.CONFIGS:
-        for packed in (False, True):
+        for packed in _orders(cfg):
             yield cfg, packed, gen.program(cfg, packed)
 
 
@@ -60,7 +64,7 @@ def _regs(text):
 def _reads_writes(line):
     """Fixed registers an instruction reads and writes (operands the compiler assigns, %[...], are not
     fixed registers and are left out)."""
-    line = re.sub(r"\s+op_sel_hi:\[[^\]]*\]", "", line)
+    line = re.sub(r"\s+(op_sel(_hi)?:\[[^\]]*\]|cbsz:\d+)", "", line)
     mnem, _, rest = line.partition(" ")
     ops = [o.strip().split()[0] for o in rest.split(",")] if rest else []
     if mnem.startswith(("global_store", "ds_write", "global_load_lds", "s_")) or not ops:
@@ -159,13 +163,13 @@ def _walk(prog, rbe, kb):
 
 @pytest.mark.parametrize("kb", [4, 8, 12, 56])
 def test_each_unit_path_runs_its_blocks_once(gen, kb):
-    """For every row-tile count: 4 MFMAs (FP8; 8 bf16 ones) per row tile and K block, one barrier per K block
+    """For every row-tile count: 4 MFMAs (FP8, MXFP4; 8 bf16 ones) per row tile and K block, one barrier per K block
     but the last, plus the prologue's and the one that ends the unit (so all waves of a workgroup meet at the
     same barriers), the loads of exactly kb blocks (FP8: with one row-scale copy per 4 blocks), 4 stores (of 8
     rows each) per row tile, at most 15 LDS operations in flight, and no register used before the load or LDS
     read that fills it has been waited for."""
     for cfg in gen.CONFIGS:
-        for packed in (False, True):
+        for packed in _orders(cfg):
             prog = gen.program(cfg, packed)
             for rbe in range(2, cfg.rt + 1):
                 c = _walk(prog, rbe, kb)

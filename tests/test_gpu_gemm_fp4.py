@@ -110,10 +110,11 @@ def _check(c, D, exact=False):
     gemm_tolerance_check(oracle.bf16_bits_to_f64(bits[valid]), ref[valid], 1e-3)
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_fp4_one_hot_rows_pin_the_operand_layout(packed):
+@pytest.mark.parametrize("packed,expected_m", [(False, 64), (True, 64), (True, 128), (True, 256)])
+def test_fp4_one_hot_rows_pin_the_operand_layout(packed, expected_m):
     """Row r has one activation 2.0 at k_r (scale 1): D[r] = 2 * column k_r of the dequantised weights, exactly
-    (packed: also pins which byte of the scale dword each step's instruction selects)."""
+    (packed: also pins which byte of the scale dword each step's instruction selects; expected_m 128 and 256 run
+    the tall tiles, whose 32x32x64 instruction lays K out differently from the 16x16x128 one)."""
     require_gpu()
     c = _case(2, [40], N=256, K=512, layout=moe.LAYOUT_CONTIGUOUS)
     ks = [0, 1, 2, 31, 32, 33, 63, 64, 95, 127, 128, 129, 200, 255, 300, 383, 384, 447, 510, 511] + list(range(3, 23))
@@ -121,7 +122,7 @@ def test_fp4_one_hot_rows_pin_the_operand_layout(packed):
     c["sa"][:] = 1.0
     for r, k in enumerate(ks[:40]):
         c["a"][r, k] = 0x40
-    D = _run(c, 64, packed)
+    D = _run(c, expected_m, packed)
     bits = u16(D)[:40]
     wd = oracle.dequant_weight_fp4(c["w4"][0], c["sw"][0])
     for r, k in enumerate(ks[:40]):
@@ -162,14 +163,54 @@ def test_pack_weight_fp4_matches_the_layout_definition():
     assert np.array_equal(swp.cpu().numpy().reshape(E, -1), cs)
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_fp4_small_integers_exact_and_deterministic(packed):
+@pytest.mark.parametrize("packed,expected_m", [(False, 64), (True, 64), (True, 128), (True, 256)])
+def test_fp4_small_integers_exact_and_deterministic(packed, expected_m):
     require_gpu()
-    c = _case(5, [7, 64, 129], N=512, K=512, layout=moe.LAYOUT_CONTIGUOUS, ints=True)
-    D = _run(c, 64, packed)
+    c = _case(5, [7, 64, 129, 300], N=512, K=512, layout=moe.LAYOUT_CONTIGUOUS, ints=True)
+    D = _run(c, expected_m, packed)
     _check(c, D, exact=True)
     for _ in range(20):
-        assert torch.equal(_run(c, 64, packed), D)
+        assert torch.equal(_run(c, expected_m, packed), D)
+
+
+@pytest.mark.parametrize("K", [1536, 2560])
+def test_fp4_tall_every_row_tile_count_long_k(K):
+    """Packed weights on both tall heights: units of every 32-row count (1..256 rows, so every loop body),
+    N = 384 (the second 256-column tile has two idle waves), K/128 = 12 or 20 blocks (main loop iterations
+    before the last)."""
+    require_gpu()
+    counts = [32 * r - 5 for r in range(1, 9)] + [32 * r for r in range(1, 9)] + [0, 3, 256 + 100, 192 + 40]
+    c = _case(71 + K, counts, N=384, K=K, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (128, 256):
+        _check(c, _run(c, em, True))
+
+
+def test_fp4_tall_masked_segments_and_short_k_fallback():
+    """Masked segments taller than a tall tile; K/128 not a multiple of 4 (the tall loop's row-scale copies
+    cover 4 K blocks: such calls run on the 64-row tile)."""
+    require_gpu()
+    c = _case(12, [150, 0, 300, 65], N=256, K=1024, layout=moe.LAYOUT_MASKED, max_m=300)
+    for em in (0, 200, 256):
+        _check(c, _run(c, em, True))
+    c = _case(14, [0, 1, 17, 130, 300], N=256, K=640, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (0, 128, 256):
+        _check(c, _run(c, em, True))
+
+
+def test_fp4_tall_degenerate_expert_counts():
+    """No rows at all, 1024 experts with 0..3 rows (N = 128: half of each tall tile's waves store nothing), and
+    one expert with several tall chunks."""
+    require_gpu()
+    c = _case(31, [0] * 8, N=256, K=512, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (128, 256):
+        _check(c, _run(c, em, True))
+    counts = np.random.default_rng(33).integers(0, 4, size=1024).tolist()
+    c = _case(33, counts, N=128, K=512, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (128, 256):
+        _check(c, _run(c, em, True))
+    c = _case(34, [700], N=384, K=512, layout=moe.LAYOUT_CONTIGUOUS)
+    for em in (128, 256):
+        _check(c, _run(c, em, True))
 
 
 def test_fp4_full_size_dsv3_decode_and_prefill_samples():
