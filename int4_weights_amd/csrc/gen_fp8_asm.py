@@ -79,9 +79,10 @@ GROUP = 4         # K blocks per row-scale copy (one 16-byte copy per row)
 
 
 class Cfg:
-    def __init__(self, rows: int, S: int, name: str, dtype: str = "fp8"):
+    def __init__(self, rows: int, S: int, name: str, dtype: str = "fp8", wnt: bool = False):
         assert rows in (192, 256) and dtype in ("fp8", "bf16", "fp4")
         self.rows, self.S, self.name = rows, S, name
+        self.wnt = wnt                            # weight loads nontemporal (each weight byte read by one unit)
         self.bf16 = dtype == "bf16"               # bf16 operands: four 32x32x16 instructions per 128-byte step, no scales
         self.fp4 = dtype == "fp4"                 # MXFP4 weights (packed order only): 16 bytes per lane and K half,
         # one E8M0 scale per 32 K values and lane (two scale dwords per K block, shifted per lane)
@@ -154,12 +155,13 @@ def issue_items(cfg, t, packed):
         for kk in range(2):
             if cfg.fp4:  # E2M1: 16 bytes per lane and K half (packed: chunk 2 kk + h of the column's 1 KB fragment)
                 assert packed
-                items.append([f"global_load_dwordx4 {wreg(cfg, t, ct, kk, 0, 3)}, %[wo{ct}], %[wb] offset:{512 * kk}"])
+                items.append([f"global_load_dwordx4 {wreg(cfg, t, ct, kk, 0, 3)}, %[wo{ct}], %[wb] offset:{512 * kk}"
+                              + (" nt" if cfg.wnt else "")])
                 continue
             for p in range(2):
                 off = kk * 1024 + p * 256 if packed else kk * 64 + p * 16
                 items.append([f"global_load_dwordx4 {wreg(cfg, t, ct, kk, 4 * p, 4 * p + 3)}, %[wo{ct}], %[wb] "
-                              f"offset:{off}"])
+                              f"offset:{off}" + (" nt" if cfg.wnt else "")])
     for i in range(cfg.apw):
         items.append([f"s_add_u32 m0, %[ma], {t * cfg.slot + i * 1024}", "s_nop 0",
                       f"global_load_lds_dwordx4 %[ao{i}], %[ab]"])
@@ -460,9 +462,11 @@ def clobbers(cfg):
     return ", ".join(regs)
 
 
-CONFIGS = [Cfg(192, 4, "TALL192"), Cfg(256, 4, "TALL256"),
-           Cfg(192, 4, "BF16_TALL192", "bf16"), Cfg(256, 4, "BF16_TALL256", "bf16"),
-           Cfg(192, 4, "FP4_TALL192", "fp4"), Cfg(256, 4, "FP4_TALL256", "fp4")]
+# The 192-row tiles serve experts of about one chunk (each weight byte read by one unit): their weight loads are
+# nontemporal.  The 256-row tiles serve experts of many chunks, whose units re-read the weights from L2.
+CONFIGS = [Cfg(192, 4, "TALL192", wnt=True), Cfg(256, 4, "TALL256"),
+           Cfg(192, 4, "BF16_TALL192", "bf16", wnt=True), Cfg(256, 4, "BF16_TALL256", "bf16"),
+           Cfg(192, 4, "FP4_TALL192", "fp4", wnt=True), Cfg(256, 4, "FP4_TALL256", "fp4")]
 
 
 def main():
