@@ -473,8 +473,10 @@ def time_workload(args, torch, wl, cycles_per_ms):
     return start.elapsed_time(end) / args.steps, tm.per_kernel(), host_ms
 
 
-def clock_pass(torch, wl, seconds=0.6):
-    """GPU clock (MHz) sampled every 5 ms by the SMI library while steps run back to back."""
+def clock_pass(torch, wl, seconds=2.2):
+    """GPU clock (MHz) while steps run back to back.  The SMI's current GFX clock is refreshed about once a
+    second (each value covers the preceding interval), so the pass runs for a little over two seconds, the
+    value is read every 10 ms, and only the values published after the pass started are kept."""
     samples, stop = [], threading.Event()
     try:
         torch.cuda.clock_rate()
@@ -487,7 +489,7 @@ def clock_pass(torch, wl, seconds=0.6):
                 samples.append(float(torch.cuda.clock_rate()))
             except Exception:
                 pass
-            time.sleep(0.005)
+            time.sleep(0.01)
 
     tm = Timer(torch, wl["names"], 1)
     th = threading.Thread(target=sampler, daemon=True)
@@ -503,12 +505,19 @@ def clock_pass(torch, wl, seconds=0.6):
     torch.cuda.synchronize()
     stop.set()
     th.join()
-    busy = samples[2:] if len(samples) > 4 else samples
-    if not busy:
+    if not samples:
         return {"error": "no samples"}
-    return {"median_mhz": statistics.median(busy), "min_mhz": min(busy), "max_mhz": max(busy),
-            "samples": len(busy), "steps": n,
-            "source": "torch.cuda.clock_rate() (SMI current GFX clock) every 5 ms over back-to-back steps"}
+    # drop the value current when the pass started (it covers the time before it)
+    first_change = next((i for i, v in enumerate(samples) if v != samples[0]), None)
+    if first_change is None:
+        return {"median_mhz": samples[0], "min_mhz": samples[0], "max_mhz": samples[0], "updates": 0, "steps": n,
+                "note": "the SMI value did not change during the pass",
+                "source": "torch.cuda.clock_rate() (SMI current GFX clock, refreshed about once a second)"}
+    busy = samples[first_change:]
+    updates = 1 + sum(1 for a, b in zip(busy, busy[1:]) if a != b)
+    return {"median_mhz": statistics.median(busy), "min_mhz": min(busy), "max_mhz": max(busy), "updates": updates,
+            "steps": n, "source": "torch.cuda.clock_rate() (SMI current GFX clock, refreshed about once a second), "
+                                  "read every 10 ms over back-to-back steps; the value current at the start dropped"}
 
 
 def summarise(args, np, wl, ms_step, per, host_ms, clock):

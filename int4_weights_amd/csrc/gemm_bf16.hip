@@ -253,8 +253,8 @@ __device__ __forceinline__ void bf16_unit_tall(const GemmArgs& a, const Unit& u,
   uint32_t ao[kTApw];
 #pragma unroll
   for (int i = 0; i < kTApw; ++i) {
-    const int r = 8 * (wv * kTApw + i) + (lane >> 3);  // tile row this lane copies
-    const int c = (lane & 7) ^ ((r >> 1) & 7);         // its chunk, landing at position lane & 7
+    const int r = 8 * (4 * i + wv) + (lane >> 3);  // tile row this lane copies (copy i of the wave)
+    const int c = (lane & 7) ^ ((r >> 1) & 7);     // its chunk, landing at position lane & 7
     ao[i] = (uint32_t)min(r, u.mrows - 1) * rowb + 16u * c;
   }
   const uint64_t sb = 0, swb = 0;
@@ -267,7 +267,7 @@ __device__ __forceinline__ void bf16_unit_tall(const GemmArgs& a, const Unit& u,
 #pragma unroll
   for (int i = 0; i < 4; ++i) af[i] = abase + l32 * 128 + 16 * ((4 * (i >> 1) + 2 * hh + (i & 1)) ^ fsw);
   const uint32_t sadr = 0;
-  const uint32_t ma = (uint32_t)uniform((int)lds_offset(smem + wv * kTApw * 1024));
+  const uint32_t ma = (uint32_t)uniform((int)lds_offset(smem + wv * 1024));  // copy i at + 4096 i
   uint32_t msg = 0;
   // epilogue staging, as in the FP8 tall tile (each wave's 4 KB of ring slot 0)
   const uint32_t epb = abase + (uint32_t)(wv * 4096 + l32 * 128 + 16 * (l32 & 7) + 8 * hh);

@@ -301,7 +301,7 @@ __device__ __forceinline__ void fp4_unit_tall(const GemmArgs& a, const Unit& u, 
   uint32_t ao[kTApw];
 #pragma unroll
   for (int i = 0; i < kTApw; ++i) {
-    const int r = 8 * (wv * kTApw + i) + (lane >> 3);
+    const int r = 8 * (4 * i + wv) + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     ao[i] = (uint32_t)min(r, u.mrows - 1) * (uint32_t)K + 16u * c;
   }
@@ -315,7 +315,7 @@ __device__ __forceinline__ void fp4_unit_tall(const GemmArgs& a, const Unit& u, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) af[i] = abase + l32 * 128 + 16 * ((4 * (i >> 1) + hh + 2 * (i & 1)) ^ fsw);
   const uint32_t sadr = abase + kScOff + 16 * l32;
-  const uint32_t ma = (uint32_t)uniform((int)lds_offset(smem + wv * kTApw * 1024));
+  const uint32_t ma = (uint32_t)uniform((int)lds_offset(smem + wv * 1024));  // copy i at + 4096 i
   uint32_t msg = (uint32_t)uniform((int)lds_offset(smem + kScOff + wv * 1024));
   const uint32_t epb = abase + (uint32_t)(wv * 4096 + l32 * 128 + 16 * (l32 & 7) + 8 * hh);
   const int l8 = lane >> 3;

@@ -322,8 +322,8 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   uint32_t ao[kTApw];
 #pragma unroll
   for (int i = 0; i < kTApw; ++i) {
-    const int r = 8 * (wv * kTApw + i) + (lane >> 3);  // tile row this lane copies
-    const int c = (lane & 7) ^ ((r >> 1) & 7);         // its chunk, landing at position lane & 7
+    const int r = 8 * (4 * i + wv) + (lane >> 3);  // tile row this lane copies (copy i of the wave)
+    const int c = (lane & 7) ^ ((r >> 1) & 7);     // its chunk, landing at position lane & 7
     ao[i] = (uint32_t)min(r, u.mrows - 1) * (uint32_t)K + 16u * c;
   }
   // row scales: lane copies row 64 wv + lane (the unit's last row past its end), 16 bytes per 4 K blocks
@@ -341,7 +341,7 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) af[i] = abase + l32 * 128 + 16 * ((4 * (i >> 1) + 2 * hh + (i & 1)) ^ fsw);
   const uint32_t sadr = abase + kScOff + 16 * l32;  // row scale of row tile j, block s of the group: +512 j + 4 s
-  const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.b[wv * kTApw * 1024]));
+  const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.b[wv * 1024]));  // copy i at + 4096 i
   uint32_t msg = (uint32_t)uniform((int)lds_offset(&sm.b[kScOff + wv * 1024]));  // group buffer 0, this wave's rows
   // epilogue: one 32-row tile of the wave's bf16 rows at a time goes through its own 4 KB of ring slot 0
   // (row m at m*128, 16-byte chunk c at position c ^ (m & 7)); each lane writes 8 bytes of row l32 (epb:

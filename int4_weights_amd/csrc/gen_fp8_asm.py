@@ -33,6 +33,10 @@ block's fp32 row scales (one global_load_lds_dword per wave: 64 rows each, the
 4 waves cover 256 rows); each wave also loads its weight scale for the block
 into a VGPR ring.  The exponent is the fp32 bit pattern shifted right by 23.
 
+Activation copies.  A unit of rbe row tiles copies only the 32 rbe rows it computes: copy i of wave w moves
+rows 8 (4 i + w) .. +7 of the K block (1 KB) into the ring slot, so each loop body issues rbe copies per wave
+and K block, with its own wait counts and its own prologue.
+
 Pipeline.  Step ks multiplies K block ks and issues the loads of block ks + 3
 (into the slot block ks - 1 used).  The barrier that publishes block ks + 1 sits
 inside step ks, after the fragments of the step's last row tile have been read
@@ -92,9 +96,10 @@ class Cfg:
         self.sc_off = S * self.slot               # (fp8) two scale-group buffers of SCALE_ROWS x 16 bytes follow
         self.lds = self.sc_off + (0 if self.bf16 else 2 * SCALE_ROWS * 16)
         self.rt = rows // 32                      # 32-row tiles per unit at most
-        self.apw = rows // 32                     # 1-KB activation copies per wave per K block
+        self.apw = rows // 32                     # 1-KB activation copies per wave per K block at most (a unit of
+        # rbe row tiles issues rbe: copy i of wave w is rows 8 (4 i + w) .. +7)
         self.nsw = 0 if self.bf16 else (2 if self.fp4 else 1)  # weight-scale loads per K block
-        self.ops = (4 if self.fp4 else 8) + self.apw + self.nsw  # vector-memory instructions per wave per K block
+        self.ops = self.ops_for(self.apw)          # vector-memory instructions per wave per K block, at most
         # (+1 more for the blocks that start a row-scale group)
         assert 2 * self.ops + 2 <= 63, "vmcnt holds at most 63"
         self.wbase = 256 - 32 * S
@@ -124,11 +129,15 @@ class Cfg:
     def acc(self, j, ct):
         return 32 * j + 16 * ct
 
-    def wait_at(self, s, issued):
+    def ops_for(self, rbe):
+        """Vector-memory instructions per wave per K block for units of rbe row tiles (rbe activation copies)."""
+        return (4 if self.fp4 else 8) + rbe + self.nsw
+
+    def wait_at(self, s, issued, ops):
         """Loads allowed outstanding at the barrier of step s (K block ks = s mod S) that publishes block
         ks + 1: those of block ks + 2 (issued in the previous step, plus one if it starts a scale group) and
         the `issued` loads of block ks + 3 this step has issued so far."""
-        return self.ops + (1 if (s + 2) % GROUP == 0 and not self.bf16 else 0) + issued
+        return ops + (1 if (s + 2) % GROUP == 0 and not self.bf16 else 0) + issued
 
     @staticmethod
     def bufid(j):
@@ -145,7 +154,7 @@ def wreg(cfg, s, ct, kk, lo, hi):
     return f"v[{r + lo}:{r + hi}]"
 
 
-def issue_items(cfg, t, packed):
+def issue_items(cfg, t, packed, rbe):
     """The loads of one K block into ring slot t, as separate items, and the offset update after them
     (offsets advance unless the next block would be past the last one).  Block t mod S == 0 starts a scale
     group: one 16-byte copy per row of the group's 4 row scales into the group buffer %[msg] points at
@@ -162,15 +171,15 @@ def issue_items(cfg, t, packed):
                 off = kk * 1024 + p * 256 if packed else kk * 64 + p * 16
                 items.append([f"global_load_dwordx4 {wreg(cfg, t, ct, kk, 4 * p, 4 * p + 3)}, %[wo{ct}], %[wb] "
                               f"offset:{off}" + (" nt" if cfg.wnt else "")])
-    for i in range(cfg.apw):
-        items.append([f"s_add_u32 m0, %[ma], {t * cfg.slot + i * 1024}", "s_nop 0",
+    for i in range(rbe):  # rows 8 (4 i + w) .. +7 of the slot for wave w: the unit's rbe row tiles, no more
+        items.append([f"s_add_u32 m0, %[ma], {t * cfg.slot + i * 4096}", "s_nop 0",
                       f"global_load_lds_dwordx4 %[ao{i}], %[ab]"])
     upd = []
     if cfg.bf16:  # no scales: only the weight and activation offsets advance
         upd += ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0",
                 "s_cselect_b32 %[t], %[wstep], 0"]
         upd += [f"v_add_u32_e32 %[wo{ct}], %[t], %[wo{ct}]" for ct in range(2)]
-        upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(cfg.apw)]
+        upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(rbe)]
         return items, upd
     if cfg.fp4:  # the scale dwords of K halves 0 and 1 (block 2 kk + h of the lane's 16-column group)
         items += [[f"global_load_dword v{cfg.v_swr + 2 * t + kk}, %[wso], %[swb]" + (" offset:128" if kk else "")]
@@ -184,7 +193,7 @@ def issue_items(cfg, t, packed):
     upd += ["s_add_u32 %[q], %[q], 1", "s_cmp_lt_u32 %[q], %[kb]", "s_cselect_b32 %[inc], 128, 0",
            "s_cselect_b32 %[t], %[wstep], 0", "s_cselect_b32 %[inc4], " + ("%[sstep]" if cfg.fp4 else "4") + ", 0"]
     upd += [f"v_add_u32_e32 %[wo{ct}], %[t], %[wo{ct}]" for ct in range(2)]
-    upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(cfg.apw)]
+    upd += [f"v_add_u32_e32 %[ao{i}], %[inc], %[ao{i}]" for i in range(rbe)]
     upd += ["v_add_u32_e32 %[wso], %[inc4], %[wso]"]
     return items, upd
 
@@ -255,7 +264,7 @@ def compute(cfg, s, t, packed, rbe, final=False, first=False):
     accumulator, so the accumulators need no zeroing."""
     if final and s == cfg.S - 1:
         return compute_last(cfg, s, rbe)
-    items, upd = issue_items(cfg, t, packed)
+    items, upd = issue_items(cfg, t, packed, rbe)
     if final and s > 0:
         items, upd = [], []
     nslots = 4 * rbe
@@ -285,7 +294,7 @@ def compute(cfg, s, t, packed, rbe, final=False, first=False):
                                                [f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"])
             if j + 2 == rbe and not (final and s == cfg.S - 1):  # row tile j + 1 is the last one
                 issued = sum(len(place[i]) for i in range(4 * (j + 1)))
-                wait = 0 if final and s == 2 else cfg.wait_at(s, issued)
+                wait = 0 if final and s == 2 else cfg.wait_at(s, issued, cfg.ops_for(rbe))
                 out += publish(cfg, s, wait)
     out += upd
     return out
@@ -426,6 +435,18 @@ def epilogue(cfg, rbe):
     return out
 
 
+def prologue(cfg, packed, rbe):
+    """The loads of K blocks 0 .. 2, then block 0 in place (blocks 1 and 2 may still be in flight) and its row
+    tile 0 read into fragment buffer 2."""
+    out = ["s_mov_b32 %[q], 0"]
+    for t in range(cfg.S - 1):
+        items, upd = issue_items(cfg, t, packed, rbe)
+        out += [ins for it in items for ins in it] + upd
+    out += [f"s_waitcnt vmcnt({2 * cfg.ops_for(rbe)})", "s_barrier"] + frag_reads(cfg, 0, 2, 0) + (
+        [] if cfg.bf16 else [f"ds_read_b32 v{cfg.v_sae + 2}, v{cfg.v_sadr}"])
+    return out
+
+
 def program(cfg, packed):
     S = cfg.S
     out = []
@@ -438,18 +459,12 @@ def program(cfg, packed):
         for kk in range(2):
             for p in range(2):
                 out.append(f"v_add_u32_e32 v{cfg.v_aadr + 4 * s + 2 * kk + p}, {s * cfg.slot}, %[a{kk}{p}]")
-    out += ["s_mov_b32 %[q], 0"]
-    for t in range(S - 1):
-        items, upd = issue_items(cfg, t, packed)
-        out += [ins for it in items for ins in it] + upd
-    # block 0 in place (blocks 1 and 2 may still be in flight), then its row tile 0 into buffer 2
-    out += [f"s_waitcnt vmcnt({2 * cfg.ops})", "s_barrier"] + frag_reads(cfg, 0, 2, 0) + (
-        [] if cfg.bf16 else [f"ds_read_b32 v{cfg.v_sae + 2}, v{cfg.v_sadr}"])
-    # one loop body per row-tile count (2 .. rt): no branch between the matrix instructions of a step
+    # one prologue and loop body per row-tile count (2 .. rt): no branch between the matrix instructions of a
+    # step, and a unit copies the activation rows of its row tiles only
     for r in range(2, cfg.rt):
         out += [f"s_cmp_eq_u32 %[rbe], {r}", f"s_cbranch_scc1 {100 + r}f"]
     for r in range(cfg.rt, 1, -1):
-        out += [f"{100 + r}:"] + body(cfg, packed, r)
+        out += [f"{100 + r}:"] + prologue(cfg, packed, r) + body(cfg, packed, r)
     for r in range(cfg.rt, 1, -1):
         out += epilogue(cfg, r)
     out += ["7:", "s_barrier"]

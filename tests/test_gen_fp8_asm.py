@@ -165,7 +165,8 @@ def _walk(prog, rbe, kb):
 def test_each_unit_path_runs_its_blocks_once(gen, kb):
     """For every row-tile count: 4 MFMAs (FP8, MXFP4; 8 bf16 ones) per row tile and K block, one barrier per K block
     but the last, plus the prologue's and the one that ends the unit (so all waves of a workgroup meet at the
-    same barriers), the loads of exactly kb blocks (FP8: with one row-scale copy per 4 blocks), 4 stores (of 8
+    same barriers), the loads of exactly kb blocks (rbe activation copies per wave and block; FP8: with one
+    row-scale copy per 4 blocks), 4 stores (of 8
     rows each) per row tile, at most 15 LDS operations in flight, and no register used before the load or LDS
     read that fills it has been waited for."""
     for cfg in gen.CONFIGS:
@@ -176,7 +177,7 @@ def test_each_unit_path_runs_its_blocks_once(gen, kb):
                 assert c["mfma"] == (8 if cfg.bf16 else 4) * rbe * kb, (cfg.name, rbe, kb, c)
                 assert c["barrier"] == 1 + (kb - 1) + 1, (cfg.name, rbe, kb, c)
                 groups = 0 if cfg.bf16 else kb // gen.GROUP
-                assert c["load"] == kb * cfg.ops + groups, (cfg.name, rbe, kb, c)
+                assert c["load"] == kb * cfg.ops_for(rbe) + groups, (cfg.name, rbe, kb, c)
                 assert c["store"] == 4 * rbe, (cfg.name, rbe, kb, c)
                 assert c["lds_max"] <= 15, (cfg.name, rbe, kb, c)
 
