@@ -14,9 +14,13 @@ contiguous 128-row-aligned layout).  The other workloads (the Qwen3-shaped
 skewed prefill, whose up-projection is the MFMA-bound GEMM, the masked FP8
 decode and the 4-bit decode) are timed in the same run and reported under
 "workloads", and the DeepSeek-V3-shaped steps with MXFP4 or bf16 expert
-weights under "variants".  Prints ONE JSON line.
+weights under "variants".  The HBM-bound rooflines are given against the
+nominal 8 TB/s and, as `frac_of_measured_read`, against the rate a plain
+8 GiB streaming read reaches on the same GPU (`measured_hbm_read`).  Prints
+ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME] [--also NAMES|none] [--cpu-baseline off]
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--also NAMES|none] [--variants LIST|none]
+                    [--cpu-baseline off] [--clock off] [--ceiling off]
 """
 
 from __future__ import annotations
@@ -49,6 +53,9 @@ def parse():
                     help="weight-format variants timed in the same run: <fp4|bf16>_<workload> (or 'none')")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-experts", type=int, default=128, help="experts in the timed oracle sample")
+    ap.add_argument("--ceiling", choices=["on", "off"], default="on",
+                    help="time a plain 8 GiB streaming read (moe_stream_read) and report each HBM-bound kernel's "
+                         "fraction of it beside the nominal peak")
     ap.add_argument("--clock", choices=["on", "off"], default="on",
                     help="sample the GPU clock over back-to-back steps after the timed ones")
     ap.add_argument("--expected-m", type=int, default=0,
@@ -621,6 +628,16 @@ def run(args):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
+    ceiling = stream_ceiling(torch, moe) if args.ceiling == "on" else None
+    if ceiling and "read_gbs" in ceiling:
+        log(f"[bench] HBM streaming read (moe_stream_read, {ceiling['bytes'] / 2**30:.0f} GiB): "
+            f"{ceiling['read_gbs']:.0f} GB/s")
+        for r in list(results.values()) + list(variants.values()):
+            for key in ("roofline", "roofline_down"):
+                roof = r.get(key)
+                if roof and roof.get("bound") == "hbm":
+                    roof["frac_of_measured_read"] = roof["achieved"] / ceiling["read_gbs"]
+
     p = results[args.config]
     out = {
         "metric": METRIC,
@@ -645,7 +662,34 @@ def run(args):
         out["roofline_down"] = p["roofline_down"]
     out["workloads"] = {n: {kk: v for kk, v in r.items()} for n, r in results.items() if n != args.config}
     out["variants"] = variants
+    out["measured_hbm_read"] = ceiling
     print(json.dumps(out), flush=True)
+
+
+def stream_ceiling(torch, moe, gib=8, reps=5):
+    """The HBM read rate a plain streaming kernel (moe_stream_read) reaches on this GPU: GB/s over a `gib` GiB
+    buffer, the median of `reps` event-timed launches after one untimed."""
+    nbytes = gib << 30
+    try:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    except RuntimeError as e:  # not enough free memory
+        return {"error": f"no {gib} GiB buffer: {type(e).__name__}"}
+    words = torch.empty(moe.moe_stream_read_words(), dtype=torch.int32, device="cuda")
+    moe.moe_stream_read(buf, words)
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moe.moe_stream_read(buf, words)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del buf
+    torch.cuda.empty_cache()
+    ms = statistics.median(times)
+    return {"read_gbs": nbytes / ms / 1e6, "bytes": nbytes, "median_ms": ms, "min_ms": min(times), "reps": reps,
+            "method": "moe_stream_read: every byte read once with 16-byte nontemporal loads, 8 in flight per lane, "
+                      "one 256-lane workgroup per CU; HIP events around each launch"}
 
 
 def cpu_baseline(np, torch, wl):

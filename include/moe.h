@@ -407,6 +407,18 @@ moe_status moe_unpermute_combine(const uint16_t* Y, int64_t y_rows,
                                  int T, int k, int N,
                                  uint16_t* Z, void* stream);
 
+/* moe_stream_read: a measurement helper, not a step of the method.  Reads the
+ * `bytes` bytes at `buf` once with 16-byte nontemporal loads (eight in
+ * flight per lane, one 256-lane workgroup per compute unit) and writes an XOR fold
+ * of every 32-bit word read to out[0 .. moe_stream_read_words() - 1] (one
+ * word per workgroup; the XOR of all of them is the XOR of the buffer), so
+ * that the reads cannot be dropped.  Timing it gives the HBM read rate the
+ * memory-bound kernels are compared with besides the nominal peak.
+ *   Requires bytes % 16 == 0, buf 16-byte and out 4-byte aligned (device
+ *   pointers owned by the caller); bytes == 0 writes zeros. */
+int moe_stream_read_words(void);
+moe_status moe_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

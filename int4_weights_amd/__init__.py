@@ -34,5 +34,7 @@ from ._lib import (  # noqa: F401
     moe_route_pack_noalloc_max_bytes,
     moe_route_pack_workspace_bytes,
     moe_swiglu_quant,
+    moe_stream_read,
+    moe_stream_read_words,
     moe_unpermute_combine,
 )

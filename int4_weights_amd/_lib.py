@@ -57,6 +57,8 @@ SIGNATURES = {
     "moe_grouped_gemm_fp8_fp4": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_unpermute_combine": (_c_i32, [_vp, _c_i64, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
+    "moe_stream_read_words": (ctypes.c_int, []),
+    "moe_stream_read": (_c_i32, [_vp, _c_i64, _vp, _vp]),
 }
 
 
@@ -356,3 +358,20 @@ def moe_unpermute_combine(Y, output_index, topk_weights, Z, stream=None):
         raise ValueError("moe_unpermute_combine: shape mismatch")
     _check(load().moe_unpermute_combine(_ptr(Y), Y.shape[0], _ptr(output_index), _ptr(topk_weights), T, k, N,
                                         _ptr(Z), _stream(stream)), "moe_unpermute_combine")
+
+
+def moe_stream_read_words() -> int:
+    """Words moe_stream_read writes (one per workgroup of its grid)."""
+    return int(load().moe_stream_read_words())
+
+
+def moe_stream_read(buf, out, stream=None):
+    """Read every byte of the device tensor buf once (a measurement helper); out: int32 [moe_stream_read_words()]
+    receives the XOR fold of the words read."""
+    if buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("moe_stream_read: buf must be a contiguous device tensor")
+    _dev(out, "out", torch.int32, 1)
+    nbytes = buf.numel() * buf.element_size()
+    if out.numel() < moe_stream_read_words():
+        raise ValueError("moe_stream_read: out too small")
+    _check(load().moe_stream_read(_ptr(buf), nbytes, _ptr(out), _stream(stream)), "moe_stream_read")

@@ -509,4 +509,16 @@ moe_status moe_unpermute_combine(const uint16_t* Y, int64_t y_rows, const int32_
                     "moe_unpermute_combine");
 }
 
+int moe_stream_read_words(void) { return stream_read_grid(); }
+
+moe_status moe_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
+  g_err[0] = 0;
+  if (bytes < 0 || bytes % 16)
+    return fail(MOE_ERR_SHAPE, "moe_stream_read: bytes=%lld must be a multiple of 16", (long long)bytes);
+  if (!out || (bytes && !buf)) return fail(MOE_ERR_NULL, "moe_stream_read: null pointer");
+  if ((buf && !aligned(buf, 16)) || !aligned(out, 4))
+    return fail(MOE_ERR_ALIGN, "moe_stream_read: buf must be 16-byte and out 4-byte aligned");
+  return hip_status(launch_stream_read(buf, bytes, out, (hipStream_t)stream), "moe_stream_read");
+}
+
 }  // extern "C"

@@ -330,7 +330,7 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int expected_m, hipStream_t s) {
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 256);
-  if (em <= 16) return launch_bf16<1, 8>(a, s);
+  if (em <= 16) return launch_bf16<1, 3>(a, s);  // two K steps in flight per wave (as the FP8 decode tile)
   const bool tall_ok = (a.K / 64) % 4 == 0;  // the tall loop body is 4 steps
   if (em <= 64 || !tall_ok) return launch_bf16<4, 4>(a, s);
   if (em >= 256) return launch_bf16_tall<256>(a, s);

@@ -361,7 +361,7 @@ static hipError_t launch_fp4_tall(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_fp4(const GemmArgs& a, int expected_m, hipStream_t s) {
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 256);
   if (a.wpacked) {
-    if (em <= 16) return launch_fp4<1, 8, true>(a, s);
+    if (em <= 16) return launch_fp4<1, 3, true>(a, s);  // two K steps in flight per wave (as the FP8 decode tile)
     // the tall tiles copy 4 K blocks of row scales per 16-byte load
     const bool tall_ok = (a.K / 128) % MOE_FP8_TALL_SCALE_GROUP == 0 && (((uintptr_t)a.SFA) & 15) == 0;
     if (em <= 64 || !tall_ok) return launch_fp4<4, 6, true>(a, s);

@@ -409,10 +409,14 @@ static hipError_t launch_fp8_tall(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s) {
   // Tile height from the expected rows per active expert: decode-sized
-  // segments keep the weights in a deep register ring (short tiles), prefill
-  // segments use the tall tile (up to 192 rows).
+  // segments stream the weights through a register ring (short tiles),
+  // prefill segments use the tall tiles (192 or 256 rows).  The decode ring
+  // keeps two K blocks in flight per wave (32 KB per CU per block): deeper
+  // rings (3 to 7 blocks) were 1-3% slower on the DeepSeek-V3-shaped decode,
+  // one block 7% slower -- a plain streaming read is also fastest with about
+  // 32 KB in flight per CU.
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 256);
-  if (em <= 16) return launch_fp8<1, 8, 4>(a, s);
+  if (em <= 16) return launch_fp8<1, 3, 4>(a, s);
   // the tall tile copies 4 K blocks of row scales per 16-byte load
   const bool tall_ok = (a.K / 128) % MOE_FP8_TALL_SCALE_GROUP == 0 && (((uintptr_t)a.SFA) & 15) == 0;
   if (em <= 64 || !tall_ok) return launch_fp8<4, 6, 4>(a, s);

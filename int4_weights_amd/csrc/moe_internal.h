@@ -87,6 +87,8 @@ struct SwigluArgs {
 };
 hipError_t launch_swiglu_quant(const SwigluArgs& a, hipStream_t s);
 
+int stream_read_grid();
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
 hipError_t launch_combine(const uint16_t* Y, int64_t y_rows, const int32_t* oi, const float* w, int T, int k,
                           int N, uint16_t* Z, hipStream_t s);
 

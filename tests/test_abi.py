@@ -165,6 +165,13 @@ def test_host_validation_rejects_without_launching(lib):
     assert gb(W=0) == MOE_ERR_NULL
     assert gb(A=A16 + 8) == MOE_ERR_ALIGN
     assert gb(K=128 * 300) == MOE_ERR_UNSUPPORTED
+    # moe_stream_read(buf, bytes, out, stream): the measurement helper validates like the path's calls
+    assert lib.moe_stream_read(_p(A16), 100, _p(A16), None) == MOE_ERR_SHAPE
+    assert lib.moe_stream_read(_p(A16), -16, _p(A16), None) == MOE_ERR_SHAPE
+    assert lib.moe_stream_read(_p(A16), 64, None, None) == MOE_ERR_NULL
+    assert lib.moe_stream_read(None, 64, _p(A16), None) == MOE_ERR_NULL
+    assert lib.moe_stream_read(_p(A16 + 8), 64, _p(A16), None) == MOE_ERR_ALIGN
+    assert lib.moe_stream_read(_p(A16), 64, _p(A16 + 2), None) == MOE_ERR_ALIGN
     # moe_grouped_gemm_fp8_fp4(layout, A, SFA, W4, SW, D, counts, seg, E, rows, N, K, expected_m, stream)
     def g4(layout=0, N=256, K=256, E=4, rows=512, seg=A16, A=A16, SW=A16, SFA=A16):
         return lib.moe_grouped_gemm_fp8_fp4(layout, _p(A) if A else None, _p(SFA) if SFA else None, _p(A16),
