@@ -228,7 +228,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 //  * Weights are private to a wave and stream from HBM straight into a 4-deep
 //    register ring; activations are shared and copied global->LDS
 //    (global_load_lds) into a 4-deep LDS ring.  K step ks issues the loads of
-//    block ks + 3; the barrier that publishes block ks + 1 sits before the
+//    block ks + 2; the barrier that publishes block ks + 1 sits before the
 //    step's last row tile, so the next block's first fragments are read
 //    behind that tile's matrix instructions.
 //  * Scales ride the same pipeline, so a unit starts without any staging

@@ -37,8 +37,10 @@ Activation copies.  A unit of rbe row tiles copies only the 32 rbe rows it compu
 rows 8 (4 i + w) .. +7 of the K block (1 KB) into the ring slot, so each loop body issues rbe copies per wave
 and K block, with its own wait counts and its own prologue.
 
-Pipeline.  Step ks multiplies K block ks and issues the loads of block ks + 3
-(into the slot block ks - 1 used).  The barrier that publishes block ks + 1 sits
+Pipeline.  Step ks multiplies K block ks and issues the loads of block ks + dist
+(dist = 2: one block in flight beyond the next, about 64 KB per CU; 3 was no
+faster on HBM-bound shapes and 1-2% slower on the Qwen3-shaped ones, as a plain
+streaming read also slows down with more bytes in flight).  The barrier that publishes block ks + 1 sits
 inside step ks, after the fragments of the step's last row tile have been read
 into registers: from then on no wave reads slot ks, so row tile 0 of block
 ks + 1 (and its row scale) is read into a third fragment buffer while the last
@@ -83,10 +85,12 @@ GROUP = 4         # K blocks per row-scale copy (one 16-byte copy per row)
 
 
 class Cfg:
-    def __init__(self, rows: int, S: int, name: str, dtype: str = "fp8", wnt: bool = False):
+    def __init__(self, rows: int, S: int, name: str, dtype: str = "fp8", wnt: bool = False, dist: int = 2):
         assert rows in (192, 256) and dtype in ("fp8", "bf16", "fp4")
         self.rows, self.S, self.name = rows, S, name
         self.wnt = wnt                            # weight loads nontemporal (each weight byte read by one unit)
+        assert dist in (2, 3)
+        self.dist = dist                          # step ks issues the loads of block ks + dist
         self.bf16 = dtype == "bf16"               # bf16 operands: four 32x32x16 instructions per 128-byte step, no scales
         self.fp4 = dtype == "fp4"                 # MXFP4 weights (packed order only): 16 bytes per lane and K half,
         # one E8M0 scale per 32 K values and lane (two scale dwords per K block, shifted per lane)
@@ -135,8 +139,11 @@ class Cfg:
 
     def wait_at(self, s, issued, ops):
         """Loads allowed outstanding at the barrier of step s (K block ks = s mod S) that publishes block
-        ks + 1: those of block ks + 2 (issued in the previous step, plus one if it starts a scale group) and
-        the `issued` loads of block ks + 3 this step has issued so far."""
+        ks + 1: those of the blocks issued after it in earlier steps (ks + 2 when dist = 3, plus one if it
+        starts a scale group; none when dist = 2) and the `issued` loads of block ks + dist this step has
+        issued so far."""
+        if self.dist == 2:
+            return issued
         return ops + (1 if (s + 2) % GROUP == 0 and not self.bf16 else 0) + issued
 
     @staticmethod
@@ -251,21 +258,21 @@ def mfma(cfg, s, b, j, ct, kk, src_zero):
 
 def compute(cfg, s, t, packed, rbe, final=False, first=False):
     """Multiply K block s of the ring (row tiles 0 .. rbe-1; rbe >= 2 is fixed for the body, so the code has no
-    branch between matrix instructions) and issue the loads of ring slot t (block ks + 3) on the way, one item
+    branch between matrix instructions) and issue the loads of ring slot t (block ks + dist) on the way, one item
     after each of the evenly spaced matrix instructions (a burst of loads stalls every wave on the shared load
     path).  Row tile 0's fragments and row scale were read into buffer 2 by the previous step; the barrier that
     publishes the next block sits after row tile rbe - 2 (publish).
 
-    final: step s of the loop's last iteration (K blocks kb-4 .. kb-1).  Step 0 still issues block kb - 1;
-    steps 1 .. 3 issue nothing, so their waits are for fewer loads (step 1: block kb - 1's; step 2: none),
-    and step 3 has no next block to publish.
+    final: step s of the loop's last iteration (K blocks kb-4 .. kb-1).  Steps 0 .. 3 - dist still issue
+    blocks up to kb - 1, the later ones issue nothing, so their waits are for fewer loads (step 2: none), and
+    step 3 has no next block to publish.
 
     first: the unit's first K block; each accumulator's first matrix instruction adds to 0 instead of the
     accumulator, so the accumulators need no zeroing."""
     if final and s == cfg.S - 1:
         return compute_last(cfg, s, rbe)
     items, upd = issue_items(cfg, t, packed, rbe)
-    if final and s > 0:
+    if final and s > cfg.S - 1 - cfg.dist:  # its block would be past the last one
         items, upd = [], []
     nslots = 4 * rbe
     place = [[] for _ in range(nslots)]  # matrix-instruction slot -> the items issued right after it
@@ -294,7 +301,7 @@ def compute(cfg, s, t, packed, rbe, final=False, first=False):
                                                [f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"])
             if j + 2 == rbe and not (final and s == cfg.S - 1):  # row tile j + 1 is the last one
                 issued = sum(len(place[i]) for i in range(4 * (j + 1)))
-                wait = 0 if final and s == 2 else cfg.wait_at(s, issued, cfg.ops_for(rbe))
+                wait = 0 if final and s == cfg.S - 2 else cfg.wait_at(s, issued, cfg.ops_for(rbe))
                 out += publish(cfg, s, wait)
     out += upd
     return out
@@ -302,22 +309,22 @@ def compute(cfg, s, t, packed, rbe, final=False, first=False):
 
 def body(cfg, packed, rbe):
     """The K loop for units of rbe row tiles: iterations of S steps (one per ring slot, S = 4 K blocks); all
-    but the last issue the loads of the block 3 ahead in every step, the last one (final) is emitted apart.
+    but the last issue the loads of the block dist ahead in every step, the last one (final) is emitted apart.
     The unit's first step (accumulating onto 0) is emitted once more for either kind of iteration and then
     joins the loop at its second step."""
     head, mid, fin, fin_mid, first_fin = 200 + rbe, 300 + rbe, 400 + rbe, 500 + rbe, 600 + rbe
-    t0 = cfg.S - 1  # ring slot of the loads issued by step 0
+    t0 = cfg.dist  # ring slot of the loads issued by step 0
     out = ["s_cmp_le_u32 %[kb], 4", f"s_cbranch_scc1 {first_fin}f", "s_mov_b32 %[ks], 4"]
     out += compute(cfg, 0, t0, packed, rbe, first=True) + [f"s_branch {mid}f", f"{head}:"]
     out += compute(cfg, 0, t0, packed, rbe) + [f"{mid}:"]
     for s in range(1, cfg.S):
-        out += compute(cfg, s, (s + cfg.S - 1) % cfg.S, packed, rbe)
+        out += compute(cfg, s, (s + cfg.dist) % cfg.S, packed, rbe)
     out += ["s_add_u32 %[ks], %[ks], 4", "s_cmp_lt_u32 %[ks], %[kb]", f"s_cbranch_scc1 {head}b", f"s_branch {fin}f",
             f"{first_fin}:"]
     out += compute(cfg, 0, t0, packed, rbe, final=True, first=True) + [f"s_branch {fin_mid}f", f"{fin}:"]
     out += compute(cfg, 0, t0, packed, rbe, final=True) + [f"{fin_mid}:"]
     for s in range(1, cfg.S):
-        out += compute(cfg, s, (s + cfg.S - 1) % cfg.S, packed, rbe, final=True)
+        out += compute(cfg, s, (s + cfg.dist) % cfg.S, packed, rbe, final=True)
     out.append(f"s_branch {700 + rbe}f")
     return out
 
@@ -436,13 +443,13 @@ def epilogue(cfg, rbe):
 
 
 def prologue(cfg, packed, rbe):
-    """The loads of K blocks 0 .. 2, then block 0 in place (blocks 1 and 2 may still be in flight) and its row
-    tile 0 read into fragment buffer 2."""
+    """The loads of K blocks 0 .. dist - 1, then block 0 in place (the later ones may still be in flight) and
+    its row tile 0 read into fragment buffer 2."""
     out = ["s_mov_b32 %[q], 0"]
-    for t in range(cfg.S - 1):
+    for t in range(cfg.dist):
         items, upd = issue_items(cfg, t, packed, rbe)
         out += [ins for it in items for ins in it] + upd
-    out += [f"s_waitcnt vmcnt({2 * cfg.ops_for(rbe)})", "s_barrier"] + frag_reads(cfg, 0, 2, 0) + (
+    out += [f"s_waitcnt vmcnt({(cfg.dist - 1) * cfg.ops_for(rbe)})", "s_barrier"] + frag_reads(cfg, 0, 2, 0) + (
         [] if cfg.bf16 else [f"ds_read_b32 v{cfg.v_sae + 2}, v{cfg.v_sadr}"])
     return out
 
