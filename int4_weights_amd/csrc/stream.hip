@@ -6,7 +6,7 @@
 // walk of the buffer, one 256-lane workgroup per CU: 32 KB in flight per CU.
 // Of 4, 8 or 16 loads per lane, 256 to 1024 lanes and 1 to 8 workgroups per
 // CU, grid-stride or one contiguous slice per workgroup, this was the fastest
-// for an 8 GiB read (7.3-7.4 TB/s on one box; 4 loads per lane with two
+// for an 8 GiB read (7.3-7.4 TB/s on one MI355X; 4 loads per lane with two
 // workgroups per CU, the same bytes in flight, 6.8).  The loaded words are
 // XOR-folded and the fold is written once per workgroup so that no load can
 // be dropped.
