@@ -23,8 +23,14 @@ def _orders(cfg):
     return (True,) if cfg.fp4 else (False, True)  # MXFP4 weights: packed order only
 
 
+def _configs(gen):
+    """The built configurations, plus the generator's other load distance (3) on each operand format."""
+    return list(gen.CONFIGS) + [gen.Cfg(192, 4, "TALL192_D3", dist=3), gen.Cfg(256, 4, "BF16_TALL256_D3", "bf16", dist=3),
+                                gen.Cfg(256, 4, "FP4_TALL256_D3", "fp4", dist=3)]
+
+
 def _programs(gen):
-    for cfg in gen.CONFIGS:
+    for cfg in _configs(gen):
         for packed in _orders(cfg):
             yield cfg, packed, gen.program(cfg, packed)
 
@@ -169,7 +175,7 @@ def test_each_unit_path_runs_its_blocks_once(gen, kb):
     row-scale copy per 4 blocks), 4 stores (of 8
     rows each) per row tile, at most 15 LDS operations in flight, and no register used before the load or LDS
     read that fills it has been waited for."""
-    for cfg in gen.CONFIGS:
+    for cfg in _configs(gen):
         for packed in _orders(cfg):
             prog = gen.program(cfg, packed)
             for rbe in range(2, cfg.rt + 1):
