@@ -91,7 +91,8 @@ class Cfg:
         self.wnt = wnt                            # weight loads nontemporal (each weight byte read by one unit)
         assert dist in (2, 3)
         self.dist = dist                          # step ks issues the loads of block ks + dist
-        self.bf16 = dtype == "bf16"               # bf16 operands: four 32x32x16 instructions per 128-byte step, no scales
+        self.bf16 = dtype == "bf16"               # bf16 operands: four 32x32x16 instructions per 128-byte step,
+        # no scales
         self.fp4 = dtype == "fp4"                 # MXFP4 weights (packed order only): 16 bytes per lane and K half,
         # one E8M0 scale per 32 K values and lane (two scale dwords per K block, shifted per lane)
         assert S == GROUP, "the unrolled loop body is one scale group"
@@ -252,8 +253,8 @@ def mfma(cfg, s, b, j, ct, kk, src_zero):
     if not cfg.bf16:
         return [f"v_mfma_scale_f32_32x32x64_f8f6f4 {acc}, {wreg(cfg, s, ct, kk, 0, 7)}, {cfg.buf(b, kk)}, "
                 f"{'0' if src_zero else acc}, v{cfg.v_swe}, v{cfg.v_sae + b} op_sel_hi:[0,0,0]"]
-    return [f"v_mfma_f32_32x32x16_bf16 {acc}, {wreg(cfg, s, ct, kk, 4 * p, 4 * p + 3)}, {cfg.buf(b, kk, 4 * p, 4 * p + 3)}, "
-            f"{'0' if src_zero and p == 0 else acc}" for p in range(2)]
+    return [f"v_mfma_f32_32x32x16_bf16 {acc}, {wreg(cfg, s, ct, kk, 4 * p, 4 * p + 3)}, "
+            f"{cfg.buf(b, kk, 4 * p, 4 * p + 3)}, {'0' if src_zero and p == 0 else acc}" for p in range(2)]
 
 
 def compute(cfg, s, t, packed, rbe, final=False, first=False):
