@@ -11,6 +11,7 @@
  *   moe_grouped_gemm_bf16  (BF16 variant) bf16 rows x bf16 expert weights -> bf16
  *   moe_grouped_gemm_fp8_fp4 (FP4 variant) FP8 rows x MXFP4 (E2M1 + E8M0) weights -> bf16
  *   moe_swiglu_quant       (between up- and down-projection) silu(gate) * up -> FP8 + 1x128 scales
+ *   moe_grouped_gemm_fp8_swiglu (up-projection with the step above in its epilogue) -> FP8 + 1x128 scales
  *   moe_unpermute_combine  topk_weights-weighted sum back to token order
  *
  * plus weight-preparation calls (moe_quant_weight_fp8 / _int4 / _fp4,
@@ -390,6 +391,34 @@ moe_status moe_grouped_gemm_fp8_fp4(int layout,
 moe_status moe_swiglu_quant(int layout, const uint16_t* gate_up, int64_t rows_cap_or_max_m, int I,
                             const int32_t* counts, const int32_t* seg_offsets, int E,
                             uint8_t* q, float* sf, void* stream);
+
+/* moe_grouped_gemm_fp8_swiglu: the up-projection's FP8 grouped GEMM with
+ * SwiGLU and the 1x128 requantisation in its epilogue, so the [rows, 2I] bf16
+ * gate/up output never goes through HBM (the same sources as
+ * moe_grouped_gemm_fp8 and moe_swiglu_quant).
+ *   The result is, bit for bit, that of moe_grouped_gemm_fp8 with N = 2I
+ *   into a bf16 gate_up followed by moe_swiglu_quant on it: every gate and up
+ *   value is the GEMM's fp32 accumulation rounded to bf16 (nearest even),
+ *   then h = silu(gate) * up in fp32 and the 1x128 power-of-two quantisation
+ *   exactly as moe_swiglu_quant computes them.
+ *     A [rows, K] E4M3FN, SFA [rows, K/128] fp32 powers of two (moe_quant_act);
+ *     W [E, 2I, K] E4M3FN, SFW [E, 2I/128, K/128] fp32 powers of two: the
+ *       gate rows 0..I-1, then the up rows I..2I-1 (the weight of the plain
+ *       up-projection; layout | MOE_WEIGHTS_PACKED: in the order written by
+ *       moe_pack_weight_fp8 with N = 2I);
+ *     Q [rows, I] E4M3FN codes, SQ [rows, I/128] fp32 powers of two.
+ *   Layout, counts, seg_offsets and expected_m as for moe_grouped_gemm_fp8;
+ *   rows of Q and SQ outside the segments are never written.
+ *   Requires I % 128 == 0, K % 512 == 0 (K <= 32768), 1 <= E <= 1024, A, W and
+ *   Q 16-byte aligned, SFA 16-byte and SFW, SQ 4-byte aligned; otherwise
+ *   MOE_ERR_UNSUPPORTED / MOE_ERR_ALIGN and nothing is launched. */
+moe_status moe_grouped_gemm_fp8_swiglu(int layout,
+                                       const uint8_t* A, const float* SFA,
+                                       const uint8_t* W, const float* SFW,
+                                       uint8_t* Q, float* SQ,
+                                       const int32_t* counts, const int32_t* seg_offsets,
+                                       int E, int64_t rows_cap_or_max_m, int I, int K,
+                                       int expected_m, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* moe_unpermute_combine: weighted combine back to token order ("gather").

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     moe_grouped_gemm_bf16,
     moe_grouped_gemm_fp8,
     moe_grouped_gemm_fp8_fp4,
+    moe_grouped_gemm_fp8_swiglu,
     moe_grouped_gemm_int4,
     moe_pack_weight_bf16,
     moe_pack_weight_fp4,

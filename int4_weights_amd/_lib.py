@@ -46,6 +46,8 @@ SIGNATURES = {
                                         _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_fp8": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
+    "moe_grouped_gemm_fp8_swiglu": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_grouped_gemm_int4": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                                        ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_swiglu_quant": (_c_i32, [ctypes.c_int, _vp, _c_i64, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp]),
@@ -266,6 +268,23 @@ def moe_grouped_gemm_fp8(layout: int, A, SFA, W, SFW, D, counts, seg_offsets, E:
     _check(load().moe_grouped_gemm_fp8(layout, _ptr(A), _ptr(SFA), _ptr(W), _ptr(SFW), _ptr(D), _ptr(counts),
                                        _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
            "moe_grouped_gemm_fp8")
+
+
+def moe_grouped_gemm_fp8_swiglu(layout: int, A, SFA, W, SFW, Q, SQ, counts, seg_offsets, E: int,
+                                rows_cap_or_max_m: int, I: int, K: int, expected_m: int = 0, stream=None):
+    """The up-projection (W [E, 2I, K]: gate rows, then up rows) with SwiGLU and the 1x128 requantisation:
+    Q uint8 [rows, I] E4M3 codes, SQ float32 [rows, I/128] (see include/moe.h)."""
+    _dev(A, "A", torch.uint8), _dev(SFA, "SFA", torch.float32), _dev(W, "W", torch.uint8)
+    _dev(SFW, "SFW", torch.float32), _dev(Q, "Q", torch.uint8), _dev(SQ, "SQ", torch.float32)
+    _dev(counts, "counts", torch.int32), _dev(seg_offsets, "seg_offsets", torch.int32)
+    _gemm_sizes("moe_grouped_gemm_fp8_swiglu", layout, E, rows_cap_or_max_m, counts, seg_offsets,
+                lambda rows: (("A", A, rows * K), ("SFA", SFA, rows * (K // 128)), ("W", W, E * 2 * I * K),
+                              ("SFW", SFW, E * (2 * I // 128) * (K // 128)), ("Q", Q, rows * I),
+                              ("SQ", SQ, rows * (I // 128))))
+    _check(load().moe_grouped_gemm_fp8_swiglu(layout, _ptr(A), _ptr(SFA), _ptr(W), _ptr(SFW), _ptr(Q), _ptr(SQ),
+                                              _ptr(counts), _ptr(seg_offsets), E, rows_cap_or_max_m, I, K,
+                                              expected_m, _stream(stream)),
+           "moe_grouped_gemm_fp8_swiglu")
 
 
 def moe_grouped_gemm_int4(layout: int, A, W4, S16, D, counts, seg_offsets, E: int, rows_cap_or_max_m: int,

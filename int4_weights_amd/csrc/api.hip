@@ -300,7 +300,7 @@ moe_status moe_grouped_gemm_fp8(int layout, const uint8_t* A, const float* SFA, 
   if (st) return st;
   if (!SFA) return fail(MOE_ERR_NULL, "moe_grouped_gemm_fp8: SFA is null");
   if (!aligned(SFA, 4) || !aligned(SFW, 4)) return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_fp8: scales misaligned");
-  GemmArgs a;
+  GemmArgs a{};
   a.A = A;
   a.SFA = SFA;
   a.W = W;
@@ -318,6 +318,44 @@ moe_status moe_grouped_gemm_fp8(int layout, const uint8_t* A, const float* SFA, 
   return hip_status(launch_gemm_fp8(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_fp8");
 }
 
+moe_status moe_grouped_gemm_fp8_swiglu(int layout, const uint8_t* A, const float* SFA, const uint8_t* W,
+                                       const float* SFW, uint8_t* Q, float* SQ, const int32_t* counts,
+                                       const int32_t* seg_offsets, int E, int64_t rows_cap_or_max_m, int I, int K,
+                                       int expected_m, void* stream) {
+  g_err[0] = 0;
+  const int wpacked = (layout & MOE_WEIGHTS_PACKED) ? 1 : 0;
+  layout &= ~MOE_WEIGHTS_PACKED;
+  if (I <= 0 || I > 0x3fffffff) return fail(MOE_ERR_SHAPE, "moe_grouped_gemm_fp8_swiglu: I=%d", I);
+  if (I % 128) return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_gemm_fp8_swiglu: I=%d is not a multiple of 128", I);
+  moe_status st = check_gemm("moe_grouped_gemm_fp8_swiglu", layout, A, W, SFW, Q, counts, seg_offsets, E,
+                             rows_cap_or_max_m, 2 * I, K);
+  if (st) return st;
+  if (!SFA || !SQ) return fail(MOE_ERR_NULL, "moe_grouped_gemm_fp8_swiglu: SFA or SQ is null");
+  if (!aligned(SFW, 4) || !aligned(SQ, 4))
+    return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_fp8_swiglu: SFW and SQ must be 4-byte aligned");
+  // the tall tile it runs on copies 4 K blocks of row scales per 16-byte load
+  if ((K / 128) % 4)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_gemm_fp8_swiglu: K=%d must be a multiple of 512", K);
+  if (!aligned(SFA, 16)) return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_fp8_swiglu: SFA must be 16-byte aligned");
+  GemmArgs a{};
+  a.A = A;
+  a.SFA = SFA;
+  a.W = W;
+  a.SW = SFW;
+  a.Q = Q;
+  a.SQ = SQ;
+  a.counts = counts;
+  a.seg_offsets = seg_offsets;
+  a.E = E;
+  a.masked = layout == MOE_LAYOUT_MASKED;
+  a.max_m = a.masked ? (int)rows_cap_or_max_m : 0;
+  a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
+  a.N = 2 * I;
+  a.K = K;
+  a.wpacked = wpacked;
+  return hip_status(launch_gemm_fp8_swiglu(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_fp8_swiglu");
+}
+
 moe_status moe_grouped_gemm_int4(int layout, const uint16_t* A, const uint8_t* W4, const uint16_t* S16, uint16_t* D,
                                  const int32_t* counts, const int32_t* seg_offsets, int E, int64_t rows_cap_or_max_m,
                                  int N, int K, int expected_m, void* stream) {
@@ -331,7 +369,7 @@ moe_status moe_grouped_gemm_int4(int layout, const uint16_t* A, const uint8_t* W
   // the packed kernel reads one lane's 4 scales of a group as one 8-byte load
   if (wpacked && !aligned(S16, 8))
     return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_int4: packed scales must be 8-byte aligned");
-  GemmArgs a;
+  GemmArgs a{};
   a.A = (const uint8_t*)A;
   a.SFA = nullptr;
   a.W = W4;
@@ -378,7 +416,7 @@ moe_status moe_grouped_gemm_bf16(int layout, const uint16_t* A, const uint16_t* 
   if (st) return st;
   if ((int64_t)N * K * 2 > 0xffffffffll)
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_gemm_bf16: one expert's weights exceed 4 GiB");
-  GemmArgs a;
+  GemmArgs a{};
   a.A = (const uint8_t*)A;
   a.SFA = nullptr;
   a.W = (const uint8_t*)W;
@@ -443,7 +481,7 @@ moe_status moe_grouped_gemm_fp8_fp4(int layout, const uint8_t* A, const float* S
   if (!SFA) return fail(MOE_ERR_NULL, "moe_grouped_gemm_fp8_fp4: SFA is null");
   if (!aligned(SFA, 4) || !aligned(SW, 4))
     return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_fp8_fp4: SFA and SW must be 4-byte aligned");
-  GemmArgs a;
+  GemmArgs a{};
   a.A = A;
   a.SFA = SFA;
   a.W = W4;

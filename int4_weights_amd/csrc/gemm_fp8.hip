@@ -281,6 +281,15 @@ static_assert(MOE_FP8_TALL_SCALE_ROWS == 256, "row scales: 4 waves x 64 lanes");
 static_assert(MOE_FP8_TALL_SCALE_GROUP == 4, "a row-scale copy covers 4 K blocks (16 bytes)");
 static_assert(TallCfg<192>::kSlotA == 192 * 128 && TallCfg<192>::kApw * 32 == 192, "192-row slots");
 static_assert(TallCfg<256>::kSlotA == 256 * 128 && TallCfg<256>::kApw * 32 == 256, "256-row slots");
+// the SwiGLU loops share the register and LDS layout of the plain ones
+static_assert(MOE_SWIGLU_TALL192_LDS == MOE_FP8_TALL192_LDS && MOE_SWIGLU_TALL192_SLOT == MOE_FP8_TALL192_SLOT &&
+                  MOE_SWIGLU_TALL192_S == MOE_FP8_TALL192_S && MOE_SWIGLU_TALL192_APW == MOE_FP8_TALL192_APW,
+              "SwiGLU 192-row layout");
+static_assert(MOE_SWIGLU_TALL256_LDS == MOE_FP8_TALL256_LDS && MOE_SWIGLU_TALL256_SLOT == MOE_FP8_TALL256_SLOT &&
+                  MOE_SWIGLU_TALL256_S == MOE_FP8_TALL256_S && MOE_SWIGLU_TALL256_APW == MOE_FP8_TALL256_APW,
+              "SwiGLU 256-row layout");
+// SwiGLU staging: row m's 128 gate and 128 up bf16 values at 512 m, over the ring (which ends at the scales)
+static_assert(TallCfg<192>::kScOff == 192 * 512 && TallCfg<256>::kScOff == 256 * 512, "SwiGLU staging fits");
 
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
@@ -300,13 +309,41 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
                  [l8] "v"(l8), [epb] "v"(epb), [rb] "v"(rb)                                                      \
                : "memory", "vcc", "exec", "scc", CLOBBERS)
 
-template <int ROWS, bool PACKED>
+// SwiGLU after the up-projection's loop (SWIGLU units): the unit's gate and up values, rounded to bf16, are in
+// LDS (row m at 512 m: gate values 0 .. 127 of the unit's 128 outputs, then up values; 16-byte chunk c at
+// position c ^ (m & 31)).  16 lanes per row, 4 rows per wave: each lane takes 8 consecutive outputs, and the
+// row's 128 outputs are one 1x128 quantisation block (column tile n0 / 256).  Rows of the computed row tiles
+// past the unit's end are read (they repeat its last row) but not stored.  The closing barrier keeps the next
+// unit's copies into the ring behind these reads.
+// The unit is passed as wave-uniform values (SGPRs), since every VGPR outside the loop's own is scarce across it.
+template <int ROWS>
+__device__ __forceinline__ void swiglu_unit_rows(const GemmArgs& a, const Fp8TallSmem<ROWS>& sm, int row0,
+                                                 int mrows, int nt, int rbe) {
+  const int I = a.N / 2, ib = I / 128, lane = lane_id(), sub = lane & 15, wv = uniform(threadIdx.x >> 6);
+  for (int m0 = 0; m0 < 32 * rbe; m0 += 16) {
+    const int m = m0 + 4 * wv + (lane >> 4), sw = m & 31;
+    const v4i g = *(const v4i*)&sm.b[m * 512 + 16 * (sub ^ sw)];
+    const v4i up = *(const v4i*)&sm.b[m * 512 + 16 * ((16 + sub) ^ sw)];
+    uint2 o;
+    const int e = swiglu_quant16(g, up, &o);
+    if (m < mrows) {
+      const int64_t row = (int64_t)row0 + m;
+      *(uint2*)(a.Q + row * I + 128 * nt + 8 * sub) = o;
+      if (sub == 0) a.SQ[row * ib + nt] = pow2f(e);
+    }
+  }
+  __syncthreads();
+}
+
+template <int ROWS, bool PACKED, bool SWIGLU>
 __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, Fp8TallSmem<ROWS>& sm, int wv,
                                               int lane) {
   constexpr int kTApw = TallCfg<ROWS>::kApw, kScOff = TallCfg<ROWS>::kScOff;
   const int l32 = lane & 31, hh = lane >> 5;  // operand row and K half of this lane
   const int K = a.K, N = a.N, KB = K / 128, NB = N / 128;
-  const int ncol0 = u.n0 + 64 * wv;
+  // SwiGLU: the unit's 128 outputs are gate columns n0 / 2 .. + 127 (waves 0, 1) and the up columns N / 2
+  // further (waves 2, 3); every wave has columns (N / 2 is a multiple of 128)
+  const int ncol0 = SWIGLU ? (wv >= 2 ? N / 2 : 0) + u.n0 / 2 + 64 * (wv & 1) : u.n0 + 64 * wv;
   const int won = ncol0 < N ? 1 : 0;
   const int ncl = won ? ncol0 : N - 64;  // an idle wave re-reads valid columns and stores nothing
 
@@ -347,20 +384,36 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   // (row m at m*128, 16-byte chunk c at position c ^ (m & 7)); each lane writes 8 bytes of row l32 (epb:
   // chunk 0's address, including the lane's half) and reads back 16 bytes (chunk lane & 7) of row lane >> 3
   // of every 8-row group, stored as whole 128-byte rows
-  const uint32_t epb = abase + (uint32_t)(wv * 4096 + l32 * 128 + 16 * (l32 & 7) + 8 * hh);
+  // (SwiGLU: epb is this lane's 8 bytes of chunk 8 wv of row l32 of the staged bf16 rows, see swiglu_unit_rows)
+  const uint32_t epb = SWIGLU ? abase + (uint32_t)(l32 * 512 + 16 * ((8 * wv) ^ l32) + 8 * hh)
+                              : abase + (uint32_t)(wv * 4096 + l32 * 128 + 16 * (l32 & 7) + 8 * hh);
   const int l8 = lane >> 3;
   const uint32_t rb = abase + (uint32_t)(wv * 4096 + l8 * 128 + 16 * ((lane & 7) ^ (l8 & 7)));
   const uint64_t wm = uniform_u64(won ? ~0ull : 0ull);  // exec mask of the stores: none for an idle wave
-  const uint64_t db = uniform_u64((uint64_t)(a.D + (int64_t)u.row0 * N));
+  const uint64_t db = SWIGLU ? 0 : uniform_u64((uint64_t)(a.D + (int64_t)u.row0 * N));  // (SwiGLU: no D)
   uint32_t doff = (uint32_t)(l8 * N + ncol0 + 8 * (lane & 7)) * 2u;
   const int dstep = uniform(16 * N);  // output bytes between 8-row groups
   // row tiles computed: at least 2, so the barrier that publishes the next K block (after the fragments of
   // the second-to-last row tile's successor are read) has a place in every step
   const int rbe = uniform(max(2, (u.mrows + 31) / 32));
   const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
+  const int row0 = uniform(u.row0), nt = uniform(u.n0 / 256);  // (SwiGLU, after the loop)
   int ks, q, t, inc, inc4, m0v = 0;
   uint64_t sv;
-  if constexpr (ROWS == 192) {
+  if constexpr (SWIGLU) {
+    if constexpr (ROWS == 192) {
+      if constexpr (PACKED)
+        MOE_TALL_ASM(MOE_SWIGLU_TALL192_LOOP_PACKED, MOE_SWIGLU_TALL192_AO_OUTS, MOE_SWIGLU_TALL192_CLOBBERS);
+      else
+        MOE_TALL_ASM(MOE_SWIGLU_TALL192_LOOP, MOE_SWIGLU_TALL192_AO_OUTS, MOE_SWIGLU_TALL192_CLOBBERS);
+    } else {
+      if constexpr (PACKED)
+        MOE_TALL_ASM(MOE_SWIGLU_TALL256_LOOP_PACKED, MOE_SWIGLU_TALL256_AO_OUTS, MOE_SWIGLU_TALL256_CLOBBERS);
+      else
+        MOE_TALL_ASM(MOE_SWIGLU_TALL256_LOOP, MOE_SWIGLU_TALL256_AO_OUTS, MOE_SWIGLU_TALL256_CLOBBERS);
+    }
+    swiglu_unit_rows<ROWS>(a, sm, row0, mrows, nt, rbe);
+  } else if constexpr (ROWS == 192) {
     if constexpr (PACKED)
       MOE_TALL_ASM(MOE_FP8_TALL192_LOOP_PACKED, MOE_FP8_TALL192_AO_OUTS, MOE_FP8_TALL192_CLOBBERS);
     else
@@ -384,8 +437,26 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(const GemmArgs a)
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
     const Unit u = sched_unit<ROWS>(a, sc, v);
-    if (a.wpacked) fp8_unit_tall<ROWS, true>(a, u, sm, wv, lane);
-    else fp8_unit_tall<ROWS, false>(a, u, sm, wv, lane);
+    if (a.wpacked) fp8_unit_tall<ROWS, true, false>(a, u, sm, wv, lane);
+    else fp8_unit_tall<ROWS, false, false>(a, u, sm, wv, lane);
+  }
+}
+
+// The up-projection with SwiGLU and its 1x128 requantisation in the epilogue (a separate kernel, so the plain
+// GEMM's code is untouched): the same tall units over N = 2I columns, with Q / SQ written instead of D.
+template <int ROWS>
+__global__ __launch_bounds__(256, 1) void gemm_fp8_swiglu_tall_kernel(const GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) Fp8TallSmem<ROWS> sm;
+  __shared__ SchedSmem s_sched;
+  const Sched sc{&s_sched};
+  sched_build<ROWS>(a, sc);
+  const Walk walk = sched_walk(s_sched.total);
+  const int lane = lane_id();
+  const int wv = uniform(threadIdx.x >> 6);
+  for (int v = walk.first; v < walk.end; v += walk.stride) {
+    const Unit u = sched_unit<ROWS>(a, sc, v);
+    if (a.wpacked) fp8_unit_tall<ROWS, true, true>(a, u, sm, wv, lane);
+    else fp8_unit_tall<ROWS, false, true>(a, u, sm, wv, lane);
   }
 }
 
@@ -398,12 +469,13 @@ static hipError_t launch_fp8(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int ROWS>
+template <int ROWS, bool SWIGLU = false>
 static hipError_t launch_fp8_tall(const GemmArgs& a, hipStream_t s) {
   const int cus = device_info().cus;
   int grid = cus - cus % kXcds;
   if (grid < kXcds) grid = kXcds;
-  gemm_fp8_tall_kernel<ROWS><<<grid, 256, 0, s>>>(a);
+  if (SWIGLU) gemm_fp8_swiglu_tall_kernel<ROWS><<<grid, 256, 0, s>>>(a);
+  else gemm_fp8_tall_kernel<ROWS><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -425,6 +497,14 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s) {
   // once a typical expert fills them
   if (em >= 256) return launch_fp8_tall<256>(a, s);
   return launch_fp8_tall<192>(a, s);
+}
+
+hipError_t launch_gemm_fp8_swiglu(const GemmArgs& a, int expected_m, hipStream_t s) {
+  // tall tiles only (the caller checked K / 128 % 4 == 0 and the 16-byte row-scale alignment they need); the
+  // tile height as for the plain GEMM
+  const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 256);
+  if (em >= 256) return launch_fp8_tall<256, true>(a, s);
+  return launch_fp8_tall<192, true>(a, s);
 }
 
 }  // namespace moe

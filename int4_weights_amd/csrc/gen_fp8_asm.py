@@ -72,6 +72,10 @@ Register map (physical, listed as clobbers of the asm statement):
   0 .. 2, idle in the last K block: two 16-register buffers for the rows read
   back from LDS, 32 temporaries, 16 packed bf16 pairs and 8 LDS addresses.
 
+SwiGLU variant (up-projection with the activation fused): the unit's waves 0, 1 take 128 gate columns and
+waves 2, 3 the 128 up columns of the same outputs; after the loop the bf16-rounded accumulators of every row
+tile go to LDS, and the unit's C++ code computes silu(gate) * up and its 1x128 quantisation from there.
+
 Usage: python gen_fp8_asm.py OUT.inc
 """
 
@@ -85,8 +89,10 @@ GROUP = 4         # K blocks per row-scale copy (one 16-byte copy per row)
 
 
 class Cfg:
-    def __init__(self, rows: int, S: int, name: str, dtype: str = "fp8", wnt: bool = False, dist: int = 2):
-        assert rows in (192, 256) and dtype in ("fp8", "bf16", "fp4")
+    def __init__(self, rows: int, S: int, name: str, dtype: str = "fp8", wnt: bool = False, dist: int = 2,
+                 swiglu: bool = False):
+        assert rows in (192, 256) and dtype in ("fp8", "bf16", "fp4") and not (swiglu and dtype != "fp8")
+        self.swiglu = swiglu                      # epilogue: gate and up columns to LDS for SwiGLU (no stores)
         self.rows, self.S, self.name = rows, S, name
         self.wnt = wnt                            # weight loads nontemporal (each weight byte read by one unit)
         assert dist in (2, 3)
@@ -266,11 +272,11 @@ def compute(cfg, s, t, packed, rbe, final=False, first=False):
 
     final: step s of the loop's last iteration (K blocks kb-4 .. kb-1).  Steps 0 .. 3 - dist still issue
     blocks up to kb - 1, the later ones issue nothing, so their waits are for fewer loads (step 2: none), and
-    step 3 has no next block to publish.
+    step 3 has no next block to publish (it carries the bf16 epilogue, except with SwiGLU).
 
     first: the unit's first K block; each accumulator's first matrix instruction adds to 0 instead of the
     accumulator, so the accumulators need no zeroing."""
-    if final and s == cfg.S - 1:
+    if final and s == cfg.S - 1 and not cfg.swiglu:
         return compute_last(cfg, s, rbe)
     items, upd = issue_items(cfg, t, packed, rbe)
     if final and s > cfg.S - 1 - cfg.dist:  # its block would be past the last one
@@ -431,11 +437,47 @@ def compute_last(cfg, s, rbe):
     return out
 
 
+def swiglu_epilogue(cfg, rbe):
+    """After the loop, for units of rbe row tiles of the up-projection with SwiGLU: the unit's 128 gate
+    columns are computed by waves 0 and 1 and the matching 128 up columns by waves 2 and 3, so the pairs meet
+    in LDS.  Once every wave is done with the ring (barrier), each row tile's accumulators are rounded to
+    bf16 (as the GEMM's output) and written over the ring: row m at m * 512 (gate values 0 .. 127, then up
+    values 0 .. 127), 16-byte chunk c (values 8 c .. 8 c + 7 of the row) at position c ^ (m & 31).  %[epb] is
+    the address of this lane's 8 bytes in chunk 8 w of its row (the chunk of column tile ct and register
+    group g is 8 w + 4 ct + g, an XOR away); row tiles 4 .. 7 use a second set of addresses 64 KB higher, as
+    the instruction offset holds 16 bits.  The bf16 pairs alternate between two buffers, so a row tile's
+    conversion overlaps the previous row tile's writes.  SwiGLU and the quantisation follow the final
+    barrier, in the unit's C++ code."""
+    E, E2 = cfg.v_ep, cfg.v_pk  # chunk addresses of row tiles 0 .. 3, and + 64 KB for row tiles 4 .. 7
+    out = [f"{700 + rbe}:", "s_waitcnt lgkmcnt(0)", "s_barrier", f"v_mov_b32_e32 v{E}, %[epb]"]
+    out += [f"v_xor_b32_e32 v{E + c}, {16 * c}, %[epb]" for c in range(1, 8)]
+    if rbe > 4:
+        out += [f"v_add_u32_e32 v{E2 + c}, 0x10000, v{E + c}" for c in range(8)]
+    out.append("s_nop 15")
+    for j in range(rbe):
+        T, PK, A = cfg.v_t, cfg.v_rbk + 16 * (j % 2), (E if j < 4 else E2)
+        out += [f"v_accvgpr_read_b32 v{T + 16 * ct + r}, a{cfg.acc(j, ct) + r}" for ct in range(2) for r in range(16)]
+        out.append("s_nop 1")
+        if j:  # row tile j - 2's writes (from this buffer) done, at most 15 LDS operations in flight
+            out.append("s_waitcnt lgkmcnt(7)")
+        for ct in range(2):
+            for g in range(4):
+                t, pr = T + 16 * ct + 4 * g, PK + 8 * ct + 2 * g
+                out += [f"v_cvt_pk_bf16_f32 v{pr}, v{t}, v{t + 1}", f"v_cvt_pk_bf16_f32 v{pr + 1}, v{t + 2}, v{t + 3}"]
+        off = 16384 * (j % 4)
+        out += [f"ds_write_b64 v{A + 4 * ct + g}, v[{PK + 8 * ct + 2 * g}:{PK + 8 * ct + 2 * g + 1}]"
+                + (f" offset:{off}" if off else "") for ct in range(2) for g in range(4)]
+    out += ["s_waitcnt lgkmcnt(0)", "s_branch 7f"]
+    return out
+
+
 def epilogue(cfg, rbe):
     """After the loop, for units of rbe row tiles: store row tile rbe - 2 (staged while the last row tile was
     multiplied) and convert, stage and store row tile rbe - 1, masking rows at or past the unit's end.  A
     wave without columns stores nothing.  The final barrier (label 7, shared) keeps the next unit's copies
     into the ring behind every wave's use of its staging area."""
+    if cfg.swiglu:
+        return swiglu_epilogue(cfg, rbe)
     out = [f"{700 + rbe}:", "s_cmp_eq_u32 %[won], 0", "s_cbranch_scc1 7f", "s_waitcnt lgkmcnt(0)"]
     out += ep_store_masked(cfg, rbe - 2) + ["s_nop 15", "s_nop 15"]
     out += ep_convert(cfg, rbe - 1, 0) + ep_convert(cfg, rbe - 1, 1) + ["s_nop 1"] + ep_stage(cfg, rbe - 1)
@@ -488,6 +530,7 @@ def clobbers(cfg):
 # The 192-row tiles serve experts of about one chunk (each weight byte read by one unit): their weight loads are
 # nontemporal.  The 256-row tiles serve experts of many chunks, whose units re-read the weights from L2.
 CONFIGS = [Cfg(192, 4, "TALL192", wnt=True), Cfg(256, 4, "TALL256"),
+           Cfg(192, 4, "SWIGLU_TALL192", wnt=True, swiglu=True), Cfg(256, 4, "SWIGLU_TALL256", swiglu=True),
            Cfg(192, 4, "BF16_TALL192", "bf16", wnt=True), Cfg(256, 4, "BF16_TALL256", "bf16"),
            Cfg(192, 4, "FP4_TALL192", "fp4", wnt=True), Cfg(256, 4, "FP4_TALL256", "fp4")]
 
@@ -497,7 +540,7 @@ def main():
         f.write("// Generated by gen_fp8_asm.py -- do not edit.\n")
         f.write(f"#define MOE_FP8_TALL_SCALE_ROWS {SCALE_ROWS}\n#define MOE_FP8_TALL_SCALE_GROUP {GROUP}\n")
         for cfg in CONFIGS:
-            n = cfg.name if cfg.bf16 or cfg.fp4 else "FP8_" + cfg.name
+            n = cfg.name if cfg.bf16 or cfg.fp4 or cfg.swiglu else "FP8_" + cfg.name
             f.write(f"// {n}: {cfg.rows} rows, ring {cfg.S}, {cfg.rt} row tiles, {cfg.ops} loads/K block "
                     + ("\n" if cfg.bf16 else "(+1 per scale group)\n"))
             f.write(f"#define MOE_{n}_SLOT_A {cfg.slot_a}\n#define MOE_{n}_SLOT {cfg.slot}\n"

@@ -61,6 +61,51 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
   return code | s;
 }
 
+// ---------------------------------------------------------------- SwiGLU --
+// silu(g) = g / (1 + exp(-g)) in fp32: x = -g log2(e) carried as hi + lo (hi the rounded product, lo its
+// error by one fma plus g times the error of the fp32 log2(e)); t = exp2(hi) * (1 + lo ln 2) with the
+// hardware exp2; silu = g * rcp(1 + t) with the hardware reciprocal.  Relative error a few fp32 ulps (about
+// 3e-7); a gate below about -88 makes t infinite and the result -0, never NaN.
+__device__ __forceinline__ float silu_f32(float g) {
+  constexpr float kLog2e = 1.44269504088896341f;       // log2(e) rounded to fp32
+  constexpr float kLog2eLo = 1.92596299e-08f;            // log2(e) - kLog2e
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float hi = -g * kLog2e;
+  const float lo = __builtin_fmaf(-g, kLog2e, -hi) - g * kLog2eLo;
+  const float t = __builtin_amdgcn_exp2f(hi) * __builtin_fmaf(lo, kLn2, 1.0f);
+  return g * __builtin_amdgcn_rcpf(1.0f + t);
+}
+
+// One 128-value block of SwiGLU and its 1x128 requantisation, spread over 16 consecutive lanes (all active):
+// each lane holds 8 consecutive gate and up values as bf16 pairs (element 2i in the low half of word i),
+// h = silu(gate) * up in fp32, the block's amax over the 16 lanes, e = pow2_exponent(amax), and this lane's
+// 8 E4M3 codes of h * 2^-e (round to nearest even) packed little-endian into *codes.  Returns e.
+__device__ __forceinline__ int swiglu_quant16(const v4i g, const v4i u, uint2* codes) {
+  float h[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t gw = (uint32_t)g[i], uw = (uint32_t)u[i];
+    h[2 * i] = silu_f32(bf16_to_f32(gw & 0xffffu)) * bf16_to_f32(uw & 0xffffu);
+    h[2 * i + 1] = silu_f32(bf16_to_f32(gw >> 16)) * bf16_to_f32(uw >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  const int e = pow2_exponent(amax);
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = __builtin_amdgcn_ldexpf(h[i], -e);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  codes->x = (uint32_t)lo;
+  codes->y = (uint32_t)hi;
+  return e;
+}
+
 // ----------------------------------------------------------- compile time --
 template <int V>
 struct IntC {

@@ -56,6 +56,8 @@ struct GemmArgs {
   const uint8_t* W;      // fp8 [E, N, K], int4 or fp4 [E, N, K/2], or bf16 [E, N, K]
   const void* SW;        // SFW fp32 [E, N/128, K/128], S16 fp16 [E, N, K/128] or E8M0 bytes [E, N, K/32] (fp4)
   uint16_t* D;           // bf16 [rows, N]
+  uint8_t* Q;            // SwiGLU GEMM: E4M3 [rows, N/2] (instead of D)
+  float* SQ;             // SwiGLU GEMM: fp32 [rows, N/256]
   const int32_t* counts;
   const int32_t* seg_offsets;
   int E;
@@ -66,6 +68,7 @@ struct GemmArgs {
   int wpacked;           // W in the fragment-packed order (moe_pack_weight_fp8 / _int4)
 };
 hipError_t launch_gemm_fp8(const GemmArgs& a, int expected_m, hipStream_t s);
+hipError_t launch_gemm_fp8_swiglu(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_fp4(const GemmArgs& a, int expected_m, hipStream_t s);

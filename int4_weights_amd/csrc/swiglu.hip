@@ -9,12 +9,9 @@
 // and the E4M3 codes of h * 2^-e (nxmr.cn DeepGEMM FP8 article, "补偿机制一").
 // h is quantised as computed in fp32, never rounded to bf16 in between.
 //
-// fp32 evaluation: g, u exact from bf16; x = -g * log2(e) carried as hi + lo
-// (hi the rounded product, lo its error by one fma, plus g times the error of
-// the fp32 log2(e)); t = exp2(hi) * (1 + lo * ln 2) with the hardware exp2;
-// s = g * rcp(1 + t) with the hardware reciprocal; h = s * u.  Relative error
-// a few fp32 ulps (about 3e-7) against the exact value; a gate below about
-// -88 makes t infinite and s = -0, never NaN.
+// fp32 evaluation (swiglu_quant16, shared with the up-projection GEMM that
+// fuses this step): g, u exact from bf16, silu_f32(g) * u; relative error a
+// few fp32 ulps (about 3e-7) against the exact value.
 //
 // Only the rows of the segments are touched (counts clipped to the segment
 // capacity, as in the grouped GEMM): padding rows are neither read nor
@@ -29,17 +26,6 @@
 namespace moe {
 
 constexpr int kSwQ = 6;  // 128-column blocks of loads in flight per lane
-
-// silu(g) = g / (1 + exp(-g)) in fp32, as stated in the file header.
-__device__ __forceinline__ float silu_f32(float g) {
-  constexpr float kLog2e = 1.44269504088896341f;       // log2(e) rounded to fp32
-  constexpr float kLog2eLo = 1.92596299e-08f;            // log2(e) - kLog2e
-  constexpr float kLn2 = 0.693147180559945309f;
-  const float hi = -g * kLog2e;
-  const float lo = __builtin_fmaf(-g, kLog2e, -hi) - g * kLog2eLo;
-  const float t = __builtin_amdgcn_exp2f(hi) * __builtin_fmaf(lo, kLn2, 1.0f);
-  return g * __builtin_amdgcn_rcpf(1.0f + t);
-}
 
 __global__ __launch_bounds__(256) void swiglu_quant_kernel(const SwigluArgs a) {
   __shared__ int s_cum[kMaxExperts + 1];
@@ -96,30 +82,9 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const SwigluArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < kSwQ; ++j) {
-        float h[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t gw = (uint32_t)g[j][i], uw = (uint32_t)u[j][i];
-          h[2 * i] = silu_f32(bf16_to_f32(gw & 0xffffu)) * bf16_to_f32(uw & 0xffffu);
-          h[2 * i + 1] = silu_f32(bf16_to_f32(gw >> 16)) * bf16_to_f32(uw >> 16);
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-        const int e = pow2_exponent(amax);
-        float y[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = __builtin_amdgcn_ldexpf(h[i], -e);
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+        uint2 o;
+        const int e = swiglu_quant16(g[j], u[j], &o);
         if (rok && kb0 + j < ib) {
-          uint2 o;
-          o.x = (uint32_t)lo;
-          o.y = (uint32_t)hi;
           *(uint2*)(qrow + (kb0 + j) * 128) = o;
           if (sub == 0) sfrow[kb0 + j] = pow2f(e);
         }

@@ -82,6 +82,15 @@ class MoeFP8Layer:
         am = self.am if self.layout == L.LAYOUT_MASKED else self.rows_cap
         L.moe_swiglu_quant(self.layout, D, am, self.counts, self.seg_offsets, self.E, q, sf)
 
+    def gemm_swiglu(self, q, sf):
+        """The up-projection on the packed rows with SwiGLU and the requantisation fused (this layer's weights
+        are the up-projection's, N = 2I): codes q [rows, N/2] and 1x128 scales sf [rows, N/256], the same bits
+        as gemm() followed by swiglu_quant(), without the bf16 output D."""
+        am = self.am if self.layout == L.LAYOUT_MASKED else self.rows_cap
+        L.moe_grouped_gemm_fp8_swiglu(self.layout | self.wflag, self.packed, self.packed_sf, self.w, self.sfw, q, sf,
+                                      self.counts, self.seg_offsets, self.E, am, self.N // 2, self.K,
+                                      self.expected_m)
+
     def combine(self, topk_weights, D=None, Z=None):
         """Weighted combine of packed rows D (default: this layer's GEMM output) into Z [T, D.shape[1]]."""
         T = topk_weights.shape[0]

@@ -214,6 +214,25 @@ def test_host_validation_rejects_without_launching(lib):
     assert sw(seg=0) == MOE_ERR_NULL                 # contiguous needs seg_offsets
     assert sw(q=A16 + 8) == MOE_ERR_ALIGN
     assert sw(sf=A16 + 2) == MOE_ERR_ALIGN
+    # moe_grouped_gemm_fp8_swiglu(layout, A, SFA, W, SFW, Q, SQ, counts, seg, E, rows, I, K, expected_m, stream)
+    def gs(layout=0, I=256, K=512, E=4, rows=512, seg=A16, A=A16, SFA=A16, SQ=A16, Q=A16):
+        return lib.moe_grouped_gemm_fp8_swiglu(layout, _p(A) if A else None, _p(SFA) if SFA else None, _p(A16),
+                                               _p(A16), _p(Q) if Q else None, _p(SQ) if SQ else None, _p(A16),
+                                               _p(seg) if seg else None, E, rows, I, K, 0, None)
+
+    assert gs(I=192) == MOE_ERR_UNSUPPORTED          # I must be a multiple of 128 (N = 2I of 256)
+    assert gs(I=0) == MOE_ERR_SHAPE
+    assert gs(K=384) == MOE_ERR_UNSUPPORTED          # the tall tile needs K % 512 == 0
+    assert gs(K=100) == MOE_ERR_UNSUPPORTED
+    assert gs(layout=0x10 | 7) == MOE_ERR_SHAPE
+    assert gs(E=0) == MOE_ERR_SHAPE
+    assert gs(seg=0) == MOE_ERR_NULL
+    assert gs(SFA=0) == MOE_ERR_NULL
+    assert gs(SQ=0) == MOE_ERR_NULL
+    assert gs(Q=0) == MOE_ERR_NULL
+    assert gs(Q=A16 + 8) == MOE_ERR_ALIGN
+    assert gs(SFA=A16 + 4) == MOE_ERR_ALIGN          # row scales: 16-byte copies
+    assert gs(SQ=A16 + 2) == MOE_ERR_ALIGN
     # moe_unpermute_combine
     assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 2, 12, _p(A16), None) == MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 0, 16, _p(A16), None) == MOE_ERR_SHAPE

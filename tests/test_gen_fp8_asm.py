@@ -172,20 +172,20 @@ def _walk(prog, rbe, kb):
 def test_each_unit_path_runs_its_blocks_once(gen, kb):
     """For every row-tile count: 4 MFMAs (FP8, MXFP4; 8 bf16 ones) per row tile and K block, one barrier per K block
     but the last, plus the prologue's and the one that ends the unit (so all waves of a workgroup meet at the
-    same barriers), the loads of exactly kb blocks (rbe activation copies per wave and block; FP8: with one
-    row-scale copy per 4 blocks), 4 stores (of 8
-    rows each) per row tile, at most 15 LDS operations in flight, and no register used before the load or LDS
-    read that fills it has been waited for."""
+    same barriers; SwiGLU: one more before its LDS writes), the loads of exactly kb blocks (rbe activation
+    copies per wave and block; FP8: with one row-scale copy per 4 blocks), 4 stores (of 8 rows each) per row
+    tile (SwiGLU: none, the C++ code stores), at most 15 LDS operations in flight, and no register used before
+    the load or LDS read that fills it has been waited for."""
     for cfg in _configs(gen):
         for packed in _orders(cfg):
             prog = gen.program(cfg, packed)
             for rbe in range(2, cfg.rt + 1):
                 c = _walk(prog, rbe, kb)
                 assert c["mfma"] == (8 if cfg.bf16 else 4) * rbe * kb, (cfg.name, rbe, kb, c)
-                assert c["barrier"] == 1 + (kb - 1) + 1, (cfg.name, rbe, kb, c)
+                assert c["barrier"] == 1 + (kb - 1) + 1 + cfg.swiglu, (cfg.name, rbe, kb, c)
                 groups = 0 if cfg.bf16 else kb // gen.GROUP
                 assert c["load"] == kb * cfg.ops_for(rbe) + groups, (cfg.name, rbe, kb, c)
-                assert c["store"] == 4 * rbe, (cfg.name, rbe, kb, c)
+                assert c["store"] == (0 if cfg.swiglu else 4 * rbe), (cfg.name, rbe, kb, c)
                 assert c["lds_max"] <= 15, (cfg.name, rbe, kb, c)
 
 
@@ -205,3 +205,76 @@ def test_register_regions_do_not_overlap(gen):
         used = [r for base, n in ep for r in range(base, base + n)]
         assert len(set(used)) == len(used)
         assert min(used) >= cfg.wbase and max(used) < cfg.wbase + 32 * (cfg.S - 1)
+
+
+def _swiglu_epilogue_lines(prog, rbe):
+    i = prog.index(f"{700 + rbe}:")
+    j = prog.index("s_branch 7f", i)
+    return prog[i + 1:j]
+
+
+@pytest.mark.parametrize("rows", [192, 256])
+def test_swiglu_staging_puts_each_value_where_the_rows_are_read(gen, rows):
+    """Follow the SwiGLU epilogue's address and data registers per lane (symbolically: which accumulator each
+    bf16 written to LDS came from) and check the bytes against the layout the unit's C++ code reads: row m at
+    512 m, chunk c (gate values 8 c .. 8 c + 7 for c < 16, up values 8 (c - 16) .. for c >= 16) at position
+    c ^ (m & 31).  Waves 0, 1 hold gate columns 64 w .. + 63 of the unit's 128 outputs, waves 2, 3 the up
+    columns 64 (w - 2) ..; accumulator register r of lane L holds row L % 32 and column 8 (r / 4) +
+    4 (L / 32) + r % 4 of its 32-column tile.  Every (row, gate/up, output) of the computed row tiles is
+    written exactly once, inside the staging area, and nothing else is."""
+    cfg = next(c for c in gen.CONFIGS if c.swiglu and c.rows == rows)
+    for packed in (False, True):
+        prog = gen.program(cfg, packed)
+        for rbe in range(2, cfg.rt + 1):
+            lines = _swiglu_epilogue_lines(prog, rbe)
+            seen = {}
+            for w in range(4):
+                for lane in range(64):
+                    l32, hh = lane % 32, lane // 32
+                    epb = l32 * 512 + 16 * ((8 * w) ^ l32) + 8 * hh  # the lane's address, as the C++ code sets it
+                    reg = {}
+                    for ln in lines:
+                        m = re.fullmatch(r"v_mov_b32_e32 v(\d+), %\[epb\]", ln)
+                        if m:
+                            reg[int(m.group(1))] = epb
+                            continue
+                        m = re.fullmatch(r"v_xor_b32_e32 v(\d+), (\d+), %\[epb\]", ln)
+                        if m:
+                            reg[int(m.group(1))] = epb ^ int(m.group(2))
+                            continue
+                        m = re.fullmatch(r"v_add_u32_e32 v(\d+), 0x10000, v(\d+)", ln)
+                        if m:
+                            reg[int(m.group(1))] = reg[int(m.group(2))] + 0x10000
+                            continue
+                        m = re.fullmatch(r"v_accvgpr_read_b32 v(\d+), a(\d+)", ln)
+                        if m:
+                            reg[int(m.group(1))] = ("acc", int(m.group(2)))
+                            continue
+                        m = re.fullmatch(r"v_cvt_pk_bf16_f32 v(\d+), v(\d+), v(\d+)", ln)
+                        if m:
+                            reg[int(m.group(1))] = (reg[int(m.group(2))], reg[int(m.group(3))])
+                            continue
+                        m = re.fullmatch(r"ds_write_b64 v(\d+), v\[(\d+):(\d+)\](?: offset:(\d+))?", ln)
+                        if m:
+                            p0, p1 = int(m.group(2)), int(m.group(3))
+                            assert p1 == p0 + 1
+                            addr = reg[int(m.group(1))] + int(m.group(4) or 0)
+                            vals = [*reg[p0], *reg[p1]]
+                            for k, v in enumerate(vals):
+                                a = addr + 2 * k
+                                assert 0 <= a < rows * 512 and a not in seen, (rbe, w, lane, ln)
+                                seen[a] = (w, l32, hh, v)
+                            continue
+                        assert ln.startswith("s_"), ln  # nothing else touches registers or memory
+            assert len(seen) == rbe * 32 * 512 // 2
+            for a, (w, l32, hh, v) in seen.items():
+                m, pos, within = a // 512, (a % 512) // 16, a % 16
+                c = pos ^ (m & 31)
+                kind, f = ("gate", 8 * c + within // 2) if c < 16 else ("up", 8 * (c - 16) + within // 2)
+                _, accreg = v
+                j, ct, r = accreg // 32, (accreg % 32) // 16, accreg % 16
+                assert m == 32 * j + l32, (a, v)
+                col = 32 * ct + 8 * (r // 4) + 4 * hh + r % 4
+                assert (kind, f) == (("gate", 64 * w + col) if w < 2 else ("up", 64 * (w - 2) + col)), (a, v)
+            # the C++ reads rows 0 .. 32 rbe - 1, all 32 chunks each
+            assert {a // 512 for a in seen} == set(range(32 * rbe))

@@ -238,6 +238,12 @@ def test_full_size_qwen3_skewed_up_down_combine():
     Dd = torch.empty(layer.rows_cap, Nd, dtype=torch.bfloat16, device=DEV)
     Zd = torch.empty(c["T"], Nd, dtype=torch.bfloat16, device=DEV)
     layer.swiglu_quant(qd, sfd)
+    # the up-projection with SwiGLU fused gives the same bits on every valid row (checked below against the
+    # oracle through qd on the sampled rows)
+    qf = torch.full((layer.rows_cap, Kd), 0xA5, dtype=torch.uint8, device=DEV)
+    sff = torch.full((layer.rows_cap, Kd // 128), -3.0, dtype=torch.float32, device=DEV)
+    print("[fullsize] qwen3_skewed fused up-projection + SwiGLU", flush=True)
+    layer.gemm_swiglu(qf, sff)
     layer.gemm(A=qd, SFA=sfd, D=Dd, w=dpacked, sfw=dsfw, N=Nd, K=Kd)
     layer.combine(torch.from_numpy(c["tw"]).to(DEV), D=Dd, Z=Zd)
     torch.cuda.synchronize()
@@ -275,6 +281,13 @@ def test_full_size_qwen3_skewed_up_down_combine():
     # instruction's accumulation, about 1% of its outputs by one ulp) or the fp32 SwiGLU lands on the other side of
     # an E4M3 rounding midpoint: rare
     assert flips <= total // 200, f"{flips} of {total} SwiGLU codes differ"
+    vrows = np.zeros(layer.rows_cap, bool)
+    for e in range(c["E"]):
+        st = int(r["seg_offsets"][e])
+        vrows[st:st + int(r["counts"][e])] = True
+    vsel = torch.from_numpy(vrows).to(DEV)
+    assert torch.equal(qf[vsel], qd[vsel]) and torch.equal(sff[vsel], sfd[vsel])
+    assert (qf[~vsel] == 0xA5).all() and (sff[~vsel] == -3.0).all()
     t = c["tok"]
     zr = sum(float(c["tw"][t, s]) * yrow[int(r["output_index"][t, s])] for s in range(c["k"]))
     zg = Zd[t][torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)

@@ -1,18 +1,6 @@
-"""GPU SwiGLU + 1x128 FP8 requantisation (moe_swiglu_quant) vs the oracle.
-
-The kernel evaluates h = silu(gate) * up in fp32 (expf, one IEEE division, one
-multiply: a few fp32 ulps from the exact value) and the oracle in float64, so
-a code or a scale can differ only where the float64 value lies within that
-error of a rounding boundary of the E4M3 grid or of the power-of-two scale
-rule.  The test therefore requires:
-  * every scale a power of two, and equal to the oracle's unless the block's
-    float64 amax is within 1e-6 (relative) of a boundary 448 * 2^k, or below
-    the fp32 normal range (h underflows to 0 in fp32: zero codes either way);
-  * every code equal to the oracle's unless the block's scale differs or the
-    float64 scaled value is within 1e-6 (relative) of an E4M3 rounding
-    midpoint -- and such exceptions to be rare;
-  * every dequantised value within the E4M3 rounding bound of the float64 h;
-  * rows outside the segments untouched.
+"""GPU SwiGLU + 1x128 FP8 requantisation (moe_swiglu_quant) vs the oracle (the bar is that of
+gpu_helpers.check_swiglu_quant: codes and scales equal to the float64 oracle's except within fp32 error of a
+rounding boundary, every value within the E4M3 rounding bound, rows outside the segments untouched).
 """
 
 import numpy as np
@@ -21,26 +9,10 @@ import torch
 
 import int4_weights_amd as moe
 import oracle
-from gpu_helpers import DEV, bf16_from_u16, require_gpu, u16
+from gpu_helpers import DEV, bf16_from_u16, check_swiglu_quant, require_gpu, u16
 
 pytestmark = pytest.mark.gpu
 SENT = 0xA5
-
-
-def _midpoints():
-    """Sorted float64 midpoints between consecutive non-negative E4M3 values (0 .. 448)."""
-    tab = oracle.e4m3_decode_table()[:127]
-    return (tab[:-1] + tab[1:]) / 2.0
-
-
-MID = _midpoints()
-
-
-def _near_midpoint(v, rel=1e-6):
-    a = np.abs(v)
-    i = np.clip(np.searchsorted(MID, a), 1, len(MID) - 1)
-    d = np.minimum(np.abs(a - MID[i - 1]), np.abs(a - MID[i]))
-    return d <= rel * np.maximum(a, 2.0 ** -9)
 
 
 def _run(gu_bits, layout, am, counts, seg, E):
@@ -64,33 +36,7 @@ def _valid_rows(counts, seg, rows, layout, am):
 
 
 def _check(gu_bits, q, sf, valid):
-    I = gu_bits.shape[1] // 2
-    assert (q[~valid] == SENT).all() and (sf[~valid] == -3.0).all(), "rows outside the segments were written"
-    gu = oracle.bf16_bits_to_f64(gu_bits[valid])
-    h = oracle.swiglu(gu)
-    qo, so = oracle.quant_act_values(h)
-    qg, sg = q[valid], sf[valid]
-    bits = sg.view(np.uint32)
-    assert ((bits & 0x807FFFFF) == 0).all() and (bits != 0).all(), "scales must be powers of two"
-    nb = I // 128
-    amax = np.abs(h.reshape(-1, nb, 128)).max(axis=2)
-    ratio = amax / 448.0
-    near_scale = (ratio > 0) & (np.abs(ratio / np.exp2(np.round(np.log2(np.maximum(ratio, 1e-300)))) - 1.0) <= 1e-6)
-    # a block whose float64 amax lies below the fp32 normal range underflows to 0 in fp32 (scale 1, zero codes)
-    # while float64 keeps a tiny value (scale 2^-126, zero codes): the same zeros, encoded with another scale
-    tiny = amax < 2.0 ** -120
-    scale_ok = (sg == so) | near_scale | tiny
-    assert scale_ok.all(), f"{int((~scale_ok).sum())} block scales differ away from a boundary"
-    same_scale = np.repeat(sg == so, 128, axis=1)
-    scaled = h / np.repeat(so.astype(np.float64), 128, axis=1)
-    code_ok = (qg == qo) | ~same_scale | _near_midpoint(scaled)
-    assert code_ok.all(), f"{int((~code_ok).sum())} codes differ away from a rounding midpoint"
-    exceptions = int(((qg != qo) & same_scale).sum())
-    assert exceptions <= max(2, qg.size // 10000), f"{exceptions} of {qg.size} codes differ"
-    deq = oracle.dequant_act(qg, sg)
-    s = np.repeat(sg.astype(np.float64), 128, axis=1)
-    assert (np.abs(deq - h) <= np.maximum(2.0 ** -4 * np.abs(h), 2.0 ** -10 * s) * (1 + 1e-5) + 1e-30).all()
-    return exceptions
+    return check_swiglu_quant(gu_bits[valid], q, sf, valid, SENT, -3.0)
 
 
 def _gu(rng, rows, I, scale=2.0):
