@@ -4,9 +4,10 @@
 A step is one pass of the whole path over one batch of synthetic input with
 everything already resident in HBM:
     moe_quant_act -> moe_route_pack -> moe_grouped_gemm_fp8 -> moe_unpermute_combine
-(for the Qwen3-shaped workload the whole expert FFN: up-projection, SwiGLU +
-requantisation (moe_swiglu_quant), down-projection, then the combine; the
-4-bit GEMM in place of the FP8 one for the INT4 workload).
+(for the Qwen3-shaped workload the whole expert FFN: the up-projection with
+SwiGLU and the requantisation in its epilogue (moe_grouped_gemm_fp8_swiglu),
+the down-projection, then the combine; the 4-bit GEMM in place of the FP8 one
+for the INT4 workload).
 
 Default workload: DeepSeek-V3-shaped prefill (T=4096 tokens, 256 experts,
 top-8, K=7168, N=4096, FP8 E4M3 with 1x128 / 128x128 power-of-two scales,
@@ -85,6 +86,8 @@ def copy_calibration(mib):
 KERNEL_SOURCES = {
     "moe_grouped_gemm_fp8": ["csrc/gemm_fp8.hip", "csrc/gen_fp8_asm.py", "csrc/gemm_common.h", "csrc/moe_device.h",
                              "csrc/moe_internal.h", "build.py"],
+    "moe_grouped_gemm_fp8_swiglu": ["csrc/gemm_fp8.hip", "csrc/gen_fp8_asm.py", "csrc/gemm_common.h",
+                                    "csrc/moe_device.h", "csrc/moe_internal.h", "build.py"],
     "moe_grouped_gemm_int4": ["csrc/gemm_int4.hip", "csrc/gemm_common.h", "csrc/moe_device.h", "csrc/moe_internal.h",
                               "build.py"],
     "moe_grouped_gemm_fp8_fp4": ["csrc/gemm_fp4.hip", "csrc/gemm_common.h", "csrc/moe_device.h",
@@ -227,11 +230,13 @@ def fp8_weights(torch, moe, synth, cfg, N, K, stream_id, keep=()):
     return codes, sfw, kept
 
 
-def fp8_gemm_roofline(rows_valid, active, N, K, t_ms):
-    """Algorithmic flops and bytes of one FP8 grouped-GEMM launch and where they put it on the roofline."""
+def fp8_gemm_roofline(rows_valid, active, N, K, t_ms, swiglu=False):
+    """Algorithmic flops and bytes of one FP8 grouped-GEMM launch and where they put it on the roofline
+    (swiglu: the up-projection that writes N/2 FP8 codes and N/256 scales per row instead of N bf16)."""
     flops = 2.0 * rows_valid * N * K
+    out_row = (N // 2 + 4 * (N // 256)) if swiglu else 2 * N
     nbytes = active * N * K + active * (N // 128) * (K // 128) * 4 + rows_valid * (K + 4 * K // 128) \
-        + rows_valid * N * 2
+        + rows_valid * out_row
     t = t_ms / 1e3
     ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if flops / nbytes < ridge:
@@ -280,9 +285,9 @@ def build_workload(args, cfg, torch, np, moe, synth, want_cpu):
                 layer.combine(tw)
                 tm.mark(s, 4)
         else:
-            # the whole expert FFN: up-projection (gate and up columns), SwiGLU + requantisation, down-projection
-            names = ["moe_quant_act", "moe_route_pack", "gemm", "moe_swiglu_quant", "gemm_down",
-                     "moe_unpermute_combine"]
+            # the whole expert FFN: up-projection (gate and up columns) with SwiGLU + requantisation in its
+            # epilogue, down-projection
+            names = ["moe_quant_act", "moe_route_pack", "gemm", "gemm_down", "moe_unpermute_combine"]
             assert N == 2 * cfg.K_down
             dcodes, dsfw, _ = fp8_weights(torch, moe, synth, cfg, cfg.N_down, cfg.K_down, synth.STREAM_WEIGHTS_DOWN)
             qd = torch.empty(layer.rows_cap, cfg.K_down, dtype=torch.uint8, device=dev)
@@ -296,14 +301,12 @@ def build_workload(args, cfg, torch, np, moe, synth, want_cpu):
                 tm.mark(s, 1)
                 layer.route(ids)
                 tm.mark(s, 2)
-                layer.gemm()
+                layer.gemm_swiglu(qd, sfd)
                 tm.mark(s, 3)
-                layer.swiglu_quant(qd, sfd)
-                tm.mark(s, 4)
                 layer.gemm(A=qd, SFA=sfd, D=Dd, w=dcodes, sfw=dsfw, N=cfg.N_down, K=cfg.K_down)
-                tm.mark(s, 5)
+                tm.mark(s, 4)
                 layer.combine(tw, D=Dd, Z=Zd)
-                tm.mark(s, 6)
+                tm.mark(s, 5)
     else:
         # 4-bit weights: several copies rotate across steps so the 256 MB cache never holds the weights
         # (one allocation holds all copies, made before the generation temporaries)
@@ -537,7 +540,7 @@ def summarise(args, np, wl, ms_step, per, host_ms, clock):
     kern = {n: stats(v) for n, v in per.items()}
     out = {"ms_per_step": ms_step, "kernels_ms": kern}
     if cfg.weights == "fp8":
-        roof = fp8_gemm_roofline(rows_valid, active, N, K, kern["gemm"]["mean"])
+        roof = fp8_gemm_roofline(rows_valid, active, N, K, kern["gemm"]["mean"], swiglu=bool(cfg.K_down))
         flops = roof["flops_per_launch"]
         if cfg.K_down:
             rd = fp8_gemm_roofline(rows_valid, active, cfg.N_down, cfg.K_down, kern["gemm_down"]["mean"])
@@ -551,7 +554,7 @@ def summarise(args, np, wl, ms_step, per, host_ms, clock):
         else:
             value, unit = flops / (ms_step / 1e3) / 1e12, "TFLOP/s"
         dtype = "fp8_e4m3"
-        kernel = "moe_grouped_gemm_fp8"
+        kernel = "moe_grouped_gemm_fp8_swiglu" if cfg.K_down else "moe_grouped_gemm_fp8"
     else:
         nbytes = active * N * (K // 2) + active * N * (K // 128) * 2 + rows_valid * K * 2 + rows_valid * N * 2
         t = kern["gemm"]["mean"] / 1e3

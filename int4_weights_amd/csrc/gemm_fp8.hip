@@ -320,7 +320,8 @@ template <int ROWS>
 __device__ __forceinline__ void swiglu_unit_rows(const GemmArgs& a, const Fp8TallSmem<ROWS>& sm, int row0,
                                                  int mrows, int nt, int rbe) {
   const int I = a.N / 2, ib = I / 128, lane = lane_id(), sub = lane & 15, wv = uniform(threadIdx.x >> 6);
-  for (int m0 = 0; m0 < 32 * rbe; m0 += 16) {
+#pragma unroll 2
+  for (int m0 = 0; m0 < 32 * rbe; m0 += 16) {  // (2 rbe iterations; two rows' chains interleave: 4 was slower)
     const int m = m0 + 4 * wv + (lane >> 4), sw = m & 31;
     const v4i g = *(const v4i*)&sm.b[m * 512 + 16 * (sub ^ sw)];
     const v4i up = *(const v4i*)&sm.b[m * 512 + 16 * ((16 + sub) ^ sw)];

@@ -76,6 +76,17 @@ __device__ __forceinline__ float silu_f32(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + t);
 }
 
+// Maximum over each group of 16 lanes (lanes 16r .. 16r + 15), every lane of the group receiving it, by four
+// DPP moves inside the VALU (no LDS round trip): swap neighbours (quad_perm [1,0,3,2]), swap pairs
+// ([2,3,0,1]), mirror each 8 lanes (row_half_mirror), mirror the 16 (row_mirror).  All lanes active.
+__device__ __forceinline__ float max16_lanes(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
 // One 128-value block of SwiGLU and its 1x128 requantisation, spread over 16 consecutive lanes (all active):
 // each lane holds 8 consecutive gate and up values as bf16 pairs (element 2i in the low half of word i),
 // h = silu(gate) * up in fp32, the block's amax over the 16 lanes, e = pow2_exponent(amax), and this lane's
@@ -91,8 +102,7 @@ __device__ __forceinline__ int swiglu_quant16(const v4i g, const v4i u, uint2* c
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  amax = max16_lanes(amax);
   const int e = pow2_exponent(amax);
   float y[8];
 #pragma unroll
