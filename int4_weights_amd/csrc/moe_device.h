@@ -76,15 +76,17 @@ __device__ __forceinline__ float silu_f32(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + t);
 }
 
-// Maximum over each group of 16 lanes (lanes 16r .. 16r + 15), every lane of the group receiving it, by four
-// DPP moves inside the VALU (no LDS round trip): swap neighbours (quad_perm [1,0,3,2]), swap pairs
-// ([2,3,0,1]), mirror each 8 lanes (row_half_mirror), mirror the 16 (row_mirror).  All lanes active.
-__device__ __forceinline__ float max16_lanes(float v) {
+// Maximum over each group of 8 (16) lanes, every lane of the group receiving it, by DPP moves inside the VALU
+// (no LDS round trip): swap neighbours (quad_perm [1,0,3,2]), swap pairs ([2,3,0,1]), mirror each 8 lanes
+// (row_half_mirror), and for 16 lanes mirror the 16 (row_mirror).  All lanes active.
+__device__ __forceinline__ float max8_lanes(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
-  return v;
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float max16_lanes(float v) {
+  v = max8_lanes(v);
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
 }
 
 // One 128-value block of SwiGLU and its 1x128 requantisation, spread over 16 consecutive lanes (all active):

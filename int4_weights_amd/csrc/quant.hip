@@ -33,8 +33,7 @@ __device__ __forceinline__ void quant_act_block(const v4i raw0, const v4i raw1, 
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-  for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 8));
+  amax = max8_lanes(amax);
   const int e = pow2_exponent(amax);
   // gfx950's v_cvt_pk_fp8_f32 converts to OCP E4M3FN with round to nearest
   // even, subnormals kept, sign kept; the scaled values never exceed 448
