@@ -316,6 +316,23 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
 // past the unit's end are read (they repeat its last row) but not stored.  The closing barrier keeps the next
 // unit's copies into the ring behind these reads.
 // The unit is passed as wave-uniform values (SGPRs), since every VGPR outside the loop's own is scarce across it.
+// The plain tall loops also take the next unit's copy offsets and bases, whether this unit's first copies were
+// issued by the previous unit (pfd) and whether a next unit follows (hasnext).
+#define MOE_TALL_XPF_ASM(LOOP, AO_OUTS, CLOBBERS)                                                      \
+  asm volatile(LOOP                                                                                             \
+               : [wo0] "+v"(wo[0]), [wo1] "+v"(wo[1]), AO_OUTS,                                                    \
+                 [so] "+v"(so), [wso] "+v"(wso), [doff] "+v"(doff), [ks] "=&s"(ks), [q] "=&s"(q), [t] "=&s"(t),  \
+                 [inc] "=&s"(inc), [inc4] "=&s"(inc4), [sv] "=&s"(sv), [m0v] "+{m0}"(m0v), [msg] "+s"(msg),       \
+                 [nso] "+v"(nso), [uo0] "+v"(uo0), [cc] "+v"(cc), [nwo0] "+v"(nwo[0]), [nwo1] "+v"(nwo[1]),      \
+                 [nwso] "+v"(nwso)                                                                               \
+               : [wb] "s"(wb), [ab] "s"(ab), [sb] "s"(sb), [swb] "s"(swb), [ma] "s"(ma),                       \
+                 [a00] "v"(af[0]), [a01] "v"(af[1]), [a10] "v"(af[2]), [a11] "v"(af[3]), [sadr] "v"(sadr),        \
+                 [db] "s"(db), [dstep] "s"(dstep), [kb] "s"(kb),                                                 \
+                 [rbe] "s"(rbe), [mrows] "s"(mrows), [won] "s"(wons), [wm] "s"(wm), [wstep] "s"(wstep),           \
+                 [l8] "v"(l8), [epb] "v"(epb), [rb] "v"(rb), [nab] "s"(nab), [nsb] "s"(nsb),                      \
+                 [nlim] "s"(nlim), [fl] "s"(flags), [nwb] "s"(nwb), [nswb] "s"(nswb)                              \
+               : "memory", "vcc", "exec", "scc", CLOBBERS)
+
 template <int ROWS>
 __device__ __forceinline__ void swiglu_unit_rows(const GemmArgs& a, const Fp8TallSmem<ROWS>& sm, int row0,
                                                  int mrows, int nt, int rbe) {
@@ -336,10 +353,16 @@ __device__ __forceinline__ void swiglu_unit_rows(const GemmArgs& a, const Fp8Tal
   __syncthreads();
 }
 
+// Plain units (not SWIGLU) pipeline across units: the last K block of unit u issues the activation copies of
+// K blocks 0 and 1 of the next unit nu (and its first row-scale group) into the ring slots 0 and 1, idle by
+// then, and u's loop ends by issuing nu's weights and weight scales of those blocks into the ring registers,
+// so nu's loop starts with its first two K blocks in flight; msgs carries the row-scale group buffer across
+// units.  pfd: u's first loads were issued that way; hasnext: nu is a real unit (else nu is u itself, its
+// copies repeat u's own harmlessly and the loop waits for them instead of issuing weights).
 template <int ROWS, bool PACKED, bool SWIGLU>
 __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, Fp8TallSmem<ROWS>& sm, int wv,
-                                              int lane) {
-  constexpr int kTApw = TallCfg<ROWS>::kApw, kScOff = TallCfg<ROWS>::kScOff;
+                                              int lane, const Unit& nu, int pfd, int hasnext, uint32_t& msgs) {
+  constexpr int kTApw = TallCfg<ROWS>::kApw, kScOff = TallCfg<ROWS>::kScOff, kSlot = TallCfg<ROWS>::kSlot;
   const int l32 = lane & 31, hh = lane >> 5;  // operand row and K half of this lane
   const int K = a.K, N = a.N, KB = K / 128, NB = N / 128;
   // SwiGLU: the unit's 128 outputs are gate columns n0 / 2 .. + 127 (waves 0, 1) and the up columns N / 2
@@ -350,26 +373,46 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
 
   // weights: column tile c (32 columns) of this wave; see the operand notes in gen_fp8_asm.py
   const uint64_t wb = uniform_u64((uint64_t)(a.W + (int64_t)u.e * N * K));
-  uint32_t wo[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-    wo[c] = PACKED ? (uint32_t)((ncl + 32 * c) / 16 + l32 / 16) * 2048u + (uint32_t)((l32 & 15) + 32 * hh) * 16u
-                   : (uint32_t)(ncl + 32 * c + l32) * (uint32_t)K + 32u * hh;
   const int wstep = uniform(PACKED ? 128 * N : 128);  // weight bytes per K block
+  const auto wcol = [&](int col, int c) {
+    return PACKED ? (uint32_t)((col + 32 * c) / 16 + l32 / 16) * 2048u + (uint32_t)((l32 & 15) + 32 * hh) * 16u
+                  : (uint32_t)(col + 32 * c + l32) * (uint32_t)K + 32u * hh;
+  };
+  uint32_t wo[2], nwo[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) wo[c] = wcol(ncl, c) + (pfd ? 2u * (uint32_t)wstep : 0u);  // (pfd: from block 2)
+  // the next unit's weights, loaded at the end of this unit's loop (an idle wave's columns clamped as above)
+  const int nncol0 = nu.n0 + 64 * wv, nncl = nncol0 < N ? nncol0 : N - 64;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) nwo[c] = SWIGLU ? 0u : wcol(nncl, c);
+  const uint64_t nwb = SWIGLU ? 0 : uniform_u64((uint64_t)(a.W + (int64_t)nu.e * N * K));
+  const uint64_t nswb =
+      SWIGLU ? 0 : uniform_u64((uint64_t)((const float*)a.SW + ((int64_t)nu.e * NB + nncl / 128) * KB));
+  uint32_t nwso = 0;
   const uint64_t ab = uniform_u64((uint64_t)(a.A + (int64_t)u.row0 * K));
   uint32_t ao[kTApw];
+  // (copies of K blocks 0 and 1 already issued: the offsets start at block 2)
+  const uint32_t a_skip = pfd ? 256u : 0u;
 #pragma unroll
   for (int i = 0; i < kTApw; ++i) {
     const int r = 8 * (4 * i + wv) + (lane >> 3);  // tile row this lane copies (copy i of the wave)
-    const int c = (lane & 7) ^ ((r >> 1) & 7);     // its chunk, landing at position lane & 7
-    ao[i] = (uint32_t)min(r, u.mrows - 1) * (uint32_t)K + 16u * c;
+    const int c = (lane & 7) ^ ((r >> 1) & 7);     // its chunk, landing at position lane & 7 (c = cc / 16 below)
+    ao[i] = (uint32_t)min(r, u.mrows - 1) * (uint32_t)K + 16u * c + a_skip;
   }
+  // the next unit's copies (the loop derives their offsets): row 8 wv + lane / 8 of copy 0, unclamped
+  // (cc, uo0, nso: in/out operands of the loop, so that no output can share their registers)
+  uint32_t cc = SWIGLU ? 0u : 16u * (uint32_t)((lane & 7) ^ ((4 * wv + (lane >> 4)) & 7));
+  uint32_t uo0 = SWIGLU ? 0u : (uint32_t)(8 * wv + (lane >> 3)) * (uint32_t)K + cc;
+  const int nlim = SWIGLU ? 0 : uniform((nu.mrows - 1) * K);
+  const uint64_t nab = SWIGLU ? 0 : uniform_u64((uint64_t)(a.A + (int64_t)nu.row0 * K));
   // row scales: lane copies row 64 wv + lane (the unit's last row past its end), 16 bytes per 4 K blocks
   const uint64_t sb = uniform_u64((uint64_t)(a.SFA + (int64_t)u.row0 * KB));
-  uint32_t so = (uint32_t)min(64 * wv + lane, u.mrows - 1) * (uint32_t)(KB * 4);
+  uint32_t so = (uint32_t)min(64 * wv + lane, u.mrows - 1) * (uint32_t)(KB * 4) + (pfd && KB > 4 ? 16u : 0u);
+  const uint64_t nsb = SWIGLU ? 0 : uniform_u64((uint64_t)(a.SFA + (int64_t)nu.row0 * KB));
+  uint32_t nso = SWIGLU ? 0u : (uint32_t)min(64 * wv + lane, nu.mrows - 1) * (uint32_t)(KB * 4);
   // weight scale of this wave's 64 columns (one 128-column block), the same address in every lane
   const uint64_t swb = uniform_u64((uint64_t)((const float*)a.SW + ((int64_t)u.e * NB + ncl / 128) * KB));
-  uint32_t wso = 0;
+  uint32_t wso = pfd ? 8u : 0u;
 
   // fragment reads: row m at m*128, chunk c at position c ^ ((m >> 1) & 7); lane (row l32, half hh) reads
   // chunks 4 kk + 2 hh + p for the halves kk and pieces p of the K block
@@ -378,18 +421,24 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   uint32_t af[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) af[i] = abase + l32 * 128 + 16 * ((4 * (i >> 1) + 2 * hh + (i & 1)) ^ fsw);
-  const uint32_t sadr = abase + kScOff + 16 * l32;  // row scale of row tile j, block s of the group: +512 j + 4 s
   const uint32_t ma = (uint32_t)uniform((int)lds_offset(&sm.b[wv * 1024]));  // copy i at + 4096 i
-  uint32_t msg = (uint32_t)uniform((int)lds_offset(&sm.b[kScOff + wv * 1024]));  // group buffer 0, this wave's rows
+  // row-scale group buffer of the next group copy (0 or 1, 4 KB apart); the unit's first group is in the one
+  // msg points at, or (pfd) was copied there before the previous unit's copy toggled msg
+  const uint32_t msg0 = (uint32_t)uniform((int)lds_offset(&sm.b[kScOff + wv * 1024]));
+  uint32_t msg = SWIGLU ? msg0 : (uint32_t)uniform((int)msgs);
+  const uint32_t sbuf = (pfd ? msg ^ 4096u : msg) - msg0;
+  const uint32_t sadr = abase + kScOff + 16 * l32 + sbuf;  // row scale of row tile j, block s: +512 j + 4 s
   // epilogue: one 32-row tile of the wave's bf16 rows at a time goes through its own 4 KB of ring slot 0
   // (row m at m*128, 16-byte chunk c at position c ^ (m & 7)); each lane writes 8 bytes of row l32 (epb:
   // chunk 0's address, including the lane's half) and reads back 16 bytes (chunk lane & 7) of row lane >> 3
   // of every 8-row group, stored as whole 128-byte rows
   // (SwiGLU: epb is this lane's 8 bytes of chunk 8 wv of row l32 of the staged bf16 rows, see swiglu_unit_rows)
+  // (plain units stage through ring slot 2: slots 0 and 1 receive the next unit's copies meanwhile)
+  const uint32_t stg = abase + (SWIGLU ? 0u : 2u * kSlot);
   const uint32_t epb = SWIGLU ? abase + (uint32_t)(l32 * 512 + 16 * ((8 * wv) ^ l32) + 8 * hh)
-                              : abase + (uint32_t)(wv * 4096 + l32 * 128 + 16 * (l32 & 7) + 8 * hh);
+                              : stg + (uint32_t)(wv * 4096 + l32 * 128 + 16 * (l32 & 7) + 8 * hh);
   const int l8 = lane >> 3;
-  const uint32_t rb = abase + (uint32_t)(wv * 4096 + l8 * 128 + 16 * ((lane & 7) ^ (l8 & 7)));
+  const uint32_t rb = stg + (uint32_t)(wv * 4096 + l8 * 128 + 16 * ((lane & 7) ^ (l8 & 7)));
   const uint64_t wm = uniform_u64(won ? ~0ull : 0ull);  // exec mask of the stores: none for an idle wave
   const uint64_t db = SWIGLU ? 0 : uniform_u64((uint64_t)(a.D + (int64_t)u.row0 * N));  // (SwiGLU: no D)
   uint32_t doff = (uint32_t)(l8 * N + ncol0 + 8 * (lane & 7)) * 2u;
@@ -398,6 +447,7 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   // the second-to-last row tile's successor are read) has a place in every step
   const int rbe = uniform(max(2, (u.mrows + 31) / 32));
   const int kb = uniform(KB), mrows = uniform(u.mrows), wons = uniform(won);
+  const int flags = uniform(pfd | (hasnext << 1));  // bit 0: pfd, bit 1: hasnext
   const int row0 = uniform(u.row0), nt = uniform(u.n0 / 256);  // (SwiGLU, after the loop)
   int ks, q, t, inc, inc4, m0v = 0;
   uint64_t sv;
@@ -416,15 +466,16 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
     swiglu_unit_rows<ROWS>(a, sm, row0, mrows, nt, rbe);
   } else if constexpr (ROWS == 192) {
     if constexpr (PACKED)
-      MOE_TALL_ASM(MOE_FP8_TALL192_LOOP_PACKED, MOE_FP8_TALL192_AO_OUTS, MOE_FP8_TALL192_CLOBBERS);
+      MOE_TALL_XPF_ASM(MOE_FP8_TALL192_LOOP_PACKED, MOE_FP8_TALL192_AO_OUTS, MOE_FP8_TALL192_CLOBBERS);
     else
-      MOE_TALL_ASM(MOE_FP8_TALL192_LOOP, MOE_FP8_TALL192_AO_OUTS, MOE_FP8_TALL192_CLOBBERS);
+      MOE_TALL_XPF_ASM(MOE_FP8_TALL192_LOOP, MOE_FP8_TALL192_AO_OUTS, MOE_FP8_TALL192_CLOBBERS);
   } else {
     if constexpr (PACKED)
-      MOE_TALL_ASM(MOE_FP8_TALL256_LOOP_PACKED, MOE_FP8_TALL256_AO_OUTS, MOE_FP8_TALL256_CLOBBERS);
+      MOE_TALL_XPF_ASM(MOE_FP8_TALL256_LOOP_PACKED, MOE_FP8_TALL256_AO_OUTS, MOE_FP8_TALL256_CLOBBERS);
     else
-      MOE_TALL_ASM(MOE_FP8_TALL256_LOOP, MOE_FP8_TALL256_AO_OUTS, MOE_FP8_TALL256_CLOBBERS);
+      MOE_TALL_XPF_ASM(MOE_FP8_TALL256_LOOP, MOE_FP8_TALL256_AO_OUTS, MOE_FP8_TALL256_CLOBBERS);
   }
+  if constexpr (!SWIGLU) msgs = msg;
 }
 
 template <int ROWS>
@@ -436,10 +487,18 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_tall_kernel(const GemmArgs a)
   const Walk walk = sched_walk(s_sched.total);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
+  // each unit's last K block issues the next unit's first activation copies (see fp8_unit_tall)
+  uint32_t msgs = (uint32_t)uniform((int)lds_offset(&sm.b[TallCfg<ROWS>::kScOff + wv * 1024]));
+  int pfd = 0;
+  Unit u;
+  if (walk.first < walk.end) u = sched_unit<ROWS>(a, sc, walk.first);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
-    const Unit u = sched_unit<ROWS>(a, sc, v);
-    if (a.wpacked) fp8_unit_tall<ROWS, true, false>(a, u, sm, wv, lane);
-    else fp8_unit_tall<ROWS, false, false>(a, u, sm, wv, lane);
+    const int hasnext = v + walk.stride < walk.end;
+    const Unit nu = hasnext ? sched_unit<ROWS>(a, sc, v + walk.stride) : u;
+    if (a.wpacked) fp8_unit_tall<ROWS, true, false>(a, u, sm, wv, lane, nu, pfd, hasnext, msgs);
+    else fp8_unit_tall<ROWS, false, false>(a, u, sm, wv, lane, nu, pfd, hasnext, msgs);
+    u = nu;
+    pfd = hasnext;
   }
 }
 
@@ -456,8 +515,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_swiglu_tall_kernel(const Gemm
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
     const Unit u = sched_unit<ROWS>(a, sc, v);
-    if (a.wpacked) fp8_unit_tall<ROWS, true, true>(a, u, sm, wv, lane);
-    else fp8_unit_tall<ROWS, false, true>(a, u, sm, wv, lane);
+    uint32_t msgs = 0;  // (SwiGLU units start at group buffer 0)
+    if (a.wpacked) fp8_unit_tall<ROWS, true, true>(a, u, sm, wv, lane, u, 0, 0, msgs);
+    else fp8_unit_tall<ROWS, false, true>(a, u, sm, wv, lane, u, 0, 0, msgs);
   }
 }
 

@@ -90,9 +90,13 @@ GROUP = 4         # K blocks per row-scale copy (one 16-byte copy per row)
 
 class Cfg:
     def __init__(self, rows: int, S: int, name: str, dtype: str = "fp8", wnt: bool = False, dist: int = 2,
-                 swiglu: bool = False):
+                 swiglu: bool = False, xpf: bool = False):
         assert rows in (192, 256) and dtype in ("fp8", "bf16", "fp4") and not (swiglu and dtype != "fp8")
         self.swiglu = swiglu                      # epilogue: gate and up columns to LDS for SwiGLU (no stores)
+        # the last K block issues the next unit's activation and row-scale copies of its blocks 0 and 1 (ring slots
+        # 0 and 1, idle by then); the epilogue stages through slot 2 instead of slot 0
+        self.xpf = xpf
+        assert not xpf or (dtype == "fp8" and not swiglu and dist == 2)
         self.rows, self.S, self.name = rows, S, name
         self.wnt = wnt                            # weight loads nontemporal (each weight byte read by one unit)
         assert dist in (2, 3)
@@ -212,6 +216,32 @@ def issue_items(cfg, t, packed, rbe):
     return items, upd
 
 
+def prefetch_items(cfg, nb):
+    """The next unit's activation copies of its K block nb (0 or 1) into ring slot nb: all apw copies per wave
+    (rows past that unit's end repeat its last row); with block 0 also its first row-scale group into the group
+    buffer %[msg] points at, which then alternates as for the unit's own groups.
+
+    The copy offsets reuse %[ao*], idle once the unit's last block is issued: copy i of the next unit reads
+    row min(r_i, m - 1) (m its rows), chunk c, i.e. min(%[uo0] + 32 i K, (m - 1) K + c) with %[uo0] the
+    unclamped offset r_0 K + c (c, the lane's chunk, is the same for every copy), computed with two registers of
+    ring slot 0 (idle in the last K block until its epilogue uses it) before the first copy.  For block 1 each
+    offset first advances by 128 bytes: an instruction offset would move the copy's LDS destination as well."""
+    T, U = cfg.wbase, cfg.wbase + 1
+    items = [([f"v_add_u32_e32 %[ao{i}], 128, %[ao{i}]"] if nb else [])
+             + [f"s_add_u32 m0, %[ma], {nb * cfg.slot + i * 4096}", "s_nop 0",
+                f"global_load_lds_dwordx4 %[ao{i}], %[nab]"] for i in range(cfg.apw)]
+    if nb == 0:
+        # (%[t] = 32 K, free in the last K block)
+        setup = ["s_lshl_b32 %[t], %[kb], 12", f"v_add_u32_e32 v{T}, %[nlim], %[cc]", f"v_mov_b32_e32 v{U}, %[uo0]"]
+        for i in range(cfg.apw):
+            setup += [f"v_min_u32_e32 %[ao{i}], v{U}, v{T}"] + ([f"v_add_u32_e32 v{U}, %[t], v{U}"]
+                                                               if i + 1 < cfg.apw else [])
+        items[0] = setup + items[0]
+        items.append(["s_mov_b32 m0, %[msg]", "s_nop 0", "global_load_lds_dwordx4 %[nso], %[nsb]",
+                      f"s_xor_b32 %[msg], %[msg], {SCALE_ROWS * 16}"])
+    return items
+
+
 def weight_exponents(cfg, s):
     """The weight scale exponents of ring slot s: the fp32 scale's bit pattern shifted right by 23 (FP8), or
     (fp4) each K half's scale dword shifted right by 8 (l32 / 16) bytes, so that byte 2 ct is the scale of the
@@ -280,7 +310,7 @@ def compute(cfg, s, t, packed, rbe, final=False, first=False):
         return compute_last(cfg, s, rbe)
     items, upd = issue_items(cfg, t, packed, rbe)
     if final and s > cfg.S - 1 - cfg.dist:  # its block would be past the last one
-        items, upd = [], []
+        items, upd = (prefetch_items(cfg, 0) if cfg.xpf and s == cfg.S - 2 else []), []
     nslots = 4 * rbe
     place = [[] for _ in range(nslots)]  # matrix-instruction slot -> the items issued right after it
     for i, it in enumerate(items):
@@ -308,7 +338,7 @@ def compute(cfg, s, t, packed, rbe, final=False, first=False):
                                                [f"v_lshrrev_b32_e32 v{cfg.v_sae + bn}, 23, v{cfg.v_sae + bn}"])
             if j + 2 == rbe and not (final and s == cfg.S - 1):  # row tile j + 1 is the last one
                 issued = sum(len(place[i]) for i in range(4 * (j + 1)))
-                wait = 0 if final and s == cfg.S - 2 else cfg.wait_at(s, issued, cfg.ops_for(rbe))
+                wait = issued if final and s == cfg.S - 2 else cfg.wait_at(s, issued, cfg.ops_for(rbe))
                 out += publish(cfg, s, wait)
     out += upd
     return out
@@ -401,11 +431,14 @@ def compute_last(cfg, s, rbe):
     out = (["s_waitcnt lgkmcnt(0)"] if cfg.bf16 else
            weight_exponents(cfg, s) + ["s_waitcnt lgkmcnt(0)",
                                        f"v_lshrrev_b32_e32 v{cfg.v_sae + 2}, 23, v{cfg.v_sae + 2}"])
+    pf = prefetch_items(cfg, 1) if cfg.xpf else []  # the next unit's block 1 copies, one per matrix instruction
     for j in range(rbe):
         b = cfg.bufid(j)
         nxt = j + 1 < rbe
         bn = cfg.bufid(j + 1)
         place = [[] for _ in range(4)]
+        for q in range(4):
+            place[q] += [ins for it in pf[4 * j + q:4 * j + q + 1] for ins in it]
         if nxt:
             if j >= 2:  # row tile j - 2's 12 staging operations may be in flight
                 place[0].append("s_waitcnt lgkmcnt(10)")
@@ -487,12 +520,21 @@ def epilogue(cfg, rbe):
 
 def prologue(cfg, packed, rbe):
     """The loads of K blocks 0 .. dist - 1, then block 0 in place (the later ones may still be in flight) and
-    its row tile 0 read into fragment buffer 2."""
+    its row tile 0 read into fragment buffer 2.
+
+    xpf: when bit 0 of %[fl] is set, the previous unit has issued all of this unit's loads of blocks 0 and 1 (its last K
+    block the activation copies and the first row-scale group, its end the weights and weight scales into ring
+    slots 0 and 1; the offsets already point past them): only the wait for block 0 remains."""
     out = ["s_mov_b32 %[q], 0"]
     for t in range(cfg.dist):
         items, upd = issue_items(cfg, t, packed, rbe)
         out += [ins for it in items for ins in it] + upd
-    out += [f"s_waitcnt vmcnt({(cfg.dist - 1) * cfg.ops_for(rbe)})", "s_barrier"] + frag_reads(cfg, 0, 2, 0) + (
+    out += [f"s_waitcnt vmcnt({(cfg.dist - 1) * cfg.ops_for(rbe)})"]
+    if cfg.xpf:  # (block 1's weights and weight scale may still be in flight)
+        pre = ["s_bitcmp1_b32 %[fl], 0", f"s_cbranch_scc0 {800 + rbe}f", f"s_mov_b32 %[q], {cfg.dist}",
+               f"s_waitcnt vmcnt({cfg.ops_for(0)})", f"s_branch {850 + rbe}f", f"{800 + rbe}:"]
+        out = pre + out + [f"{850 + rbe}:"]
+    out += ["s_barrier"] + frag_reads(cfg, 0, 2, 0) + (
         [] if cfg.bf16 else [f"ds_read_b32 v{cfg.v_sae + 2}, v{cfg.v_sadr}"])
     return out
 
@@ -518,7 +560,29 @@ def program(cfg, packed):
     for r in range(cfg.rt, 1, -1):
         out += epilogue(cfg, r)
     out += ["7:", "s_barrier"]
+    if cfg.xpf:
+        out += next_unit_weights(cfg, packed)
     return out
+
+
+def next_unit_weights(cfg, packed):
+    """After the unit's final barrier (no wave uses the ring registers any more): the next unit's weights and
+    weight scales of K blocks 0 and 1 into ring slots 0 and 1, left in flight for the next unit's loop (the
+    code between two loops references none of the loop's registers; a build test checks the compiled kernel).
+    The last unit of the workgroup (bit 1 of %[fl] clear) instead waits until nothing is in flight, LDS copies
+    included."""
+    out = ["s_bitcmp1_b32 %[fl], 1", "s_cbranch_scc0 8f"]
+    for t in range(2):
+        items, _ = issue_items(cfg, t, packed, 0)
+        for it in items:
+            for ins in it:
+                if ins.startswith("global_load_dwordx4 v["):
+                    out.append(ins.replace("%[wo", "%[nwo").replace("%[wb]", "%[nwb]"))
+                elif ins.startswith("global_load_dword v"):
+                    out.append(ins.replace("%[wso], %[swb]", "%[nwso], %[nswb]") + (" offset:4" if t else ""))
+        if t == 0:
+            out += [f"v_add_u32_e32 %[nwo{ct}], %[wstep], %[nwo{ct}]" for ct in range(2)]
+    return out + ["s_branch 9f", "8:", "s_waitcnt vmcnt(0)", "9:"]
 
 
 def clobbers(cfg):
@@ -529,7 +593,7 @@ def clobbers(cfg):
 
 # The 192-row tiles serve experts of about one chunk (each weight byte read by one unit): their weight loads are
 # nontemporal.  The 256-row tiles serve experts of many chunks, whose units re-read the weights from L2.
-CONFIGS = [Cfg(192, 4, "TALL192", wnt=True), Cfg(256, 4, "TALL256"),
+CONFIGS = [Cfg(192, 4, "TALL192", wnt=True, xpf=True), Cfg(256, 4, "TALL256", xpf=True),
            Cfg(192, 4, "SWIGLU_TALL192", wnt=True, swiglu=True), Cfg(256, 4, "SWIGLU_TALL256", swiglu=True),
            Cfg(192, 4, "BF16_TALL192", "bf16", wnt=True), Cfg(256, 4, "BF16_TALL256", "bf16"),
            Cfg(192, 4, "FP4_TALL192", "fp4", wnt=True), Cfg(256, 4, "FP4_TALL256", "fp4")]
@@ -548,6 +612,7 @@ def main():
                     f"#define MOE_{n}_APW {cfg.apw}\n#define MOE_{n}_S {cfg.S}\n")
             f.write(f"#define MOE_{n}_AO_OUTS " + ", ".join(f'[ao{i}] "+v"(ao[{i}])' for i in range(cfg.apw))
                     + "\n")
+
             for suffix, packed in ((("_PACKED", True),) if cfg.fp4 else (("", False), ("_PACKED", True))):
                 f.write(f"#define MOE_{n}_LOOP{suffix} \\\n")
                 for ln in program(cfg, packed):

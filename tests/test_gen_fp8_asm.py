@@ -79,10 +79,11 @@ def _reads_writes(line):
     return set().union(set(), *map(_regs, ops[1:])), _regs(ops[0])
 
 
-def _walk(prog, rbe, kb):
+def _walk(prog, rbe, kb, pfd=False, hasnext=True, inflight=()):
     """Follow the generated control flow for one unit (row-tile count rbe, kb K blocks) and count what it
     executes: barriers, matrix instructions, vector-memory loads and stores.  Scalar tests are evaluated for
-    the three conditions the text branches on (the row-tile dispatch, kb <= 4, the loop back-edge).
+    the conditions the text branches on (the row-tile dispatch, kb <= 4, the loop back-edge; with the cross-unit
+    prefetch, whether this unit's first copies were issued by the previous unit and whether a next unit follows).
 
     Along the way it models this wave's own counters with nothing completing before it is waited for: an
     instruction that reads or overwrites a register still targeted by a pending LDS read or vector-memory load
@@ -100,6 +101,7 @@ def _walk(prog, rbe, kb):
     pc, scc, ks = 0, False, None
     counts = {"barrier": 0, "mfma": 0, "load": 0, "store": 0, "lds_max": 0}
     lgkm, vm = [], []   # pending LDS / vector-memory operations: the registers each will write
+    vm += [set(r) for r in inflight]  # loads the previous unit left in flight (pfd)
     ws = 0              # wait states so far
     mfma_w, valu_w = {}, {}
     for _ in range(10_000_000):
@@ -155,6 +157,10 @@ def _walk(prog, rbe, kb):
             scc = ks < kb
         if line == "s_cmp_eq_u32 %[won], 0":
             scc = False  # a wave with columns
+        if line == "s_bitcmp1_b32 %[fl], 0":
+            scc = pfd
+        if line == "s_bitcmp1_b32 %[fl], 1":
+            scc = hasnext
         m = re.fullmatch(r"s_cbranch_scc([01]) (\d+[fb])", line)
         if m:
             if scc == (m.group(1) == "1"):
@@ -180,13 +186,26 @@ def test_each_unit_path_runs_its_blocks_once(gen, kb):
         for packed in _orders(cfg):
             prog = gen.program(cfg, packed)
             for rbe in range(2, cfg.rt + 1):
-                c = _walk(prog, rbe, kb)
-                assert c["mfma"] == (8 if cfg.bf16 else 4) * rbe * kb, (cfg.name, rbe, kb, c)
-                assert c["barrier"] == 1 + (kb - 1) + 1 + cfg.swiglu, (cfg.name, rbe, kb, c)
-                groups = 0 if cfg.bf16 else kb // gen.GROUP
-                assert c["load"] == kb * cfg.ops_for(rbe) + groups, (cfg.name, rbe, kb, c)
-                assert c["store"] == (0 if cfg.swiglu else 4 * rbe), (cfg.name, rbe, kb, c)
-                assert c["lds_max"] <= 15, (cfg.name, rbe, kb, c)
+                for pfd, hasnext in ((False, True), (True, True), (True, False), (False, False)):
+                    if not cfg.xpf and (pfd or not hasnext):
+                        continue
+                    inflight = []
+                    if pfd:  # the previous unit's end: this unit's first weights and weight scales, in order
+                        for ln in gen.next_unit_weights(cfg, packed):
+                            if ln.startswith("global_load"):
+                                inflight.append(_reads_writes(ln)[1])
+                    c = _walk(prog, rbe, kb, pfd, hasnext, inflight)
+                    assert c["mfma"] == (8 if cfg.bf16 else 4) * rbe * kb, (cfg.name, rbe, kb, c)
+                    assert c["barrier"] == 1 + (kb - 1) + 1 + cfg.swiglu, (cfg.name, rbe, kb, c)
+                    groups = 0 if cfg.bf16 else kb // gen.GROUP
+                    loads = kb * cfg.ops_for(rbe) + groups
+                    if cfg.xpf:  # the next unit's copies of its blocks 0 and 1 and its first row-scale group, and
+                        # (hasnext) its weights and weight scales of those blocks; none of this unit's own loads of
+                        # blocks 0 and 1 when the previous unit issued them (pfd)
+                        loads += 2 * cfg.apw + 1 + (18 if hasnext else 0) - (2 * cfg.ops_for(rbe) + 1 if pfd else 0)
+                    assert c["load"] == loads, (cfg.name, rbe, kb, pfd, c)
+                    assert c["store"] == (0 if cfg.swiglu else 4 * rbe), (cfg.name, rbe, kb, c)
+                    assert c["lds_max"] <= 15, (cfg.name, rbe, kb, c)
 
 
 def test_register_regions_do_not_overlap(gen):
@@ -278,3 +297,45 @@ def test_swiglu_staging_puts_each_value_where_the_rows_are_read(gen, rows):
                 assert (kind, f) == (("gate", 64 * w + col) if w < 2 else ("up", 64 * (w - 2) + col)), (a, v)
             # the C++ reads rows 0 .. 32 rbe - 1, all 32 chunks each
             assert {a // 512 for a in seen} == set(range(32 * rbe))
+
+
+def test_code_between_two_loops_leaves_their_registers_alone(gen, tmp_path):
+    """The plain tall loops end with the next unit's first weights and weight scales still in flight into the
+    loop's registers (ring slots 0 and 1 and the weight-scale ring), and the next loop reads them: so the
+    compiled kernel must not reference any of the loop's registers (v[v_alo] .. v255) outside its inline
+    assembly.  Compiles gemm_fp8.hip for gfx950 to assembly text (no GPU needed) and scans every instruction
+    of the plain tall kernels that the compiler wrote."""
+    import subprocess
+    import sys
+    sys.path.insert(0, os.path.join(HERE, ".."))
+    from int4_weights_amd import build as B
+    gen.main.__globals__["sys"].argv = ["gen", os.path.join(B.CSRC, "gemm_fp8_tall_loop.inc")]
+    gen.main()
+    out = str(tmp_path / "gemm_fp8.s")
+    r = subprocess.run([B.hipcc(), *B.flags(), "-S", "--cuda-device-only", os.path.join(B.CSRC, "gemm_fp8.hip"),
+                        "-o", out], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    text = open(out).read().split("\n")
+    cfgs = {int(c.rows): c for c in gen.CONFIGS if c.xpf}
+    assert set(cfgs) == {192, 256}
+    for rows, cfg in cfgs.items():
+        name = f"_ZN3moe20gemm_fp8_tall_kernelILi{rows}EEEvNS_8GemmArgsE"
+        start = next(i for i, ln in enumerate(text) if ln.startswith(name + ":"))
+        end = next(i for i in range(start, len(text)) if text[i].startswith(f"\t.size\t{name},"))
+        in_asm, seen = False, 0
+        for ln in text[start:end + 1]:
+            if ";;#ASMSTART" in ln:
+                in_asm = True
+                continue
+            if ";;#ASMEND" in ln:
+                in_asm = False
+                continue
+            code = ln.split(";")[0]
+            if in_asm or not code.strip() or code.strip().startswith("."):
+                continue
+            seen += 1
+            for m in re.finditer(r"\bv(\d+)\b", code):
+                assert int(m.group(1)) < cfg.v_alo, (rows, ln)
+            for m in re.finditer(r"\bv\[(\d+):(\d+)\]", code):
+                assert int(m.group(2)) < cfg.v_alo, (rows, ln)
+        assert seen > 100  # the kernel's own code was scanned
