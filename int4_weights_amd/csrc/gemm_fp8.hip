@@ -336,7 +336,11 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
 template <int ROWS>
 __device__ __forceinline__ void swiglu_unit_rows(const GemmArgs& a, const Fp8TallSmem<ROWS>& sm, int row0,
                                                  int mrows, int nt, int rbe) {
-  const int I = a.N / 2, ib = I / 128, lane = lane_id(), sub = lane & 15, wv = uniform(threadIdx.x >> 6);
+  // (the lane id through a volatile statement: nothing of this pass is hoisted out of the unit loop to stay live
+  // across the loop's assembly, where the compiler has few registers)
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int I = a.N / 2, ib = I / 128, sub = lane & 15, wv = uniform(threadIdx.x >> 6);
 #pragma unroll 2
   for (int m0 = 0; m0 < 32 * rbe; m0 += 16) {  // (2 rbe iterations; two rows' chains interleave: 4 was slower)
     const int m = m0 + 4 * wv + (lane >> 4), sw = m & 31;
