@@ -174,9 +174,9 @@ def test_pack_weight_fp8_bit_exact():
 
 
 def _int_codes(rng, shape, lo=-4, hi=4):
-    code_of = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48}
+    code_of = np.array([0x00, 0x38, 0x40, 0x44, 0x48], np.uint8)  # E4M3 codes of 0 .. 4
     v = rng.integers(lo, hi + 1, size=shape)
-    codes = np.vectorize(lambda t: code_of[abs(int(t))] | (0x80 if t < 0 else 0))(v).astype(np.uint8)
+    codes = code_of[np.abs(v)] | np.where(v < 0, 0x80, 0).astype(np.uint8)
     return v, codes
 
 
@@ -199,6 +199,35 @@ def test_fp8_small_integers_bit_exact():
             s, n = int(starts[e]), int(counts[e])
             exact = av[s:s + n] @ wv[e].T
             assert np.array_equal(u16(D)[s:s + n], oracle.f64_to_bf16_bits(exact.astype(np.float64)))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_fp8_tall_units_in_sequence_bit_exact(packed):
+    """Several tall units per workgroup (each unit issues the next one's first K blocks before it ends), of
+    every row-tile count in a row and with idle waves (N = 384), on small-integer codes with power-of-two scales
+    (every sum exact): each output must equal the integer product rounded to bf16."""
+    require_gpu()
+    rng = np.random.default_rng(8)
+    E, N, K = 128, 896, 512
+    counts = rng.integers(1, 520, size=E).astype(np.int32)
+    starts, rows, _ = _layout_rows(counts, moe.LAYOUT_CONTIGUOUS)
+    av, a = _int_codes(rng, (rows, K), -2, 2)
+    wv, w = _int_codes(rng, (E, N, K), -2, 2)
+    sa = np.exp2(rng.integers(-2, 2, size=(rows, K // 128))).astype(np.float32)
+    sw = np.exp2(rng.integers(-2, 1, size=(E, N // 128, K // 128))).astype(np.float32)
+    c = dict(E=E, N=N, K=K, rows=rows, starts=starts, eff=counts, counts=counts, layout=moe.LAYOUT_CONTIGUOUS,
+             max_m=0, a=a, sfa=sa, w=w, sfw=sw)
+    ref = np.zeros((rows, N), np.uint16)
+    for e in range(E):
+        s0, n = int(starts[e]), int(counts[e])
+        av_e = (av[s0:s0 + n].reshape(n, K // 128, 128) * sa[s0:s0 + n, :, None]).reshape(n, K)
+        wv_e = (wv[e].reshape(N, K // 128, 128) * np.repeat(sw[e], 128, axis=0)[:, :, None]).reshape(N, K)
+        ref[s0:s0 + n] = oracle.f64_to_bf16_bits_normal(av_e.astype(np.float64) @ wv_e.astype(np.float64).T)
+    for em in (128, 256):  # 192- and 256-row units: about 2 per workgroup
+        D = u16(_run_fp8(c, em, packed=packed))
+        for e in range(E):
+            s0, n = int(starts[e]), int(counts[e])
+            assert np.array_equal(D[s0:s0 + n], ref[s0:s0 + n]), (em, e)
 
 
 def test_fp8_scale_invariance_bit_exact():
