@@ -204,8 +204,9 @@ def test_fp8_small_integers_bit_exact():
 @pytest.mark.parametrize("packed", [False, True])
 def test_fp8_tall_units_in_sequence_bit_exact(packed):
     """Several tall units per workgroup (each unit issues the next one's first K blocks before it ends), of
-    every row-tile count in a row and with idle waves (N = 384), on small-integer codes with power-of-two scales
-    (every sum exact): each output must equal the integer product rounded to bf16."""
+    every row-tile count in a row and with idle waves (N = 896: the last column tile has 128), on small-integer
+    codes with power-of-two scales (every sum exact): each output must equal the integer product rounded to
+    bf16."""
     require_gpu()
     rng = np.random.default_rng(8)
     E, N, K = 128, 896, 512
