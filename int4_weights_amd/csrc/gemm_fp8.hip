@@ -246,10 +246,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_fp8_kernel(const GemmArgs a) 
 //    instruction, exact vmcnt waits, a unit computes max(2, ceil(rows/32))
 //    row tiles (the surplus rows repeat the last valid row and are never
 //    stored), and v_cvt_pk_bf16_f32 (round to nearest even).  The epilogue
-//    runs inside the last K block, which issues no loads: while row tile j is
-//    multiplied, row tile j - 1 is converted and staged through the wave's
-//    4 KB of the idle ring slot 0 and row tile j - 2 is stored as whole
-//    128-byte rows; only the last row tile is stored after the loop.
+//    runs inside the last K block, which issues none of the unit's own
+//    loads: while row tile j is multiplied, row tile j - 1 is converted and
+//    staged through the wave's 4 KB of the idle ring slot 2 and row tile
+//    j - 2 is stored as whole 128-byte rows; only the last row tile is stored
+//    after the loop.  Meanwhile the next unit's first two K blocks are issued
+//    (see fp8_unit_tall).
 //  * The 192-row tile's weight loads are nontemporal: it serves experts of
 //    about one chunk, whose weight bytes are read by one unit each (2-4%
 //    faster on DeepSeek-V3-shaped prefill); the 256-row tile's are not,
@@ -432,12 +434,11 @@ __device__ __forceinline__ void fp8_unit_tall(const GemmArgs& a, const Unit& u, 
   uint32_t msg = SWIGLU ? msg0 : (uint32_t)uniform((int)msgs);
   const uint32_t sbuf = (pfd ? msg ^ 4096u : msg) - msg0;
   const uint32_t sadr = abase + kScOff + 16 * l32 + sbuf;  // row scale of row tile j, block s: +512 j + 4 s
-  // epilogue: one 32-row tile of the wave's bf16 rows at a time goes through its own 4 KB of ring slot 0
-  // (row m at m*128, 16-byte chunk c at position c ^ (m & 7)); each lane writes 8 bytes of row l32 (epb:
-  // chunk 0's address, including the lane's half) and reads back 16 bytes (chunk lane & 7) of row lane >> 3
-  // of every 8-row group, stored as whole 128-byte rows
+  // epilogue: one 32-row tile of the wave's bf16 rows at a time goes through its own 4 KB of ring slot 2
+  // (slots 0 and 1 receive the next unit's copies meanwhile; row m at m*128, 16-byte chunk c at position
+  // c ^ (m & 7)); each lane writes 8 bytes of row l32 (epb: chunk 0's address, including the lane's half) and
+  // reads back 16 bytes (chunk lane & 7) of row lane >> 3 of every 8-row group, stored as whole 128-byte rows
   // (SwiGLU: epb is this lane's 8 bytes of chunk 8 wv of row l32 of the staged bf16 rows, see swiglu_unit_rows)
-  // (plain units stage through ring slot 2: slots 0 and 1 receive the next unit's copies meanwhile)
   const uint32_t stg = abase + (SWIGLU ? 0u : 2u * kSlot);
   const uint32_t epb = SWIGLU ? abase + (uint32_t)(l32 * 512 + 16 * ((8 * wv) ^ l32) + 8 * hh)
                               : stg + (uint32_t)(wv * 4096 + l32 * 128 + 16 * (l32 & 7) + 8 * hh);

@@ -54,11 +54,14 @@ tile left the matrix pipe idle; the branch-free bodies are 4-9% faster).  The
 loop's last iteration is emitted apart (it issues only block kb - 1 and waits
 for fewer loads), so the main loop's only branch is its back-edge, and a
 unit's first step is emitted apart too: its matrix instructions add to 0, so
-the accumulators are never zeroed.  The unit's last K block issues no loads
-and leaves ring slots 0 .. 2 idle, so the epilogue runs inside it: while row
-tile j is multiplied, row tile j - 1 is converted to bf16 and staged through
-the wave's 4 KB of LDS slot 0, and row tile j - 2 is stored as whole 128-byte
-rows; after the loop only the last row tile remains.
+the accumulators are never zeroed.  The unit's last K block issues none of the
+unit's own loads and leaves ring slots 0 .. 2 idle, so the epilogue runs inside
+it: while row tile j is multiplied, row tile j - 1 is converted to bf16 and
+staged through the wave's 4 KB of LDS slot 0 (slot 2 with the cross-unit
+pipeline, xpf, whose last two steps issue the next unit's copies of its blocks
+0 and 1 into slots 0 and 1, and whose loop ends by issuing that unit's weights
+of those blocks), and row tile j - 2 is stored as whole 128-byte rows; after the
+loop only the last row tile remains.
 
 Register map (physical, listed as clobbers of the asm statement):
   a[0:rows-1] accumulators (row tile j, column tile ct at a[32j + 16ct]);
@@ -138,7 +141,7 @@ class Cfg:
         self.v_pk = self.wbase + 64
         self.v_ep = self.wbase + 80
         assert self.v_ep + 8 <= self.wbase + 32 * (S - 1)
-        # each wave stages one 32-row tile of bf16 (32 x 128 bytes) in its 4 KB of ring slot 0
+        # each wave stages one 32-row tile of bf16 (32 x 128 bytes) in its 4 KB of ring slot 0 (xpf: slot 2)
         assert 4 * 4096 <= self.slot
 
     def acc(self, j, ct):
@@ -421,9 +424,10 @@ def ep_store_masked(cfg, j):
 def compute_last(cfg, s, rbe):
     """The unit's last K block (ring slot s = S - 1 of the final iteration), with the epilogue folded in.
 
-    No loads are issued and no block is published, so the load path and ring slots 0 .. 2 are idle: while row
+    None of the unit's own loads are issued and no block is published, so ring slots 0 .. 2 are idle: while row
     tile j is multiplied, row tile j - 1 (final since the previous row tile's matrix instructions) is
-    converted to bf16 and staged through the wave's 4 KB of slot 0, and row tile j - 2, read back in the
+    converted to bf16 and staged through the wave's 4 KB of slot 0 (xpf: slot 2, the next unit's block 1
+    copies being issued meanwhile), and row tile j - 2, read back in the
     previous row tile, is stored as whole 128-byte rows.  All rows of the row tiles stored here are valid
     (only the last row tile, and row tile 0 of a two-tile unit, can be partial; both are stored by the
     epilogue after the loop).  Row tile j + 1's fragments are read after row tile j's first matrix
