@@ -58,6 +58,9 @@ from .quant import (
     pow2_exponent_e2m1,
     quant_weight_fp4,
     dequant_weight_fp4,
+    INT8_MAX,
+    quant_int8,
+    dequant_int8,
 )
 from .routing import (
     DEV_ID_RANGE,
@@ -66,7 +69,8 @@ from .routing import (
     route,
     pack_rows,
 )
-from .gemm import grouped_gemm_bf16, grouped_gemm_fp8, grouped_gemm_fp8_fp4, grouped_gemm_int4, segments
+from .gemm import (grouped_gemm_bf16, grouped_gemm_fp8, grouped_gemm_fp8_fp4, grouped_gemm_int4, grouped_gemm_int8,
+                   segments)
 from .combine import combine, combine_fp32, f32_to_bf16_bits
 from .activation import quant_act_values, silu, swiglu, swiglu_quant
 from .metrics import calc_diff, elementwise_ok, elementwise_excess
@@ -83,4 +87,5 @@ __all__ = [
     "quant_weight_fp4", "dequant_weight_fp4", "combine", "combine_fp32", "f32_to_bf16_bits",
     "calc_diff", "elementwise_ok", "elementwise_excess",
     "silu", "swiglu", "quant_act_values", "swiglu_quant",
+    "INT8_MAX", "quant_int8", "dequant_int8", "grouped_gemm_int8",
 ]

@@ -20,6 +20,10 @@ FP8 x FP4 ([AsymGEMM] "API Reference", FP4 grouped GEMMs; [CuTeDSL] MXFP4 block 
 [DG-FP8] "精度与吞吐的平衡点": one FP4 side is held to calc_diff < 0.01):
     D[p, n] = sum_k (dec8(a[p,k]) * sa[p, k/128]) * (dec4(w[e,n,k]) * 2^(sw[e,n,k/32] - 127)).
 
+INT8 ([AsymGEMM] "API Reference", INT8 m_grouped contiguous / masked with the (1, 1, 128) recipe):
+    D[p, n] = sum_k (a[p,k] * sa[p, k/128]) * (w[e,n,k] * sw[e, n, k/128])   with int8 codes.
+Each 128-block's integer sum is exact, and so is every product with the two fp32 scales in float64.
+
 BF16 ([AsymGEMM] "API Reference", BF16 m_grouped contiguous / masked; [GEMM-modes]
 sec. 4.6, the BF16 contiguous grouped GEMM SGLang calls):
     D[p, n] = sum_k a[p,k] * w[e,n,k]   with bf16 operands, in float64.
@@ -33,7 +37,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import bf16_bits_to_f64
-from .quant import dequant_act, dequant_weight_fp4, dequant_weight_fp8, dequant_weight_int4
+from .quant import dequant_act, dequant_int8, dequant_weight_fp4, dequant_weight_fp8, dequant_weight_int4
 
 
 def segments(counts, seg_offsets):
@@ -147,4 +151,28 @@ def grouped_gemm_int4(a_bits, w_q4, s16_bits, counts, seg_offsets, rows_out=None
         a = bf16_bits_to_f64(a_bits[p0:p0 + c])
         w = dequant_weight_int4(w_q4[wi], s16_bits[wi])
         out[p0:p0 + c] = a @ w.T
+    return out
+
+
+def grouped_gemm_int8(a_q, sa, w_q, sw, counts, seg_offsets, rows_out=None, experts=None):
+    """INT8 (1, 1, 128) grouped GEMM in float64.
+
+    a_q int8 [rows, K], sa float32 [rows, K/128]; w_q int8 [E, N, K], sw float32 [E, N, K/128];
+    segments and ``experts`` as for grouped_gemm_fp8.  Returns float64 [rows_out, N] (NaN outside valid rows).
+
+    Pinned by: exact rational brute force on tiny shapes, integer codes with unit scales against an integer
+    matmul, per-row and per-channel scale factoring, per-expert single-GEMM equivalence, a swapped-scale
+    mistake caught.
+    """
+    rows = a_q.shape[0] if rows_out is None else rows_out
+    N = w_q.shape[-2]
+    out = np.full((rows, N), np.nan, dtype=np.float64)
+    sel = range(len(counts)) if experts is None else list(experts)
+    for j, e in enumerate(sel):
+        c = int(counts[e])
+        if c <= 0:
+            continue
+        wi = e if experts is None else j
+        p0 = int(seg_offsets[e])
+        out[p0:p0 + c] = dequant_int8(a_q[p0:p0 + c], sa[p0:p0 + c]) @ dequant_int8(w_q[wi], sw[wi]).T
     return out

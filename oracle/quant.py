@@ -216,3 +216,39 @@ def dequant_weight_fp4(w4: np.ndarray, sw: np.ndarray) -> np.ndarray:
     """float64 [..., N, K] = decode(code) * 2^(sw - 127) of the code's 32-block."""
     codes = unpack_int4(w4)
     return e2m1_decode_table()[codes] * np.repeat(e8m0_value(sw), FP4_BLOCK, axis=-1)
+
+
+# ------------------------------------------------------------------------------------------ INT8 (1, 1, 128) --
+INT8_MAX = 127
+
+
+def quant_int8(x_bits: np.ndarray):
+    """INT8 (1, 1, 128) block quantisation ([AsymGEMM] "API Reference", INT8 asymmetric GEMM: (int8 data, fp32
+    scale) pairs with one scale per row and 128-element block along K, per token for activations and per output
+    channel for weights).  The page gives no rule for choosing the scale; reading taken: symmetric,
+    s = fp32(amax) / 127 (fp32 division, round to nearest), and q = clip(rne(x / s), -127, 127) with the
+    division in fp32 (it decides an integer code, and the GPU kernel decides it in fp32); amax == 0 gives s = 1
+    and q = 0.
+
+    x_bits: uint16 [..., K] bf16 patterns (rows: tokens, or the N rows of each expert's weight).
+    Returns (q int8 [..., K], s float32 [..., K/128]).
+    Pinned by: an exact rational evaluation of every step (fp32 rounding written out from its definition) on
+    random and edge blocks; |q| <= 127 with the block's largest magnitude at +-127; the error bound
+    |x - q s| <= s / 2 (plus the fp32 rounding of x / s); sign symmetry; 2^j x giving the same codes and
+    scales 2^j s.
+    """
+    x32 = bf16_bits_to_f64(x_bits).astype(np.float32)  # exact
+    K = x32.shape[-1]
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    xb = x32.reshape(x32.shape[:-1] + (K // BLOCK, BLOCK))
+    amax = np.abs(xb).max(axis=-1)
+    s = np.where(amax > 0, amax / np.float32(INT8_MAX), np.float32(1.0)).astype(np.float32)
+    q = np.rint(xb / s[..., None]).astype(np.float32)  # fp32 division, ties to even
+    q = np.clip(q, -INT8_MAX, INT8_MAX).astype(np.int8)
+    return q.reshape(x32.shape), s
+
+
+def dequant_int8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """float64 [..., K] = q * s of the value's 128-block."""
+    return np.asarray(q, dtype=np.float64) * np.repeat(np.asarray(s, dtype=np.float64), BLOCK, axis=-1)
