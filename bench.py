@@ -39,6 +39,7 @@ METRIC = "grouped-GEMM FP8 TFLOPS (prefill) & HBM GB/s (decode), % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (TOP/s)
 WORKLOADS = ["tiny", "dsv3_prefill", "dsv3_decode", "qwen3_skewed", "int4_decode"]
 
 
@@ -50,8 +51,8 @@ def parse():
     ap.add_argument("--config", default="dsv3_prefill", choices=WORKLOADS)
     ap.add_argument("--also", default="qwen3_skewed,dsv3_decode,int4_decode",
                     help="further workloads timed in the same run (comma-separated, or 'none')")
-    ap.add_argument("--variants", default="fp4_dsv3_decode,fp4_dsv3_prefill,bf16_dsv3_decode,bf16_dsv3_prefill",
-                    help="weight-format variants timed in the same run: <fp4|bf16>_<workload> (or 'none')")
+    ap.add_argument("--variants", default="fp4_dsv3_decode,fp4_dsv3_prefill,int8_dsv3_decode,int8_dsv3_prefill,bf16_dsv3_decode,bf16_dsv3_prefill",
+                    help="weight-format variants timed in the same run: <fp4|int8|bf16>_<workload> (or 'none')")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-experts", type=int, default=128, help="experts in the timed oracle sample")
     ap.add_argument("--ceiling", choices=["on", "off"], default="on",
@@ -92,6 +93,8 @@ KERNEL_SOURCES = {
                               "build.py"],
     "moe_grouped_gemm_fp8_fp4": ["csrc/gemm_fp4.hip", "csrc/gemm_common.h", "csrc/moe_device.h",
                                  "csrc/moe_internal.h", "build.py"],
+    "moe_grouped_gemm_int8": ["csrc/gemm_int8.hip", "csrc/gemm_common.h", "csrc/moe_device.h", "csrc/moe_internal.h",
+                              "build.py"],
     "moe_grouped_gemm_bf16": ["csrc/gemm_bf16.hip", "csrc/gemm_common.h", "csrc/moe_device.h", "csrc/moe_internal.h",
                               "csrc/gen_fp8_asm.py", "build.py"],
 }
@@ -348,6 +351,7 @@ def build_workload(args, cfg, torch, np, moe, synth, want_cpu):
 def build_variant(args, fmt, cfg, torch, np, moe, synth):
     """The same routing and step as the FP8 workload, with the expert weights in another format:
     fp4 -- MXFP4 weights (E2M1 codes, one E8M0 scale per 32 K values) x FP8 activations;
+    int8 -- INT8 (1, 1, 128) activations and weights (per-row / per-channel fp32 scales per 128 K);
     bf16 -- bf16 weights x bf16 activations (the rows are packed as bf16, no quantisation)."""
     dev = "cuda"
     T, E, k, K, N = cfg.T, cfg.E, cfg.topk, cfg.K, cfg.N
@@ -397,6 +401,36 @@ def build_variant(args, fmt, cfg, torch, np, moe, synth):
             tm.mark(s, 3)
             moe.moe_unpermute_combine(D, oi, tw, Z)
             tm.mark(s, 4)
+    elif fmt == "int8":
+        # INT8 codes in moe_pack_weight_fp8's fragment order, per-channel scales K-block-major (prepared once)
+        W8 = torch.empty(E, N, K, dtype=torch.uint8, device=dev)
+        SW = torch.empty(E, K // 128, N, dtype=torch.float32, device=dev)
+        r8 = torch.empty(16, N, K, dtype=torch.int8, device=dev)
+        for e0 in range(0, E, 16):
+            ex = list(range(e0, min(E, e0 + 16)))
+            w = synth.expert_weights(cfg, N, K, experts=ex, stream=synth.STREAM_WEIGHTS, device=dev)
+            moe.moe_quant_weight_int8(w, r8[:len(ex)], SW[e0:e0 + len(ex)])
+            moe.moe_pack_weight_fp8(r8[:len(ex)].view(torch.uint8), W8[e0:e0 + len(ex)])
+            del w
+        del r8
+        q = torch.empty(T, K, dtype=torch.int8, device=dev)
+        sf = torch.empty(T, K // 128, dtype=torch.float32, device=dev)
+        P = torch.empty(rows_cap, K, dtype=torch.int8, device=dev)
+        Psf = torch.empty(rows_cap, K // 128, dtype=torch.float32, device=dev)
+        names = ["moe_quant_act_int8", "moe_route_pack", "gemm", "moe_unpermute_combine"]
+
+        def step(tm, s):
+            tm.mark(s, 0)
+            moe.moe_quant_act_int8(x, q, sf)
+            tm.mark(s, 1)
+            moe.moe_route_pack(ids, E, layout, am, q, P, counts, seg, mi, oi, st, payload2=sf, packed2=Psf,
+                               workspace=ws)
+            tm.mark(s, 2)
+            moe.moe_grouped_gemm_int8(layout | moe.WEIGHTS_PACKED, P, Psf, W8, SW, D, counts, seg, E, am_gemm, N, K,
+                                      em)
+            tm.mark(s, 3)
+            moe.moe_unpermute_combine(D, oi, tw, Z)
+            tm.mark(s, 4)
     else:
         # bf16 weights in the fragment-packed order (moe_pack_weight_bf16, prepared once)
         W = torch.empty(E, N, K, dtype=torch.bfloat16, device=dev)
@@ -437,6 +471,9 @@ def summarise_variant(np, wl, ms_step, per, host_ms):
     if fmt == "fp4":
         nbytes = active * N * (K // 2 + K // 32) + rows_valid * (K + 4 * K // 128) + rows_valid * N * 2
         peak_f, kernel = FP8_PEAK_TFLOPS, "moe_grouped_gemm_fp8_fp4"
+    elif fmt == "int8":
+        nbytes = active * N * K * (1 + 4 / 128) + rows_valid * (K + 4 * K // 128) + rows_valid * N * 2
+        peak_f, kernel = INT8_PEAK_TOPS, "moe_grouped_gemm_int8"
     else:
         nbytes = active * N * K * 2 + rows_valid * K * 2 + rows_valid * N * 2
         peak_f, kernel = BF16_PEAK_TFLOPS, "moe_grouped_gemm_bf16"
@@ -444,13 +481,14 @@ def summarise_variant(np, wl, ms_step, per, host_ms):
     if flops / nbytes < ridge:
         roof = {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": peak_f,
+                "unit": "TOP/s" if fmt == "int8" else "TFLOP/s"}
     roof.update(frac=roof["achieved"] / roof["peak"], tflops=flops / t / 1e12, hbm_gbs=nbytes / t / 1e9,
                 flops_per_launch=flops, bytes_per_launch=nbytes, kernel=kernel, avg_launch_ms=kern["gemm"]["mean"],
                 median_launch_ms=kern["gemm"]["median"], min_launch_ms=kern["gemm"]["min"],
                 traffic=measured_traffic(kernel, f"{fmt}_{cfg.name}"))
-    return {"ms_per_step": ms_step, "kernels_ms": kern, "roofline": roof, "dtype": "fp8xe2m1" if fmt == "fp4" else
-            "bf16", "config": {"workload": cfg.name, "weights": fmt, "T": cfg.T, "E": E, "topk": cfg.topk, "K": K,
+    return {"ms_per_step": ms_step, "kernels_ms": kern, "roofline": roof,
+            "dtype": {"fp4": "fp8xe2m1", "int8": "int8"}.get(fmt, "bf16"), "config": {"workload": cfg.name, "weights": fmt, "T": cfg.T, "E": E, "topk": cfg.topk, "K": K,
                                "N": N, "layout": cfg.layout, "rows_valid": rows_valid, "experts_active": active},
             "host_enqueue_ms_per_step": host_ms}
 
@@ -616,7 +654,7 @@ def run(args):
     variants = {}
     for v in ([] if args.variants in ("", "none") else args.variants.split(",")):
         fmt, _, name = v.partition("_")
-        if fmt not in ("fp4", "bf16") or name not in WORKLOADS or synth.config_by_name(name).weights != "fp8":
+        if fmt not in ("fp4", "int8", "bf16") or name not in WORKLOADS or synth.config_by_name(name).weights != "fp8":
             raise SystemExit(f"unknown variant {v}")
         t_setup = time.perf_counter()
         wl = build_variant(args, fmt, synth.config_by_name(name), torch, np, moe, synth)

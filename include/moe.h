@@ -10,13 +10,15 @@
  *   moe_grouped_gemm_int4  (weight-only variant) bf16 rows x 4-bit weights -> bf16
  *   moe_grouped_gemm_bf16  (BF16 variant) bf16 rows x bf16 expert weights -> bf16
  *   moe_grouped_gemm_fp8_fp4 (FP4 variant) FP8 rows x MXFP4 (E2M1 + E8M0) weights -> bf16
+ *   moe_grouped_gemm_int8  (INT8 variant) int8 rows x int8 weights, (1, 1, 128) fp32 scales -> bf16
  *   moe_swiglu_quant       (between up- and down-projection) silu(gate) * up -> FP8 + 1x128 scales
  *   moe_grouped_gemm_fp8_swiglu (up-projection with the step above in its epilogue) -> FP8 + 1x128 scales
  *   moe_unpermute_combine  topk_weights-weighted sum back to token order
  *
- * plus weight-preparation calls (moe_quant_weight_fp8 / _int4 / _fp4,
+ * plus weight-preparation calls (moe_quant_weight_fp8 / _int4 / _fp4 / _int8,
  * moe_pack_weight_fp8 / _int4 / _fp4 / _bf16) that turn bf16 expert weights
- * into the formats the GEMMs read.
+ * into the formats the GEMMs read, and moe_quant_act_int8 (the INT8 variant's
+ * activation codes).
  *
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers owned by the caller.  The library
@@ -68,9 +70,10 @@ enum {
 enum { MOE_LAYOUT_CONTIGUOUS = 0, MOE_LAYOUT_MASKED = 1 };
 
 /* Flag ORed into the layout argument of moe_grouped_gemm_fp8 (and _int4,
- * _fp8_fp4, _bf16): the weights are in the fragment-packed order written by
- * moe_pack_weight_fp8 (moe_pack_weight_int4, _fp4, _bf16) instead of
- * row-major [E, N, K] ([E, N, K/2]). */
+ * _fp8_fp4, _bf16, _int8): the weights are in the fragment-packed order
+ * written by moe_pack_weight_fp8 (moe_pack_weight_int4, _fp4, _bf16; the INT8
+ * codes use moe_pack_weight_fp8's order) instead of row-major [E, N, K]
+ * ([E, N, K/2]). */
 enum { MOE_WEIGHTS_PACKED = 0x10 };
 
 enum { MOE_MAX_EXPERTS = 1024, MOE_MAX_TOPK = 64 };
@@ -365,6 +368,51 @@ moe_status moe_grouped_gemm_fp8_fp4(int layout,
                                     const int32_t* counts, const int32_t* seg_offsets,
                                     int E, int64_t rows_cap_or_max_m, int N, int K,
                                     int expected_m, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* INT8 (1, 1, 128) variant (AsymGEMM README, "API Reference", INT8 asymmetric
+ * GEMM: int8 data paired with fp32 scales of fixed granularity (1, 1, 128):
+ * one scale per token row and 128 K for the activations, one per output
+ * channel and 128 K for the weights; contiguous and masked grouped layouts,
+ * bf16 output).  The page fixes no rule for choosing a scale; these calls use
+ * the symmetric one: s = amax / 127 over the 128-element block (fp32,
+ * correctly rounded division; s = 1 for an all-zero block) and codes
+ * rne(x / s) (the same division) clamped to [-127, 127].
+ *
+ * moe_quant_act_int8: x [rows, K] bf16 -> q [rows, K] int8 and
+ *   s [rows, K/128] fp32.  Requires K % 128 == 0; x and q 16-byte aligned, s
+ *   4-byte aligned; rows == 0 is a no-op.  Outputs must not overlap x. */
+moe_status moe_quant_act_int8(const uint16_t* x, int64_t rows, int K, int8_t* q, float* s, void* stream);
+
+/* moe_quant_weight_int8: expert weights w [E, N, K] bf16 -> q [E, N, K] int8
+ *   (row n of expert e quantised as one activation row) and the per-channel
+ *   scales in the K-block-major order the grouped GEMM reads:
+ *   sw[(e * K/128 + kb) * N + n] is the scale of q[e, n, 128kb .. 128kb+127]
+ *   (the page's [E, N, K/128] scales transposed in their last two dimensions).
+ *   Requires N % 128 == 0 and K % 128 == 0; w and q 16-byte aligned, sw
+ *   4-byte aligned; E == 0 is a no-op.  q may be passed to
+ *   moe_pack_weight_fp8 (a byte permutation) for the packed weight order. */
+moe_status moe_quant_weight_int8(const uint16_t* w, int E, int N, int K, int8_t* q, float* sw, void* stream);
+
+/* moe_grouped_gemm_int8: int8 activations x int8 weights grouped GEMM.
+ *   For every segment e and row p in [start_e, start_e + counts[e]):
+ *     D[p, n] = bf16_rne( sum_kb SA[p, kb] * SW[e, kb, n] *
+ *                         sum_{k in block kb} A[p, k] * W[e, n, k] )
+ *   each block's integer sum exact, the scaled sums accumulated in fp32.
+ *     A [rows, K] int8, SA [rows, K/128] fp32 (moe_quant_act_int8);
+ *     W [E, N, K] int8, SW [E, K/128, N] fp32 (moe_quant_weight_int8);
+ *     D [rows, N] bf16.
+ *   Layout, counts, seg_offsets, expected_m, the rows of D that are written,
+ *   and size limits as for moe_grouped_gemm_fp8; SA 4-byte aligned, SW
+ *   16-byte aligned.  layout | MOE_WEIGHTS_PACKED: W in the fragment order of
+ *   moe_pack_weight_fp8 (SW unchanged). */
+moe_status moe_grouped_gemm_int8(int layout,
+                                 const int8_t* A, const float* SA,
+                                 const int8_t* W, const float* SW,
+                                 uint16_t* D,
+                                 const int32_t* counts, const int32_t* seg_offsets,
+                                 int E, int64_t rows_cap_or_max_m, int N, int K,
+                                 int expected_m, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* moe_swiglu_quant: SwiGLU between the up- and down-projection, requantised

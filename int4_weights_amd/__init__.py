@@ -1,4 +1,4 @@
-"""MoE grouped GEMM on gfx950 (MI355X): FP8 block-scaled and 4-bit weight-only.
+"""MoE grouped GEMM on gfx950 (MI355X): FP8 block-scaled, 4-bit weight-only, FP4, INT8 and BF16.
 
 The compute path is libmoe.so (hand-written HIP kernels behind the C ABI in
 include/moe.h); this package is its thin Python binding.  Build the library
@@ -21,15 +21,18 @@ from ._lib import (  # noqa: F401
     moe_grouped_gemm_fp8_fp4,
     moe_grouped_gemm_fp8_swiglu,
     moe_grouped_gemm_int4,
+    moe_grouped_gemm_int8,
     moe_pack_weight_bf16,
     moe_pack_weight_fp4,
     moe_pack_weight_fp8,
     moe_pack_weight_int4,
     moe_packed_rows_cap,
     moe_quant_act,
+    moe_quant_act_int8,
     moe_quant_weight_fp4,
     moe_quant_weight_fp8,
     moe_quant_weight_int4,
+    moe_quant_weight_int8,
     moe_route_pack,
     moe_route_pack_noalloc,
     moe_route_pack_noalloc_max_bytes,

@@ -58,6 +58,10 @@ SIGNATURES = {
     "moe_pack_weight_fp4": (_c_i32, [_vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
     "moe_grouped_gemm_fp8_fp4": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
+    "moe_quant_act_int8": (_c_i32, [_vp, _c_i64, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_quant_weight_int8": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_grouped_gemm_int8": (_c_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_unpermute_combine": (_c_i32, [_vp, _c_i64, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
     "moe_stream_read_words": (ctypes.c_int, []),
     "moe_stream_read": (_c_i32, [_vp, _c_i64, _vp, _vp]),
@@ -351,6 +355,42 @@ def moe_grouped_gemm_fp8_fp4(layout: int, A, SFA, W4, SW, D, counts, seg_offsets
     _check(load().moe_grouped_gemm_fp8_fp4(layout, _ptr(A), _ptr(SFA), _ptr(W4), _ptr(SW), _ptr(D), _ptr(counts),
                                            _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m,
                                            _stream(stream)), "moe_grouped_gemm_fp8_fp4")
+
+
+def moe_quant_act_int8(x, q, s, stream=None):
+    """x bf16 [rows, K] -> q int8 [rows, K], s float32 [rows, K/128] (INT8 (1, 1, 128), symmetric amax / 127)."""
+    _dev(x, "x", torch.bfloat16, 2), _dev(q, "q", torch.int8, 2), _dev(s, "s", torch.float32, 2)
+    rows, K = x.shape
+    if tuple(q.shape) != (rows, K) or tuple(s.shape) != (rows, K // 128):
+        raise ValueError("moe_quant_act_int8: shape mismatch")
+    _check(load().moe_quant_act_int8(_ptr(x), rows, K, _ptr(q), _ptr(s), _stream(stream)), "moe_quant_act_int8")
+
+
+def moe_quant_weight_int8(w, q, sw, stream=None):
+    """w bf16 [E, N, K] -> q int8 [E, N, K], sw float32 [E, K/128, N] (per-channel scales, K-block-major)."""
+    _dev(w, "w", torch.bfloat16, 3), _dev(q, "q", torch.int8, 3), _dev(sw, "sw", torch.float32, 3)
+    E, N, K = w.shape
+    if tuple(q.shape) != (E, N, K) or tuple(sw.shape) != (E, K // 128, N):
+        raise ValueError("moe_quant_weight_int8: shape mismatch")
+    _check(load().moe_quant_weight_int8(_ptr(w), E, N, K, _ptr(q), _ptr(sw), _stream(stream)),
+           "moe_quant_weight_int8")
+
+
+def moe_grouped_gemm_int8(layout: int, A, SA, W, SW, D, counts, seg_offsets, E: int, rows_cap_or_max_m: int,
+                          N: int, K: int, expected_m: int = 0, stream=None):
+    """int8 A [rows, K] with SA [rows, K/128] x int8 W [E, N, K] (or moe_pack_weight_fp8's order) with
+    SW [E, K/128, N] -> D bf16 [rows, N]."""
+    _dev(A, "A", torch.int8), _dev(SA, "SA", torch.float32), _dev(W, "W")
+    _dev(SW, "SW", torch.float32), _dev(D, "D", torch.bfloat16), _dev(counts, "counts", torch.int32)
+    _dev(seg_offsets, "seg_offsets", torch.int32)
+    if W.dtype not in (torch.int8, torch.uint8):
+        raise ValueError("W must be int8 (or uint8 from moe_pack_weight_fp8)")
+    _gemm_sizes("moe_grouped_gemm_int8", layout, E, rows_cap_or_max_m, counts, seg_offsets,
+                lambda rows: (("A", A, rows * K), ("SA", SA, rows * (K // 128)), ("W", W, E * N * K),
+                              ("SW", SW, E * (K // 128) * N), ("D", D, rows * N)))
+    _check(load().moe_grouped_gemm_int8(layout, _ptr(A), _ptr(SA), _ptr(W), _ptr(SW), _ptr(D), _ptr(counts),
+                                        _ptr(seg_offsets), E, rows_cap_or_max_m, N, K, expected_m, _stream(stream)),
+           "moe_grouped_gemm_int8")
 
 
 def moe_swiglu_quant(layout: int, gate_up, rows_cap_or_max_m: int, counts, seg_offsets, E: int, q, sf,

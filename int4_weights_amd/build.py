@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["api.hip", "quant.hip", "route.hip", "gemm_fp8.hip", "gemm_int4.hip", "gemm_bf16.hip", "gemm_fp4.hip",
-           "swiglu.hip", "combine.hip", "stream.hip"]
+           "gemm_int8.hip", "swiglu.hip", "combine.hip", "stream.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 

@@ -499,6 +499,60 @@ moe_status moe_grouped_gemm_fp8_fp4(int layout, const uint8_t* A, const float* S
   return hip_status(launch_gemm_fp4(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_fp8_fp4");
 }
 
+moe_status moe_quant_act_int8(const uint16_t* x, int64_t rows, int K, int8_t* q, float* s, void* stream) {
+  g_err[0] = 0;
+  if (rows < 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_quant_act_int8: rows=%lld K=%d", (long long)rows, K);
+  if (K % 128) return fail(MOE_ERR_UNSUPPORTED, "moe_quant_act_int8: K=%d is not a multiple of 128", K);
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !s) return fail(MOE_ERR_NULL, "moe_quant_act_int8: null pointer");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4))
+    return fail(MOE_ERR_ALIGN, "moe_quant_act_int8: x and q must be 16-byte aligned, s 4-byte aligned");
+  return hip_status(launch_quant_int8(x, rows, K, 0, q, s, (hipStream_t)stream), "moe_quant_act_int8");
+}
+
+moe_status moe_quant_weight_int8(const uint16_t* w, int E, int N, int K, int8_t* q, float* sw, void* stream) {
+  g_err[0] = 0;
+  if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "moe_quant_weight_int8: E=%d N=%d K=%d", E, N, K);
+  if (N % 128 || K % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_quant_weight_int8: N=%d and K=%d must be multiples of 128", N, K);
+  if (E == 0) return MOE_OK;
+  if (!w || !q || !sw) return fail(MOE_ERR_NULL, "moe_quant_weight_int8: null pointer");
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(sw, 4))
+    return fail(MOE_ERR_ALIGN, "moe_quant_weight_int8: w and q must be 16-byte aligned, sw 4-byte aligned");
+  return hip_status(launch_quant_int8(w, (int64_t)E * N, K, N, q, sw, (hipStream_t)stream), "moe_quant_weight_int8");
+}
+
+moe_status moe_grouped_gemm_int8(int layout, const int8_t* A, const float* SA, const int8_t* W, const float* SW,
+                                 uint16_t* D, const int32_t* counts, const int32_t* seg_offsets, int E,
+                                 int64_t rows_cap_or_max_m, int N, int K, int expected_m, void* stream) {
+  g_err[0] = 0;
+  const int wpacked = (layout & MOE_WEIGHTS_PACKED) ? 1 : 0;
+  layout &= ~MOE_WEIGHTS_PACKED;
+  moe_status st = check_gemm("moe_grouped_gemm_int8", layout, A, W, SW, D, counts, seg_offsets, E, rows_cap_or_max_m,
+                             N, K);
+  if (st) return st;
+  if (!SA) return fail(MOE_ERR_NULL, "moe_grouped_gemm_int8: SA is null");
+  // a lane reads 4 consecutive weight scales of a K block as one 16-byte load
+  if (!aligned(SA, 4) || !aligned(SW, 16))
+    return fail(MOE_ERR_ALIGN, "moe_grouped_gemm_int8: SA must be 4-byte aligned, SW 16-byte aligned");
+  GemmArgs a{};
+  a.A = (const uint8_t*)A;
+  a.SFA = SA;
+  a.W = (const uint8_t*)W;
+  a.SW = SW;
+  a.D = D;
+  a.counts = counts;
+  a.seg_offsets = seg_offsets;
+  a.E = E;
+  a.masked = layout == MOE_LAYOUT_MASKED;
+  a.max_m = a.masked ? (int)rows_cap_or_max_m : 0;
+  a.rows_cap = a.masked ? (int64_t)E * rows_cap_or_max_m : rows_cap_or_max_m;
+  a.N = N;
+  a.K = K;
+  a.wpacked = wpacked;
+  return hip_status(launch_gemm_int8(a, expected_m, (hipStream_t)stream), "moe_grouped_gemm_int8");
+}
+
 moe_status moe_swiglu_quant(int layout, const uint16_t* gate_up, int64_t rows_cap_or_max_m, int I,
                             const int32_t* counts, const int32_t* seg_offsets, int E, uint8_t* q, float* sf,
                             void* stream) {

@@ -13,6 +13,8 @@ struct DeviceInfo {
 DeviceInfo device_info();
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int K, uint8_t* q, float* sf, hipStream_t s);
+// INT8 (1, 1, 128): wn = 0 writes scales [rows, K/128]; wn = N (rows = E*N) writes them [E, K/128, N]
+hipError_t launch_quant_int8(const uint16_t* x, int64_t rows, int K, int wn, int8_t* q, float* sf, hipStream_t s);
 hipError_t launch_quant_weight_fp8(const uint16_t* w, int E, int N, int K, uint8_t* q, float* sfw, hipStream_t s);
 hipError_t launch_pack_weight_fp8(const uint8_t* q, int E, int N, int K, uint8_t* packed, hipStream_t s);
 hipError_t launch_pack_weight_int4(const uint8_t* q4, const uint16_t* s16, int E, int N, int K, uint8_t* q4_packed,
@@ -51,10 +53,11 @@ hipError_t route_scratch_ptr(int32_t** out);
 hipError_t launch_route_pack(const RouteArgs& a, hipStream_t s);
 
 struct GemmArgs {
-  const uint8_t* A;      // fp8 codes [rows, K] or bf16 [rows, K] (int4 and bf16 paths)
-  const float* SFA;      // [rows, K/128] (fp8 path)
-  const uint8_t* W;      // fp8 [E, N, K], int4 or fp4 [E, N, K/2], or bf16 [E, N, K]
-  const void* SW;        // SFW fp32 [E, N/128, K/128], S16 fp16 [E, N, K/128] or E8M0 bytes [E, N, K/32] (fp4)
+  const uint8_t* A;      // fp8 or int8 codes [rows, K] or bf16 [rows, K] (int4 and bf16 paths)
+  const float* SFA;      // [rows, K/128] (fp8 and int8 paths)
+  const uint8_t* W;      // fp8 or int8 [E, N, K], int4 or fp4 [E, N, K/2], or bf16 [E, N, K]
+  const void* SW;        // SFW fp32 [E, N/128, K/128], S16 fp16 [E, N, K/128], E8M0 bytes [E, N, K/32] (fp4)
+                         // or fp32 [E, K/128, N] (int8)
   uint16_t* D;           // bf16 [rows, N]
   uint8_t* Q;            // SwiGLU GEMM: E4M3 [rows, N/2] (instead of D)
   float* SQ;             // SwiGLU GEMM: fp32 [rows, N/256]
@@ -72,6 +75,7 @@ hipError_t launch_gemm_fp8_swiglu(const GemmArgs& a, int expected_m, hipStream_t
 hipError_t launch_gemm_int4(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_gemm_fp4(const GemmArgs& a, int expected_m, hipStream_t s);
+hipError_t launch_gemm_int8(const GemmArgs& a, int expected_m, hipStream_t s);
 hipError_t launch_quant_weight_fp4(const uint16_t* w, int E, int N, int K, uint8_t* w4, uint8_t* sw, hipStream_t s);
 hipError_t launch_pack_weight_fp4(const uint8_t* w4, const uint8_t* sw, int E, int N, int K, uint8_t* w4p,
                                   uint8_t* swp, hipStream_t s);

@@ -1,5 +1,5 @@
-// quant.hip -- FP8 1x128 / 128x128 power-of-two quantisation and the group-128
-// 4-bit weight format.
+// quant.hip -- FP8 1x128 / 128x128 power-of-two quantisation, INT8 (1, 1, 128)
+// quantisation and the group-128 4-bit weight format.
 //
 // FP8 rule (nxmr.cn DeepGEMM FP8 article, "补偿机制一"): each block's scale is an
 // exact power of two, amax/448 rounded up, so scaling is an exponent shift and
@@ -246,6 +246,74 @@ __global__ __launch_bounds__(256) void pack_scale_int4_kernel(const uint16_t* __
   }
 }
 
+// INT8 (1, 1, 128) blocks (AsymGEMM README, "API Reference", INT8 asymmetric
+// GEMM: int8 data with one fp32 scale per row and 128 elements along K).
+// Symmetric rule: s = amax / 127 (fp32, correctly rounded), codes
+// rne(x / s) clamped to +-127, s = 1 for an all-zero block.  The division is
+// the correctly rounded fp32 one (hipcc's default for '/'), since it decides
+// the integer code.  One 8-lane group per block, lane holds 16 consecutive
+// elements, as for the FP8 activation codes.  The scales are written
+// [rows, K/128] for activations and in the K-block-major [E, K/128, N] order
+// for weights (the order the grouped GEMM reads them in).
+__device__ __forceinline__ void quant_int8_block(const v4i raw0, const v4i raw1, bool ok, int sub,
+                                                 int8_t* __restrict__ qblk, float* __restrict__ sfp) {
+  float f[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w0 = (uint32_t)raw0[i], w1 = (uint32_t)raw1[i];
+    f[2 * i] = bf16_to_f32(w0 & 0xffffu);
+    f[2 * i + 1] = bf16_to_f32(w0 >> 16);
+    f[8 + 2 * i] = bf16_to_f32(w1 & 0xffffu);
+    f[8 + 2 * i + 1] = bf16_to_f32(w1 >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = max8_lanes(amax);
+  const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
+  uint32_t o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float c = fminf(fmaxf(__builtin_rintf(f[4 * r + i] / s), -127.0f), 127.0f);
+      w |= ((uint32_t)(int)c & 0xffu) << (8 * i);
+    }
+    o[r] = w;
+  }
+  if (ok) {
+    *(uint4*)(qblk + sub * 16) = uint4{o[0], o[1], o[2], o[3]};
+    if (sub == 0) *sfp = s;
+  }
+}
+
+// Activations: block b = row * kb + j; scale at sf[b].  Weights (wn > 0):
+// row = e * wn + n, scale at sf[(e * kb + j) * wn + n].
+__global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restrict__ x, int64_t nblocks, int kb,
+                                                         int wn, int8_t* __restrict__ q, float* __restrict__ sf) {
+  const int lane = lane_id();
+  const int sub = lane & 7;
+  const int64_t gwave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t b0 = gwave * 8; b0 < nblocks; b0 += nwaves * 8) {
+    const int64_t blk = b0 + (lane >> 3);
+    const bool ok = blk < nblocks;
+    v4i r0 = {0, 0, 0, 0}, r1 = {0, 0, 0, 0};
+    if (ok) {
+      r0 = *(const v4i*)(x + blk * 128 + sub * 16);
+      r1 = *(const v4i*)(x + blk * 128 + sub * 16 + 8);
+    }
+    int64_t si = blk;
+    if (wn > 0) {
+      const int64_t row = blk / kb, j = blk - row * kb;
+      const int64_t e = row / wn, n = row - e * wn;
+      si = (e * kb + j) * wn + n;
+    }
+    quant_int8_block(r0, r1, ok, sub, q + blk * 128, sf + (ok ? si : 0));
+  }
+}
+
 static int grid_for(int64_t work_items, int per_block, int cap) {
   int64_t g = (work_items + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -258,6 +326,14 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t rows, int K, uint8_t* q, 
   if (nblocks == 0) return hipSuccess;
   const int grid = grid_for(nblocks, 32, device_info().cus * 16);  // 32 blocks per 256-thread WG per pass
   quant_act_kernel<<<grid, 256, 0, s>>>(x, nblocks, K / 128, q, sf);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_int8(const uint16_t* x, int64_t rows, int K, int wn, int8_t* q, float* sf, hipStream_t s) {
+  const int64_t nblocks = rows * (K / 128);
+  if (nblocks == 0) return hipSuccess;
+  const int grid = grid_for(nblocks, 32, device_info().cus * 16);  // 32 blocks per 256-thread WG per pass
+  quant_int8_kernel<<<grid, 256, 0, s>>>(x, nblocks, K / 128, wn, q, sf);
   return hipGetLastError();
 }
 

@@ -233,6 +233,36 @@ def test_host_validation_rejects_without_launching(lib):
     assert gs(Q=A16 + 8) == MOE_ERR_ALIGN
     assert gs(SFA=A16 + 4) == MOE_ERR_ALIGN          # row scales: 16-byte copies
     assert gs(SQ=A16 + 2) == MOE_ERR_ALIGN
+    # moe_quant_act_int8 / moe_quant_weight_int8
+    assert lib.moe_quant_act_int8(_p(A16), 4, 100, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_quant_act_int8(None, 4, 128, _p(A16), _p(A16), None) == MOE_ERR_NULL
+    assert lib.moe_quant_act_int8(_p(A16), 4, 128, _p(A16 + 8), _p(A16), None) == MOE_ERR_ALIGN
+    assert lib.moe_quant_act_int8(_p(A16), 4, 128, _p(A16), _p(A16 + 2), None) == MOE_ERR_ALIGN
+    assert lib.moe_quant_act_int8(_p(A16), -1, 128, _p(A16), _p(A16), None) == MOE_ERR_SHAPE
+    assert lib.moe_quant_act_int8(None, 0, 128, None, None, None) == MOE_OK
+    assert lib.moe_quant_weight_int8(_p(A16), 2, 100, 128, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_quant_weight_int8(_p(A16), 2, 128, 192, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_quant_weight_int8(_p(A16 + 2), 2, 128, 128, _p(A16), _p(A16), None) == MOE_ERR_ALIGN
+    assert lib.moe_quant_weight_int8(None, 2, 128, 128, _p(A16), _p(A16), None) == MOE_ERR_NULL
+    assert lib.moe_quant_weight_int8(None, 0, 128, 128, None, None, None) == MOE_OK
+    # moe_grouped_gemm_int8(layout, A, SA, W, SW, D, counts, seg, E, rows, N, K, expected_m, stream)
+    def g8(layout=0, N=256, K=256, E=4, rows=512, seg=A16, A=A16, SA=A16, SW=A16, D=A16):
+        return lib.moe_grouped_gemm_int8(layout, _p(A) if A else None, _p(SA) if SA else None, _p(A16),
+                                         _p(SW) if SW else None, _p(D) if D else None, _p(A16),
+                                         _p(seg) if seg else None, E, rows, N, K, 0, None)
+
+    assert g8(N=200) == MOE_ERR_UNSUPPORTED
+    assert g8(K=192) == MOE_ERR_UNSUPPORTED
+    assert g8(layout=0x10 | 7) == MOE_ERR_SHAPE
+    assert g8(E=0) == MOE_ERR_SHAPE
+    assert g8(rows=0) == MOE_ERR_SHAPE
+    assert g8(seg=0) == MOE_ERR_NULL
+    assert g8(SA=0) == MOE_ERR_NULL
+    assert g8(SW=0) == MOE_ERR_NULL
+    assert g8(D=0) == MOE_ERR_NULL
+    assert g8(A=A16 + 8) == MOE_ERR_ALIGN
+    assert g8(SA=A16 + 2) == MOE_ERR_ALIGN
+    assert g8(SW=A16 + 4) == MOE_ERR_ALIGN            # 4 columns' scales per 16-byte load
     # moe_unpermute_combine
     assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 2, 12, _p(A16), None) == MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(_p(A16), 10, _p(A16), _p(A16), 4, 0, 16, _p(A16), None) == MOE_ERR_SHAPE
