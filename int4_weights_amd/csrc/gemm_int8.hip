@@ -20,12 +20,24 @@
 //    2/3 of the int8 matrix peak.
 //  * Tiles, rings and scheduling follow the short FP8 tiles: the weight tile
 //    is the instruction's A operand (16 output columns), the activations its B
-//    operand (16 rows); each wave owns 64 columns and streams their weight
+//    operand (16 rows); each wave owns 256/NW columns and streams their weight
 //    fragments and weight scales from HBM into an S-deep register ring; the
 //    activation row slices and their scales go through registers into two
-//    XOR-swizzled LDS slots shared by the 4 waves.  A lane's weight scales for
+//    XOR-swizzled LDS slots shared by the waves.  A lane's weight scales for
 //    a K block are 4 consecutive columns of the K-block-major scale rows: one
 //    16-byte load per 16-column block.
+//  * Decode-sized segments: 16-row units, 4 waves of 64 columns, 3-deep ring.
+//    Larger segments: 192-row units (a DeepSeek-V3-shaped prefill expert of
+//    about 128 rows is one unit, so its weights stream once), 8 waves of 32
+//    columns (two per SIMD, so one wave's promotion overlaps the other's
+//    matrix instructions), 2-deep ring; the computed height is 64, 128 or
+//    192 rows, whichever covers the unit.  Within a K block, row block rb's
+//    matrix instructions are issued before row block rb - 1 is promoted.
+//    Measured on the DeepSeek-V3-shaped prefill (32768 routed rows, N 4096,
+//    K 7168): 64-row units with 4 waves 3.5 ms, 128-row units with 8 waves
+//    2.6 ms, 192-row units 2.2 ms; deeper rings, weight scales staged through
+//    LDS, and a 2 x 4 wave layout that halves the LDS fragment reads were not
+//    faster.
 //  * The K-to-lane assignment of the two instructions is the same for both
 //    operands (lane group g supplies bytes 16g..16g+15 of the block to the
 //    first and 64+16g.. to the second), so the row-major weights and the
@@ -36,32 +48,39 @@
 
 namespace moe {
 
+#ifndef MOE_I8_RB
+#define MOE_I8_RB 12
+#define MOE_I8_S 2
+#define MOE_I8_NW 8
+#endif
+
 // RB: 16-row blocks per unit (BM = 16*RB); S: register-ring depth (K blocks);
-// 4 waves, each owning 4 blocks of 16 columns (BN = 256).
-template <int RB, int S>
+// NW: waves per workgroup, each owning CB = 16/NW blocks of 16 columns (BN = 256).
+template <int RB, int S, int NW>
 struct Int8Cfg {
-  static constexpr int NW = 4;
   static constexpr int BM = 16 * RB;
-  static constexpr int CB = 4;
-  static constexpr int kWcols = 64;                    // columns per wave
+  static constexpr int CB = 16 / NW;
+  static constexpr int kWcols = 16 * CB;               // columns per wave
   static constexpr int kApw = (2 * RB + NW - 1) / NW;  // 16-byte A loads per lane per stage (1 KB = 8 rows each)
   static constexpr int kArows = NW * 8 * kApw;         // rows held per LDS slot (>= BM)
   static constexpr int kAStage = kArows * 128;         // bytes per LDS slot
   static constexpr int kSaStage = NW * 64;             // row-scale floats per slot (one per lane)
   static_assert(kArows >= BM, "A stage too small");
   static_assert(S >= 2, "ring depth");
+  static_assert(NW * CB == 16, "256 columns per unit");
 };
 
-template <int RB, int S>
+template <int RB, int S, int NW>
 struct Int8Smem {
-  uint8_t a[2][Int8Cfg<RB, S>::kAStage];
-  float sa[2][Int8Cfg<RB, S>::kSaStage];
+  uint8_t a[2][Int8Cfg<RB, S, NW>::kAStage];
+  float sa[2][Int8Cfg<RB, S, NW>::kSaStage];
 };
 
 // One unit with RBE (<= RB) row blocks computed.
-template <int RB, int S, int RBE>
-__device__ __forceinline__ void int8_unit(const GemmArgs& a, const Unit& u, Int8Smem<RB, S>& sm, int wv, int lane) {
-  using C = Int8Cfg<RB, S>;
+template <int RB, int S, int NW, int RBE>
+__device__ __forceinline__ void int8_unit(const GemmArgs& a, const Unit& u, Int8Smem<RB, S, NW>& sm, int wv,
+                                          int lane) {
+  using C = Int8Cfg<RB, S, NW>;
   constexpr int CB = C::CB;
   const int l16 = lane & 15, lg = lane >> 4;
   const int K = a.K, N = a.N, KB = K / 128;
@@ -146,23 +165,40 @@ __device__ __forceinline__ void int8_unit(const GemmArgs& a, const Unit& u, Int8
     sm.sa[ks & 1][64 * wv + lane] = sr[slot];
   };
 
+  // Row block rb's matrix instructions are issued before row block rb - 1 is
+  // promoted, and rb + 1's fragments are read meanwhile, so the VALU work of
+  // one row block overlaps the matrix pipe and LDS latency of the next.
   auto compute = [&](int ks, auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
     const uint8_t* ab = &sm.a[ks & 1][0];
     const float* sab = &sm.sa[ks & 1][l16];
-#pragma unroll
-    for (int rb = 0; rb < RBE; ++rb) {
-      const v4i alo = *(const v4i*)(ab + off_lo + rb * 2048);
-      const v4i ahi = *(const v4i*)(ab + off_hi + rb * 2048);
+    v4i alo[2], ahi[2], sum[2][CB];
+    alo[0] = *(const v4i*)(ab + off_lo);
+    ahi[0] = *(const v4i*)(ab + off_hi);
+    auto promote = [&](int rb, int b) {
       const float sa = sab[16 * rb];
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        v4i s = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo[slot][cb], alo, v4i{0, 0, 0, 0}, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi[slot][cb], ahi, s, 0, 0, 0);
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[rb][cb][r] = fmaf((float)s[r], sa * wsc[slot][cb][r], acc[rb][cb][r]);
+        for (int r = 0; r < 4; ++r)
+          acc[rb][cb][r] = fmaf((float)sum[b][cb][r], sa * wsc[slot][cb][r], acc[rb][cb][r]);
+    };
+#pragma unroll
+    for (int rb = 0; rb < RBE; ++rb) {
+      const int b = rb & 1;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        sum[b][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo[slot][cb], alo[b], v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        sum[b][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi[slot][cb], ahi[b], sum[b][cb], 0, 0, 0);
+      if (rb + 1 < RBE) {
+        alo[b ^ 1] = *(const v4i*)(ab + off_lo + (rb + 1) * 2048);
+        ahi[b ^ 1] = *(const v4i*)(ab + off_hi + (rb + 1) * 2048);
       }
+      if (rb > 0) promote(rb - 1, b ^ 1);
     }
+    promote(RBE - 1, (RBE - 1) & 1);
   };
 
   // One K block: publish its activations, refill the ring, multiply.  LDS
@@ -203,10 +239,10 @@ __device__ __forceinline__ void int8_unit(const GemmArgs& a, const Unit& u, Int8
   }
 }
 
-template <int RB, int S>
-__global__ __launch_bounds__(256, 1) void gemm_int8_kernel(const GemmArgs a) {
-  using C = Int8Cfg<RB, S>;
-  __shared__ __attribute__((aligned(1024))) Int8Smem<RB, S> sm;
+template <int RB, int S, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_int8_kernel(const GemmArgs a) {
+  using C = Int8Cfg<RB, S, NW>;
+  __shared__ __attribute__((aligned(1024))) Int8Smem<RB, S, NW> sm;
   __shared__ SchedSmem s_sched;
 
   const Sched sc{&s_sched};
@@ -214,29 +250,36 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_kernel(const GemmArgs a) {
   const Walk walk = sched_walk(s_sched.total);
   const int lane = lane_id();
   const int wv = uniform(threadIdx.x >> 6);
-  constexpr int RH = (RB + 1) / 2;  // the shorter tile height
-
   for (int v = walk.first; v < walk.end; v += walk.stride) {
     const Unit u = sched_unit<C::BM>(a, sc, v);
-    if (RB > 1 && u.mrows <= 16 * RH) int8_unit<RB, S, RH>(a, u, sm, wv, lane);
-    else int8_unit<RB, S, RB>(a, u, sm, wv, lane);
+    // computed height in steps of a third of the full one (RB % 3 == 0) or a half; padding rows never stored
+    if constexpr (RB % 3 == 0) {
+      if (u.mrows <= 16 * (RB / 3)) int8_unit<RB, S, NW, RB / 3>(a, u, sm, wv, lane);
+      else if (u.mrows <= 16 * (2 * RB / 3)) int8_unit<RB, S, NW, 2 * RB / 3>(a, u, sm, wv, lane);
+      else int8_unit<RB, S, NW, RB>(a, u, sm, wv, lane);
+    } else if constexpr (RB > 1) {
+      if (u.mrows <= 16 * ((RB + 1) / 2)) int8_unit<RB, S, NW, (RB + 1) / 2>(a, u, sm, wv, lane);
+      else int8_unit<RB, S, NW, RB>(a, u, sm, wv, lane);
+    } else {
+      int8_unit<RB, S, NW, 1>(a, u, sm, wv, lane);
+    }
   }
 }
 
-template <int RB, int S>
+template <int RB, int S, int NW>
 static hipError_t launch_int8(const GemmArgs& a, hipStream_t s) {
   const int cus = device_info().cus;
   int grid = cus - cus % kXcds;
   if (grid < kXcds) grid = kXcds;
-  gemm_int8_kernel<RB, S><<<grid, 256, 0, s>>>(a);
+  gemm_int8_kernel<RB, S, NW><<<grid, NW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_int8(const GemmArgs& a, int expected_m, hipStream_t s) {
   // decode-sized segments: one 16-row block per unit, weights streamed once; larger ones: 64-row units
   const int em = expected_m > 0 ? expected_m : (a.masked ? a.max_m : 256);
-  if (em <= 16) return launch_int8<1, 3>(a, s);
-  return launch_int8<4, 6>(a, s);
+  if (em <= 16) return launch_int8<1, 3, 4>(a, s);
+  return launch_int8<MOE_I8_RB, MOE_I8_S, MOE_I8_NW>(a, s);
 }
 
 }  // namespace moe
