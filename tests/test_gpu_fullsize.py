@@ -360,3 +360,94 @@ def test_full_size_int4_decode_layer():
 
     c = dict(T=T, k=k, N=N, K=K, tok=tok, tw=tw.numpy(), sample=sample)
     _fp8_gemm_and_combine(c, r, lambda tt: oracle.bf16_bits_to_f64(x_bits[tt]), layer.D, z, wfn, "int4")
+
+
+@pytest.mark.parametrize("name", ["dsv3_decode", "dsv3_prefill"])
+def test_full_size_int8_variant(name):
+    """The benchmark's INT8 (1, 1, 128) variant of a DeepSeek-V3-shaped workload at full size, launched as the
+    benchmark launches it (codes and scales routed together, packed weights, tiling hint = routes per expert):
+    routing bit-exact on every route, quantisation bit-exact on sampled tokens and weight blocks, packing a byte
+    copy, GEMM and combine on sampled outputs."""
+    require_gpu()
+    cfg = synth.config_by_name(name)
+    print(f"[fullsize] int8 {name}", flush=True)
+    T, E, k, K, N = cfg.T, cfg.E, cfg.topk, cfg.K, cfg.N
+    ids, tw = synth.route_inputs(cfg)
+    ids_np = ids.numpy()
+    tok = cfg.T // 3 + 2
+    sample, _ = _sample_experts(ids_np, E, tok)
+    x = synth.activations(cfg, T, K)
+    codes = torch.empty(E, N, K, dtype=torch.int8, device=DEV)
+    sw = torch.empty(E, K // 128, N, dtype=torch.float32, device=DEV)
+    kept = {}
+    for e0 in range(0, E, 16):
+        ex = list(range(e0, min(E, e0 + 16)))
+        w = synth.expert_weights(cfg, N, K, experts=ex, stream=synth.STREAM_WEIGHTS, device=DEV)
+        moe.moe_quant_weight_int8(w, codes[e0:e0 + len(ex)], sw[e0:e0 + len(ex)])
+        for i, e in enumerate(ex):
+            if e in sample:
+                kept[e] = u16(w[i])
+        del w
+    W = torch.empty(E, N, K, dtype=torch.uint8, device=DEV)
+    moe.moe_pack_weight_fp8(codes.view(torch.uint8), W)
+    layout = moe.LAYOUT_MASKED if cfg.layout == "masked" else moe.LAYOUT_CONTIGUOUS
+    am = cfg.max_m if cfg.layout == "masked" else cfg.align
+    rows_cap = moe.moe_packed_rows_cap(T, k, E, am) if layout == moe.LAYOUT_CONTIGUOUS else E * am
+    em = max(1, T * k // E)
+    xd = x.to(DEV)
+    q = torch.empty(T, K, dtype=torch.int8, device=DEV)
+    sf = torch.empty(T, K // 128, dtype=torch.float32, device=DEV)
+    P = torch.empty(rows_cap, K, dtype=torch.int8, device=DEV)
+    Psf = torch.empty(rows_cap, K // 128, dtype=torch.float32, device=DEV)
+    counts = torch.zeros(E, dtype=torch.int32, device=DEV)
+    seg = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
+    mi = torch.empty(rows_cap, dtype=torch.int32, device=DEV)
+    oi = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(moe.moe_route_pack_workspace_bytes(T, k, E), 16), dtype=torch.uint8, device=DEV)
+    D = torch.empty(rows_cap, N, dtype=torch.bfloat16, device=DEV)
+    Z = torch.empty(T, N, dtype=torch.bfloat16, device=DEV)
+    moe.moe_quant_act_int8(xd, q, sf)
+    moe.moe_route_pack(ids.to(DEV), E, layout, am, q, P, counts, seg, mi, oi, st, payload2=sf, packed2=Psf,
+                       workspace=ws)
+    am_gemm = am if layout == moe.LAYOUT_MASKED else rows_cap
+    moe.moe_grouped_gemm_int8(layout | moe.WEIGHTS_PACKED, P, Psf, W, sw, D, counts, seg, E, am_gemm, N, K, em)
+    moe.moe_unpermute_combine(D, oi, tw.to(DEV), Z)
+    torch.cuda.synchronize()
+
+    class _L:
+        pass
+
+    lay = _L()
+    lay.counts, lay.seg_offsets, lay.output_index, lay.m_indices, lay.dev_status = counts, seg, oi, mi, st
+    lay.rows_cap = rows_cap
+    r = _check_routing(lay, ids_np, E, cfg.layout, am)
+    x_bits = u16(x)
+    toks = np.array(sorted(set([0, T - 1, tok] + list(range(1, T, max(1, T // 16))))))
+    oq, os_ = oracle.quant_int8(x_bits[toks])
+    assert np.array_equal(q[torch.from_numpy(toks).to(DEV)].cpu().numpy(), oq)
+    assert np.array_equal(sf[torch.from_numpy(toks).to(DEV)].cpu().numpy(), os_)
+    oiv = r["output_index"].reshape(-1)
+    ok = oiv >= 0
+    src = torch.from_numpy((np.arange(oiv.size) // k)[ok].astype(np.int64)).to(DEV)
+    dst = torch.from_numpy(oiv[ok].astype(np.int64)).to(DEV)
+    assert torch.equal(P[dst], q[src]) and torch.equal(Psf[dst], sf[src])
+
+    cache = {}
+
+    def wfn(e, blocks):
+        if e not in cache:
+            rows = np.concatenate([np.arange(128 * b, 128 * b + 128) for b in blocks])
+            qq, ss = oracle.quant_int8(kept[e][rows])
+            rr = torch.from_numpy(rows).to(DEV)
+            assert np.array_equal(codes[e][rr].cpu().numpy(), qq), f"int8 codes of expert {e}"
+            assert np.array_equal(sw[e][:, rr].cpu().numpy(), ss.T), f"int8 scales of expert {e}"
+            cache[e] = oracle.dequant_int8(qq, ss)
+        return cache[e]
+
+    def a_of_tokens(tt):
+        a, sa = oracle.quant_int8(x_bits[tt])
+        return oracle.dequant_int8(a, sa)
+
+    c = dict(T=T, k=k, N=N, K=K, tok=tok, tw=tw.numpy(), sample=sample)
+    _fp8_gemm_and_combine(c, r, a_of_tokens, D, Z, wfn, "fp8")
