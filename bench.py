@@ -3,8 +3,10 @@
 
 A step is one pass of the whole path over one batch of synthetic input with
 everything already resident in HBM:
-    moe_quant_act -> moe_route_pack -> moe_grouped_gemm_fp8 -> moe_unpermute_combine
-(for the Qwen3-shaped workload the whole expert FFN: the up-projection with
+    moe_route_pack_quant -> moe_grouped_gemm_fp8 -> moe_unpermute_combine
+(moe_route_pack_quant quantises the bf16 token rows to 1x128 FP8 while it
+routes and packs them: the same bits as moe_quant_act then moe_route_pack;
+for the Qwen3-shaped workload the whole expert FFN: the up-projection with
 SwiGLU and the requantisation in its epilogue (moe_grouped_gemm_fp8_swiglu),
 the down-projection, then the combine; the 4-bit GEMM in place of the FP8 one
 for the INT4 workload).
@@ -275,22 +277,21 @@ def build_workload(args, cfg, torch, np, moe, synth, want_cpu):
         layer = MoeFP8Layer(codes, sfw, k, T, layout, am, expected_m=em, weights_packed=True)
         w["kept"] = kept
         if not cfg.K_down:
-            names = ["moe_quant_act", "moe_route_pack", "gemm", "moe_unpermute_combine"]
+            # quantisation folded into the pack (moe_route_pack_quant): one pass over the token rows
+            names = ["moe_route_pack_quant", "gemm", "moe_unpermute_combine"]
 
             def step(tm, s):
                 tm.mark(s, 0)
-                layer.quant(x)
+                layer.quant_route(x, ids)
                 tm.mark(s, 1)
-                layer.route(ids)
-                tm.mark(s, 2)
                 layer.gemm()
-                tm.mark(s, 3)
+                tm.mark(s, 2)
                 layer.combine(tw)
-                tm.mark(s, 4)
+                tm.mark(s, 3)
         else:
             # the whole expert FFN: up-projection (gate and up columns) with SwiGLU + requantisation in its
             # epilogue, down-projection
-            names = ["moe_quant_act", "moe_route_pack", "gemm", "gemm_down", "moe_unpermute_combine"]
+            names = ["moe_route_pack_quant", "gemm", "gemm_down", "moe_unpermute_combine"]
             assert N == 2 * cfg.K_down
             dcodes, dsfw, _ = fp8_weights(torch, moe, synth, cfg, cfg.N_down, cfg.K_down, synth.STREAM_WEIGHTS_DOWN)
             qd = torch.empty(layer.rows_cap, cfg.K_down, dtype=torch.uint8, device=dev)
@@ -300,16 +301,14 @@ def build_workload(args, cfg, torch, np, moe, synth, want_cpu):
 
             def step(tm, s):
                 tm.mark(s, 0)
-                layer.quant(x)
+                layer.quant_route(x, ids)
                 tm.mark(s, 1)
-                layer.route(ids)
-                tm.mark(s, 2)
                 layer.gemm_swiglu(qd, sfd)
-                tm.mark(s, 3)
+                tm.mark(s, 2)
                 layer.gemm(A=qd, SFA=sfd, D=Dd, w=dcodes, sfw=dsfw, N=cfg.N_down, K=cfg.K_down)
-                tm.mark(s, 4)
+                tm.mark(s, 3)
                 layer.combine(tw, D=Dd, Z=Zd)
-                tm.mark(s, 5)
+                tm.mark(s, 4)
     else:
         # 4-bit weights: several copies rotate across steps so the 256 MB cache never holds the weights
         # (one allocation holds all copies, made before the generation temporaries)
@@ -383,24 +382,19 @@ def build_variant(args, fmt, cfg, torch, np, moe, synth):
             moe.moe_quant_weight_fp4(w, r4[:len(ex)], rs[:len(ex)])
             moe.moe_pack_weight_fp4(r4[:len(ex)], rs[:len(ex)], W4[e0:e0 + len(ex)], SW[e0:e0 + len(ex)])
             del w
-        q = torch.empty(T, K, dtype=torch.uint8, device=dev)
-        sf = torch.empty(T, K // 128, dtype=torch.float32, device=dev)
         P = torch.empty(rows_cap, K, dtype=torch.uint8, device=dev)
         Psf = torch.empty(rows_cap, K // 128, dtype=torch.float32, device=dev)
-        names = ["moe_quant_act", "moe_route_pack", "gemm", "moe_unpermute_combine"]
+        names = ["moe_route_pack_quant", "gemm", "moe_unpermute_combine"]
 
         def step(tm, s):
             tm.mark(s, 0)
-            moe.moe_quant_act(x, q, sf)
+            moe.moe_route_pack_quant(ids, E, layout, am, x, P, Psf, counts, seg, mi, oi, st, workspace=ws)
             tm.mark(s, 1)
-            moe.moe_route_pack(ids, E, layout, am, q, P, counts, seg, mi, oi, st, payload2=sf, packed2=Psf,
-                               workspace=ws)
-            tm.mark(s, 2)
             moe.moe_grouped_gemm_fp8_fp4(layout | moe.WEIGHTS_PACKED, P, Psf, W4, SW, D, counts, seg, E, am_gemm, N, K,
                                          em)
-            tm.mark(s, 3)
+            tm.mark(s, 2)
             moe.moe_unpermute_combine(D, oi, tw, Z)
-            tm.mark(s, 4)
+            tm.mark(s, 3)
     elif fmt == "int8":
         # INT8 codes in moe_pack_weight_fp8's fragment order, per-channel scales K-block-major (prepared once)
         W8 = torch.empty(E, N, K, dtype=torch.uint8, device=dev)

@@ -6,6 +6,7 @@
  *
  *   moe_quant_act          bf16 tokens -> FP8 E4M3 codes + 1x128 pow2 scales
  *   moe_route_pack         topk_ids -> per-expert segments; copies token rows
+ *   moe_route_pack_quant   (the two steps above in one call) quantises bf16 rows into the segments
  *   moe_grouped_gemm_fp8   packed rows x expert weights (128x128 pow2 scales) -> bf16
  *   moe_grouped_gemm_int4  (weight-only variant) bf16 rows x 4-bit weights -> bf16
  *   moe_grouped_gemm_bf16  (BF16 variant) bf16 rows x bf16 expert weights -> bf16
@@ -214,6 +215,29 @@ moe_status moe_route_pack(const int32_t* topk_ids, int T, int k, int E,
                           int32_t* dev_status,
                           void* workspace, int64_t workspace_bytes,
                           void* stream);
+
+/* moe_route_pack_quant: moe_quant_act and moe_route_pack in one call -- the
+ * bf16 token rows are quantised (1x128 blocks, power-of-two scales, E4M3
+ * codes: exactly the rule of moe_quant_act, nxmr.cn DeepGEMM article,
+ * "补偿机制一") on the way into the packed layout, so the token-order codes
+ * are never written to HBM and read back (rainlin, "GEMM 执行方式", sec. 4.6
+ * flow: scatter -> grouped GEMM -> gather, with the quantisation folded into
+ * the scatter).
+ *   x [T, K] bf16 (16-byte aligned, K % 128 == 0, K <= 32768); packed_q [rows_cap, K]
+ *   E4M3 codes (16-byte aligned) and packed_sf [rows_cap, K/128] fp32 scales
+ *   (4-byte aligned) receive what moe_route_pack would copy from
+ *   moe_quant_act's q and sf (payload = q, payload2 = sf), bit for bit; every
+ *   other argument, output, error and the workspace as for moe_route_pack.
+ *   Each token's row is quantised once however many experts it is routed to. */
+moe_status moe_route_pack_quant(const int32_t* topk_ids, int T, int k, int E,
+                                int layout, int align_or_max_m,
+                                const uint16_t* x, int K,
+                                uint8_t* packed_q, float* packed_sf, int64_t rows_cap,
+                                int32_t* counts, int32_t* seg_offsets,
+                                int32_t* m_indices, int32_t* output_index,
+                                int32_t* dev_status,
+                                void* workspace, int64_t workspace_bytes,
+                                void* stream);
 
 /* moe_route_pack_noalloc: moe_route_pack for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses

@@ -35,6 +35,7 @@ from ._lib import (  # noqa: F401
     moe_quant_weight_int8,
     moe_route_pack,
     moe_route_pack_noalloc,
+    moe_route_pack_quant,
     moe_route_pack_noalloc_max_bytes,
     moe_route_pack_workspace_bytes,
     moe_swiglu_quant,

@@ -40,6 +40,9 @@ SIGNATURES = {
     "moe_route_pack": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_i64,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "moe_route_pack_quant": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      _vp, ctypes.c_int, _vp, _vp, _c_i64,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "moe_route_pack_noalloc_max_bytes": (_c_i64, []),
     "moe_route_pack_noalloc": (_c_i32, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_i64,
@@ -216,6 +219,31 @@ def moe_route_pack(topk_ids, E: int, layout: int, align_or_max_m: int, payload, 
                                  _ptr(payload), rb, _ptr(payload2), rb2, _ptr(packed), _ptr(packed2), rows_cap,
                                  _ptr(counts), _ptr(seg_offsets), _ptr(m_indices), _ptr(output_index),
                                  _ptr(dev_status), _ptr(workspace), ws_bytes, _stream(stream)), "moe_route_pack")
+
+
+def moe_route_pack_quant(topk_ids, E: int, layout: int, align_or_max_m: int, x, packed_q, packed_sf, counts,
+                         seg_offsets, m_indices, output_index, dev_status, workspace=None, stream=None):
+    """moe_quant_act + moe_route_pack in one call: x bf16 [T, K] -> packed_q uint8 [rows_cap, K] (E4M3 codes) and
+    packed_sf float32 [rows_cap, K/128], plus the routing outputs of moe_route_pack."""
+    _dev(topk_ids, "topk_ids", torch.int32, 2), _dev(x, "x", torch.bfloat16, 2)
+    _dev(packed_q, "packed_q", torch.uint8, 2), _dev(packed_sf, "packed_sf", torch.float32, 2)
+    for n, t in (("counts", counts), ("seg_offsets", seg_offsets), ("m_indices", m_indices),
+                 ("output_index", output_index), ("dev_status", dev_status)):
+        _dev(t, n, torch.int32)
+    _dev(workspace, "workspace")
+    T, k = topk_ids.shape
+    K = x.shape[1]
+    rows_cap = packed_q.shape[0]
+    if x.shape[0] != T or packed_q.shape[1] != K or tuple(packed_sf.shape) != (rows_cap, K // 128):
+        raise ValueError("moe_route_pack_quant: shape mismatch")
+    if m_indices.numel() < rows_cap or counts.numel() < E or seg_offsets.numel() < E + 1 or \
+            output_index.numel() < T * k:
+        raise ValueError("moe_route_pack_quant: output arrays too small")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().moe_route_pack_quant(_ptr(topk_ids), T, k, E, layout, align_or_max_m, _ptr(x), K, _ptr(packed_q),
+                                       _ptr(packed_sf), rows_cap, _ptr(counts), _ptr(seg_offsets), _ptr(m_indices),
+                                       _ptr(output_index), _ptr(dev_status), _ptr(workspace), ws_bytes,
+                                       _stream(stream)), "moe_route_pack_quant")
 
 
 def moe_route_pack_noalloc_max_bytes() -> int:

@@ -215,6 +215,8 @@ static moe_status check_route(const char* fn, const int32_t* topk_ids, int T, in
   a.dev_status = dev_status;
   a.ws = nullptr;
   a.nchunks = 0;
+  a.xq = nullptr;  // copy the payload rows (moe_route_pack_quant sets the quantising source)
+  a.K = 0;
   return MOE_OK;
 }
 
@@ -226,7 +228,7 @@ moe_status moe_route_pack(const int32_t* topk_ids, int T, int k, int E, int layo
                           int32_t* seg_offsets, int32_t* m_indices, int32_t* output_index, int32_t* dev_status,
                           void* workspace, int64_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  RouteArgs a;
+  RouteArgs a{};
   moe_status st = check_route("moe_route_pack", topk_ids, T, k, E, layout, align_or_max_m, payload,
                               payload_row_bytes, payload2, payload2_row_bytes, packed, packed2, rows_cap, counts,
                               seg_offsets, m_indices, output_index, dev_status, a);
@@ -239,6 +241,32 @@ moe_status moe_route_pack(const int32_t* topk_ids, int T, int k, int E, int layo
   return hip_status(launch_route_pack(a, (hipStream_t)stream), "moe_route_pack");
 }
 
+moe_status moe_route_pack_quant(const int32_t* topk_ids, int T, int k, int E, int layout, int align_or_max_m,
+                                const uint16_t* x, int K, uint8_t* packed_q, float* packed_sf, int64_t rows_cap,
+                                int32_t* counts, int32_t* seg_offsets, int32_t* m_indices, int32_t* output_index,
+                                int32_t* dev_status, void* workspace, int64_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (K <= 0 || K % 128 || K / 128 > kMaxKBlocks)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_route_pack_quant: K=%d must be a positive multiple of 128 up to %d", K,
+                kMaxKBlocks * 128);
+  if (rows_cap > 0 && !packed_sf) return fail(MOE_ERR_NULL, "moe_route_pack_quant: packed_sf is null");
+  if (!aligned(packed_sf, 4)) return fail(MOE_ERR_ALIGN, "moe_route_pack_quant: packed_sf must be 4-byte aligned");
+  RouteArgs a{};
+  moe_status st = check_route("moe_route_pack_quant", topk_ids, T, k, E, layout, align_or_max_m, x, 2 * (int64_t)K,
+                              nullptr, 0, packed_q, nullptr, rows_cap, counts, seg_offsets, m_indices, output_index,
+                              dev_status, a);
+  if (st) return st;
+  const int64_t ws_need = route_workspace_bytes(a.R, E);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need || !aligned(workspace, 4)))
+    return fail(MOE_ERR_WORKSPACE, "moe_route_pack_quant: needs %lld workspace bytes, got %lld", (long long)ws_need,
+                (long long)workspace_bytes);
+  a.ws = (int32_t*)workspace;
+  a.xq = x;
+  a.K = K;
+  a.packed2 = (uint8_t*)packed_sf;
+  return hip_status(launch_route_pack(a, (hipStream_t)stream), "moe_route_pack_quant");
+}
+
 int64_t moe_route_pack_noalloc_max_bytes(void) { return route_scratch_bytes(); }
 
 moe_status moe_route_pack_noalloc(const int32_t* topk_ids, int T, int k, int E, int layout, int align_or_max_m,
@@ -247,7 +275,7 @@ moe_status moe_route_pack_noalloc(const int32_t* topk_ids, int T, int k, int E, 
                                   int32_t* counts, int32_t* seg_offsets, int32_t* m_indices, int32_t* output_index,
                                   int32_t* dev_status, void* stream) {
   g_err[0] = 0;
-  RouteArgs a;
+  RouteArgs a{};
   moe_status st = check_route("moe_route_pack_noalloc", topk_ids, T, k, E, layout, align_or_max_m, payload,
                               payload_row_bytes, payload2, payload2_row_bytes, packed, packed2, rows_cap, counts,
                               seg_offsets, m_indices, output_index, dev_status, a);

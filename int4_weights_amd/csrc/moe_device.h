@@ -91,6 +91,38 @@ __device__ __forceinline__ float max16_lanes(float v) {
 
 // One 128-value block of SwiGLU and its 1x128 requantisation, spread over 16 consecutive lanes (all active):
 // each lane holds 8 consecutive gate and up values as bf16 pairs (element 2i in the low half of word i),
+// One 1x128 FP8 block held by 8 consecutive lanes, 16 consecutive bf16 per
+// lane (raw0: elements 0..7, raw1: 8..15): the block's power-of-two exponent
+// e (amax <= 448 * 2^e, smallest such e) and this lane's 16 E4M3 codes of
+// x * 2^-e.  gfx950's v_cvt_pk_fp8_f32 converts to OCP E4M3FN with round to
+// nearest even, subnormals and sign kept; the scaled values never exceed 448.
+__device__ __forceinline__ uint4 fp8_block16(const v4i raw0, const v4i raw1, int& e) {
+  float f[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w0 = (uint32_t)raw0[i], w1 = (uint32_t)raw1[i];
+    f[2 * i] = bf16_to_f32(w0 & 0xffffu);
+    f[2 * i + 1] = bf16_to_f32(w0 >> 16);
+    f[8 + 2 * i] = bf16_to_f32(w1 & 0xffffu);
+    f[8 + 2 * i + 1] = bf16_to_f32(w1 >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = max8_lanes(amax);
+  e = pow2_exponent(amax);
+  uint32_t o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(f[4 * r], -e),
+                                           __builtin_amdgcn_ldexpf(f[4 * r + 1], -e), 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(f[4 * r + 2], -e),
+                                       __builtin_amdgcn_ldexpf(f[4 * r + 3], -e), c, true);
+    o[r] = (uint32_t)c;
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
+}
+
 // h = silu(gate) * up in fp32, the block's amax over the 16 lanes, e = pow2_exponent(amax), and this lane's
 // 8 E4M3 codes of h * 2^-e (round to nearest even) packed little-endian into *codes.  Returns e.
 __device__ __forceinline__ int swiglu_quant16(const v4i g, const v4i u, uint2* codes) {

@@ -42,6 +42,8 @@ struct RouteArgs {
   int32_t* dev_status;
   int32_t* ws;      // workspace (large path): chunk counts [nchunks*E] then status [nchunks]
   int nchunks;
+  const uint16_t* xq;  // quantising pack: bf16 token rows [T, K] (nullptr: copy payload rows)
+  int K;               // quantising pack: packed = E4M3 codes [rows_cap, K], packed2 = fp32 scales [rows_cap, K/128]
 };
 constexpr int kRouteSmallMax = 4096;   // routes handled by the single-launch path
 constexpr int kRouteChunk = 1024;      // routes per counting workgroup (large path)

@@ -21,33 +21,10 @@ namespace moe {
 // slower on 4096 x 7168 and 8192 x 4096).
 __device__ __forceinline__ void quant_act_block(const v4i raw0, const v4i raw1, int64_t blk, bool ok, int sub,
                                                 uint8_t* __restrict__ q, float* __restrict__ sf) {
-  float f[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w0 = (uint32_t)raw0[i], w1 = (uint32_t)raw1[i];
-    f[2 * i] = bf16_to_f32(w0 & 0xffffu);
-    f[2 * i + 1] = bf16_to_f32(w0 >> 16);
-    f[8 + 2 * i] = bf16_to_f32(w1 & 0xffffu);
-    f[8 + 2 * i + 1] = bf16_to_f32(w1 >> 16);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  amax = max8_lanes(amax);
-  const int e = pow2_exponent(amax);
-  // gfx950's v_cvt_pk_fp8_f32 converts to OCP E4M3FN with round to nearest
-  // even, subnormals kept, sign kept; the scaled values never exceed 448
-  uint32_t o[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    int c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(f[4 * r], -e),
-                                           __builtin_amdgcn_ldexpf(f[4 * r + 1], -e), 0, false);
-    c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(f[4 * r + 2], -e),
-                                       __builtin_amdgcn_ldexpf(f[4 * r + 3], -e), c, true);
-    o[r] = (uint32_t)c;
-  }
+  int e;
+  const uint4 codes = fp8_block16(raw0, raw1, e);
   if (ok) {
-    *(uint4*)(q + blk * 128 + sub * 16) = uint4{o[0], o[1], o[2], o[3]};
+    *(uint4*)(q + blk * 128 + sub * 16) = codes;
     if (sub == 0) sf[blk] = pow2f(e);
   }
 }

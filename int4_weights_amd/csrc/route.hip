@@ -1,5 +1,6 @@
 // route.hip -- moe_route_pack: per-expert counts, segment offsets, a stable
-// rank for every route, and the copy of token rows into the packed layout.
+// rank for every route, and the copy of token rows into the packed layout
+// (moe_route_pack_quant: the bf16 rows quantised to 1x128 FP8 on the way).
 //
 // What is computed (rainlin, "GEMM 执行方式", sec. 4.2-4.3, 4.6; AsymGEMM README,
 // "Token Layout Protocols"; CuTeDSL bei Perplexity, MoE dispatch):
@@ -25,6 +26,7 @@
 namespace moe {
 
 constexpr int kDevIdRange = 1, kDevCapacity = 2;
+constexpr int kMaxTopk = 64;  // the largest k the C ABI accepts
 
 // Rank of each route among the earlier routes of one 256-route sub-chunk with
 // the same expert, plus per-expert totals.  Every thread holds one route id
@@ -100,6 +102,46 @@ __device__ inline void place_route(const RouteArgs& a, int i, int p) {
     copy_row(a.payload2 + (int64_t)t * a.row_bytes2, a.packed2 + (int64_t)p * a.row_bytes2, a.row_bytes2);
 }
 
+// Quantising pack: token t's bf16 row quantised once (1x128 blocks, power-of-
+// two scales, E4M3 codes: the rule of moe_quant_act) and written to every
+// packed row of its routes, s_p[j] (j < k, -1 = none).  All 4 waves of the
+// workgroup call this with the same t: wave w takes the 8-block passes w,
+// w + 4, ... (8 lanes per block), so a token's row is spread over the
+// workgroup and each lane stores its 16 codes to all k rows.  The block
+// scales are collected in s_sc and written as whole scale rows once every
+// wave is done (a caller's barrier follows), so each packed scale row is
+// one contiguous store rather than eight 32-byte pieces.
+__device__ inline void place_token_quant(const RouteArgs& a, int t, const int* s_p, float* s_sc) {
+  const int w = threadIdx.x >> 6, lane = lane_id(), sub = lane & 7;
+  const int nblk = a.K / 128;
+  const uint16_t* x = a.xq + (int64_t)t * a.K;
+  for (int b0 = 8 * w; b0 < nblk; b0 += 32) {
+    const int blk = b0 + (lane >> 3);
+    const bool ok = blk < nblk;
+    v4i r0 = {0, 0, 0, 0}, r1 = {0, 0, 0, 0};
+    if (ok) {
+      r0 = *(const v4i*)(x + (int64_t)blk * 128 + sub * 16);
+      r1 = *(const v4i*)(x + (int64_t)blk * 128 + sub * 16 + 8);
+    }
+    int e;
+    const uint4 cw = fp8_block16(r0, r1, e);
+    const v4i codes = {(int)cw.x, (int)cw.y, (int)cw.z, (int)cw.w};
+    if (!ok) continue;
+    if (sub == 0) s_sc[blk] = pow2f(e);
+    for (int j = 0; j < a.k; ++j) {
+      const int p = s_p[j];
+      if (p < 0) continue;
+      __builtin_nontemporal_store(codes, (v4i*)(a.packed + (int64_t)p * a.K + (int64_t)blk * 128 + sub * 16));
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.k * nblk; i += blockDim.x) {
+    const int j = i / nblk, b = i - j * nblk;
+    const int p = s_p[j];
+    if (p >= 0) __builtin_nontemporal_store(s_sc[b], (float*)a.packed2 + (int64_t)p * nblk + b);
+  }
+}
+
 // m_indices[r] for r in this workgroup's grid-stride share; s_start[0..E] in LDS.
 __device__ inline void fill_m_indices(const RouteArgs& a, const int* s_start) {
   const int64_t total = s_start[a.E];
@@ -167,14 +209,35 @@ __global__ __launch_bounds__(256) void route_small_kernel(const RouteArgs a) {
     if (tid == 0 && s_flags) *a.dev_status |= s_flags;
   }
   const int w = tid >> 6;
-  for (int i = blockIdx.x * 4 + w; i < a.R; i += gridDim.x * 4) {
-    const int id = s_ids[i];
-    int p = -1;
-    if (id >= 0) {
-      const int rank = s_rank[i];
-      if (!(a.masked && rank >= a.max_m)) p = s_start[id] + rank;
+  if (a.xq) {
+    // quantising pack: one token (its k routes) per workgroup
+    __shared__ int s_p[kMaxTopk];
+    __shared__ float s_sc[kMaxKBlocks];
+    for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
+      if (tid < a.k) {
+        const int i = t * a.k + tid;
+        int p = -1;
+        if (s_ids[i] >= 0) {
+          const int rank = s_rank[i];
+          if (!(a.masked && rank >= a.max_m)) p = s_start[s_ids[i]] + rank;
+        }
+        a.output_index[i] = p;
+        s_p[tid] = p;
+      }
+      __syncthreads();
+      place_token_quant(a, t, s_p, s_sc);
+      __syncthreads();  // s_p is rewritten for the next token
     }
-    place_route(a, i, p);
+  } else {
+    for (int i = blockIdx.x * 4 + w; i < a.R; i += gridDim.x * 4) {
+      const int id = s_ids[i];
+      int p = -1;
+      if (id >= 0) {
+        const int rank = s_rank[i];
+        if (!(a.masked && rank >= a.max_m)) p = s_start[id] + rank;
+      }
+      place_route(a, i, p);
+    }
   }
   fill_m_indices(a, s_start);
 }
@@ -257,15 +320,34 @@ __global__ __launch_bounds__(256) void route_gather_kernel(const RouteArgs a) {
   for (int e = threadIdx.x; e <= a.E; e += blockDim.x) s_start[e] = a.seg_offsets[e];
   __syncthreads();
   const int w = threadIdx.x >> 6;
-  for (int i = blockIdx.x * 4 + w; i < a.R; i += gridDim.x * 4) {
-    int id = a.ids[i];
+  auto packed_row = [&](int i) {
+    const int id = a.ids[i];
     int p = -1;
     if (id >= 0 && id < a.E) {
       const int local = a.output_index[i];
       const int rank = a.ws[(int64_t)(i / kRouteChunk) * a.E + id] + local;
       if (!(a.masked && rank >= a.max_m)) p = s_start[id] + rank;
     }
-    place_route(a, i, p);
+    return p;
+  };
+  if (a.xq) {
+    // quantising pack: one token (its k routes) per workgroup; thread j reads route j's rank from output_index
+    // and replaces it with the packed row
+    __shared__ int s_p[kMaxTopk];
+    __shared__ float s_sc[kMaxKBlocks];
+    for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
+      if (threadIdx.x < a.k) {
+        const int i = t * a.k + threadIdx.x;
+        const int p = packed_row(i);
+        a.output_index[i] = p;
+        s_p[threadIdx.x] = p;
+      }
+      __syncthreads();
+      place_token_quant(a, t, s_p, s_sc);
+      __syncthreads();  // s_p is rewritten for the next token
+    }
+  } else {
+    for (int i = blockIdx.x * 4 + w; i < a.R; i += gridDim.x * 4) place_route(a, i, packed_row(i));
   }
   fill_m_indices(a, s_start);
 }
@@ -309,8 +391,8 @@ int64_t route_workspace_bytes(int R, int E) {
 hipError_t launch_route_pack(const RouteArgs& a0, hipStream_t s) {
   RouteArgs a = a0;
   const int cus = device_info().cus;
-  const int64_t row_work = (int64_t)a.R;  // one wave per route
-  int gather_grid = (int)((row_work + 3) / 4);
+  // one wave per route (quantising: one workgroup per token)
+  int gather_grid = a.xq ? a.T : (int)(((int64_t)a.R + 3) / 4);
   const int64_t mi_grid = (a.rows_cap + 255) / 256;
   if (mi_grid > gather_grid) gather_grid = (int)mi_grid;
   if (a.R <= kRouteSmallMax) {

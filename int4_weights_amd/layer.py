@@ -1,8 +1,9 @@
 """MoE expert layer built on the libmoe entry points.
 
-One forward pass is the page-5 data flow (rainlin, "GEMM 执行方式", sec. 4.6):
-quantise tokens -> route and pack -> grouped GEMM -> weighted combine, four
-launches on one stream with no host synchronisation.  Buffers are allocated
+One forward pass is the data flow of rainlin, "GEMM 执行方式", sec. 4.6:
+quantise tokens -> route and pack -> grouped GEMM -> weighted combine, on one
+stream with no host synchronisation (the first two steps can run as one call
+that quantises while it packs).  Buffers are allocated
 once, for a maximum token count, so a forward allocates nothing.
 """
 
@@ -62,6 +63,17 @@ class MoeFP8Layer:
                          self.seg_offsets, self.m_indices[:rows], oi, self.dev_status, payload2=sf,
                          packed2=self.packed_sf[:rows], workspace=self.workspace)
 
+    def quant_route(self, x, topk_ids):
+        """quant() and route() in one launch sequence (moe_route_pack_quant): the packed codes and scales are the
+        same bits, each token row is quantised once, and the token-order codes (self.q, self.sf) are not written."""
+        T = topk_ids.shape[0]
+        _, _, oi, _ = self._views(T)
+        rows = L.moe_packed_rows_cap(T, self.topk, self.E, self.am) if self.layout == L.LAYOUT_CONTIGUOUS \
+            else self.rows_cap
+        L.moe_route_pack_quant(topk_ids, self.E, self.layout, self.am, x, self.packed[:rows],
+                               self.packed_sf[:rows], self.counts, self.seg_offsets, self.m_indices[:rows], oi,
+                               self.dev_status, workspace=self.workspace)
+
     def gemm(self, A=None, SFA=None, D=None, w=None, sfw=None, N=None, K=None):
         """Grouped GEMM on the packed rows (defaults: this layer's buffers and weights)."""
         A = self.packed if A is None else A
@@ -103,9 +115,13 @@ class MoeFP8Layer:
         L.moe_unpermute_combine(D, oi, topk_weights, Z)
         return Z
 
-    def forward(self, x, topk_ids, topk_weights):
-        self.quant(x)
-        self.route(topk_ids)
+    def forward(self, x, topk_ids, topk_weights, fused_quant=False):
+        """fused_quant: quantise while packing (quant_route) instead of quant() then route()."""
+        if fused_quant:
+            self.quant_route(x, topk_ids)
+        else:
+            self.quant(x)
+            self.route(topk_ids)
         self.gemm()
         return self.combine(topk_weights)
 

@@ -53,6 +53,10 @@ def _p(v):
     return ctypes.c_void_p(v)
 
 
+def moe_cap(lib, T, k, E, align):
+    return lib.moe_packed_rows_cap(T, k, E, align)
+
+
 A16 = 1 << 20  # a fake, 16-byte aligned address: never dereferenced on these error paths
 
 
@@ -233,6 +237,25 @@ def test_host_validation_rejects_without_launching(lib):
     assert gs(Q=A16 + 8) == MOE_ERR_ALIGN
     assert gs(SFA=A16 + 4) == MOE_ERR_ALIGN          # row scales: 16-byte copies
     assert gs(SQ=A16 + 2) == MOE_ERR_ALIGN
+    # moe_route_pack_quant(ids, T, k, E, layout, am, x, K, packed_q, packed_sf, rows_cap, counts, seg, mi, oi,
+    #                      status, ws, ws_bytes, stream)
+    def rq(T=5, k=2, E=4, layout=0, am=128, K=256, x=A16, pq=A16 << 4, psf=A16 << 6, rows_cap=640, ids=A16):
+        return lib.moe_route_pack_quant(_p(ids) if ids else None, T, k, E, layout, am, _p(x) if x else None, K,
+                                        _p(pq) if pq else None, _p(psf) if psf else None, rows_cap, _p(A16),
+                                        _p(A16), _p(A16), _p(A16), _p(A16), None, 0, None)
+
+    assert rq(K=200) == MOE_ERR_UNSUPPORTED
+    assert rq(K=0) == MOE_ERR_UNSUPPORTED
+    assert rq(K=257 * 128) == MOE_ERR_UNSUPPORTED       # more 128-blocks than a row's scales the kernel stages
+    assert rq(x=0) == MOE_ERR_NULL
+    assert rq(psf=0) == MOE_ERR_NULL
+    assert rq(pq=0) == MOE_ERR_NULL
+    assert rq(x=A16 + 8) == MOE_ERR_ALIGN
+    assert rq(pq=(A16 << 4) + 8) == MOE_ERR_ALIGN
+    assert rq(psf=(A16 << 6) + 2) == MOE_ERR_ALIGN
+    assert rq(rows_cap=100) == MOE_ERR_SHAPE           # below what the routes need
+    assert rq(layout=3) == MOE_ERR_SHAPE
+    assert rq(T=5000, k=8, rows_cap=moe_cap(lib, 5000, 8, 4, 128)) == MOE_ERR_WORKSPACE  # multi-launch path, no workspace
     # moe_quant_act_int8 / moe_quant_weight_int8
     assert lib.moe_quant_act_int8(_p(A16), 4, 100, _p(A16), _p(A16), None) == MOE_ERR_UNSUPPORTED
     assert lib.moe_quant_act_int8(None, 4, 128, _p(A16), _p(A16), None) == MOE_ERR_NULL

@@ -1,6 +1,7 @@
 """Full-size parity: every workload at its measured shape, launched the way the
 benchmark launches it (MoeFP8Layer / MoeInt4Layer, tiling hint = routes per
-expert), checked against the oracle.
+expert; for the FP8 workloads both the two-call quantise + pack and the
+quantising pack the benchmark times), checked against the oracle.
 
 Routing and packing are checked bit-exactly on every route; activation and
 weight quantisation bit-exactly on sampled token rows and weight blocks; the
@@ -169,6 +170,22 @@ def _fp8_gemm_and_combine(c, r, A_bits_of_token, D, Z, kept_codes_fn, label):
     gemm_tolerance_check(zg[None], zr[None], 1e-3 if label == "fp8" else 1e-2)
 
 
+def _check_fused_quant_pack(layer, x, ids, r, T):
+    """The benchmark's launch: moe_route_pack_quant (quantise while packing) gives the same routing outputs and
+    the same packed codes and scale rows, on every valid route, as the two-call path checked against the oracle."""
+    oiv = r["output_index"].reshape(-1)
+    rows = torch.from_numpy(oiv[oiv >= 0].astype(np.int64)).to(DEV)
+    pk, psf = layer.packed[rows].clone(), layer.packed_sf[rows].clone()
+    mi, oi = layer.m_indices.clone(), layer.output_index[:T].clone()
+    layer.packed[rows] = 0
+    layer.packed_sf[rows] = -1.0
+    layer.quant_route(x.to(DEV), ids.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(layer.packed[rows], pk)
+    assert torch.equal(layer.packed_sf[rows].view(torch.int32), psf.view(torch.int32))
+    assert torch.equal(layer.m_indices, mi) and torch.equal(layer.output_index[:T], oi)
+
+
 def _oracle_fp8_weight_blocks(c, codes, sfw, kept, N, K):
     """Oracle quantisation of the sampled 128-row blocks of an expert, checked bit-exactly against the GPU's."""
     cache = {}
@@ -199,6 +216,7 @@ def test_full_size_fp8_layer(name):
     toks = sorted(set([0, c["T"] - 1, c["tok"]] + list(range(1, c["T"], max(1, c["T"] // 16)))))
     _check_quant_rows(layer, x_bits, np.array(toks))
     _check_packing(layer, r, c["T"])
+    _check_fused_quant_pack(layer, c["x"], torch.from_numpy(c["ids"]), r, c["T"])
 
     def a_of_tokens(tt):
         a, sa = oracle.quant_act(x_bits[tt])
@@ -219,6 +237,7 @@ def test_full_size_qwen3_skewed_up_down_combine():
     x_bits = u16(c["x"])
     _check_quant_rows(layer, x_bits, np.array([0, 1, c["tok"], c["T"] - 1]))
     _check_packing(layer, r, c["T"])
+    _check_fused_quant_pack(layer, c["x"], torch.from_numpy(c["ids"]), r, c["T"])
 
     def a_of_tokens(tt):
         a, sa = oracle.quant_act(x_bits[tt])

@@ -126,3 +126,73 @@ def test_quant_then_gather_equals_gather_then_quant():
     used = oi[oi >= 0].long()
     assert torch.equal(r1.packed[used], q2[used]) and torch.equal(r1.packed2[used], sf2[used])
     assert rows.numel() >= used.numel()
+
+
+def _route_quant(ids, E, layout, am, x, fill=SENT):
+    """One moe_route_pack_quant call (sentinel-filled outputs)."""
+    T, k = ids.shape
+    K = x.shape[1]
+    rows_cap = moe.moe_packed_rows_cap(T, k, E, am) if layout == moe.LAYOUT_CONTIGUOUS else E * am
+    r = type("RQ", (), {})()
+    r.E, r.layout, r.am, r.rows_cap = E, layout, am, rows_cap
+    r.packed = torch.full((rows_cap, K), fill, dtype=torch.uint8, device=DEV)
+    r.packed2 = torch.empty(rows_cap, K // 128, dtype=torch.float32, device=DEV)
+    r.packed2.view(torch.uint8).fill_(fill)
+    r.counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    r.seg_offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    r.m_indices = torch.full((rows_cap,), -7, dtype=torch.int32, device=DEV)
+    r.output_index = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    r.dev_status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    wsb = moe.moe_route_pack_workspace_bytes(T, k, E)
+    ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=DEV) if wsb > 0 else None
+    moe.moe_route_pack_quant(ids, E, layout, am, x, r.packed, r.packed2, r.counts, r.seg_offsets, r.m_indices,
+                             r.output_index, r.dev_status, workspace=ws)
+    torch.cuda.synchronize()
+    return r
+
+
+QUANT_CASES = [
+    # (T, k, E, layout, align/max_m, id low..high, K): single-launch and multi-launch paths
+    (1, 1, 1, 0, 128, 0, 1, 128),
+    (37, 3, 9, 0, 16, -2, 11, 384),      # negative and out-of-range ids
+    (512, 8, 64, 1, 20, 0, 64, 256),     # masked, capacity overflow
+    (600, 8, 64, 0, 128, -1, 66, 4352),  # multi-launch path (4800 routes), 34 blocks per row (a partial group of 32)
+    (700, 8, 96, 1, 40, 0, 96, 1024),    # multi-launch, masked with overflow
+    (0, 4, 8, 0, 128, 0, 8, 256),        # empty
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES)
+def test_route_pack_quant_equals_quant_then_pack(case):
+    """The quantising pack against the oracle (routing outputs and, for every route, the oracle's 1x128 codes and
+    scales of its token row; untouched padding rows) and against moe_quant_act followed by moe_route_pack, bit for
+    bit."""
+    require_gpu()
+    from gpu_helpers import fp8_quant_gpu
+    T, k, E, layout, am, lo, hi, K = case
+    g = torch.Generator().manual_seed(T * 17 + k + E + K)
+    ids = torch.randint(lo, hi, (T, k), generator=g, dtype=torch.int32)
+    x = (torch.randn(T, K, generator=g) * torch.exp2(torch.randint(-8, 9, (T, 1), generator=g).float()))
+    x = x.to(torch.bfloat16)
+    if T > 2:
+        x[1, :128] = 0.0                      # an all-zero block
+        x[2, 128 % K:] *= 1e-30               # tiny values
+    r = _route_quant(ids.to(DEV), E, layout, am, x.to(DEV))
+    o = oracle_route(ids, E, layout, am, r.rows_cap)
+    assert np.array_equal(r.counts.cpu().numpy(), o["counts"])
+    assert np.array_equal(r.seg_offsets.cpu().numpy(), o["seg_offsets"])
+    assert np.array_equal(r.output_index.cpu().numpy(), o["output_index"])
+    assert np.array_equal(r.m_indices.cpu().numpy(), o["m_indices"])
+    assert int(r.dev_status.item()) == o["status"]
+    xb = x.view(torch.int16).numpy().view(np.uint16)
+    q_o, s_o = oracle.quant_act(xb) if T > 0 else (np.zeros((0, K), np.uint8), np.zeros((0, K // 128), np.float32))
+    assert np.array_equal(r.packed.cpu().numpy(), oracle.pack_rows(q_o, o["output_index"], r.rows_cap, fill=SENT))
+    sf_bytes = s_o.view(np.uint8).reshape(T, 4 * (K // 128))
+    got_sf = r.packed2.view(torch.uint8).cpu().numpy()
+    assert np.array_equal(got_sf, oracle.pack_rows(sf_bytes, o["output_index"], r.rows_cap, fill=SENT))
+    if T > 0:
+        q, sf = fp8_quant_gpu(x.to(DEV))
+        chain = Routed(ids.to(DEV), E, layout, am, q, payload2=sf, fill=SENT)
+        assert torch.equal(chain.packed, r.packed) and torch.equal(chain.packed2.view(torch.uint8),
+                                                                   r.packed2.view(torch.uint8))
+        assert torch.equal(chain.output_index, r.output_index) and torch.equal(chain.m_indices, r.m_indices)
