@@ -159,6 +159,8 @@ QUANT_CASES = [
     (600, 8, 64, 0, 128, -1, 66, 4352),  # multi-launch path (4800 routes), 34 blocks per row (a partial group of 32)
     (700, 8, 96, 1, 40, 0, 96, 1024),    # multi-launch, masked with overflow
     (0, 4, 8, 0, 128, 0, 8, 256),        # empty
+    (60, 64, 1024, 0, 128, 0, 1024, 128),  # the largest k and E, one block per row
+    (5, 2, 3, 1, 8, 0, 3, 32768),        # the largest K (256 blocks per row: every scale slot of the kernel)
 ]
 
 
