@@ -30,13 +30,14 @@
 //    Larger segments: 192-row units (a DeepSeek-V3-shaped prefill expert of
 //    about 128 rows is one unit, so its weights stream once), 8 waves of 32
 //    columns (two per SIMD, so one wave's promotion overlaps the other's
-//    matrix instructions), 2-deep ring; the computed height is 64, 128 or
-//    192 rows, whichever covers the unit.  Within a K block, row block rb's
-//    matrix instructions are issued before row block rb - 1 is promoted.
-//    Measured on the DeepSeek-V3-shaped prefill (32768 routed rows, N 4096,
-//    K 7168): 64-row units with 4 waves 3.5 ms, 128-row units with 8 waves
-//    2.6 ms, 192-row units 2.2 ms; deeper rings, weight scales staged through
-//    LDS, and a 2 x 4 wave layout that halves the LDS fragment reads were not
+//    matrix instructions), 2-deep ring; the computed height is the smallest
+//    of 64, 96, 128, 160 and 192 rows that covers the unit.  Within a K
+//    block, row block rb's matrix instructions are issued before row block
+//    rb - 1 is promoted.  Measured on the DeepSeek-V3-shaped prefill (32768
+//    routed rows, N 4096, K 7168): 64-row units with 4 waves 3.5 ms, 128-row
+//    units with 8 waves 2.6 ms, 192-row units 2.2 ms, 2.07 ms with the 96-
+//    and 160-row heights; deeper rings, weight scales staged through LDS,
+//    and a 2 x 4 wave layout that halves the LDS fragment reads were not
 //    faster.
 //  * The K-to-lane assignment of the two instructions is the same for both
 //    operands (lane group g supplies bytes 16g..16g+15 of the block to the
@@ -252,11 +253,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_int8_kernel(const GemmArgs a)
   const int wv = uniform(threadIdx.x >> 6);
   for (int v = walk.first; v < walk.end; v += walk.stride) {
     const Unit u = sched_unit<C::BM>(a, sc, v);
-    // computed height in steps of a third of the full one (RB % 3 == 0) or a half; padding rows never stored
-    if constexpr (RB % 3 == 0) {
-      if (u.mrows <= 16 * (RB / 3)) int8_unit<RB, S, NW, RB / 3>(a, u, sm, wv, lane);
-      else if (u.mrows <= 16 * (2 * RB / 3)) int8_unit<RB, S, NW, 2 * RB / 3>(a, u, sm, wv, lane);
-      else int8_unit<RB, S, NW, RB>(a, u, sm, wv, lane);
+    // computed height: the smallest of 64, 96, 128, 160, 192 rows (RB = 12) that covers the unit, or a half of
+    // the full height; padding rows are never stored
+    if constexpr (RB == 12) {
+      if (u.mrows <= 64) int8_unit<RB, S, NW, 4>(a, u, sm, wv, lane);
+      else if (u.mrows <= 96) int8_unit<RB, S, NW, 6>(a, u, sm, wv, lane);
+      else if (u.mrows <= 128) int8_unit<RB, S, NW, 8>(a, u, sm, wv, lane);
+      else if (u.mrows <= 160) int8_unit<RB, S, NW, 10>(a, u, sm, wv, lane);
+      else int8_unit<RB, S, NW, 12>(a, u, sm, wv, lane);
     } else if constexpr (RB > 1) {
       if (u.mrows <= 16 * ((RB + 1) / 2)) int8_unit<RB, S, NW, (RB + 1) / 2>(a, u, sm, wv, lane);
       else int8_unit<RB, S, NW, RB>(a, u, sm, wv, lane);

@@ -196,7 +196,7 @@ def test_int8_one_hot_rows_pin_the_operand_layout(packed, expected_m):
 @pytest.mark.parametrize("packed,expected_m", [(False, 0), (False, 16), (True, 16), (True, 64)])
 def test_int8_small_integers_exact_and_deterministic(packed, expected_m):
     require_gpu()
-    c = _case(5, [7, 64, 129, 300], N=512, K=1024, layout=moe.LAYOUT_CONTIGUOUS, ints=True)
+    c = _case(5, [7, 64, 90, 129, 300], N=512, K=1024, layout=moe.LAYOUT_CONTIGUOUS, ints=True)
     D = _run(c, expected_m, packed)
     _check(c, D, exact=True)
     for _ in range(10):
@@ -206,10 +206,11 @@ def test_int8_small_integers_exact_and_deterministic(packed, expected_m):
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("expected_m", [0, 16, 64])
 def test_int8_contiguous_ragged(expected_m, packed):
-    """Segments of 0, 1, 17, 130 and 300 rows (partial 16- and 64-row units), N = 384 (the second 256-column tile
-    has two idle waves), K/128 = 13 (ring wrap-arounds plus a tail)."""
+    """Segments of 0, 1, 17, 80, 130 and 300 rows (every computed height of both tiles: 16-row units; 64, 96,
+    128, 160 and 192 of the 192-row units), N = 384 (the second 256-column tile has idle waves), K/128 = 13 (ring
+    wrap-arounds plus a tail)."""
     require_gpu()
-    c = _case(3, [0, 1, 17, 130, 300], N=384, K=1664, layout=moe.LAYOUT_CONTIGUOUS)
+    c = _case(3, [0, 1, 17, 80, 130, 300], N=384, K=1664, layout=moe.LAYOUT_CONTIGUOUS)
     _check(c, _run(c, expected_m, packed))
 
 
