@@ -256,17 +256,23 @@ __global__ __launch_bounds__(256) void route_count_kernel(const RouteArgs a) {
   __syncthreads();
   const int nbits = id_bits(a.E);
   const int c = blockIdx.x;
-  for (int sub = 0; sub < kRouteChunk; sub += 256) {
-    const int i = c * kRouteChunk + sub + tid;
-    int id = -1;
-    if (i < a.R) {
-      id = a.ids[i];
-      if (id >= a.E) {
-        atomicOr(&s_flags, kDevIdRange);
-        id = -1;
-      }
-      if (id < 0) id = -1;
+  // the chunk's ids are loaded up front (one memory round trip, not one per 256-route sub-chunk)
+  constexpr int kSubs = kRouteChunk / 256;
+  int ids[kSubs];
+#pragma unroll
+  for (int j = 0; j < kSubs; ++j) {
+    const int i = c * kRouteChunk + 256 * j + tid;
+    ids[j] = i < a.R ? a.ids[i] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kSubs; ++j) {
+    const int i = c * kRouteChunk + 256 * j + tid;
+    int id = ids[j];
+    if (id >= a.E) {
+      atomicOr(&s_flags, kDevIdRange);
+      id = -1;
     }
+    if (id < 0) id = -1;
     const int rank = rank_subchunk(id, a.E, nbits, s_hist, s_base);
     if (i < a.R) a.output_index[i] = rank;
   }
@@ -288,15 +294,15 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const RouteArgs a) {
     if (f) atomicOr(&s_flags, f);
   }
   for (int e = tid; e < a.E; e += blockDim.x) {
-    // 16 chunks' counts are loaded before any prefix is written back (a plain
+    // 32 chunks' counts are loaded before any prefix is written back (a plain
     // loop would pay one memory round trip per chunk: the store may alias)
     int run = 0;
-    for (int c0 = 0; c0 < a.nchunks; c0 += 16) {
-      int v[16];
+    for (int c0 = 0; c0 < a.nchunks; c0 += 32) {
+      int v[32];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = c0 + j < a.nchunks ? a.ws[(int64_t)(c0 + j) * a.E + e] : 0;
+      for (int j = 0; j < 32; ++j) v[j] = c0 + j < a.nchunks ? a.ws[(int64_t)(c0 + j) * a.E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < 32; ++j)
         if (c0 + j < a.nchunks) {
           a.ws[(int64_t)(c0 + j) * a.E + e] = run;
           run += v[j];
