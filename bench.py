@@ -16,7 +16,7 @@ top-8, K=7168, N=4096, FP8 E4M3 with 1x128 / 128x128 power-of-two scales,
 contiguous 128-row-aligned layout).  The other workloads (the Qwen3-shaped
 skewed prefill, whose up-projection is the MFMA-bound GEMM, the masked FP8
 decode and the 4-bit decode) are timed in the same run and reported under
-"workloads", and the DeepSeek-V3-shaped steps with MXFP4 or bf16 expert
+"workloads", and the DeepSeek-V3-shaped steps with MXFP4, INT8 or bf16 expert
 weights under "variants".  The HBM-bound rooflines are given against the
 nominal 8 TB/s and, as `frac_of_measured_read`, against the rate a plain
 8 GiB streaming read reaches on the same GPU (`measured_hbm_read`).  Prints
