@@ -27,7 +27,8 @@ def _configs(gen):
     """The built configurations, plus the generator's other load distance (3) on each operand format."""
     return list(gen.CONFIGS) + [gen.Cfg(192, 4, "TALL192_D3", dist=3),
                                 gen.Cfg(256, 4, "BF16_TALL256_D3", "bf16", dist=3),
-                                gen.Cfg(256, 4, "FP4_TALL256_D3", "fp4", dist=3)]
+                                gen.Cfg(256, 4, "FP4_TALL256_D3", "fp4", dist=3),
+                                gen.Cfg(256, 4, "SWIGLU_TALL256_D3", swiglu=True, dist=3)]
 
 
 def _programs(gen):
