@@ -248,13 +248,25 @@ __device__ __forceinline__ void quant_int8_block(const v4i raw0, const v4i raw1,
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
   amax = max8_lanes(amax);
   const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
+  // The code is rne of the correctly rounded quotient x / s.  y = x * rn(1/s)
+  // is within 1.5 * 2^-16 of that quotient (two roundings of relative size
+  // 2^-24 each, |x / s| <= 127 * (1 + 2^-23)), so rint(y) is the same code
+  // unless a half-integer lies within 2^-15 of y; those rare elements, and
+  // every element of a block whose scale is below 2^-100 (its reciprocal may
+  // not be a normal fp32 number), take the division itself.
+  const float rs = 1.0f / s;
+  const bool fast = s >= 0x1p-100f;
   uint32_t o[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float c = fminf(fmaxf(__builtin_rintf(f[4 * r + i] / s), -127.0f), 127.0f);
+      const float x = f[4 * r + i];
+      const float y = x * rs;
+      float q = __builtin_rintf(y);
+      if (!(fast && fabsf(y - (floorf(y) + 0.5f)) > 0x1p-15f)) q = __builtin_rintf(x / s);
+      const float c = fminf(fmaxf(q, -127.0f), 127.0f);
       w |= ((uint32_t)(int)c & 0xffu) << (8 * i);
     }
     o[r] = w;

@@ -71,6 +71,24 @@ def test_quant_act_int8_bit_exact():
     assert np.array_equal(gq, oq)
 
 
+def test_quant_act_int8_near_ties_bit_exact():
+    """Many blocks with non-power-of-two scales: a few hundred codes whose quotient x / s lies within 2^-15 of a
+    half-integer (where the kernel re-divides instead of multiplying by the rounded reciprocal) plus every other
+    code, against the oracle's correctly rounded fp32 quotients; heavy-tailed values spread the scales."""
+    require_gpu()
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((20000, 256)) * np.exp(rng.standard_normal((20000, 1)) * 4)).astype(np.float32)
+    bits = _bf16_bits(x)
+    gq, gs = _quant_act_gpu(bits)
+    oq, os_ = oracle.quant_int8(bits)
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(gq, oq)
+    xf = oracle.bf16_bits_to_f64(bits).astype(np.float32).reshape(20000, 2, 128)
+    y = (xf / os_[..., None]).astype(np.float32)
+    near = np.abs(y - (np.floor(y) + 0.5)) <= 2.0 ** -15
+    assert near.sum() > 50, "the draw should exercise the re-division"
+
+
 def test_quant_weight_int8_bit_exact_k_block_major_scales():
     require_gpu()
     rng = np.random.default_rng(2)
