@@ -53,7 +53,6 @@ template <int RB, int S, int NW>
 struct Fp8Smem {
   uint8_t a[2][Fp8Cfg<RB, S, NW>::kAStage];
   float sa[2][Fp8Cfg<RB, S, NW>::kSaStage];
-  float sw[NW][kMaxKBlocks];  // per-wave weight scales of the current unit
 };
 
 // One unit with RBE (<= RB) row blocks computed.
@@ -81,9 +80,8 @@ __device__ __forceinline__ void fp8_unit(const GemmArgs& a, const Unit& u, Fp8Sm
     if (n >= N) n = N - 1;
     woff[cb] = a.wpacked ? (uint32_t)(n / 16) * 2048u + 16u * lane : (uint32_t)n * (uint32_t)K + 16u * lg;
   }
-  // this wave's 128-column block of weight scales for the whole unit -> LDS
+  // this wave's 128-column block of weight scales: one per K block, loaded with the block's weights
   const float* sw_ptr = (const float*)a.SW + ((int64_t)u.e * NB + (wave_on ? ncol0 : 0) / 128) * KB;
-  for (int j = 0; j < KB; j += 64) sm.sw[wv][j + lane] = sw_ptr[min(j + lane, KB - 1)];
   // activation rows this lane's loads fetch (clamped to valid rows)
   const uint8_t* abase = a.A + (int64_t)u.row0 * K;
   uint32_t aoff[C::kApw];
@@ -104,7 +102,7 @@ __device__ __forceinline__ void fp8_unit(const GemmArgs& a, const Unit& u, Fp8Sm
 
   v8i wf[S][CB];
   v4i ar[S][C::kApw];
-  float sr[S];
+  float sr[S], swr[S];
   v4f acc[RBE][CB];
 #pragma unroll
   for (int rb = 0; rb < RBE; ++rb)
@@ -134,6 +132,7 @@ __device__ __forceinline__ void fp8_unit(const GemmArgs& a, const Unit& u, Fp8Sm
 #pragma unroll
     for (int i = 0; i < C::kApw; ++i) ar[slot][i] = *(const v4i*)(abase + (aoff[i] + koff));
     sr[slot] = sarow[ks];
+    swr[slot] = sw_ptr[ks];
   };
 
   // stage registers -> LDS slot (ks & 1)
@@ -147,7 +146,7 @@ __device__ __forceinline__ void fp8_unit(const GemmArgs& a, const Unit& u, Fp8Sm
 
   auto compute = [&](int ks, auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
-    const int swe = (int)(__float_as_uint(sm.sw[wv][ks]) >> 23);
+    const int swe = (int)(__float_as_uint(swr[slot]) >> 23);
     const uint8_t* ab = &sm.a[ks & 1][0];
     const float* sab = &sm.sa[ks & 1][l16];
 #pragma unroll
