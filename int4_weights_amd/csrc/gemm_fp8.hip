@@ -21,8 +21,8 @@
 //    are loaded into VGPRs with the weights (same ring depth), then written
 //    to one of two LDS slots XOR-swizzled so fragment reads are bank-conflict
 //    free; the row scales ride along.  All loads are plain vector loads, so the
-//    compiler's wait counts stay exact.  Each wave's weight scales for the unit
-//    are staged once per unit.
+//    compiler's wait counts stay exact.  Each wave's weight scale of a K block
+//    (one per 128 columns) is loaded into the ring with the block's weights.
 //  * Every stage issues the same loads (the tail re-reads the last K block
 //    instead of skipping), so the wait pattern is identical for every stage.
 //  * Rows: a unit holds at most BM = 16*RB rows; it runs with the smaller of
